@@ -1,0 +1,238 @@
+"""Pins of the MoE oracle: brute force, closed forms, library special cases,
+a dense masked evaluation, invariants and the page-printed block arithmetic."""
+
+import os
+
+import numpy as np
+import pytest
+
+from oracle import formats as F
+from oracle import moe as O
+from quantized_moe_expert_route_amd import fixtures as X
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _brute_topk(l, k):
+    """Repeatedly take the largest remaining logit, lowest index on ties."""
+    l = [float(v) for v in l]
+    taken = []
+    for _ in range(k):
+        best = None
+        for e, v in enumerate(l):
+            if e in taken:
+                continue
+            if best is None or v > l[best]:
+                best = e
+        taken.append(best)
+    return taken
+
+
+@pytest.mark.parametrize("kind", ["normal", "uniform", "ties", "correlated", "zipf"])
+def test_route_ids_brute_force(kind):
+    shape = X.Shape(M=24, H=512, E=64 if kind != "correlated" else 64, I=128, top_k=8)
+    logits = X.make_logits(shape, kind, 11)
+    ids, w = O.route(logits, 8, 2.5)
+    for t in range(shape.M):
+        assert list(ids[t]) == _brute_topk(logits[t], 8)
+
+
+def test_route_ties_signed_zero():
+    l = np.array([[-0.0, 0.0, -0.0, 0.0, -1.0, -0.0]], np.float32)
+    ids, _ = O.route(l, 4, 1.0)
+    assert list(ids[0]) == [0, 1, 2, 3]
+
+
+def test_route_weights_closed_forms():
+    # equal logits 0: sigma = 1/2, S = k/2, w = scaling / k exactly
+    ids, w = O.route(np.zeros((3, 16), np.float32), 8, 2.5)
+    assert list(ids[0]) == list(range(8))
+    assert np.all(w == np.float32(2.5 / 8))
+    # sum of weights = scaling factor
+    l = X.make_logits(X.Shape(M=64, H=512, E=256, I=128, top_k=8), "zipf", 5)
+    _, w = O.route(l, 8, 2.5)
+    assert np.allclose(w.astype(np.float64).sum(1), 2.5, rtol=1e-6, atol=0)
+    # two selected logits a, b: w_a = 2.5 * s(a) / (s(a) + s(b))
+    l = np.array([[3.0, -1.0, -5.0]], np.float32)
+    _, w = O.route(l, 2, 2.5)
+    sa, sb = 1 / (1 + np.exp(-3.0)), 1 / (1 + np.exp(1.0))
+    assert abs(w[0, 0] - 2.5 * sa / (sa + sb)) < 1e-6
+    # all selected logits -inf: zero weights
+    _, w = O.route(np.full((1, 8), -np.inf, np.float32), 4, 2.5)
+    assert np.all(w == 0)
+
+
+def test_align_brute_force():
+    rng = np.random.default_rng(0)
+    for M, E, k in [(1, 4, 1), (5, 16, 2), (37, 32, 8), (64, 256, 8)]:
+        ids = np.stack([rng.choice(E, k, replace=False) for _ in range(M)])
+        count, offset, se = O.align(ids, E)
+        expect = []
+        for e in range(E):
+            for t in range(M):
+                for j in range(k):
+                    if ids[t, j] == e:
+                        expect.append(t * k + j)
+        assert list(se) == expect
+        assert offset[E] == M * k and offset[0] == 0
+        assert all(count[e] == sum(1 for v in ids.ravel() if v == e) for e in range(E))
+
+
+def _grid_x(rng, M, H):
+    """bf16 x whose 32-blocks sit on the E2M1 grid with block max 4: MX
+    quantization is then the identity (scale code 127)."""
+    x = F.e2m1_decode(rng.integers(0, 16, size=(M, H)))
+    x[:, ::32] = 4.0
+    return F.bf16_encode(x), x
+
+
+def test_dequant_nibbles_and_scales():
+    # byte 0x21 with scale code 128 -> [0.5, 1.0] * 2
+    packed = np.zeros((1, 16), np.uint8)
+    packed[0, 0] = 0x21
+    d = O.dequant_mxfp4(packed, np.array([[128]], np.uint8))
+    assert d[0, 0] == 1.0 and d[0, 1] == 2.0 and np.all(d[0, 2:] == 0)
+
+
+def test_gate_up_on_grid_is_matmul():
+    rng = np.random.default_rng(1)
+    M, H, I = 5, 256, 128
+    xb, x = _grid_x(rng, M, H)
+    xq, xs = O.quantize_x(xb)
+    assert np.all(xs == 127)
+    xd = F.mx_fp4_decode(xq, xs)
+    assert np.array_equal(xd, x)
+    wc = rng.integers(0, 16, size=(2 * I, H)).astype(np.uint8)
+    w13 = F.pack_fp4(wc)
+    s13 = np.full((2 * I, H // 32), 127, np.uint8)
+    wd = O.dequant_mxfp4(w13, s13)
+    assert np.array_equal(wd, F.e2m1_decode(wc))
+    h = O.gate_up(xd, wd, I)
+    g = np.matmul(x, F.e2m1_decode(wc[:I]).T).astype(np.float32)
+    u = np.matmul(x, F.e2m1_decode(wc[I:]).T).astype(np.float32)
+    silu = g.astype(np.float64) / (1 + np.exp(-g.astype(np.float64)))
+    assert np.array_equal(h, (silu * u).astype(np.float32))
+    # the halves are not interchangeable: gate rows are [0, I)
+    swapped = np.concatenate([wd[I:], wd[:I]])
+    assert not np.array_equal(O.gate_up(xd, swapped, I), h)
+
+
+def test_down_on_grid_is_matmul():
+    rng = np.random.default_rng(2)
+    r, H, I = 6, 256, 256
+    q = (rng.integers(0, 126, size=(r, I)) | (rng.integers(0, 2, size=(r, I)) << 7)).astype(np.uint8)
+    s = np.ones((r, I // 128), np.float32)
+    wc = rng.integers(0, 16, size=(H, I)).astype(np.uint8)
+    w2d = O.dequant_mxfp4(F.pack_fp4(wc), np.full((H, I // 32), 127, np.uint8))
+    y = O.down(q, s, w2d)
+    assert np.array_equal(y, np.matmul(F.e4m3_decode(q), F.e2m1_decode(wc).T).astype(np.float32))
+    # a power-of-two block scale scales that block's contribution exactly
+    s2 = s.copy()
+    s2[:, 1] = 4.0
+    q0 = q.copy()
+    q0[:, :128] = 0
+    assert np.array_equal(O.down(q0, s2, w2d), (4 * O.down(q0, s, w2d)).astype(np.float32))
+
+
+def test_shared_linear_on_grid_is_matmul():
+    rng = np.random.default_rng(3)
+    a = (rng.integers(0, 120, size=(4, 256))).astype(np.uint8)
+    w = (rng.integers(0, 120, size=(256, 256))).astype(np.uint8)
+    y = O._block_fp8_linear(a, np.ones((4, 2), np.float32), w, np.ones((2, 2), np.float32))
+    assert np.array_equal(y, np.matmul(F.e4m3_decode(a), F.e4m3_decode(w).T).astype(np.float32))
+    ws = np.array([[1.0, 2.0], [0.5, 8.0]], np.float32)  # per 128x128 block
+    y2 = O._block_fp8_linear(a, np.ones((4, 2), np.float32), w, ws)
+    ad, wd = F.e4m3_decode(a), F.e4m3_decode(w)
+    ref = np.zeros((4, 256))
+    for nb in range(2):
+        for kb in range(2):
+            ref[:, 128 * nb:128 * (nb + 1)] += ws[nb, kb] * (
+                ad[:, 128 * kb:128 * (kb + 1)] @ wd[128 * nb:128 * (nb + 1), 128 * kb:128 * (kb + 1)].T)
+    assert np.array_equal(y2, ref.astype(np.float32))
+
+
+def _run(d, fn=O.moe_forward, **kw):
+    s = d["shape"]
+    shared = (d["ws13"], d["ss13"], d["ws2"], d["ss2"]) if s.shared_I else None
+    args = dict(x_bits=d["x"], logits=d["logits"], w13=d["w13"], s13=d["s13"], w2=d["w2"],
+                s2=d["s2"], top_k=s.top_k, scaling=s.routed_scaling, shared=shared)
+    args.update(kw)
+    return fn(**args)
+
+
+@pytest.mark.parametrize("M,E,k,kind", [(4, 16, 2, "normal"), (1, 4, 1, "normal"), (8, 16, 4, "ties"),
+                                        (3, 4, 4, "uniform"), (6, 8, 2, "normal")])
+def test_dense_equals_sparse(M, E, k, kind):
+    shape = X.Shape(M=M, H=512, E=E, I=128, top_k=k)
+    d = X.make_inputs(shape, kind, 7)
+    sparse = _run(d)["out"]
+    dense = _run(d, fn=O.moe_dense)
+    assert np.array_equal(sparse, dense)
+
+
+def test_dense_equals_sparse_c0_and_shared():
+    d = X.make_inputs("c0")
+    assert np.array_equal(_run(d)["out"], _run(d, fn=O.moe_dense))
+    shape = X.Shape(M=3, H=256, E=4, I=128, top_k=2, shared_I=128)
+    d = X.make_inputs(shape, "normal", 9)
+    assert np.array_equal(_run(d)["out"], _run(d, fn=O.moe_dense))
+
+
+def test_zero_input_and_no_active_expert():
+    d = X.make_inputs("c0")
+    out = _run(d, x_bits=np.zeros_like(d["x"]))["out"]
+    assert np.all(F.bf16_decode(out) == 0)
+    out = _run(d, logits=np.full_like(d["logits"], -np.inf))["out"]
+    assert np.all(F.bf16_decode(out) == 0)
+
+
+def test_token_permutation_equivariance():
+    d = X.make_inputs("c0")
+    p = np.array([2, 0, 3, 1])
+    a = _run(d)["out"]
+    b = _run(d, x_bits=d["x"][p], logits=d["logits"][p])["out"]
+    assert np.array_equal(a[p], b)
+
+
+def test_expert_relabelling_invariance():
+    d = X.make_inputs("c0")
+    assert len(np.unique(d["logits"])) == d["logits"].size  # tie-free
+    p = np.random.default_rng(4).permutation(16)  # new expert e holds old p[e]
+    a = _run(d)["out"]
+    b = _run(d, logits=d["logits"][:, p], w13=d["w13"][p], s13=d["s13"][p], w2=d["w2"][p],
+             s2=d["s2"][p])["out"]
+    assert np.array_equal(a, b)
+
+
+def test_scaling_linearity():
+    d = X.make_inputs("c0")
+    a = F.bf16_decode(_run(d, scaling=2.5)["out"])
+    b = F.bf16_decode(_run(d, scaling=5.0)["out"])
+    assert np.array_equal(2 * a, b)
+
+
+def test_intermediate_layout():
+    d = X.make_inputs("c0")
+    r = _run(d)
+    s = d["shape"]
+    n = s.M * s.top_k
+    assert r["midq"].shape == (n, s.I) and r["mids"].shape == (n, s.I // 128)
+    assert r["y"].shape == (n, s.H) and r["xq"].shape == (s.M, s.H) and r["xs"].shape == (s.M, s.H // 32)
+    # midq rows are in sorted order: row r belongs to entry sorted_entry[r]
+    ids = r["ids"].ravel()
+    for e in range(s.E):
+        assert np.all(ids[r["sorted_entry"][r["offset"][e]:r["offset"][e + 1]]] == e)
+
+
+def test_page_mid_block_arithmetic():
+    """288 blocks at TP4 with 8 rows x 9 slots; ~19 / ~38 KB of FP8 + scales;
+    fp32 mid four times the FP8 bytes (tests/golden/mid_blocks.txt)."""
+    rows = [l.split() for l in open(os.path.join(HERE, "golden", "mid_blocks.txt"))
+            if l.strip() and not l.startswith("#")]
+    for rws, slots, I, blocks, kb_fp8, kb_f32 in [[int(v) for v in r] for r in rows]:
+        h = np.random.default_rng(0).normal(size=(rws * slots, I)).astype(np.float32)
+        q, s = O.quantize_mid(h)
+        assert s.size == blocks
+        nbytes = q.size * q.itemsize + s.size * s.itemsize
+        assert round(nbytes / 1000) == kb_fp8
+        assert round(h.size * 4 / 1000) == kb_f32
