@@ -1,0 +1,156 @@
+/*
+ * qmoe.h - C ABI of one tensor-parallel rank's routed-MoE layer call on an
+ * MI355X (gfx950) GPU.
+ *
+ * The call (pages: "IQ2R: load GLM-5.3 packed MoE checkpoints with TP
+ * slicing" and "[HIP] IQ2R: GLM-5.3 packed MoE path for TP4/TP8 on gfx950",
+ * Summary sections; "glm53: FP8 mid hand-off, early split rows, per-row
+ * up/gate jobs, ...", Modifications table) computes, for M tokens:
+ *
+ *   1. top-k routing of fp32 router logits (ties go to the lower expert id),
+ *      weights = sigmoid scores renormalized over the k slots x routed scaling
+ *   2. a stable sort of the M*k (token, slot) entries by expert
+ *   3. x (bf16) -> MXFP4 once per token (E2M1, one E8M0 scale per 32)
+ *   4. gate/up GEMM on MXFP4 expert weights, h = SiLU(gate) * up
+ *   5. h -> FP8 E4M3 once per 128-element block, with an fp32 scale
+ *   6. down GEMM on MXFP4 expert weights
+ *   7. out (bf16) = sum over slots of weight * down output (+ shared expert)
+ *   8. optional block-FP8 shared expert (128x128 weight scales), weight 1
+ *
+ * Conventions for every entry point:
+ *   - All tensors are dense, row-major, 16-byte aligned device pointers on
+ *     the plan's device. The caller owns every buffer (inputs, weights,
+ *     output, workspace); the library never allocates device memory and
+ *     never synchronizes a stream. `stream` is a hipStream_t (NULL = the
+ *     default stream). All GPU work of a call is enqueued on that stream in
+ *     order, so a call may be captured into a HIP graph.
+ *   - Arguments are validated before anything is enqueued; on an error
+ *     nothing is launched and nothing is written.
+ *   - MXFP4 bytes hold two E2M1 codes, element 2i in the low nibble.
+ *   - One plan, with its workspace, serves one stream at a time.
+ */
+#ifndef QMOE_H
+#define QMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,  /* null / misaligned pointer, bad size, k > E, M > plan maximum */
+  MOE_ERR_UNSUPPORTED = 2,  /* shape outside what the kernels handle (see moe_plan_create) */
+  MOE_ERR_WORKSPACE = 3,    /* workspace missing, too small or misaligned */
+  MOE_ERR_DEVICE = 4,       /* no usable gfx950 device, or pointers on another device */
+  MOE_ERR_HIP = 5           /* the HIP runtime reported an error while enqueueing */
+} moe_status;
+
+/* One rank's shape. M is the largest token count a call on this plan may use. */
+typedef struct {
+  int64_t M;              /* max tokens per call, >= 0 */
+  int64_t H;              /* hidden size, multiple of 512 */
+  int64_t E;              /* routed experts, 1..1024 */
+  int64_t I;              /* intermediate size per rank: 128, 256, 384 or 512 */
+  int64_t top_k;          /* 1..min(E, 16) */
+  float routed_scaling;   /* routing weights of a token sum to this (finite, > 0) */
+  int64_t shared_I;       /* shared-expert intermediate size (multiple of 128), 0 = none */
+} moe_shape;
+
+typedef struct moe_plan moe_plan; /* opaque; host memory only */
+
+/* Byte offsets into the workspace of the intermediates a call leaves behind
+ * (valid until the next call on the plan). Layouts, with n = M * top_k:
+ *   topk_ids     int32 [M, k]       expert of slot j of token t
+ *   topk_w       fp32  [M, k]       routing weight (includes routed_scaling)
+ *   count        int32 [E]          entries per expert
+ *   offset       int32 [E + 1]      exclusive prefix of count
+ *   sorted_entry int32 [n]          entries t*k+j grouped by expert, t ascending
+ *   xq           u8    [M, H/2]     x as E2M1 codes (MXFP4)
+ *   xs           u8    [M, H/32]    x's E8M0 scales
+ *   midq         u8    [n, I]       E4M3 mid, rows in sorted order
+ *   mids         fp32  [n, I/128]   mid block scales, rows in sorted order
+ *   y            fp32  [n, H]       unweighted down output, row = entry t*k+j
+ *   sh_xq/sh_xs  u8 [M, H] / fp32 [M, H/128]      shared expert x in E4M3
+ *   sh_hq/sh_hs  u8 [M, Is] / fp32 [M, Is/128]    shared expert mid in E4M3
+ *   sh_y         fp32  [M, H]       shared expert output
+ * Offsets of absent parts (no shared expert) are 0. */
+typedef struct {
+  size_t total_bytes;
+  size_t topk_ids, topk_w, count, offset, sorted_entry;
+  size_t xq, xs, midq, mids, y;
+  size_t sh_xq, sh_xs, sh_hq, sh_hs, sh_y;
+} moe_ws_layout;
+
+/* Create a host-side plan for `shape` on the current HIP device.
+ * Returns MOE_ERR_INVALID_ARG for null arguments, negative or zero sizes,
+ * top_k > E or a non-positive routed_scaling; MOE_ERR_UNSUPPORTED for
+ * H % 512 != 0, I not in {128, 256, 384, 512}, E > 1024, top_k > 16,
+ * shared_I % 128 != 0 or shared_I > 2048, M > 2^20; MOE_ERR_DEVICE when the
+ * current HIP device cannot be queried or is not a gfx950. Creating a plan
+ * enqueues no GPU work. */
+moe_status moe_plan_create(const moe_shape* shape, moe_plan** out);
+
+/* Workspace bytes a plan of this shape needs, computed on the host alone
+ * (no device is queried). Same validation as moe_plan_create. */
+moe_status moe_shape_workspace_bytes(const moe_shape* shape, size_t* bytes);
+
+/* Free the plan (not the caller's workspace). NULL is accepted. */
+void moe_plan_destroy(moe_plan* plan);
+
+/* Bytes of device workspace the plan needs (multiple of 256). */
+size_t moe_plan_workspace_bytes(const moe_plan* plan);
+
+/* Offsets of the intermediates inside the workspace. */
+moe_status moe_plan_layout(const moe_plan* plan, moe_ws_layout* out);
+
+/* Bind a caller-owned device workspace (256-byte aligned, at least
+ * moe_plan_workspace_bytes) to the plan and enqueue on `stream` the one-time
+ * initialisation of its synchronisation counters. The workspace must not be
+ * written by the caller afterwards. MOE_ERR_WORKSPACE if it is too small or
+ * misaligned, MOE_ERR_DEVICE if it lives on another device. */
+moe_status moe_plan_set_workspace(moe_plan* plan, void* workspace, size_t bytes, void* stream);
+
+/* Bind the block-FP8 shared expert (required iff shape.shared_I > 0):
+ *   ws13 u8 (E4M3) [2*Is, H]  rows [0, Is) gate, [Is, 2*Is) up
+ *   ss13 fp32 [2*Is/128, H/128]  one scale per 128x128 block
+ *   ws2  u8 (E4M3) [H, Is];  ss2 fp32 [H/128, Is/128]
+ * Pointers are kept, not copied; they must stay valid while the plan is used. */
+moe_status moe_plan_set_shared(moe_plan* plan, const void* ws13, const float* ss13,
+                               const void* ws2, const float* ss2);
+
+/* The routed-MoE call on M tokens (0 <= M <= shape.M; M = 0 enqueues nothing):
+ *   x      bf16 [M, H]
+ *   logits fp32 [M, E]     (finite or -inf)
+ *   w13    u8 MXFP4 [E, 2I, H/2]   rows [0, I) gate, [I, 2I) up, along H
+ *   s13    u8 E8M0  [E, 2I, H/32]
+ *   w2     u8 MXFP4 [E, H, I/2]    along I
+ *   s2     u8 E8M0  [E, H, I/32]
+ *   out    bf16 [M, H]  fully overwritten; must not alias any input
+ * Returns after enqueueing; faults inside kernels surface at the caller's
+ * next synchronisation. MOE_ERR_WORKSPACE if no workspace is bound,
+ * MOE_ERR_INVALID_ARG if the shared expert is required but not bound. */
+moe_status moe_forward(moe_plan* plan, int64_t M, const void* x, const float* logits,
+                       const void* w13, const void* s13, const void* w2, const void* s2,
+                       void* out, void* stream);
+
+/* Profiling aid: when `events` is non-NULL, moe_forward records
+ * events[i] (hipEvent_t) on the stream before stage i and events[n_stages]
+ * after the last stage, so that each stage's duration can be read with
+ * hipEventElapsedTime. `n` must be moe_stage_count() + 1. NULL disables. */
+moe_status moe_plan_set_stage_events(moe_plan* plan, void* const* events, int n);
+
+/* Number and names of the launch stages of a call (for the events above). */
+int moe_stage_count(void);
+const char* moe_stage_name(int i);
+
+/* Static text for a status code. */
+const char* moe_status_str(moe_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMOE_H */

@@ -1,0 +1,214 @@
+"""Python binding of libqmoe.so (ctypes): argument marshalling only.
+
+Every step of the routed-MoE call runs in the library's HIP kernels; torch is
+used for device memory and the current stream. The names follow the C ABI in
+include/qmoe.h. Importing this module does not load the library; the first
+use does, and fails loudly when it has not been built.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libqmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE, MOE_ERR_HIP = range(6)
+
+
+class moe_shape(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_int64), ("H", ctypes.c_int64), ("E", ctypes.c_int64), ("I", ctypes.c_int64),
+                ("top_k", ctypes.c_int64), ("routed_scaling", ctypes.c_float), ("shared_I", ctypes.c_int64)]
+
+
+LAYOUT_FIELDS = ["total_bytes", "topk_ids", "topk_w", "count", "offset", "sorted_entry", "xq", "xs", "midq",
+                 "mids", "y", "sh_xq", "sh_xs", "sh_hq", "sh_hs", "sh_y"]
+
+
+class moe_ws_layout(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_size_t) for f in LAYOUT_FIELDS]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)} (status {status})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (built in-tree by quantized_moe_expert_route_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m quantized_moe_expert_route_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, st = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.moe_status_str.restype = ctypes.c_char_p
+    L.moe_status_str.argtypes = [st]
+    L.moe_stage_count.restype = ctypes.c_int
+    L.moe_stage_count.argtypes = []
+    L.moe_stage_name.restype = ctypes.c_char_p
+    L.moe_stage_name.argtypes = [ctypes.c_int]
+    L.moe_shape_workspace_bytes.restype = st
+    L.moe_shape_workspace_bytes.argtypes = [ctypes.POINTER(moe_shape), ctypes.POINTER(ctypes.c_size_t)]
+    L.moe_plan_create.restype = st
+    L.moe_plan_create.argtypes = [ctypes.POINTER(moe_shape), ctypes.POINTER(vp)]
+    L.moe_plan_destroy.restype = None
+    L.moe_plan_destroy.argtypes = [vp]
+    L.moe_plan_workspace_bytes.restype = ctypes.c_size_t
+    L.moe_plan_workspace_bytes.argtypes = [vp]
+    L.moe_plan_layout.restype = st
+    L.moe_plan_layout.argtypes = [vp, ctypes.POINTER(moe_ws_layout)]
+    L.moe_plan_set_workspace.restype = st
+    L.moe_plan_set_workspace.argtypes = [vp, vp, ctypes.c_size_t, vp]
+    L.moe_plan_set_shared.restype = st
+    L.moe_plan_set_shared.argtypes = [vp, vp, vp, vp, vp]
+    L.moe_plan_set_stage_events.restype = st
+    L.moe_plan_set_stage_events.argtypes = [vp, ctypes.POINTER(vp), ctypes.c_int]
+    L.moe_forward.restype = st
+    L.moe_forward.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp]
+    _lib = L
+    return L
+
+
+def status_str(status: int) -> str:
+    return lib().moe_status_str(status).decode()
+
+
+def stage_names():
+    L = lib()
+    return [L.moe_stage_name(i).decode() for i in range(L.moe_stage_count())]
+
+
+def shape_workspace_bytes(M, H, E, I, top_k, routed_scaling=2.5, shared_I=0) -> int:
+    s = moe_shape(M, H, E, I, top_k, routed_scaling, shared_I)
+    out = ctypes.c_size_t(0)
+    st = lib().moe_shape_workspace_bytes(ctypes.byref(s), ctypes.byref(out))
+    if st != MOE_OK:
+        raise MoeError(st, "moe_shape_workspace_bytes")
+    return out.value
+
+
+def _ptr(t) -> int:
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+class Plan:
+    """A plan for one shape, owning a device workspace allocated through torch."""
+
+    def __init__(self, M: int, H: int, E: int, I: int, top_k: int, routed_scaling: float = 2.5,
+                 shared_I: int = 0, device=None):
+        import torch
+
+        self.shape = moe_shape(M, H, E, I, top_k, routed_scaling, shared_I)
+        self._h = ctypes.c_void_p()
+        st = lib().moe_plan_create(ctypes.byref(self.shape), ctypes.byref(self._h))
+        if st != MOE_OK:
+            raise MoeError(st, "moe_plan_create")
+        self.device = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+        nbytes = lib().moe_plan_workspace_bytes(self._h)
+        self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        st = lib().moe_plan_set_workspace(self._h, _ptr(self.workspace), self.workspace.numel(), _stream(None))
+        if st != MOE_OK:
+            raise MoeError(st, "moe_plan_set_workspace")
+        self._shared = None
+        self._events = None
+
+    def layout(self) -> Dict[str, int]:
+        L = moe_ws_layout()
+        st = lib().moe_plan_layout(self._h, ctypes.byref(L))
+        if st != MOE_OK:
+            raise MoeError(st, "moe_plan_layout")
+        return {f: getattr(L, f) for f in LAYOUT_FIELDS}
+
+    def set_shared(self, ws13, ss13, ws2, ss2):
+        self._shared = (ws13, ss13, ws2, ss2)  # keep the tensors alive
+        st = lib().moe_plan_set_shared(self._h, _ptr(ws13), _ptr(ss13), _ptr(ws2), _ptr(ss2))
+        if st != MOE_OK:
+            raise MoeError(st, "moe_plan_set_shared")
+
+    def set_stage_events(self, events):
+        """events: list of raw hipEvent_t handles (ints), len = stages + 1; None clears."""
+        if events is None:
+            st = lib().moe_plan_set_stage_events(self._h, None, 0)
+            self._events = None
+        else:
+            arr = (ctypes.c_void_p * len(events))(*events)
+            st = lib().moe_plan_set_stage_events(self._h, arr, len(events))
+            self._events = arr
+        if st != MOE_OK:
+            raise MoeError(st, "moe_plan_set_stage_events")
+
+    def forward(self, x, logits, w13, s13, w2, s2, out, M: Optional[int] = None, stream=None):
+        """Enqueue the call on `stream` (default: torch's current stream)."""
+        if M is None:
+            M = x.shape[0]
+        st = lib().moe_forward(self._h, int(M), _ptr(x), _ptr(logits), _ptr(w13), _ptr(s13), _ptr(w2),
+                               _ptr(s2), _ptr(out), _stream(stream))
+        if st != MOE_OK:
+            raise MoeError(st, "moe_forward")
+        return out
+
+    def view(self, name: str, dtype, shape):
+        """A torch view of an intermediate inside the workspace (see moe_ws_layout)."""
+        import math
+
+        import torch
+
+        off = self.layout()[name]
+        itemsize = torch.empty(0, dtype=dtype).element_size()
+        n = math.prod(shape)
+        return self.workspace[off:off + n * itemsize].view(dtype).view(*shape)
+
+    def close(self):
+        if self._h:
+            lib().moe_plan_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class HipEvents:
+    """A few raw hipEvent_t handles from libamdhip64 (for per-stage timing)."""
+
+    def __init__(self, n: int):
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self._hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.handles = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            if self._hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.handles.append(h.value)
+
+    def elapsed_ms(self, i: int, j: int) -> float:
+        self._hip.hipEventSynchronize(self.handles[j])
+        ms = ctypes.c_float(0)
+        if self._hip.hipEventElapsedTime(ctypes.byref(ms), self.handles[i], self.handles[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def close(self):
+        for h in self.handles:
+            self._hip.hipEventDestroy(h)
+        self.handles = []

@@ -1,0 +1,256 @@
+// C ABI of the routed-MoE call: validation, workspace layout and the launch
+// sequence. Nothing here allocates device memory or synchronizes a stream.
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+
+#include "internal.h"
+
+using namespace qmoe;
+
+namespace {
+
+const char* kStageNames[] = {"route", "align", "gate_up", "act_quant", "down", "shared", "combine"};
+constexpr int kStages = 7;
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+moe_status check_shape(const moe_shape* s) {
+  if (!s) return MOE_ERR_INVALID_ARG;
+  if (s->M < 0 || s->H <= 0 || s->E <= 0 || s->I <= 0 || s->top_k <= 0 || s->shared_I < 0)
+    return MOE_ERR_INVALID_ARG;
+  if (!(s->routed_scaling > 0.f) || s->routed_scaling > 3.0e38f) return MOE_ERR_INVALID_ARG;
+  if (s->top_k > s->E) return MOE_ERR_INVALID_ARG;
+  if (s->H % 512 != 0 || s->I % 128 != 0 || s->I > 512 || s->E > 1024 || s->top_k > 16 ||
+      s->shared_I % 128 != 0 || s->shared_I > 2048)
+    return MOE_ERR_UNSUPPORTED;
+  if (s->M > (int64_t)1 << 20 || s->H > 65536) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+struct Layout {
+  moe_ws_layout L;
+  Internal X;
+  int64_t t16, words;
+};
+
+Layout make_layout(const moe_shape& s) {
+  Layout r;
+  memset(&r, 0, sizeof(r));
+  const size_t M = (size_t)s.M, H = (size_t)s.H, E = (size_t)s.E, I = (size_t)s.I, k = (size_t)s.top_k;
+  const size_t Is = (size_t)s.shared_I;
+  const size_t n = M * k;
+  r.t16 = (int64_t)((n + std::min(E, n) * (kTileRows - 1) + kTileRows - 1) / kTileRows);
+  r.words = (int64_t)((M + 31) / 32);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    off = align256(off);
+    size_t at = off;
+    off += bytes;
+    return at;
+  };
+  r.L.topk_ids = take(4 * n);
+  r.L.topk_w = take(4 * n);
+  r.L.count = take(4 * E);
+  r.L.offset = take(4 * (E + 1));
+  r.L.sorted_entry = take(4 * n);
+  r.X.tiles = take(16 * (size_t)r.t16);
+  r.X.meta = take(256);
+  r.X.bitmap = take(4 * E * (size_t)r.words);
+  r.X.sync_begin = r.X.bitmap;
+  r.X.sync_bytes = align256(4 * E * (size_t)r.words);
+  r.X.pre = take(4 * E * (size_t)r.words);
+  r.L.xq = take(M * H / 2);
+  r.L.xs = take(M * H / 32);
+  r.X.h = take(4 * n * I);
+  r.L.midq = take(n * I);
+  r.L.mids = take(4 * n * (I / 128));
+  r.L.y = take(4 * n * H);
+  if (Is > 0) {
+    r.L.sh_xq = take(M * H);
+    r.L.sh_xs = take(4 * M * (H / 128));
+    r.X.sh_h = take(4 * M * Is);
+    r.L.sh_hq = take(M * Is);
+    r.L.sh_hs = take(4 * M * (Is / 128));
+    r.L.sh_y = take(4 * M * H);
+  }
+  r.L.total_bytes = align256(off);
+  return r;
+}
+
+// Device that owns a device pointer, or -1.
+int ptr_device(const void* p) {
+  hipPointerAttribute_t a;
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return -1;
+  }
+  if (a.type != hipMemoryTypeDevice && a.type != hipMemoryTypeManaged) return -1;
+  return a.device;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = true;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) { ok = false; return; }
+    if (prev != dev && hipSetDevice(dev) != hipSuccess) ok = false;
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(moe_status st) {
+  switch (st) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape";
+    case MOE_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case MOE_ERR_DEVICE: return "no usable gfx950 device, or pointer on another device";
+    case MOE_ERR_HIP: return "HIP runtime error while enqueueing";
+  }
+  return "unknown status";
+}
+
+int moe_stage_count(void) { return kStages; }
+
+const char* moe_stage_name(int i) { return (i >= 0 && i < kStages) ? kStageNames[i] : nullptr; }
+
+moe_status moe_shape_workspace_bytes(const moe_shape* shape, size_t* bytes) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  *bytes = make_layout(*shape).L.total_bytes;
+  return MOE_OK;
+}
+
+moe_status moe_plan_create(const moe_shape* shape, moe_plan** out) {
+  if (!out) return MOE_ERR_INVALID_ARG;
+  *out = nullptr;
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return MOE_ERR_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_ERR_DEVICE;
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return MOE_ERR_DEVICE;
+  moe_plan* p = new (std::nothrow) moe_plan;
+  if (!p) return MOE_ERR_INVALID_ARG;
+  memset(p, 0, sizeof(*p));
+  p->s = *shape;
+  p->device = dev;
+  p->n_max = shape->M * shape->top_k;
+  Layout lay = make_layout(*shape);
+  p->L = lay.L;
+  p->X = lay.X;
+  p->t16_max = lay.t16;
+  p->words = lay.words;
+  *out = p;
+  return MOE_OK;
+}
+
+void moe_plan_destroy(moe_plan* plan) { delete plan; }
+
+size_t moe_plan_workspace_bytes(const moe_plan* plan) { return plan ? plan->L.total_bytes : 0; }
+
+moe_status moe_plan_layout(const moe_plan* plan, moe_ws_layout* out) {
+  if (!plan || !out) return MOE_ERR_INVALID_ARG;
+  *out = plan->L;
+  return MOE_OK;
+}
+
+moe_status moe_plan_set_workspace(moe_plan* plan, void* workspace, size_t bytes, void* stream) {
+  if (!plan) return MOE_ERR_INVALID_ARG;
+  if (!workspace || ((uintptr_t)workspace & 255u) != 0 || bytes < plan->L.total_bytes) return MOE_ERR_WORKSPACE;
+  if (ptr_device(workspace) != plan->device) return MOE_ERR_DEVICE;
+  DeviceGuard guard(plan->device);
+  if (!guard.ok) return MOE_ERR_DEVICE;
+  plan->ws = reinterpret_cast<uint8_t*>(workspace);
+  plan->ws_bytes = bytes;
+  if (launch_zero(plan->ws + plan->X.sync_begin, plan->X.sync_bytes, (hipStream_t)stream) != hipSuccess) {
+    plan->ws = nullptr;
+    return MOE_ERR_HIP;
+  }
+  return MOE_OK;
+}
+
+moe_status moe_plan_set_shared(moe_plan* plan, const void* ws13, const float* ss13, const void* ws2,
+                               const float* ss2) {
+  if (!plan) return MOE_ERR_INVALID_ARG;
+  if (plan->s.shared_I == 0) return MOE_ERR_INVALID_ARG;
+  const void* ptrs[4] = {ws13, ss13, ws2, ss2};
+  for (const void* q : ptrs) {
+    if (!q || !aligned16(q)) return MOE_ERR_INVALID_ARG;
+    if (ptr_device(q) != plan->device) return MOE_ERR_DEVICE;
+  }
+  plan->ws13 = ws13;
+  plan->ss13 = ss13;
+  plan->ws2 = ws2;
+  plan->ss2 = ss2;
+  return MOE_OK;
+}
+
+moe_status moe_plan_set_stage_events(moe_plan* plan, void* const* events, int n) {
+  if (!plan) return MOE_ERR_INVALID_ARG;
+  if (!events) {
+    plan->n_events = 0;
+    return MOE_OK;
+  }
+  if (n != kStages + 1) return MOE_ERR_INVALID_ARG;
+  for (int i = 0; i < n; ++i) {
+    if (!events[i]) return MOE_ERR_INVALID_ARG;
+    plan->events[i] = (hipEvent_t)events[i];
+  }
+  plan->n_events = n;
+  return MOE_OK;
+}
+
+moe_status moe_forward(moe_plan* plan, int64_t M, const void* x, const float* logits, const void* w13,
+                       const void* s13, const void* w2, const void* s2, void* out, void* stream) {
+  if (!plan) return MOE_ERR_INVALID_ARG;
+  if (M < 0 || M > plan->s.M) return MOE_ERR_INVALID_ARG;
+  if (!plan->ws) return MOE_ERR_WORKSPACE;
+  if (plan->s.shared_I > 0 && !plan->ws13) return MOE_ERR_INVALID_ARG;
+  if (M == 0) return MOE_OK;
+  const void* ptrs[7] = {x, logits, w13, s13, w2, s2, out};
+  for (const void* q : ptrs)
+    if (!q || !aligned16(q)) return MOE_ERR_INVALID_ARG;
+  for (const void* q : ptrs)
+    if (ptr_device(q) != plan->device) return MOE_ERR_DEVICE;
+  const size_t H = (size_t)plan->s.H, E = (size_t)plan->s.E;
+  const size_t out_bytes = (size_t)M * H * 2;
+  if (overlaps(out, out_bytes, x, (size_t)M * H * 2) || overlaps(out, out_bytes, logits, (size_t)M * E * 4) ||
+      overlaps(out, out_bytes, plan->ws, plan->L.total_bytes))
+    return MOE_ERR_INVALID_ARG;
+
+  DeviceGuard guard(plan->device);
+  if (!guard.ok) return MOE_ERR_DEVICE;
+  CallArgs a{M, x, logits, w13, s13, w2, s2, out, (hipStream_t)stream};
+  hipError_t (*stages[kStages])(const moe_plan*, const CallArgs&) = {
+      launch_route, launch_align, launch_gate_up, launch_act_quant, launch_down, launch_shared, launch_combine};
+  for (int i = 0; i < kStages; ++i) {
+    if (plan->n_events && hipEventRecord(plan->events[i], a.stream) != hipSuccess) return MOE_ERR_HIP;
+    if (stages[i](plan, a) != hipSuccess) return MOE_ERR_HIP;
+  }
+  if (plan->n_events && hipEventRecord(plan->events[kStages], a.stream) != hipSuccess) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,158 @@
+// Device helpers shared by the routed-MoE kernels (gfx950, wave64).
+//
+// Format encoders are written from the public definitions: OCP Microscaling
+// v1.0 (E2M1 elements, E8M0 scales, scale exponent floor(log2 amax) - 2) and
+// the OCP 8-bit float spec (E4M3FN: bias 7, max 448, no infinities).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmoe {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// ----------------------------------------------------------------- memory
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ uint32_t ld4(const void* p) { return *reinterpret_cast<const uint32_t*>(p); }
+
+// ----------------------------------------------------------------- wave reductions
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    uint32_t lo = __shfl_xor((uint32_t)v, o, kWave);
+    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, kWave);
+    uint64_t w = ((uint64_t)hi << 32) | lo;
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+// Order-preserving unsigned key of a float (-0 counts as +0; NaN unsupported).
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __uint_as_float(u);
+}
+
+// ----------------------------------------------------------------- E2M1 / MX
+// Nearest E2M1 magnitude code of |v| (|v| < 8 here), ties to the even code,
+// saturating at 6: the decision points are the midpoints of the value grid
+// 0, .5, 1, 1.5, 2, 3, 4, 6.
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  float a = fabsf(v);
+  uint32_t c = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+             : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.0f ? 6u : 7u;
+  return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+// E8M0 scale byte of a 32-block from the largest |bf16| bit pattern of the block.
+__device__ __forceinline__ uint32_t mx_scale_code(uint32_t amax_bits16) {
+  if (amax_bits16 == 0) return 0;
+  int ex = (int)(amax_bits16 >> 7);
+  int fl;  // floor(log2 amax)
+  if (ex == 0) fl = -133 + (31 - __clz(amax_bits16 & 0x7F));
+  else fl = ex - 127;
+  int c = fl - 2 + 127;
+  return (uint32_t)(c < 0 ? 0 : (c > 254 ? 254 : c));
+}
+
+// ----------------------------------------------------------------- E4M3FN
+// Round |v| to the nearest E4M3 value, ties to the even code, saturating to
+// 448; sign copied from v. Exact: the scalings by powers of two are exact and
+// rintf rounds half to even.
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+  uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  float a = fabsf(v);
+  uint32_t c;
+  if (!(a < 448.0f)) {
+    c = 0x7Eu;
+  } else if (a < 0.015625f) {  // below 2^-6: multiples of 2^-9
+    c = (uint32_t)rintf(a * 512.0f);
+  } else {
+    int e = (int)((__float_as_uint(a) >> 23) & 255u) - 127;  // -6..8
+    uint32_t q = (uint32_t)rintf(ldexpf(a, 3 - e));          // 8..16
+    c = ((uint32_t)(e + 7) << 3) + (q - 8u);
+  }
+  return c | sign;
+}
+
+// E4M3 code -> bf16 bits (every E4M3 value is exact in bf16).
+__host__ __device__ constexpr uint16_t e4m3_to_bf16_bits(uint32_t c) {
+  uint32_t s = (c & 0x80u) << 8;
+  uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  if ((c & 0x7Fu) == 0x7Fu) return (uint16_t)(s | 0x7FC0u);  // NaN
+  if (e == 0) {
+    if (m == 0) return (uint16_t)s;
+    // m * 2^-9: normalise the 3-bit mantissa
+    int p = m >= 4 ? 2 : (m >= 2 ? 1 : 0);
+    uint32_t be = (uint32_t)(p - 9 + 127);
+    uint32_t bm = ((m << (7 - p)) & 0x7Fu);
+    return (uint16_t)(s | (be << 7) | bm);
+  }
+  return (uint16_t)(s | ((e - 7u + 127u) << 7) | (m << 4));
+}
+
+// ----------------------------------------------------------------- bf16
+// Correctly rounded double -> bf16 (nearest, ties to even): truncate to
+// binary32, make the result sticky-odd when bits were dropped (round to odd
+// keeps enough information: 24 bits > 8 + 2), then round binary32 to bf16.
+__device__ __forceinline__ uint32_t bf16_rne_from_double(double v) {
+  float f = __double2float_rz(v);
+  uint32_t u = __float_as_uint(f);
+  if ((double)f != v) u |= 1u;
+  u = u + 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// ----------------------------------------------------------------- MFMA
+// v_mfma_scale_f32_16x16x128_f8f6f4 with both operands E2M1. Lane l holds row
+// (A) / column (B) l%16 and the 32 consecutive K elements 32*(l/16).. of that
+// row in 16 bytes; its E8M0 scale byte covers exactly those 32 elements.
+// D: lane l, element i = D[4*(l/16)+i][l%16].
+__device__ __forceinline__ v4f mfma_fp4(uint4 a, uint4 b, v4f c, uint32_t sa, uint32_t sb) {
+  v8i A = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  v8i B = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, c, 4, 4, 0, (int)sa, 0, (int)sb);
+}
+
+// v_mfma_f32_16x16x32_bf16: lane l holds row/column l%16 and K elements
+// 8*(l/16)..+8. Products are exact and the sum is exact whenever it is
+// representable in binary32.
+__device__ __forceinline__ v4f mfma_bf16(v8s a, v8s b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Two E2M1 codes (one byte, selected by SEL) -> two bf16 multiplied by scale.
+template <int SEL>
+__device__ __forceinline__ uint32_t cvt_fp4x2_bf16(uint32_t src, float scale) {
+  bf16x2 r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, scale, SEL);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ float e8m0_to_float(uint32_t s) {
+  return s == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(s << 23);
+}
+
+// SiLU(g) * u in float64, one rounding to binary32.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  double gd = (double)g;
+  return (float)((gd / (1.0 + exp(-gd))) * (double)u);
+}
+
+}  // namespace qmoe

@@ -1,0 +1,72 @@
+// Host-side plan and the launch interface between the C ABI (api.hip) and
+// the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "qmoe.h"
+
+namespace qmoe {
+
+constexpr int kTileRows = 16;  // sorted rows per tile of the token-dimension tiling
+
+// Workspace regions beyond the public layout.
+struct Internal {
+  size_t tiles;    // int4 [T16]: {expert, row_begin, row_end, 0}
+  size_t meta;     // int32 [64]: meta[0] = number of tiles
+  size_t bitmap;   // uint32 [E, ceil(M/32)]: bit t of row e = token t picked e; zero between calls
+  size_t pre;      // int32 [E, ceil(M/32)]: entries of row e before word w
+  size_t h;        // fp32 [n, I]: SiLU(gate)*up, rows in sorted order
+  size_t sh_h;     // fp32 [M, Is]
+  size_t sync_begin, sync_bytes;  // region zeroed once when the workspace is bound
+};
+
+}  // namespace qmoe
+
+struct moe_plan {
+  moe_shape s;
+  int device;
+  int64_t n_max;   // M * top_k
+  int64_t t16_max; // upper bound on tiles of 16 sorted rows
+  int64_t words;   // ceil(M / 32)
+  moe_ws_layout L;
+  qmoe::Internal X;
+  uint8_t* ws;
+  size_t ws_bytes;
+  const void* ws13;
+  const float* ss13;
+  const void* ws2;
+  const float* ss2;
+  hipEvent_t events[16];
+  int n_events;
+};
+
+namespace qmoe {
+
+struct CallArgs {
+  int64_t M;
+  const void* x;
+  const float* logits;
+  const void* w13;
+  const void* s13;
+  const void* w2;
+  const void* s2;
+  void* out;
+  hipStream_t stream;
+};
+
+template <typename T>
+inline T* wsp(const moe_plan* p, size_t off) { return reinterpret_cast<T*>(p->ws + off); }
+
+hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t s);
+hipError_t launch_route(const moe_plan* p, const CallArgs& a);
+hipError_t launch_align(const moe_plan* p, const CallArgs& a);
+hipError_t launch_gate_up(const moe_plan* p, const CallArgs& a);
+hipError_t launch_act_quant(const moe_plan* p, const CallArgs& a);
+hipError_t launch_down(const moe_plan* p, const CallArgs& a);
+hipError_t launch_shared(const moe_plan* p, const CallArgs& a);
+hipError_t launch_combine(const moe_plan* p, const CallArgs& a);
+
+}  // namespace qmoe

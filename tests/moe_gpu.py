@@ -1,0 +1,110 @@
+"""Helpers of the GPU tests: run the HIP path through the C ABI binding and
+read back every intermediate it leaves in the workspace; compare with the
+oracle stage by stage."""
+
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import formats as F
+from oracle import moe as O
+
+
+def upload(d):
+    import torch
+
+    dev = torch.device("cuda", 0)
+    g = {k: torch.from_numpy(np.ascontiguousarray(d[k])).to(dev)
+         for k in ("logits", "w13", "s13", "w2", "s2") if k in d}
+    g["x"] = torch.from_numpy(np.ascontiguousarray(d["x"]).view(np.int16)).to(dev)
+    if d["shape"].shared_I:
+        for k in ("ws13", "ss13", "ws2", "ss2"):
+            g[k] = torch.from_numpy(np.ascontiguousarray(d[k])).to(dev)
+    return g
+
+
+def make_plan(shape, M_max=None):
+    from quantized_moe_expert_route_amd.binding import Plan
+
+    s = shape
+    return Plan(s.M if M_max is None else M_max, s.H, s.E, s.I, s.top_k, s.routed_scaling, s.shared_I)
+
+
+def run(d, plan=None, g=None, M=None):
+    """One call on GPU; returns (out bits [M, H] uint16, intermediates dict of numpy)."""
+    import torch
+
+    s = d["shape"]
+    M = s.M if M is None else M
+    if g is None:
+        g = upload(d)
+    if plan is None:
+        plan = make_plan(s)
+        if s.shared_I:
+            plan.set_shared(g["ws13"], g["ss13"], g["ws2"], g["ss2"])
+    out = torch.full((max(M, 1), s.H), -1, dtype=torch.int16, device=g["x"].device)
+    plan.forward(g["x"], g["logits"], g["w13"], g["s13"], g["w2"], g["s2"], out, M=M)
+    torch.cuda.synchronize()
+    return out[:M].cpu().numpy().view(np.uint16), read_intermediates(plan, s, M)
+
+
+def read_intermediates(plan, s, M):
+    import torch
+
+    k, n, I, H, E = s.top_k, M * s.top_k, s.I, s.H, s.E
+    v = plan.view
+    r = {
+        "ids": v("topk_ids", torch.int32, (M, k)),
+        "w": v("topk_w", torch.float32, (M, k)),
+        "count": v("count", torch.int32, (E,)),
+        "offset": v("offset", torch.int32, (E + 1,)),
+        "sorted_entry": v("sorted_entry", torch.int32, (n,)),
+        "xq": v("xq", torch.uint8, (M, H // 2)),
+        "xs": v("xs", torch.uint8, (M, H // 32)),
+        "midq": v("midq", torch.uint8, (n, I)),
+        "mids": v("mids", torch.float32, (n, I // 128)),
+        "y": v("y", torch.float32, (n, H)),
+    }
+    if s.shared_I:
+        Is = s.shared_I
+        r["sh_xq"] = v("sh_xq", torch.uint8, (M, H))
+        r["sh_xs"] = v("sh_xs", torch.float32, (M, H // 128))
+        r["sh_hq"] = v("sh_hq", torch.uint8, (M, Is))
+        r["sh_hs"] = v("sh_hs", torch.float32, (M, Is // 128))
+        r["sh_y"] = v("sh_y", torch.float32, (M, H))
+    return {key: t.cpu().numpy() for key, t in r.items()}
+
+
+def oracle(d, tokens=None):
+    """Oracle on all tokens, or only on `tokens` (per-token results are
+    independent of the other tokens)."""
+    s = d["shape"]
+    x, lg = d["x"], d["logits"]
+    if tokens is not None:
+        x, lg = x[tokens], lg[tokens]
+    shared = (d["ws13"], d["ss13"], d["ws2"], d["ss2"]) if s.shared_I else None
+    return O.moe_forward(x, lg, d["w13"], d["s13"], d["w2"], d["s2"], s.top_k, s.routed_scaling, shared)
+
+
+def rows_by_entry(sorted_rows, sorted_entry, n):
+    """Reorder rows given in sorted order into entry order (t*k + j)."""
+    out = np.empty((n,) + sorted_rows.shape[1:], sorted_rows.dtype)
+    out[sorted_entry] = sorted_rows
+    return out
+
+
+def e4m3_ulp_distance(a, b):
+    """|difference| in E4M3 steps between codes of equal sign (or both zero)."""
+    va, vb = F.e4m3_decode(a), F.e4m3_decode(b)
+    ia = np.searchsorted(F.E4M3_POS, np.abs(va)) * np.sign(va)
+    ib = np.searchsorted(F.E4M3_POS, np.abs(vb)) * np.sign(vb)
+    return np.abs(ia - ib)
+
+
+def out_error(gpu_bits, ref_bits):
+    """(max |gpu - ref| / RMS(ref), number of differing elements)."""
+    g = F.bf16_decode(gpu_bits)
+    r = F.bf16_decode(ref_bits)
+    rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+    err = float(np.max(np.abs(g - r))) if r.size else 0.0
+    return (err / rms if rms > 0 else err), int(np.count_nonzero(gpu_bits != ref_bits))

@@ -1,0 +1,96 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+that include/*.h declares, and validates shapes and arguments before touching
+a device. No compute call is made here."""
+
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+from quantized_moe_expert_route_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"\b([a-z_][a-z0-9_]*)\s*\([^;{]*\)\s*;", text):
+            names.add(m.group(1))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert {"moe_forward", "moe_plan_create", "moe_plan_set_workspace"} <= names
+    L = B.lib()
+    missing = [n for n in sorted(names) if not hasattr(L, n)]
+    assert not missing, f"not exported: {missing}"
+
+
+def test_status_strings_and_stages():
+    assert B.status_str(B.MOE_OK) == "ok"
+    for st in range(1, 6):
+        assert B.status_str(st) and B.status_str(st) != "ok"
+    assert B.stage_names() == ["route", "align", "gate_up", "act_quant", "down", "shared", "combine"]
+    assert B.lib().moe_stage_name(99) is None
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=4, H=6144, E=256, I=256, top_k=8), B.MOE_OK),
+    (dict(M=0, H=6144, E=256, I=256, top_k=8), B.MOE_OK),
+    (dict(M=4, H=6144, E=256, I=256, top_k=300), B.MOE_ERR_INVALID_ARG),      # k > E
+    (dict(M=-1, H=6144, E=256, I=256, top_k=8), B.MOE_ERR_INVALID_ARG),
+    (dict(M=4, H=6144, E=256, I=256, top_k=8, routed_scaling=0.0), B.MOE_ERR_INVALID_ARG),
+    (dict(M=4, H=6144 + 128, E=256, I=256, top_k=8), B.MOE_ERR_UNSUPPORTED),  # H % 512
+    (dict(M=4, H=6144, E=256, I=200, top_k=8), B.MOE_ERR_UNSUPPORTED),        # I % 128
+    (dict(M=4, H=6144, E=256, I=1024, top_k=8), B.MOE_ERR_UNSUPPORTED),       # I > 512
+    (dict(M=4, H=6144, E=2048, I=256, top_k=8), B.MOE_ERR_UNSUPPORTED),       # E > 1024
+    (dict(M=4, H=6144, E=256, I=256, top_k=17), B.MOE_ERR_UNSUPPORTED),       # k > 16
+    (dict(M=4, H=6144, E=256, I=256, top_k=8, shared_I=100), B.MOE_ERR_UNSUPPORTED),
+])
+def test_shape_validation(kw, status):
+    if status == B.MOE_OK:
+        assert B.shape_workspace_bytes(**kw) % 256 == 0
+    else:
+        with pytest.raises(B.MoeError) as e:
+            B.shape_workspace_bytes(**kw)
+        assert e.value.status == status
+
+
+def test_workspace_holds_the_documented_intermediates():
+    M, H, E, I, k, Is = 4096, 6144, 256, 512, 8, 512
+    nbytes = B.shape_workspace_bytes(M, H, E, I, k, 2.5, Is)
+    n = M * k
+    documented = (4 * n * 3 + 4 * E + 4 * (E + 1) + M * H // 2 + M * H // 32 + n * I + 4 * n * I // 128
+                  + 4 * n * H + M * H + 4 * M * H // 128 + M * Is + 4 * M * Is // 128 + 4 * M * H)
+    assert nbytes >= documented
+    assert nbytes < documented * 1.5
+
+
+def test_null_and_unbound_arguments_fail_before_any_device_work():
+    L = B.lib()
+    out = ctypes.c_void_p()
+    assert L.moe_plan_create(None, ctypes.byref(out)) == B.MOE_ERR_INVALID_ARG
+    s = B.moe_shape(4, 512, 16, 128, 2, 2.5, 0)
+    assert L.moe_plan_create(ctypes.byref(s), None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_forward(None, 4, None, None, None, None, None, None, None, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_plan_layout(None, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_plan_set_stage_events(None, None, 0) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_plan_workspace_bytes(None) == 0
+    L.moe_plan_destroy(None)
+
+
+def test_plan_needs_a_gfx950_device():
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    s = B.moe_shape(4, 512, 16, 128, 2, 2.5, 0)
+    out = ctypes.c_void_p()
+    assert B.lib().moe_plan_create(ctypes.byref(s), ctypes.byref(out)) == B.MOE_ERR_DEVICE
+    assert not out.value
