@@ -1,0 +1,313 @@
+"""Benchmark of one tensor-parallel rank's routed-MoE call on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config c1] [--also c2,c3,c4] [--no-cpu]
+
+One step = one complete call (route, align, gate/up, mid quant, down, combine
+[, shared expert]) on one batch of synthetic inputs already resident in HBM.
+Protocol: the call is captured in a HIP graph; before every timed replay a
+512 MiB buffer is rewritten so the weights are not in the 256 MB MALL (cold,
+the regime of a model whose 75 layers of experts never fit in it); each
+replay is bracketed by events on the replay stream. value = mean cold
+microseconds per call. The stage durations come from events the library
+records between its launches (eager calls, same cold protocol).
+
+Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+FP4_PEAK_TFLOPS = 10100.0  # dense MXFP4 MFMA
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def per_expert_bytes(shape):
+    H, I = shape.H, shape.I
+    w13 = 2 * I * H // 2 + 2 * I * H // 32
+    w2 = H * I // 2 + H * I // 32
+    return w13, w2
+
+
+def call_bytes(shape, n_act):
+    """Algorithmic HBM bytes of one call: active experts' weights read once,
+    x, logits and out, plus the shared expert's weights."""
+    w13, w2 = per_expert_bytes(shape)
+    b = n_act * (w13 + w2) + shape.M * shape.H * 2 + shape.M * shape.E * 4 + shape.M * shape.H * 2
+    if shape.shared_I:
+        Is, H = shape.shared_I, shape.H
+        b += 2 * Is * H + 4 * (2 * Is // 128) * (H // 128) + H * Is + 4 * (H // 128) * (Is // 128)
+    return b
+
+
+def gate_up_bytes(shape, n_act):
+    """Algorithmic bytes of the gate/up launch: active experts' w13 (values +
+    scales), the tokens' MXFP4 x (values + scales) and the fp32 h it writes."""
+    w13, _ = per_expert_bytes(shape)
+    M, H, k, I = shape.M, shape.H, shape.top_k, shape.I
+    return n_act * w13 + M * (H // 2 + H // 32) + M * k * I * 4
+
+
+def call_flops(shape):
+    f = 2 * shape.M * shape.top_k * 3 * shape.H * shape.I
+    if shape.shared_I:
+        f += 2 * shape.M * 3 * shape.H * shape.shared_I
+    return f
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "quantized_moe_expert_route_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measure(name, steps, warmup, n_sets):
+    import torch
+
+    from quantized_moe_expert_route_amd import fixtures as X
+    from quantized_moe_expert_route_amd.binding import HipEvents, Plan, stage_names
+
+    wl = X.WORKLOADS[name]
+    s = wl.shape
+    dev = torch.device("cuda", 0)
+    base = X.make_inputs(name)
+    t = {k: torch.from_numpy(base[k]).to(dev) for k in ("w13", "s13", "w2", "s2")}
+    sets = []
+    for i in range(n_sets):
+        d = X.make_inputs(X.Shape(**vars(s)), wl.logits, wl.seed * 1000 + i, with_weights=False) if i else base
+        sets.append((torch.from_numpy(d["x"].view(np.int16)).to(dev), torch.from_numpy(d["logits"]).to(dev)))
+    plan = Plan(s.M, s.H, s.E, s.I, s.top_k, s.routed_scaling, s.shared_I)
+    if s.shared_I:
+        sh = [torch.from_numpy(base[k]).to(dev) for k in ("ws13", "ss13", "ws2", "ss2")]
+        plan.set_shared(*sh)
+    x = torch.empty_like(sets[0][0])
+    logits = torch.empty_like(sets[0][1])
+    out = torch.empty((s.M, s.H), dtype=torch.int16, device=dev)
+    flush = torch.empty(128 * 1024 * 1024, dtype=torch.float32, device=dev)  # 512 MiB
+
+    def call():
+        plan.forward(x, logits, t["w13"], t["s13"], t["w2"], t["s2"], out)
+
+    # active experts of every input set, read from the library's own counts
+    n_act = []
+    for xs_, lg in sets:
+        x.copy_(xs_)
+        logits.copy_(lg)
+        call()
+        torch.cuda.synchronize()
+        cnt = plan.view("count", torch.int32, (s.E,))
+        n_act.append(int((cnt > 0).sum().item()))
+
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        call()
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(warmup):
+        x.copy_(sets[i % n_sets][0])
+        logits.copy_(sets[i % n_sets][1])
+        flush.add_(1.0)
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        x.copy_(sets[i % n_sets][0])
+        logits.copy_(sets[i % n_sets][1])
+        flush.add_(1.0)
+        ev0[i].record()
+        graph.replay()
+        ev1[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    cold_us = np.array([a.elapsed_time(b) * 1000.0 for a, b in zip(ev0, ev1)])
+
+    # warm: the same inputs back to back (weights partly MALL-resident)
+    x.copy_(sets[0][0])
+    logits.copy_(sets[0][1])
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    warm_us = e0.elapsed_time(e1) * 1000.0 / steps
+
+    # per-stage durations (eager calls, cold), on the stream the kernels run on
+    names = stage_names()
+    hev = HipEvents(len(names) + 1)
+    plan.set_stage_events(hev.handles)
+    stage_us = np.zeros((steps, len(names)))
+    for i in range(steps):
+        x.copy_(sets[i % n_sets][0])
+        logits.copy_(sets[i % n_sets][1])
+        flush.add_(1.0)
+        call()
+        torch.cuda.synchronize()
+        for j in range(len(names)):
+            stage_us[i, j] = hev.elapsed_ms(j, j + 1) * 1000.0
+    plan.set_stage_events(None)
+    hev.close()
+    per_set_act = [n_act[i % n_sets] for i in range(steps)]
+    mean_act = float(np.mean(per_set_act))
+    res = {
+        "name": name, "shape": s, "cold_us": cold_us, "warm_us": warm_us, "wall_s": wall,
+        "stage_us": dict(zip(names, stage_us.mean(0).tolist())), "n_act": mean_act,
+        "n_act_sets": n_act, "bytes": float(np.mean([call_bytes(s, a) for a in per_set_act])),
+        "gate_up_bytes": float(np.mean([gate_up_bytes(s, a) for a in per_set_act])),
+        "flops": call_flops(s), "base": base,
+    }
+    del graph, flush
+    torch.cuda.synchronize()
+    return res
+
+
+def cpu_baseline(res, budget_s=12.0):
+    """The oracle, as it stands, on the host: whole calls on the headline
+    workload's inputs until ~budget_s of CPU work."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import moe as O
+
+    d = res["base"]
+    s = d["shape"]
+    shared = (d["ws13"], d["ss13"], d["ws2"], d["ss2"]) if s.shared_I else None
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        O.moe_forward(d["x"], d["logits"], d["w13"], d["s13"], d["w2"], d["s2"], s.top_k, s.routed_scaling, shared)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > budget_s or len(times) >= 20:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": float(np.median(times) * 1e6), "unit": "us per call", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{len(times)} whole calls of the {res['name']} workload (M={s.M}), median; "
+                      f"host os.cpu_count()={os.cpu_count()}, affinity={len(os.sched_getaffinity(0))}"}
+
+
+def traffic_for(name, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 PMC
+    summary, if it was taken on the current kernel sources."""
+    p = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        j = json.load(open(p))
+    except Exception:
+        return None
+    if j.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    e = j.get("workloads", {}).get(name, {}).get(kernel)
+    return None if e is None else e.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="c1", help="headline workload (c1..c4)")
+    ap.add_argument("--also", default="c2,c3,c4", help="more workloads reported in the same line ('' for none)")
+    ap.add_argument("--sets", type=int, default=8, help="distinct input batches cycled through the steps")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the path is one tensor-parallel rank's call on one MI355X)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    from quantized_moe_expert_route_amd import fixtures as X
+
+    head = measure(args.config, args.steps, args.warmup, args.sets)
+    print(f"[bench] {args.config}: cold {head['cold_us'].mean():.1f} us, warm {head['warm_us']:.1f} us, "
+          f"stages {json.dumps({k: round(v, 1) for k, v in head['stage_us'].items()})}", file=sys.stderr, flush=True)
+    others = {}
+    for name in [c for c in args.also.split(",") if c and c != args.config]:
+        r = measure(name, max(10, args.steps // 2), max(3, args.warmup // 2), min(args.sets, 4))
+        mu = r["cold_us"].mean()
+        others[name] = {
+            "us_per_call_cold": round(mu, 2), "us_per_call_warm": round(r["warm_us"], 2),
+            "n_active_experts": round(r["n_act"], 1),
+            "hbm_frac": round(r["bytes"] / (mu * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "fp4_mfma_frac": round(r["flops"] / (mu * 1e-6) / 1e12 / FP4_PEAK_TFLOPS, 4),
+            "stage_us": {k: round(v, 2) for k, v in r["stage_us"].items()},
+        }
+        print(f"[bench] {name}: {others[name]}", file=sys.stderr, flush=True)
+        del r
+    mu = float(head["cold_us"].mean())
+    s = head["shape"]
+    gu_us = head["stage_us"]["gate_up"]
+    achieved = head["gate_up_bytes"] / (gu_us * 1e-6) / 1e9
+    line = {
+        "metric": "us per local MoE call (cold MALL, hipGraph replay)",
+        "value": round(mu, 3),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(mu / 1000.0, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.config}: {X.WORKLOAD_TITLES[args.config]}",
+            "M": s.M, "H": s.H, "E": s.E, "I": s.I, "top_k": s.top_k, "routed_scaling": s.routed_scaling,
+            "shared_I": s.shared_I, "n_active_experts": round(head["n_act"], 2),
+            "protocol": "cold: 512 MiB rewritten before each replay; events around the replay",
+        },
+        "us_per_call_p50": round(float(np.median(head["cold_us"])), 3),
+        "us_per_call_warm": round(head["warm_us"], 3),
+        "hbm_frac_call": round(head["bytes"] / (mu * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "fp4_mfma_frac_call": round(head["flops"] / (mu * 1e-6) / 1e12 / FP4_PEAK_TFLOPS, 6),
+        "stage_us": {k: round(v, 3) for k, v in head["stage_us"].items()},
+        "timed_region_s": round(head["wall_s"], 4),
+        "roofline": {
+            "kernel": "gate_up",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic_for(args.config, "gate_up"),
+            "algorithmic_bytes_per_launch": round(head["gate_up_bytes"]),
+            "avg_launch_us": round(gu_us, 3),
+        },
+        "others": others,
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(head)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

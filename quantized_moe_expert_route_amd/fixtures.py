@@ -27,6 +27,7 @@ the full tensor.
 from __future__ import annotations
 
 import dataclasses
+import os
 from typing import Dict, Optional
 
 import numpy as np
@@ -193,8 +194,18 @@ def make_weights(shape: Shape, seed: int, experts: Optional[np.ndarray] = None):
     s13 = np.zeros((E, 2 * I, H // 32), np.uint8)
     w2 = np.zeros((E, H, I // 2), np.uint8)
     s2 = np.zeros((E, H, I // 32), np.uint8)
-    for e in range(E) if experts is None else experts:
+    def one(e):
         w13[e], s13[e], w2[e], s2[e] = make_expert_weights(shape, seed, int(e))
+
+    todo = list(range(E) if experts is None else experts)
+    if len(todo) > 8:
+        import concurrent.futures as cf
+
+        with cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+            list(ex.map(one, todo))
+    else:
+        for e in todo:
+            one(e)
     return w13, s13, w2, s2
 
 
