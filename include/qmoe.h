@@ -136,10 +136,12 @@ moe_status moe_forward(moe_plan* plan, int64_t M, const void* x, const float* lo
                        const void* w13, const void* s13, const void* w2, const void* s2,
                        void* out, void* stream);
 
-/* Profiling aid: when `events` is non-NULL, moe_forward records
- * events[i] (hipEvent_t) on the stream before stage i and events[n_stages]
- * after the last stage, so that each stage's duration can be read with
- * hipEventElapsedTime. `n` must be moe_stage_count() + 1. NULL disables. */
+/* Profiling aid: when `events` is non-NULL, moe_forward brackets stage i
+ * with events[2i] (start of its first kernel) and events[2i+1] (end of its
+ * last kernel), hipEvent_t handles, so hipEventElapsedTime(events[2i],
+ * events[2i+1]) is the stage's execution time. A stage folded into another
+ * one for small M records an empty interval. `n` must be
+ * 2 * moe_stage_count(). NULL disables. */
 moe_status moe_plan_set_stage_events(moe_plan* plan, void* const* events, int n);
 
 /* Number and names of the launch stages of a call (for the events above). */

@@ -141,7 +141,8 @@ class Plan:
             raise MoeError(st, "moe_plan_set_shared")
 
     def set_stage_events(self, events):
-        """events: list of raw hipEvent_t handles (ints), len = stages + 1; None clears."""
+        """events: raw hipEvent_t handles (ints), [start0, stop0, start1, stop1, ...]
+        for every stage; None clears."""
         if events is None:
             st = lib().moe_plan_set_stage_events(self._h, None, 0)
             self._events = None

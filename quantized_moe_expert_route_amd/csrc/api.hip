@@ -11,7 +11,7 @@ using namespace qmoe;
 
 namespace {
 
-const char* kStageNames[] = {"route", "align", "gate_up", "act_quant", "down", "shared", "combine"};
+const char* kStageNames[] = {"route", "align", "gate_up", "act_quant", "shared", "down", "combine"};
 constexpr int kStages = 7;
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -57,9 +57,13 @@ Layout make_layout(const moe_shape& s) {
   r.L.sorted_entry = take(4 * n);
   r.X.tiles = take(16 * (size_t)r.t16);
   r.X.meta = take(256);
+  // counters and the token bitmap: zeroed when the workspace is bound, and
+  // left zero by every call
   r.X.bitmap = take(4 * E * (size_t)r.words);
+  r.X.qctr = take(4 * (size_t)r.t16 * (I / 128));
+  r.X.cctr = take(4 * M * (H / 256));
   r.X.sync_begin = r.X.bitmap;
-  r.X.sync_bytes = align256(4 * E * (size_t)r.words);
+  r.X.sync_bytes = align256(off) - r.X.bitmap;
   r.X.pre = take(4 * E * (size_t)r.words);
   r.L.xq = take(M * H / 2);
   r.L.xs = take(M * H / 32);
@@ -213,7 +217,7 @@ moe_status moe_plan_set_stage_events(moe_plan* plan, void* const* events, int n)
     plan->n_events = 0;
     return MOE_OK;
   }
-  if (n != kStages + 1) return MOE_ERR_INVALID_ARG;
+  if (n != 2 * kStages) return MOE_ERR_INVALID_ARG;
   for (int i = 0; i < n; ++i) {
     if (!events[i]) return MOE_ERR_INVALID_ARG;
     plan->events[i] = (hipEvent_t)events[i];
@@ -243,14 +247,31 @@ moe_status moe_forward(moe_plan* plan, int64_t M, const void* x, const float* lo
   DeviceGuard guard(plan->device);
   if (!guard.ok) return MOE_ERR_DEVICE;
   CallArgs a{M, x, logits, w13, s13, w2, s2, out, (hipStream_t)stream};
-  hipError_t (*stages[kStages])(const moe_plan*, const CallArgs&) = {
-      launch_route, launch_align, launch_gate_up, launch_act_quant, launch_down, launch_shared, launch_combine};
-  for (int i = 0; i < kStages; ++i) {
-    if (plan->n_events && hipEventRecord(plan->events[i], a.stream) != hipSuccess) return MOE_ERR_HIP;
-    if (stages[i](plan, a) != hipSuccess) return MOE_ERR_HIP;
-  }
-  if (plan->n_events && hipEventRecord(plan->events[kStages], a.stream) != hipSuccess) return MOE_ERR_HIP;
-  return MOE_OK;
+  Ev ev[kStages];
+  if (plan->n_events)
+    for (int i = 0; i < kStages; ++i) ev[i] = Ev{plan->events[2 * i], plan->events[2 * i + 1]};
+  // a stage with no launch of its own still records its (empty) interval
+  auto none = [&](int i) -> hipError_t {
+    if (!plan->n_events) return hipSuccess;
+    hipError_t e = hipEventRecord(ev[i].start, a.stream);
+    return e != hipSuccess ? e : hipEventRecord(ev[i].stop, a.stream);
+  };
+  // Up to kSmallM tokens, routing + sort + x quantization run in one
+  // workgroup (one launch); above, routing is spread over the GPU and a
+  // second launch sorts. The other stages are one launch each: folding the
+  // mid quantization or the combine into the producing launch needs a
+  // device-scope release/acquire per workgroup, which writes back and
+  // invalidates a whole L2 of an XCD each time and costs more than a launch.
+  const bool small = M <= kSmallM;
+  const bool fuse = false;
+  hipError_t e = small ? launch_route_small(plan, a, ev[0]) : launch_route(plan, a, ev[0]);
+  if (e == hipSuccess) e = small ? none(1) : launch_align(plan, a, ev[1]);
+  if (e == hipSuccess) e = launch_gate_up(plan, a, ev[2], fuse);
+  if (e == hipSuccess) e = fuse ? none(3) : launch_act_quant(plan, a, ev[3]);
+  if (e == hipSuccess) e = plan->s.shared_I > 0 ? launch_shared(plan, a, ev[4]) : none(4);
+  if (e == hipSuccess) e = launch_down(plan, a, ev[5], fuse);
+  if (e == hipSuccess) e = fuse ? none(6) : launch_combine(plan, a, ev[6]);
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 }  // extern "C"

@@ -56,13 +56,33 @@ __device__ __forceinline__ v8s fp4x8_to_bf16(uint32_t src, float scale) {
 // K=32 take, in step q, K = 32g + 8q.. for lane group g, so a lane reads 32
 // contiguous mid bytes and 16 contiguous weight bytes (one MX block, one
 // scale byte) per block.
-template <int NB>  // I / 128
+// out[t, c0 .. c0 + n) from y (float64 products and sum in slot order, plus
+// the shared expert), one bf16 rounding; thread i does columns c0 + i + kk*step.
+__device__ __forceinline__ void combine_cols(const float* __restrict__ y, const float* __restrict__ w,
+                                             const float* __restrict__ ys, int t, int k, int H, int c0, int ncols,
+                                             uint16_t* __restrict__ out) {
+  for (int c = c0 + (int)threadIdx.x; c < c0 + ncols; c += blockDim.x) {
+    double acc = 0.0;
+    for (int j = 0; j < k; ++j)
+      acc += (double)w[(size_t)t * k + j] * (double)y[((size_t)t * k + j) * H + c];
+    if (ys) acc += (double)ys[(size_t)t * H + c];
+    out[(size_t)t * H + c] = (uint16_t)bf16_rne_from_double(acc);
+  }
+}
+
+// FUSED: after writing its y rows of a 256-column chunk, the workgroup counts
+// one finished slot per (token, chunk); the workgroup that brings a token's
+// count to k combines that token's chunk (and resets the counter).
+template <int NB, bool FUSED>  // NB = I / 128
 __global__ __launch_bounds__(256) void down_m16_kernel(
     const uint8_t* __restrict__ midq, const float* __restrict__ mids, const uint8_t* __restrict__ w2,
     const uint8_t* __restrict__ s2, const int* __restrict__ sorted_entry, const int4* __restrict__ tiles,
-    const int* __restrict__ meta, float* __restrict__ y, int H) {
+    const int* __restrict__ meta, float* __restrict__ y, int H, int k, const float* __restrict__ topk_w,
+    const float* __restrict__ ys, uint32_t* __restrict__ cctr, uint16_t* __restrict__ out) {
   constexpr int I = NB * 128;
   __shared__ uint16_t tab[256];
+  __shared__ int s_done[16];
+  __shared__ int s_ndone;
   tab[threadIdx.x] = kE4m3Bf16.v[threadIdx.x];
   __syncthreads();
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -100,16 +120,27 @@ __global__ __launch_bounds__(256) void down_m16_kernel(
 #pragma unroll
       for (int b = 0; b < NB; ++b) sc[b][i] = v ? mids[(size_t)(r0 + m) * NB + b] : 0.f;
     }
+    // all weight loads of the wave's 4 column tiles go out first
+    uint4 wbuf[4][NB];
+    uint32_t wsbuf[4][NB];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       const int n = nc * 256 + wave * 64 + nt * 16 + r;  // this lane's weight row (B column)
       const uint8_t* pw = w2 + ((size_t)e * H + n) * (I / 2);
       const uint8_t* ps = s2 + ((size_t)e * H + n) * (I / 32);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        wbuf[nt][b] = ld16(pw + b * 64 + g * 16);
+        wsbuf[nt][b] = ps[b * 4 + g];
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
       double acc[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        const uint4 wb = ld16(pw + b * 64 + g * 16);
-        const float wsc = e8m0_to_float(ps[b * 4 + g]);
+        const uint4 wb = wbuf[nt][b];
+        const float wsc = e8m0_to_float(wsbuf[nt][b]);
         v4f P = {0.f, 0.f, 0.f, 0.f};
         P = mfma_bf16(A[b][0], fp4x8_to_bf16(wb.x, wsc), P);
         P = mfma_bf16(A[b][1], fp4x8_to_bf16(wb.y, wsc), P);
@@ -121,6 +152,26 @@ __global__ __launch_bounds__(256) void down_m16_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (orow[i] >= 0) y[(size_t)orow[i] * H + nc * 256 + wave * 64 + nt * 16 + r] = (float)acc[i];
+    }
+    if (FUSED) {
+      if (threadIdx.x == 0) s_ndone = 0;
+      __threadfence();
+      __syncthreads();
+      if (threadIdx.x < 16 && r0 + (int)threadIdx.x < r1) {
+        const int t = sorted_entry[r0 + threadIdx.x] / k;
+        if (atomicAdd(&cctr[(size_t)t * n_chunks + nc], 1u) == (uint32_t)(k - 1)) s_done[atomicAdd(&s_ndone, 1)] = t;
+      }
+      __syncthreads();
+      const int nd = s_ndone;
+      if (nd > 0) {
+        __threadfence();
+        for (int q = 0; q < nd; ++q) {
+          const int t = s_done[q];
+          combine_cols(y, topk_w, ys, t, k, H, nc * 256, 256, out);
+          if (threadIdx.x == 0) cctr[(size_t)t * n_chunks + nc] = 0u;
+        }
+      }
+      __syncthreads();
     }
   }
 }
@@ -157,37 +208,36 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
 }
 
-hipError_t launch_down(const moe_plan* p, const CallArgs& a) {
+hipError_t launch_down(const moe_plan* p, const CallArgs& a, Ev ev, bool fused) {
   const int64_t n = a.M * p->s.top_k;
   const int64_t t16 = (n + std::min<int64_t>(p->s.E, n) * (kTileRows - 1) + kTileRows - 1) / kTileRows;
   const int H = (int)p->s.H;
   const int64_t work_max = t16 * (H / 256);
   const int blocks = (int)std::min<int64_t>(work_max, 4096);
+  const float* ys = p->s.shared_I > 0 ? wsp<float>(p, p->L.sh_y) : nullptr;
   auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, a.stream, wsp<uint8_t>(p, p->L.midq),
-                       wsp<float>(p, p->L.mids), reinterpret_cast<const uint8_t*>(a.w2),
-                       reinterpret_cast<const uint8_t*>(a.s2), wsp<int>(p, p->L.sorted_entry),
-                       wsp<int4>(p, p->X.tiles), wsp<int>(p, p->X.meta), wsp<float>(p, p->L.y), H);
+    return launch_k(kern, dim3(blocks), dim3(256), 0, a.stream, ev, wsp<uint8_t>(p, p->L.midq),
+                    wsp<float>(p, p->L.mids), reinterpret_cast<const uint8_t*>(a.w2),
+                    reinterpret_cast<const uint8_t*>(a.s2), wsp<int>(p, p->L.sorted_entry), wsp<int4>(p, p->X.tiles),
+                    wsp<int>(p, p->X.meta), wsp<float>(p, p->L.y), H, (int)p->s.top_k, wsp<float>(p, p->L.topk_w),
+                    ys, wsp<uint32_t>(p, p->X.cctr), reinterpret_cast<uint16_t*>(a.out));
   };
   switch (p->s.I / 128) {
-    case 1: go(down_m16_kernel<1>); break;
-    case 2: go(down_m16_kernel<2>); break;
-    case 3: go(down_m16_kernel<3>); break;
-    case 4: go(down_m16_kernel<4>); break;
+    case 1: return fused ? go(down_m16_kernel<1, true>) : go(down_m16_kernel<1, false>);
+    case 2: return fused ? go(down_m16_kernel<2, true>) : go(down_m16_kernel<2, false>);
+    case 3: return fused ? go(down_m16_kernel<3, true>) : go(down_m16_kernel<3, false>);
+    case 4: return fused ? go(down_m16_kernel<4, true>) : go(down_m16_kernel<4, false>);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
-hipError_t launch_combine(const moe_plan* p, const CallArgs& a) {
+hipError_t launch_combine(const moe_plan* p, const CallArgs& a, Ev ev) {
   const int H = (int)p->s.H;
   const int64_t total = a.M * (H / 8);
   const int blocks = (int)std::min<int64_t>((total + 255) / 256, 8192);
   const float* ys = p->s.shared_I > 0 ? wsp<float>(p, p->L.sh_y) : nullptr;
-  hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(256), 0, a.stream, wsp<float>(p, p->L.y),
-                     wsp<float>(p, p->L.topk_w), ys, (int)a.M, H, (int)p->s.top_k,
-                     reinterpret_cast<uint16_t*>(a.out));
-  return hipGetLastError();
+  return launch_k(combine_kernel, dim3(blocks), dim3(256), 0, a.stream, ev, wsp<float>(p, p->L.y),
+                  wsp<float>(p, p->L.topk_w), ys, (int)a.M, H, (int)p->s.top_k, reinterpret_cast<uint16_t*>(a.out));
 }
 
 }  // namespace qmoe

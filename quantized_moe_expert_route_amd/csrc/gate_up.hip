@@ -22,12 +22,40 @@
 
 namespace qmoe {
 
+constexpr int kSS = 3;  // super-steps (512 K each) whose loads a wave keeps in flight
+
+// One wave quantizes rows [r0, r1) of mid block b: s = fl32(amax / 448),
+// q = E4M3(fl32(h / s)); 128 values = 2 per lane.
+__device__ __forceinline__ void quant_mid_rows(const float* __restrict__ h, int r0, int r1, int row_step, int I, int b,
+                                               uint8_t* __restrict__ q, float* __restrict__ s) {
+  const int lane = threadIdx.x & 63;
+  const int nb = I / 128;
+  for (int row = r0; row < r1; row += row_step) {
+    const size_t base = (size_t)row * I + b * 128 + 2 * lane;
+    const float2 v = *reinterpret_cast<const float2*>(h + base);
+    const float amax = wave_max(fmaxf(fabsf(v.x), fabsf(v.y)));
+    const float sc = __fdiv_rn(amax, 448.0f);
+    uint32_t c0 = 0, c1 = 0;
+    if (sc > 0.f) {
+      c0 = e4m3_code(__fdiv_rn(v.x, sc));
+      c1 = e4m3_code(__fdiv_rn(v.y, sc));
+    }
+    *reinterpret_cast<uint16_t*>(q + base) = (uint16_t)(c0 | (c1 << 8));
+    if (lane == 0) s[(size_t)row * nb + b] = sc;
+  }
+}
+
+// FUSED: the workgroup that finishes the last of the 8 items of a (tile,
+// 128-block) quantizes that block for the tile's rows (a counter per
+// (tile, block), released by every writer and reset by the last one).
+template <bool FUSED>
 __global__ __launch_bounds__(256) void gate_up_m16_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const uint8_t* __restrict__ w13,
     const uint8_t* __restrict__ s13, const int* __restrict__ sorted_entry,
     const int4* __restrict__ tiles, const int* __restrict__ meta, float* __restrict__ hout, int H,
-    int I, int k) {
+    int I, int k, uint32_t* __restrict__ qctr, uint8_t* __restrict__ midq, float* __restrict__ mids) {
   __shared__ v4f red[2][4][64];
+  __shared__ int s_last;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4;
   const int n_it = I / 16;
@@ -48,24 +76,39 @@ __global__ __launch_bounds__(256) void gate_up_m16_kernel(
     const uint8_t* pu = pg + (size_t)I * Hb;
     const uint8_t* psu = psg + (size_t)I * Hs;
     v4f accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
-    for (int ss = wave; ss < nss; ss += 4) {
-      const int boff = ss * 256 + g * 64;
-      const int soff = ss * 16 + g * 4;
-      uint4 a[4], bg[4], bu[4];
+    // wave w owns the contiguous super-steps [w*per, (w+1)*per); all loads of
+    // up to kSS of them are in flight before the first MFMA
+    const int per = (nss + 3) / 4;
+    const int ss_end = min(nss, (wave + 1) * per);
+    for (int ss0 = wave * per; ss0 < ss_end; ss0 += kSS) {
+      uint4 a[kSS][4], bg[kSS][4], bu[kSS][4];
+      uint32_t sa[kSS], sg[kSS], su[kSS];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        a[j] = rv ? ld16(pa + boff + 16 * j) : make_uint4(0, 0, 0, 0);
-        bg[j] = ld16(pg + boff + 16 * j);
-        bu[j] = ld16(pu + boff + 16 * j);
+      for (int q = 0; q < kSS; ++q) {
+        const int ss = min(ss0 + q, ss_end - 1);  // clamped: a duplicate step is loaded but not used
+        const int boff = ss * 256 + g * 64;
+        const int soff = ss * 16 + g * 4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          bg[q][j] = ld16(pg + boff + 16 * j);
+          bu[q][j] = ld16(pu + boff + 16 * j);
+        }
+        sg[q] = ld4(psg + soff);
+        su[q] = ld4(psu + soff);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a[q][j] = rv ? ld16(pa + boff + 16 * j) : make_uint4(0, 0, 0, 0);
+        sa[q] = rv ? ld4(psa + soff) : 0x7F7F7F7Fu;
       }
-      const uint32_t sa = rv ? ld4(psa + soff) : 0x7F7F7F7Fu;
-      const uint32_t sg = ld4(psg + soff);
-      const uint32_t su = ld4(psu + soff);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t xa = (sa >> (8 * j)) & 0xFFu;
-        accg = mfma_fp4(a[j], bg[j], accg, xa, (sg >> (8 * j)) & 0xFFu);
-        accu = mfma_fp4(a[j], bu[j], accu, xa, (su >> (8 * j)) & 0xFFu);
+      for (int q = 0; q < kSS; ++q) {
+        if (ss0 + q < ss_end) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t xa = (sa[q] >> (8 * j)) & 0xFFu;
+            accg = mfma_fp4(a[q][j], bg[q][j], accg, xa, (sg[q] >> (8 * j)) & 0xFFu);
+            accu = mfma_fp4(a[q][j], bu[q][j], accu, xa, (su[q] >> (8 * j)) & 0xFFu);
+          }
+        }
       }
     }
     red[0][wave][lane] = accg;
@@ -79,6 +122,17 @@ __global__ __launch_bounds__(256) void gate_up_m16_kernel(
       const float U = ((red[1][0][l][i] + red[1][1][l][i]) + red[1][2][l][i]) + red[1][3][l][i];
       if (r0 + m < r1) hout[(size_t)(r0 + m) * I + it * 16 + n] = silu_mul(G, U);
     }
+    if (FUSED) {
+      __threadfence();
+      __syncthreads();
+      if (threadIdx.x == 0) s_last = atomicAdd(&qctr[(size_t)(w / n_it) * (I / 128) + it / 8], 1u) == 7u;
+      __syncthreads();
+      if (s_last) {
+        __threadfence();
+        quant_mid_rows(hout, r0 + wave, r1, 4, I, it / 8, midq, mids);
+        if (threadIdx.x == 0) qctr[(size_t)(w / n_it) * (I / 128) + it / 8] = 0u;
+      }
+    }
     __syncthreads();
   }
 }
@@ -86,47 +140,38 @@ __global__ __launch_bounds__(256) void gate_up_m16_kernel(
 // One wave per (row, 128-block): s = fl32(amax / 448), q = E4M3(fl32(h / s)).
 __global__ __launch_bounds__(256) void act_quant_kernel(const float* __restrict__ h, int rows, int I,
                                                         uint8_t* __restrict__ q, float* __restrict__ s) {
-  const int lane = threadIdx.x & 63;
   const int nb = I / 128;
   const int total = rows * nb;
   for (int wv = blockIdx.x * 4 + (threadIdx.x >> 6); wv < total; wv += gridDim.x * 4) {
     const int row = wv / nb, b = wv % nb;
-    const size_t base = (size_t)row * I + b * 128 + 2 * lane;
-    const float2 v = *reinterpret_cast<const float2*>(h + base);
-    const float amax = wave_max(fmaxf(fabsf(v.x), fabsf(v.y)));
-    const float sc = __fdiv_rn(amax, 448.0f);
-    uint32_t c0 = 0, c1 = 0;
-    if (sc > 0.f) {
-      c0 = e4m3_code(__fdiv_rn(v.x, sc));
-      c1 = e4m3_code(__fdiv_rn(v.y, sc));
-    }
-    *reinterpret_cast<uint16_t*>(q + base) = (uint16_t)(c0 | (c1 << 8));
-    if (lane == 0) s[(size_t)row * nb + b] = sc;
+    quant_mid_rows(h, row, row + 1, 1, I, b, q, s);
   }
 }
 
-hipError_t launch_gate_up(const moe_plan* p, const CallArgs& a) {
+hipError_t launch_gate_up(const moe_plan* p, const CallArgs& a, Ev ev, bool fused) {
   const int I = (int)p->s.I;
   const int64_t n = a.M * p->s.top_k;
   const int64_t t16 = (n + std::min<int64_t>(p->s.E, n) * (kTileRows - 1) + kTileRows - 1) / kTileRows;
   const int64_t work_max = t16 * (I / 16);
   const int blocks = (int)std::min<int64_t>(work_max, 2048);
-  hipLaunchKernelGGL(gate_up_m16_kernel, dim3(blocks), dim3(256), 0, a.stream,
-                     wsp<uint8_t>(p, p->L.xq), wsp<uint8_t>(p, p->L.xs),
-                     reinterpret_cast<const uint8_t*>(a.w13), reinterpret_cast<const uint8_t*>(a.s13),
-                     wsp<int>(p, p->L.sorted_entry), wsp<int4>(p, p->X.tiles), wsp<int>(p, p->X.meta),
-                     wsp<float>(p, p->X.h), (int)p->s.H, I, (int)p->s.top_k);
-  return hipGetLastError();
+  auto go = [&](auto kern) {
+    return launch_k(kern, dim3(blocks), dim3(256), 0, a.stream, ev, wsp<uint8_t>(p, p->L.xq),
+                    wsp<uint8_t>(p, p->L.xs), reinterpret_cast<const uint8_t*>(a.w13),
+                    reinterpret_cast<const uint8_t*>(a.s13), wsp<int>(p, p->L.sorted_entry),
+                    wsp<int4>(p, p->X.tiles), wsp<int>(p, p->X.meta), wsp<float>(p, p->X.h), (int)p->s.H, I,
+                    (int)p->s.top_k, wsp<uint32_t>(p, p->X.qctr), wsp<uint8_t>(p, p->L.midq),
+                    wsp<float>(p, p->L.mids));
+  };
+  return fused ? go(gate_up_m16_kernel<true>) : go(gate_up_m16_kernel<false>);
 }
 
-hipError_t launch_act_quant(const moe_plan* p, const CallArgs& a) {
+hipError_t launch_act_quant(const moe_plan* p, const CallArgs& a, Ev ev) {
   const int rows = (int)(a.M * p->s.top_k);
   const int I = (int)p->s.I;
   const int64_t waves = (int64_t)rows * (I / 128);
   const int blocks = (int)std::min<int64_t>((waves + 3) / 4, 8192);
-  hipLaunchKernelGGL(act_quant_kernel, dim3(blocks), dim3(256), 0, a.stream, wsp<float>(p, p->X.h), rows, I,
-                     wsp<uint8_t>(p, p->L.midq), wsp<float>(p, p->L.mids));
-  return hipGetLastError();
+  return launch_k(act_quant_kernel, dim3(blocks), dim3(256), 0, a.stream, ev, wsp<float>(p, p->X.h), rows, I,
+                  wsp<uint8_t>(p, p->L.midq), wsp<float>(p, p->L.mids));
 }
 
 }  // namespace qmoe

@@ -2,6 +2,7 @@
 // the kernel files.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -20,6 +21,8 @@ struct Internal {
   size_t pre;      // int32 [E, ceil(M/32)]: entries of row e before word w
   size_t h;        // fp32 [n, I]: SiLU(gate)*up, rows in sorted order
   size_t sh_h;     // fp32 [M, Is]
+  size_t qctr;     // uint32 [T16, I/128]: finished 16-column items per (tile, mid block)
+  size_t cctr;     // uint32 [M, H/256]: finished slots per (token, 256-column chunk)
   size_t sync_begin, sync_bytes;  // region zeroed once when the workspace is bound
 };
 
@@ -45,6 +48,25 @@ struct moe_plan {
 
 namespace qmoe {
 
+// Stage timing: a launch with non-null events records them around itself.
+struct Ev {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
+template <typename... KArgs, typename... Args>
+inline hipError_t launch_k(void (*kern)(KArgs...), dim3 grid, dim3 block, size_t lds, hipStream_t s, Ev ev,
+                           Args... args) {
+  if (ev.start || ev.stop)
+    hipExtLaunchKernelGGL(kern, grid, block, lds, s, ev.start, ev.stop, 0, static_cast<KArgs>(args)...);
+  else
+    hipLaunchKernelGGL(kern, grid, block, lds, s, static_cast<KArgs>(args)...);
+  return hipGetLastError();
+}
+
+// Largest M served by the single-workgroup routing/sort path and the fused
+// small-token kernels.
+constexpr int kSmallM = 64;
+
 struct CallArgs {
   int64_t M;
   const void* x;
@@ -61,12 +83,16 @@ template <typename T>
 inline T* wsp(const moe_plan* p, size_t off) { return reinterpret_cast<T*>(p->ws + off); }
 
 hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t s);
-hipError_t launch_route(const moe_plan* p, const CallArgs& a);
-hipError_t launch_align(const moe_plan* p, const CallArgs& a);
-hipError_t launch_gate_up(const moe_plan* p, const CallArgs& a);
-hipError_t launch_act_quant(const moe_plan* p, const CallArgs& a);
-hipError_t launch_down(const moe_plan* p, const CallArgs& a);
-hipError_t launch_shared(const moe_plan* p, const CallArgs& a);
-hipError_t launch_combine(const moe_plan* p, const CallArgs& a);
+// Small M (<= kSmallM): route + sort + x quantization in one workgroup.
+hipError_t launch_route_small(const moe_plan* p, const CallArgs& a, Ev ev);
+hipError_t launch_route(const moe_plan* p, const CallArgs& a, Ev ev);
+hipError_t launch_align(const moe_plan* p, const CallArgs& a, Ev ev);
+// fused = mid quantization done by the last item of each (tile, 128-block)
+hipError_t launch_gate_up(const moe_plan* p, const CallArgs& a, Ev ev, bool fused);
+hipError_t launch_act_quant(const moe_plan* p, const CallArgs& a, Ev ev);
+// fused = combine done by the last slot of each (token, 256-column chunk)
+hipError_t launch_down(const moe_plan* p, const CallArgs& a, Ev ev, bool fused);
+hipError_t launch_shared(const moe_plan* p, const CallArgs& a, Ev ev);
+hipError_t launch_combine(const moe_plan* p, const CallArgs& a, Ev ev);
 
 }  // namespace qmoe

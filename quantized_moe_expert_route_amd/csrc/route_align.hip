@@ -3,9 +3,10 @@
 // Routing: "glm53: FP8 mid hand-off, early split rows, per-row up/gate jobs,
 // ..." (Modifications table, row "per-row up/gate jobs", and its commit):
 // top-8 by rounds, each round a wave maximum of the lane heads, a tie going
-// to the lower expert ID. Here a wave routes one token; every round is one
-// 64-bit wave maximum over keys (order-preserving logit bits, ~expert) so a
-// tie resolves to the lower ID inside the same compare.
+// to the lower expert ID. Here a wave routes one token: each round takes the
+// wave maximum of the lanes' best order-preserving logit keys (DPP within
+// rows, scalar reads across rows), then the wave minimum expert ID among the
+// lanes holding that key, so a tie resolves to the lower ID.
 //
 // x -> MXFP4 happens once per token in the same launch (the pages' frontend
 // converts activations next to the route sort: "IQ2R: load GLM-5.3 packed MoE
@@ -14,9 +15,12 @@
 // Sort: the entries (t, j) of each expert in ascending t, so each expert's
 // weights are read once for all its rows ("glm53_flash: Score a verify
 // request's index tiles once for its rows", commit "Run verify steps of up
-// to 16 rows": expert-major MoE). Route waves set bit t of expert e's row in
-// a bitmap; the align pass turns per-row prefix popcounts into each entry's
-// rank, which is deterministic and needs no ordering between waves.
+// to 16 rows": expert-major MoE). Every token sets bit t of its experts'
+// rows of a token bitmap; an entry's rank is the popcount of its row below t,
+// so the order is deterministic and needs no ordering between waves. Up to
+// 64 tokens the bitmap lives in LDS and one workgroup routes, quantizes and
+// sorts in a single launch; above that the route launch sets the bits in
+// global memory and a one-workgroup align launch ranks the entries.
 #include "common.h"
 #include "internal.h"
 
@@ -24,76 +28,75 @@
 
 namespace qmoe {
 
+// Top-k of one logits row by one wave. Lane j < k receives slot j's expert
+// and logit.
+// Keys of one logits row: lane l holds experts l + 64c; every real key is > 0.
 template <int EC>
-__global__ __launch_bounds__(256) void route_kernel(
-    const float* __restrict__ logits, const uint16_t* __restrict__ x, int M, int E, int k, int H,
-    float scaling, int* __restrict__ topk_ids, float* __restrict__ topk_w,
-    uint32_t* __restrict__ bitmap, int words, uint8_t* __restrict__ xq, uint8_t* __restrict__ xs) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int t = blockIdx.x * 4 + wave; t < M; t += gridDim.x * 4) {
-    // ---- top-k
-    uint64_t key[EC];
+__device__ __forceinline__ void load_keys(const float* __restrict__ row, int E, int lane, uint32_t (&key)[EC]) {
 #pragma unroll
-    for (int c = 0; c < EC; ++c) {
-      int e = lane + 64 * c;
-      key[c] = e < E ? ((uint64_t)order_key(logits[(size_t)t * E + e]) << 32) | (0xFFFFFFFFu - (uint32_t)e) : 0;
+  for (int c = 0; c < EC; ++c) key[c] = lane + 64 * c < E ? order_key(row[lane + 64 * c]) : 0u;
+}
+
+template <int EC>
+__device__ __forceinline__ void topk_wave(uint32_t (&key)[EC], int k, int lane, uint32_t& sel_e, float& sel_l) {
+  for (int j = 0; j < k; ++j) {
+    uint32_t bk = 0, bc = 0;
+#pragma unroll
+    for (int c = 0; c < EC; ++c)
+      if (key[c] > bk) {  // strict: the lowest index of equal keys stays
+        bk = key[c];
+        bc = (uint32_t)c;
+      }
+    const uint32_t kmax = wave_max_u32(bk);
+    const uint32_t win = wave_min_u32(bk == kmax ? (bc << 6) | (uint32_t)lane : 0xFFFFFFFFu);
+    if ((win & 63u) == (uint32_t)lane) {
+      const uint32_t wc = win >> 6;
+#pragma unroll
+      for (int c = 0; c < EC; ++c) key[c] = ((uint32_t)c == wc) ? 0u : key[c];
     }
-    uint32_t sel_e = 0;
-    float sel_l = 0.f;
-    for (int j = 0; j < k; ++j) {
-      uint64_t best = 0;
-#pragma unroll
-      for (int c = 0; c < EC; ++c) best = key[c] > best ? key[c] : best;
-      best = wave_max_u64(best);
-#pragma unroll
-      for (int c = 0; c < EC; ++c)
-        if (key[c] == best) key[c] = 0;
-      if (lane == j) {
-        sel_e = 0xFFFFFFFFu - (uint32_t)best;
-        sel_l = key_to_float((uint32_t)(best >> 32));
-      }
-    }
-    // ---- weights: sigmoid scores, renormalised over the k slots, scaled
-    float sig = 0.f;
-    if (lane < k) sig = (float)(1.0 / (1.0 + exp(-(double)sel_l)));
-    float S = 0.f;
-    for (int j = 0; j < k; ++j) S += __shfl(sig, j, 64);
-    if (lane < k) {
-      float w = __fdiv_rn(sig, S + 1e-20f) * scaling;
-      topk_ids[(size_t)t * k + lane] = (int)sel_e;
-      topk_w[(size_t)t * k + lane] = w;
-      atomicOr(&bitmap[(size_t)sel_e * words + (t >> 5)], 1u << (t & 31));
-    }
-    // ---- x -> MXFP4: per 32-block, E8M0 = floor(log2 amax) - 2, E2M1 RNE
-    const uint16_t* xr = x + (size_t)t * H;
-    const int nblk = H >> 5;
-    for (int b = lane; b < nblk; b += 64) {
-      uint32_t w32[16];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint4 v = ld16(xr + b * 32 + q * 8);
-        w32[4 * q + 0] = v.x; w32[4 * q + 1] = v.y; w32[4 * q + 2] = v.z; w32[4 * q + 3] = v.w;
-      }
-      uint32_t amax = 0;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        amax = max(amax, w32[i] & 0x7FFFu);
-        amax = max(amax, (w32[i] >> 16) & 0x7FFFu);
-      }
-      const uint32_t sc = mx_scale_code(amax);
-      const int sh = 127 - (int)sc;
-      uint32_t packed[4] = {0, 0, 0, 0};
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float f0 = ldexpf(__uint_as_float(w32[i] << 16), sh);
-        float f1 = ldexpf(__uint_as_float(w32[i] & 0xFFFF0000u), sh);
-        uint32_t byte = e2m1_code(f0) | (e2m1_code(f1) << 4);
-        packed[i >> 2] |= byte << (8 * (i & 3));
-      }
-      *reinterpret_cast<uint4*>(xq + (size_t)t * (H >> 1) + b * 16) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-      xs[(size_t)t * nblk + b] = (uint8_t)sc;
+    if (lane == j) {
+      sel_e = win;
+      sel_l = key_to_float(kmax);
     }
   }
+}
+
+// Sigmoid scores of the k selected logits (float64, one rounding), their
+// binary32 sum in slot order, w = fl32(fl32(s / (S + 1e-20)) * scaling).
+__device__ __forceinline__ float route_weight(float sel_l, int k, int lane, float scaling) {
+  float sig = 0.f;
+  if (lane < k) sig = (float)(1.0 / (1.0 + exp(-(double)sel_l)));
+  float S = 0.f;
+  for (int j = 0; j < k; ++j) S += __shfl(sig, j, 64);
+  return __fdiv_rn(sig, S + 1e-20f) * scaling;
+}
+
+// One 32-element block of a bf16 row -> 16 bytes of E2M1 + an E8M0 byte.
+__device__ __forceinline__ void quant_block_mx(const uint16_t* __restrict__ src, uint8_t* __restrict__ dq,
+                                               uint8_t* __restrict__ ds) {
+  uint32_t w32[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 v = ld16(src + q * 8);
+    w32[4 * q + 0] = v.x; w32[4 * q + 1] = v.y; w32[4 * q + 2] = v.z; w32[4 * q + 3] = v.w;
+  }
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    amax = max(amax, w32[i] & 0x7FFFu);
+    amax = max(amax, (w32[i] >> 16) & 0x7FFFu);
+  }
+  const uint32_t sc = mx_scale_code(amax);
+  const int sh = 127 - (int)sc;
+  uint32_t packed[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float f0 = ldexpf(__uint_as_float(w32[i] << 16), sh);
+    const float f1 = ldexpf(__uint_as_float(w32[i] & 0xFFFF0000u), sh);
+    packed[i >> 2] |= (e2m1_code(f0) | (e2m1_code(f1) << 4)) << (8 * (i & 3));
+  }
+  *reinterpret_cast<uint4*>(dq) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  *ds = (uint8_t)sc;
 }
 
 // Exclusive prefix over the block (blockDim.x == 1024): returns the prefix
@@ -126,6 +129,105 @@ __device__ int block_exclusive_scan(int v, int* s_tmp, int* total) {
   return r;
 }
 
+// Offsets, tiles of kTileRows sorted rows and meta from per-expert counts
+// (thread e holds count c of expert e). Leaves offsets in s_off.
+__device__ void write_offsets_tiles(int c, int E, int* s_off, int* s_tmp, int* __restrict__ count,
+                                    int* __restrict__ offset, int4* __restrict__ tiles, int* __restrict__ meta) {
+  const int tid = threadIdx.x;
+  const int nt = (c + kTileRows - 1) / kTileRows;
+  int total_rows, total_tiles;
+  const int off = block_exclusive_scan(c, s_tmp, &total_rows);
+  const int toff = block_exclusive_scan(nt, s_tmp, &total_tiles);
+  if (tid < E) {
+    count[tid] = c;
+    offset[tid] = off;
+    s_off[tid] = off;
+    for (int i = 0; i < nt; ++i) {
+      const int r0 = off + i * kTileRows;
+      tiles[toff + i] = make_int4(tid, r0, min(r0 + kTileRows, off + c), 0);
+    }
+  }
+  if (tid == 0) {
+    offset[E] = total_rows;
+    meta[0] = total_tiles;
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------- M <= 64
+template <int EC>
+__global__ __launch_bounds__(1024) void route_align_small_kernel(
+    const float* __restrict__ logits, const uint16_t* __restrict__ x, int M, int E, int k, int H, float scaling,
+    int* __restrict__ topk_ids, float* __restrict__ topk_w, int* __restrict__ count, int* __restrict__ offset,
+    int* __restrict__ sorted_entry, int4* __restrict__ tiles, int* __restrict__ meta, uint8_t* __restrict__ xq,
+    uint8_t* __restrict__ xs) {
+  __shared__ uint32_t s_mask[1024][2];  // expert -> tokens 0..63
+  __shared__ int s_ids[64 * 16];
+  __shared__ int s_off[1024];
+  __shared__ int s_tmp[64];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  for (int e = tid; e < E; e += 1024) s_mask[e][0] = s_mask[e][1] = 0u;
+  // the first token's logits are loaded before the x blocks so that both
+  // memory latencies overlap
+  uint32_t key[EC];
+  if (wave < M) load_keys<EC>(logits + (size_t)wave * E, E, lane, key);
+  // x -> MXFP4: one 32-block per thread per pass
+  const int nblk = H >> 5;
+  for (int bi = tid; bi < M * nblk; bi += 1024) {
+    const int t = bi / nblk, b = bi - t * nblk;
+    quant_block_mx(x + (size_t)t * H + b * 32, xq + (size_t)t * (H >> 1) + b * 16, xs + (size_t)t * nblk + b);
+  }
+  __syncthreads();
+  // top-k, one wave per token
+  for (int t = wave; t < M; t += 16) {
+    uint32_t sel_e = 0;
+    float sel_l = 0.f;
+    if (t != wave) load_keys<EC>(logits + (size_t)t * E, E, lane, key);
+    topk_wave<EC>(key, k, lane, sel_e, sel_l);
+    const float w = route_weight(sel_l, k, lane, scaling);
+    if (lane < k) {
+      topk_ids[t * k + lane] = (int)sel_e;
+      topk_w[t * k + lane] = w;
+      s_ids[t * k + lane] = (int)sel_e;
+      atomicOr(&s_mask[sel_e][t >> 5], 1u << (t & 31));
+    }
+  }
+  __syncthreads();
+  const int c = tid < E ? __popc(s_mask[tid][0]) + __popc(s_mask[tid][1]) : 0;
+  write_offsets_tiles(c, E, s_off, s_tmp, count, offset, tiles, meta);
+  for (int i = tid; i < M * k; i += 1024) {
+    const int e = s_ids[i], t = i / k;
+    const uint32_t lo = s_mask[e][0], hi = s_mask[e][1];
+    const int rank = t < 32 ? __popc(lo & ((1u << t) - 1u)) : __popc(lo) + __popc(hi & ((1u << (t - 32)) - 1u));
+    sorted_entry[s_off[e] + rank] = i;
+  }
+}
+
+// ---------------------------------------------------------------- M > 64
+template <int EC>
+__global__ __launch_bounds__(256) void route_kernel(
+    const float* __restrict__ logits, const uint16_t* __restrict__ x, int M, int E, int k, int H,
+    float scaling, int* __restrict__ topk_ids, float* __restrict__ topk_w,
+    uint32_t* __restrict__ bitmap, int words, uint8_t* __restrict__ xq, uint8_t* __restrict__ xs) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nblk = H >> 5;
+  for (int t = blockIdx.x * 4 + wave; t < M; t += gridDim.x * 4) {
+    uint32_t sel_e = 0;
+    float sel_l = 0.f;
+    uint32_t key[EC];
+    load_keys<EC>(logits + (size_t)t * E, E, lane, key);
+    topk_wave<EC>(key, k, lane, sel_e, sel_l);
+    const float w = route_weight(sel_l, k, lane, scaling);
+    if (lane < k) {
+      topk_ids[(size_t)t * k + lane] = (int)sel_e;
+      topk_w[(size_t)t * k + lane] = w;
+      atomicOr(&bitmap[(size_t)sel_e * words + (t >> 5)], 1u << (t & 31));
+    }
+    for (int b = lane; b < nblk; b += 64)
+      quant_block_mx(x + (size_t)t * H + b * 32, xq + (size_t)t * (H >> 1) + b * 16, xs + (size_t)t * nblk + b);
+  }
+}
+
 __global__ __launch_bounds__(1024) void align_kernel(
     const int* __restrict__ topk_ids, int M, int E, int k, uint32_t* __restrict__ bitmap,
     int* __restrict__ pre, int words, int* __restrict__ count, int* __restrict__ offset,
@@ -153,27 +255,8 @@ __global__ __launch_bounds__(1024) void align_kernel(
     if (lane == 0) s_cnt[e] = carry;
   }
   __syncthreads();
-  // 2. offsets and tiles of kTileRows sorted rows per expert
-  const int c = tid < E ? s_cnt[tid] : 0;
-  const int nt = (c + kTileRows - 1) / kTileRows;
-  int total_rows, total_tiles;
-  const int off = block_exclusive_scan(c, s_tmp, &total_rows);
-  const int toff = block_exclusive_scan(nt, s_tmp, &total_tiles);
-  if (tid < E) {
-    count[tid] = c;
-    offset[tid] = off;
-    s_off[tid] = off;
-    for (int i = 0; i < nt; ++i) {
-      const int r0 = off + i * kTileRows;
-      tiles[toff + i] = make_int4(tid, r0, min(r0 + kTileRows, off + c), 0);
-    }
-  }
-  if (tid == 0) {
-    offset[E] = total_rows;
-    meta[0] = total_tiles;
-  }
-  __syncthreads();
-  // 3. each entry's slot in its expert's run: rows of earlier tokens first
+  write_offsets_tiles(tid < E ? s_cnt[tid] : 0, E, s_off, s_tmp, count, offset, tiles, meta);
+  // each entry's slot in its expert's run: rows of earlier tokens first
   const int n = M * k;
   for (int i = tid; i < n; i += 1024) {
     const int e = topk_ids[i];
@@ -183,7 +266,7 @@ __global__ __launch_bounds__(1024) void align_kernel(
     sorted_entry[s_off[e] + rank] = i;
   }
   __syncthreads();
-  // 4. leave the bitmap zero for the next call
+  // leave the bitmap zero for the next call
   for (int i = tid; i < E * words; i += 1024) bitmap[i] = 0u;
 }
 
@@ -196,37 +279,48 @@ hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t s) {
   const size_t n16 = bytes / 16;
   if (n16 == 0) return hipSuccess;
   const int blocks = (int)std::min<size_t>((n16 + 255) / 256, 4096);
-  hipLaunchKernelGGL(zero_kernel, dim3(blocks), dim3(256), 0, s, reinterpret_cast<uint4*>(ptr), n16);
-  return hipGetLastError();
+  return launch_k(zero_kernel, dim3(blocks), dim3(256), 0, s, Ev{}, reinterpret_cast<uint4*>(ptr), n16);
 }
 
-hipError_t launch_route(const moe_plan* p, const CallArgs& a) {
+template <typename F>
+static hipError_t by_ec(int E, F&& f) {
+  const int ec = (E + 63) / 64;
+  if (ec <= 1) return f(std::integral_constant<int, 1>{});
+  if (ec <= 2) return f(std::integral_constant<int, 2>{});
+  if (ec <= 4) return f(std::integral_constant<int, 4>{});
+  if (ec <= 8) return f(std::integral_constant<int, 8>{});
+  return f(std::integral_constant<int, 16>{});
+}
+
+hipError_t launch_route_small(const moe_plan* p, const CallArgs& a, Ev ev) {
+  const int M = (int)a.M, E = (int)p->s.E, k = (int)p->s.top_k, H = (int)p->s.H;
+  return by_ec(E, [&](auto ec) {
+    return launch_k(route_align_small_kernel<decltype(ec)::value>, dim3(1), dim3(1024), 0, a.stream, ev, a.logits,
+                    reinterpret_cast<const uint16_t*>(a.x), M, E, k, H, p->s.routed_scaling,
+                    wsp<int>(p, p->L.topk_ids), wsp<float>(p, p->L.topk_w), wsp<int>(p, p->L.count),
+                    wsp<int>(p, p->L.offset), wsp<int>(p, p->L.sorted_entry), wsp<int4>(p, p->X.tiles),
+                    wsp<int>(p, p->X.meta), wsp<uint8_t>(p, p->L.xq), wsp<uint8_t>(p, p->L.xs));
+  });
+}
+
+hipError_t launch_route(const moe_plan* p, const CallArgs& a, Ev ev) {
   const int M = (int)a.M, E = (int)p->s.E, k = (int)p->s.top_k, H = (int)p->s.H;
   const int blocks = (int)std::min<int64_t>((a.M + 3) / 4, 2048);
   const int words = (int)((a.M + 31) / 32);
-  auto args = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, a.stream, a.logits,
-                       reinterpret_cast<const uint16_t*>(a.x), M, E, k, H, p->s.routed_scaling,
-                       wsp<int>(p, p->L.topk_ids), wsp<float>(p, p->L.topk_w),
-                       wsp<uint32_t>(p, p->X.bitmap), words, wsp<uint8_t>(p, p->L.xq),
-                       wsp<uint8_t>(p, p->L.xs));
-  };
-  const int ec = (E + 63) / 64;
-  if (ec <= 1) args(route_kernel<1>);
-  else if (ec <= 2) args(route_kernel<2>);
-  else if (ec <= 4) args(route_kernel<4>);
-  else if (ec <= 8) args(route_kernel<8>);
-  else args(route_kernel<16>);
-  return hipGetLastError();
+  return by_ec(E, [&](auto ec) {
+    return launch_k(route_kernel<decltype(ec)::value>, dim3(blocks), dim3(256), 0, a.stream, ev, a.logits,
+                    reinterpret_cast<const uint16_t*>(a.x), M, E, k, H, p->s.routed_scaling,
+                    wsp<int>(p, p->L.topk_ids), wsp<float>(p, p->L.topk_w), wsp<uint32_t>(p, p->X.bitmap), words,
+                    wsp<uint8_t>(p, p->L.xq), wsp<uint8_t>(p, p->L.xs));
+  });
 }
 
-hipError_t launch_align(const moe_plan* p, const CallArgs& a) {
+hipError_t launch_align(const moe_plan* p, const CallArgs& a, Ev ev) {
   const int words = (int)((a.M + 31) / 32);
-  hipLaunchKernelGGL(align_kernel, dim3(1), dim3(1024), 0, a.stream, wsp<int>(p, p->L.topk_ids),
-                     (int)a.M, (int)p->s.E, (int)p->s.top_k, wsp<uint32_t>(p, p->X.bitmap),
-                     wsp<int>(p, p->X.pre), words, wsp<int>(p, p->L.count), wsp<int>(p, p->L.offset),
-                     wsp<int>(p, p->L.sorted_entry), wsp<int4>(p, p->X.tiles), wsp<int>(p, p->X.meta));
-  return hipGetLastError();
+  return launch_k(align_kernel, dim3(1), dim3(1024), 0, a.stream, ev, wsp<int>(p, p->L.topk_ids), (int)a.M,
+                  (int)p->s.E, (int)p->s.top_k, wsp<uint32_t>(p, p->X.bitmap), wsp<int>(p, p->X.pre), words,
+                  wsp<int>(p, p->L.count), wsp<int>(p, p->L.offset), wsp<int>(p, p->L.sorted_entry),
+                  wsp<int4>(p, p->X.tiles), wsp<int>(p, p->X.meta));
 }
 
 }  // namespace qmoe

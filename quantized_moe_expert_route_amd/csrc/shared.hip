@@ -149,23 +149,26 @@ __global__ __launch_bounds__(256) void sh_act_quant_kernel(const float* __restri
   }
 }
 
-hipError_t launch_shared(const moe_plan* p, const CallArgs& a) {
+hipError_t launch_shared(const moe_plan* p, const CallArgs& a, Ev ev) {
   if (p->s.shared_I == 0) return hipSuccess;
   const int M = (int)a.M, H = (int)p->s.H, Is = (int)p->s.shared_I;
   auto blocks_for = [](int64_t waves, int64_t cap) { return (int)std::min<int64_t>((waves + 3) / 4, cap); };
-  hipLaunchKernelGGL(sh_quant_x_kernel, dim3(blocks_for((int64_t)M * (H / 128), 8192)), dim3(256), 0, a.stream,
-                     reinterpret_cast<const uint16_t*>(a.x), M, H, wsp<uint8_t>(p, p->L.sh_xq), wsp<float>(p, p->L.sh_xs));
+  hipError_t e = launch_k(sh_quant_x_kernel, dim3(blocks_for((int64_t)M * (H / 128), 8192)), dim3(256), 0, a.stream,
+                          Ev{ev.start, nullptr}, reinterpret_cast<const uint16_t*>(a.x), M, H,
+                          wsp<uint8_t>(p, p->L.sh_xq), wsp<float>(p, p->L.sh_xs));
+  if (e != hipSuccess) return e;
   const int64_t t1 = (int64_t)((M + 15) / 16) * (Is / 16);
-  hipLaunchKernelGGL(sh_linear_kernel<true>, dim3(blocks_for(t1, 8192)), dim3(256), 0, a.stream,
-                     wsp<uint8_t>(p, p->L.sh_xq), wsp<float>(p, p->L.sh_xs), reinterpret_cast<const uint8_t*>(p->ws13),
-                     p->ss13, M, H, 2 * Is, wsp<float>(p, p->X.sh_h));
-  hipLaunchKernelGGL(sh_act_quant_kernel, dim3(blocks_for((int64_t)M * (Is / 128), 8192)), dim3(256), 0, a.stream,
-                     wsp<float>(p, p->X.sh_h), M, Is, wsp<uint8_t>(p, p->L.sh_hq), wsp<float>(p, p->L.sh_hs));
+  e = launch_k(sh_linear_kernel<true>, dim3(blocks_for(t1, 8192)), dim3(256), 0, a.stream, Ev{},
+               wsp<uint8_t>(p, p->L.sh_xq), wsp<float>(p, p->L.sh_xs), reinterpret_cast<const uint8_t*>(p->ws13),
+               p->ss13, M, H, 2 * Is, wsp<float>(p, p->X.sh_h));
+  if (e != hipSuccess) return e;
+  e = launch_k(sh_act_quant_kernel, dim3(blocks_for((int64_t)M * (Is / 128), 8192)), dim3(256), 0, a.stream, Ev{},
+               wsp<float>(p, p->X.sh_h), M, Is, wsp<uint8_t>(p, p->L.sh_hq), wsp<float>(p, p->L.sh_hs));
+  if (e != hipSuccess) return e;
   const int64_t t2 = (int64_t)((M + 15) / 16) * (H / 16);
-  hipLaunchKernelGGL(sh_linear_kernel<false>, dim3(blocks_for(t2, 8192)), dim3(256), 0, a.stream,
-                     wsp<uint8_t>(p, p->L.sh_hq), wsp<float>(p, p->L.sh_hs), reinterpret_cast<const uint8_t*>(p->ws2),
-                     p->ss2, M, Is, H, wsp<float>(p, p->L.sh_y));
-  return hipGetLastError();
+  return launch_k(sh_linear_kernel<false>, dim3(blocks_for(t2, 8192)), dim3(256), 0, a.stream, Ev{nullptr, ev.stop},
+                  wsp<uint8_t>(p, p->L.sh_hq), wsp<float>(p, p->L.sh_hs), reinterpret_cast<const uint8_t*>(p->ws2),
+                  p->ss2, M, Is, H, wsp<float>(p, p->L.sh_y));
 }
 
 }  // namespace qmoe

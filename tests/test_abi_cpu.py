@@ -36,7 +36,7 @@ def test_status_strings_and_stages():
     assert B.status_str(B.MOE_OK) == "ok"
     for st in range(1, 6):
         assert B.status_str(st) and B.status_str(st) != "ok"
-    assert B.stage_names() == ["route", "align", "gate_up", "act_quant", "down", "shared", "combine"]
+    assert B.stage_names() == ["route", "align", "gate_up", "act_quant", "shared", "down", "combine"]
     assert B.lib().moe_stage_name(99) is None
 
 
