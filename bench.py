@@ -130,14 +130,14 @@ def measure(name, steps, warmup, n_sets):
     for i in range(warmup):
         x.copy_(sets[i % n_sets][0])
         logits.copy_(sets[i % n_sets][1])
-        torch.sum(flush, out=sink)
+        torch.sum(flush, 0, out=sink)
         graph.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         x.copy_(sets[i % n_sets][0])
         logits.copy_(sets[i % n_sets][1])
-        torch.sum(flush, out=sink)
+        torch.sum(flush, 0, out=sink)
         ev0[i].record()
         graph.replay()
         ev1[i].record()
@@ -167,7 +167,7 @@ def measure(name, steps, warmup, n_sets):
     for i in range(steps):
         x.copy_(sets[i % n_sets][0])
         logits.copy_(sets[i % n_sets][1])
-        torch.sum(flush, out=sink)
+        torch.sum(flush, 0, out=sink)
         call()
         torch.cuda.synchronize()
         for j in range(len(names)):
