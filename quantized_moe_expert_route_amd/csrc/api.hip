@@ -32,7 +32,7 @@ moe_status check_shape(const moe_shape* s) {
 struct Layout {
   moe_ws_layout L;
   Internal X;
-  int64_t t16, words;
+  int64_t t16, tb, words;
 };
 
 Layout make_layout(const moe_shape& s) {
@@ -42,6 +42,7 @@ Layout make_layout(const moe_shape& s) {
   const size_t Is = (size_t)s.shared_I;
   const size_t n = M * k;
   r.t16 = (int64_t)((n + std::min(E, n) * (kTileRows - 1) + kTileRows - 1) / kTileRows);
+  r.tb = (int64_t)((n + std::min(E, n) * (kBigRows - 1) + kBigRows - 1) / kBigRows);
   r.words = (int64_t)((M + 31) / 32);
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -57,6 +58,8 @@ Layout make_layout(const moe_shape& s) {
   r.L.sorted_entry = take(4 * n);
   r.X.tiles = take(16 * (size_t)r.t16);
   r.X.meta = take(256);
+  r.X.gu_items = take(16 * (size_t)r.tb * (I / 128));
+  r.X.dn_items = take(16 * (size_t)r.tb * (H / kDownCols));
   // counters and the token bitmap: zeroed when the workspace is bound, and
   // left zero by every call
   r.X.bitmap = take(4 * E * (size_t)r.words);
@@ -166,6 +169,7 @@ moe_status moe_plan_create(const moe_shape* shape, moe_plan** out) {
   p->X = lay.X;
   p->t16_max = lay.t16;
   p->words = lay.words;
+  p->tb_max = lay.tb;
   *out = p;
   return MOE_OK;
 }
@@ -262,14 +266,16 @@ moe_status moe_forward(moe_plan* plan, int64_t M, const void* x, const float* lo
   // mid quantization or the combine into the producing launch needs a
   // device-scope release/acquire per workgroup, which writes back and
   // invalidates a whole L2 of an XCD each time and costs more than a launch.
+  // Above kSmallM, gate/up runs on 128-row tiles with the mid quantization
+  // inside (every item owns whole mid blocks).
   const bool small = M <= kSmallM;
   const bool fuse = false;
   hipError_t e = small ? launch_route_small(plan, a, ev[0]) : launch_route(plan, a, ev[0]);
   if (e == hipSuccess) e = small ? none(1) : launch_align(plan, a, ev[1]);
-  if (e == hipSuccess) e = launch_gate_up(plan, a, ev[2], fuse);
-  if (e == hipSuccess) e = fuse ? none(3) : launch_act_quant(plan, a, ev[3]);
+  if (e == hipSuccess) e = small ? launch_gate_up(plan, a, ev[2], fuse) : launch_gate_up_big(plan, a, ev[2]);
+  if (e == hipSuccess) e = (fuse || !small) ? none(3) : launch_act_quant(plan, a, ev[3]);
   if (e == hipSuccess) e = plan->s.shared_I > 0 ? launch_shared(plan, a, ev[4]) : none(4);
-  if (e == hipSuccess) e = launch_down(plan, a, ev[5], fuse);
+  if (e == hipSuccess) e = small ? launch_down(plan, a, ev[5], fuse) : launch_down_big(plan, a, ev[5]);
   if (e == hipSuccess) e = fuse ? none(6) : launch_combine(plan, a, ev[6]);
   return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

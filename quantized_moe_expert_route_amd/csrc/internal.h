@@ -11,12 +11,16 @@
 
 namespace qmoe {
 
-constexpr int kTileRows = 16;  // sorted rows per tile of the token-dimension tiling
+constexpr int kTileRows = 16;  // sorted rows per tile of the small-token kernels
+constexpr int kBigRows = 128;  // sorted rows per tile of the large-token kernels
+constexpr int kDownCols = 128; // output columns per down work item of the large-token kernel
 
 // Workspace regions beyond the public layout.
 struct Internal {
   size_t tiles;    // int4 [T16]: {expert, row_begin, row_end, 0}
-  size_t meta;     // int32 [64]: meta[0] = number of tiles
+  size_t meta;     // int32 [64]: meta[0] tiles, meta[1] gate/up items, meta[2] down items
+  size_t gu_items; // int4 [TB * I/128]: {expert, row_begin, row_end, column block}, large M
+  size_t dn_items; // int4 [TB * H/kDownCols]: {expert, row_begin, row_end, column chunk}, large M
   size_t bitmap;   // uint32 [E, ceil(M/32)]: bit t of row e = token t picked e; zero between calls
   size_t pre;      // int32 [E, ceil(M/32)]: entries of row e before word w
   size_t h;        // fp32 [n, I]: SiLU(gate)*up, rows in sorted order
@@ -34,6 +38,7 @@ struct moe_plan {
   int64_t n_max;   // M * top_k
   int64_t t16_max; // upper bound on tiles of 16 sorted rows
   int64_t words;   // ceil(M / 32)
+  int64_t tb_max;  // upper bound on tiles of kBigRows sorted rows
   moe_ws_layout L;
   qmoe::Internal X;
   uint8_t* ws;
@@ -93,6 +98,9 @@ hipError_t launch_act_quant(const moe_plan* p, const CallArgs& a, Ev ev);
 // fused = combine done by the last slot of each (token, 256-column chunk)
 hipError_t launch_down(const moe_plan* p, const CallArgs& a, Ev ev, bool fused);
 hipError_t launch_shared(const moe_plan* p, const CallArgs& a, Ev ev);
+// large M: LDS-staged 128-row tiles; gate/up includes the mid quantization
+hipError_t launch_gate_up_big(const moe_plan* p, const CallArgs& a, Ev ev);
+hipError_t launch_down_big(const moe_plan* p, const CallArgs& a, Ev ev);
 hipError_t launch_combine(const moe_plan* p, const CallArgs& a, Ev ev);
 
 }  // namespace qmoe

@@ -228,10 +228,39 @@ __global__ __launch_bounds__(256) void route_kernel(
   }
 }
 
+// Work items of the large-token GEMMs, per expert in the order (column
+// block, row tile) so that the row tiles sharing a weight block are adjacent.
+__device__ void write_big_items(int c, int E, int n_iblk, int n_nc, int* s_tmp, int4* __restrict__ gu_items,
+                                int4* __restrict__ dn_items, int* __restrict__ meta) {
+  const int tid = threadIdx.x;
+  const int nt = (c + kBigRows - 1) / kBigRows;
+  int total_rows, total_tiles;
+  const int off = block_exclusive_scan(c, s_tmp, &total_rows);
+  const int toff = block_exclusive_scan(nt, s_tmp, &total_tiles);
+  if (tid < E) {
+    for (int b = 0; b < n_iblk; ++b)
+      for (int i = 0; i < nt; ++i) {
+        const int r0 = off + i * kBigRows;
+        gu_items[toff * n_iblk + b * nt + i] = make_int4(tid, r0, min(r0 + kBigRows, off + c), b);
+      }
+    for (int b = 0; b < n_nc; ++b)
+      for (int i = 0; i < nt; ++i) {
+        const int r0 = off + i * kBigRows;
+        dn_items[toff * n_nc + b * nt + i] = make_int4(tid, r0, min(r0 + kBigRows, off + c), b);
+      }
+  }
+  if (tid == 0) {
+    meta[1] = total_tiles * n_iblk;
+    meta[2] = total_tiles * n_nc;
+  }
+  __syncthreads();
+}
+
 __global__ __launch_bounds__(1024) void align_kernel(
     const int* __restrict__ topk_ids, int M, int E, int k, uint32_t* __restrict__ bitmap,
     int* __restrict__ pre, int words, int* __restrict__ count, int* __restrict__ offset,
-    int* __restrict__ sorted_entry, int4* __restrict__ tiles, int* __restrict__ meta) {
+    int* __restrict__ sorted_entry, int4* __restrict__ tiles, int* __restrict__ meta, int n_iblk, int n_nc,
+    int4* __restrict__ gu_items, int4* __restrict__ dn_items) {
   __shared__ int s_cnt[1024];
   __shared__ int s_off[1024];
   __shared__ int s_tmp[64];
@@ -256,6 +285,7 @@ __global__ __launch_bounds__(1024) void align_kernel(
   }
   __syncthreads();
   write_offsets_tiles(tid < E ? s_cnt[tid] : 0, E, s_off, s_tmp, count, offset, tiles, meta);
+  write_big_items(tid < E ? s_cnt[tid] : 0, E, n_iblk, n_nc, s_tmp, gu_items, dn_items, meta);
   // each entry's slot in its expert's run: rows of earlier tokens first
   const int n = M * k;
   for (int i = tid; i < n; i += 1024) {
@@ -320,7 +350,8 @@ hipError_t launch_align(const moe_plan* p, const CallArgs& a, Ev ev) {
   return launch_k(align_kernel, dim3(1), dim3(1024), 0, a.stream, ev, wsp<int>(p, p->L.topk_ids), (int)a.M,
                   (int)p->s.E, (int)p->s.top_k, wsp<uint32_t>(p, p->X.bitmap), wsp<int>(p, p->X.pre), words,
                   wsp<int>(p, p->L.count), wsp<int>(p, p->L.offset), wsp<int>(p, p->L.sorted_entry),
-                  wsp<int4>(p, p->X.tiles), wsp<int>(p, p->X.meta));
+                  wsp<int4>(p, p->X.tiles), wsp<int>(p, p->X.meta), (int)(p->s.I / 128),
+                  (int)(p->s.H / kDownCols), wsp<int4>(p, p->X.gu_items), wsp<int4>(p, p->X.dn_items));
 }
 
 }  // namespace qmoe

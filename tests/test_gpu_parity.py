@@ -127,6 +127,12 @@ SMALL = [
     (40, 1024, 32, 256, 4, "zipf", 0),         # skew: one expert takes most tokens
     (3, 512, 4, 128, 2, "normal", 128),        # shared expert
     (20, 512, 1024, 128, 16, "uniform", 0),    # largest E and k
+    # above 64 tokens: 128-row tiles, mid quantization inside gate/up
+    (65, 512, 16, 128, 2, "normal", 0),        # one token past the small path
+    (130, 1024, 32, 256, 8, "zipf", 0),        # skewed: a tile of 128 plus ragged tails
+    (300, 512, 8, 512, 2, "normal", 0),        # several full tiles per expert, I = 512
+    (96, 512, 64, 384, 8, "ties", 0),
+    (70, 512, 4, 128, 2, "normal", 128),       # with the shared expert
 ]
 
 
@@ -238,3 +244,23 @@ def test_graph_replay_matches_eager():
         assert torch.equal(out, eager), f"replay {i} differs from the eager call"
         plan.forward(g["x"], g["logits"], g["w13"], g["s13"], g["w2"], g["s2"], eager)  # eager work between
         torch.cuda.synchronize()
+
+
+def test_variable_m_across_paths_one_plan():
+    """One plan, calls alternating between the small-token and large-token paths."""
+    base = X.Shape(M=300, H=512, E=16, I=256, top_k=4)
+    plan = make_plan(base)
+    w = X.make_inputs(base, "normal", 31)
+    import torch
+
+    for it, M in enumerate([70, 4, 300, 65, 64, 128, 1]):
+        shape = X.Shape(M=M, H=512, E=16, I=256, top_k=4)
+        d = X.make_inputs(shape, "zipf" if it % 2 else "normal", 900 + it, with_weights=False)
+        for key in ("w13", "s13", "w2", "s2"):
+            d[key] = w[key]
+        g = upload(d)
+        gout, gi = run(d, plan=plan, g=g, M=M)
+        ref = oracle(d)
+        _check_routing(gi, ref["ids"], ref["w"], ref["count"], ref["offset"], ref["sorted_entry"])
+        _check_mid(gi["midq"], gi["mids"], ref["midq"], ref["mids"])
+        assert np.array_equal(gout, ref["out"]), f"M={M}: output differs"
