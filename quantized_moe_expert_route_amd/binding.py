@@ -195,12 +195,19 @@ class HipEvents:
         self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self._hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self._hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.handles = []
         for _ in range(n):
             h = ctypes.c_void_p()
             if self._hip.hipEventCreate(ctypes.byref(h)) != 0:
                 raise RuntimeError("hipEventCreate failed")
             self.handles.append(h.value)
+
+    def record(self, i: int, stream) -> None:
+        """Record event i on a torch stream (or a raw hipStream_t)."""
+        h = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+        if self._hip.hipEventRecord(self.handles[i], h) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def elapsed_ms(self, i: int, j: int) -> float:
         self._hip.hipEventSynchronize(self.handles[j])

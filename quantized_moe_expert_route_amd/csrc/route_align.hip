@@ -230,28 +230,43 @@ __global__ __launch_bounds__(256) void route_kernel(
 
 // Work items of the large-token GEMMs, per expert in the order (column
 // block, row tile) so that the row tiles sharing a weight block are adjacent.
-__device__ void write_big_items(int c, int E, int n_iblk, int n_nc, int* s_tmp, int4* __restrict__ gu_items,
-                                int4* __restrict__ dn_items, int* __restrict__ meta) {
+// Thread per item: the expert is found by binary search of the tile prefix.
+__device__ void write_big_items(int c, int E, int n_iblk, int n_nc, int* s_toff, int* s_off, int* s_tmp,
+                                int4* __restrict__ gu_items, int4* __restrict__ dn_items, int* __restrict__ meta) {
   const int tid = threadIdx.x;
   const int nt = (c + kBigRows - 1) / kBigRows;
   int total_rows, total_tiles;
   const int off = block_exclusive_scan(c, s_tmp, &total_rows);
   const int toff = block_exclusive_scan(nt, s_tmp, &total_tiles);
   if (tid < E) {
-    for (int b = 0; b < n_iblk; ++b)
-      for (int i = 0; i < nt; ++i) {
-        const int r0 = off + i * kBigRows;
-        gu_items[toff * n_iblk + b * nt + i] = make_int4(tid, r0, min(r0 + kBigRows, off + c), b);
-      }
-    for (int b = 0; b < n_nc; ++b)
-      for (int i = 0; i < nt; ++i) {
-        const int r0 = off + i * kBigRows;
-        dn_items[toff * n_nc + b * nt + i] = make_int4(tid, r0, min(r0 + kBigRows, off + c), b);
-      }
+    s_toff[tid] = toff;
+    s_off[tid] = off;
   }
   if (tid == 0) {
+    s_toff[E] = total_tiles;
+    s_off[E] = total_rows;
     meta[1] = total_tiles * n_iblk;
     meta[2] = total_tiles * n_nc;
+  }
+  __syncthreads();
+  for (int pass = 0; pass < 2; ++pass) {
+    const int nb = pass == 0 ? n_iblk : n_nc;
+    int4* out = pass == 0 ? gu_items : dn_items;
+    for (int i = tid; i < total_tiles * nb; i += blockDim.x) {
+      const int tile = i / nb;  // items of expert e occupy [toff[e] * nb, toff[e + 1] * nb)
+      int lo = 0, hi = E;       // largest e with toff[e] <= tile and a tile of its own
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_toff[mid] <= tile) lo = mid; else hi = mid;
+      }
+      int e = lo;
+      while (s_toff[e + 1] == s_toff[e]) ++e;  // skip experts without tiles
+      const int nte = s_toff[e + 1] - s_toff[e];
+      const int local = i - s_toff[e] * nb;
+      const int b = local / nte, mt = local - b * nte;
+      const int r0 = s_off[e] + mt * kBigRows;
+      out[i] = make_int4(e, r0, min(r0 + kBigRows, s_off[e + 1]), b);
+    }
   }
   __syncthreads();
 }
@@ -263,6 +278,8 @@ __global__ __launch_bounds__(1024) void align_kernel(
     int4* __restrict__ gu_items, int4* __restrict__ dn_items) {
   __shared__ int s_cnt[1024];
   __shared__ int s_off[1024];
+  __shared__ int s_toff2[1025];
+  __shared__ int s_off2[1025];
   __shared__ int s_tmp[64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // 1. per expert row: prefix popcount of each bitmap word, and the row total
@@ -285,7 +302,7 @@ __global__ __launch_bounds__(1024) void align_kernel(
   }
   __syncthreads();
   write_offsets_tiles(tid < E ? s_cnt[tid] : 0, E, s_off, s_tmp, count, offset, tiles, meta);
-  write_big_items(tid < E ? s_cnt[tid] : 0, E, n_iblk, n_nc, s_tmp, gu_items, dn_items, meta);
+  write_big_items(tid < E ? s_cnt[tid] : 0, E, n_iblk, n_nc, s_toff2, s_off2, s_tmp, gu_items, dn_items, meta);
   // each entry's slot in its expert's run: rows of earlier tokens first
   const int n = M * k;
   for (int i = tid; i < n; i += 1024) {
