@@ -148,6 +148,10 @@ moe_status moe_plan_set_stage_events(moe_plan* plan, void* const* events, int n)
 int moe_stage_count(void);
 const char* moe_stage_name(int i);
 
+/* Kernels that stage `stage` launches for a call of M tokens on this plan
+ * (0 when the stage is folded into another one), or -1 for bad arguments. */
+int moe_plan_stage_launches(const moe_plan* plan, int64_t M, int stage);
+
 /* Static text for a status code. */
 const char* moe_status_str(moe_status status);
 

@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
     L.moe_plan_set_shared.argtypes = [vp, vp, vp, vp, vp]
     L.moe_plan_set_stage_events.restype = st
     L.moe_plan_set_stage_events.argtypes = [vp, ctypes.POINTER(vp), ctypes.c_int]
+    L.moe_plan_stage_launches.restype = ctypes.c_int
+    L.moe_plan_stage_launches.argtypes = [vp, i64, ctypes.c_int]
     L.moe_forward.restype = st
     L.moe_forward.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp]
     _lib = L
@@ -162,6 +164,10 @@ class Plan:
         if st != MOE_OK:
             raise MoeError(st, "moe_forward")
         return out
+
+    def stage_launches(self, M: int):
+        """Kernels each stage launches for a call of M tokens."""
+        return [lib().moe_plan_stage_launches(self._h, int(M), i) for i in range(lib().moe_stage_count())]
 
     def view(self, name: str, dtype, shape):
         """A torch view of an intermediate inside the workspace (see moe_ws_layout)."""

@@ -135,6 +135,21 @@ const char* moe_status_str(moe_status st) {
 
 int moe_stage_count(void) { return kStages; }
 
+int moe_plan_stage_launches(const moe_plan* plan, int64_t M, int stage) {
+  if (!plan || M < 0 || M > plan->s.M || stage < 0 || stage >= kStages) return -1;
+  if (M == 0) return 0;
+  const bool small = M <= kSmallM;
+  switch (stage) {
+    case 0: return 1;                             // route (+ sort + x quantization when small)
+    case 1: return small ? 0 : 1;                 // align
+    case 2: return 1;                             // gate_up (+ mid quantization when large)
+    case 3: return small ? 1 : 0;                 // act_quant
+    case 4: return plan->s.shared_I > 0 ? 4 : 0;  // shared expert
+    case 5: return 1;                             // down
+    default: return 1;                            // combine
+  }
+}
+
 const char* moe_stage_name(int i) { return (i >= 0 && i < kStages) ? kStageNames[i] : nullptr; }
 
 moe_status moe_shape_workspace_bytes(const moe_shape* shape, size_t* bytes) {

@@ -20,16 +20,7 @@
 namespace qmoe {
 
 constexpr int kBM = kBigRows;  // 128 sorted rows per tile
-constexpr int kLD = 80;        // LDS bytes per row of a 64-byte K-step slice (+16 pad)
 
-struct GuSmem {
-  uint8_t a[2][kBM * kLD];      // x rows (MXFP4), K-step slice
-  uint8_t b[2][256 * kLD];      // 128 gate + 128 up weight rows
-  uint32_t as[2][kBM];          // 4 E8M0 bytes per row per K-step
-  uint32_t bs[2][256];
-  int tok[kBM];
-  float red[2][kBM];            // row amax of the two column halves
-};
 
 // Item order inside an XCD-contiguous run: workgroup b handles items
 // first(b), first(b) + stride, ... of the run of its XCD.
@@ -43,11 +34,38 @@ __device__ __forceinline__ void xcd_run(int n_items, int& first, int& stride, in
   end = min(n_items, (x + 1) * run);
 }
 
+// Workgroup barrier that orders LDS only: the fences are limited to the
+// local address space, so the barrier does not wait for the wave's global
+// loads still in flight (a plain __syncthreads() waits for all of them).
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+constexpr int kLDG = 80;  // LDS bytes per row of a 64-byte K-step slice (+16 pad)
+
+struct GuSmem {
+  uint8_t a[2][kBM * kLDG];   // x rows (MXFP4), K-step slice
+  uint8_t b[2][256 * kLDG];   // 128 gate + 128 up weight rows
+  uint32_t as[2][kBM];        // 4 E8M0 bytes per row per K-step
+  uint32_t bs[2][256];
+};
+
+// One K-step of global data held in registers: 2 + 4 16-byte chunks and the
+// scale dwords of this thread.
+struct GuRegs {
+  uint4 a[2], b[4];
+  uint32_t sa, sb;
+};
+
 __global__ __launch_bounds__(256) void gate_up_big_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const uint8_t* __restrict__ w13,
     const uint8_t* __restrict__ s13, const int* __restrict__ sorted_entry, const int4* __restrict__ items,
     const int* __restrict__ meta, int H, int I, int k, uint8_t* __restrict__ midq, float* __restrict__ mids) {
   __shared__ GuSmem sm;
+  __shared__ int tok[kBM];
+  __shared__ float red[2][kBM];  // row amax of the two column halves
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave & 1, wn = wave >> 1;
   const int r = lane & 15, g = lane >> 4;
@@ -59,46 +77,52 @@ __global__ __launch_bounds__(256) void gate_up_big_kernel(
     const int4 item = items[it];
     const int e = item.x, r0 = item.y, r1 = item.z, ib = item.w;
     const int rows = r1 - r0;
-    if (tid < kBM) sm.tok[tid] = tid < rows ? sorted_entry[r0 + tid] / k : -1;
+    if (tid < kBM) tok[tid] = tid < rows ? sorted_entry[r0 + tid] / k : -1;
     __syncthreads();
-    // global -> register staging of one K-step: A 2 chunks, B 4 chunks, 1 scale dword each
-    uint4 ra[2], rb[4];
-    uint32_t rsa = 0x7F7F7F7Fu, rsb = 0;
-    auto load = [&](int kk) {
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int idx = tid + 256 * q, row = idx >> 2, c = idx & 3;
-        const int t = sm.tok[row];
-        ra[q] = t >= 0 ? ld16(xq + (size_t)t * Hb + kk * 64 + 16 * c) : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int idx = tid + 256 * q, rr = idx >> 2, c = idx & 3;
-        const size_t wrow = (size_t)e * 2 * I + (rr < 128 ? 128 * ib + rr : I + 128 * ib + rr - 128);
-        rb[q] = ld16(w13 + wrow * Hb + kk * 64 + 16 * c);
-      }
-      if (tid < kBM) {
-        const int t = sm.tok[tid];
-        rsa = t >= 0 ? ld4(xs + (size_t)t * Hs + kk * 4) : 0x7F7F7F7Fu;
-      }
-      {
-        const size_t wrow = (size_t)e * 2 * I + (tid < 128 ? 128 * ib + tid : I + 128 * ib + tid - 128);
-        rsb = ld4(s13 + wrow * Hs + kk * 4);
-      }
+    auto wrow = [&](int rr) {
+      return (size_t)e * 2 * I + (rr < 128 ? 128 * ib + rr : I + 128 * ib + rr - 128);
     };
-    auto store = [&](int s) {
+    // This thread's global addresses do not change between K-steps. Every
+    // load is unconditional (rows past the tile read row 0, whose results for
+    // those rows are never written), so the number of loads in flight is the
+    // same on every path and the waits before each store stay exact.
+    const int tok0 = tok[0];
+    const uint8_t* pa[2];
+    const uint8_t* pb[4];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int idx = tid + 256 * q, t = tok[idx >> 2];
+      pa[q] = xq + (size_t)(t >= 0 ? t : tok0) * Hb + 16 * (idx & 3);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int idx = tid + 256 * q;
+      pb[q] = w13 + wrow(idx >> 2) * Hb + 16 * (idx & 3);
+    }
+    const int ts = tok[tid & (kBM - 1)];
+    const uint8_t* psa = xs + (size_t)(ts >= 0 ? ts : tok0) * Hs;
+    const uint8_t* psb = s13 + wrow(tid) * Hs;
+    auto load = [&](int kk, GuRegs& R) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) R.a[q] = ld16(pa[q] + kk * 64);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) R.b[q] = ld16(pb[q] + kk * 64);
+      R.sa = ld4(psa + kk * 4);
+      R.sb = ld4(psb + kk * 4);
+    };
+    auto store = [&](const GuRegs& R, int s) {
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int idx = tid + 256 * q;
-        *reinterpret_cast<uint4*>(&sm.a[s][(idx >> 2) * kLD + 16 * (idx & 3)]) = ra[q];
+        *reinterpret_cast<uint4*>(&sm.a[s][(idx >> 2) * kLDG + 16 * (idx & 3)]) = R.a[q];
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int idx = tid + 256 * q;
-        *reinterpret_cast<uint4*>(&sm.b[s][(idx >> 2) * kLD + 16 * (idx & 3)]) = rb[q];
+        *reinterpret_cast<uint4*>(&sm.b[s][(idx >> 2) * kLDG + 16 * (idx & 3)]) = R.b[q];
       }
-      if (tid < kBM) sm.as[s][tid] = rsa;
-      sm.bs[s][tid] = rsb;
+      if (tid < kBM) sm.as[s][tid] = R.sa;
+      sm.bs[s][tid] = R.sb;
     };
     v4f accg[4][4], accu[4][4];
 #pragma unroll
@@ -108,25 +132,20 @@ __global__ __launch_bounds__(256) void gate_up_big_kernel(
         accg[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
         accu[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
       }
-    load(0);
-    store(0);
-    __syncthreads();
-    for (int kk = 0; kk < nk; ++kk) {
-      const int s = kk & 1;
-      if (kk + 1 < nk) load(kk + 1);
+    auto compute = [&](int s) {
       uint4 fa[4];
       uint32_t sa[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 64 * wm + 16 * i + r;
-        fa[i] = *reinterpret_cast<const uint4*>(&sm.a[s][row * kLD + 16 * g]);
+        fa[i] = *reinterpret_cast<const uint4*>(&sm.a[s][row * kLDG + 16 * g]);
         sa[i] = (sm.as[s][row] >> (8 * g)) & 0xFFu;
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int col = 64 * wn + 16 * j + r;
-        const uint4 fg = *reinterpret_cast<const uint4*>(&sm.b[s][col * kLD + 16 * g]);
-        const uint4 fu = *reinterpret_cast<const uint4*>(&sm.b[s][(col + 128) * kLD + 16 * g]);
+        const uint4 fg = *reinterpret_cast<const uint4*>(&sm.b[s][col * kLDG + 16 * g]);
+        const uint4 fu = *reinterpret_cast<const uint4*>(&sm.b[s][(col + 128) * kLDG + 16 * g]);
         const uint32_t sg = (sm.bs[s][col] >> (8 * g)) & 0xFFu;
         const uint32_t su = (sm.bs[s][col + 128] >> (8 * g)) & 0xFFu;
 #pragma unroll
@@ -135,8 +154,27 @@ __global__ __launch_bounds__(256) void gate_up_big_kernel(
           accu[i][j] = mfma_fp4(fa[i], fu, accu[i][j], sa[i], su);
         }
       }
-      if (kk + 1 < nk) store(s ^ 1);
-      __syncthreads();
+    };
+    // K-steps kk+1..kk+3 are in flight while kk is multiplied: step kk's
+    // registers are refilled with step kk+3 right after they were stored.
+    // Past the last step the loads repeat it and the stores fill a buffer
+    // nobody reads; only the MFMA work is skipped.
+    GuRegs S0, S1, S2;
+    auto iter = [&](int kk, GuRegs& cur, GuRegs& nxt) {
+      load(min(kk + 3, nk - 1), cur);
+      if (kk < nk) compute(kk & 1);
+      store(nxt, (kk + 1) & 1);
+      barrier_lds();
+    };
+    load(0, S0);
+    load(min(1, nk - 1), S1);
+    load(min(2, nk - 1), S2);
+    store(S0, 0);
+    barrier_lds();
+    for (int kk = 0; kk < nk; kk += 3) {
+      iter(kk, S0, S1);
+      iter(kk + 1, S1, S2);
+      iter(kk + 2, S2, S0);
     }
     // ---- epilogue: h = SiLU(g) * u (float64, one rounding), row amax over
     // the item's 128 columns, s = amax / 448, q = E4M3(h / s)
@@ -164,16 +202,16 @@ __global__ __launch_bounds__(256) void gate_up_big_kernel(
         u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x4E, 0xF, 0xF, false));
         u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x141, 0xF, 0xF, false));
         u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x140, 0xF, 0xF, false));
-        if (r == 0) sm.red[wn][64 * wm + 16 * i + 4 * g + v] = __uint_as_float(u);
+        if (r == 0) red[wn][64 * wm + 16 * i + 4 * g + v] = __uint_as_float(u);
       }
-    __syncthreads();
-    uint8_t* qs = reinterpret_cast<uint8_t*>(&sm.a);  // [128][128] codes, in the (now idle) A buffers
+    __syncthreads();  // also: every wave is past its last read of the staging buffers
+    uint8_t* qs = reinterpret_cast<uint8_t*>(&sm.a);  // [128][128] codes, in the idle A buffers
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int row = 64 * wm + 16 * i + 4 * g + v;
-        const float amax = fmaxf(sm.red[0][row], sm.red[1][row]);
+        const float amax = fmaxf(red[0][row], red[1][row]);
         const float sc = __fdiv_rn(amax, 448.0f);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {

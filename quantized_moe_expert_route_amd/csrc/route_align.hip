@@ -132,7 +132,8 @@ __device__ int block_exclusive_scan(int v, int* s_tmp, int* total) {
 // Offsets, tiles of kTileRows sorted rows and meta from per-expert counts
 // (thread e holds count c of expert e). Leaves offsets in s_off.
 __device__ void write_offsets_tiles(int c, int E, int* s_off, int* s_tmp, int* __restrict__ count,
-                                    int* __restrict__ offset, int4* __restrict__ tiles, int* __restrict__ meta) {
+                                    int* __restrict__ offset, int4* __restrict__ tiles, int* __restrict__ meta,
+                                    bool with_tiles = true) {
   const int tid = threadIdx.x;
   const int nt = (c + kTileRows - 1) / kTileRows;
   int total_rows, total_tiles;
@@ -142,7 +143,7 @@ __device__ void write_offsets_tiles(int c, int E, int* s_off, int* s_tmp, int* _
     count[tid] = c;
     offset[tid] = off;
     s_off[tid] = off;
-    for (int i = 0; i < nt; ++i) {
+    for (int i = 0; with_tiles && i < nt; ++i) {
       const int r0 = off + i * kTileRows;
       tiles[toff + i] = make_int4(tid, r0, min(r0 + kTileRows, off + c), 0);
     }
@@ -301,7 +302,7 @@ __global__ __launch_bounds__(1024) void align_kernel(
     if (lane == 0) s_cnt[e] = carry;
   }
   __syncthreads();
-  write_offsets_tiles(tid < E ? s_cnt[tid] : 0, E, s_off, s_tmp, count, offset, tiles, meta);
+  write_offsets_tiles(tid < E ? s_cnt[tid] : 0, E, s_off, s_tmp, count, offset, tiles, meta, false);
   write_big_items(tid < E ? s_cnt[tid] : 0, E, n_iblk, n_nc, s_toff2, s_off2, s_tmp, gu_items, dn_items, meta);
   // each entry's slot in its expert's run: rows of earlier tokens first
   const int n = M * k;
