@@ -59,7 +59,7 @@ Layout make_layout(const moe_shape& s) {
   r.X.tiles = take(16 * (size_t)r.t16);
   r.X.meta = take(256);
   r.X.gu_items = take(16 * (size_t)r.tb * (I / 128));
-  r.X.dn_items = take(16 * (size_t)r.tb * (H / kDownCols));
+  r.X.dn_items = take(16 * (size_t)r.tb * (H / kDownItemCols));
   // counters and the token bitmap: zeroed when the workspace is bound, and
   // left zero by every call
   r.X.bitmap = take(4 * E * (size_t)r.words);

@@ -93,6 +93,20 @@ __global__ __launch_bounds__(256) void down_m16_kernel(
     const int4 tl = tiles[w / n_chunks];
     const int nc = w % n_chunks;
     const int e = tl.x, r0 = tl.y, r1 = tl.z;
+    // all weight loads of the wave's 4 column tiles go out first (the weights come from HBM; mid is in L2)
+    uint4 wbuf[4][NB];
+    uint32_t wsbuf[4][NB];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int n = nc * 256 + wave * 64 + nt * 16 + r;  // this lane's weight row (B column)
+      const uint8_t* pw = w2 + ((size_t)e * H + n) * (I / 2);
+      const uint8_t* ps = s2 + ((size_t)e * H + n) * (I / 32);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        wbuf[nt][b] = ld16(pw + b * 64 + g * 16);
+        wsbuf[nt][b] = ps[b * 4 + g];
+      }
+    }
     // A: this lane's mid row (r0 + r), all blocks, widened to bf16
     const bool rv = r0 + r < r1;
     v8s A[NB][4];
@@ -119,20 +133,6 @@ __global__ __launch_bounds__(256) void down_m16_kernel(
       orow[i] = v ? sorted_entry[r0 + m] : -1;
 #pragma unroll
       for (int b = 0; b < NB; ++b) sc[b][i] = v ? mids[(size_t)(r0 + m) * NB + b] : 0.f;
-    }
-    // all weight loads of the wave's 4 column tiles go out first
-    uint4 wbuf[4][NB];
-    uint32_t wsbuf[4][NB];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int n = nc * 256 + wave * 64 + nt * 16 + r;  // this lane's weight row (B column)
-      const uint8_t* pw = w2 + ((size_t)e * H + n) * (I / 2);
-      const uint8_t* ps = s2 + ((size_t)e * H + n) * (I / 32);
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        wbuf[nt][b] = ld16(pw + b * 64 + g * 16);
-        wsbuf[nt][b] = ps[b * 4 + g];
-      }
     }
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {

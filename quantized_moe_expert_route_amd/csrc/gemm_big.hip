@@ -235,21 +235,29 @@ __global__ __launch_bounds__(256) void gate_up_big_kernel(
 
 
 // ---------------------------------------------------------------- down
-// Item = (expert, 128 sorted rows, 128 output columns). Per mid block b
-// (128 K): the rows' E4M3 bytes are widened to bf16 while staged in LDS
-// (exact), the weights' E2M1 nibbles are widened with their E8M0 scale when a
-// wave reads them (exact), and 4 bf16 MFMAs of K = 32 give the block's fp32
-// partial, which is exact while the block sum fits binary32; the partial is
+// Item = (expert, 128 sorted rows, kDnItemCols output columns). The tile's
+// E4M3 mid bytes go to LDS once per item; the weights stream through
+// kDnItemCols/128 column sub-tiles x I/128 mid blocks, three steps in flight.
+// Per step the E4M3 values and the E2M1 * 2^scale weights are widened to
+// bf16 when a wave reads them (both exact) and 4 bf16 MFMAs of K = 32 give
+// the 128-block's fp32 partial (exact while the sum fits binary32); it is
 // scaled by the row's mid scale in float64 and the blocks are summed in order.
-constexpr int kLDA16 = 136;  // bf16 elements per LDS row of a 128-K block (+8 pad)
-constexpr int kLDB = 80;     // bytes per LDS row of a weight column's 64-byte block slice
+constexpr int kDnItemCols = kDownItemCols;
+constexpr int kLDM = 16;   // pad bytes per LDS mid row
+constexpr int kLDW = 80;   // LDS bytes per weight column slice (64 + 16 pad)
 
+template <int NB>
 struct DnSmem {
-  uint16_t a[2][kBM * kLDA16];   // mid rows as bf16
-  uint8_t b[2][kDownCols * kLDB];
-  uint32_t bs[2][kDownCols];     // 4 E8M0 bytes per column per block
-  float ms[4][kBM];              // mid scales, per block (I <= 512)
+  uint8_t a[kBM * (NB * 128 + kLDM)];   // mid rows, E4M3
+  uint8_t b[2][kDownCols * kLDW];        // weight column slices of one mid block
+  uint32_t bs[2][kDownCols];             // 4 E8M0 bytes per column per block
+  float ms[NB][kBM];                     // mid scales
   int ent[kBM];
+};
+
+struct DnRegs {
+  uint4 b[2];
+  uint32_t s;
 };
 
 template <int NB>
@@ -258,7 +266,10 @@ __global__ __launch_bounds__(256) void down_big_kernel(
     const uint8_t* __restrict__ s2, const int* __restrict__ sorted_entry, const int4* __restrict__ items,
     const int* __restrict__ meta, float* __restrict__ y, int H) {
   constexpr int I = NB * 128;
-  __shared__ DnSmem sm;
+  constexpr int LDA = I + kLDM;
+  constexpr int NSUB = kDnItemCols / kDownCols;  // column sub-tiles per item
+  constexpr int NSTEP = NSUB * NB;               // (sub-tile, block) steps per item
+  __shared__ DnSmem<NB> sm;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave & 1, wn = wave >> 1;
   const int r = lane & 15, g = lane >> 4;
@@ -266,83 +277,88 @@ __global__ __launch_bounds__(256) void down_big_kernel(
   xcd_run(meta[2], first, stride, end);
   for (int it = first; it < end; it += stride) {
     const int4 item = items[it];
-    const int e = item.x, r0 = item.y, r1 = item.z, nc = item.w;
+    const int e = item.x, r0 = item.y, r1 = item.z, c0 = item.w * kDnItemCols;
     const int rows = r1 - r0;
+    // weight addresses of this thread (2 chunks of a 64-byte block slice, 1 scale dword)
+    const uint8_t* pw[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int idx = tid + 256 * q;
+      pw[q] = w2 + ((size_t)e * H + c0 + (idx >> 2)) * (I / 2) + 16 * (idx & 3);
+    }
+    const uint8_t* psw = s2 + ((size_t)e * H + c0 + (tid & (kDownCols - 1))) * (I / 32);
+    // step st = (sub-tile st / NB, block st % NB); the step past the last
+    // repeats it (loaded, stored to an unread buffer, not multiplied)
+    auto load = [&](int st, DnRegs& R) {
+      st = min(st, NSTEP - 1);
+      const int sub = st / NB, b = st - sub * NB;
+      const size_t coff = (size_t)sub * kDownCols * (I / 2) + 64 * b;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) R.b[q] = ld16(pw[q] + coff);
+      R.s = ld4(psw + (size_t)sub * kDownCols * (I / 32) + 4 * b);
+    };
+    auto store = [&](const DnRegs& R, int sb) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int idx = tid + 256 * q;
+        *reinterpret_cast<uint4*>(&sm.b[sb][(idx >> 2) * kLDW + 16 * (idx & 3)]) = R.b[q];
+      }
+      if (tid < kDownCols) sm.bs[sb][tid] = R.s;
+    };
+    DnRegs S0, S1, S2;
+    load(0, S0);
+    load(1, S1);
+    load(2, S2);
+    // the tile's mid rows and scales, once per item
     if (tid < kBM) {
       sm.ent[tid] = tid < rows ? sorted_entry[r0 + tid] : -1;
 #pragma unroll
       for (int b = 0; b < NB; ++b) sm.ms[b][tid] = tid < rows ? mids[(size_t)(r0 + tid) * NB + b] : 0.f;
     }
-    uint4 ra[4], rb[2];
-    uint32_t rsb = 0;
-    auto load = [&](int b) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int idx = tid + 256 * q, row = idx >> 3, c = idx & 7;
-        ra[q] = row < rows ? ld16(midq + (size_t)(r0 + row) * I + 128 * b + 16 * c) : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int idx = tid + 256 * q, col = idx >> 2, c = idx & 3;
-        const size_t wrow = (size_t)e * H + (size_t)nc * kDownCols + col;
-        rb[q] = ld16(w2 + wrow * (I / 2) + 64 * b + 16 * c);
-      }
-      if (tid < kDownCols) rsb = ld4(s2 + ((size_t)e * H + (size_t)nc * kDownCols + tid) * (I / 32) + 4 * b);
-    };
-    auto store = [&](int s) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int idx = tid + 256 * q, row = idx >> 3, c = idx & 7;
-        const uint32_t w[4] = {ra[q].x, ra[q].y, ra[q].z, ra[q].w};
-        uint32_t o[8];
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          o[2 * d] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[d], 1.0f, false));
-          o[2 * d + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[d], 1.0f, true));
-        }
-        uint4* dst = reinterpret_cast<uint4*>(&sm.a[s][row * kLDA16 + 16 * c]);
-        dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-        dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
-      }
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int idx = tid + 256 * q;
-        *reinterpret_cast<uint4*>(&sm.b[s][(idx >> 2) * kLDB + 16 * (idx & 3)]) = rb[q];
-      }
-      if (tid < kDownCols) sm.bs[s][tid] = rsb;
-    };
-    double acc[4][4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[i][j][v] = 0.0;
-    __syncthreads();  // ent / ms visible
-    load(0);
-    store(0);
+    for (int idx = tid; idx < kBM * (I / 16); idx += 256) {
+      const int row = idx / (I / 16), c = idx - row * (I / 16);
+      const uint4 v = row < rows ? ld16(midq + (size_t)(r0 + row) * I + 16 * c) : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(&sm.a[row * LDA + 16 * c]) = v;
+    }
+    store(S0, 0);
     __syncthreads();
-    for (int b = 0; b < NB; ++b) {
-      const int s = b & 1;
-      if (b + 1 < NB) load(b + 1);
-      v4f P[4][4];
+    double acc[4][4][4];
+    v4f P[4][4];
+    auto compute = [&](int st, int sb) {
+      const int sub = st / NB, b = st - sub * NB;
+      if (b == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[i][j][v] = 0.0;
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) P[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {  // K = 32 chunks of the block; lane group g: K 32q + 8g ..
+      for (int q = 0; q < 4; ++q) {  // K = 32 chunks; lane group g holds K 32q + 8g ..
         v8s fa[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int row = 64 * wm + 16 * i + r;
-          fa[i] = *reinterpret_cast<const v8s*>(&sm.a[s][row * kLDA16 + 32 * q + 8 * g]);
+          const uint2 raw = *reinterpret_cast<const uint2*>(&sm.a[row * LDA + 128 * b + 32 * q + 8 * g]);
+          const uint32_t d0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, 1.0f, false));
+          const uint32_t d1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, 1.0f, true));
+          const uint32_t d2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.y, 1.0f, false));
+          const uint32_t d3 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.y, 1.0f, true));
+          fa[i][0] = (short)(d0 & 0xFFFF); fa[i][1] = (short)(d0 >> 16);
+          fa[i][2] = (short)(d1 & 0xFFFF); fa[i][3] = (short)(d1 >> 16);
+          fa[i][4] = (short)(d2 & 0xFFFF); fa[i][5] = (short)(d2 >> 16);
+          fa[i][6] = (short)(d3 & 0xFFFF); fa[i][7] = (short)(d3 >> 16);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int col = 64 * wn + 16 * j + r;
-          const uint32_t wv = *reinterpret_cast<const uint32_t*>(&sm.b[s][col * kLDB + 16 * q + 4 * g]);
-          const float wsc = e8m0_to_float((sm.bs[s][col] >> (8 * q)) & 0xFFu);
+          const uint32_t wv = *reinterpret_cast<const uint32_t*>(&sm.b[sb][col * kLDW + 16 * q + 4 * g]);
+          const float wsc = e8m0_to_float((sm.bs[sb][col] >> (8 * q)) & 0xFFu);
           const uint32_t d0 = cvt_fp4x2_bf16<0>(wv, wsc), d1 = cvt_fp4x2_bf16<1>(wv, wsc);
           const uint32_t d2 = cvt_fp4x2_bf16<2>(wv, wsc), d3 = cvt_fp4x2_bf16<3>(wv, wsc);
           v8s fb;
@@ -362,21 +378,31 @@ __global__ __launch_bounds__(256) void down_big_kernel(
 #pragma unroll
           for (int j = 0; j < 4; ++j) acc[i][j][v] += sc * (double)P[i][j][v];
         }
-      if (b + 1 < NB) store(s ^ 1);
-      __syncthreads();
-    }
+      if (b == NB - 1) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = 64 * wm + 16 * i + 4 * g + v;
-        const int en = sm.ent[row];
-        if (en >= 0) {
+          for (int v = 0; v < 4; ++v) {
+            const int en = sm.ent[64 * wm + 16 * i + 4 * g + v];
+            if (en >= 0) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            y[(size_t)en * H + (size_t)nc * kDownCols + 64 * wn + 16 * j + r] = (float)acc[i][j][v];
-        }
+              for (int j = 0; j < 4; ++j)
+                y[(size_t)en * H + c0 + sub * kDownCols + 64 * wn + 16 * j + r] = (float)acc[i][j][v];
+            }
+          }
       }
+    };
+    auto iter = [&](int st, DnRegs& cur, DnRegs& nxt) {
+      load(st + 3, cur);
+      if (st < NSTEP) compute(st, st & 1);
+      store(nxt, (st + 1) & 1);
+      barrier_lds();
+    };
+    for (int st = 0; st < NSTEP; st += 3) {
+      iter(st, S0, S1);
+      iter(st + 1, S1, S2);
+      iter(st + 2, S2, S0);
+    }
     __syncthreads();
   }
 }
@@ -397,7 +423,7 @@ hipError_t launch_gate_up_big(const moe_plan* p, const CallArgs& a, Ev ev) {
 hipError_t launch_down_big(const moe_plan* p, const CallArgs& a, Ev ev) {
   const int64_t n = a.M * p->s.top_k;
   const int64_t tiles = (n + std::min<int64_t>(p->s.E, n) * (kBM - 1) + kBM - 1) / kBM;
-  const int64_t items = tiles * (p->s.H / kDownCols);
+  const int64_t items = tiles * (p->s.H / kDnItemCols);
   const int blocks = (int)std::min<int64_t>(items, 256);
   auto go = [&](auto kern) {
     return launch_k(kern, dim3(blocks), dim3(256), 0, a.stream, ev, wsp<uint8_t>(p, p->L.midq),

@@ -156,6 +156,7 @@ __device__ void write_offsets_tiles(int c, int E, int* s_off, int* s_tmp, int* _
 }
 
 // ---------------------------------------------------------------- M <= 64
+// Workgroup 0 routes, sorts and writes the tiles; workgroups 1.. quantize x.
 template <int EC>
 __global__ __launch_bounds__(1024) void route_align_small_kernel(
     const float* __restrict__ logits, const uint16_t* __restrict__ x, int M, int E, int k, int H, float scaling,
@@ -167,23 +168,25 @@ __global__ __launch_bounds__(1024) void route_align_small_kernel(
   __shared__ int s_off[1024];
   __shared__ int s_tmp[64];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  for (int e = tid; e < E; e += 1024) s_mask[e][0] = s_mask[e][1] = 0u;
-  // the first token's logits are loaded before the x blocks so that both
-  // memory latencies overlap
-  uint32_t key[EC];
-  if (wave < M) load_keys<EC>(logits + (size_t)wave * E, E, lane, key);
-  // x -> MXFP4: one 32-block per thread per pass
-  const int nblk = H >> 5;
-  for (int bi = tid; bi < M * nblk; bi += 1024) {
-    const int t = bi / nblk, b = bi - t * nblk;
-    quant_block_mx(x + (size_t)t * H + b * 32, xq + (size_t)t * (H >> 1) + b * 16, xs + (size_t)t * nblk + b);
+  if (blockIdx.x > 0) {
+    // x -> MXFP4 is independent of the routing: workgroups 1.. take 64
+    // blocks of 32 each, on their own CUs (the conversion is ALU work)
+    const int nblk = H >> 5;
+    const int bi = (blockIdx.x - 1) * 64 + tid;
+    if (tid < 64 && bi < M * nblk) {
+      const int t = bi / nblk, b = bi - t * nblk;
+      quant_block_mx(x + (size_t)t * H + b * 32, xq + (size_t)t * (H >> 1) + b * 16, xs + (size_t)t * nblk + b);
+    }
+    return;
   }
+  for (int e = tid; e < E; e += 1024) s_mask[e][0] = s_mask[e][1] = 0u;
   __syncthreads();
   // top-k, one wave per token
   for (int t = wave; t < M; t += 16) {
     uint32_t sel_e = 0;
     float sel_l = 0.f;
-    if (t != wave) load_keys<EC>(logits + (size_t)t * E, E, lane, key);
+    uint32_t key[EC];
+    load_keys<EC>(logits + (size_t)t * E, E, lane, key);
     topk_wave<EC>(key, k, lane, sel_e, sel_l);
     const float w = route_weight(sel_l, k, lane, scaling);
     if (lane < k) {
@@ -342,8 +345,10 @@ static hipError_t by_ec(int E, F&& f) {
 
 hipError_t launch_route_small(const moe_plan* p, const CallArgs& a, Ev ev) {
   const int M = (int)a.M, E = (int)p->s.E, k = (int)p->s.top_k, H = (int)p->s.H;
+  const int xq_groups = (int)((a.M * (H / 32) + 63) / 64);
   return by_ec(E, [&](auto ec) {
-    return launch_k(route_align_small_kernel<decltype(ec)::value>, dim3(1), dim3(1024), 0, a.stream, ev, a.logits,
+    return launch_k(route_align_small_kernel<decltype(ec)::value>, dim3(1 + xq_groups), dim3(1024), 0, a.stream, ev,
+                    a.logits,
                     reinterpret_cast<const uint16_t*>(a.x), M, E, k, H, p->s.routed_scaling,
                     wsp<int>(p, p->L.topk_ids), wsp<float>(p, p->L.topk_w), wsp<int>(p, p->L.count),
                     wsp<int>(p, p->L.offset), wsp<int>(p, p->L.sorted_entry), wsp<int4>(p, p->X.tiles),
@@ -369,7 +374,7 @@ hipError_t launch_align(const moe_plan* p, const CallArgs& a, Ev ev) {
                   (int)p->s.E, (int)p->s.top_k, wsp<uint32_t>(p, p->X.bitmap), wsp<int>(p, p->X.pre), words,
                   wsp<int>(p, p->L.count), wsp<int>(p, p->L.offset), wsp<int>(p, p->L.sorted_entry),
                   wsp<int4>(p, p->X.tiles), wsp<int>(p, p->X.meta), (int)(p->s.I / 128),
-                  (int)(p->s.H / kDownCols), wsp<int4>(p, p->X.gu_items), wsp<int4>(p, p->X.dn_items));
+                  (int)(p->s.H / kDownItemCols), wsp<int4>(p, p->X.gu_items), wsp<int4>(p, p->X.dn_items));
 }
 
 }  // namespace qmoe
