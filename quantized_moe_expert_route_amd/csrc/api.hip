@@ -60,11 +60,9 @@ Layout make_layout(const moe_shape& s) {
   r.X.meta = take(256);
   r.X.gu_items = take(16 * (size_t)r.tb * (I / 128));
   r.X.dn_items = take(16 * (size_t)r.tb * (H / kDownItemCols));
-  // counters and the token bitmap: zeroed when the workspace is bound, and
+  // the token bitmap: zeroed when the workspace is bound, and
   // left zero by every call
   r.X.bitmap = take(4 * E * (size_t)r.words);
-  r.X.qctr = take(4 * (size_t)r.t16 * (I / 128));
-  r.X.cctr = take(4 * M * (H / 256));
   r.X.sync_begin = r.X.bitmap;
   r.X.sync_bytes = align256(off) - r.X.bitmap;
   r.X.pre = take(4 * E * (size_t)r.words);
@@ -145,8 +143,8 @@ int moe_plan_stage_launches(const moe_plan* plan, int64_t M, int stage) {
     case 2: return 1;                             // gate_up (+ mid quantization when large)
     case 3: return small ? 1 : 0;                 // act_quant
     case 4: return plan->s.shared_I > 0 ? 4 : 0;  // shared expert
-    case 5: return 1;                             // down
-    default: return 1;                            // combine
+    case 5: return 1;                             // down (+ combine when small)
+    default: return small ? 0 : 1;                // combine
   }
 }
 
@@ -275,23 +273,25 @@ moe_status moe_forward(moe_plan* plan, int64_t M, const void* x, const float* lo
     hipError_t e = hipEventRecord(ev[i].start, a.stream);
     return e != hipSuccess ? e : hipEventRecord(ev[i].stop, a.stream);
   };
-  // Up to kSmallM tokens, routing + sort + x quantization run in one
-  // workgroup (one launch); above, routing is spread over the GPU and a
-  // second launch sorts. The other stages are one launch each: folding the
-  // mid quantization or the combine into the producing launch needs a
-  // device-scope release/acquire per workgroup, which writes back and
-  // invalidates a whole L2 of an XCD each time and costs more than a launch.
-  // Above kSmallM, gate/up runs on 128-row tiles with the mid quantization
-  // inside (every item owns whole mid blocks).
+  // Up to kSmallM tokens: routing + sort + x quantization in one launch
+  // (workgroup 0 routes and sorts, the others quantize x); gate/up on 16-row
+  // tiles; the mid quantization; down with the combine (a workgroup owns 16
+  // output columns of every slot, so the slot results never leave it).
+  // Above kSmallM: routing spread over the GPU, a second launch sorts;
+  // gate/up on 128-row tiles with the mid quantization inside (every item
+  // owns whole mid blocks); down to y in HBM; the combine.
+  // A stage is never folded into its producer through a last-arriver
+  // counter: the device-scope release/acquire that needs writes back and
+  // invalidates a whole L2 of an XCD per workgroup and costs more than a
+  // launch.
   const bool small = M <= kSmallM;
-  const bool fuse = false;
   hipError_t e = small ? launch_route_small(plan, a, ev[0]) : launch_route(plan, a, ev[0]);
   if (e == hipSuccess) e = small ? none(1) : launch_align(plan, a, ev[1]);
-  if (e == hipSuccess) e = small ? launch_gate_up(plan, a, ev[2], fuse) : launch_gate_up_big(plan, a, ev[2]);
-  if (e == hipSuccess) e = (fuse || !small) ? none(3) : launch_act_quant(plan, a, ev[3]);
+  if (e == hipSuccess) e = small ? launch_gate_up(plan, a, ev[2]) : launch_gate_up_big(plan, a, ev[2]);
+  if (e == hipSuccess) e = small ? launch_act_quant(plan, a, ev[3]) : none(3);
   if (e == hipSuccess) e = plan->s.shared_I > 0 ? launch_shared(plan, a, ev[4]) : none(4);
-  if (e == hipSuccess) e = small ? launch_down(plan, a, ev[5], fuse) : launch_down_big(plan, a, ev[5]);
-  if (e == hipSuccess) e = fuse ? none(6) : launch_combine(plan, a, ev[6]);
+  if (e == hipSuccess) e = small ? launch_down_combine(plan, a, ev[5]) : launch_down_big(plan, a, ev[5]);
+  if (e == hipSuccess) e = small ? none(6) : launch_combine(plan, a, ev[6]);
   return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

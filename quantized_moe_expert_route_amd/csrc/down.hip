@@ -11,7 +11,8 @@
 // float64 and the blocks are summed in order, then rounded once to fp32.
 //
 // combine: out[t] = bf16(sum_j w[t, j] * y[t, j] (+ shared[t])): products and
-// sum in float64 in slot order, one rounding to bf16.
+// sum in float64 in slot order, one rounding to bf16. Up to kSmallM tokens it
+// runs inside the down launch; above, y goes through HBM to its own launch.
 #include "common.h"
 #include "internal.h"
 
@@ -19,160 +20,134 @@
 
 namespace qmoe {
 
-struct E4m3Bf16Table {
-  uint16_t v[256];
-  constexpr E4m3Bf16Table() : v() {
-    for (int c = 0; c < 256; ++c) v[c] = e4m3_to_bf16_bits((uint32_t)c);
-  }
+// Up to kSmallM tokens, down and combine are one launch. A workgroup owns 16
+// output columns of every token: its four waves take the 16-row tiles in turn
+// (tile i to wave i % 4), keep each (sorted row, column) result in LDS, and
+// when every tile is done the workgroup forms out[t, c0 .. c0 + 16) from the
+// token's k slots, so no slot result leaves the workgroup.
+//
+// In MFMA step q of a 128-block, lane group g supplies K = 32g + 8q .. + 8:
+// a lane reads 32 contiguous mid bytes and 16 contiguous weight bytes (one MX
+// block with its one scale byte) per block. Each wave keeps D tiles of loads
+// in flight (weights from HBM, mid rows and scales from L2).
+constexpr int kDcMaxRows = kSmallM * 16;  // M * k on this path
+
+template <int NB>
+struct DcSlot {
+  uint4 w[NB];      // this lane's 32 E2M1 weights of each block
+  uint4 a[NB][2];   // this lane's 32 E4M3 mid bytes of each block
+  uint32_t ws[NB];  // the weights' E8M0 byte
+  float sc[NB][4];  // mid scales of the lane's four D rows
 };
-__constant__ E4m3Bf16Table kE4m3Bf16 = E4m3Bf16Table();
 
-// 8 E4M3 bytes (two dwords) -> 8 bf16 (v8s) through an LDS copy of the table.
-__device__ __forceinline__ v8s e4m3x8_to_bf16(uint32_t lo, uint32_t hi, const uint16_t* tab) {
-  v8s r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = (short)tab[(lo >> (8 * i)) & 0xFFu];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[4 + i] = (short)tab[(hi >> (8 * i)) & 0xFFu];
-  return r;
-}
-
-// 8 E2M1 codes (one dword, element 2i low nibble) * scale -> 8 bf16.
-__device__ __forceinline__ v8s fp4x8_to_bf16(uint32_t src, float scale) {
-  uint32_t d0 = cvt_fp4x2_bf16<0>(src, scale);
-  uint32_t d1 = cvt_fp4x2_bf16<1>(src, scale);
-  uint32_t d2 = cvt_fp4x2_bf16<2>(src, scale);
-  uint32_t d3 = cvt_fp4x2_bf16<3>(src, scale);
-  v8s r;
-  r[0] = (short)(d0 & 0xFFFF); r[1] = (short)(d0 >> 16);
-  r[2] = (short)(d1 & 0xFFFF); r[3] = (short)(d1 >> 16);
-  r[4] = (short)(d2 & 0xFFFF); r[5] = (short)(d2 >> 16);
-  r[6] = (short)(d3 & 0xFFFF); r[7] = (short)(d3 >> 16);
-  return r;
-}
-
-// Work item = (tile of up to 16 sorted rows, 256 output columns); each of the
-// 4 waves owns 4 tiles of 16 columns. For a 128-block the four bf16 MFMAs of
-// K=32 take, in step q, K = 32g + 8q.. for lane group g, so a lane reads 32
-// contiguous mid bytes and 16 contiguous weight bytes (one MX block, one
-// scale byte) per block.
-// out[t, c0 .. c0 + n) from y (float64 products and sum in slot order, plus
-// the shared expert), one bf16 rounding; thread i does columns c0 + i + kk*step.
-__device__ __forceinline__ void combine_cols(const float* __restrict__ y, const float* __restrict__ w,
-                                             const float* __restrict__ ys, int t, int k, int H, int c0, int ncols,
-                                             uint16_t* __restrict__ out) {
-  for (int c = c0 + (int)threadIdx.x; c < c0 + ncols; c += blockDim.x) {
-    double acc = 0.0;
-    for (int j = 0; j < k; ++j)
-      acc += (double)w[(size_t)t * k + j] * (double)y[((size_t)t * k + j) * H + c];
-    if (ys) acc += (double)ys[(size_t)t * H + c];
-    out[(size_t)t * H + c] = (uint16_t)bf16_rne_from_double(acc);
-  }
-}
-
-// FUSED: after writing its y rows of a 256-column chunk, the workgroup counts
-// one finished slot per (token, chunk); the workgroup that brings a token's
-// count to k combines that token's chunk (and resets the counter).
-template <int NB, bool FUSED>  // NB = I / 128
-__global__ __launch_bounds__(256) void down_m16_kernel(
+template <int NB, int D>
+__global__ __launch_bounds__(256) void down_combine_kernel(
     const uint8_t* __restrict__ midq, const float* __restrict__ mids, const uint8_t* __restrict__ w2,
     const uint8_t* __restrict__ s2, const int* __restrict__ sorted_entry, const int4* __restrict__ tiles,
-    const int* __restrict__ meta, float* __restrict__ y, int H, int k, const float* __restrict__ topk_w,
-    const float* __restrict__ ys, uint32_t* __restrict__ cctr, uint16_t* __restrict__ out) {
+    const int* __restrict__ meta, int H, int k, int M, const float* __restrict__ topk_w,
+    const float* __restrict__ ys, uint16_t* __restrict__ out) {
   constexpr int I = NB * 128;
-  __shared__ uint16_t tab[256];
-  __shared__ int s_done[16];
-  __shared__ int s_ndone;
-  tab[threadIdx.x] = kE4m3Bf16.v[threadIdx.x];
-  __syncthreads();
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __shared__ float yl[kDcMaxRows * 16];
+  __shared__ int inv[kDcMaxRows];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, g = lane >> 4;
-  const int n_chunks = H / 256;
-  const int n_work = meta[0] * n_chunks;
-  for (int w = blockIdx.x; w < n_work; w += gridDim.x) {
-    const int4 tl = tiles[w / n_chunks];
-    const int nc = w % n_chunks;
-    const int e = tl.x, r0 = tl.y, r1 = tl.z;
-    // all weight loads of the wave's 4 column tiles go out first (the weights come from HBM; mid is in L2)
-    uint4 wbuf[4][NB];
-    uint32_t wsbuf[4][NB];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int n = nc * 256 + wave * 64 + nt * 16 + r;  // this lane's weight row (B column)
-      const uint8_t* pw = w2 + ((size_t)e * H + n) * (I / 2);
-      const uint8_t* ps = s2 + ((size_t)e * H + n) * (I / 32);
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        wbuf[nt][b] = ld16(pw + b * 64 + g * 16);
-        wsbuf[nt][b] = ps[b * 4 + g];
-      }
-    }
-    // A: this lane's mid row (r0 + r), all blocks, widened to bf16
-    const bool rv = r0 + r < r1;
-    v8s A[NB][4];
+  const int c0 = blockIdx.x * 16;
+  const int n = M * k;
+  for (int q = tid; q < n; q += 256) inv[sorted_entry[q]] = q;
+  const int nt = meta[0];
+  const int my = nt > wave ? (nt - wave + 3) / 4 : 0;  // tiles wave, wave + 4, ...
+
+  auto load = [&](int i, DcSlot<NB>& S) {
+    const int4 tl = tiles[wave + 4 * i];
+    const uint8_t* pw = w2 + ((size_t)tl.x * H + c0 + r) * (I / 2) + 16 * g;
+    const uint8_t* ps = s2 + ((size_t)tl.x * H + c0 + r) * (I / 32) + g;
+    // rows past the tile's end read the tile's first row; their results are dropped
+    const int row = tl.y + r < tl.z ? tl.y + r : tl.y;
+    const uint8_t* pq = midq + (size_t)row * I + 32 * g;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      uint4 q0 = make_uint4(0, 0, 0, 0), q1 = make_uint4(0, 0, 0, 0);
-      if (rv) {
-        const uint8_t* pq = midq + (size_t)(r0 + r) * I + b * 128 + g * 32;
-        q0 = ld16(pq);
-        q1 = ld16(pq + 16);
-      }
-      A[b][0] = e4m3x8_to_bf16(q0.x, q0.y, tab);
-      A[b][1] = e4m3x8_to_bf16(q0.z, q0.w, tab);
-      A[b][2] = e4m3x8_to_bf16(q1.x, q1.y, tab);
-      A[b][3] = e4m3x8_to_bf16(q1.z, q1.w, tab);
-    }
-    // mid scales and output rows of this lane's four D rows (4g + i)
-    float sc[NB][4];
-    int orow[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 4 * g + i;
-      const bool v = r0 + m < r1;
-      orow[i] = v ? sorted_entry[r0 + m] : -1;
-#pragma unroll
-      for (int b = 0; b < NB; ++b) sc[b][i] = v ? mids[(size_t)(r0 + m) * NB + b] : 0.f;
+      S.w[b] = ld16(pw + 64 * b);
+      S.ws[b] = ps[4 * b];
+      S.a[b][0] = ld16(pq + 128 * b);
+      S.a[b][1] = ld16(pq + 128 * b + 16);
     }
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int i2 = 0; i2 < 4; ++i2) {
+      const int m = tl.y + 4 * g + i2 < tl.z ? tl.y + 4 * g + i2 : tl.y;
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const uint4 wb = wbuf[nt][b];
-        const float wsc = e8m0_to_float(wsbuf[nt][b]);
-        v4f P = {0.f, 0.f, 0.f, 0.f};
-        P = mfma_bf16(A[b][0], fp4x8_to_bf16(wb.x, wsc), P);
-        P = mfma_bf16(A[b][1], fp4x8_to_bf16(wb.y, wsc), P);
-        P = mfma_bf16(A[b][2], fp4x8_to_bf16(wb.z, wsc), P);
-        P = mfma_bf16(A[b][3], fp4x8_to_bf16(wb.w, wsc), P);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] += (double)sc[b][i] * (double)P[i];
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (orow[i] >= 0) y[(size_t)orow[i] * H + nc * 256 + wave * 64 + nt * 16 + r] = (float)acc[i];
+      for (int b = 0; b < NB; ++b) S.sc[b][i2] = mids[(size_t)m * NB + b];
     }
-    if (FUSED) {
-      if (threadIdx.x == 0) s_ndone = 0;
-      __threadfence();
-      __syncthreads();
-      if (threadIdx.x < 16 && r0 + (int)threadIdx.x < r1) {
-        const int t = sorted_entry[r0 + threadIdx.x] / k;
-        if (atomicAdd(&cctr[(size_t)t * n_chunks + nc], 1u) == (uint32_t)(k - 1)) s_done[atomicAdd(&s_ndone, 1)] = t;
+  };
+  auto compute = [&](int i, const DcSlot<NB>& S) {
+    const int4 tl = tiles[wave + 4 * i];
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const float wsc = e8m0_to_float(S.ws[b]);
+      const uint32_t qa[8] = {S.a[b][0].x, S.a[b][0].y, S.a[b][0].z, S.a[b][0].w,
+                              S.a[b][1].x, S.a[b][1].y, S.a[b][1].z, S.a[b][1].w};
+      const uint32_t qw[4] = {S.w[b].x, S.w[b].y, S.w[b].z, S.w[b].w};
+      v4f P = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t d0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(qa[2 * q], 1.0f, false));
+        const uint32_t d1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(qa[2 * q], 1.0f, true));
+        const uint32_t d2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(qa[2 * q + 1], 1.0f, false));
+        const uint32_t d3 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(qa[2 * q + 1], 1.0f, true));
+        v8s fa;
+        fa[0] = (short)(d0 & 0xFFFF); fa[1] = (short)(d0 >> 16);
+        fa[2] = (short)(d1 & 0xFFFF); fa[3] = (short)(d1 >> 16);
+        fa[4] = (short)(d2 & 0xFFFF); fa[5] = (short)(d2 >> 16);
+        fa[6] = (short)(d3 & 0xFFFF); fa[7] = (short)(d3 >> 16);
+        const uint32_t e0 = cvt_fp4x2_bf16<0>(qw[q], wsc), e1 = cvt_fp4x2_bf16<1>(qw[q], wsc);
+        const uint32_t e2 = cvt_fp4x2_bf16<2>(qw[q], wsc), e3 = cvt_fp4x2_bf16<3>(qw[q], wsc);
+        v8s fb;
+        fb[0] = (short)(e0 & 0xFFFF); fb[1] = (short)(e0 >> 16);
+        fb[2] = (short)(e1 & 0xFFFF); fb[3] = (short)(e1 >> 16);
+        fb[4] = (short)(e2 & 0xFFFF); fb[5] = (short)(e2 >> 16);
+        fb[6] = (short)(e3 & 0xFFFF); fb[7] = (short)(e3 >> 16);
+        P = mfma_bf16(fa, fb, P);
       }
-      __syncthreads();
-      const int nd = s_ndone;
-      if (nd > 0) {
-        __threadfence();
-        for (int q = 0; q < nd; ++q) {
-          const int t = s_done[q];
-          combine_cols(y, topk_w, ys, t, k, H, nc * 256, 256, out);
-          if (threadIdx.x == 0) cctr[(size_t)t * n_chunks + nc] = 0u;
-        }
-      }
-      __syncthreads();
+#pragma unroll
+      for (int i2 = 0; i2 < 4; ++i2) acc[i2] += (double)S.sc[b][i2] * (double)P[i2];
     }
+#pragma unroll
+    for (int i2 = 0; i2 < 4; ++i2) {
+      const int m = tl.y + 4 * g + i2;
+      if (m < tl.z) yl[m * 16 + r] = (float)acc[i2];
+    }
+  };
+
+  if (my > 0) {
+    DcSlot<NB> S[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) load(d < my ? d : my - 1, S[d]);
+    for (int i0 = 0; i0 < my; i0 += D) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        const int i = i0 + d;
+        if (i < my) compute(i, S[d]);
+        load(i + D < my ? i + D : my - 1, S[d]);
+      }
+    }
+  }
+  __syncthreads();
+  // out[t, c0 + 2p .. + 2): float64 products and sum in slot order (+ shared), one bf16 rounding
+  for (int idx = tid; idx < M * 8; idx += 256) {
+    const int t = idx >> 3, cc = 2 * (idx & 7);
+    double a0 = 0.0, a1 = 0.0;
+    for (int j = 0; j < k; ++j) {
+      const double wj = (double)topk_w[t * k + j];
+      const float* py = yl + inv[t * k + j] * 16 + cc;
+      a0 += wj * (double)py[0];
+      a1 += wj * (double)py[1];
+    }
+    if (ys) {
+      a0 += (double)ys[(size_t)t * H + c0 + cc];
+      a1 += (double)ys[(size_t)t * H + c0 + cc + 1];
+    }
+    *reinterpret_cast<uint32_t*>(out + (size_t)t * H + c0 + cc) =
+        bf16_rne_from_double(a0) | (bf16_rne_from_double(a1) << 16);
   }
 }
 
@@ -208,25 +183,22 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
 }
 
-hipError_t launch_down(const moe_plan* p, const CallArgs& a, Ev ev, bool fused) {
-  const int64_t n = a.M * p->s.top_k;
-  const int64_t t16 = (n + std::min<int64_t>(p->s.E, n) * (kTileRows - 1) + kTileRows - 1) / kTileRows;
+hipError_t launch_down_combine(const moe_plan* p, const CallArgs& a, Ev ev) {
   const int H = (int)p->s.H;
-  const int64_t work_max = t16 * (H / 256);
-  const int blocks = (int)std::min<int64_t>(work_max, 4096);
+  if (a.M * p->s.top_k > kDcMaxRows) return hipErrorInvalidValue;
   const float* ys = p->s.shared_I > 0 ? wsp<float>(p, p->L.sh_y) : nullptr;
   auto go = [&](auto kern) {
-    return launch_k(kern, dim3(blocks), dim3(256), 0, a.stream, ev, wsp<uint8_t>(p, p->L.midq),
+    return launch_k(kern, dim3(H / 16), dim3(256), 0, a.stream, ev, wsp<uint8_t>(p, p->L.midq),
                     wsp<float>(p, p->L.mids), reinterpret_cast<const uint8_t*>(a.w2),
                     reinterpret_cast<const uint8_t*>(a.s2), wsp<int>(p, p->L.sorted_entry), wsp<int4>(p, p->X.tiles),
-                    wsp<int>(p, p->X.meta), wsp<float>(p, p->L.y), H, (int)p->s.top_k, wsp<float>(p, p->L.topk_w),
-                    ys, wsp<uint32_t>(p, p->X.cctr), reinterpret_cast<uint16_t*>(a.out));
+                    wsp<int>(p, p->X.meta), H, (int)p->s.top_k, (int)a.M, wsp<float>(p, p->L.topk_w), ys,
+                    reinterpret_cast<uint16_t*>(a.out));
   };
   switch (p->s.I / 128) {
-    case 1: return fused ? go(down_m16_kernel<1, true>) : go(down_m16_kernel<1, false>);
-    case 2: return fused ? go(down_m16_kernel<2, true>) : go(down_m16_kernel<2, false>);
-    case 3: return fused ? go(down_m16_kernel<3, true>) : go(down_m16_kernel<3, false>);
-    case 4: return fused ? go(down_m16_kernel<4, true>) : go(down_m16_kernel<4, false>);
+    case 1: return go(down_combine_kernel<1, 8>);
+    case 2: return go(down_combine_kernel<2, 4>);
+    case 3: return go(down_combine_kernel<3, 3>);
+    case 4: return go(down_combine_kernel<4, 2>);
     default: return hipErrorInvalidValue;
   }
 }

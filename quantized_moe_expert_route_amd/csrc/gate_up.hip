@@ -45,17 +45,12 @@ __device__ __forceinline__ void quant_mid_rows(const float* __restrict__ h, int 
   }
 }
 
-// FUSED: the workgroup that finishes the last of the 8 items of a (tile,
-// 128-block) quantizes that block for the tile's rows (a counter per
-// (tile, block), released by every writer and reset by the last one).
-template <bool FUSED>
 __global__ __launch_bounds__(256) void gate_up_m16_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const uint8_t* __restrict__ w13,
     const uint8_t* __restrict__ s13, const int* __restrict__ sorted_entry,
     const int4* __restrict__ tiles, const int* __restrict__ meta, float* __restrict__ hout, int H,
-    int I, int k, uint32_t* __restrict__ qctr, uint8_t* __restrict__ midq, float* __restrict__ mids) {
+    int I, int k) {
   __shared__ v4f red[2][4][64];
-  __shared__ int s_last;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4;
   const int n_it = I / 16;
@@ -122,17 +117,6 @@ __global__ __launch_bounds__(256) void gate_up_m16_kernel(
       const float U = ((red[1][0][l][i] + red[1][1][l][i]) + red[1][2][l][i]) + red[1][3][l][i];
       if (r0 + m < r1) hout[(size_t)(r0 + m) * I + it * 16 + n] = silu_mul(G, U);
     }
-    if (FUSED) {
-      __threadfence();
-      __syncthreads();
-      if (threadIdx.x == 0) s_last = atomicAdd(&qctr[(size_t)(w / n_it) * (I / 128) + it / 8], 1u) == 7u;
-      __syncthreads();
-      if (s_last) {
-        __threadfence();
-        quant_mid_rows(hout, r0 + wave, r1, 4, I, it / 8, midq, mids);
-        if (threadIdx.x == 0) qctr[(size_t)(w / n_it) * (I / 128) + it / 8] = 0u;
-      }
-    }
     __syncthreads();
   }
 }
@@ -148,21 +132,16 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const float* __restrict_
   }
 }
 
-hipError_t launch_gate_up(const moe_plan* p, const CallArgs& a, Ev ev, bool fused) {
+hipError_t launch_gate_up(const moe_plan* p, const CallArgs& a, Ev ev) {
   const int I = (int)p->s.I;
   const int64_t n = a.M * p->s.top_k;
   const int64_t t16 = (n + std::min<int64_t>(p->s.E, n) * (kTileRows - 1) + kTileRows - 1) / kTileRows;
   const int64_t work_max = t16 * (I / 16);
   const int blocks = (int)std::min<int64_t>(work_max, 2048);
-  auto go = [&](auto kern) {
-    return launch_k(kern, dim3(blocks), dim3(256), 0, a.stream, ev, wsp<uint8_t>(p, p->L.xq),
-                    wsp<uint8_t>(p, p->L.xs), reinterpret_cast<const uint8_t*>(a.w13),
-                    reinterpret_cast<const uint8_t*>(a.s13), wsp<int>(p, p->L.sorted_entry),
-                    wsp<int4>(p, p->X.tiles), wsp<int>(p, p->X.meta), wsp<float>(p, p->X.h), (int)p->s.H, I,
-                    (int)p->s.top_k, wsp<uint32_t>(p, p->X.qctr), wsp<uint8_t>(p, p->L.midq),
-                    wsp<float>(p, p->L.mids));
-  };
-  return fused ? go(gate_up_m16_kernel<true>) : go(gate_up_m16_kernel<false>);
+  return launch_k(gate_up_m16_kernel, dim3(blocks), dim3(256), 0, a.stream, ev, wsp<uint8_t>(p, p->L.xq),
+                  wsp<uint8_t>(p, p->L.xs), reinterpret_cast<const uint8_t*>(a.w13),
+                  reinterpret_cast<const uint8_t*>(a.s13), wsp<int>(p, p->L.sorted_entry), wsp<int4>(p, p->X.tiles),
+                  wsp<int>(p, p->X.meta), wsp<float>(p, p->X.h), (int)p->s.H, I, (int)p->s.top_k);
 }
 
 hipError_t launch_act_quant(const moe_plan* p, const CallArgs& a, Ev ev) {

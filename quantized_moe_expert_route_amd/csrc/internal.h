@@ -26,8 +26,6 @@ struct Internal {
   size_t pre;      // int32 [E, ceil(M/32)]: entries of row e before word w
   size_t h;        // fp32 [n, I]: SiLU(gate)*up, rows in sorted order
   size_t sh_h;     // fp32 [M, Is]
-  size_t qctr;     // uint32 [T16, I/128]: finished 16-column items per (tile, mid block)
-  size_t cctr;     // uint32 [M, H/256]: finished slots per (token, 256-column chunk)
   size_t sync_begin, sync_bytes;  // region zeroed once when the workspace is bound
 };
 
@@ -69,8 +67,8 @@ inline hipError_t launch_k(void (*kern)(KArgs...), dim3 grid, dim3 block, size_t
   return hipGetLastError();
 }
 
-// Largest M served by the single-workgroup routing/sort path and the fused
-// small-token kernels.
+// Largest M served by the single-workgroup routing/sort path and the
+// small-token kernels (down and combine in one launch).
 constexpr int kSmallM = 64;
 
 struct CallArgs {
@@ -93,11 +91,10 @@ hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t s);
 hipError_t launch_route_small(const moe_plan* p, const CallArgs& a, Ev ev);
 hipError_t launch_route(const moe_plan* p, const CallArgs& a, Ev ev);
 hipError_t launch_align(const moe_plan* p, const CallArgs& a, Ev ev);
-// fused = mid quantization done by the last item of each (tile, 128-block)
-hipError_t launch_gate_up(const moe_plan* p, const CallArgs& a, Ev ev, bool fused);
+hipError_t launch_gate_up(const moe_plan* p, const CallArgs& a, Ev ev);
 hipError_t launch_act_quant(const moe_plan* p, const CallArgs& a, Ev ev);
-// fused = combine done by the last slot of each (token, 256-column chunk)
-hipError_t launch_down(const moe_plan* p, const CallArgs& a, Ev ev, bool fused);
+// small M: down and the combine in one launch; y stays on chip
+hipError_t launch_down_combine(const moe_plan* p, const CallArgs& a, Ev ev);
 hipError_t launch_shared(const moe_plan* p, const CallArgs& a, Ev ev);
 // large M: LDS-staged 128-row tiles; gate/up includes the mid quantization
 hipError_t launch_gate_up_big(const moe_plan* p, const CallArgs& a, Ev ev);

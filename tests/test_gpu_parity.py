@@ -41,6 +41,11 @@ def _check_xq(gi, ref, tokens=None):
     assert np.array_equal(F.e2m1_decode(xq), F.e2m1_decode(ref["xq"])), "x E2M1 values differ"
 
 
+# the library writes y to the workspace only above this many tokens (below,
+# the combine runs inside the down launch)
+Y_WRITTEN_ABOVE_M = 64
+
+
 def _check_mid(gi_midq, gi_mids, ref_midq, ref_mids):
     d = e4m3_ulp_distance(gi_midq, ref_midq)
     assert d.max(initial=0) <= 1, f"mid codes more than one step apart: {d.max()}"
@@ -82,8 +87,10 @@ def test_stagewise_full(name):
     _check_xq(gi, ref)
     n = s.M * s.top_k
     frac = _check_mid(gi["midq"], gi["mids"], ref["midq"], ref["mids"])
-    ydiff = _check_y(gi["y"], ref["y"])
-    print(f"{name}: mid exact fraction {frac}, y differs in {ydiff} of {ref['y'].size}")
+    print(f"{name}: mid exact fraction {frac}")
+    if s.M > Y_WRITTEN_ABOVE_M:
+        ydiff = _check_y(gi["y"], ref["y"])
+        print(f"{name}: y differs in {ydiff} of {ref['y'].size}")
     ndiff = _check_out(gout, ref["out"])
     assert ndiff == 0, "expected the oracle's bf16 output exactly on these inputs"
 
