@@ -136,7 +136,7 @@ int moe_stage_count(void) { return kStages; }
 int moe_plan_stage_launches(const moe_plan* plan, int64_t M, int stage) {
   if (!plan || M < 0 || M > plan->s.M || stage < 0 || stage >= kStages) return -1;
   if (M == 0) return 0;
-  const bool small = M <= kSmallM;
+  const bool small = small_path(M, plan->s.top_k);
   switch (stage) {
     case 0: return 1;                             // route (+ sort + x quantization when small)
     case 1: return small ? 0 : 1;                 // align
@@ -284,7 +284,7 @@ moe_status moe_forward(moe_plan* plan, int64_t M, const void* x, const float* lo
   // counter: the device-scope release/acquire that needs writes back and
   // invalidates a whole L2 of an XCD per workgroup and costs more than a
   // launch.
-  const bool small = M <= kSmallM;
+  const bool small = small_path(M, plan->s.top_k);
   hipError_t e = small ? launch_route_small(plan, a, ev[0]) : launch_route(plan, a, ev[0]);
   if (e == hipSuccess) e = small ? none(1) : launch_align(plan, a, ev[1]);
   if (e == hipSuccess) e = small ? launch_gate_up(plan, a, ev[2]) : launch_gate_up_big(plan, a, ev[2]);

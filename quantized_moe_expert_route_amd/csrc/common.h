@@ -21,6 +21,15 @@ constexpr int kWave = 64;
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ uint32_t ld4(const void* p) { return *reinterpret_cast<const uint32_t*>(p); }
 
+// Workgroup barrier that orders LDS only: the fences are limited to the
+// local address space, so the barrier does not wait for the wave's global
+// loads still in flight (a plain __syncthreads() waits for all of them).
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ----------------------------------------------------------------- wave reductions
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -17,128 +17,278 @@
 #include "internal.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace qmoe {
 
-// Up to kSmallM tokens, down and combine are one launch. A workgroup owns 16
-// output columns of every token: its four waves take the 16-row tiles in turn
-// (tile i to wave i % 4), keep each (sorted row, column) result in LDS, and
-// when every tile is done the workgroup forms out[t, c0 .. c0 + 16) from the
-// token's k slots, so no slot result leaves the workgroup.
+// Up to kSmallM tokens (and kSmallRows entries), down and combine are one
+// launch. A workgroup owns 16 output columns of every token: its four waves
+// take contiguous runs of the 16-row tiles, keep each (entry, column) result
+// in LDS, and when every tile is done the workgroup forms out[t, c0 .. c0+16)
+// from the token's k slots, so no slot result leaves the workgroup.
 //
 // In MFMA step q of a 128-block, lane group g supplies K = 32g + 8q .. + 8:
-// a lane reads 32 contiguous mid bytes and 16 contiguous weight bytes (one MX
-// block with its one scale byte) per block. Each wave keeps D tiles of loads
-// in flight (weights from HBM, mid rows and scales from L2).
-constexpr int kDcMaxRows = kSmallM * 16;  // M * k on this path
+// a lane reads 16 contiguous weight bytes (one MX block, one scale byte) per
+// block. Each wave keeps the weights of D tiles in flight in a ring of
+// register slots, issued slot by slot; the ring's steady-state body has no
+// branches, so the wait for a slot counts only the loads issued after it,
+// and no tile is loaded twice. The tile descriptors arrive through scalar
+// loads, so the first weight loads do not queue behind the mid staging.
+//
+// MID_LDS: the n mid rows are widened to bf16 once per workgroup into LDS,
+// with their scales; otherwise each slot carries its tile's E4M3 mid rows
+// in registers and widens them itself. (Quantizing mid inside this launch
+// instead, redundantly per workgroup, measured slower than its own launch.)
+constexpr int kDcThreads = 256;
+constexpr int kDcWaves = kDcThreads / 64;
+constexpr int kDcMidBytes = 32 * 1024;  // n * I staged in LDS from E4M3: 8 uint4 per thread
+constexpr int kDcPad = 16;              // LDS bytes after each staged bf16 mid row
 
-template <int NB>
+template <int NB, bool MID_LDS>
 struct DcSlot {
-  uint4 w[NB];      // this lane's 32 E2M1 weights of each block
-  uint4 a[NB][2];   // this lane's 32 E4M3 mid bytes of each block
-  uint32_t ws[NB];  // the weights' E8M0 byte
-  float sc[NB][4];  // mid scales of the lane's four D rows
+  uint4 w[NB];                                            // this lane's 32 E2M1 weights of each block
+  typename std::conditional<NB == 1, uint32_t, typename std::conditional<NB == 2, uint2,
+      typename std::conditional<NB == 3, uint3, uint4>::type>::type>::type ws;  // the column's E8M0 bytes
+  uint4 a[MID_LDS ? 1 : NB][2];                           // this lane's 32 E4M3 mid bytes of each block
+  float sc[MID_LDS ? 1 : NB][4];                          // mid scales of the lane's four D rows
+  int ent[MID_LDS ? 1 : 4];                               // entries t*k+j of the lane's four D rows
 };
 
-template <int NB, int D>
-__global__ __launch_bounds__(256) void down_combine_kernel(
-    const uint8_t* __restrict__ midq, const float* __restrict__ mids, const uint8_t* __restrict__ w2,
-    const uint8_t* __restrict__ s2, const int* __restrict__ sorted_entry, const int4* __restrict__ tiles,
-    const int* __restrict__ meta, int H, int k, int M, const float* __restrict__ topk_w,
-    const float* __restrict__ ys, uint16_t* __restrict__ out) {
+__device__ __forceinline__ uint32_t scale_byte(uint32_t v, int b, int g) { return (v >> (8 * g)) & 0xFFu; }
+__device__ __forceinline__ uint32_t scale_byte(const uint2& v, int b, int g) {
+  return ((b == 0 ? v.x : v.y) >> (8 * g)) & 0xFFu;
+}
+__device__ __forceinline__ uint32_t scale_byte(const uint3& v, int b, int g) {
+  return ((b == 0 ? v.x : b == 1 ? v.y : v.z) >> (8 * g)) & 0xFFu;
+}
+__device__ __forceinline__ uint32_t scale_byte(const uint4& v, int b, int g) {
+  return ((b == 0 ? v.x : b == 1 ? v.y : b == 2 ? v.z : v.w) >> (8 * g)) & 0xFFu;
+}
+
+size_t down_combine_lds_bytes(int64_t n, int64_t I, bool mid_lds) {
+  size_t b = (size_t)(n + 1) * 16 * 4;
+  if (mid_lds) b += (size_t)n * (2 * I + kDcPad) + (size_t)n * (I / 128) * 4 + (size_t)n * 4;
+  return b;
+}
+
+__device__ __forceinline__ v8s as_v8s(uint32_t d0, uint32_t d1, uint32_t d2, uint32_t d3) {
+  v8s r;
+  r[0] = (short)(d0 & 0xFFFF); r[1] = (short)(d0 >> 16);
+  r[2] = (short)(d1 & 0xFFFF); r[3] = (short)(d1 >> 16);
+  r[4] = (short)(d2 & 0xFFFF); r[5] = (short)(d2 >> 16);
+  r[6] = (short)(d3 & 0xFFFF); r[7] = (short)(d3 >> 16);
+  return r;
+}
+
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_bf16(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
+template <int NB, int D, bool MID_LDS>
+__global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
+    const uint8_t* __restrict__ midq, const float* __restrict__ mids, const uint8_t* __restrict__ w2, const uint8_t* __restrict__ s2, const int* __restrict__ sorted_entry,
+    const int4* __restrict__ tiles, const int* __restrict__ meta, int H, int k, int M,
+    const float* __restrict__ topk_w, const float* __restrict__ ys, uint16_t* __restrict__ out) {
   constexpr int I = NB * 128;
-  __shared__ float yl[kDcMaxRows * 16];
-  __shared__ int inv[kDcMaxRows];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  constexpr int LDA = 2 * I + kDcPad;  // bytes per staged bf16 mid row
+  extern __shared__ __align__(16) uint8_t dyn[];
+  const int n = M * k;
+  float* yl = reinterpret_cast<float*>(dyn);            // [n + 1][16]; row n takes dropped rows
+  uint8_t* ml = reinterpret_cast<uint8_t*>(yl + (n + 1) * 16);  // [n][LDA]  (MID_LDS) bf16 mid
+  float* msl = reinterpret_cast<float*>(ml + n * LDA);  // [n][NB]   (MID_LDS)
+  int* sel = reinterpret_cast<int*>(msl + n * NB);      // [n]       (MID_LDS) sorted_entry
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int r = lane & 15, g = lane >> 4;
   const int c0 = blockIdx.x * 16;
-  const int n = M * k;
-  for (int q = tid; q < n; q += 256) inv[sorted_entry[q]] = q;
   const int nt = meta[0];
-  const int my = nt > wave ? (nt - wave + 3) / 4 : 0;  // tiles wave, wave + 4, ...
+  const int per = (nt + kDcWaves - 1) / kDcWaves;
+  const int base = wave * per;                                    // this wave's tiles [base, base + my)
+  const int my = max(0, min(per, nt - base));
 
-  auto load = [&](int i, DcSlot<NB>& S) {
-    const int4 tl = tiles[wave + 4 * i];
-    const uint8_t* pw = w2 + ((size_t)tl.x * H + c0 + r) * (I / 2) + 16 * g;
-    const uint8_t* ps = s2 + ((size_t)tl.x * H + c0 + r) * (I / 32) + g;
-    // rows past the tile's end read the tile's first row; their results are dropped
-    const int row = tl.y + r < tl.z ? tl.y + r : tl.y;
-    const uint8_t* pq = midq + (size_t)row * I + 32 * g;
+  // ---- descriptors of the wave's first D tiles, then the staging loads
+  // (both from L2); the weight loads wait only for the descriptors, the LDS
+  // staging waits for its loads after the weight loads have gone out.
+  // Slots past the wave's run repeat its last tile (computed again: the
+  // same values to the same places); a wave without tiles loads tile 0 and
+  // computes nothing. The loads are unconditional so that every later wait
+  // counts exactly.
+  int4 T[D];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      S.w[b] = ld16(pw + 64 * b);
-      S.ws[b] = ps[4 * b];
-      S.a[b][0] = ld16(pq + 128 * b);
-      S.a[b][1] = ld16(pq + 128 * b + 16);
+  for (int d = 0; d < D; ++d) T[d] = tiles[my > 0 ? base + min(d, my - 1) : 0];
+  __builtin_amdgcn_sched_barrier(0);
+  constexpr int kSt = MID_LDS ? kDcMidBytes / 16 / kDcThreads : 1;
+  uint4 st[kSt];
+  float sts = 0.f;
+  int ste = 0;
+  if (MID_LDS) {
+#pragma unroll
+    for (int q = 0; q < kSt; ++q) {
+      const int idx = tid + kDcThreads * q;
+      st[q] = idx < n * (I / 16) ? ld16(midq + 16 * (size_t)idx) : make_uint4(0, 0, 0, 0);
     }
+    sts = tid < n * NB ? mids[tid] : 0.f;
+    ste = tid < n ? sorted_entry[tid] : 0;
+  }
+
+  auto load = [&](const int4 tl, DcSlot<NB, MID_LDS>& S) {
+    const size_t col = (size_t)tl.x * H + c0 + r;
+    const uint8_t* pw = w2 + col * (I / 2) + 16 * g;
 #pragma unroll
-    for (int i2 = 0; i2 < 4; ++i2) {
-      const int m = tl.y + 4 * g + i2 < tl.z ? tl.y + 4 * g + i2 : tl.y;
+    for (int b = 0; b < NB; ++b) S.w[b] = ld16(pw + 64 * b);
+    S.ws = *reinterpret_cast<const decltype(S.ws)*>(s2 + col * (I / 32));
+    if (!MID_LDS) {
+      // rows past the tile's end read the tile's first row; their results are dropped
+      const int row = tl.y + r < tl.z ? tl.y + r : tl.y;
+      const uint8_t* pq = midq + (size_t)row * I + 32 * g;
 #pragma unroll
-      for (int b = 0; b < NB; ++b) S.sc[b][i2] = mids[(size_t)m * NB + b];
+      for (int b = 0; b < (MID_LDS ? 1 : NB); ++b) {
+        S.a[b][0] = ld16(pq + 128 * b);
+        S.a[b][1] = ld16(pq + 128 * b + 16);
+      }
+#pragma unroll
+      for (int i2 = 0; i2 < 4; ++i2) {
+        const int m = min(tl.y + 4 * g + i2, tl.z - 1);
+#pragma unroll
+        for (int b = 0; b < (MID_LDS ? 1 : NB); ++b) S.sc[b][i2] = mids[(size_t)m * NB + b];
+        S.ent[MID_LDS ? 0 : i2] = sorted_entry[m];
+      }
     }
   };
-  auto compute = [&](int i, const DcSlot<NB>& S) {
-    const int4 tl = tiles[wave + 4 * i];
+  auto compute = [&](const int4 tl, const DcSlot<NB, MID_LDS>& S) {
+    const int arow = min(tl.y + r, tl.z - 1);
     double acc[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const float wsc = e8m0_to_float(S.ws[b]);
-      const uint32_t qa[8] = {S.a[b][0].x, S.a[b][0].y, S.a[b][0].z, S.a[b][0].w,
-                              S.a[b][1].x, S.a[b][1].y, S.a[b][1].z, S.a[b][1].w};
+      const float wsc = e8m0_to_float(scale_byte(S.ws, b, g));
       const uint32_t qw[4] = {S.w[b].x, S.w[b].y, S.w[b].z, S.w[b].w};
+      float sc[4];
       v4f P = {0.f, 0.f, 0.f, 0.f};
+      if (MID_LDS) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t d0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(qa[2 * q], 1.0f, false));
-        const uint32_t d1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(qa[2 * q], 1.0f, true));
-        const uint32_t d2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(qa[2 * q + 1], 1.0f, false));
-        const uint32_t d3 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(qa[2 * q + 1], 1.0f, true));
-        v8s fa;
-        fa[0] = (short)(d0 & 0xFFFF); fa[1] = (short)(d0 >> 16);
-        fa[2] = (short)(d1 & 0xFFFF); fa[3] = (short)(d1 >> 16);
-        fa[4] = (short)(d2 & 0xFFFF); fa[5] = (short)(d2 >> 16);
-        fa[6] = (short)(d3 & 0xFFFF); fa[7] = (short)(d3 >> 16);
-        const uint32_t e0 = cvt_fp4x2_bf16<0>(qw[q], wsc), e1 = cvt_fp4x2_bf16<1>(qw[q], wsc);
-        const uint32_t e2 = cvt_fp4x2_bf16<2>(qw[q], wsc), e3 = cvt_fp4x2_bf16<3>(qw[q], wsc);
-        v8s fb;
-        fb[0] = (short)(e0 & 0xFFFF); fb[1] = (short)(e0 >> 16);
-        fb[2] = (short)(e1 & 0xFFFF); fb[3] = (short)(e1 >> 16);
-        fb[4] = (short)(e2 & 0xFFFF); fb[5] = (short)(e2 >> 16);
-        fb[6] = (short)(e3 & 0xFFFF); fb[7] = (short)(e3 >> 16);
-        P = mfma_bf16(fa, fb, P);
+        for (int i2 = 0; i2 < 4; ++i2) sc[i2] = msl[min(tl.y + 4 * g + i2, tl.z - 1) * NB + b];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint4 av = *reinterpret_cast<const uint4*>(ml + arow * LDA + 2 * (128 * b + 32 * g + 8 * q));
+          const v8s fa = as_v8s(av.x, av.y, av.z, av.w);
+          const v8s fb = as_v8s(cvt_fp4x2_bf16<0>(qw[q], wsc), cvt_fp4x2_bf16<1>(qw[q], wsc),
+                                cvt_fp4x2_bf16<2>(qw[q], wsc), cvt_fp4x2_bf16<3>(qw[q], wsc));
+          P = mfma_bf16(fa, fb, P);
+        }
+      } else {
+        const uint4 a0 = S.a[MID_LDS ? 0 : b][0], a1 = S.a[MID_LDS ? 0 : b][1];
+        const uint32_t qa[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) sc[i2] = S.sc[MID_LDS ? 0 : b][i2];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const v8s fa = as_v8s(fp8x2_bf16<false>(qa[2 * q]), fp8x2_bf16<true>(qa[2 * q]),
+                                fp8x2_bf16<false>(qa[2 * q + 1]), fp8x2_bf16<true>(qa[2 * q + 1]));
+          const v8s fb = as_v8s(cvt_fp4x2_bf16<0>(qw[q], wsc), cvt_fp4x2_bf16<1>(qw[q], wsc),
+                                cvt_fp4x2_bf16<2>(qw[q], wsc), cvt_fp4x2_bf16<3>(qw[q], wsc));
+          P = mfma_bf16(fa, fb, P);
+        }
       }
 #pragma unroll
-      for (int i2 = 0; i2 < 4; ++i2) acc[i2] += (double)S.sc[b][i2] * (double)P[i2];
+      for (int i2 = 0; i2 < 4; ++i2) acc[i2] += (double)sc[i2] * (double)P[i2];
     }
+    // rows past the tile's end go to the dropped row n
 #pragma unroll
     for (int i2 = 0; i2 < 4; ++i2) {
       const int m = tl.y + 4 * g + i2;
-      if (m < tl.z) yl[m * 16 + r] = (float)acc[i2];
+      const int ent = MID_LDS ? sel[min(m, tl.z - 1)] : S.ent[MID_LDS ? 0 : i2];
+      yl[(m < tl.z ? ent : n) * 16 + r] = (float)acc[i2];
     }
   };
 
-  if (my > 0) {
-    DcSlot<NB> S[D];
+  __builtin_amdgcn_sched_barrier(0);
+  // ---- the first D tiles' weights
+  DcSlot<NB, MID_LDS> S[D];
 #pragma unroll
-    for (int d = 0; d < D; ++d) load(d < my ? d : my - 1, S[d]);
-    for (int i0 = 0; i0 < my; i0 += D) {
+  for (int d = 0; d < D; ++d) {
+    load(T[d], S[d]);
+    __builtin_amdgcn_sched_barrier(0);  // slot by slot, in issue order
+  }
+
+  // ---- staged mid to LDS, widened to bf16
+  if (MID_LDS) {
+#pragma unroll
+    for (int q = 0; q < kSt; ++q) {
+      const int idx = tid + kDcThreads * q;
+      if (idx < n * (I / 16)) {
+        const int row = idx / (I / 16), c = idx - row * (I / 16);
+        uint4* dst = reinterpret_cast<uint4*>(ml + row * LDA + 32 * c);  // E4M3 -> bf16, exact
+        dst[0] = make_uint4(fp8x2_bf16<false>(st[q].x), fp8x2_bf16<true>(st[q].x), fp8x2_bf16<false>(st[q].y),
+                            fp8x2_bf16<true>(st[q].y));
+        dst[1] = make_uint4(fp8x2_bf16<false>(st[q].z), fp8x2_bf16<true>(st[q].z), fp8x2_bf16<false>(st[q].w),
+                            fp8x2_bf16<true>(st[q].w));
+      }
+    }
+    if (tid < n * NB) msl[tid] = sts;
+    if (tid < n) sel[tid] = ste;
+    barrier_lds();
+  }
+
+  // ---- the ring. A run that fits the slots is computed straight from the
+  // prologue's loads (one path, so each wait counts exactly); a longer one
+  // goes through full batches (every reload is a new tile), then the tail.
+  if (my > 0 && my <= D) {
+#pragma unroll
+    for (int d = 0; d < D; d += 2) {
+      compute(T[d], S[d]);
+      if (d + 1 < D) compute(T[d + 1], S[d + 1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else if (my > D) {
+    int i0 = 0;
+    for (; i0 + 2 * D <= my; i0 += D) {
+#pragma unroll
+      for (int d = 0; d < D; d += 2) {  // two independent tiles per step
+        const int4 tn0 = tiles[base + i0 + D + d];
+        const int4 tn1 = tiles[base + i0 + D + min(d + 1, D - 1)];
+        compute(T[d], S[d]);
+        if (d + 1 < D) compute(T[d + 1], S[d + 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        load(tn0, S[d]);
+        T[d] = tn0;
+        if (d + 1 < D) {
+          load(tn1, S[d + 1]);
+          T[d + 1] = tn1;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // the slots hold tiles i0 .. i0 + D - 1 (past my: repeats of the last);
+    // fewer than D tiles remain after them
+#pragma unroll
+    for (int d = 0; d < D; d += 2) {
+      compute(T[d], S[d]);
+      if (d + 1 < D) compute(T[d + 1], S[d + 1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const int rest = my - i0 - D;  // tiles after the slots' ones: fewer than D
+    if (rest > 0) {
 #pragma unroll
       for (int d = 0; d < D; ++d) {
-        const int i = i0 + d;
-        if (i < my) compute(i, S[d]);
-        load(i + D < my ? i + D : my - 1, S[d]);
+        if (d < rest) {
+          T[d] = tiles[base + i0 + D + d];
+          load(T[d], S[d]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
+#pragma unroll
+      for (int d = 0; d < D; ++d)
+        if (d < rest) compute(T[d], S[d]);
     }
   }
   __syncthreads();
   // out[t, c0 + 2p .. + 2): float64 products and sum in slot order (+ shared), one bf16 rounding
-  for (int idx = tid; idx < M * 8; idx += 256) {
+  for (int idx = tid; idx < M * 8; idx += kDcThreads) {
     const int t = idx >> 3, cc = 2 * (idx & 7);
     double a0 = 0.0, a1 = 0.0;
     for (int j = 0; j < k; ++j) {
       const double wj = (double)topk_w[t * k + j];
-      const float* py = yl + inv[t * k + j] * 16 + cc;
+      const float* py = yl + (t * k + j) * 16 + cc;
       a0 += wj * (double)py[0];
       a1 += wj * (double)py[1];
     }
@@ -185,20 +335,25 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 hipError_t launch_down_combine(const moe_plan* p, const CallArgs& a, Ev ev) {
   const int H = (int)p->s.H;
-  if (a.M * p->s.top_k > kDcMaxRows) return hipErrorInvalidValue;
+  const int64_t n = a.M * p->s.top_k, I = p->s.I;
+  if (n > kSmallRows) return hipErrorInvalidValue;
+  const bool mid_lds = n * I <= kDcMidBytes && n * (I / 128) <= kDcThreads && n <= kDcThreads;
+  const size_t lds = down_combine_lds_bytes(n, I, mid_lds);
+  if (lds > 160 * 1024) return hipErrorInvalidValue;
   const float* ys = p->s.shared_I > 0 ? wsp<float>(p, p->L.sh_y) : nullptr;
   auto go = [&](auto kern) {
-    return launch_k(kern, dim3(H / 16), dim3(256), 0, a.stream, ev, wsp<uint8_t>(p, p->L.midq),
+    return launch_k(kern, dim3(H / 16), dim3(kDcThreads), lds, a.stream, ev, wsp<uint8_t>(p, p->L.midq),
                     wsp<float>(p, p->L.mids), reinterpret_cast<const uint8_t*>(a.w2),
                     reinterpret_cast<const uint8_t*>(a.s2), wsp<int>(p, p->L.sorted_entry), wsp<int4>(p, p->X.tiles),
                     wsp<int>(p, p->X.meta), H, (int)p->s.top_k, (int)a.M, wsp<float>(p, p->L.topk_w), ys,
                     reinterpret_cast<uint16_t*>(a.out));
   };
-  switch (p->s.I / 128) {
-    case 1: return go(down_combine_kernel<1, 8>);
-    case 2: return go(down_combine_kernel<2, 4>);
-    case 3: return go(down_combine_kernel<3, 3>);
-    case 4: return go(down_combine_kernel<4, 2>);
+  // weights of D tiles in flight per wave; fewer when the slots also carry mid rows
+  switch (I / 128) {
+    case 1: return mid_lds ? go(down_combine_kernel<1, 8, true>) : go(down_combine_kernel<1, 6, false>);
+    case 2: return mid_lds ? go(down_combine_kernel<2, 8, true>) : go(down_combine_kernel<2, 3, false>);
+    case 3: return mid_lds ? go(down_combine_kernel<3, 5, true>) : go(down_combine_kernel<3, 2, false>);
+    case 4: return mid_lds ? go(down_combine_kernel<4, 4, true>) : go(down_combine_kernel<4, 2, false>);
     default: return hipErrorInvalidValue;
   }
 }

@@ -34,15 +34,6 @@ __device__ __forceinline__ void xcd_run(int n_items, int& first, int& stride, in
   end = min(n_items, (x + 1) * run);
 }
 
-// Workgroup barrier that orders LDS only: the fences are limited to the
-// local address space, so the barrier does not wait for the wave's global
-// loads still in flight (a plain __syncthreads() waits for all of them).
-__device__ __forceinline__ void barrier_lds() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 constexpr int kLDG = 80;  // LDS bytes per row of a 64-byte K-step slice (+16 pad)
 
 struct GuSmem {

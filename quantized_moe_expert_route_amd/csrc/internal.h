@@ -67,9 +67,12 @@ inline hipError_t launch_k(void (*kern)(KArgs...), dim3 grid, dim3 block, size_t
   return hipGetLastError();
 }
 
-// Largest M served by the single-workgroup routing/sort path and the
-// small-token kernels (down and combine in one launch).
+// Largest M (and M * top_k) served by the single-workgroup routing/sort
+// path and the small-token kernels (down and combine in one launch, whose
+// per-entry results must fit in LDS).
 constexpr int kSmallM = 64;
+constexpr int kSmallRows = 896;
+inline bool small_path(int64_t M, int64_t k) { return M <= kSmallM && M * k <= kSmallRows; }
 
 struct CallArgs {
   int64_t M;
