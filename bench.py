@@ -4,14 +4,18 @@
 
 One step = one complete call (route, align, gate/up, mid quant, down, combine
 [, shared expert]) on one batch of synthetic inputs already resident in HBM.
-Protocol: the call is captured in a HIP graph; before every timed replay a
-1 GiB buffer is read (a reduction) so the weights are not in the 256 MB MALL
-(cold, the regime of a model whose 75 layers of experts never fit in it) and
-the MALL holds only clean lines (a flush that writes would leave dirty lines
-whose write-back competes with the measured call); each replay is bracketed
-by events on the replay stream. value = mean cold
-microseconds per call. The stage durations come from events the library
-records between its launches (eager calls, same cold protocol).
+Protocol: before every timed call a 1 GiB buffer is read (a reduction) so the
+weights are not in the 256 MB MALL (cold, the regime of a model whose 75
+layers of experts never fit in it) and the MALL holds only clean lines (a
+flush that writes would leave dirty lines whose write-back competes with the
+measured call). value = mean cold device span per call: from the start of
+the call's first kernel to the end of its last kernel, read from events the
+library binds to those two launches (the host's launch latency is outside
+it, as it is for a layer inside a captured model step). The same calls as
+hipGraph replays bracketed by stream events are reported beside it
+(us_per_call_graph_replay: adds the runtime's graph launch latency). The
+stage durations come from events the library binds to each stage's first
+and last launch (eager calls, same cold protocol).
 
 Prints one JSON line.
 """
@@ -125,15 +129,33 @@ def measure(name, steps, warmup, n_sets):
         call()
     torch.cuda.synchronize()
 
-    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    # timed region: K cold calls; each call's device span (its first kernel's
+    # start to its last kernel's end) comes from events the library records
+    # with those two launches, so host launch latency is not in it
+    cev = HipEvents(2 * steps)
     for i in range(warmup):
         x.copy_(sets[i % n_sets][0])
         logits.copy_(sets[i % n_sets][1])
         torch.sum(flush, 0, out=sink)
-        graph.replay()
+        call()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for i in range(steps):
+        x.copy_(sets[i % n_sets][0])
+        logits.copy_(sets[i % n_sets][1])
+        torch.sum(flush, 0, out=sink)
+        plan.set_call_events(cev.handles[2 * i], cev.handles[2 * i + 1])
+        call()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    plan.set_call_events(None, None)
+    cold_us = np.array([cev.elapsed_ms(2 * i, 2 * i + 1) * 1000.0 for i in range(steps)])
+    cev.close()
+
+    # the same calls as graph replays, timed by stream events around each
+    # replay (adds the graph launch latency of the host runtime)
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     for i in range(steps):
         x.copy_(sets[i % n_sets][0])
         logits.copy_(sets[i % n_sets][1])
@@ -142,8 +164,7 @@ def measure(name, steps, warmup, n_sets):
         graph.replay()
         ev1[i].record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    cold_us = np.array([a.elapsed_time(b) * 1000.0 for a, b in zip(ev0, ev1)])
+    graph_us = np.array([a.elapsed_time(b) * 1000.0 for a, b in zip(ev0, ev1)])
 
     # warm: the same inputs back to back (weights partly MALL-resident)
     x.copy_(sets[0][0])
@@ -180,7 +201,7 @@ def measure(name, steps, warmup, n_sets):
     per_set_act = [n_act[i % n_sets] for i in range(steps)]
     mean_act = float(np.mean(per_set_act))
     res = {
-        "name": name, "shape": s, "cold_us": cold_us, "warm_us": warm_us, "wall_s": wall,
+        "name": name, "shape": s, "cold_us": cold_us, "graph_us": graph_us, "warm_us": warm_us, "wall_s": wall,
         "stage_us": dict(zip(names, kern_us.mean(0).tolist())), "n_act": mean_act,
         "n_act_sets": n_act, "bytes": float(np.mean([call_bytes(s, a) for a in per_set_act])),
         "gate_up_bytes": float(np.mean([gate_up_bytes(s, a) for a in per_set_act])),
@@ -253,14 +274,16 @@ def main():
     from quantized_moe_expert_route_amd import fixtures as X
 
     head = measure(args.config, args.steps, args.warmup, args.sets)
-    print(f"[bench] {args.config}: cold {head['cold_us'].mean():.1f} us, warm {head['warm_us']:.1f} us, "
+    print(f"[bench] {args.config}: cold {head['cold_us'].mean():.1f} us (graph replay {head['graph_us'].mean():.1f}), "
+          f"warm {head['warm_us']:.1f} us, "
           f"stages {json.dumps({k: round(v, 1) for k, v in head['stage_us'].items()})}", file=sys.stderr, flush=True)
     others = {}
     for name in [c for c in args.also.split(",") if c and c != args.config]:
         r = measure(name, max(10, args.steps // 2), max(3, args.warmup // 2), min(args.sets, 4))
         mu = r["cold_us"].mean()
         others[name] = {
-            "us_per_call_cold": round(mu, 2), "us_per_call_warm": round(r["warm_us"], 2),
+            "us_per_call_cold": round(mu, 2), "us_per_call_graph_replay": round(float(r["graph_us"].mean()), 2),
+            "us_per_call_warm": round(r["warm_us"], 2),
             "n_active_experts": round(r["n_act"], 1),
             "hbm_frac": round(r["bytes"] / (mu * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "fp4_mfma_frac": round(r["flops"] / (mu * 1e-6) / 1e12 / FP4_PEAK_TFLOPS, 4),
@@ -289,9 +312,11 @@ def main():
             "workload": f"{args.config}: {X.WORKLOAD_TITLES[args.config]}",
             "M": s.M, "H": s.H, "E": s.E, "I": s.I, "top_k": s.top_k, "routed_scaling": s.routed_scaling,
             "shared_I": s.shared_I, "n_active_experts": round(head["n_act"], 2),
-            "protocol": "cold: 1 GiB read before each replay; events around the replay",
+            "protocol": "cold: a 1 GiB read before each call; value = device span of the call (its first "
+                        "kernel's start to its last kernel's end, events bound to those launches)",
         },
         "us_per_call_p50": round(float(np.median(head["cold_us"])), 3),
+        "us_per_call_graph_replay": round(float(head["graph_us"].mean()), 3),
         "us_per_call_warm": round(head["warm_us"], 3),
         "hbm_frac_call": round(head["bytes"] / (mu * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "fp4_mfma_frac_call": round(head["flops"] / (mu * 1e-6) / 1e12 / FP4_PEAK_TFLOPS, 6),

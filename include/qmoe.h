@@ -147,6 +147,14 @@ moe_status moe_forward(moe_plan* plan, int64_t M, const void* x, const float* lo
  * 2 * moe_stage_count(). NULL disables. */
 moe_status moe_plan_set_stage_events(moe_plan* plan, void* const* events, int n);
 
+/* Profiling aid: when `start` and `stop` are non-NULL hipEvent_t handles,
+ * moe_forward records `start` as its first kernel begins and `stop` as its
+ * last kernel ends, so hipEventElapsedTime(start, stop) is the call's device
+ * time without the host's launch latency. Replaces the stage events above
+ * (and they replace these); NULL, NULL disables. Both or neither must be
+ * NULL, else MOE_ERR_INVALID_ARG. */
+moe_status moe_plan_set_call_events(moe_plan* plan, void* start, void* stop);
+
 /* Number and names of the launch stages of a call (for the events above). */
 int moe_stage_count(void);
 const char* moe_stage_name(int i);

@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
     L.moe_plan_set_shared.argtypes = [vp, vp, vp, vp, vp]
     L.moe_plan_set_stage_events.restype = st
     L.moe_plan_set_stage_events.argtypes = [vp, ctypes.POINTER(vp), ctypes.c_int]
+    L.moe_plan_set_call_events.restype = st
+    L.moe_plan_set_call_events.argtypes = [vp, vp, vp]
     L.moe_plan_stage_launches.restype = ctypes.c_int
     L.moe_plan_stage_launches.argtypes = [vp, i64, ctypes.c_int]
     L.moe_forward.restype = st
@@ -154,6 +156,15 @@ class Plan:
             self._events = arr
         if st != MOE_OK:
             raise MoeError(st, "moe_plan_set_stage_events")
+
+    def set_call_events(self, start, stop):
+        """start/stop: raw hipEvent_t handles (ints) recorded at the first
+        kernel's start and the last kernel's end of every call; None clears."""
+        st = lib().moe_plan_set_call_events(self._h, start, stop)
+        if st != MOE_OK:
+            raise MoeError(st, "moe_plan_set_call_events")
+        if start is not None:
+            self._events = None
 
     def forward(self, x, logits, w13, s13, w2, s2, out, M: Optional[int] = None, stream=None):
         """Enqueue the call on `stream` (default: torch's current stream)."""

@@ -240,6 +240,16 @@ moe_status moe_plan_set_stage_events(moe_plan* plan, void* const* events, int n)
     plan->events[i] = (hipEvent_t)events[i];
   }
   plan->n_events = n;
+  plan->call_start = plan->call_stop = nullptr;
+  return MOE_OK;
+}
+
+moe_status moe_plan_set_call_events(moe_plan* plan, void* start, void* stop) {
+  if (!plan) return MOE_ERR_INVALID_ARG;
+  if (!start != !stop) return MOE_ERR_INVALID_ARG;
+  plan->call_start = (hipEvent_t)start;
+  plan->call_stop = (hipEvent_t)stop;
+  if (start) plan->n_events = 0;
   return MOE_OK;
 }
 
@@ -264,9 +274,14 @@ moe_status moe_forward(moe_plan* plan, int64_t M, const void* x, const float* lo
   DeviceGuard guard(plan->device);
   if (!guard.ok) return MOE_ERR_DEVICE;
   CallArgs a{M, x, logits, w13, s13, w2, s2, out, (hipStream_t)stream};
+  const bool small = small_path(M, plan->s.top_k);
   Ev ev[kStages];
   if (plan->n_events)
     for (int i = 0; i < kStages; ++i) ev[i] = Ev{plan->events[2 * i], plan->events[2 * i + 1]};
+  if (plan->call_start) {
+    ev[0].start = plan->call_start;             // the route launch comes first
+    ev[small ? 5 : 6].stop = plan->call_stop;   // down (+ combine) or the combine comes last
+  }
   // a stage with no launch of its own still records its (empty) interval
   auto none = [&](int i) -> hipError_t {
     if (!plan->n_events) return hipSuccess;
@@ -284,7 +299,6 @@ moe_status moe_forward(moe_plan* plan, int64_t M, const void* x, const float* lo
   // counter: the device-scope release/acquire that needs writes back and
   // invalidates a whole L2 of an XCD per workgroup and costs more than a
   // launch.
-  const bool small = small_path(M, plan->s.top_k);
   hipError_t e = small ? launch_route_small(plan, a, ev[0]) : launch_route(plan, a, ev[0]);
   if (e == hipSuccess) e = small ? none(1) : launch_align(plan, a, ev[1]);
   if (e == hipSuccess) e = small ? launch_gate_up(plan, a, ev[2]) : launch_gate_up_big(plan, a, ev[2]);

@@ -48,6 +48,7 @@ struct moe_plan {
   const float* ss2;
   hipEvent_t events[16];
   int n_events;
+  hipEvent_t call_start, call_stop;
 };
 
 namespace qmoe {
