@@ -262,6 +262,9 @@ def main():
     ap.add_argument("--also", default="c2,c3,c4", help="more workloads reported in the same line ('' for none)")
     ap.add_argument("--sets", type=int, default=8, help="distinct input batches cycled through the steps")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 5 plain device-to-device copies of MIB MiB (the known-size kernel that "
+                         "scales the HBM byte counters of a profiler run), then exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -271,6 +274,15 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = args.copy_calibration * 1024 * 1024 // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": 4 * n, "copy_calibration_bytes_written": 4 * n, "copies": 5}))
+        return
     from quantized_moe_expert_route_amd import fixtures as X
 
     head = measure(args.config, args.steps, args.warmup, args.sets)
