@@ -35,6 +35,7 @@ __device__ __forceinline__ void xcd_run(int n_items, int& first, int& stride, in
 }
 
 constexpr int kLDG = 80;  // LDS bytes per row of a 64-byte K-step slice (+16 pad)
+constexpr int kGuStages = 4;  // K-steps of gate/up loads held in registers
 
 struct GuSmem {
   uint8_t a[2][kBM * kLDG];   // x rows (MXFP4), K-step slice
@@ -146,29 +147,28 @@ __global__ __launch_bounds__(256) void gate_up_big_kernel(
         }
       }
     };
-    // K-steps kk+1..kk+3 are in flight while kk is multiplied: step kk's
-    // registers are refilled with step kk+3 right after they were stored.
-    // Past the last step the loads repeat it and the stores fill a buffer
-    // nobody reads; only the MFMA work is skipped.
-    GuRegs S0, S1, S2;
-    auto iter = [&](int kk, GuRegs& cur, GuRegs& nxt) {
-      load(min(kk + 3, nk - 1), cur);
-      if (kk < nk) compute(kk & 1);
-      store(nxt, (kk + 1) & 1);
-      barrier_lds();
-    };
-    load(0, S0);
-    load(min(1, nk - 1), S1);
-    load(min(2, nk - 1), S2);
-    store(S0, 0);
+    // K-steps kk+1..kk+kGuStages are in flight while kk is multiplied: step
+    // kk's registers are refilled with step kk+kGuStages right after they
+    // were stored. Past the last step the loads repeat it and the stores fill
+    // a buffer nobody reads; only the MFMA work is skipped.
+    GuRegs S[kGuStages];
+#pragma unroll
+    for (int q = 0; q < kGuStages; ++q) load(min(q, nk - 1), S[q]);
+    store(S[0], 0);
     barrier_lds();
-    for (int kk = 0; kk < nk; kk += 3) {
-      iter(kk, S0, S1);
-      iter(kk + 1, S1, S2);
-      iter(kk + 2, S2, S0);
+    for (int kk = 0; kk < nk; kk += kGuStages) {
+#pragma unroll
+      for (int q = 0; q < kGuStages; ++q) {
+        load(min(kk + q + kGuStages, nk - 1), S[q]);
+        if (kk + q < nk) compute((kk + q) & 1);
+        store(S[(q + 1) % kGuStages], (kk + q + 1) & 1);
+        barrier_lds();
+      }
     }
     // ---- epilogue: h = SiLU(g) * u (float64, one rounding), row amax over
     // the item's 128 columns, s = amax / 448, q = E4M3(h / s)
+    // (rows past the tile's end are skipped: a quarter-wave's four rows are
+    // uniform per (i, v), so a wave whose rows are all padding branches over)
     float hv[4][4][4];
     float pm[4][4];
 #pragma unroll
@@ -176,9 +176,10 @@ __global__ __launch_bounds__(256) void gate_up_big_kernel(
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         float m = 0.f;
+        const bool live = 64 * wm + 16 * i + 4 * g + v < rows;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          hv[i][j][v] = silu_mul(accg[i][j][v], accu[i][j][v]);
+          hv[i][j][v] = live ? silu_mul(accg[i][j][v], accu[i][j][v]) : 0.f;
           m = fmaxf(m, fabsf(hv[i][j][v]));
         }
         pm[i][v] = m;
@@ -206,7 +207,7 @@ __global__ __launch_bounds__(256) void gate_up_big_kernel(
         const float sc = __fdiv_rn(amax, 448.0f);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const uint32_t c = sc > 0.f ? e4m3_code(__fdiv_rn(hv[i][j][v], sc)) : 0u;
+          const uint32_t c = sc > 0.f && row < rows ? e4m3_code(__fdiv_rn(hv[i][j][v], sc)) : 0u;
           qs[row * 128 + 64 * wn + 16 * j + r] = (uint8_t)c;
         }
         if (wn == 0 && r == 0 && row < rows) mids[(size_t)(r0 + row) * (I / 128) + ib] = sc;

@@ -6,32 +6,14 @@
 // glm52 mono): serve a BF16-attention checkpoint" (group-128 FP8
 // activations): x is quantized per token per 128 channels to E4M3 with an
 // fp32 scale (the same rule as the mid blocks), gate/up and down run on the
-// FP8 codes widened to bf16, every 128-block partial is scaled by the
-// activation scale times the weight block scale in float64, and h is
-// quantized like the routed mid.
+// FP8 MFMA, every 128-block partial is scaled by the activation scale times
+// the weight block scale, and h is quantized like the routed mid.
 #include "common.h"
 #include "internal.h"
 
 #include <algorithm>
 
 namespace qmoe {
-
-struct E4m3Bf16TableS {
-  uint16_t v[256];
-  constexpr E4m3Bf16TableS() : v() {
-    for (int c = 0; c < 256; ++c) v[c] = e4m3_to_bf16_bits((uint32_t)c);
-  }
-};
-__constant__ E4m3Bf16TableS kE4m3Bf16S = E4m3Bf16TableS();
-
-__device__ __forceinline__ v8s e4m3x8_bf16(uint32_t lo, uint32_t hi, const uint16_t* tab) {
-  v8s r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = (short)tab[(lo >> (8 * i)) & 0xFFu];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[4 + i] = (short)tab[(hi >> (8 * i)) & 0xFFu];
-  return r;
-}
 
 // x bf16 [M, H] -> E4M3 [M, H] + fp32 scale per 128; one wave per block.
 __global__ __launch_bounds__(256) void sh_quant_x_kernel(const uint16_t* __restrict__ x, int M, int H,
@@ -56,75 +38,172 @@ __global__ __launch_bounds__(256) void sh_quant_x_kernel(const uint16_t* __restr
   }
 }
 
-// out[t, o] = fl32( sum_kb a_scale[t, kb] * w_scale[o/128, kb] * (a_kb . w_kb) )
-// for a 16x16 tile per wave; a [rows, K] E4M3 with fp32 scales per 128 along
-// K, w [N, K] E4M3 with fp32 scales per 128x128. With GATED, the tile's
-// columns o and o + N/2 are gate and up and the output is SiLU(g) * u.
+// out[t, o] = sum_kb a_scale[t, kb] * w_scale[o/128, kb] * (a_kb . w_kb), a
+// [rows, K] E4M3 with fp32 scales per 128 along K, w [N, K] E4M3 with fp32
+// scales per 128x128 block. With GATED the output is SiLU(g) * u, g and u
+// from weight rows o and o + n_out.
+//
+// Workgroup tile: 128 token rows x 128 weight rows (GATED: 64 gate + the 64
+// matching up rows, 64 outputs; else 128 outputs), one 128-K block per step:
+// both operands staged in LDS as E4M3 through two register-held steps in
+// flight; each wave multiplies 64 rows x 64 weight rows: the E4M3 codes are
+// widened to bf16 as they are read (exact) and multiplied on the bf16 MFMA
+// (exact products, fp32 sums inside the block), and the block's partial
+// times (activation scale x weight scale) is added into fp32 accumulators.
+// (The FP8 MFMA drops products far below the largest of their 32-group; its
+// error, amplified by the E4M3 requantization of h, exceeded the output
+// tolerance.) E4M3 x E4M3 block sums can need more than binary32's 24 bits,
+// so these outputs are close to, not equal to, the exact ones.
+constexpr int kShBM = 128;  // token rows per tile
+constexpr int kShLD = 144;  // LDS bytes per staged 128-byte row (+16 pad)
+
+struct ShSmem {
+  uint8_t a[2][kShBM * kShLD];
+  uint8_t b[2][128 * kShLD];
+  float as[2][kShBM];
+};
+
+struct ShRegs {
+  uint4 a[4], b[4];
+  float sa;
+};
+
+// 8 E4M3 codes (two dwords, low byte first) -> 8 bf16, exact
+__device__ __forceinline__ v8s e4m3x8_to_bf16(uint2 w) {
+  const uint32_t d0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false));
+  const uint32_t d1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true));
+  const uint32_t d2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false));
+  const uint32_t d3 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true));
+  v8s r;
+  r[0] = (short)(d0 & 0xFFFF); r[1] = (short)(d0 >> 16);
+  r[2] = (short)(d1 & 0xFFFF); r[3] = (short)(d1 >> 16);
+  r[4] = (short)(d2 & 0xFFFF); r[5] = (short)(d2 >> 16);
+  r[6] = (short)(d3 & 0xFFFF); r[7] = (short)(d3 >> 16);
+  return r;
+}
+
 template <bool GATED>
-__global__ __launch_bounds__(256) void sh_linear_kernel(const uint8_t* __restrict__ a, const float* __restrict__ as,
-                                                        const uint8_t* __restrict__ w, const float* __restrict__ ws,
-                                                        int rows, int K, int N, float* __restrict__ out) {
-  __shared__ uint16_t tab[256];
-  tab[threadIdx.x] = kE4m3Bf16S.v[threadIdx.x];
-  __syncthreads();
-  const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
-  const int n_out = GATED ? N / 2 : N;
-  const int tiles_n = n_out / 16, tiles_m = (rows + 15) / 16;
+__global__ __launch_bounds__(256) void sh_gemm_kernel(const uint8_t* __restrict__ a, const float* __restrict__ as,
+                                                      const uint8_t* __restrict__ w, const float* __restrict__ ws,
+                                                      int rows, int K, int n_out, float* __restrict__ out) {
+  __shared__ ShSmem sm;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int r = lane & 15, g = lane >> 4;
+  constexpr int BN = GATED ? 64 : 128;  // outputs per tile
+  const int tiles_n = n_out / BN;
+  const int row0 = (blockIdx.x / tiles_n) * kShBM, o0 = (blockIdx.x % tiles_n) * BN;
   const int nkb = K / 128;
-  const int kbw = K / 128;  // weight scale row length
-  for (int wv = blockIdx.x * 4 + (threadIdx.x >> 6); wv < tiles_m * tiles_n; wv += gridDim.x * 4) {
-    const int tm = wv / tiles_n, tn = wv % tiles_n;
-    const int row = tm * 16 + r;
-    const bool rv = row < rows;
-    const int o = tn * 16 + r;  // this lane's weight row (B column)
-    const uint8_t* pa = a + (size_t)(rv ? row : 0) * K;
-    const uint8_t* pg = w + (size_t)o * K;
-    const uint8_t* pu = w + (size_t)(o + n_out) * K;
-    double accg[4] = {0, 0, 0, 0}, accu[4] = {0, 0, 0, 0};
-    for (int kb = 0; kb < nkb; ++kb) {
-      uint4 a0 = make_uint4(0, 0, 0, 0), a1 = make_uint4(0, 0, 0, 0);
-      if (rv) {
-        a0 = ld16(pa + kb * 128 + g * 32);
-        a1 = ld16(pa + kb * 128 + g * 32 + 16);
-      }
-      const v8s A0 = e4m3x8_bf16(a0.x, a0.y, tab), A1 = e4m3x8_bf16(a0.z, a0.w, tab);
-      const v8s A2 = e4m3x8_bf16(a1.x, a1.y, tab), A3 = e4m3x8_bf16(a1.z, a1.w, tab);
-      v4f P = {0, 0, 0, 0}, Q = {0, 0, 0, 0};
-      {
-        const uint4 b0 = ld16(pg + kb * 128 + g * 32), b1 = ld16(pg + kb * 128 + g * 32 + 16);
-        P = mfma_bf16(A0, e4m3x8_bf16(b0.x, b0.y, tab), P);
-        P = mfma_bf16(A1, e4m3x8_bf16(b0.z, b0.w, tab), P);
-        P = mfma_bf16(A2, e4m3x8_bf16(b1.x, b1.y, tab), P);
-        P = mfma_bf16(A3, e4m3x8_bf16(b1.z, b1.w, tab), P);
-      }
-      if (GATED) {
-        const uint4 b0 = ld16(pu + kb * 128 + g * 32), b1 = ld16(pu + kb * 128 + g * 32 + 16);
-        Q = mfma_bf16(A0, e4m3x8_bf16(b0.x, b0.y, tab), Q);
-        Q = mfma_bf16(A1, e4m3x8_bf16(b0.z, b0.w, tab), Q);
-        Q = mfma_bf16(A2, e4m3x8_bf16(b1.x, b1.y, tab), Q);
-        Q = mfma_bf16(A3, e4m3x8_bf16(b1.z, b1.w, tab), Q);
-      }
-      // D rows 4g+i (activations), column r (weights)
-      const double wsg = (double)ws[(size_t)(o / 128) * kbw + kb];
-      const double wsu = GATED ? (double)ws[(size_t)((o + n_out) / 128) * kbw + kb] : 0.0;
+  // tile weight row rr -> weight matrix row
+  auto brow = [&](int rr) { return GATED ? (rr < 64 ? o0 + rr : n_out + o0 + rr - 64) : o0 + rr; };
+  // staging: 128-byte rows in 8 chunks of 16; rows past the end read the
+  // last row (their results are never written)
+  const uint8_t* pa[4];
+  const uint8_t* pb[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = tm * 16 + 4 * g + i;
-        const double sa = m < rows ? (double)as[(size_t)m * nkb + kb] : 0.0;
-        accg[i] += (sa * wsg) * (double)P[i];
-        if (GATED) accu[i] += (sa * wsu) * (double)Q[i];
-      }
+  for (int q = 0; q < 4; ++q) {
+    const int idx = tid + 256 * q;
+    pa[q] = a + (size_t)min(row0 + (idx >> 3), rows - 1) * K + 16 * (idx & 7);
+    pb[q] = w + (size_t)brow(idx >> 3) * K + 16 * (idx & 7);
+  }
+  const float* psa = as + (size_t)min(row0 + (tid & (kShBM - 1)), rows - 1) * nkb;
+  const float* pwg = ws + (size_t)(brow(0) / 128) * nkb;
+  const float* pwu = ws + (size_t)(brow(127) / 128) * nkb;
+  auto load = [&](int kb, ShRegs& R) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      R.a[q] = ld16(pa[q] + 128 * kb);
+      R.b[q] = ld16(pb[q] + 128 * kb);
+    }
+    R.sa = psa[kb];
+  };
+  auto store = [&](const ShRegs& R, int s) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int idx = tid + 256 * q;
+      *reinterpret_cast<uint4*>(&sm.a[s][(idx >> 3) * kShLD + 16 * (idx & 7)]) = R.a[q];
+      *reinterpret_cast<uint4*>(&sm.b[s][(idx >> 3) * kShLD + 16 * (idx & 7)]) = R.b[q];
+    }
+    if (tid < kShBM) sm.as[s][tid] = R.sa;
+  };
+  float acc[4][4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[i][j][v] = 0.f;
+  // wave (wm, wn): rows 64 wm .. + 64; weight rows: GATED gate 32 wn + 16 j
+  // (j < 2) and up 64 + 32 wn + 16 (j - 2); else 64 wn + 16 j
+  auto wrow = [&](int j) { return GATED ? (j < 2 ? 32 * wn + 16 * j : 64 + 32 * wn + 16 * (j - 2)) : 64 * wn + 16 * j; };
+  // in bf16 MFMA step q of a 128-block, lane group g supplies K = 32g + 8q .. + 8
+  auto compute = [&](int s, int kb) {
+    const float swg = pwg[kb], swu = pwu[kb];
+    v4f P[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) P[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v8s fa[4], fb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        fa[i] = e4m3x8_to_bf16(*reinterpret_cast<const uint2*>(&sm.a[s][(64 * wm + 16 * i + r) * kShLD + 32 * g + 8 * q]));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        fb[j] = e4m3x8_to_bf16(*reinterpret_cast<const uint2*>(&sm.b[s][(wrow(j) + r) * kShLD + 32 * g + 8 * q]));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) P[i][j] = mfma_bf16(fa[i], fb[j], P[i][j]);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int m = tm * 16 + 4 * g + i;
-      if (m < rows) {
-        float v = (float)accg[i];
-        if (GATED) v = silu_mul(v, (float)accu[i]);
-        out[(size_t)m * n_out + o] = v;
+      float sa[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sa[v] = sm.as[s][64 * wm + 16 * i + 4 * g + v];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float sw = GATED && j >= 2 ? swu : swg;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[i][j][v] = fmaf(P[i][j][v], sa[v] * sw, acc[i][j][v]);
       }
     }
+  };
+  ShRegs S0, S1;
+  load(0, S0);
+  load(min(1, nkb - 1), S1);
+  store(S0, 0);
+  barrier_lds();
+  // step kb is multiplied while kb + 1 and kb + 2 are in flight; past the last
+  // step the loads repeat it and the stores fill a buffer nobody reads
+  for (int kb = 0; kb < nkb; kb += 2) {
+    load(min(kb + 2, nkb - 1), S0);
+    compute(0, kb);
+    store(S1, 1);
+    barrier_lds();
+    load(min(kb + 3, nkb - 1), S1);
+    if (kb + 1 < nkb) compute(1, kb + 1);
+    store(S0, 0);
+    barrier_lds();
   }
+  // D row 4g + v of 16-row group i, column r of weight-row group j
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int m = row0 + 64 * wm + 16 * i + 4 * g + v;
+      if (m >= rows) continue;
+      if (GATED) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          out[(size_t)m * n_out + o0 + 32 * wn + 16 * j + r] = silu_mul(acc[i][j][v], acc[i][j + 2][v]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) out[(size_t)m * n_out + o0 + 64 * wn + 16 * j + r] = acc[i][j][v];
+      }
+    }
 }
 
 // h fp32 [rows, I] -> E4M3 + fp32 scale per 128 (same rule as the routed mid)
@@ -157,18 +236,17 @@ hipError_t launch_shared(const moe_plan* p, const CallArgs& a, Ev ev) {
                           Ev{ev.start, nullptr}, reinterpret_cast<const uint16_t*>(a.x), M, H,
                           wsp<uint8_t>(p, p->L.sh_xq), wsp<float>(p, p->L.sh_xs));
   if (e != hipSuccess) return e;
-  const int64_t t1 = (int64_t)((M + 15) / 16) * (Is / 16);
-  e = launch_k(sh_linear_kernel<true>, dim3(blocks_for(t1, 8192)), dim3(256), 0, a.stream, Ev{},
+  const int64_t mt = (M + kShBM - 1) / kShBM;
+  e = launch_k(sh_gemm_kernel<true>, dim3((unsigned)(mt * (Is / 64))), dim3(256), 0, a.stream, Ev{},
                wsp<uint8_t>(p, p->L.sh_xq), wsp<float>(p, p->L.sh_xs), reinterpret_cast<const uint8_t*>(p->ws13),
-               p->ss13, M, H, 2 * Is, wsp<float>(p, p->X.sh_h));
+               p->ss13, M, H, Is, wsp<float>(p, p->X.sh_h));
   if (e != hipSuccess) return e;
   e = launch_k(sh_act_quant_kernel, dim3(blocks_for((int64_t)M * (Is / 128), 8192)), dim3(256), 0, a.stream, Ev{},
                wsp<float>(p, p->X.sh_h), M, Is, wsp<uint8_t>(p, p->L.sh_hq), wsp<float>(p, p->L.sh_hs));
   if (e != hipSuccess) return e;
-  const int64_t t2 = (int64_t)((M + 15) / 16) * (H / 16);
-  return launch_k(sh_linear_kernel<false>, dim3(blocks_for(t2, 8192)), dim3(256), 0, a.stream, Ev{nullptr, ev.stop},
-                  wsp<uint8_t>(p, p->L.sh_hq), wsp<float>(p, p->L.sh_hs), reinterpret_cast<const uint8_t*>(p->ws2),
-                  p->ss2, M, Is, H, wsp<float>(p, p->L.sh_y));
+  return launch_k(sh_gemm_kernel<false>, dim3((unsigned)(mt * (H / 128))), dim3(256), 0, a.stream,
+                  Ev{nullptr, ev.stop}, wsp<uint8_t>(p, p->L.sh_hq), wsp<float>(p, p->L.sh_hs),
+                  reinterpret_cast<const uint8_t*>(p->ws2), p->ss2, M, Is, H, wsp<float>(p, p->L.sh_y));
 }
 
 }  // namespace qmoe
