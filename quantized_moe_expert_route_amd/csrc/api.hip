@@ -65,7 +65,7 @@ Layout make_layout(const moe_shape& s) {
   r.X.bitmap = take(4 * E * (size_t)r.words);
   r.X.sync_begin = r.X.bitmap;
   r.X.sync_bytes = align256(off) - r.X.bitmap;
-  r.X.pre = take(4 * E * (size_t)r.words);
+  r.X.pw = take(8 * E * (size_t)r.words);
   r.L.xq = take(M * H / 2);
   r.L.xs = take(M * H / 32);
   r.X.h = take(4 * n * I);
@@ -139,7 +139,7 @@ int moe_plan_stage_launches(const moe_plan* plan, int64_t M, int stage) {
   const bool small = small_path(M, plan->s.top_k);
   switch (stage) {
     case 0: return 1;                             // route (+ sort + x quantization when small)
-    case 1: return small ? 0 : 1;                 // align
+    case 1: return small ? 0 : 3;                 // align
     case 2: return 1;                             // gate_up (+ mid quantization when large)
     case 3: return small ? 1 : 0;                 // act_quant
     case 4: return plan->s.shared_I > 0 ? 4 : 0;  // shared expert

@@ -23,7 +23,7 @@ struct Internal {
   size_t gu_items; // int4 [TB * I/128]: {expert, row_begin, row_end, column block}, large M
   size_t dn_items; // int4 [TB * H/kDownItemCols]: {expert, row_begin, row_end, column chunk}, large M
   size_t bitmap;   // uint32 [E, ceil(M/32)]: bit t of row e = token t picked e; zero between calls
-  size_t pre;      // int32 [E, ceil(M/32)]: entries of row e before word w
+  size_t pw;       // int2 [E, ceil(M/32)]: {set bits of row e before word w, word w}
   size_t h;        // fp32 [n, I]: SiLU(gate)*up, rows in sorted order
   size_t sh_h;     // fp32 [M, Is]
   size_t sync_begin, sync_bytes;  // region zeroed once when the workspace is bound

@@ -275,50 +275,74 @@ __device__ void write_big_items(int c, int E, int n_iblk, int n_nc, int* s_toff,
   __syncthreads();
 }
 
-__global__ __launch_bounds__(1024) void align_kernel(
-    const int* __restrict__ topk_ids, int M, int E, int k, uint32_t* __restrict__ bitmap,
-    int* __restrict__ pre, int words, int* __restrict__ count, int* __restrict__ offset,
-    int* __restrict__ sorted_entry, int4* __restrict__ tiles, int* __restrict__ meta, int n_iblk, int n_nc,
-    int4* __restrict__ gu_items, int4* __restrict__ dn_items) {
-  __shared__ int s_cnt[1024];
+// Sort for M > kSmallM in three launches, none with a serial chain:
+// 1. one workgroup per expert row of the token bitmap (bit t of row e: token
+//    t picked e): the exclusive prefix of the words' popcounts, stored with
+//    the word, and the row total (the expert's count); it is the bitmap's
+//    only reader and leaves it zero for the next call;
+// 2. one workgroup: offsets, 16-row tiles and the work items from the counts;
+// 3. one thread per entry t*k+j: its place in expert e's run is offset[e]
+//    plus the number of e's tokens before t (prefix + popcount below bit t),
+//    so entries of earlier tokens come first.
+__global__ __launch_bounds__(256) void align_rows_kernel(uint32_t* __restrict__ bitmap, int words,
+                                                         int2* __restrict__ pw, int* __restrict__ count) {
+  __shared__ int s_wsum[4];
+  const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t* row = bitmap + (size_t)e * words;
+  int2* prow = pw + (size_t)e * words;
+  int carry = 0;
+  for (int w0 = 0; w0 < words; w0 += 256) {
+    const int w = w0 + tid;
+    const uint32_t bits = w < words ? row[w] : 0u;
+    const int c = __popc(bits);
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int n = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += n;
+    }
+    if (lane == 63) s_wsum[wave] = incl;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      before += q < wave ? s_wsum[q] : 0;
+      total += s_wsum[q];
+    }
+    if (w < words) {
+      prow[w] = make_int2(carry + before + incl - c, (int)bits);
+      if (bits) row[w] = 0u;
+    }
+    carry += total;
+    __syncthreads();  // s_wsum is reused
+  }
+  if (tid == 0) count[e] = carry;
+}
+
+__global__ __launch_bounds__(1024) void align_offsets_kernel(
+    const int* __restrict__ count_in, int E, int* __restrict__ count, int* __restrict__ offset,
+    int4* __restrict__ tiles, int* __restrict__ meta, int n_iblk, int n_nc, int4* __restrict__ gu_items,
+    int4* __restrict__ dn_items) {
   __shared__ int s_off[1024];
   __shared__ int s_toff2[1025];
   __shared__ int s_off2[1025];
   __shared__ int s_tmp[64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // 1. per expert row: prefix popcount of each bitmap word, and the row total
-  for (int e = wave; e < E; e += 16) {
-    int carry = 0;
-    for (int w0 = 0; w0 < words; w0 += 64) {
-      const int w = w0 + lane;
-      const uint32_t bits = w < words ? bitmap[(size_t)e * words + w] : 0u;
-      const int c = __popc(bits);
-      int incl = c;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        int n = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += n;
-      }
-      if (w < words) pre[(size_t)e * words + w] = carry + incl - c;
-      carry += __shfl(incl, 63, 64);
-    }
-    if (lane == 0) s_cnt[e] = carry;
+  const int tid = threadIdx.x;
+  const int c = tid < E ? count_in[tid] : 0;
+  __syncthreads();  // count_in may be count itself
+  write_offsets_tiles(c, E, s_off, s_tmp, count, offset, tiles, meta, false);
+  write_big_items(c, E, n_iblk, n_nc, s_toff2, s_off2, s_tmp, gu_items, dn_items, meta);
+}
+
+__global__ __launch_bounds__(256) void align_place_kernel(const int* __restrict__ topk_ids, int n, int k, int words,
+                                                          const int2* __restrict__ pw, const int* __restrict__ offset,
+                                                          int* __restrict__ sorted_entry) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) {
+    const int e = topk_ids[i], t = i / k;
+    const int2 v = pw[(size_t)e * words + (t >> 5)];
+    const int rank = v.x + __popc((uint32_t)v.y & ((1u << (t & 31)) - 1u));
+    sorted_entry[offset[e] + rank] = i;
   }
-  __syncthreads();
-  write_offsets_tiles(tid < E ? s_cnt[tid] : 0, E, s_off, s_tmp, count, offset, tiles, meta, false);
-  write_big_items(tid < E ? s_cnt[tid] : 0, E, n_iblk, n_nc, s_toff2, s_off2, s_tmp, gu_items, dn_items, meta);
-  // each entry's slot in its expert's run: rows of earlier tokens first
-  const int n = M * k;
-  for (int i = tid; i < n; i += 1024) {
-    const int e = topk_ids[i];
-    const int t = i / k;
-    const size_t wi = (size_t)e * words + (t >> 5);
-    const int rank = pre[wi] + __popc(bitmap[wi] & ((1u << (t & 31)) - 1u));
-    sorted_entry[s_off[e] + rank] = i;
-  }
-  __syncthreads();
-  // leave the bitmap zero for the next call
-  for (int i = tid; i < E * words; i += 1024) bitmap[i] = 0u;
 }
 
 __global__ void zero_kernel(uint4* p, size_t n16) {
@@ -370,11 +394,18 @@ hipError_t launch_route(const moe_plan* p, const CallArgs& a, Ev ev) {
 
 hipError_t launch_align(const moe_plan* p, const CallArgs& a, Ev ev) {
   const int words = (int)((a.M + 31) / 32);
-  return launch_k(align_kernel, dim3(1), dim3(1024), 0, a.stream, ev, wsp<int>(p, p->L.topk_ids), (int)a.M,
-                  (int)p->s.E, (int)p->s.top_k, wsp<uint32_t>(p, p->X.bitmap), wsp<int>(p, p->X.pre), words,
-                  wsp<int>(p, p->L.count), wsp<int>(p, p->L.offset), wsp<int>(p, p->L.sorted_entry),
-                  wsp<int4>(p, p->X.tiles), wsp<int>(p, p->X.meta), (int)(p->s.I / 128),
-                  (int)(p->s.H / kDownItemCols), wsp<int4>(p, p->X.gu_items), wsp<int4>(p, p->X.dn_items));
+  const int64_t n = a.M * p->s.top_k;
+  hipError_t e = launch_k(align_rows_kernel, dim3((unsigned)p->s.E), dim3(256), 0, a.stream, Ev{ev.start, nullptr},
+                          wsp<uint32_t>(p, p->X.bitmap), words, wsp<int2>(p, p->X.pw), wsp<int>(p, p->L.count));
+  if (e != hipSuccess) return e;
+  e = launch_k(align_offsets_kernel, dim3(1), dim3(1024), 0, a.stream, Ev{}, wsp<int>(p, p->L.count),
+               (int)p->s.E, wsp<int>(p, p->L.count), wsp<int>(p, p->L.offset), wsp<int4>(p, p->X.tiles),
+               wsp<int>(p, p->X.meta), (int)(p->s.I / 128), (int)(p->s.H / kDownItemCols),
+               wsp<int4>(p, p->X.gu_items), wsp<int4>(p, p->X.dn_items));
+  if (e != hipSuccess) return e;
+  return launch_k(align_place_kernel, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 4096)), dim3(256), 0,
+                  a.stream, Ev{nullptr, ev.stop}, wsp<int>(p, p->L.topk_ids), (int)n, (int)p->s.top_k, words,
+                  wsp<int2>(p, p->X.pw), wsp<int>(p, p->L.offset), wsp<int>(p, p->L.sorted_entry));
 }
 
 }  // namespace qmoe
