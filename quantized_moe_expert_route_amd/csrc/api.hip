@@ -32,7 +32,7 @@ moe_status check_shape(const moe_shape* s) {
 struct Layout {
   moe_ws_layout L;
   Internal X;
-  int64_t t16, tb, words;
+  int64_t t16, tb, tg, words;
 };
 
 Layout make_layout(const moe_shape& s) {
@@ -43,6 +43,7 @@ Layout make_layout(const moe_shape& s) {
   const size_t n = M * k;
   r.t16 = (int64_t)((n + std::min(E, n) * (kTileRows - 1) + kTileRows - 1) / kTileRows);
   r.tb = (int64_t)((n + std::min(E, n) * (kBigRows - 1) + kBigRows - 1) / kBigRows);
+  r.tg = (int64_t)((n + std::min(E, n) * (kGuRows - 1) + kGuRows - 1) / kGuRows);
   r.words = (int64_t)((M + 31) / 32);
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -58,7 +59,7 @@ Layout make_layout(const moe_shape& s) {
   r.L.sorted_entry = take(4 * n);
   r.X.tiles = take(16 * (size_t)r.t16);
   r.X.meta = take(256);
-  r.X.gu_items = take(16 * (size_t)r.tb * (I / 128));
+  r.X.gu_items = take(16 * (size_t)r.tg * (I / 128));
   r.X.dn_items = take(16 * (size_t)r.tb * (H / kDownItemCols));
   // the token bitmap: zeroed when the workspace is bound, and
   // left zero by every call

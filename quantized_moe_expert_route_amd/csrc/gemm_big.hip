@@ -34,32 +34,52 @@ __device__ __forceinline__ void xcd_run(int n_items, int& first, int& stride, in
   end = min(n_items, (x + 1) * run);
 }
 
-constexpr int kLDG = 80;  // LDS bytes per row of a 64-byte K-step slice (+16 pad)
-constexpr int kGuStages = 4;  // K-steps of gate/up loads held in registers
+// LDS layout of a K-step slice: 64-byte rows, and 16-byte chunk c of row R
+// at R * 64 + 16 * (c ^ ((R >> 1) & 3)). With it both the staging stores
+// (four lanes per row) and the fragment reads (sixteen rows, one chunk) hit
+// no LDS bank twice (measured with the bank-conflict counter; rows padded to
+// 80 bytes cost 4 conflict cycles per read and 8 per store).
+__device__ __forceinline__ int opaque_zero() {
+  int z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return z;
+}
+__device__ __forceinline__ int sw64(int row, int chunk) { return row * 64 + 16 * (chunk ^ ((row >> 1) & 3)); }
+constexpr int kGuStages = 2;  // K-steps of gate/up loads held in registers
+
+// Item = (expert, kGuRows sorted rows, one 128-column mid block): the 256
+// weight rows it reads (128 gate + 128 up) cover exactly the columns one mid
+// block needs. A 64-row tile keeps a wave's registers within 256 so that two
+// workgroups share a CU: one's MFMAs run while the other stages its next
+// K-step and waits at its barrier (with one workgroup per CU those phases
+// ran one after another).
+constexpr int kGuR = kGuRows;
 
 struct GuSmem {
-  uint8_t a[2][kBM * kLDG];   // x rows (MXFP4), K-step slice
-  uint8_t b[2][256 * kLDG];   // 128 gate + 128 up weight rows
-  uint32_t as[2][kBM];        // 4 E8M0 bytes per row per K-step
+  uint8_t a[2][kGuR * 64];    // x rows (MXFP4), K-step slice (sw64 layout)
+  uint8_t b[2][256 * 64];     // 128 gate + 128 up weight rows
+  uint32_t as[2][kGuR];       // 4 E8M0 bytes per row per K-step
   uint32_t bs[2][256];
 };
 
-// One K-step of global data held in registers: 2 + 4 16-byte chunks and the
+// One K-step of global data held in registers: 1 + 4 16-byte chunks and the
 // scale dwords of this thread.
 struct GuRegs {
-  uint4 a[2], b[4];
+  uint4 a, b[4];
   uint32_t sa, sb;
 };
 
-__global__ __launch_bounds__(256) void gate_up_big_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gate_up_big_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const uint8_t* __restrict__ w13,
     const uint8_t* __restrict__ s13, const int* __restrict__ sorted_entry, const int4* __restrict__ items,
     const int* __restrict__ meta, int H, int I, int k, uint8_t* __restrict__ midq, float* __restrict__ mids) {
   __shared__ GuSmem sm;
-  __shared__ int tok[kBM];
-  __shared__ float red[2][kBM];  // row amax of the two column halves
+  __shared__ int tok[kGuR];
+  __shared__ float red[4][kGuR];  // row amax of the four column quarters
+  // wave w multiplies all kGuR rows with gate columns 32 w .. + 32 and the
+  // matching up columns
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wn = wave;
   const int r = lane & 15, g = lane >> 4;
   const size_t Hb = (size_t)H / 2, Hs = (size_t)H / 32;
   const int nk = H / 128;
@@ -69,7 +89,7 @@ __global__ __launch_bounds__(256) void gate_up_big_kernel(
     const int4 item = items[it];
     const int e = item.x, r0 = item.y, r1 = item.z, ib = item.w;
     const int rows = r1 - r0;
-    if (tid < kBM) tok[tid] = tid < rows ? sorted_entry[r0 + tid] / k : -1;
+    if (tid < kGuR) tok[tid] = tid < rows ? sorted_entry[r0 + tid] / k : -1;
     __syncthreads();
     auto wrow = [&](int rr) {
       return (size_t)e * 2 * I + (rr < 128 ? 128 * ib + rr : I + 128 * ib + rr - 128);
@@ -79,48 +99,48 @@ __global__ __launch_bounds__(256) void gate_up_big_kernel(
     // those rows are never written), so the number of loads in flight is the
     // same on every path and the waits before each store stay exact.
     const int tok0 = tok[0];
-    const uint8_t* pa[2];
-    const uint8_t* pb[4];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int idx = tid + 256 * q, t = tok[idx >> 2];
-      pa[q] = xq + (size_t)(t >= 0 ? t : tok0) * Hb + 16 * (idx & 3);
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int idx = tid + 256 * q;
-      pb[q] = w13 + wrow(idx >> 2) * Hb + 16 * (idx & 3);
-    }
-    const int ts = tok[tid & (kBM - 1)];
+    const int ta = tok[tid >> 2];
+    const uint8_t* pa = xq + (size_t)(ta >= 0 ? ta : tok0) * Hb + 16 * (tid & 3);
+    // The expert's weights and their scales are read through buffer
+    // descriptors (base and size in scalar registers, a 32-bit offset per
+    // lane), which keeps the per-thread addresses out of vector registers.
+    // Staged weight row (tid >> 2) + 64 q: gate rows for q < 2, up rows for
+    // q >= 2; the row offsets per q are the same for every thread.
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(w13 + (size_t)e * 2 * I * Hb), (short)0, (int)(2 * I * Hb), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(s13 + (size_t)e * 2 * I * Hs), (short)0, (int)(2 * I * Hs), 0x00020000);
+    const int ob = (128 * ib + (tid >> 2)) * (int)Hb + 16 * (tid & 3);
+    const int boff[4] = {0, 64 * (int)Hb, (I - 128 + 128) * (int)Hb, (I - 128 + 192) * (int)Hb};
+    const int os = (int)(wrow(tid) - (size_t)e * 2 * I) * (int)Hs;
+    const int ts = tok[tid & (kGuR - 1)];
     const uint8_t* psa = xs + (size_t)(ts >= 0 ? ts : tok0) * Hs;
-    const uint8_t* psb = s13 + wrow(tid) * Hs;
     auto load = [&](int kk, GuRegs& R) {
+      R.a = ld16(pa + kk * 64);
 #pragma unroll
-      for (int q = 0; q < 2; ++q) R.a[q] = ld16(pa[q] + kk * 64);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) R.b[q] = ld16(pb[q] + kk * 64);
+      for (int q = 0; q < 4; ++q) {
+        typedef unsigned v4u __attribute__((ext_vector_type(4)));
+        const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rw, ob, boff[q] + kk * 64, 0);
+        R.b[q] = make_uint4(v.x, v.y, v.z, v.w);
+      }
       R.sa = ld4(psa + kk * 4);
-      R.sb = ld4(psb + kk * 4);
+      R.sb = __builtin_amdgcn_raw_buffer_load_b32(rs, os, kk * 4, 0);
     };
     auto store = [&](const GuRegs& R, int s) {
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int idx = tid + 256 * q;
-        *reinterpret_cast<uint4*>(&sm.a[s][(idx >> 2) * kLDG + 16 * (idx & 3)]) = R.a[q];
-      }
+      *reinterpret_cast<uint4*>(&sm.a[s][sw64(tid >> 2, tid & 3)]) = R.a;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int idx = tid + 256 * q;
-        *reinterpret_cast<uint4*>(&sm.b[s][(idx >> 2) * kLDG + 16 * (idx & 3)]) = R.b[q];
+        *reinterpret_cast<uint4*>(&sm.b[s][sw64(idx >> 2, idx & 3)]) = R.b[q];
       }
-      if (tid < kBM) sm.as[s][tid] = R.sa;
+      if (tid < kGuR) sm.as[s][tid] = R.sa;
       sm.bs[s][tid] = R.sb;
     };
-    v4f accg[4][4], accu[4][4];
+    v4f accg[4][2], accu[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 2; ++j) {
         accg[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
         accu[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
       }
@@ -129,15 +149,15 @@ __global__ __launch_bounds__(256) void gate_up_big_kernel(
       uint32_t sa[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = 64 * wm + 16 * i + r;
-        fa[i] = *reinterpret_cast<const uint4*>(&sm.a[s][row * kLDG + 16 * g]);
+        const int row = 16 * i + r;
+        fa[i] = *reinterpret_cast<const uint4*>(&sm.a[s][sw64(row, g)]);
         sa[i] = (sm.as[s][row] >> (8 * g)) & 0xFFu;
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = 64 * wn + 16 * j + r;
-        const uint4 fg = *reinterpret_cast<const uint4*>(&sm.b[s][col * kLDG + 16 * g]);
-        const uint4 fu = *reinterpret_cast<const uint4*>(&sm.b[s][(col + 128) * kLDG + 16 * g]);
+      for (int j = 0; j < 2; ++j) {
+        const int col = 32 * wn + 16 * j + r;
+        const uint4 fg = *reinterpret_cast<const uint4*>(&sm.b[s][sw64(col, g)]);
+        const uint4 fu = *reinterpret_cast<const uint4*>(&sm.b[s][sw64(col + 128, g)]);
         const uint32_t sg = (sm.bs[s][col] >> (8 * g)) & 0xFFu;
         const uint32_t su = (sm.bs[s][col + 128] >> (8 * g)) & 0xFFu;
 #pragma unroll
@@ -166,19 +186,24 @@ __global__ __launch_bounds__(256) void gate_up_big_kernel(
       }
     }
     // ---- epilogue: h = SiLU(g) * u (float64, one rounding), row amax over
-    // the item's 128 columns, s = amax / 448, q = E4M3(h / s)
+    // the item's 128 columns, s = amax / 448, q = E4M3(h / s). Its lane
+    // indices come from an opaque zero, so the compiler computes its
+    // addresses here rather than before the item loop (where they would stay
+    // live through the K-loop and crowd it out of registers).
+    const int lz = (int)(threadIdx.x & 63) + opaque_zero();
+    const int re = lz & 15, ge = lz >> 4;
     // (rows past the tile's end are skipped: a quarter-wave's four rows are
     // uniform per (i, v), so a wave whose rows are all padding branches over)
-    float hv[4][4][4];
+    float hv[4][2][4];
     float pm[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         float m = 0.f;
-        const bool live = 64 * wm + 16 * i + 4 * g + v < rows;
+        const bool live = 16 * i + 4 * ge + v < rows;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 2; ++j) {
           hv[i][j][v] = live ? silu_mul(accg[i][j][v], accu[i][j][v]) : 0.f;
           m = fmaxf(m, fabsf(hv[i][j][v]));
         }
@@ -194,28 +219,28 @@ __global__ __launch_bounds__(256) void gate_up_big_kernel(
         u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x4E, 0xF, 0xF, false));
         u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x141, 0xF, 0xF, false));
         u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x140, 0xF, 0xF, false));
-        if (r == 0) red[wn][64 * wm + 16 * i + 4 * g + v] = __uint_as_float(u);
+        if (re == 0) red[wn][16 * i + 4 * ge + v] = __uint_as_float(u);
       }
     __syncthreads();  // also: every wave is past its last read of the staging buffers
-    uint8_t* qs = reinterpret_cast<uint8_t*>(&sm.a);  // [128][128] codes, in the idle A buffers
+    uint8_t* qs = reinterpret_cast<uint8_t*>(&sm.a);  // [kGuR][128] codes, in the idle A buffers
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int row = 64 * wm + 16 * i + 4 * g + v;
-        const float amax = fmaxf(red[0][row], red[1][row]);
+        const int row = 16 * i + 4 * ge + v;
+        const float amax = fmaxf(fmaxf(red[0][row], red[1][row]), fmaxf(red[2][row], red[3][row]));
         const float sc = __fdiv_rn(amax, 448.0f);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 2; ++j) {
           const uint32_t c = sc > 0.f && row < rows ? e4m3_code(__fdiv_rn(hv[i][j][v], sc)) : 0u;
-          qs[row * 128 + 64 * wn + 16 * j + r] = (uint8_t)c;
+          qs[row * 128 + 32 * wn + 16 * j + re] = (uint8_t)c;
         }
-        if (wn == 0 && r == 0 && row < rows) mids[(size_t)(r0 + row) * (I / 128) + ib] = sc;
+        if (wn == 0 && re == 0 && row < rows) mids[(size_t)(r0 + row) * (I / 128) + ib] = sc;
       }
     __syncthreads();
-    // coalesced copy of the item's codes: 128 rows x 128 bytes
+    // coalesced copy of the item's codes: kGuR rows x 128 bytes
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < kGuR * 8 / 256; ++q) {
       const int idx = tid + 256 * q, row = idx >> 3, c = idx & 7;
       if (row < rows)
         *reinterpret_cast<uint4*>(midq + (size_t)(r0 + row) * I + 128 * ib + 16 * c) =
@@ -224,7 +249,6 @@ __global__ __launch_bounds__(256) void gate_up_big_kernel(
     __syncthreads();
   }
 }
-
 
 // ---------------------------------------------------------------- down
 // Item = (expert, 128 sorted rows, kDnItemCols output columns). The tile's
@@ -401,9 +425,9 @@ __global__ __launch_bounds__(256) void down_big_kernel(
 
 hipError_t launch_gate_up_big(const moe_plan* p, const CallArgs& a, Ev ev) {
   const int64_t n = a.M * p->s.top_k;
-  const int64_t tiles = (n + std::min<int64_t>(p->s.E, n) * (kBM - 1) + kBM - 1) / kBM;
+  const int64_t tiles = (n + std::min<int64_t>(p->s.E, n) * (kGuR - 1) + kGuR - 1) / kGuR;
   const int64_t items = tiles * (p->s.I / 128);
-  const int blocks = (int)std::min<int64_t>(items, 256);
+  const int blocks = (int)std::min<int64_t>(items, 512);  // two per CU
   return launch_k(gate_up_big_kernel, dim3(blocks), dim3(256), 0, a.stream, ev, wsp<uint8_t>(p, p->L.xq),
                   wsp<uint8_t>(p, p->L.xs), reinterpret_cast<const uint8_t*>(a.w13),
                   reinterpret_cast<const uint8_t*>(a.s13), wsp<int>(p, p->L.sorted_entry),

@@ -12,7 +12,8 @@
 namespace qmoe {
 
 constexpr int kTileRows = 16;  // sorted rows per tile of the small-token kernels
-constexpr int kBigRows = 128;  // sorted rows per tile of the large-token kernels
+constexpr int kBigRows = 128;  // sorted rows per tile of the large-token down kernel
+constexpr int kGuRows = 64;    // sorted rows per tile of the large-token gate/up kernel
 constexpr int kDownCols = 128; // output columns per sub-tile of the large-token down kernel
 constexpr int kDownItemCols = 512; // output columns per down work item of the large-token kernel
 
@@ -20,7 +21,7 @@ constexpr int kDownItemCols = 512; // output columns per down work item of the l
 struct Internal {
   size_t tiles;    // int4 [T16]: {expert, row_begin, row_end, 0}
   size_t meta;     // int32 [64]: meta[0] tiles, meta[1] gate/up items, meta[2] down items
-  size_t gu_items; // int4 [TB * I/128]: {expert, row_begin, row_end, column block}, large M
+  size_t gu_items; // int4 [TG * I/128]: {expert, row_begin, row_end, column block}, tiles of kGuRows, large M
   size_t dn_items; // int4 [TB * H/kDownItemCols]: {expert, row_begin, row_end, column chunk}, large M
   size_t bitmap;   // uint32 [E, ceil(M/32)]: bit t of row e = token t picked e; zero between calls
   size_t pw;       // int2 [E, ceil(M/32)]: {set bits of row e before word w, word w}

@@ -233,29 +233,29 @@ __global__ __launch_bounds__(256) void route_kernel(
 }
 
 // Work items of the large-token GEMMs, per expert in the order (column
-// block, row tile) so that the row tiles sharing a weight block are adjacent.
+// block, row tile) so that the row tiles sharing a weight block are adjacent:
+// gate/up items on tiles of kGuRows rows, down items on tiles of kBigRows.
 // Thread per item: the expert is found by binary search of the tile prefix.
 __device__ void write_big_items(int c, int E, int n_iblk, int n_nc, int* s_toff, int* s_off, int* s_tmp,
                                 int4* __restrict__ gu_items, int4* __restrict__ dn_items, int* __restrict__ meta) {
   const int tid = threadIdx.x;
-  const int nt = (c + kBigRows - 1) / kBigRows;
-  int total_rows, total_tiles;
+  int total_rows;
   const int off = block_exclusive_scan(c, s_tmp, &total_rows);
-  const int toff = block_exclusive_scan(nt, s_tmp, &total_tiles);
-  if (tid < E) {
-    s_toff[tid] = toff;
-    s_off[tid] = off;
-  }
-  if (tid == 0) {
-    s_toff[E] = total_tiles;
-    s_off[E] = total_rows;
-    meta[1] = total_tiles * n_iblk;
-    meta[2] = total_tiles * n_nc;
-  }
-  __syncthreads();
+  if (tid < E) s_off[tid] = off;
+  if (tid == 0) s_off[E] = total_rows;
   for (int pass = 0; pass < 2; ++pass) {
+    const int tr = pass == 0 ? kGuRows : kBigRows;
     const int nb = pass == 0 ? n_iblk : n_nc;
     int4* out = pass == 0 ? gu_items : dn_items;
+    const int nt = (c + tr - 1) / tr;
+    int total_tiles;
+    const int toff = block_exclusive_scan(nt, s_tmp, &total_tiles);
+    if (tid < E) s_toff[tid] = toff;
+    if (tid == 0) {
+      s_toff[E] = total_tiles;
+      meta[1 + pass] = total_tiles * nb;
+    }
+    __syncthreads();
     for (int i = tid; i < total_tiles * nb; i += blockDim.x) {
       const int tile = i / nb;  // items of expert e occupy [toff[e] * nb, toff[e + 1] * nb)
       int lo = 0, hi = E;       // largest e with toff[e] <= tile and a tile of its own
@@ -268,11 +268,11 @@ __device__ void write_big_items(int c, int E, int n_iblk, int n_nc, int* s_toff,
       const int nte = s_toff[e + 1] - s_toff[e];
       const int local = i - s_toff[e] * nb;
       const int b = local / nte, mt = local - b * nte;
-      const int r0 = s_off[e] + mt * kBigRows;
-      out[i] = make_int4(e, r0, min(r0 + kBigRows, s_off[e + 1]), b);
+      const int r0 = s_off[e] + mt * tr;
+      out[i] = make_int4(e, r0, min(r0 + tr, s_off[e + 1]), b);
     }
+    __syncthreads();  // s_toff is rewritten by the next pass
   }
-  __syncthreads();
 }
 
 // Sort for M > kSmallM in three launches, none with a serial chain:
