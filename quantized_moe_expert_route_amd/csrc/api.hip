@@ -177,6 +177,7 @@ moe_status moe_plan_create(const moe_shape* shape, moe_plan** out) {
   memset(p, 0, sizeof(*p));
   p->s = *shape;
   p->device = dev;
+  p->num_cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
   p->n_max = shape->M * shape->top_k;
   Layout lay = make_layout(*shape);
   p->L = lay.L;

@@ -22,7 +22,10 @@
 namespace qmoe {
 
 // Up to kSmallM tokens (and kSmallRows entries), down and combine are one
-// launch. A workgroup owns 16 output columns of every token: its four waves
+// launch. A workgroup owns cw <= 16 output columns of every token (cw is
+// picked per H so that the CUs carry equal shares of w2; lanes of the
+// 16-column MFMA past cw repeat column cw - 1 and their results are never
+// read): its four waves
 // take contiguous runs of the 16-row tiles, keep each (entry, column) result
 // in LDS, and when every tile is done the workgroup forms out[t, c0 .. c0+16)
 // from the token's k slots, so no slot result leaves the workgroup.
@@ -88,7 +91,7 @@ __device__ __forceinline__ uint32_t fp8x2_bf16(uint32_t w) {
 template <int NB, int D, bool MID_LDS>
 __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
     const uint8_t* __restrict__ midq, const float* __restrict__ mids, const uint8_t* __restrict__ w2, const uint8_t* __restrict__ s2, const int* __restrict__ sorted_entry,
-    const int4* __restrict__ tiles, const int* __restrict__ meta, int H, int k, int M,
+    const int4* __restrict__ tiles, const int* __restrict__ meta, int H, int k, int M, int cw,
     const float* __restrict__ topk_w, const float* __restrict__ ys, uint16_t* __restrict__ out) {
   constexpr int I = NB * 128;
   constexpr int LDA = 2 * I + kDcPad;  // bytes per staged bf16 mid row
@@ -100,7 +103,8 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
   int* sel = reinterpret_cast<int*>(msl + n * NB);      // [n]       (MID_LDS) sorted_entry
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int r = lane & 15, g = lane >> 4;
-  const int c0 = blockIdx.x * 16;
+  const int c0 = blockIdx.x * cw;
+  const int rc = min(r, cw - 1);  // the lane's weight column
   const int nt = meta[0];
   const int per = (nt + kDcWaves - 1) / kDcWaves;
   const int base = wave * per;                                    // this wave's tiles [base, base + my)
@@ -132,7 +136,7 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
   }
 
   auto load = [&](const int4 tl, DcSlot<NB, MID_LDS>& S) {
-    const size_t col = (size_t)tl.x * H + c0 + r;
+    const size_t col = (size_t)tl.x * H + c0 + rc;
     const uint8_t* pw = w2 + col * (I / 2) + 16 * g;
 #pragma unroll
     for (int b = 0; b < NB; ++b) S.w[b] = ld16(pw + 64 * b);
@@ -283,8 +287,9 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
   }
   __syncthreads();
   // out[t, c0 + 2p .. + 2): float64 products and sum in slot order (+ shared), one bf16 rounding
-  for (int idx = tid; idx < M * 8; idx += kDcThreads) {
-    const int t = idx >> 3, cc = 2 * (idx & 7);
+  const int pairs = cw >> 1;
+  for (int idx = tid; idx < M * pairs; idx += kDcThreads) {
+    const int t = idx / pairs, cc = 2 * (idx - t * pairs);
     double a0 = 0.0, a1 = 0.0;
     for (int j = 0; j < k; ++j) {
       const double wj = (double)topk_w[t * k + j];
@@ -333,6 +338,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
 }
 
+// Columns per workgroup: the even width in 8..16 that divides H and gives
+// the busiest CU the fewest columns (workgroups are spread round-robin over
+// the CUs); ties go to the wider one.
+int down_combine_cols(int H, int cus) {
+  int best = 16, best_load = 1 << 30;
+  for (int cw = 16; cw >= 8; cw -= 2) {
+    if (H % cw) continue;
+    const int wgs = H / cw;
+    const int load = (wgs + cus - 1) / cus * cw;
+    if (load < best_load) best = cw, best_load = load;
+  }
+  return best;
+}
+
 hipError_t launch_down_combine(const moe_plan* p, const CallArgs& a, Ev ev) {
   const int H = (int)p->s.H;
   const int64_t n = a.M * p->s.top_k, I = p->s.I;
@@ -341,11 +360,12 @@ hipError_t launch_down_combine(const moe_plan* p, const CallArgs& a, Ev ev) {
   const size_t lds = down_combine_lds_bytes(n, I, mid_lds);
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   const float* ys = p->s.shared_I > 0 ? wsp<float>(p, p->L.sh_y) : nullptr;
+  const int cw = down_combine_cols(H, p->num_cus);
   auto go = [&](auto kern) {
-    return launch_k(kern, dim3(H / 16), dim3(kDcThreads), lds, a.stream, ev, wsp<uint8_t>(p, p->L.midq),
+    return launch_k(kern, dim3(H / cw), dim3(kDcThreads), lds, a.stream, ev, wsp<uint8_t>(p, p->L.midq),
                     wsp<float>(p, p->L.mids), reinterpret_cast<const uint8_t*>(a.w2),
                     reinterpret_cast<const uint8_t*>(a.s2), wsp<int>(p, p->L.sorted_entry), wsp<int4>(p, p->X.tiles),
-                    wsp<int>(p, p->X.meta), H, (int)p->s.top_k, (int)a.M, wsp<float>(p, p->L.topk_w), ys,
+                    wsp<int>(p, p->X.meta), H, (int)p->s.top_k, (int)a.M, cw, wsp<float>(p, p->L.topk_w), ys,
                     reinterpret_cast<uint16_t*>(a.out));
   };
   // weights of D tiles in flight per wave; fewer when the slots also carry mid rows

@@ -35,6 +35,7 @@ struct Internal {
 struct moe_plan {
   moe_shape s;
   int device;
+  int num_cus;     // compute units of the device
   int64_t n_max;   // M * top_k
   int64_t t16_max; // upper bound on tiles of 16 sorted rows
   int64_t words;   // ceil(M / 32)
@@ -99,6 +100,7 @@ hipError_t launch_align(const moe_plan* p, const CallArgs& a, Ev ev);
 hipError_t launch_gate_up(const moe_plan* p, const CallArgs& a, Ev ev);
 hipError_t launch_act_quant(const moe_plan* p, const CallArgs& a, Ev ev);
 // small M: down and the combine in one launch; y stays on chip
+int down_combine_cols(int H, int cus);
 hipError_t launch_down_combine(const moe_plan* p, const CallArgs& a, Ev ev);
 hipError_t launch_shared(const moe_plan* p, const CallArgs& a, Ev ev);
 // large M: LDS-staged 128-row tiles; gate/up includes the mid quantization
