@@ -168,6 +168,22 @@ __device__ __forceinline__ uint32_t cvt_fp4x2_bf16(uint32_t src, float scale) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// Four packed bf16 pairs as the 8-element bf16 MFMA operand.
+__device__ __forceinline__ v8s as_v8s(uint32_t d0, uint32_t d1, uint32_t d2, uint32_t d3) {
+  v8s r;
+  r[0] = (short)(d0 & 0xFFFF); r[1] = (short)(d0 >> 16);
+  r[2] = (short)(d1 & 0xFFFF); r[3] = (short)(d1 >> 16);
+  r[4] = (short)(d2 & 0xFFFF); r[5] = (short)(d2 >> 16);
+  r[6] = (short)(d3 & 0xFFFF); r[7] = (short)(d3 >> 16);
+  return r;
+}
+
+// Two E4M3 bytes of w (the low or the high half) widened to bf16 (exact).
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_bf16(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
 __device__ __forceinline__ float e8m0_to_float(uint32_t s) {
   return s == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(s << 23);
 }

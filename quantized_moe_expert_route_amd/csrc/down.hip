@@ -74,20 +74,6 @@ size_t down_combine_lds_bytes(int64_t n, int64_t I, bool mid_lds) {
   return b;
 }
 
-__device__ __forceinline__ v8s as_v8s(uint32_t d0, uint32_t d1, uint32_t d2, uint32_t d3) {
-  v8s r;
-  r[0] = (short)(d0 & 0xFFFF); r[1] = (short)(d0 >> 16);
-  r[2] = (short)(d1 & 0xFFFF); r[3] = (short)(d1 >> 16);
-  r[4] = (short)(d2 & 0xFFFF); r[5] = (short)(d2 >> 16);
-  r[6] = (short)(d3 & 0xFFFF); r[7] = (short)(d3 >> 16);
-  return r;
-}
-
-template <bool HI>
-__device__ __forceinline__ uint32_t fp8x2_bf16(uint32_t w) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
-}
-
 template <int NB, int D, bool MID_LDS>
 __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
     const uint8_t* __restrict__ midq, const float* __restrict__ mids, const uint8_t* __restrict__ w2, const uint8_t* __restrict__ s2, const int* __restrict__ sorted_entry,

@@ -19,7 +19,6 @@
 
 namespace qmoe {
 
-constexpr int kBM = kBigRows;  // 128 sorted rows per tile
 
 
 // Item order inside an XCD-contiguous run: workgroup b handles items
@@ -251,175 +250,175 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
 }
 
 // ---------------------------------------------------------------- down
-// Item = (expert, 128 sorted rows, kDnItemCols output columns). The tile's
-// E4M3 mid bytes go to LDS once per item; the weights stream through
-// kDnItemCols/128 column sub-tiles x I/128 mid blocks, three steps in flight.
-// Per step the E4M3 values and the E2M1 * 2^scale weights are widened to
-// bf16 when a wave reads them (both exact) and 4 bf16 MFMAs of K = 32 give
-// the 128-block's fp32 partial (exact while the sum fits binary32); it is
-// scaled by the row's mid scale in float64 and the blocks are summed in order.
+// Item = (expert, tile of up to kDnRows sorted rows, kDnItemCols output
+// columns); a workgroup takes one item at a time and two workgroups share a
+// CU. At the start of an item the tile's E4M3 mid rows, fetched into
+// registers during the previous item, are widened to bf16 (exactly) into
+// LDS. Wave w then covers all the tile's rows x 64 columns, one 128-block per
+// step; its MXFP4 weights for the next item are loaded into the ring slot a
+// step has just used, so the loads run one item ahead without a barrier.
+// Within a 128-block, lane group g holds K 32 g .. 32 g + 31 of its column
+// (16 bytes and one E8M0 byte), fed to the bf16 MFMA as K 32 g + 8 q .. + 8
+// in step q; the mid operand follows the same assignment. Products and block
+// sums are exact while the sum fits binary32; the block sum is scaled by the
+// row's mid scale in float64 and the blocks are summed in order, then rounded
+// once to fp32. Rows past the tile's end repeat its last row: they compute
+// the same values and store them to the same place, so every load and store
+// is unconditional and each wait counts exactly.
+constexpr int kDnRows = kBigRows;
 constexpr int kDnItemCols = kDownItemCols;
-constexpr int kLDM = 16;   // pad bytes per LDS mid row
-constexpr int kLDW = 80;   // LDS bytes per weight column slice (64 + 16 pad)
+constexpr int kDnThreads = 256;
+
+// LDS byte offset of 16-byte chunk c (8 bf16) of widened mid row r (rows of
+// 2 I bytes): c is XORed with r & 15 inside its aligned group of 16 chunks,
+// so that consecutive rows reading one chunk fall in different bank groups.
+template <int NB>
+__device__ __forceinline__ int sw_mid16(int r, int c) { return r * (NB * 256) + 16 * (c ^ (r & 15)); }
 
 template <int NB>
-struct DnSmem {
-  uint8_t a[kBM * (NB * 128 + kLDM)];   // mid rows, E4M3
-  uint8_t b[2][kDownCols * kLDW];        // weight column slices of one mid block
-  uint32_t bs[2][kDownCols];             // 4 E8M0 bytes per column per block
-  float ms[NB][kBM];                     // mid scales
-  int ent[kBM];
-};
-
-struct DnRegs {
-  uint4 b[2];
-  uint32_t s;
-};
+constexpr size_t down_big_lds() {
+  return (size_t)kDnRows * NB * 256 + sizeof(float) * NB * kDnRows + sizeof(int) * kDnRows;
+}
 
 template <int NB>
-__global__ __launch_bounds__(256) void down_big_kernel(
+__global__ __launch_bounds__(kDnThreads) __attribute__((amdgpu_waves_per_eu(2))) void down_big_kernel(
     const uint8_t* __restrict__ midq, const float* __restrict__ mids, const uint8_t* __restrict__ w2,
     const uint8_t* __restrict__ s2, const int* __restrict__ sorted_entry, const int4* __restrict__ items,
     const int* __restrict__ meta, float* __restrict__ y, int H) {
   constexpr int I = NB * 128;
-  constexpr int LDA = I + kLDM;
-  constexpr int NSUB = kDnItemCols / kDownCols;  // column sub-tiles per item
-  constexpr int NSTEP = NSUB * NB;               // (sub-tile, block) steps per item
-  __shared__ DnSmem<NB> sm;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wm = wave & 1, wn = wave >> 1;
-  const int r = lane & 15, g = lane >> 4;
+  constexpr int Wb = I / 2, Sb = I / 32;       // bytes per w2 row / s2 row
+  constexpr int CPR = I / 16;                  // E4M3 16-byte chunks per mid row
+  constexpr int QA = kDnRows * CPR / kDnThreads;  // of them per thread and tile
+  static_assert(kDnRows * CPR % kDnThreads == 0 && kDnRows == 32 && kDnItemCols == 4 * 64, "tile shape");
+  extern __shared__ __align__(16) uint8_t dyn_lds[];
+  uint8_t* a16 = dyn_lds;                                             // [kDnRows] widened mid rows
+  float* ms = reinterpret_cast<float*>(dyn_lds + kDnRows * NB * 256);  // [NB][kDnRows] mid scales
+  int* ent = reinterpret_cast<int*>(ms + NB * kDnRows);                // [kDnRows] entries
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = lane & 15, g = lane >> 4;
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  struct Stage {
+    v4u w[4];
+    uint32_t s[4];
+  };
   int first, stride, end;
   xcd_run(meta[2], first, stride, end);
+  if (first >= end) return;
+
+  // a tile's mid rows (past its end: the last row again), entries and scales
+  v4u va[QA];
+  int ve;
+  float vs[NB];
+  auto fetch_tile = [&](const int4 item) {
+    const int r0 = item.y, rows = item.z - item.y;
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(midq + (size_t)r0 * I), (short)0, rows * I, 0x00020000);
+#pragma unroll
+    for (int q = 0; q < QA; ++q) {
+      const int idx = tid + kDnThreads * q;
+      const int row = min(idx / CPR, rows - 1), c = idx % CPR;
+      va[q] = __builtin_amdgcn_raw_buffer_load_b128(ra, row * I + 16 * c, 0, 0);
+    }
+    const int row = min(tid & (kDnRows - 1), rows - 1);
+    ve = sorted_entry[r0 + row];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) vs[b] = mids[(size_t)(r0 + row) * NB + b];
+  };
+  // weights of block b of an item into a ring slot: column c0 + 64 w + 16 j
+  // + m, 16 bytes at 64 b + 16 g of its w2 row and byte 4 b + g of its s2 row
+  auto load_block = [&](const int4 item, int b, Stage& S) {
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(w2 + (size_t)item.x * H * Wb), (short)0, H * Wb, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(s2 + (size_t)item.x * H * Sb), (short)0, H * Sb, 0x00020000);
+    const int col = item.w * kDnItemCols + 64 * wave + m;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      S.w[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, col * Wb + 16 * g, 16 * j * Wb + 64 * b, 0);
+      S.s[j] = __builtin_amdgcn_raw_buffer_load_b8(rs, col * Sb + g, 16 * j * Sb + 4 * b, 0);
+    }
+  };
+  Stage R[NB];
+  {
+    const int4 item = items[first];
+    fetch_tile(item);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) load_block(item, b, R[b]);
+  }
   for (int it = first; it < end; it += stride) {
     const int4 item = items[it];
-    const int e = item.x, r0 = item.y, r1 = item.z, c0 = item.w * kDnItemCols;
-    const int rows = r1 - r0;
-    // weight addresses of this thread (2 chunks of a 64-byte block slice, 1 scale dword)
-    const uint8_t* pw[2];
+    const int4 next = items[min(it + stride, end - 1)];  // the last item loads itself again, unused
+    __syncthreads();  // every wave is done with the previous item's LDS
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int idx = tid + 256 * q;
-      pw[q] = w2 + ((size_t)e * H + c0 + (idx >> 2)) * (I / 2) + 16 * (idx & 3);
+    for (int q = 0; q < QA; ++q) {
+      const int idx = tid + kDnThreads * q;
+      const int row = idx / CPR, c = idx % CPR;
+      const v4u v = va[q];
+      const v4u lo = {fp8x2_bf16<false>(v.x), fp8x2_bf16<true>(v.x), fp8x2_bf16<false>(v.y), fp8x2_bf16<true>(v.y)};
+      const v4u hi = {fp8x2_bf16<false>(v.z), fp8x2_bf16<true>(v.z), fp8x2_bf16<false>(v.w), fp8x2_bf16<true>(v.w)};
+      *reinterpret_cast<v4u*>(&a16[sw_mid16<NB>(row, 2 * c)]) = lo;
+      *reinterpret_cast<v4u*>(&a16[sw_mid16<NB>(row, 2 * c + 1)]) = hi;
     }
-    const uint8_t* psw = s2 + ((size_t)e * H + c0 + (tid & (kDownCols - 1))) * (I / 32);
-    // step st = (sub-tile st / NB, block st % NB); the step past the last
-    // repeats it (loaded, stored to an unread buffer, not multiplied)
-    auto load = [&](int st, DnRegs& R) {
-      st = min(st, NSTEP - 1);
-      const int sub = st / NB, b = st - sub * NB;
-      const size_t coff = (size_t)sub * kDownCols * (I / 2) + 64 * b;
+    if (tid < kDnRows) {
+      ent[tid] = ve;
 #pragma unroll
-      for (int q = 0; q < 2; ++q) R.b[q] = ld16(pw[q] + coff);
-      R.s = ld4(psw + (size_t)sub * kDownCols * (I / 32) + 4 * b);
-    };
-    auto store = [&](const DnRegs& R, int sb) {
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int idx = tid + 256 * q;
-        *reinterpret_cast<uint4*>(&sm.b[sb][(idx >> 2) * kLDW + 16 * (idx & 3)]) = R.b[q];
-      }
-      if (tid < kDownCols) sm.bs[sb][tid] = R.s;
-    };
-    DnRegs S0, S1, S2;
-    load(0, S0);
-    load(1, S1);
-    load(2, S2);
-    // the tile's mid rows and scales, once per item
-    if (tid < kBM) {
-      sm.ent[tid] = tid < rows ? sorted_entry[r0 + tid] : -1;
-#pragma unroll
-      for (int b = 0; b < NB; ++b) sm.ms[b][tid] = tid < rows ? mids[(size_t)(r0 + tid) * NB + b] : 0.f;
+      for (int b = 0; b < NB; ++b) ms[b * kDnRows + tid] = vs[b];
     }
-    for (int idx = tid; idx < kBM * (I / 16); idx += 256) {
-      const int row = idx / (I / 16), c = idx - row * (I / 16);
-      const uint4 v = row < rows ? ld16(midq + (size_t)(r0 + row) * I + 16 * c) : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(&sm.a[row * LDA + 16 * c]) = v;
-    }
-    store(S0, 0);
     __syncthreads();
-    double acc[4][4][4];
-    v4f P[4][4];
-    auto compute = [&](int st, int sb) {
-      const int sub = st / NB, b = st - sub * NB;
-      if (b == 0) {
+    fetch_tile(next);
+    double acc[2][4][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+    for (int b = 0; b < NB; ++b) {
+      const Stage& S = R[b];
+      float wsc[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j) wsc[j] = e8m0_to_float(S.s[j] & 0xFFu);
+      v4f P[2][4];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc[i][j][v] = 0.0;
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) P[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {  // K = 32 chunks; lane group g holds K 32q + 8g ..
-        v8s fa[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = 64 * wm + 16 * i + r;
-          const uint2 raw = *reinterpret_cast<const uint2*>(&sm.a[row * LDA + 128 * b + 32 * q + 8 * g]);
-          const uint32_t d0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, 1.0f, false));
-          const uint32_t d1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, 1.0f, true));
-          const uint32_t d2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.y, 1.0f, false));
-          const uint32_t d3 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.y, 1.0f, true));
-          fa[i][0] = (short)(d0 & 0xFFFF); fa[i][1] = (short)(d0 >> 16);
-          fa[i][2] = (short)(d1 & 0xFFFF); fa[i][3] = (short)(d1 >> 16);
-          fa[i][4] = (short)(d2 & 0xFFFF); fa[i][5] = (short)(d2 >> 16);
-          fa[i][6] = (short)(d3 & 0xFFFF); fa[i][7] = (short)(d3 >> 16);
-        }
+      for (int q = 0; q < 4; ++q) {
+        v8s fb[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int col = 64 * wn + 16 * j + r;
-          const uint32_t wv = *reinterpret_cast<const uint32_t*>(&sm.b[sb][col * kLDW + 16 * q + 4 * g]);
-          const float wsc = e8m0_to_float((sm.bs[sb][col] >> (8 * q)) & 0xFFu);
-          const uint32_t d0 = cvt_fp4x2_bf16<0>(wv, wsc), d1 = cvt_fp4x2_bf16<1>(wv, wsc);
-          const uint32_t d2 = cvt_fp4x2_bf16<2>(wv, wsc), d3 = cvt_fp4x2_bf16<3>(wv, wsc);
-          v8s fb;
-          fb[0] = (short)(d0 & 0xFFFF); fb[1] = (short)(d0 >> 16);
-          fb[2] = (short)(d1 & 0xFFFF); fb[3] = (short)(d1 >> 16);
-          fb[4] = (short)(d2 & 0xFFFF); fb[5] = (short)(d2 >> 16);
-          fb[6] = (short)(d3 & 0xFFFF); fb[7] = (short)(d3 >> 16);
+          const uint32_t wq = S.w[j][q];
+          fb[j] = as_v8s(cvt_fp4x2_bf16<0>(wq, wsc[j]), cvt_fp4x2_bf16<1>(wq, wsc[j]),
+                         cvt_fp4x2_bf16<2>(wq, wsc[j]), cvt_fp4x2_bf16<3>(wq, wsc[j]));
+        }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) P[i][j] = mfma_bf16(fa[i], fb, P[i][j]);
+        for (int i = 0; i < 2; ++i) {
+          const v8s fa = *reinterpret_cast<const v8s*>(&a16[sw_mid16<NB>(16 * i + m, 16 * b + 4 * g + q)]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) P[i][j] = mfma_bf16(fa, fb[j], P[i][j]);
         }
       }
+      load_block(next, b, R[b]);  // the slot's weights are in registers now
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 2; ++i) {
+        const float4 sc = *reinterpret_cast<const float4*>(&ms[b * kDnRows + 16 * i + 4 * g]);
+        const double scd[4] = {(double)sc.x, (double)sc.y, (double)sc.z, (double)sc.w};
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const double sc = (double)sm.ms[b][64 * wm + 16 * i + 4 * g + v];
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j][v] += sc * (double)P[i][j][v];
-        }
-      if (b == NB - 1) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int en = sm.ent[64 * wm + 16 * i + 4 * g + v];
-            if (en >= 0) {
-#pragma unroll
-              for (int j = 0; j < 4; ++j)
-                y[(size_t)en * H + c0 + sub * kDownCols + 64 * wn + 16 * j + r] = (float)acc[i][j][v];
-            }
-          }
+          for (int v = 0; v < 4; ++v)
+            acc[i][j][v] = b == 0 ? scd[v] * (double)P[i][j][v] : fma(scd[v], (double)P[i][j][v], acc[i][j][v]);
       }
-    };
-    auto iter = [&](int st, DnRegs& cur, DnRegs& nxt) {
-      load(st + 3, cur);
-      if (st < NSTEP) compute(st, st & 1);
-      store(nxt, (st + 1) & 1);
-      barrier_lds();
-    };
-    for (int st = 0; st < NSTEP; st += 3) {
-      iter(st, S0, S1);
-      iter(st + 1, S1, S2);
-      iter(st + 2, S2, S0);
     }
-    __syncthreads();
+    // y row = entry (rows past the tile's end repeat its last row)
+    const int col = item.w * kDnItemCols + 64 * wave + m;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int4 en = *reinterpret_cast<const int4*>(&ent[16 * i + 4 * g]);
+      const int env[4] = {en.x, en.y, en.z, en.w};
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float* py = y + (size_t)env[v] * H + col;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) py[16 * j] = (float)acc[i][j][v];
+      }
+    }
   }
 }
 
@@ -438,20 +437,20 @@ hipError_t launch_gate_up_big(const moe_plan* p, const CallArgs& a, Ev ev) {
 
 hipError_t launch_down_big(const moe_plan* p, const CallArgs& a, Ev ev) {
   const int64_t n = a.M * p->s.top_k;
-  const int64_t tiles = (n + std::min<int64_t>(p->s.E, n) * (kBM - 1) + kBM - 1) / kBM;
+  const int64_t tiles = (n + std::min<int64_t>(p->s.E, n) * (kDnRows - 1) + kDnRows - 1) / kDnRows;
   const int64_t items = tiles * (p->s.H / kDnItemCols);
-  const int blocks = (int)std::min<int64_t>(items, 256);
-  auto go = [&](auto kern) {
-    return launch_k(kern, dim3(blocks), dim3(256), 0, a.stream, ev, wsp<uint8_t>(p, p->L.midq),
+  const int blocks = (int)std::min<int64_t>(items, 2 * (int64_t)p->num_cus);  // two per CU
+  auto go = [&](auto kern, size_t lds) {
+    return launch_k(kern, dim3(blocks), dim3(kDnThreads), lds, a.stream, ev, wsp<uint8_t>(p, p->L.midq),
                     wsp<float>(p, p->L.mids), reinterpret_cast<const uint8_t*>(a.w2),
                     reinterpret_cast<const uint8_t*>(a.s2), wsp<int>(p, p->L.sorted_entry),
                     wsp<int4>(p, p->X.dn_items), wsp<int>(p, p->X.meta), wsp<float>(p, p->L.y), (int)p->s.H);
   };
   switch (p->s.I / 128) {
-    case 1: return go(down_big_kernel<1>);
-    case 2: return go(down_big_kernel<2>);
-    case 3: return go(down_big_kernel<3>);
-    case 4: return go(down_big_kernel<4>);
+    case 1: return go(down_big_kernel<1>, down_big_lds<1>());
+    case 2: return go(down_big_kernel<2>, down_big_lds<2>());
+    case 3: return go(down_big_kernel<3>, down_big_lds<3>());
+    case 4: return go(down_big_kernel<4>, down_big_lds<4>());
     default: return hipErrorInvalidValue;
   }
 }

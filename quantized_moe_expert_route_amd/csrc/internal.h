@@ -12,10 +12,9 @@
 namespace qmoe {
 
 constexpr int kTileRows = 16;  // sorted rows per tile of the small-token kernels
-constexpr int kBigRows = 128;  // sorted rows per tile of the large-token down kernel
+constexpr int kBigRows = 32;   // sorted rows per tile of the large-token down kernel
 constexpr int kGuRows = 64;    // sorted rows per tile of the large-token gate/up kernel
-constexpr int kDownCols = 128; // output columns per sub-tile of the large-token down kernel
-constexpr int kDownItemCols = 512; // output columns per down work item of the large-token kernel
+constexpr int kDownItemCols = 256; // output columns per down work item of the large-token kernel
 
 // Workspace regions beyond the public layout.
 struct Internal {
