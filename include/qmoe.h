@@ -91,7 +91,9 @@ typedef struct {
  * Returns MOE_ERR_INVALID_ARG for null arguments, negative or zero sizes,
  * top_k > E or a non-positive routed_scaling; MOE_ERR_UNSUPPORTED for
  * H % 512 != 0, I not in {128, 256, 384, 512}, E > 1024, top_k > 16,
- * shared_I % 128 != 0 or shared_I > 2048, M > 2^20; MOE_ERR_DEVICE when the
+ * shared_I % 128 != 0 or shared_I > 2048, M > 2^20, H > 65536 or
+ * M * H / 2 > 2^31 - 1 (x's FP4 codes are addressed with 32-bit byte
+ * offsets); MOE_ERR_DEVICE when the
  * current HIP device cannot be queried or is not a gfx950. Creating a plan
  * enqueues no GPU work. */
 moe_status moe_plan_create(const moe_shape* shape, moe_plan** out);

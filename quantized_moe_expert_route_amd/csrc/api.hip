@@ -7,6 +7,8 @@
 
 #include "internal.h"
 
+#include <climits>
+
 using namespace qmoe;
 
 namespace {
@@ -26,6 +28,7 @@ moe_status check_shape(const moe_shape* s) {
       s->shared_I % 128 != 0 || s->shared_I > 2048)
     return MOE_ERR_UNSUPPORTED;
   if (s->M > (int64_t)1 << 20 || s->H > 65536) return MOE_ERR_UNSUPPORTED;
+  if (s->M * (s->H / 2) > INT32_MAX) return MOE_ERR_UNSUPPORTED;  // x codes addressed with 32-bit offsets
   return MOE_OK;
 }
 

@@ -52,6 +52,8 @@ def test_status_strings_and_stages():
     (dict(M=4, H=6144, E=2048, I=256, top_k=8), B.MOE_ERR_UNSUPPORTED),       # E > 1024
     (dict(M=4, H=6144, E=256, I=256, top_k=17), B.MOE_ERR_UNSUPPORTED),       # k > 16
     (dict(M=4, H=6144, E=256, I=256, top_k=8, shared_I=100), B.MOE_ERR_UNSUPPORTED),
+    (dict(M=1 << 20, H=4096, E=256, I=256, top_k=8), B.MOE_ERR_UNSUPPORTED),  # M * H / 2 >= 2^31
+    (dict(M=1 << 19, H=8192, E=256, I=256, top_k=1), B.MOE_ERR_UNSUPPORTED),
 ])
 def test_shape_validation(kw, status):
     if status == B.MOE_OK:
