@@ -264,7 +264,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
 // row's mid scale in float64 and the blocks are summed in order, then rounded
 // once to fp32. Rows past the tile's end repeat its last row: they compute
 // the same values and store them to the same place, so every load and store
-// is unconditional and each wait counts exactly.
+// is unconditional and each wait counts exactly. The item's E8M0 weight
+// scales (its 256 w2 rows' scale rows, one contiguous run) come with the mid
+// rows into LDS: a load whose lanes cover whole cache lines costs the memory
+// pipeline about a quarter of one that reads 4 bytes from each of 16 rows.
 constexpr int kDnRows = kBigRows;
 constexpr int kDnItemCols = kDownItemCols;
 constexpr int kDnThreads = 256;
@@ -277,7 +280,8 @@ __device__ __forceinline__ int sw_mid16(int r, int c) { return r * (NB * 256) + 
 
 template <int NB>
 constexpr size_t down_big_lds() {
-  return (size_t)kDnRows * NB * 256 + sizeof(float) * NB * kDnRows + sizeof(int) * kDnRows;
+  return (size_t)kDnRows * NB * 256 + sizeof(float) * NB * kDnRows + sizeof(int) * kDnRows +
+         (size_t)kDnItemCols * NB * 4;
 }
 
 template <int NB>
@@ -294,12 +298,12 @@ __global__ __launch_bounds__(kDnThreads) __attribute__((amdgpu_waves_per_eu(2)))
   uint8_t* a16 = dyn_lds;                                             // [kDnRows] widened mid rows
   float* ms = reinterpret_cast<float*>(dyn_lds + kDnRows * NB * 256);  // [NB][kDnRows] mid scales
   int* ent = reinterpret_cast<int*>(ms + NB * kDnRows);                // [kDnRows] entries
+  uint8_t* wsl = reinterpret_cast<uint8_t*>(ent + kDnRows);           // [kDnItemCols][4 NB] weight scales
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = lane & 15, g = lane >> 4;
   typedef unsigned v4u __attribute__((ext_vector_type(4)));
   struct Stage {
     v4u w[4];
-    uint32_t s[4];
   };
   int first, stride, end;
   xcd_run(meta[2], first, stride, end);
@@ -309,6 +313,10 @@ __global__ __launch_bounds__(kDnThreads) __attribute__((amdgpu_waves_per_eu(2)))
   v4u va[QA];
   int ve;
   float vs[NB];
+  typedef unsigned v2u __attribute__((ext_vector_type(2)));
+  v4u vsc4;
+  v2u vsc2;
+  unsigned vsc1, vsc3[3];
   auto fetch_tile = [&](const int4 item) {
     const int r0 = item.y, rows = item.z - item.y;
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
@@ -323,20 +331,27 @@ __global__ __launch_bounds__(kDnThreads) __attribute__((amdgpu_waves_per_eu(2)))
     ve = sorted_entry[r0 + row];
 #pragma unroll
     for (int b = 0; b < NB; ++b) vs[b] = mids[(size_t)(r0 + row) * NB + b];
+    // the item's scale rows: kDnItemCols x 4 NB contiguous bytes, 4 NB bytes a thread
+    const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(s2 + ((size_t)item.x * H + (size_t)item.w * kDnItemCols) * Sb), (short)0,
+        kDnItemCols * Sb, 0x00020000);
+    if (NB == 4) vsc4 = __builtin_amdgcn_raw_buffer_load_b128(rsc, 16 * tid, 0, 0);
+    else if (NB == 2) vsc2 = __builtin_amdgcn_raw_buffer_load_b64(rsc, 8 * tid, 0, 0);
+    else if (NB == 3) {
+      vsc3[0] = __builtin_amdgcn_raw_buffer_load_b32(rsc, 12 * tid, 0, 0);
+      vsc3[1] = __builtin_amdgcn_raw_buffer_load_b32(rsc, 12 * tid + 4, 0, 0);
+      vsc3[2] = __builtin_amdgcn_raw_buffer_load_b32(rsc, 12 * tid + 8, 0, 0);
+    } else vsc1 = __builtin_amdgcn_raw_buffer_load_b32(rsc, 4 * tid, 0, 0);
   };
   // weights of block b of an item into a ring slot: column c0 + 64 w + 16 j
   // + m, 16 bytes at 64 b + 16 g of its w2 row and byte 4 b + g of its s2 row
   auto load_block = [&](const int4 item, int b, Stage& S) {
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(w2 + (size_t)item.x * H * Wb), (short)0, H * Wb, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(s2 + (size_t)item.x * H * Sb), (short)0, H * Sb, 0x00020000);
     const int col = item.w * kDnItemCols + 64 * wave + m;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 4; ++j)
       S.w[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, col * Wb + 16 * g, 16 * j * Wb + 64 * b, 0);
-      S.s[j] = __builtin_amdgcn_raw_buffer_load_b8(rs, col * Sb + g, 16 * j * Sb + 4 * b, 0);
-    }
   };
   Stage R[NB];
   {
@@ -364,6 +379,12 @@ __global__ __launch_bounds__(kDnThreads) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
       for (int b = 0; b < NB; ++b) ms[b * kDnRows + tid] = vs[b];
     }
+    if (NB == 4) *reinterpret_cast<v4u*>(&wsl[16 * tid]) = vsc4;
+    else if (NB == 2) *reinterpret_cast<v2u*>(&wsl[8 * tid]) = vsc2;
+    else if (NB == 3) {
+#pragma unroll
+      for (int q = 0; q < 3; ++q) *reinterpret_cast<unsigned*>(&wsl[12 * tid + 4 * q]) = vsc3[q];
+    } else *reinterpret_cast<unsigned*>(&wsl[4 * tid]) = vsc1;
     __syncthreads();
     fetch_tile(next);
     double acc[2][4][4];
@@ -372,7 +393,7 @@ __global__ __launch_bounds__(kDnThreads) __attribute__((amdgpu_waves_per_eu(2)))
       const Stage& S = R[b];
       float wsc[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) wsc[j] = e8m0_to_float(S.s[j] & 0xFFu);
+      for (int j = 0; j < 4; ++j) wsc[j] = e8m0_to_float(wsl[(64 * wave + 16 * j + m) * Sb + 4 * b + g]);
       v4f P[2][4];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
