@@ -16,6 +16,7 @@
 #include "internal.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace qmoe {
 
@@ -255,8 +256,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
 // CU. At the start of an item the tile's E4M3 mid rows, fetched into
 // registers during the previous item, are widened to bf16 (exactly) into
 // LDS. Wave w then covers all the tile's rows x 64 columns, one 128-block per
-// step; its MXFP4 weights for the next item are loaded into the ring slot a
-// step has just used, so the loads run one item ahead without a barrier.
+// step. The item's 256 w2 rows are contiguous; they are read in halves of up
+// to two 128-blocks (128 bytes a row: every load instruction covers whole
+// cache lines) into registers while the previous half is multiplied, and
+// pass through one LDS buffer to the MFMA layout.
 // Within a 128-block, lane group g holds K 32 g .. 32 g + 31 of its column
 // (16 bytes and one E8M0 byte), fed to the bf16 MFMA as K 32 g + 8 q .. + 8
 // in step q; the mid operand follows the same assignment. Products and block
@@ -278,10 +281,19 @@ constexpr int kDnThreads = 256;
 template <int NB>
 __device__ __forceinline__ int sw_mid16(int r, int c) { return r * (NB * 256) + 16 * (c ^ (r & 15)); }
 
+// LDS place of 16-byte chunk c of weight row r in a half of BH blocks (rows
+// of 64 BH bytes): c is XORed with a row function inside the row, so that
+// sixteen consecutive rows reading one chunk, and a row's chunks written by
+// consecutive lanes, fall in different bank groups.
+template <int BH>
+__device__ __forceinline__ int sw_w(int r, int c) {
+  return BH == 2 ? r * 128 + 16 * (c ^ ((r >> 1) & 7)) : r * 64 + 16 * (c ^ ((r >> 2) & 3));
+}
+
 template <int NB>
 constexpr size_t down_big_lds() {
   return (size_t)kDnRows * NB * 256 + sizeof(float) * NB * kDnRows + sizeof(int) * kDnRows +
-         (size_t)kDnItemCols * NB * 4;
+         (size_t)kDnItemCols * NB * 4 + (size_t)kDnItemCols * (NB > 1 ? 128 : 64);
 }
 
 template <int NB>
@@ -299,12 +311,11 @@ __global__ __launch_bounds__(kDnThreads) __attribute__((amdgpu_waves_per_eu(2)))
   float* ms = reinterpret_cast<float*>(dyn_lds + kDnRows * NB * 256);  // [NB][kDnRows] mid scales
   int* ent = reinterpret_cast<int*>(ms + NB * kDnRows);                // [kDnRows] entries
   uint8_t* wsl = reinterpret_cast<uint8_t*>(ent + kDnRows);           // [kDnItemCols][4 NB] weight scales
+  uint8_t* wld = wsl + kDnItemCols * Sb;                               // [kDnItemCols] rows of a weight half
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = lane & 15, g = lane >> 4;
   typedef unsigned v4u __attribute__((ext_vector_type(4)));
-  struct Stage {
-    v4u w[4];
-  };
+  constexpr int NH = (NB + 1) / 2;  // weight halves
   int first, stride, end;
   xcd_run(meta[2], first, stride, end);
   if (first >= end) return;
@@ -343,22 +354,32 @@ __global__ __launch_bounds__(kDnThreads) __attribute__((amdgpu_waves_per_eu(2)))
       vsc3[2] = __builtin_amdgcn_raw_buffer_load_b32(rsc, 12 * tid + 8, 0, 0);
     } else vsc1 = __builtin_amdgcn_raw_buffer_load_b32(rsc, 4 * tid, 0, 0);
   };
-  // weights of block b of an item into a ring slot: column c0 + 64 w + 16 j
-  // + m, 16 bytes at 64 b + 16 g of its w2 row and byte 4 b + g of its s2 row
-  auto load_block = [&](const int4 item, int b, Stage& S) {
+  // weight half h of an item (blocks 2h, 2h+1): thread t holds chunks
+  // t + 256 q, 4 BH chunks of 16 bytes to a row
+  v4u vw[8];
+  auto load_half = [&](const int4 item, auto hc) {
+    constexpr int h = decltype(hc)::value, BH = NB - 2 * h >= 2 ? 2 : 1;
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(w2 + (size_t)item.x * H * Wb), (short)0, H * Wb, 0x00020000);
-    const int col = item.w * kDnItemCols + 64 * wave + m;
+        const_cast<uint8_t*>(w2 + ((size_t)item.x * H + (size_t)item.w * kDnItemCols) * Wb), (short)0,
+        kDnItemCols * Wb, 0x00020000);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      S.w[j] = __builtin_amdgcn_raw_buffer_load_b128(rw, col * Wb + 16 * g, 16 * j * Wb + 64 * b, 0);
+    for (int q = 0; q < 4 * BH; ++q) {
+      const int idx = tid + kDnThreads * q, row = idx / (4 * BH), c = idx % (4 * BH);
+      vw[q] = __builtin_amdgcn_raw_buffer_load_b128(rw, row * Wb + 16 * c, 128 * h, 0);
+    }
   };
-  Stage R[NB];
+  auto store_half = [&](auto hc) {
+    constexpr int h = decltype(hc)::value, BH = NB - 2 * h >= 2 ? 2 : 1;
+#pragma unroll
+    for (int q = 0; q < 4 * BH; ++q) {
+      const int idx = tid + kDnThreads * q, row = idx / (4 * BH), c = idx % (4 * BH);
+      *reinterpret_cast<v4u*>(&wld[sw_w<BH>(row, c)]) = vw[q];
+    }
+  };
   {
     const int4 item = items[first];
     fetch_tile(item);
-#pragma unroll
-    for (int b = 0; b < NB; ++b) load_block(item, b, R[b]);
+    load_half(item, std::integral_constant<int, 0>());
   }
   for (int it = first; it < end; it += stride) {
     const int4 item = items[it];
@@ -385,12 +406,14 @@ __global__ __launch_bounds__(kDnThreads) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
       for (int q = 0; q < 3; ++q) *reinterpret_cast<unsigned*>(&wsl[12 * tid + 4 * q]) = vsc3[q];
     } else *reinterpret_cast<unsigned*>(&wsl[4 * tid]) = vsc1;
-    __syncthreads();
-    fetch_tile(next);
     double acc[2][4][4];
+    // one 128-block: B fragments from the weight half in LDS
+    auto block = [&](auto bc) {
+      constexpr int b = decltype(bc)::value, h = b / 2, BH = NB - 2 * h >= 2 ? 2 : 1;
+      v4u Sw[4];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const Stage& S = R[b];
+      for (int j = 0; j < 4; ++j)
+        Sw[j] = *reinterpret_cast<const v4u*>(&wld[sw_w<BH>(64 * wave + 16 * j + m, 4 * (b % 2) + g)]);
       float wsc[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) wsc[j] = e8m0_to_float(wsl[(64 * wave + 16 * j + m) * Sb + 4 * b + g]);
@@ -404,7 +427,7 @@ __global__ __launch_bounds__(kDnThreads) __attribute__((amdgpu_waves_per_eu(2)))
         v8s fb[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const uint32_t wq = S.w[j][q];
+          const uint32_t wq = Sw[j][q];
           fb[j] = as_v8s(cvt_fp4x2_bf16<0>(wq, wsc[j]), cvt_fp4x2_bf16<1>(wq, wsc[j]),
                          cvt_fp4x2_bf16<2>(wq, wsc[j]), cvt_fp4x2_bf16<3>(wq, wsc[j]));
         }
@@ -415,7 +438,6 @@ __global__ __launch_bounds__(kDnThreads) __attribute__((amdgpu_waves_per_eu(2)))
           for (int j = 0; j < 4; ++j) P[i][j] = mfma_bf16(fa, fb[j], P[i][j]);
         }
       }
-      load_block(next, b, R[b]);  // the slot's weights are in registers now
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const float4 sc = *reinterpret_cast<const float4*>(&ms[b * kDnRows + 16 * i + 4 * g]);
@@ -426,6 +448,27 @@ __global__ __launch_bounds__(kDnThreads) __attribute__((amdgpu_waves_per_eu(2)))
           for (int v = 0; v < 4; ++v)
             acc[i][j][v] = b == 0 ? scd[v] * (double)P[i][j][v] : fma(scd[v], (double)P[i][j][v], acc[i][j][v]);
       }
+    };
+    // half 0 (in registers) to LDS; the next half's loads run while a half
+    // is multiplied; after the last half's loads go out, the next item's
+    // mid rows and first half
+    store_half(std::integral_constant<int, 0>());
+    __syncthreads();
+    if (NH > 1) load_half(item, std::integral_constant<int, 1>());
+    else {
+      fetch_tile(next);
+      load_half(next, std::integral_constant<int, 0>());
+    }
+    block(std::integral_constant<int, 0>());
+    if (NB > 1) block(std::integral_constant<int, 1 % NB>());
+    if (NH > 1) {
+      __syncthreads();  // every wave is done with half 0
+      store_half(std::integral_constant<int, NH - 1>());
+      __syncthreads();
+      fetch_tile(next);
+      load_half(next, std::integral_constant<int, 0>());
+      block(std::integral_constant<int, 2 % NB>());
+      if (NB > 3) block(std::integral_constant<int, 3 % NB>());
     }
     // y row = entry (rows past the tile's end repeat its last row)
     const int col = item.w * kDnItemCols + 64 * wave + m;
