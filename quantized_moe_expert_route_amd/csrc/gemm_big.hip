@@ -55,18 +55,27 @@ constexpr int kGuStages = 2;  // K-steps of gate/up loads held in registers
 // ran one after another).
 constexpr int kGuR = kGuRows;
 
+// Scales: a load whose lanes read 4 bytes from each of 64 rows costs the
+// memory pipeline about four times one that reads 16 bytes from each of 16
+// rows, so the x scales of the tile's rows (192 bytes a row at H = 6144)
+// come once per item, row by row, and the weight scales come 16 bytes a row
+// per 512-wide K stage: each wave loads a quarter of its own 64 rows' next
+// stage with every K-step, into a region of LDS only it reads.
+constexpr int kGuXsSteps = 48;  // K-steps of x scales staged at a time (all of them up to H = 6144)
+constexpr int kGuXsLd = 13;     // 16-byte chunks per staged x-scale row (12 used; 13 keeps reads conflict-free)
+
 struct GuSmem {
-  uint8_t a[2][kGuR * 64];    // x rows (MXFP4), K-step slice (sw64 layout)
-  uint8_t b[2][256 * 64];     // 128 gate + 128 up weight rows
-  uint32_t as[2][kGuR];       // 4 E8M0 bytes per row per K-step
-  uint32_t bs[2][256];
+  uint8_t a[2][kGuR * 64];      // x rows (MXFP4), K-step slice (sw64 layout)
+  uint8_t b[2][256 * 64];       // 128 gate + 128 up weight rows
+  uint32_t xs[kGuR][4 * kGuXsLd];  // x scales of kGuXsSteps K-steps, 4 E8M0 bytes per K-step
+  uint32_t bs[2][256][4];       // weight scales of a 512-wide stage (by stage parity)
 };
 
-// One K-step of global data held in registers: 1 + 4 16-byte chunks and the
-// scale dwords of this thread.
+// One K-step of global data held in registers: 1 + 4 16-byte chunks and a
+// quarter of the wave's weight scales of a later stage.
 struct GuRegs {
   uint4 a, b[4];
-  uint32_t sa, sb;
+  uint32_t sb;
 };
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gate_up_big_kernel(
@@ -112,9 +121,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
         const_cast<uint8_t*>(s13 + (size_t)e * 2 * I * Hs), (short)0, (int)(2 * I * Hs), 0x00020000);
     const int ob = (128 * ib + (tid >> 2)) * (int)Hb + 16 * (tid & 3);
     const int boff[4] = {0, 64 * (int)Hb, (I - 128 + 128) * (int)Hb, (I - 128 + 192) * (int)Hb};
-    const int os = (int)(wrow(tid) - (size_t)e * 2 * I) * (int)Hs;
-    const int ts = tok[tid & (kGuR - 1)];
-    const uint8_t* psa = xs + (size_t)(ts >= 0 ? ts : tok0) * Hs;
+    // weight-scale quarter q of a stage for this lane: local row
+    // (gate 0..127, up 128..255) and the E8M0 dword lane & 3 of it
+    auto sq_row = [&](int q) { return (q < 2 ? 32 * wn + 16 * q : 128 + 32 * wn + 16 * (q - 2)) + (lane >> 2); };
+    auto sq_off = [&](int q) {
+      const int lr = sq_row(q);
+      return (lr < 128 ? 128 * ib + lr : I + 128 * ib + lr - 128) * (int)Hs + 4 * (lane & 3);
+    };
+    const int ns = nk / 4;  // 512-wide stages
     auto load = [&](int kk, GuRegs& R) {
       R.a = ld16(pa + kk * 64);
 #pragma unroll
@@ -123,18 +137,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
         const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rw, ob, boff[q] + kk * 64, 0);
         R.b[q] = make_uint4(v.x, v.y, v.z, v.w);
       }
-      R.sa = ld4(psa + kk * 4);
-      R.sb = __builtin_amdgcn_raw_buffer_load_b32(rs, os, kk * 4, 0);
+      // quarter kk % 4 of stage kk / 4 + 1 (past the last stage: the last one again, unread)
+      R.sb = __builtin_amdgcn_raw_buffer_load_b32(rs, sq_off(kk & 3), 16 * min(kk / 4 + 1, ns - 1), 0);
     };
-    auto store = [&](const GuRegs& R, int s) {
+    // R holds K-step kk's data (to buffer kk & 1) and a scale quarter
+    auto store = [&](const GuRegs& R, int kk) {
+      const int s = kk & 1;
       *reinterpret_cast<uint4*>(&sm.a[s][sw64(tid >> 2, tid & 3)]) = R.a;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int idx = tid + 256 * q;
         *reinterpret_cast<uint4*>(&sm.b[s][sw64(idx >> 2, idx & 3)]) = R.b[q];
       }
-      if (tid < kGuR) sm.as[s][tid] = R.sa;
-      sm.bs[s][tid] = R.sb;
+      sm.bs[(kk / 4 + 1) & 1][sq_row(kk & 3)][lane & 3] = R.sb;
     };
     v4f accg[4][2], accu[4][2];
 #pragma unroll
@@ -144,22 +159,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
         accg[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
         accu[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
       }
-    auto compute = [&](int s) {
+    auto compute = [&](int kk) {
+      const int s = kk & 1, ss = (kk / 4) & 1, q4 = kk & 3;
       uint4 fa[4];
       uint32_t sa[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * i + r;
         fa[i] = *reinterpret_cast<const uint4*>(&sm.a[s][sw64(row, g)]);
-        sa[i] = (sm.as[s][row] >> (8 * g)) & 0xFFu;
+        sa[i] = (sm.xs[row][kk % kGuXsSteps] >> (8 * g)) & 0xFFu;
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int col = 32 * wn + 16 * j + r;
         const uint4 fg = *reinterpret_cast<const uint4*>(&sm.b[s][sw64(col, g)]);
         const uint4 fu = *reinterpret_cast<const uint4*>(&sm.b[s][sw64(col + 128, g)]);
-        const uint32_t sg = (sm.bs[s][col] >> (8 * g)) & 0xFFu;
-        const uint32_t su = (sm.bs[s][col + 128] >> (8 * g)) & 0xFFu;
+        const uint32_t sg = (sm.bs[ss][col][q4] >> (8 * g)) & 0xFFu;
+        const uint32_t su = (sm.bs[ss][col + 128][q4] >> (8 * g)) & 0xFFu;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           accg[i][j] = mfma_fp4(fa[i], fg, accg[i][j], sa[i], sg);
@@ -171,6 +187,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
     // kk's registers are refilled with step kk+kGuStages right after they
     // were stored. Past the last step the loads repeat it and the stores fill
     // a buffer nobody reads; only the MFMA work is skipped.
+    // the tile's x scales of K-steps kGuXsSteps m .. (one row of 16-byte
+    // chunks per token, read row by row)
+    auto stage_xs = [&](int m) {
+      const int nxc = min(kGuXsSteps, nk - kGuXsSteps * m) / 4;  // 16-byte chunks per row
+      for (int idx = tid; idx < kGuR * nxc; idx += 256) {
+        const int row = idx / nxc, c = idx - row * nxc;
+        const int t = tok[row];
+        *reinterpret_cast<uint4*>(&sm.xs[row][4 * c]) =
+            ld16(xs + (size_t)(t >= 0 ? t : tok0) * Hs + kGuXsSteps * 4 * m + 16 * c);
+      }
+    };
+    // prologue: x scales and the wave's stage-0 weight scales into LDS, then
+    // the first K-steps
+    stage_xs(0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      sm.bs[0][sq_row(q)][lane & 3] = __builtin_amdgcn_raw_buffer_load_b32(rs, sq_off(q), 0, 0);
     GuRegs S[kGuStages];
 #pragma unroll
     for (int q = 0; q < kGuStages; ++q) load(min(q, nk - 1), S[q]);
@@ -180,8 +213,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
 #pragma unroll
       for (int q = 0; q < kGuStages; ++q) {
         load(min(kk + q + kGuStages, nk - 1), S[q]);
-        if (kk + q < nk) compute((kk + q) & 1);
-        store(S[(q + 1) % kGuStages], (kk + q + 1) & 1);
+        if (kk + q < nk) {
+          if (kk + q > 0 && (kk + q) % kGuXsSteps == 0) {  // only when H > 6144
+            stage_xs((kk + q) / kGuXsSteps);  // every wave is past the previous step's barrier
+            barrier_lds();
+          }
+          compute(kk + q);
+        }
+        store(S[(q + 1) % kGuStages], kk + q + 1);
         barrier_lds();
       }
     }

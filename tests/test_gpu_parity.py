@@ -140,6 +140,7 @@ SMALL = [
     (300, 512, 8, 512, 2, "normal", 0),        # several full tiles per expert, I = 512
     (96, 512, 64, 384, 8, "ties", 0),
     (70, 512, 4, 128, 2, "normal", 128),       # with the shared expert
+    (72, 8192, 8, 128, 2, "normal", 0),        # H past 6144: x scales staged in two parts
 ]
 
 
