@@ -64,6 +64,7 @@ Layout make_layout(const moe_shape& s) {
   r.X.meta = take(256);
   r.X.gu_items = take(16 * (size_t)r.tg * (I / 128));
   r.X.dn_items = take(16 * (size_t)r.tb * (H / kDownItemCols));
+  r.X.toff = take(4 * 2 * (E + 1));
   // the token bitmap: zeroed when the workspace is bound, and
   // left zero by every call
   r.X.bitmap = take(4 * E * (size_t)r.words);

@@ -22,6 +22,7 @@ struct Internal {
   size_t meta;     // int32 [64]: meta[0] tiles, meta[1] gate/up items, meta[2] down items
   size_t gu_items; // int4 [TG * I/128]: {expert, row_begin, row_end, column block}, tiles of kGuRows, large M
   size_t dn_items; // int4 [TB * H/kDownItemCols]: {expert, row_begin, row_end, column chunk}, large M
+  size_t toff;     // int32 [2][E + 1]: tile prefix per expert of the gate/up and the down tiles, large M
   size_t bitmap;   // uint32 [E, ceil(M/32)]: bit t of row e = token t picked e; zero between calls
   size_t pw;       // int2 [E, ceil(M/32)]: {set bits of row e before word w, word w}
   size_t h;        // fp32 [n, I]: SiLU(gate)*up, rows in sorted order

@@ -235,44 +235,42 @@ __global__ __launch_bounds__(256) void route_kernel(
 // Work items of the large-token GEMMs, per expert in the order (column
 // block, row tile) so that the row tiles sharing a weight block are adjacent:
 // gate/up items on tiles of kGuRows rows, down items on tiles of kBigRows.
-// Thread per item: the expert is found by binary search of the tile prefix.
-__device__ void write_big_items(int c, int E, int n_iblk, int n_nc, int* s_toff, int* s_off, int* s_tmp,
-                                int4* __restrict__ gu_items, int4* __restrict__ dn_items, int* __restrict__ meta) {
+// One workgroup forms the tile prefixes (write_tile_prefixes); the items
+// themselves are written by every workgroup of the placement launch, a
+// thread per item, the expert found by binary search of the prefix in LDS
+// (one workgroup writing all of them was bound by one CU's store rate).
+__device__ void write_tile_prefixes(int c, int E, int n_iblk, int n_nc, int* s_tmp, int* __restrict__ toff,
+                                    int* __restrict__ meta) {
   const int tid = threadIdx.x;
-  int total_rows;
-  const int off = block_exclusive_scan(c, s_tmp, &total_rows);
-  if (tid < E) s_off[tid] = off;
-  if (tid == 0) s_off[E] = total_rows;
   for (int pass = 0; pass < 2; ++pass) {
     const int tr = pass == 0 ? kGuRows : kBigRows;
-    const int nb = pass == 0 ? n_iblk : n_nc;
-    int4* out = pass == 0 ? gu_items : dn_items;
     const int nt = (c + tr - 1) / tr;
     int total_tiles;
-    const int toff = block_exclusive_scan(nt, s_tmp, &total_tiles);
-    if (tid < E) s_toff[tid] = toff;
+    const int t0 = block_exclusive_scan(nt, s_tmp, &total_tiles);
+    if (tid < E) toff[pass * (E + 1) + tid] = t0;
     if (tid == 0) {
-      s_toff[E] = total_tiles;
-      meta[1 + pass] = total_tiles * nb;
+      toff[pass * (E + 1) + E] = total_tiles;
+      meta[1 + pass] = total_tiles * (pass == 0 ? n_iblk : n_nc);
     }
-    __syncthreads();
-    for (int i = tid; i < total_tiles * nb; i += blockDim.x) {
-      const int tile = i / nb;  // items of expert e occupy [toff[e] * nb, toff[e + 1] * nb)
-      int lo = 0, hi = E;       // largest e with toff[e] <= tile and a tile of its own
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (s_toff[mid] <= tile) lo = mid; else hi = mid;
-      }
-      int e = lo;
-      while (s_toff[e + 1] == s_toff[e]) ++e;  // skip experts without tiles
-      const int nte = s_toff[e + 1] - s_toff[e];
-      const int local = i - s_toff[e] * nb;
-      const int b = local / nte, mt = local - b * nte;
-      const int r0 = s_off[e] + mt * tr;
-      out[i] = make_int4(e, r0, min(r0 + tr, s_off[e + 1]), b);
-    }
-    __syncthreads();  // s_toff is rewritten by the next pass
+    __syncthreads();  // s_tmp is reused
   }
+}
+
+// Item i of a pass from the tile prefix s_toff and the row offsets s_off.
+__device__ __forceinline__ int4 big_item(int i, int E, int nb, int tr, const int* s_toff, const int* s_off) {
+  const int tile = i / nb;  // items of expert e occupy [toff[e] * nb, toff[e + 1] * nb)
+  int lo = 0, hi = E;       // largest e with toff[e] <= tile and a tile of its own
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_toff[mid] <= tile) lo = mid; else hi = mid;
+  }
+  int e = lo;
+  while (s_toff[e + 1] == s_toff[e]) ++e;  // skip experts without tiles
+  const int nte = s_toff[e + 1] - s_toff[e];
+  const int local = i - s_toff[e] * nb;
+  const int b = local / nte, mt = local - b * nte;
+  const int r0 = s_off[e] + mt * tr;
+  return make_int4(e, r0, min(r0 + tr, s_off[e + 1]), b);
 }
 
 // Sort for M > kSmallM in three launches, none with a serial chain:
@@ -280,10 +278,10 @@ __device__ void write_big_items(int c, int E, int n_iblk, int n_nc, int* s_toff,
 //    t picked e): the exclusive prefix of the words' popcounts, stored with
 //    the word, and the row total (the expert's count); it is the bitmap's
 //    only reader and leaves it zero for the next call;
-// 2. one workgroup: offsets, 16-row tiles and the work items from the counts;
+// 2. one workgroup: offsets and the tile prefixes from the counts;
 // 3. one thread per entry t*k+j: its place in expert e's run is offset[e]
 //    plus the number of e's tokens before t (prefix + popcount below bit t),
-//    so entries of earlier tokens come first.
+//    so entries of earlier tokens come first; and one thread per work item.
 __global__ __launch_bounds__(256) void align_rows_kernel(uint32_t* __restrict__ bitmap, int words,
                                                          int2* __restrict__ pw, int* __restrict__ count) {
   __shared__ int s_wsum[4];
@@ -321,28 +319,40 @@ __global__ __launch_bounds__(256) void align_rows_kernel(uint32_t* __restrict__ 
 
 __global__ __launch_bounds__(1024) void align_offsets_kernel(
     const int* __restrict__ count_in, int E, int* __restrict__ count, int* __restrict__ offset,
-    int4* __restrict__ tiles, int* __restrict__ meta, int n_iblk, int n_nc, int4* __restrict__ gu_items,
-    int4* __restrict__ dn_items) {
+    int4* __restrict__ tiles, int* __restrict__ meta, int n_iblk, int n_nc, int* __restrict__ toff) {
   __shared__ int s_off[1024];
-  __shared__ int s_toff2[1025];
-  __shared__ int s_off2[1025];
   __shared__ int s_tmp[64];
   const int tid = threadIdx.x;
   const int c = tid < E ? count_in[tid] : 0;
   __syncthreads();  // count_in may be count itself
   write_offsets_tiles(c, E, s_off, s_tmp, count, offset, tiles, meta, false);
-  write_big_items(c, E, n_iblk, n_nc, s_toff2, s_off2, s_tmp, gu_items, dn_items, meta);
+  write_tile_prefixes(c, E, n_iblk, n_nc, s_tmp, toff, meta);
 }
 
 __global__ __launch_bounds__(256) void align_place_kernel(const int* __restrict__ topk_ids, int n, int k, int words,
                                                           const int2* __restrict__ pw, const int* __restrict__ offset,
-                                                          int* __restrict__ sorted_entry) {
+                                                          int* __restrict__ sorted_entry, int E, int n_iblk, int n_nc,
+                                                          const int* __restrict__ toff, const int* __restrict__ meta,
+                                                          int4* __restrict__ gu_items, int4* __restrict__ dn_items) {
+  __shared__ int s_off[1025];
+  __shared__ int s_toff[2][1025];
   for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) {
     const int e = topk_ids[i], t = i / k;
     const int2 v = pw[(size_t)e * words + (t >> 5)];
     const int rank = v.x + __popc((uint32_t)v.y & ((1u << (t & 31)) - 1u));
     sorted_entry[offset[e] + rank] = i;
   }
+  for (int i = threadIdx.x; i <= E; i += 256) {
+    s_off[i] = offset[i];
+    s_toff[0][i] = toff[i];
+    s_toff[1][i] = toff[E + 1 + i];
+  }
+  __syncthreads();
+  const int n_gu = meta[1], n_dn = meta[2];
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n_gu; i += gridDim.x * 256)
+    gu_items[i] = big_item(i, E, n_iblk, kGuRows, s_toff[0], s_off);
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n_dn; i += gridDim.x * 256)
+    dn_items[i] = big_item(i, E, n_nc, kBigRows, s_toff[1], s_off);
 }
 
 __global__ void zero_kernel(uint4* p, size_t n16) {
@@ -400,12 +410,13 @@ hipError_t launch_align(const moe_plan* p, const CallArgs& a, Ev ev) {
   if (e != hipSuccess) return e;
   e = launch_k(align_offsets_kernel, dim3(1), dim3(1024), 0, a.stream, Ev{}, wsp<int>(p, p->L.count),
                (int)p->s.E, wsp<int>(p, p->L.count), wsp<int>(p, p->L.offset), wsp<int4>(p, p->X.tiles),
-               wsp<int>(p, p->X.meta), (int)(p->s.I / 128), (int)(p->s.H / kDownItemCols),
-               wsp<int4>(p, p->X.gu_items), wsp<int4>(p, p->X.dn_items));
+               wsp<int>(p, p->X.meta), (int)(p->s.I / 128), (int)(p->s.H / kDownItemCols), wsp<int>(p, p->X.toff));
   if (e != hipSuccess) return e;
   return launch_k(align_place_kernel, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 4096)), dim3(256), 0,
                   a.stream, Ev{nullptr, ev.stop}, wsp<int>(p, p->L.topk_ids), (int)n, (int)p->s.top_k, words,
-                  wsp<int2>(p, p->X.pw), wsp<int>(p, p->L.offset), wsp<int>(p, p->L.sorted_entry));
+                  wsp<int2>(p, p->X.pw), wsp<int>(p, p->L.offset), wsp<int>(p, p->L.sorted_entry), (int)p->s.E,
+                  (int)(p->s.I / 128), (int)(p->s.H / kDownItemCols), wsp<int>(p, p->X.toff), wsp<int>(p, p->X.meta),
+                  wsp<int4>(p, p->X.gu_items), wsp<int4>(p, p->X.dn_items));
 }
 
 }  // namespace qmoe
