@@ -292,35 +292,30 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
   }
 }
 
-// out[t, c..c+7]: float64 products and sum in slot order (+ shared), then bf16.
+// out[t, c..c+3]: float64 products and sum in slot order (+ shared), then
+// bf16. A thread per 4 columns: consecutive lanes read consecutive 16 bytes
+// of a y row, so each load instruction covers whole cache lines.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, const float* __restrict__ w,
                                                       const float* __restrict__ ys, int M, int H, int k,
                                                       uint16_t* __restrict__ out) {
-  const int per_tok = H / 8;
+  const int per_tok = H / 4;
   const int64_t total = (int64_t)M * per_tok;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
     const int t = (int)(i / per_tok);
-    const int c = (int)(i % per_tok) * 8;
-    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    const int c = (int)(i % per_tok) * 4;
+    double acc[4] = {0, 0, 0, 0};
     for (int j = 0; j < k; ++j) {
       const double wj = (double)w[(size_t)t * k + j];
-      const float* py = y + ((size_t)t * k + j) * H + c;
-      const float4 a = *reinterpret_cast<const float4*>(py);
-      const float4 b = *reinterpret_cast<const float4*>(py + 4);
+      const float4 a = *reinterpret_cast<const float4*>(y + ((size_t)t * k + j) * H + c);
       acc[0] += wj * (double)a.x; acc[1] += wj * (double)a.y; acc[2] += wj * (double)a.z; acc[3] += wj * (double)a.w;
-      acc[4] += wj * (double)b.x; acc[5] += wj * (double)b.y; acc[6] += wj * (double)b.z; acc[7] += wj * (double)b.w;
     }
     if (ys) {
-      const float* ps = ys + (size_t)t * H + c;
-      const float4 a = *reinterpret_cast<const float4*>(ps);
-      const float4 b = *reinterpret_cast<const float4*>(ps + 4);
+      const float4 a = *reinterpret_cast<const float4*>(ys + (size_t)t * H + c);
       acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
-      acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
     }
-    uint32_t o[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) o[q] = bf16_rne_from_double(acc[2 * q]) | (bf16_rne_from_double(acc[2 * q + 1]) << 16);
-    *reinterpret_cast<uint4*>(out + (size_t)t * H + c) = make_uint4(o[0], o[1], o[2], o[3]);
+    const uint32_t o0 = bf16_rne_from_double(acc[0]) | (bf16_rne_from_double(acc[1]) << 16);
+    const uint32_t o1 = bf16_rne_from_double(acc[2]) | (bf16_rne_from_double(acc[3]) << 16);
+    *reinterpret_cast<uint2*>(out + (size_t)t * H + c) = make_uint2(o0, o1);
   }
 }
 
@@ -366,7 +361,7 @@ hipError_t launch_down_combine(const moe_plan* p, const CallArgs& a, Ev ev) {
 
 hipError_t launch_combine(const moe_plan* p, const CallArgs& a, Ev ev) {
   const int H = (int)p->s.H;
-  const int64_t total = a.M * (H / 8);
+  const int64_t total = a.M * (H / 4);
   const int blocks = (int)std::min<int64_t>((total + 255) / 256, 8192);
   const float* ys = p->s.shared_I > 0 ? wsp<float>(p, p->L.sh_y) : nullptr;
   return launch_k(combine_kernel, dim3(blocks), dim3(256), 0, a.stream, ev, wsp<float>(p, p->L.y),
