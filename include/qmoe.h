@@ -76,8 +76,10 @@ typedef struct moe_plan moe_plan; /* opaque; host memory only */
  *                                   written only by calls with M > 64 (up to
  *                                   64 tokens the combine runs in the down
  *                                   launch and slot results stay on chip)
- *   sh_xq/sh_xs  u8 [M, H] / fp32 [M, H/128]      shared expert x in E4M3
- *   sh_hq/sh_hs  u8 [M, Is] / fp32 [M, Is/128]    shared expert mid in E4M3
+ *   sh_xq/sh_xs  u8 [M, H] / fp32 [H/128, M]      shared expert x in E4M3
+ *   sh_hq/sh_hs  u8 [M, Is] / fp32 [Is/128, M]    shared expert mid in E4M3
+ *                                   (scales K-block major: block b of token t
+ *                                   at b * M + t)
  *   sh_y         fp32  [M, H]       shared expert output
  * Offsets of absent parts (no shared expert) are 0. */
 typedef struct {

@@ -15,7 +15,10 @@
 
 namespace qmoe {
 
-// x bf16 [M, H] -> E4M3 [M, H] + fp32 scale per 128; one wave per block.
+// x bf16 [M, H] -> E4M3 [M, H] + fp32 scale per 128, scales stored
+// K-block major ([H/128, M]: a block's scales of consecutive rows are
+// contiguous, so the GEMM reads them with one contiguous load); one wave per
+// block.
 __global__ __launch_bounds__(256) void sh_quant_x_kernel(const uint16_t* __restrict__ x, int M, int H,
                                                          uint8_t* __restrict__ q, float* __restrict__ s) {
   const int lane = threadIdx.x & 63;
@@ -34,12 +37,12 @@ __global__ __launch_bounds__(256) void sh_quant_x_kernel(const uint16_t* __restr
       c1 = e4m3_code(__fdiv_rn(v1, sc));
     }
     *reinterpret_cast<uint16_t*>(q + base) = (uint16_t)(c0 | (c1 << 8));
-    if (lane == 0) s[(size_t)t * nb + b] = sc;
+    if (lane == 0) s[(size_t)b * M + t] = sc;
   }
 }
 
-// out[t, o] = sum_kb a_scale[t, kb] * w_scale[o/128, kb] * (a_kb . w_kb), a
-// [rows, K] E4M3 with fp32 scales per 128 along K, w [N, K] E4M3 with fp32
+// out[t, o] = sum_kb a_scale[kb, t] * w_scale[o/128, kb] * (a_kb . w_kb), a
+// [rows, K] E4M3 with fp32 scales per 128 along K (K-block major), w [N, K] E4M3 with fp32
 // scales per 128x128 block. With GATED the output is SiLU(g) * u, g and u
 // from weight rows o and o + n_out.
 //
@@ -106,7 +109,7 @@ __global__ __launch_bounds__(256) void sh_gemm_kernel(const uint8_t* __restrict_
     pa[q] = a + (size_t)min(row0 + (idx >> 3), rows - 1) * K + 16 * (idx & 7);
     pb[q] = w + (size_t)brow(idx >> 3) * K + 16 * (idx & 7);
   }
-  const float* psa = as + (size_t)min(row0 + (tid & (kShBM - 1)), rows - 1) * nkb;
+  const float* psa = as + min(row0 + (tid & (kShBM - 1)), rows - 1);  // + kb * rows
   const float* pwg = ws + (size_t)(brow(0) / 128) * nkb;
   const float* pwu = ws + (size_t)(brow(127) / 128) * nkb;
   auto load = [&](int kb, ShRegs& R) {
@@ -115,7 +118,7 @@ __global__ __launch_bounds__(256) void sh_gemm_kernel(const uint8_t* __restrict_
       R.a[q] = ld16(pa[q] + 128 * kb);
       R.b[q] = ld16(pb[q] + 128 * kb);
     }
-    R.sa = psa[kb];
+    R.sa = psa[(size_t)kb * rows];
   };
   auto store = [&](const ShRegs& R, int s) {
 #pragma unroll
@@ -206,7 +209,8 @@ __global__ __launch_bounds__(256) void sh_gemm_kernel(const uint8_t* __restrict_
     }
 }
 
-// h fp32 [rows, I] -> E4M3 + fp32 scale per 128 (same rule as the routed mid)
+// h fp32 [rows, I] -> E4M3 + fp32 scale per 128 (same rule as the routed mid),
+// scales K-block major ([I/128, rows])
 __global__ __launch_bounds__(256) void sh_act_quant_kernel(const float* __restrict__ h, int rows, int I,
                                                            uint8_t* __restrict__ q, float* __restrict__ s) {
   const int lane = threadIdx.x & 63;
@@ -224,7 +228,7 @@ __global__ __launch_bounds__(256) void sh_act_quant_kernel(const float* __restri
       c1 = e4m3_code(__fdiv_rn(v.y, sc));
     }
     *reinterpret_cast<uint16_t*>(q + base) = (uint16_t)(c0 | (c1 << 8));
-    if (lane == 0) s[(size_t)row * nb + b] = sc;
+    if (lane == 0) s[(size_t)b * rows + row] = sc;
   }
 }
 

@@ -68,9 +68,9 @@ def read_intermediates(plan, s, M):
     if s.shared_I:
         Is = s.shared_I
         r["sh_xq"] = v("sh_xq", torch.uint8, (M, H))
-        r["sh_xs"] = v("sh_xs", torch.float32, (M, H // 128))
+        r["sh_xs"] = v("sh_xs", torch.float32, (H // 128, M)).t()  # stored K-block major
         r["sh_hq"] = v("sh_hq", torch.uint8, (M, Is))
-        r["sh_hs"] = v("sh_hs", torch.float32, (M, Is // 128))
+        r["sh_hs"] = v("sh_hs", torch.float32, (Is // 128, M)).t()
         r["sh_y"] = v("sh_y", torch.float32, (M, H))
     return {key: t.cpu().numpy() for key, t in r.items()}
 
