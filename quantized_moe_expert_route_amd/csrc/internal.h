@@ -103,7 +103,8 @@ hipError_t launch_act_quant(const moe_plan* p, const CallArgs& a, Ev ev);
 int down_combine_cols(int H, int cus);
 hipError_t launch_down_combine(const moe_plan* p, const CallArgs& a, Ev ev);
 hipError_t launch_shared(const moe_plan* p, const CallArgs& a, Ev ev);
-// large M: LDS-staged 128-row tiles; gate/up includes the mid quantization
+// large M: LDS-staged tiles (kGuRows rows for gate/up, which includes the mid
+// quantization; kBigRows rows for down)
 hipError_t launch_gate_up_big(const moe_plan* p, const CallArgs& a, Ev ev);
 hipError_t launch_down_big(const moe_plan* p, const CallArgs& a, Ev ev);
 hipError_t launch_combine(const moe_plan* p, const CallArgs& a, Ev ev);

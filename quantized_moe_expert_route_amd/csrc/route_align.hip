@@ -37,25 +37,31 @@ __device__ __forceinline__ void load_keys(const float* __restrict__ row, int E, 
   for (int c = 0; c < EC; ++c) key[c] = lane + 64 * c < E ? order_key(row[lane + 64 * c]) : 0u;
 }
 
+// k rounds: the wave's largest key, and of the experts holding it the lowest
+// id 64 c + lane (the first slot c with a hit, then its lowest lane, found
+// with ballots), which leaves the race.
 template <int EC>
 __device__ __forceinline__ void topk_wave(uint32_t (&key)[EC], int k, int lane, uint32_t& sel_e, float& sel_l) {
   for (int j = 0; j < k; ++j) {
-    uint32_t bk = 0, bc = 0;
+    uint32_t bk = 0;
 #pragma unroll
-    for (int c = 0; c < EC; ++c)
-      if (key[c] > bk) {  // strict: the lowest index of equal keys stays
-        bk = key[c];
-        bc = (uint32_t)c;
-      }
+    for (int c = 0; c < EC; ++c) bk = max(bk, key[c]);
     const uint32_t kmax = wave_max_u32(bk);
-    const uint32_t win = wave_min_u32(bk == kmax ? (bc << 6) | (uint32_t)lane : 0xFFFFFFFFu);
-    if ((win & 63u) == (uint32_t)lane) {
-      const uint32_t wc = win >> 6;
+    int wc = EC - 1;
+    unsigned long long hits = 0;
 #pragma unroll
-      for (int c = 0; c < EC; ++c) key[c] = ((uint32_t)c == wc) ? 0u : key[c];
+    for (int c = 0; c < EC; ++c) {
+      hits = __ballot(key[c] == kmax);
+      if (hits) {
+        wc = c;
+        break;
+      }
     }
+    const int wl = __builtin_ctzll(hits);
+#pragma unroll
+    for (int c = 0; c < EC; ++c) key[c] = (lane == wl && c == wc) ? 0u : key[c];
     if (lane == j) {
-      sel_e = win;
+      sel_e = (uint32_t)(64 * wc + wl);
       sel_l = key_to_float(kmax);
     }
   }
@@ -129,16 +135,22 @@ __device__ int block_exclusive_scan(int v, int* s_tmp, int* total) {
   return r;
 }
 
-// Offsets, tiles of kTileRows sorted rows and meta from per-expert counts
-// (thread e holds count c of expert e). Leaves offsets in s_off.
+static_assert(kSmallRows < (1 << 16), "rows and tiles share one packed scan");
+
+// Offsets (and with_tiles: tiles of kTileRows sorted rows, meta[0]) from
+// per-expert counts (thread e holds count c of expert e). Leaves offsets in
+// s_off. Tiles are written only for the small-token path, where the row
+// total is at most kSmallRows: rows and tiles then share one scan, packed as
+// rows | tiles << 16.
 __device__ void write_offsets_tiles(int c, int E, int* s_off, int* s_tmp, int* __restrict__ count,
                                     int* __restrict__ offset, int4* __restrict__ tiles, int* __restrict__ meta,
                                     bool with_tiles = true) {
   const int tid = threadIdx.x;
-  const int nt = (c + kTileRows - 1) / kTileRows;
-  int total_rows, total_tiles;
-  const int off = block_exclusive_scan(c, s_tmp, &total_rows);
-  const int toff = block_exclusive_scan(nt, s_tmp, &total_tiles);
+  const int nt = with_tiles ? (c + kTileRows - 1) / kTileRows : 0;
+  int total;
+  const int pre = block_exclusive_scan(with_tiles ? c | (nt << 16) : c, s_tmp, &total);
+  const int off = with_tiles ? pre & 0xFFFF : pre, toff = pre >> 16;
+  const int total_rows = with_tiles ? total & 0xFFFF : total, total_tiles = total >> 16;
   if (tid < E) {
     count[tid] = c;
     offset[tid] = off;
@@ -150,7 +162,7 @@ __device__ void write_offsets_tiles(int c, int E, int* s_off, int* s_tmp, int* _
   }
   if (tid == 0) {
     offset[E] = total_rows;
-    meta[0] = total_tiles;
+    if (with_tiles) meta[0] = total_tiles;
   }
   __syncthreads();
 }
