@@ -143,11 +143,11 @@ int moe_plan_stage_launches(const moe_plan* plan, int64_t M, int stage) {
   if (M == 0) return 0;
   const bool small = small_path(M, plan->s.top_k);
   switch (stage) {
-    case 0: return 1;                             // route (+ sort + x quantization when small)
+    case 0: return 1;                             // route + x quantization (+ sort when small; + the shared expert's x when large)
     case 1: return small ? 0 : 3;                 // align
     case 2: return 1;                             // gate_up (+ mid quantization when large)
     case 3: return small ? 1 : 0;                 // act_quant
-    case 4: return plan->s.shared_I > 0 ? 4 : 0;  // shared expert
+    case 4: return plan->s.shared_I > 0 ? (small ? 4 : 3) : 0;  // shared expert
     case 5: return 1;                             // down (+ combine when small)
     default: return small ? 0 : 1;                // combine
   }

@@ -306,8 +306,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     double acc[4] = {0, 0, 0, 0};
     for (int j = 0; j < k; ++j) {
       const double wj = (double)w[(size_t)t * k + j];
-      const float4 a = *reinterpret_cast<const float4*>(y + ((size_t)t * k + j) * H + c);
-      acc[0] += wj * (double)a.x; acc[1] += wj * (double)a.y; acc[2] += wj * (double)a.z; acc[3] += wj * (double)a.w;
+      // y is read once: non-temporal loads keep it from displacing cached lines
+      const v4f a = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(y + ((size_t)t * k + j) * H + c));
+      acc[0] += wj * (double)a[0]; acc[1] += wj * (double)a[1]; acc[2] += wj * (double)a[2]; acc[3] += wj * (double)a[3];
     }
     if (ys) {
       const float4 a = *reinterpret_cast<const float4*>(ys + (size_t)t * H + c);

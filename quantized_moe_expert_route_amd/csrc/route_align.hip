@@ -5,8 +5,9 @@
 // top-8 by rounds, each round a wave maximum of the lane heads, a tie going
 // to the lower expert ID. Here a wave routes one token: each round takes the
 // wave maximum of the lanes' best order-preserving logit keys (DPP within
-// rows, scalar reads across rows), then the wave minimum expert ID among the
-// lanes holding that key, so a tie resolves to the lower ID.
+// rows, scalar reads across rows), then the lowest expert ID among the lanes
+// holding that key (ballots over the key slots), so a tie resolves to the
+// lower ID.
 //
 // x -> MXFP4 happens once per token in the same launch (the pages' frontend
 // converts activations next to the route sort: "IQ2R: load GLM-5.3 packed MoE
@@ -220,27 +221,97 @@ __global__ __launch_bounds__(1024) void route_align_small_kernel(
 }
 
 // ---------------------------------------------------------------- M > 64
-template <int EC>
+// x of one token, 8 elements a lane, 512 a load instruction (whole cache
+// lines): the 4 lanes of a 32-block form its E8M0 scale and E2M1 codes (the
+// same arithmetic as quant_block_mx), and with SH the 16 lanes of a
+// 128-block also form the shared expert's E4M3 codes and fp32 scale, so x is
+// read once for both. A unit is kXU loads of one row.
+constexpr int kXU = 4;
+
+template <bool SH>
+__device__ __forceinline__ void quant_x_unit(const uint16_t* __restrict__ x, int H, int M, int t, int c0, int lane,
+                                             uint8_t* __restrict__ xq, uint8_t* __restrict__ xs,
+                                             uint8_t* __restrict__ sq, float* __restrict__ ss) {
+  uint4 v[kXU];
+#pragma unroll
+  for (int i = 0; i < kXU; ++i)
+    v[i] = c0 + 512 * i < H ? ld16(x + (size_t)t * H + c0 + 512 * i + 8 * lane) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < kXU; ++i) {
+    if (c0 + 512 * i >= H) break;  // H is a multiple of 512: a load is all in or all out
+    const int e0 = c0 + 512 * i + 8 * lane;
+    const uint32_t w32[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+    uint32_t am = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) am = max(am, max(w32[q] & 0x7FFFu, (w32[q] >> 16) & 0x7FFFu));
+    // max over the quad (one 32-block)
+    am = max(am, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)am, 0xB1, 0xF, 0xF, false));
+    am = max(am, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)am, 0x4E, 0xF, 0xF, false));
+    {
+      const uint32_t sc = mx_scale_code(am);
+      const int sh = 127 - (int)sc;
+      uint32_t packed = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float f0 = ldexpf(__uint_as_float(w32[q] << 16), sh);
+        const float f1 = ldexpf(__uint_as_float(w32[q] & 0xFFFF0000u), sh);
+        packed |= (e2m1_code(f0) | (e2m1_code(f1) << 4)) << (8 * q);
+      }
+      *reinterpret_cast<uint32_t*>(xq + (size_t)t * (H >> 1) + (e0 >> 1)) = packed;
+      if ((lane & 3) == 0) xs[(size_t)t * (H >> 5) + (e0 >> 5)] = (uint8_t)sc;
+    }
+    if (SH) {
+      // on to the 16 lanes of the 128-block (max is order-free: mirrors suffice)
+      am = max(am, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)am, 0x141, 0xF, 0xF, false));
+      am = max(am, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)am, 0x140, 0xF, 0xF, false));
+      const float sc = __fdiv_rn(__uint_as_float(am << 16), 448.0f);
+      uint32_t lo = 0, hi = 0;
+      if (sc > 0.f) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t c = e4m3_code(__fdiv_rn(__uint_as_float(w32[q] << 16), sc)) |
+                             (e4m3_code(__fdiv_rn(__uint_as_float(w32[q] & 0xFFFF0000u), sc)) << 8);
+          if (q < 2) lo |= c << (16 * q); else hi |= c << (16 * (q - 2));
+        }
+      }
+      *reinterpret_cast<uint2*>(sq + (size_t)t * H + e0) = make_uint2(lo, hi);
+      if ((lane & 15) == 0) ss[(size_t)(e0 >> 7) * M + t] = sc;
+    }
+  }
+}
+
+// Workgroups [0, route_blocks) route, one wave per token (top-k, weights,
+// the token's bits in the expert x token bitmap); the rest quantize x, one
+// wave per unit of kXU loads of a row. The two roles share no registers.
+template <int EC, bool SH>
 __global__ __launch_bounds__(256) void route_kernel(
     const float* __restrict__ logits, const uint16_t* __restrict__ x, int M, int E, int k, int H,
     float scaling, int* __restrict__ topk_ids, float* __restrict__ topk_w,
-    uint32_t* __restrict__ bitmap, int words, uint8_t* __restrict__ xq, uint8_t* __restrict__ xs) {
+    uint32_t* __restrict__ bitmap, int words, uint8_t* __restrict__ xq, uint8_t* __restrict__ xs,
+    uint8_t* __restrict__ sh_xq, float* __restrict__ sh_xs, int route_blocks) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int nblk = H >> 5;
-  for (int t = blockIdx.x * 4 + wave; t < M; t += gridDim.x * 4) {
-    uint32_t sel_e = 0;
-    float sel_l = 0.f;
-    uint32_t key[EC];
-    load_keys<EC>(logits + (size_t)t * E, E, lane, key);
-    topk_wave<EC>(key, k, lane, sel_e, sel_l);
-    const float w = route_weight(sel_l, k, lane, scaling);
-    if (lane < k) {
-      topk_ids[(size_t)t * k + lane] = (int)sel_e;
-      topk_w[(size_t)t * k + lane] = w;
-      atomicOr(&bitmap[(size_t)sel_e * words + (t >> 5)], 1u << (t & 31));
+  if ((int)blockIdx.x < route_blocks) {
+    for (int t = blockIdx.x * 4 + wave; t < M; t += route_blocks * 4) {
+      uint32_t sel_e = 0;
+      float sel_l = 0.f;
+      uint32_t key[EC];
+      load_keys<EC>(logits + (size_t)t * E, E, lane, key);
+      topk_wave<EC>(key, k, lane, sel_e, sel_l);
+      const float w = route_weight(sel_l, k, lane, scaling);
+      if (lane < k) {
+        topk_ids[(size_t)t * k + lane] = (int)sel_e;
+        topk_w[(size_t)t * k + lane] = w;
+        atomicOr(&bitmap[(size_t)sel_e * words + (t >> 5)], 1u << (t & 31));
+      }
     }
-    for (int b = lane; b < nblk; b += 64)
-      quant_block_mx(x + (size_t)t * H + b * 32, xq + (size_t)t * (H >> 1) + b * 16, xs + (size_t)t * nblk + b);
+    return;
+  }
+  const int upr = (H + 512 * kXU - 1) / (512 * kXU);  // units per row
+  const int64_t units = (int64_t)M * upr;
+  const int qb = gridDim.x - route_blocks;
+  for (int64_t u = (int64_t)(blockIdx.x - route_blocks) * 4 + wave; u < units; u += (int64_t)qb * 4) {
+    const int t = (int)(u / upr), c0 = (int)(u - (int64_t)t * upr) * 512 * kXU;
+    quant_x_unit<SH>(x, H, M, t, c0, lane, xq, xs, sh_xq, sh_xs);
   }
 }
 
@@ -404,13 +475,20 @@ hipError_t launch_route_small(const moe_plan* p, const CallArgs& a, Ev ev) {
 
 hipError_t launch_route(const moe_plan* p, const CallArgs& a, Ev ev) {
   const int M = (int)a.M, E = (int)p->s.E, k = (int)p->s.top_k, H = (int)p->s.H;
-  const int blocks = (int)std::min<int64_t>((a.M + 3) / 4, 2048);
+  const int route_blocks = (int)std::min<int64_t>((a.M + 3) / 4, 2048);
+  const int64_t units = a.M * ((H + 512 * kXU - 1) / (512 * kXU));
+  const int blocks = route_blocks + (int)std::min<int64_t>((units + 3) / 4, 2048);
   const int words = (int)((a.M + 31) / 32);
+  // with a shared expert, its E4M3 x comes from the same read of x
+  const bool sh = p->s.shared_I > 0;
+  uint8_t* sh_xq = sh ? wsp<uint8_t>(p, p->L.sh_xq) : nullptr;
+  float* sh_xs = sh ? wsp<float>(p, p->L.sh_xs) : nullptr;
   return by_ec(E, [&](auto ec) {
-    return launch_k(route_kernel<decltype(ec)::value>, dim3(blocks), dim3(256), 0, a.stream, ev, a.logits,
-                    reinterpret_cast<const uint16_t*>(a.x), M, E, k, H, p->s.routed_scaling,
+    constexpr int EC = decltype(ec)::value;
+    return launch_k(sh ? route_kernel<EC, true> : route_kernel<EC, false>, dim3(blocks), dim3(256), 0, a.stream,
+                    ev, a.logits, reinterpret_cast<const uint16_t*>(a.x), M, E, k, H, p->s.routed_scaling,
                     wsp<int>(p, p->L.topk_ids), wsp<float>(p, p->L.topk_w), wsp<uint32_t>(p, p->X.bitmap), words,
-                    wsp<uint8_t>(p, p->L.xq), wsp<uint8_t>(p, p->L.xs));
+                    wsp<uint8_t>(p, p->L.xq), wsp<uint8_t>(p, p->L.xs), sh_xq, sh_xs, route_blocks);
   });
 }
 

@@ -49,14 +49,16 @@ __global__ __launch_bounds__(256) void sh_quant_x_kernel(const uint16_t* __restr
 // Workgroup tile: 128 token rows x 128 weight rows (GATED: 64 gate + the 64
 // matching up rows, 64 outputs; else 128 outputs), one 128-K block per step:
 // both operands staged in LDS as E4M3 through two register-held steps in
-// flight; each wave multiplies 64 rows x 64 weight rows: the E4M3 codes are
+// flight; each of 8 waves multiplies 64 rows x 32 weight rows: the E4M3 codes are
 // widened to bf16 as they are read (exact) and multiplied on the bf16 MFMA
-// (exact products, fp32 sums inside the block), and the block's partial
-// times (activation scale x weight scale) is added into fp32 accumulators.
-// (The FP8 MFMA drops products far below the largest of their 32-group; its
-// error, amplified by the E4M3 requantization of h, exceeded the output
-// tolerance.) E4M3 x E4M3 block sums can need more than binary32's 24 bits,
-// so these outputs are close to, not equal to, the exact ones.
+// (exact products, fp32 sums inside the block); the block's sum times
+// (activation scale x weight scale) is formed and added in float64, in block
+// order, and rounded once to fp32. (The FP8 MFMA drops products far below
+// the largest of their 32-group; its error, amplified by the E4M3
+// requantization of h, exceeded the output tolerance.) The result is the
+// exact one whenever every block sum fits binary32; E4M3 x E4M3 block sums
+// can need more than its 24 bits (a tiny product beside large ones), and
+// then the output is close to, not equal to, the exact one.
 constexpr int kShBM = 128;  // token rows per tile
 constexpr int kShLD = 144;  // LDS bytes per staged 128-byte row (+16 pad)
 
@@ -67,7 +69,7 @@ struct ShSmem {
 };
 
 struct ShRegs {
-  uint4 a[4], b[4];
+  uint4 a[2], b[2];
   float sa;
 };
 
@@ -85,13 +87,15 @@ __device__ __forceinline__ v8s e4m3x8_to_bf16(uint2 w) {
   return r;
 }
 
+constexpr int kShThreads = 512;  // 8 waves: 2 row halves x 4 weight-row quarters
+
 template <bool GATED>
-__global__ __launch_bounds__(256) void sh_gemm_kernel(const uint8_t* __restrict__ a, const float* __restrict__ as,
+__global__ __launch_bounds__(kShThreads) void sh_gemm_kernel(const uint8_t* __restrict__ a, const float* __restrict__ as,
                                                       const uint8_t* __restrict__ w, const float* __restrict__ ws,
                                                       int rows, int K, int n_out, float* __restrict__ out) {
   __shared__ ShSmem sm;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave & 1, wn = wave >> 1;  // wn 0..3
   const int r = lane & 15, g = lane >> 4;
   constexpr int BN = GATED ? 64 : 128;  // outputs per tile
   const int tiles_n = n_out / BN;
@@ -101,11 +105,11 @@ __global__ __launch_bounds__(256) void sh_gemm_kernel(const uint8_t* __restrict_
   auto brow = [&](int rr) { return GATED ? (rr < 64 ? o0 + rr : n_out + o0 + rr - 64) : o0 + rr; };
   // staging: 128-byte rows in 8 chunks of 16; rows past the end read the
   // last row (their results are never written)
-  const uint8_t* pa[4];
-  const uint8_t* pb[4];
+  const uint8_t* pa[2];
+  const uint8_t* pb[2];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int idx = tid + 256 * q;
+  for (int q = 0; q < 2; ++q) {
+    const int idx = tid + kShThreads * q;
     pa[q] = a + (size_t)min(row0 + (idx >> 3), rows - 1) * K + 16 * (idx & 7);
     pb[q] = w + (size_t)brow(idx >> 3) * K + 16 * (idx & 7);
   }
@@ -114,7 +118,7 @@ __global__ __launch_bounds__(256) void sh_gemm_kernel(const uint8_t* __restrict_
   const float* pwu = ws + (size_t)(brow(127) / 128) * nkb;
   auto load = [&](int kb, ShRegs& R) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 2; ++q) {
       R.a[q] = ld16(pa[q] + 128 * kb);
       R.b[q] = ld16(pb[q] + 128 * kb);
     }
@@ -122,56 +126,63 @@ __global__ __launch_bounds__(256) void sh_gemm_kernel(const uint8_t* __restrict_
   };
   auto store = [&](const ShRegs& R, int s) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int idx = tid + 256 * q;
+    for (int q = 0; q < 2; ++q) {
+      const int idx = tid + kShThreads * q;
       *reinterpret_cast<uint4*>(&sm.a[s][(idx >> 3) * kShLD + 16 * (idx & 7)]) = R.a[q];
       *reinterpret_cast<uint4*>(&sm.b[s][(idx >> 3) * kShLD + 16 * (idx & 7)]) = R.b[q];
     }
     if (tid < kShBM) sm.as[s][tid] = R.sa;
   };
-  float acc[4][4][4];
+  double acc[4][2][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) acc[i][j][v] = 0.f;
-  // wave (wm, wn): rows 64 wm .. + 64; weight rows: GATED gate 32 wn + 16 j
-  // (j < 2) and up 64 + 32 wn + 16 (j - 2); else 64 wn + 16 j
-  auto wrow = [&](int j) { return GATED ? (j < 2 ? 32 * wn + 16 * j : 64 + 32 * wn + 16 * (j - 2)) : 64 * wn + 16 * j; };
+      for (int v = 0; v < 4; ++v) acc[i][j][v] = 0.0;
+  // wave (wm, wn): rows 64 wm .. + 64; weight rows: GATED gate 16 wn (j = 0)
+  // and up 64 + 16 wn (j = 1); else 32 wn + 16 j
+  auto wrow = [&](int j) { return GATED ? 64 * j + 16 * wn : 32 * wn + 16 * j; };
   // in bf16 MFMA step q of a 128-block, lane group g supplies K = 32g + 8q .. + 8
   auto compute = [&](int s, int kb) {
     const float swg = pwg[kb], swu = pwu[kb];
-    v4f P[4][4];
+    v4f P[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) P[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < 2; ++j) P[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      v8s fa[4], fb[4];
+      v8s fa[4], fb[2];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         fa[i] = e4m3x8_to_bf16(*reinterpret_cast<const uint2*>(&sm.a[s][(64 * wm + 16 * i + r) * kShLD + 32 * g + 8 * q]));
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
         fb[j] = e4m3x8_to_bf16(*reinterpret_cast<const uint2*>(&sm.b[s][(wrow(j) + r) * kShLD + 32 * g + 8 * q]));
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) P[i][j] = mfma_bf16(fa[i], fb[j], P[i][j]);
+        for (int j = 0; j < 2; ++j) P[i][j] = mfma_bf16(fa[i], fb[j], P[i][j]);
     }
+    // the block sum times (activation scale x weight scale), added in
+    // float64 in block order
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float sa[4];
+      double sg[4], su[4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) sa[v] = sm.as[s][64 * wm + 16 * i + 4 * g + v];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float sw = GATED && j >= 2 ? swu : swg;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[i][j][v] = fmaf(P[i][j][v], sa[v] * sw, acc[i][j][v]);
+      for (int v = 0; v < 4; ++v) {
+        const double sa = (double)sm.as[s][64 * wm + 16 * i + 4 * g + v];
+        sg[v] = sa * (double)swg;  // exact
+        su[v] = sa * (double)swu;
       }
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const double t = (GATED && j == 1 ? su[v] : sg[v]) * (double)P[i][j][v];
+          acc[i][j][v] = __dadd_rn(acc[i][j][v], t);
+        }
     }
   };
   ShRegs S0, S1;
@@ -199,12 +210,10 @@ __global__ __launch_bounds__(256) void sh_gemm_kernel(const uint8_t* __restrict_
       const int m = row0 + 64 * wm + 16 * i + 4 * g + v;
       if (m >= rows) continue;
       if (GATED) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          out[(size_t)m * n_out + o0 + 32 * wn + 16 * j + r] = silu_mul(acc[i][j][v], acc[i][j + 2][v]);
+        out[(size_t)m * n_out + o0 + 16 * wn + r] = silu_mul((float)acc[i][0][v], (float)acc[i][1][v]);
       } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) out[(size_t)m * n_out + o0 + 64 * wn + 16 * j + r] = acc[i][j][v];
+        for (int j = 0; j < 2; ++j) out[(size_t)m * n_out + o0 + 32 * wn + 16 * j + r] = (float)acc[i][j][v];
       }
     }
 }
@@ -236,19 +245,24 @@ hipError_t launch_shared(const moe_plan* p, const CallArgs& a, Ev ev) {
   if (p->s.shared_I == 0) return hipSuccess;
   const int M = (int)a.M, H = (int)p->s.H, Is = (int)p->s.shared_I;
   auto blocks_for = [](int64_t waves, int64_t cap) { return (int)std::min<int64_t>((waves + 3) / 4, cap); };
-  hipError_t e = launch_k(sh_quant_x_kernel, dim3(blocks_for((int64_t)M * (H / 128), 8192)), dim3(256), 0, a.stream,
-                          Ev{ev.start, nullptr}, reinterpret_cast<const uint16_t*>(a.x), M, H,
-                          wsp<uint8_t>(p, p->L.sh_xq), wsp<float>(p, p->L.sh_xs));
+  // above kSmallM the route launch has quantized x for this expert already
+  const bool quant_x = small_path(M, p->s.top_k);
+  hipError_t e = hipSuccess;
+  if (quant_x)
+    e = launch_k(sh_quant_x_kernel, dim3(blocks_for((int64_t)M * (H / 128), 8192)), dim3(256), 0, a.stream,
+                 Ev{ev.start, nullptr}, reinterpret_cast<const uint16_t*>(a.x), M, H, wsp<uint8_t>(p, p->L.sh_xq),
+                 wsp<float>(p, p->L.sh_xs));
   if (e != hipSuccess) return e;
   const int64_t mt = (M + kShBM - 1) / kShBM;
-  e = launch_k(sh_gemm_kernel<true>, dim3((unsigned)(mt * (Is / 64))), dim3(256), 0, a.stream, Ev{},
+  e = launch_k(sh_gemm_kernel<true>, dim3((unsigned)(mt * (Is / 64))), dim3(kShThreads), 0, a.stream,
+               Ev{quant_x ? nullptr : ev.start, nullptr},
                wsp<uint8_t>(p, p->L.sh_xq), wsp<float>(p, p->L.sh_xs), reinterpret_cast<const uint8_t*>(p->ws13),
                p->ss13, M, H, Is, wsp<float>(p, p->X.sh_h));
   if (e != hipSuccess) return e;
   e = launch_k(sh_act_quant_kernel, dim3(blocks_for((int64_t)M * (Is / 128), 8192)), dim3(256), 0, a.stream, Ev{},
                wsp<float>(p, p->X.sh_h), M, Is, wsp<uint8_t>(p, p->L.sh_hq), wsp<float>(p, p->L.sh_hs));
   if (e != hipSuccess) return e;
-  return launch_k(sh_gemm_kernel<false>, dim3((unsigned)(mt * (H / 128))), dim3(256), 0, a.stream,
+  return launch_k(sh_gemm_kernel<false>, dim3((unsigned)(mt * (H / 128))), dim3(kShThreads), 0, a.stream,
                   Ev{nullptr, ev.stop}, wsp<uint8_t>(p, p->L.sh_hq), wsp<float>(p, p->L.sh_hs),
                   reinterpret_cast<const uint8_t*>(p->ws2), p->ss2, M, Is, H, wsp<float>(p, p->L.sh_y));
 }

@@ -77,6 +77,16 @@ def _check_out(gout, rout):
     return ndiff
 
 
+def _check_shared_x(gi, ref, tokens=None):
+    """The shared expert's E4M3 x codes and per-128 scales: bit-exact (the
+    scale and the division deciding each code are binary32 on both sides)."""
+    q, s = gi["sh_xq"], gi["sh_xs"]
+    if tokens is not None:
+        q, s = q[tokens], s[tokens]
+    np.testing.assert_array_equal(q, ref["shared"]["xq8"])
+    np.testing.assert_array_equal(s.view(np.uint32), ref["shared"]["xs8"].view(np.uint32))
+
+
 @pytest.mark.parametrize("name", ["c0", "c1", "c2"])
 def test_stagewise_full(name):
     d = X.make_inputs(name)
@@ -119,6 +129,7 @@ def test_sampled_full_size(name, n_tok):
     ydiff = _check_y(gi["y"][ent], ref["y"])
     print(f"{name}: y differs in {ydiff} of {ref['y'].size} sampled elements")
     if s.shared_I:
+        _check_shared_x(gi, ref, tokens)
         sdiff = int(np.count_nonzero(gi["sh_y"][tokens].view(np.uint32) != ref["ys"].view(np.uint32)))
         print(f"{name}: shared-expert output differs in {sdiff} of {ref['ys'].size}")
     _check_out(gout[tokens], ref["out"])
@@ -141,6 +152,8 @@ SMALL = [
     (96, 512, 64, 384, 8, "ties", 0),
     (70, 512, 4, 128, 2, "normal", 128),       # with the shared expert
     (72, 8192, 8, 128, 2, "normal", 0),        # H past 6144: x scales staged in two parts
+    (80, 1536, 8, 128, 2, "normal", 128),      # shared expert, H = 3 x 512
+    (66, 9216, 4, 128, 2, "normal", 128),      # x rows past 8192: the route reads them in two chunks
 ]
 
 
@@ -153,6 +166,8 @@ def test_small_shapes(M, H, E, I, k, kind, Is):
     _check_routing(gi, ref["ids"], ref["w"], ref["count"], ref["offset"], ref["sorted_entry"])
     _check_xq(gi, ref)
     _check_mid(gi["midq"], gi["mids"], ref["midq"], ref["mids"])
+    if Is:
+        _check_shared_x(gi, ref)
     _check_out(gout, ref["out"])
 
 
