@@ -128,12 +128,37 @@ moe_status moe_plan_set_workspace(moe_plan* plan, void* workspace, size_t bytes,
 moe_status moe_plan_set_shared(moe_plan* plan, const void* ws13, const float* ss13,
                                const void* ws2, const float* ss2);
 
+/* Rewrite the routed experts' gate/up weights into the packed layout that
+ * moe_forward reads, once, when the weights are loaded (the MoE method of
+ * "IQ2R: load GLM-5.3 packed MoE checkpoints with TP slicing", Summary,
+ * allocates packed expert tensors at load time). Inputs, row-major:
+ *   w13  u8 MXFP4 [E, 2I, H/2]   rows [0, I) gate, [I, 2I) up, along H
+ *   s13  u8 E8M0  [E, 2I, H/32]  one scale per 32 elements
+ * Outputs, caller-allocated device buffers of the same sizes:
+ *   w13_packed [E*2I/16][H/128][4][16][16]: bytes 16*g .. 16*g + 15 of
+ *     K-step ks (bytes 64*ks .. 64*ks + 63 of a row) of row 16*rb + r at
+ *     (((rb * H/128 + ks) * 4 + g) * 16 + r) * 16
+ *   s13_packed [E*2I/16][H/512][4][16][4]: byte j of the dword at
+ *     ((rb * H/512 + kq) * 4 + g) * 16 + r holds the scale of MX block
+ *     16*kq + 4*j + g of row 16*rb + r
+ * (rb runs over the E*2I/16 blocks of 16 rows, experts one after another).
+ * A byte permutation: nothing is rounded. All four pointers on one device,
+ * 16-byte aligned, outputs not overlapping each other or the inputs.
+ * Enqueued on `stream`; nothing is allocated. MOE_ERR_INVALID_ARG for null,
+ * misaligned or overlapping pointers or non-positive sizes;
+ * MOE_ERR_UNSUPPORTED for the shapes moe_plan_create rejects (H % 512 != 0,
+ * H > 65536, I not in {128, 256, 384, 512}, E > 1024); MOE_ERR_DEVICE for
+ * host pointers or pointers on different devices. */
+moe_status moe_pack_w13(const void* w13, const void* s13, int64_t E, int64_t I, int64_t H,
+                        void* w13_packed, void* s13_packed, void* stream);
+
 /* The routed-MoE call on M tokens (0 <= M <= shape.M; M = 0 enqueues nothing):
  *   x      bf16 [M, H]
  *   logits fp32 [M, E]     (finite or -inf)
- *   w13    u8 MXFP4 [E, 2I, H/2]   rows [0, I) gate, [I, 2I) up, along H
- *   s13    u8 E8M0  [E, 2I, H/32]
- *   w2     u8 MXFP4 [E, H, I/2]    along I
+ *   w13    gate/up weights in the packed layout of moe_pack_w13 (the
+ *          MXFP4 [E, 2I, H/2] rows [0, I) gate, [I, 2I) up, along H)
+ *   s13    their E8M0 scales, packed by moe_pack_w13 ([E, 2I, H/32])
+ *   w2     u8 MXFP4 [E, H, I/2]    along I, row-major
  *   s2     u8 E8M0  [E, H, I/32]
  *   out    bf16 [M, H]  fully overwritten; must not alias any input
  * Returns after enqueueing; faults inside kernels surface at the caller's

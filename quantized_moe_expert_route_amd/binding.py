@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
     L.moe_plan_stage_launches.argtypes = [vp, i64, ctypes.c_int]
     L.moe_forward.restype = st
     L.moe_forward.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.moe_pack_w13.restype = st
+    L.moe_pack_w13.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp]
     _lib = L
     return L
 
@@ -108,6 +110,25 @@ def _stream(stream) -> Optional[int]:
     if stream is None:
         stream = torch.cuda.current_stream()
     return stream.cuda_stream
+
+
+def pack_w13(w13, s13, out=None, stream=None):
+    """Gate/up weights and scales (row-major MXFP4 [E, 2I, H/2] and E8M0
+    [E, 2I, H/32], uint8 device tensors) -> (w13_packed, s13_packed) in the
+    layout moe_forward reads (moe_pack_w13). Enqueued on `stream`; `out`
+    may give the two destination tensors, else they are allocated here."""
+    import torch
+
+    E, R, Hh = w13.shape
+    if R % 2 or tuple(s13.shape) != (E, R, Hh // 16):
+        raise ValueError("w13 must be [E, 2I, H/2] and s13 [E, 2I, H/32]")
+    if out is None:
+        out = (torch.empty_like(w13), torch.empty_like(s13))
+    wp, sp = out
+    st = lib().moe_pack_w13(_ptr(w13), _ptr(s13), E, R // 2, 2 * Hh, _ptr(wp), _ptr(sp), _stream(stream))
+    if st != MOE_OK:
+        raise MoeError(st, "moe_pack_w13")
+    return wp, sp
 
 
 class Plan:

@@ -259,6 +259,29 @@ moe_status moe_plan_set_call_events(moe_plan* plan, void* start, void* stop) {
   return MOE_OK;
 }
 
+moe_status moe_pack_w13(const void* w13, const void* s13, int64_t E, int64_t I, int64_t H, void* w13_packed,
+                        void* s13_packed, void* stream) {
+  if (!w13 || !s13 || !w13_packed || !s13_packed) return MOE_ERR_INVALID_ARG;
+  if (E <= 0 || I <= 0 || H <= 0) return MOE_ERR_INVALID_ARG;
+  if (H % 512 != 0 || I % 128 != 0 || I > 512 || E > 1024 || H > 65536) return MOE_ERR_UNSUPPORTED;
+  const void* ptrs[4] = {w13, s13, w13_packed, s13_packed};
+  for (const void* q : ptrs)
+    if (!aligned16(q)) return MOE_ERR_INVALID_ARG;
+  const size_t wb = (size_t)E * 2 * I * (H / 2), sb = (size_t)E * 2 * I * (H / 32);
+  if (overlaps(w13_packed, wb, w13, wb) || overlaps(w13_packed, wb, s13, sb) || overlaps(s13_packed, sb, w13, wb) ||
+      overlaps(s13_packed, sb, s13, sb) || overlaps(w13_packed, wb, s13_packed, sb))
+    return MOE_ERR_INVALID_ARG;
+  const int dev = ptr_device(w13);
+  if (dev < 0) return MOE_ERR_DEVICE;
+  for (const void* q : ptrs)
+    if (ptr_device(q) != dev) return MOE_ERR_DEVICE;
+  DeviceGuard guard(dev);
+  if (!guard.ok) return MOE_ERR_DEVICE;
+  return launch_pack_w13(w13, s13, E, I, H, w13_packed, s13_packed, (hipStream_t)stream) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_HIP;
+}
+
 moe_status moe_forward(moe_plan* plan, int64_t M, const void* x, const float* logits, const void* w13,
                        const void* s13, const void* w2, const void* s2, void* out, void* stream) {
   if (!plan) return MOE_ERR_INVALID_ARG;

@@ -9,12 +9,13 @@
 //
 // Work item = (tile of up to 16 sorted rows of one expert, 16 columns of I).
 // A workgroup of 4 waves computes the gate and the up columns of the item,
-// each wave a quarter of the K super-steps; the four partial sums are added
-// in wave order through LDS. Within a 512-element super-step, lane group g
-// (lanes 16g..16g+15) loads 64 contiguous bytes of its row: the MX blocks
-// 4g..4g+3, fed to four MFMAs as block 4g+j in step j. A and B use the same
-// assignment, so every MFMA pairs matching K, and each lane's one scale byte
-// per step covers exactly its 32 elements.
+// each wave a quarter of the K super-steps (4 K-steps of 128); the four
+// partial sums are added in wave order through LDS. In K-step ks lane
+// 16 g + r supplies row r's MX block 4 ks + g (16 bytes and one scale byte),
+// for x and for the weights alike, so every MFMA pairs matching K. The
+// weights come packed (moe_pack_w13): a K-step of the item's 16 gate (or up)
+// rows is 1 KB contiguous in lane order, and a row block's scales of a
+// super-step are one dword per lane.
 #include "common.h"
 #include "internal.h"
 
@@ -46,8 +47,8 @@ __device__ __forceinline__ void quant_mid_rows(const float* __restrict__ h, int 
 }
 
 __global__ __launch_bounds__(256) void gate_up_m16_kernel(
-    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const uint8_t* __restrict__ w13,
-    const uint8_t* __restrict__ s13, const int* __restrict__ sorted_entry,
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const uint8_t* __restrict__ w13p,
+    const uint8_t* __restrict__ s13p, const int* __restrict__ sorted_entry,
     const int4* __restrict__ tiles, const int* __restrict__ meta, float* __restrict__ hout, int H,
     int I, int k) {
   __shared__ v4f red[2][4][64];
@@ -56,50 +57,50 @@ __global__ __launch_bounds__(256) void gate_up_m16_kernel(
   const int n_it = I / 16;
   const int n_work = meta[0] * n_it;
   const size_t Hb = (size_t)H / 2, Hs = (size_t)H / 32;
-  const int nss = H / 512;
+  const int nss = H / 512, nks = H / 128;
+  const size_t nrb = (size_t)I / 8;  // 16-row blocks of an expert's 2I rows
   for (int w = blockIdx.x; w < n_work; w += gridDim.x) {
     const int4 tl = tiles[w / n_it];
     const int it = w % n_it;
     const int e = tl.x, r0 = tl.y, r1 = tl.z;
     const bool rv = r0 + r < r1;
     const int tok = rv ? sorted_entry[r0 + r] / k : 0;
-    const uint8_t* pa = xq + (size_t)tok * Hb;
-    const uint8_t* psa = xs + (size_t)tok * Hs;
-    const size_t grow = (size_t)e * 2 * I + (size_t)it * 16 + r;
-    const uint8_t* pg = w13 + grow * Hb;
-    const uint8_t* psg = s13 + grow * Hs;
-    const uint8_t* pu = pg + (size_t)I * Hb;
-    const uint8_t* psu = psg + (size_t)I * Hs;
+    const uint8_t* pa = xq + (size_t)tok * Hb + 16 * g;  // + 64 ks
+    const uint8_t* psa = xs + (size_t)tok * Hs;          // + 16 ss: byte 4 j + g is K-step 4 ss + j
+    const size_t rbg = (size_t)e * nrb + it, rbu = rbg + I / 16;
+    const uint8_t* pg = w13p + rbg * nks * 1024 + 16 * lane;  // + 1024 ks
+    const uint8_t* pu = w13p + rbu * nks * 1024 + 16 * lane;
+    const uint8_t* psg = s13p + rbg * nss * 256 + 4 * lane;  // + 256 ss: byte j is K-step 4 ss + j
+    const uint8_t* psu = s13p + rbu * nss * 256 + 4 * lane;
     v4f accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
     // wave w owns the contiguous super-steps [w*per, (w+1)*per); all loads of
     // up to kSS of them are in flight before the first MFMA
     const int per = (nss + 3) / 4;
     const int ss_end = min(nss, (wave + 1) * per);
     for (int ss0 = wave * per; ss0 < ss_end; ss0 += kSS) {
-      uint4 a[kSS][4], bg[kSS][4], bu[kSS][4];
-      uint32_t sa[kSS], sg[kSS], su[kSS];
+      uint4 a[kSS][4], bg[kSS][4], bu[kSS][4], sa[kSS];
+      uint32_t sg[kSS], su[kSS];
 #pragma unroll
       for (int q = 0; q < kSS; ++q) {
         const int ss = min(ss0 + q, ss_end - 1);  // clamped: a duplicate step is loaded but not used
-        const int boff = ss * 256 + g * 64;
-        const int soff = ss * 16 + g * 4;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          bg[q][j] = ld16(pg + boff + 16 * j);
-          bu[q][j] = ld16(pu + boff + 16 * j);
+          bg[q][j] = ld16(pg + (size_t)(4 * ss + j) * 1024);
+          bu[q][j] = ld16(pu + (size_t)(4 * ss + j) * 1024);
         }
-        sg[q] = ld4(psg + soff);
-        su[q] = ld4(psu + soff);
+        sg[q] = ld4(psg + 256 * ss);
+        su[q] = ld4(psu + 256 * ss);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) a[q][j] = rv ? ld16(pa + boff + 16 * j) : make_uint4(0, 0, 0, 0);
-        sa[q] = rv ? ld4(psa + soff) : 0x7F7F7F7Fu;
+        for (int j = 0; j < 4; ++j) a[q][j] = rv ? ld16(pa + (4 * ss + j) * 64) : make_uint4(0, 0, 0, 0);
+        sa[q] = rv ? ld16(psa + 16 * ss) : make_uint4(0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu);
       }
 #pragma unroll
       for (int q = 0; q < kSS; ++q) {
         if (ss0 + q < ss_end) {
+          const uint32_t xw[4] = {sa[q].x, sa[q].y, sa[q].z, sa[q].w};
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const uint32_t xa = (sa[q] >> (8 * j)) & 0xFFu;
+            const uint32_t xa = (xw[j] >> (8 * g)) & 0xFFu;
             accg = mfma_fp4(a[q][j], bg[q][j], accg, xa, (sg[q] >> (8 * j)) & 0xFFu);
             accu = mfma_fp4(a[q][j], bu[q][j], accu, xa, (su[q] >> (8 * j)) & 0xFFu);
           }

@@ -35,16 +35,20 @@ __device__ __forceinline__ void xcd_run(int n_items, int& first, int& stride, in
 }
 
 // LDS layout of a K-step slice: 64-byte rows, and 16-byte chunk c of row R
-// at R * 64 + 16 * (c ^ ((R >> 1) & 3)). With it both the staging stores
-// (four lanes per row) and the fragment reads (sixteen rows, one chunk) hit
-// no LDS bank twice (measured with the bank-conflict counter; rows padded to
-// 80 bytes cost 4 conflict cycles per read and 8 per store).
+// at R * 64 + 16 * (c ^ ((R >> 2) & 3)). A 16-byte access of 16 lanes is
+// served by the 64 banks (256 bytes) together; here both the staging stores
+// of x (four lanes per row) and of the packed weights (sixteen rows, one
+// chunk) and the fragment reads (sixteen rows, one chunk) put 16 lanes on 16
+// different 16-byte bank groups: rows R and R + 4 k differ in the XOR, rows
+// within 4 in the bank group of R * 64. (XOR with (R >> 1) & 3, which
+// separates only 8 rows, stalled the kernel about half its time on bank
+// conflicts.)
 __device__ __forceinline__ int opaque_zero() {
   int z;
   asm volatile("v_mov_b32 %0, 0" : "=v"(z));
   return z;
 }
-__device__ __forceinline__ int sw64(int row, int chunk) { return row * 64 + 16 * (chunk ^ ((row >> 1) & 3)); }
+__device__ __forceinline__ int sw64(int row, int chunk) { return row * 64 + 16 * (chunk ^ ((row >> 2) & 3)); }
 constexpr int kGuStages = 2;  // K-steps of gate/up loads held in registers
 
 // Item = (expert, kGuRows sorted rows, one 128-column mid block): the 256
@@ -64,11 +68,11 @@ constexpr int kGuR = kGuRows;
 constexpr int kGuXsSteps = 48;  // K-steps of x scales staged at a time (all of them up to H = 6144)
 constexpr int kGuXsLd = 13;     // 16-byte chunks per staged x-scale row (12 used; 13 keeps reads conflict-free)
 
-struct GuSmem {
+struct alignas(16) GuSmem {  // 16-byte aligned: staging and fragment accesses compile to single b128 LDS ops
   uint8_t a[2][kGuR * 64];      // x rows (MXFP4), K-step slice (sw64 layout)
   uint8_t b[2][256 * 64];       // 128 gate + 128 up weight rows
   uint32_t xs[kGuR][4 * kGuXsLd];  // x scales of kGuXsSteps K-steps, 4 E8M0 bytes per K-step
-  uint32_t bs[2][256][4];       // weight scales of a 512-wide stage (by stage parity)
+  uint32_t bs[2][256][4];       // weight scales of a 512-wide stage (by stage parity): [row][group g], byte j = K-step j
 };
 
 // One K-step of global data held in registers: 1 + 4 16-byte chunks and a
@@ -110,46 +114,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
     const int tok0 = tok[0];
     const int ta = tok[tid >> 2];
     const uint8_t* pa = xq + (size_t)(ta >= 0 ? ta : tok0) * Hb + 16 * (tid & 3);
-    // The expert's weights and their scales are read through buffer
-    // descriptors (base and size in scalar registers, a 32-bit offset per
-    // lane), which keeps the per-thread addresses out of vector registers.
-    // Staged weight row (tid >> 2) + 64 q: gate rows for q < 2, up rows for
-    // q >= 2; the row offsets per q are the same for every thread.
+    // The expert's packed weights (moe_pack_w13) and their scales are read
+    // through buffer descriptors (base and size in scalar registers, a
+    // 32-bit offset per lane), which keeps the per-thread addresses out of
+    // vector registers. A K-step of a 16-row block is 1 KB in MFMA lane
+    // order: wave w's load q covers row block 4 q + w of the item's 16 (gate
+    // blocks for q < 2, up blocks for q >= 2), lane l holding row l & 15,
+    // chunk l >> 4. An expert's packed bytes start where its rows did.
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(w13 + (size_t)e * 2 * I * Hb), (short)0, (int)(2 * I * Hb), 0x00020000);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(s13 + (size_t)e * 2 * I * Hs), (short)0, (int)(2 * I * Hs), 0x00020000);
-    const int ob = (128 * ib + (tid >> 2)) * (int)Hb + 16 * (tid & 3);
-    const int boff[4] = {0, 64 * (int)Hb, (I - 128 + 128) * (int)Hb, (I - 128 + 192) * (int)Hb};
-    // weight-scale quarter q of a stage for this lane: local row
-    // (gate 0..127, up 128..255) and the E8M0 dword lane & 3 of it
-    auto sq_row = [&](int q) { return (q < 2 ? 32 * wn + 16 * q : 128 + 32 * wn + 16 * (q - 2)) + (lane >> 2); };
-    auto sq_off = [&](int q) {
-      const int lr = sq_row(q);
-      return (lr < 128 ? 128 * ib + lr : I + 128 * ib + lr - 128) * (int)Hs + 4 * (lane & 3);
-    };
+    // a 16-row block's K-steps take 16 * Hb bytes; row block b of the expert starts at 16 b Hb
+    const int ob = (128 * ib + 16 * wave) * (int)Hb + 16 * (tid & 63);
+    const int boff[4] = {0, 64 * (int)Hb, I * (int)Hb, (I + 64) * (int)Hb};
     const int ns = nk / 4;  // 512-wide stages
+    // weight-scale quarter q of a stage for this wave: its local row block
+    // (gate 0..7, up 8..15); lane l holds the stage's four K-steps of row
+    // l & 15, MX block group l >> 4 (one dword, 256 contiguous bytes a block)
+    auto sq_blk = [&](int q) { return q < 2 ? 2 * wn + q : 8 + 2 * wn + (q - 2); };
+    auto sq_off = [&](int q) {
+      const int lb = sq_blk(q);
+      const int rb = lb < 8 ? 8 * ib + lb : I / 16 + 8 * ib + lb - 8;
+      return rb * ns * 256 + 4 * lane;
+    };
     auto load = [&](int kk, GuRegs& R) {
       R.a = ld16(pa + kk * 64);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         typedef unsigned v4u __attribute__((ext_vector_type(4)));
-        const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rw, ob, boff[q] + kk * 64, 0);
+        const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rw, ob, boff[q] + kk * 1024, 0);
         R.b[q] = make_uint4(v.x, v.y, v.z, v.w);
       }
       // quarter kk % 4 of stage kk / 4 + 1 (past the last stage: the last one again, unread)
-      R.sb = __builtin_amdgcn_raw_buffer_load_b32(rs, sq_off(kk & 3), 16 * min(kk / 4 + 1, ns - 1), 0);
+      R.sb = __builtin_amdgcn_raw_buffer_load_b32(rs, sq_off(kk & 3), 256 * min(kk / 4 + 1, ns - 1), 0);
     };
     // R holds K-step kk's data (to buffer kk & 1) and a scale quarter
     auto store = [&](const GuRegs& R, int kk) {
       const int s = kk & 1;
       *reinterpret_cast<uint4*>(&sm.a[s][sw64(tid >> 2, tid & 3)]) = R.a;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int idx = tid + 256 * q;
-        *reinterpret_cast<uint4*>(&sm.b[s][sw64(idx >> 2, idx & 3)]) = R.b[q];
-      }
-      sm.bs[(kk / 4 + 1) & 1][sq_row(kk & 3)][lane & 3] = R.sb;
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<uint4*>(&sm.b[s][sw64(64 * q + 16 * wave + (lane & 15), lane >> 4)]) = R.b[q];
+      sm.bs[(kk / 4 + 1) & 1][16 * sq_blk(kk & 3) + (lane & 15)][lane >> 4] = R.sb;
     };
     v4f accg[4][2], accu[4][2];
 #pragma unroll
@@ -174,8 +181,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
         const int col = 32 * wn + 16 * j + r;
         const uint4 fg = *reinterpret_cast<const uint4*>(&sm.b[s][sw64(col, g)]);
         const uint4 fu = *reinterpret_cast<const uint4*>(&sm.b[s][sw64(col + 128, g)]);
-        const uint32_t sg = (sm.bs[ss][col][q4] >> (8 * g)) & 0xFFu;
-        const uint32_t su = (sm.bs[ss][col + 128][q4] >> (8 * g)) & 0xFFu;
+        const uint32_t sg = (sm.bs[ss][col][g] >> (8 * q4)) & 0xFFu;
+        const uint32_t su = (sm.bs[ss][col + 128][g] >> (8 * q4)) & 0xFFu;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           accg[i][j] = mfma_fp4(fa[i], fg, accg[i][j], sa[i], sg);
@@ -203,7 +210,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
     stage_xs(0);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      sm.bs[0][sq_row(q)][lane & 3] = __builtin_amdgcn_raw_buffer_load_b32(rs, sq_off(q), 0, 0);
+      sm.bs[0][16 * sq_blk(q) + (lane & 15)][lane >> 4] = __builtin_amdgcn_raw_buffer_load_b32(rs, sq_off(q), 0, 0);
     GuRegs S[kGuStages];
 #pragma unroll
     for (int q = 0; q < kGuStages; ++q) load(min(q, nk - 1), S[q]);

@@ -93,6 +93,9 @@ template <typename T>
 inline T* wsp(const moe_plan* p, size_t off) { return reinterpret_cast<T*>(p->ws + off); }
 
 hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t s);
+// row-major MXFP4 gate/up weights and scales -> the packed layout (pack.hip)
+hipError_t launch_pack_w13(const void* w13, const void* s13, int64_t E, int64_t I, int64_t H, void* w13p, void* s13p,
+                           hipStream_t stream);
 // Small M (<= kSmallM): route + sort + x quantization in one workgroup.
 hipError_t launch_route_small(const moe_plan* p, const CallArgs& a, Ev ev);
 hipError_t launch_route(const moe_plan* p, const CallArgs& a, Ev ev);

@@ -60,11 +60,16 @@ __global__ __launch_bounds__(256) void sh_quant_x_kernel(const uint16_t* __restr
 // can need more than its 24 bits (a tiny product beside large ones), and
 // then the output is close to, not equal to, the exact one.
 constexpr int kShBM = 128;  // token rows per tile
-constexpr int kShLD = 144;  // LDS bytes per staged 128-byte row (+16 pad)
+// Staged 128-byte rows, 16-byte chunk c of row R at R * 128 + 16 * (c ^ ((R >> 1) & 7)):
+// a 16-byte access of 16 lanes is served by the 64 banks together, and both
+// the staging stores (8 lanes a row, two rows) and the fragment reads (16
+// rows, one chunk) then meet 16 different 16-byte bank groups. (Rows padded
+// to 144 bytes, read 8 bytes a lane, stalled on 2-way conflicts.)
+__device__ __forceinline__ int sw128(int row, int chunk) { return row * 128 + 16 * (chunk ^ ((row >> 1) & 7)); }
 
-struct ShSmem {
-  uint8_t a[2][kShBM * kShLD];
-  uint8_t b[2][128 * kShLD];
+struct alignas(16) ShSmem {  // 16-byte aligned: staging and fragment accesses compile to single b128 LDS ops
+  uint8_t a[2][kShBM * 128];
+  uint8_t b[2][128 * 128];
   float as[2][kShBM];
 };
 
@@ -128,8 +133,8 @@ __global__ __launch_bounds__(kShThreads) void sh_gemm_kernel(const uint8_t* __re
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int idx = tid + kShThreads * q;
-      *reinterpret_cast<uint4*>(&sm.a[s][(idx >> 3) * kShLD + 16 * (idx & 7)]) = R.a[q];
-      *reinterpret_cast<uint4*>(&sm.b[s][(idx >> 3) * kShLD + 16 * (idx & 7)]) = R.b[q];
+      *reinterpret_cast<uint4*>(&sm.a[s][sw128(idx >> 3, idx & 7)]) = R.a[q];
+      *reinterpret_cast<uint4*>(&sm.b[s][sw128(idx >> 3, idx & 7)]) = R.b[q];
     }
     if (tid < kShBM) sm.as[s][tid] = R.sa;
   };
@@ -151,19 +156,26 @@ __global__ __launch_bounds__(kShThreads) void sh_gemm_kernel(const uint8_t* __re
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) P[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    // one 16-byte read (chunk 2 g + p) feeds MFMA steps q = 2 p and 2 p + 1
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      v8s fa[4], fb[2];
+    for (int p = 0; p < 2; ++p) {
+      uint4 ra[4], rb[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        fa[i] = e4m3x8_to_bf16(*reinterpret_cast<const uint2*>(&sm.a[s][(64 * wm + 16 * i + r) * kShLD + 32 * g + 8 * q]));
+      for (int i = 0; i < 4; ++i) ra[i] = *reinterpret_cast<const uint4*>(&sm.a[s][sw128(64 * wm + 16 * i + r, 2 * g + p)]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        fb[j] = e4m3x8_to_bf16(*reinterpret_cast<const uint2*>(&sm.b[s][(wrow(j) + r) * kShLD + 32 * g + 8 * q]));
+      for (int j = 0; j < 2; ++j) rb[j] = *reinterpret_cast<const uint4*>(&sm.b[s][sw128(wrow(j) + r, 2 * g + p)]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int h = 0; h < 2; ++h) {
+        v8s fa[4], fb[2];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) P[i][j] = mfma_bf16(fa[i], fb[j], P[i][j]);
+        for (int i = 0; i < 4; ++i) fa[i] = e4m3x8_to_bf16(h ? make_uint2(ra[i].z, ra[i].w) : make_uint2(ra[i].x, ra[i].y));
+#pragma unroll
+        for (int j = 0; j < 2; ++j) fb[j] = e4m3x8_to_bf16(h ? make_uint2(rb[j].z, rb[j].w) : make_uint2(rb[j].x, rb[j].y));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) P[i][j] = mfma_bf16(fa[i], fb[j], P[i][j]);
+      }
     }
     // the block sum times (activation scale x weight scale), added in
     // float64 in block order

@@ -17,6 +17,11 @@ def upload(d):
     g = {k: torch.from_numpy(np.ascontiguousarray(d[k])).to(dev)
          for k in ("logits", "w13", "s13", "w2", "s2") if k in d}
     g["x"] = torch.from_numpy(np.ascontiguousarray(d["x"]).view(np.int16)).to(dev)
+    if "w13" in g:
+        from quantized_moe_expert_route_amd.binding import pack_w13
+
+        # the call reads gate/up weights in the library's packed layout
+        g["w13"], g["s13"] = pack_w13(g["w13"], g["s13"])
     if d["shape"].shared_I:
         for k in ("ws13", "ss13", "ws2", "ss2"):
             g[k] = torch.from_numpy(np.ascontiguousarray(d[k])).to(dev)

@@ -87,6 +87,20 @@ def test_null_and_unbound_arguments_fail_before_any_device_work():
     L.moe_plan_destroy(None)
 
 
+def test_pack_w13_validates_before_any_device_work():
+    L = B.lib()
+    a, b, c, d = 0x10000, 0x20000, 0x30000, 0x40000  # never dereferenced: every case fails first
+    assert L.moe_pack_w13(None, b, 4, 128, 512, c, d, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_w13(a, b, 4, 128, 512, None, d, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_w13(a, b, 0, 128, 512, c, d, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_w13(a, b, 4, 128, 640, c, d, None) == B.MOE_ERR_UNSUPPORTED   # H % 512
+    assert L.moe_pack_w13(a, b, 4, 192, 512, c, d, None) == B.MOE_ERR_UNSUPPORTED   # I % 128
+    assert L.moe_pack_w13(a, b, 2048, 128, 512, c, d, None) == B.MOE_ERR_UNSUPPORTED
+    assert L.moe_pack_w13(a + 8, b, 4, 128, 512, c, d, None) == B.MOE_ERR_INVALID_ARG  # misaligned
+    # the packed weights would overlap the input
+    assert L.moe_pack_w13(a, b, 4, 128, 512, a + 256, d, None) == B.MOE_ERR_INVALID_ARG
+
+
 def test_plan_needs_a_gfx950_device():
     import torch
 
@@ -96,3 +110,5 @@ def test_plan_needs_a_gfx950_device():
     out = ctypes.c_void_p()
     assert B.lib().moe_plan_create(ctypes.byref(s), ctypes.byref(out)) == B.MOE_ERR_DEVICE
     assert not out.value
+    # host addresses are not device memory
+    assert B.lib().moe_pack_w13(0x10000, 0x80000, 4, 128, 512, 0x100000, 0x180000, None) == B.MOE_ERR_DEVICE

@@ -1,0 +1,54 @@
+"""The one-time packing of the gate/up weights (moe_pack_w13) on the GPU:
+the packed bytes are the documented permutation of the row-major inputs,
+written out here with numpy reshapes, and nothing else."""
+
+import numpy as np
+import pytest
+
+
+def expected_packed(w13, s13):
+    """w13 [E, 2I, H/2] -> [E*2I/16][H/128][4 g][16 r][16 B];
+    s13 [E, 2I, H/32] -> [E*2I/16][H/512][4 g][16 r][4 j], byte j of (g, r)
+    being MX block 16 kq + 4 j + g of the row."""
+    E, R, Hb = w13.shape
+    nrb, nks, nkq = E * R // 16, Hb // 64, Hb // 256
+    wp = w13.reshape(nrb, 16, nks, 4, 16).transpose(0, 2, 3, 1, 4)
+    sp = s13.reshape(nrb, 16, nkq, 4, 4).transpose(0, 2, 4, 1, 3)
+    return np.ascontiguousarray(wp).ravel(), np.ascontiguousarray(sp).ravel()
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("E,I,H", [(3, 128, 512), (2, 384, 1536), (5, 256, 1024)])
+def test_pack_w13_is_the_documented_permutation(E, I, H):
+    import torch
+
+    from quantized_moe_expert_route_amd.binding import pack_w13
+
+    rng = np.random.default_rng(E * 1000 + I + H)
+    w13 = rng.integers(0, 256, (E, 2 * I, H // 2), dtype=np.uint8)
+    s13 = rng.integers(0, 256, (E, 2 * I, H // 32), dtype=np.uint8)
+    dev = torch.device("cuda", 0)
+    wt, st = torch.from_numpy(w13).to(dev), torch.from_numpy(s13).to(dev)
+    wp, sp = pack_w13(wt, st)
+    torch.cuda.synchronize()
+    ew, es = expected_packed(w13, s13)
+    np.testing.assert_array_equal(wp.cpu().numpy().ravel(), ew)
+    np.testing.assert_array_equal(sp.cpu().numpy().ravel(), es)
+    # the inputs are left as they were
+    np.testing.assert_array_equal(wt.cpu().numpy(), w13)
+    np.testing.assert_array_equal(st.cpu().numpy(), s13)
+
+
+def test_expected_layout_places_a_known_byte():
+    """The numpy statement of the layout, checked on single marked bytes."""
+    E, I, H = 2, 128, 1024
+    w13 = np.zeros((E, 2 * I, H // 2), np.uint8)
+    s13 = np.zeros((E, 2 * I, H // 32), np.uint8)
+    e, row, ks, g, b = 1, 37, 5, 2, 9      # byte 64 ks + 16 g + b of the row
+    w13[e, row, 64 * ks + 16 * g + b] = 7
+    kq, j, gs = 1, 3, 1                    # MX block 16 kq + 4 j + gs
+    s13[e, row, 16 * kq + 4 * j + gs] = 9
+    ew, es = expected_packed(w13, s13)
+    rb, r = (e * 2 * I + row) // 16, row % 16
+    assert ew[(((rb * (H // 128) + ks) * 4 + g) * 16 + r) * 16 + b] == 7 and ew.sum() == 7
+    assert es[(((rb * (H // 512) + kq) * 4 + gs) * 16 + r) * 4 + j] == 9 and es.sum() == 9
