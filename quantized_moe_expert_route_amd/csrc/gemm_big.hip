@@ -1,10 +1,10 @@
-// Large-token gate/up and down grouped GEMMs: LDS-staged 128-row tiles.
+// Large-token gate/up and down grouped GEMMs (tiles of 64 and 32 sorted rows).
 //
 // gate/up (scaled FP4 MFMA, "IQ2R: load GLM-5.3 packed MoE checkpoints
 // ...", Summary: SiLU activation; the pages' MXFP4 A4W4 arm) with SiLU(gate) *
 // up and the per-128 E4M3 mid quantization ("glm53: FP8 mid hand-off ...",
 // Modifications row "mid as FP8 once") done inside the workgroup: a work item
-// is (expert, 128 sorted rows, one 128-column mid block), so the 256 weight
+// is (expert, 64 sorted rows, one 128-column mid block), so the 256 weight
 // rows it reads (128 gate + 128 up) cover exactly the columns one mid block
 // needs and no other workgroup is involved.
 //
@@ -49,38 +49,27 @@ __device__ __forceinline__ int opaque_zero() {
   return z;
 }
 __device__ __forceinline__ int sw64(int row, int chunk) { return row * 64 + 16 * (chunk ^ ((row >> 2) & 3)); }
-constexpr int kGuStages = 2;  // K-steps of gate/up loads held in registers
 
 // Item = (expert, kGuRows sorted rows, one 128-column mid block): the 256
 // weight rows it reads (128 gate + 128 up) cover exactly the columns one mid
 // block needs. A 64-row tile keeps a wave's registers within 256 so that two
-// workgroups share a CU: one's MFMAs run while the other stages its next
-// K-step and waits at its barrier (with one workgroup per CU those phases
-// ran one after another).
+// workgroups share a CU: one's MFMAs run while the other waits at its
+// barrier.
 constexpr int kGuR = kGuRows;
 
-// Scales: a load whose lanes read 4 bytes from each of 64 rows costs the
+// x scales: a load whose lanes read 4 bytes from each of 64 rows costs the
 // memory pipeline about four times one that reads 16 bytes from each of 16
 // rows, so the x scales of the tile's rows (192 bytes a row at H = 6144)
-// come once per item, row by row, and the weight scales come 16 bytes a row
-// per 512-wide K stage: each wave loads a quarter of its own 64 rows' next
-// stage with every K-step, into a region of LDS only it reads.
+// come once per item, row by row, into LDS. (The weight scales come packed:
+// one dword a lane per fragment and 512-wide stage.)
 constexpr int kGuXsSteps = 48;  // K-steps of x scales staged at a time (all of them up to H = 6144)
 constexpr int kGuXsLd = 13;     // 16-byte chunks per staged x-scale row (12 used; 13 keeps reads conflict-free)
 
 struct alignas(16) GuSmem {  // 16-byte aligned: staging and fragment accesses compile to single b128 LDS ops
-  uint8_t a[2][kGuR * 64];      // x rows (MXFP4), K-step slice (sw64 layout)
-  uint8_t b[2][256 * 64];       // 128 gate + 128 up weight rows
+  uint8_t a[2][kGuR * 64];         // x rows (MXFP4), K-step slice (sw64 layout)
   uint32_t xs[kGuR][4 * kGuXsLd];  // x scales of kGuXsSteps K-steps, 4 E8M0 bytes per K-step
-  uint32_t bs[2][256][4];       // weight scales of a 512-wide stage (by stage parity): [row][group g], byte j = K-step j
 };
-
-// One K-step of global data held in registers: 1 + 4 16-byte chunks and a
-// quarter of the wave's weight scales of a later stage.
-struct GuRegs {
-  uint4 a, b[4];
-  uint32_t sb;
-};
+constexpr int kGuBD = 2;  // K-steps of a wave's weight fragments held in registers (divides 8)
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gate_up_big_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const uint8_t* __restrict__ w13,
@@ -118,45 +107,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
     // through buffer descriptors (base and size in scalar registers, a
     // 32-bit offset per lane), which keeps the per-thread addresses out of
     // vector registers. A K-step of a 16-row block is 1 KB in MFMA lane
-    // order: wave w's load q covers row block 4 q + w of the item's 16 (gate
-    // blocks for q < 2, up blocks for q >= 2), lane l holding row l & 15,
-    // chunk l >> 4. An expert's packed bytes start where its rows did.
+    // order (lane l: row l & 15, MX block l >> 4), so each wave loads its own
+    // four fragments straight into registers, one 1 KB load each: gate row
+    // blocks 2 wn, 2 wn + 1 of the item and the matching up blocks. An
+    // expert's packed bytes start where its rows did; row block b of the
+    // expert at 16 b Hb, its scales at b * (H / 512) * 256.
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(w13 + (size_t)e * 2 * I * Hb), (short)0, (int)(2 * I * Hb), 0x00020000);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(s13 + (size_t)e * 2 * I * Hs), (short)0, (int)(2 * I * Hs), 0x00020000);
-    // a 16-row block's K-steps take 16 * Hb bytes; row block b of the expert starts at 16 b Hb
-    const int ob = (128 * ib + 16 * wave) * (int)Hb + 16 * (tid & 63);
-    const int boff[4] = {0, 64 * (int)Hb, I * (int)Hb, (I + 64) * (int)Hb};
     const int ns = nk / 4;  // 512-wide stages
-    // weight-scale quarter q of a stage for this wave: its local row block
-    // (gate 0..7, up 8..15); lane l holds the stage's four K-steps of row
-    // l & 15, MX block group l >> 4 (one dword, 256 contiguous bytes a block)
-    auto sq_blk = [&](int q) { return q < 2 ? 2 * wn + q : 8 + 2 * wn + (q - 2); };
-    auto sq_off = [&](int q) {
-      const int lb = sq_blk(q);
-      const int rb = lb < 8 ? 8 * ib + lb : I / 16 + 8 * ib + lb - 8;
-      return rb * ns * 256 + 4 * lane;
-    };
-    auto load = [&](int kk, GuRegs& R) {
-      R.a = ld16(pa + kk * 64);
+    const int rbg = 8 * ib + 2 * wn, rbu = I / 16 + rbg;
+    const int fo[4] = {rbg * 16 * (int)Hb + 16 * lane, (rbg + 1) * 16 * (int)Hb + 16 * lane,
+                       rbu * 16 * (int)Hb + 16 * lane, (rbu + 1) * 16 * (int)Hb + 16 * lane};
+    const int so[4] = {rbg * ns * 256 + 4 * lane, (rbg + 1) * ns * 256 + 4 * lane, rbu * ns * 256 + 4 * lane,
+                       (rbu + 1) * ns * 256 + 4 * lane};
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));
+    auto load_b = [&](int kk, uint4 (&B)[4]) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        typedef unsigned v4u __attribute__((ext_vector_type(4)));
-        const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rw, ob, boff[q] + kk * 1024, 0);
-        R.b[q] = make_uint4(v.x, v.y, v.z, v.w);
+      for (int f = 0; f < 4; ++f) {
+        const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rw, fo[f], kk * 1024, 0);
+        B[f] = make_uint4(v.x, v.y, v.z, v.w);
       }
-      // quarter kk % 4 of stage kk / 4 + 1 (past the last stage: the last one again, unread)
-      R.sb = __builtin_amdgcn_raw_buffer_load_b32(rs, sq_off(kk & 3), 256 * min(kk / 4 + 1, ns - 1), 0);
     };
-    // R holds K-step kk's data (to buffer kk & 1) and a scale quarter
-    auto store = [&](const GuRegs& R, int kk) {
-      const int s = kk & 1;
-      *reinterpret_cast<uint4*>(&sm.a[s][sw64(tid >> 2, tid & 3)]) = R.a;
+    // the four K-steps of stage st of each fragment: byte j of lane l's dword
+    auto load_sb = [&](int st, uint32_t (&S)[4]) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<uint4*>(&sm.b[s][sw64(64 * q + 16 * wave + (lane & 15), lane >> 4)]) = R.b[q];
-      sm.bs[(kk / 4 + 1) & 1][16 * sq_blk(kk & 3) + (lane & 15)][lane >> 4] = R.sb;
+      for (int f = 0; f < 4; ++f) S[f] = __builtin_amdgcn_raw_buffer_load_b32(rs, so[f], 256 * st, 0);
     };
     v4f accg[4][2], accu[4][2];
 #pragma unroll
@@ -166,8 +143,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
         accg[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
         accu[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
       }
-    auto compute = [&](int kk) {
-      const int s = kk & 1, ss = (kk / 4) & 1, q4 = kk & 3;
+    // x rows of K-step kk from LDS buffer kk & 1, the wave's weights from registers
+    auto compute = [&](int kk, const uint4 (&B)[4], const uint32_t (&S)[4]) {
+      const int s = kk & 1, q4 = kk & 3;
       uint4 fa[4];
       uint32_t sa[4];
 #pragma unroll
@@ -178,22 +156,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int col = 32 * wn + 16 * j + r;
-        const uint4 fg = *reinterpret_cast<const uint4*>(&sm.b[s][sw64(col, g)]);
-        const uint4 fu = *reinterpret_cast<const uint4*>(&sm.b[s][sw64(col + 128, g)]);
-        const uint32_t sg = (sm.bs[ss][col][g] >> (8 * q4)) & 0xFFu;
-        const uint32_t su = (sm.bs[ss][col + 128][g] >> (8 * q4)) & 0xFFu;
+        const uint32_t sg = (S[j] >> (8 * q4)) & 0xFFu;
+        const uint32_t su = (S[2 + j] >> (8 * q4)) & 0xFFu;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          accg[i][j] = mfma_fp4(fa[i], fg, accg[i][j], sa[i], sg);
-          accu[i][j] = mfma_fp4(fa[i], fu, accu[i][j], sa[i], su);
+          accg[i][j] = mfma_fp4(fa[i], B[j], accg[i][j], sa[i], sg);
+          accu[i][j] = mfma_fp4(fa[i], B[2 + j], accu[i][j], sa[i], su);
         }
       }
     };
-    // K-steps kk+1..kk+kGuStages are in flight while kk is multiplied: step
-    // kk's registers are refilled with step kk+kGuStages right after they
-    // were stored. Past the last step the loads repeat it and the stores fill
-    // a buffer nobody reads; only the MFMA work is skipped.
     // the tile's x scales of K-steps kGuXsSteps m .. (one row of 16-byte
     // chunks per token, read row by row)
     auto stage_xs = [&](int m) {
@@ -205,29 +176,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
             ld16(xs + (size_t)(t >= 0 ? t : tok0) * Hs + kGuXsSteps * 4 * m + 16 * c);
       }
     };
-    // prologue: x scales and the wave's stage-0 weight scales into LDS, then
-    // the first K-steps
+    // Pipeline: x rows go global -> registers (two K-steps ahead) -> LDS
+    // (double buffer, one barrier per K-step); the weights go global ->
+    // registers kGuBD K-steps ahead and their scales a stage ahead. Loads
+    // past the last step repeat it; only the MFMA work is skipped.
+    uint4 Bq[kGuBD][4];
+    uint32_t Sb[2][4];
+    uint4 Sa[2];
     stage_xs(0);
+    Sa[0] = ld16(pa);
+    Sa[1] = ld16(pa + min(1, nk - 1) * 64);
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      sm.bs[0][16 * sq_blk(q) + (lane & 15)][lane >> 4] = __builtin_amdgcn_raw_buffer_load_b32(rs, sq_off(q), 0, 0);
-    GuRegs S[kGuStages];
-#pragma unroll
-    for (int q = 0; q < kGuStages; ++q) load(min(q, nk - 1), S[q]);
-    store(S[0], 0);
+    for (int d = 0; d < kGuBD; ++d) load_b(min(d, nk - 1), Bq[d]);
+    load_sb(0, Sb[0]);
+    *reinterpret_cast<uint4*>(&sm.a[0][sw64(tid >> 2, tid & 3)]) = Sa[0];
     barrier_lds();
-    for (int kk = 0; kk < nk; kk += kGuStages) {
+    // unrolled by two stages, so every ring index is a constant
+    for (int kk = 0; kk < nk; kk += 8) {
 #pragma unroll
-      for (int q = 0; q < kGuStages; ++q) {
-        load(min(kk + q + kGuStages, nk - 1), S[q]);
-        if (kk + q < nk) {
-          if (kk + q > 0 && (kk + q) % kGuXsSteps == 0) {  // only when H > 6144
-            stage_xs((kk + q) / kGuXsSteps);  // every wave is past the previous step's barrier
+      for (int q = 0; q < 8; ++q) {
+        const int k = kk + q;
+        if (q % 4 == 0) load_sb(min(k / 4 + 1, ns - 1), Sb[(q / 4 + 1) & 1]);  // the next stage's scales
+        Sa[q & 1] = ld16(pa + min(k + 2, nk - 1) * 64);
+        if (k < nk) {
+          if (k > 0 && k % kGuXsSteps == 0) {  // only when H > 6144
+            stage_xs(k / kGuXsSteps);  // every wave is past the previous step's barrier
             barrier_lds();
           }
-          compute(kk + q);
+          compute(k, Bq[q % kGuBD], Sb[(q / 4) & 1]);
         }
-        store(S[(q + 1) % kGuStages], kk + q + 1);
+        load_b(min(k + kGuBD, nk - 1), Bq[q % kGuBD]);
+        *reinterpret_cast<uint4*>(&sm.a[(q + 1) & 1][sw64(tid >> 2, tid & 3)]) = Sa[(q + 1) & 1];
         barrier_lds();
       }
     }
