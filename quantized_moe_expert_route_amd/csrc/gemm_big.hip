@@ -431,83 +431,91 @@ __global__ __launch_bounds__(kDnThreads) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
       for (int q = 0; q < 3; ++q) *reinterpret_cast<unsigned*>(&wsl[12 * tid + 4 * q]) = vsc3[q];
     } else *reinterpret_cast<unsigned*>(&wsl[4 * tid]) = vsc1;
-    double acc[2][4][4];
-    // one 128-block: B fragments from the weight half in LDS
-    auto block = [&](auto bc) {
-      constexpr int b = decltype(bc)::value, h = b / 2, BH = NB - 2 * h >= 2 ? 2 : 1;
-      v4u Sw[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        Sw[j] = *reinterpret_cast<const v4u*>(&wld[sw_w<BH>(64 * wave + 16 * j + m, 4 * (b % 2) + g)]);
-      float wsc[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) wsc[j] = e8m0_to_float(wsl[(64 * wave + 16 * j + m) * Sb + 4 * b + g]);
-      v4f P[2][4];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) P[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        v8s fb[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t wq = Sw[j][q];
-          fb[j] = as_v8s(cvt_fp4x2_bf16<0>(wq, wsc[j]), cvt_fp4x2_bf16<1>(wq, wsc[j]),
-                         cvt_fp4x2_bf16<2>(wq, wsc[j]), cvt_fp4x2_bf16<3>(wq, wsc[j]));
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const v8s fa = *reinterpret_cast<const v8s*>(&a16[sw_mid16<NB>(16 * i + m, 16 * b + 4 * g + q)]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) P[i][j] = mfma_bf16(fa, fb[j], P[i][j]);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const float4 sc = *reinterpret_cast<const float4*>(&ms[b * kDnRows + 16 * i + 4 * g]);
-        const double scd[4] = {(double)sc.x, (double)sc.y, (double)sc.z, (double)sc.w};
-#pragma unroll
+    // RB = 16-row blocks of the tile that hold rows: a tile of at most 16
+    // rows computes and stores one (the other is padding), on a path of its
+    // own so that neither carries the other's registers
+    auto run = [&](auto rbc) {
+      constexpr int RB = decltype(rbc)::value;
+      double acc[RB][4][4];
+      // one 128-block: B fragments from the weight half in LDS
+      auto block = [&](auto bc) {
+        constexpr int b = decltype(bc)::value, h = b / 2, BH = NB - 2 * h >= 2 ? 2 : 1;
+        v4u Sw[4];
+  #pragma unroll
         for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            acc[i][j][v] = b == 0 ? scd[v] * (double)P[i][j][v] : fma(scd[v], (double)P[i][j][v], acc[i][j][v]);
+          Sw[j] = *reinterpret_cast<const v4u*>(&wld[sw_w<BH>(64 * wave + 16 * j + m, 4 * (b % 2) + g)]);
+        float wsc[4];
+  #pragma unroll
+        for (int j = 0; j < 4; ++j) wsc[j] = e8m0_to_float(wsl[(64 * wave + 16 * j + m) * Sb + 4 * b + g]);
+        v4f P[2][4];
+  #pragma unroll
+        for (int i = 0; i < RB; ++i)
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) P[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v8s fb[4];
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t wq = Sw[j][q];
+            fb[j] = as_v8s(cvt_fp4x2_bf16<0>(wq, wsc[j]), cvt_fp4x2_bf16<1>(wq, wsc[j]),
+                           cvt_fp4x2_bf16<2>(wq, wsc[j]), cvt_fp4x2_bf16<3>(wq, wsc[j]));
+          }
+  #pragma unroll
+          for (int i = 0; i < RB; ++i) {
+            const v8s fa = *reinterpret_cast<const v8s*>(&a16[sw_mid16<NB>(16 * i + m, 16 * b + 4 * g + q)]);
+  #pragma unroll
+            for (int j = 0; j < 4; ++j) P[i][j] = mfma_bf16(fa, fb[j], P[i][j]);
+          }
+        }
+  #pragma unroll
+        for (int i = 0; i < RB; ++i) {
+          const float4 sc = *reinterpret_cast<const float4*>(&ms[b * kDnRows + 16 * i + 4 * g]);
+          const double scd[4] = {(double)sc.x, (double)sc.y, (double)sc.z, (double)sc.w};
+  #pragma unroll
+          for (int j = 0; j < 4; ++j)
+  #pragma unroll
+            for (int v = 0; v < 4; ++v)
+              acc[i][j][v] = b == 0 ? scd[v] * (double)P[i][j][v] : fma(scd[v], (double)P[i][j][v], acc[i][j][v]);
+        }
+      };
+      // half 0 (in registers) to LDS; the next half's loads run while a half
+      // is multiplied; after the last half's loads go out, the next item's
+      // mid rows and first half
+      store_half(std::integral_constant<int, 0>());
+      __syncthreads();
+      if (NH > 1) load_half(item, std::integral_constant<int, 1>());
+      else {
+        fetch_tile(next);
+        load_half(next, std::integral_constant<int, 0>());
+      }
+      block(std::integral_constant<int, 0>());
+      if (NB > 1) block(std::integral_constant<int, 1 % NB>());
+      if (NH > 1) {
+        __syncthreads();  // every wave is done with half 0
+        store_half(std::integral_constant<int, NH - 1>());
+        __syncthreads();
+        fetch_tile(next);
+        load_half(next, std::integral_constant<int, 0>());
+        block(std::integral_constant<int, 2 % NB>());
+        if (NB > 3) block(std::integral_constant<int, 3 % NB>());
+      }
+      // y row = entry (rows past the tile's end repeat its last row)
+      const int col = item.w * kDnItemCols + 64 * wave + m;
+  #pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        const int4 en = *reinterpret_cast<const int4*>(&ent[16 * i + 4 * g]);
+        const int env[4] = {en.x, en.y, en.z, en.w};
+  #pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float* py = y + (size_t)env[v] * H + col;
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) py[16 * j] = (float)acc[i][j][v];
+        }
       }
     };
-    // half 0 (in registers) to LDS; the next half's loads run while a half
-    // is multiplied; after the last half's loads go out, the next item's
-    // mid rows and first half
-    store_half(std::integral_constant<int, 0>());
-    __syncthreads();
-    if (NH > 1) load_half(item, std::integral_constant<int, 1>());
-    else {
-      fetch_tile(next);
-      load_half(next, std::integral_constant<int, 0>());
-    }
-    block(std::integral_constant<int, 0>());
-    if (NB > 1) block(std::integral_constant<int, 1 % NB>());
-    if (NH > 1) {
-      __syncthreads();  // every wave is done with half 0
-      store_half(std::integral_constant<int, NH - 1>());
-      __syncthreads();
-      fetch_tile(next);
-      load_half(next, std::integral_constant<int, 0>());
-      block(std::integral_constant<int, 2 % NB>());
-      if (NB > 3) block(std::integral_constant<int, 3 % NB>());
-    }
-    // y row = entry (rows past the tile's end repeat its last row)
-    const int col = item.w * kDnItemCols + 64 * wave + m;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int4 en = *reinterpret_cast<const int4*>(&ent[16 * i + 4 * g]);
-      const int env[4] = {en.x, en.y, en.z, en.w};
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        float* py = y + (size_t)env[v] * H + col;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) py[16 * j] = (float)acc[i][j][v];
-      }
-    }
+    if (item.z - item.y > 16) run(std::integral_constant<int, 2>());
+    else run(std::integral_constant<int, 1>());
   }
 }
 
