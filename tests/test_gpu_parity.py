@@ -171,6 +171,37 @@ def test_small_shapes(M, H, E, I, k, kind, Is):
     _check_out(gout, ref["out"])
 
 
+def test_shared_x_codes_on_exact_midpoints():
+    """x blocks whose amax is 672 (scale fl32(672 / 448) = 1.5, whose
+    reciprocal is not exact) and whose other entries are 1.5 x an E4M3
+    rounding midpoint, so fl32(x / s) lands exactly on a tie (normal
+    midpoints over every binade, and the subnormal grid's): the E4M3 codes
+    must follow round-half-to-even, bit for bit with the oracle."""
+    import itertools
+
+    shape = X.Shape(M=80, H=512, E=8, I=128, top_k=2, shared_I=128)
+    d = X.make_inputs(shape, "normal", 4242)
+    mids = [(1 + (2 * j + 1) / 16) * 2.0 ** e for e in range(-6, 9) for j in range(8)]
+    mids = [m for m in mids if m < 448] + [(k + 0.5) / 512 for k in range(8)]
+    vals = np.array([1.5 * m for m in mids], np.float64)
+    x = np.empty((shape.M, shape.H), np.float64)
+    cyc = itertools.cycle(range(len(vals)))
+    for t in range(shape.M):
+        for b in range(shape.H // 128):
+            blk = np.array([vals[next(cyc)] for _ in range(128)])
+            blk *= np.where(np.arange(128) % 3 == 0, -1.0, 1.0)
+            blk[(t + b) % 128] = 672.0
+            x[t, 128 * b:128 * b + 128] = blk
+    bits = F.bf16_encode(x)
+    assert np.array_equal(F.bf16_decode(bits), x), "test values must be exact in bf16"
+    d["x"] = bits
+    gout, gi = run(d)
+    ref = oracle(d)
+    _check_shared_x(gi, ref)
+    _check_xq(gi, ref)
+    _check_out(gout, ref["out"])
+
+
 def test_degenerate_inputs():
     shape = X.Shape(M=6, H=512, E=16, I=128, top_k=4)
     d = X.make_inputs(shape, "normal", 5)
