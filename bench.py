@@ -261,7 +261,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c1", help="headline workload (c1..c4)")
-    ap.add_argument("--also", default="c2,c3,c4", help="more workloads reported in the same line ('' for none)")
+    ap.add_argument("--also", default="c2,c3,c4,m256_hot,m256_mixed",
+                    help="more workloads reported in the same line ('' for none); mid-range batches are "
+                         "m{32,64,128,256}_{hot,mixed,spread}")
     ap.add_argument("--sets", type=int, default=8, help="distinct input batches cycled through the steps")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",

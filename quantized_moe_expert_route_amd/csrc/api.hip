@@ -146,7 +146,7 @@ int moe_plan_stage_launches(const moe_plan* plan, int64_t M, int stage) {
     case 0: return 1;                             // route + x quantization (+ sort when small; + the shared expert's x when large)
     case 1: return small ? 0 : 3;                 // align
     case 2: return 1;                             // gate_up (+ mid quantization when large)
-    case 3: return small ? 1 : 0;                 // act_quant
+    case 3: return mid_path(M, plan->s.top_k) ? 1 : 0;  // act_quant (inside gate/up above kMidM)
     case 4: return plan->s.shared_I > 0 ? (small ? 4 : 3) : 0;  // shared expert
     case 5: return 1;                             // down (+ combine when small)
     default: return small ? 0 : 1;                // combine
@@ -330,8 +330,9 @@ moe_status moe_forward(moe_plan* plan, int64_t M, const void* x, const float* lo
   // launch.
   hipError_t e = small ? launch_route_small(plan, a, ev[0]) : launch_route(plan, a, ev[0]);
   if (e == hipSuccess) e = small ? none(1) : launch_align(plan, a, ev[1]);
-  if (e == hipSuccess) e = small ? launch_gate_up(plan, a, ev[2]) : launch_gate_up_big(plan, a, ev[2]);
-  if (e == hipSuccess) e = small ? launch_act_quant(plan, a, ev[3]) : none(3);
+  const bool tiles16 = mid_path(M, plan->s.top_k);  // 16-row-tile gate/up, mid quantization on its own
+  if (e == hipSuccess) e = tiles16 ? launch_gate_up(plan, a, ev[2]) : launch_gate_up_big(plan, a, ev[2]);
+  if (e == hipSuccess) e = tiles16 ? launch_act_quant(plan, a, ev[3]) : none(3);
   if (e == hipSuccess) e = plan->s.shared_I > 0 ? launch_shared(plan, a, ev[4]) : none(4);
   if (e == hipSuccess) e = small ? launch_down_combine(plan, a, ev[5]) : launch_down_big(plan, a, ev[5]);
   if (e == hipSuccess) e = small ? none(6) : launch_combine(plan, a, ev[6]);

@@ -73,9 +73,15 @@ inline hipError_t launch_k(void (*kern)(KArgs...), dim3 grid, dim3 block, size_t
 // Largest M (and M * top_k) served by the single-workgroup routing/sort
 // path and the small-token kernels (down and combine in one launch, whose
 // per-entry results must fit in LDS).
-constexpr int kSmallM = 64;
-constexpr int kSmallRows = 896;
+constexpr int kSmallM = 32;
+constexpr int kSmallRows = 512;
 inline bool small_path(int64_t M, int64_t k) { return M <= kSmallM && M * k <= kSmallRows; }
+// Up to kMidM tokens (and at most 16 slots) gate/up runs on 16-row tiles
+// with the mid quantization in its own launch (the large path's routing and
+// sort otherwise): with few rows per expert, 64-row tiles leave most of the
+// chip idle.
+constexpr int kMidM = 256;
+inline bool mid_path(int64_t M, int64_t k) { return M <= kMidM && k <= 16; }
 
 struct CallArgs {
   int64_t M;

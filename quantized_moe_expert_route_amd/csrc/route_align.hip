@@ -19,7 +19,7 @@
 // to 16 rows": expert-major MoE). Every token sets bit t of its experts'
 // rows of a token bitmap; an entry's rank is the popcount of its row below t,
 // so the order is deterministic and needs no ordering between waves. Up to
-// 64 tokens the bitmap lives in LDS and one workgroup routes, quantizes and
+// kSmallM tokens the bitmap lives in LDS and one workgroup routes, quantizes and
 // sorts in a single launch; above that the route launch sets the bits in
 // global memory and a one-workgroup align launch ranks the entries.
 #include "common.h"
@@ -136,13 +136,13 @@ __device__ int block_exclusive_scan(int v, int* s_tmp, int* total) {
   return r;
 }
 
-static_assert(kSmallRows < (1 << 16), "rows and tiles share one packed scan");
+static_assert(kSmallRows < (1 << 16) && kMidM * 16 < (1 << 16), "rows and tiles share one packed scan");
 
 // Offsets (and with_tiles: tiles of kTileRows sorted rows, meta[0]) from
 // per-expert counts (thread e holds count c of expert e). Leaves offsets in
-// s_off. Tiles are written only for the small-token path, where the row
-// total is at most kSmallRows: rows and tiles then share one scan, packed as
-// rows | tiles << 16.
+// s_off. Tiles are written only where the 16-row-tile gate/up runs (up to
+// kMidM tokens), where the row total is below 2^16: rows and tiles then
+// share one scan, packed as rows | tiles << 16.
 __device__ void write_offsets_tiles(int c, int E, int* s_off, int* s_tmp, int* __restrict__ count,
                                     int* __restrict__ offset, int4* __restrict__ tiles, int* __restrict__ meta,
                                     bool with_tiles = true) {
@@ -168,7 +168,7 @@ __device__ void write_offsets_tiles(int c, int E, int* s_off, int* s_tmp, int* _
   __syncthreads();
 }
 
-// ---------------------------------------------------------------- M <= 64
+// ---------------------------------------------------------------- M <= kSmallM
 // Workgroup 0 routes, sorts and writes the tiles; workgroups 1.. quantize x.
 template <int EC>
 __global__ __launch_bounds__(1024) void route_align_small_kernel(
@@ -220,7 +220,7 @@ __global__ __launch_bounds__(1024) void route_align_small_kernel(
   }
 }
 
-// ---------------------------------------------------------------- M > 64
+// ---------------------------------------------------------------- M > kSmallM
 // x of one token, 8 elements a lane, 512 a load instruction (whole cache
 // lines): the 4 lanes of a 32-block form its E8M0 scale and E2M1 codes (the
 // same arithmetic as quant_block_mx), and with SH the 16 lanes of a
@@ -402,13 +402,14 @@ __global__ __launch_bounds__(256) void align_rows_kernel(uint32_t* __restrict__ 
 
 __global__ __launch_bounds__(1024) void align_offsets_kernel(
     const int* __restrict__ count_in, int E, int* __restrict__ count, int* __restrict__ offset,
-    int4* __restrict__ tiles, int* __restrict__ meta, int n_iblk, int n_nc, int* __restrict__ toff) {
+    int4* __restrict__ tiles, int* __restrict__ meta, int n_iblk, int n_nc, int* __restrict__ toff,
+    int with_tiles) {
   __shared__ int s_off[1024];
   __shared__ int s_tmp[64];
   const int tid = threadIdx.x;
   const int c = tid < E ? count_in[tid] : 0;
   __syncthreads();  // count_in may be count itself
-  write_offsets_tiles(c, E, s_off, s_tmp, count, offset, tiles, meta, false);
+  write_offsets_tiles(c, E, s_off, s_tmp, count, offset, tiles, meta, with_tiles != 0);
   write_tile_prefixes(c, E, n_iblk, n_nc, s_tmp, toff, meta);
 }
 
@@ -500,7 +501,8 @@ hipError_t launch_align(const moe_plan* p, const CallArgs& a, Ev ev) {
   if (e != hipSuccess) return e;
   e = launch_k(align_offsets_kernel, dim3(1), dim3(1024), 0, a.stream, Ev{}, wsp<int>(p, p->L.count),
                (int)p->s.E, wsp<int>(p, p->L.count), wsp<int>(p, p->L.offset), wsp<int4>(p, p->X.tiles),
-               wsp<int>(p, p->X.meta), (int)(p->s.I / 128), (int)(p->s.H / kDownItemCols), wsp<int>(p, p->X.toff));
+               wsp<int>(p, p->X.meta), (int)(p->s.I / 128), (int)(p->s.H / kDownItemCols), wsp<int>(p, p->X.toff),
+               (int)mid_path(a.M, p->s.top_k));  // the 16-row tiles of the mid-range gate/up
   if (e != hipSuccess) return e;
   return launch_k(align_place_kernel, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 4096)), dim3(256), 0,
                   a.stream, Ev{nullptr, ev.stop}, wsp<int>(p, p->L.topk_ids), (int)n, (int)p->s.top_k, words,

@@ -64,7 +64,7 @@ class Shape:
 class Workload:
     name: str
     shape: Shape
-    logits: str  # "normal" | "uniform" | "correlated" | "zipf"
+    logits: str  # "normal" | "uniform" | "correlated" | "zipf" | "hot" | "mixed" | "spread"
     seed: int
 
 
@@ -76,6 +76,12 @@ WORKLOADS: Dict[str, Workload] = {
     "c4": Workload("c4", Shape(M=4096, H=6144, E=256, I=512, top_k=8, shared_I=512), "zipf", 4),
 }
 
+# Mid-range batches (MTP verify at M = 4 x concurrency) on the TP8 shapes,
+# with the expert-reuse patterns above; they share c1's weights (seed 1).
+for _m in (32, 64, 128, 256):
+    for _kind in ("hot", "mixed", "spread"):
+        WORKLOADS[f"m{_m}_{_kind}"] = Workload(f"m{_m}_{_kind}", Shape(M=_m, H=6144, E=256, I=256, top_k=8), _kind, 1)
+
 WORKLOAD_TITLES = {
     "c0": "tiny H512 E16 top2 I128 M4",
     "c1": "TP8-rank decode H6144 E256 top8 I256 M4, MXFP4 experts, uniform logits",
@@ -83,6 +89,9 @@ WORKLOAD_TITLES = {
     "c3": "TP4-rank prefill H6144 E256 top8 I512 M1024, MXFP4 experts, Zipf(1.1) routing",
     "c4": "TP4-rank large prefill H6144 E256 top8 I512 M4096 + block-FP8 shared expert I512, Zipf(1.1)",
 }
+for _name, _wl in WORKLOADS.items():
+    if _name not in WORKLOAD_TITLES:
+        WORKLOAD_TITLES[_name] = f"TP8-rank batch H6144 E256 top8 I256 M{_wl.shape.M}, {_wl.logits} routing"
 
 
 def _rng(seed: int, tid: int, e: int = 0) -> np.random.Generator:
@@ -170,6 +179,24 @@ def make_logits(shape: Shape, kind: str, seed: int) -> np.ndarray:
         pe[perm] = p
         g = rng.gumbel(size=(M, E))
         return (np.log(pe)[None, :] + g).astype(np.float32)
+    if kind in ("hot", "spread", "mixed"):
+        # Expert-reuse patterns of the mid-range batches (the pages name hot /
+        # spread / mixed routing without defining them; these are our
+        # readings): hot = every token picks the same k experts (fewest
+        # active, most rows each); spread = token t picks experts
+        # perm[(k t + j) mod E], so the batch covers as many experts as it
+        # can; mixed = the first half hot, the second half spread. The chosen
+        # k get +2.0 on U[0,1) logits, so they are exactly the top k.
+        out = rng.random((M, E), dtype=np.float32)
+        perm = _rng(seed, _T_PERM).permutation(E)
+        hot = perm[:k]
+        for t in range(M):
+            if kind == "hot" or (kind == "mixed" and t < M // 2):
+                chosen = hot
+            else:
+                chosen = perm[(k * t + np.arange(k)) % E]
+            out[t, chosen] += np.float32(2.0)
+        return out
     if kind == "ties":
         # Few distinct values, both zeros: stresses the lower-index tie rule.
         vals = np.array([-1.0, -0.0, 0.0, 0.5, 0.5, 1.0], dtype=np.float32)

@@ -43,7 +43,7 @@ def _check_xq(gi, ref, tokens=None):
 
 # the library writes y to the workspace only above this many tokens (below,
 # the combine runs inside the down launch)
-Y_WRITTEN_ABOVE_M = 64
+Y_WRITTEN_ABOVE_M = 32
 
 
 def _check_mid(gi_midq, gi_mids, ref_midq, ref_mids):
@@ -105,10 +105,13 @@ def test_stagewise_full(name):
     assert ndiff == 0, "expected the oracle's bf16 output exactly on these inputs"
 
 
-@pytest.mark.parametrize("name,n_tok", [("c3", 12), ("c4", 8)])
+@pytest.mark.parametrize("name,n_tok", [("c3", 12), ("c4", 8), ("m32_spread", 6), ("m64_mixed", 6),
+                                        ("m128_spread", 8), ("m256_hot", 8), ("m256_mixed", 8)])
 def test_sampled_full_size(name, n_tok):
     """Full-size call as the benchmark runs it; routing/sort checked on every
-    token, everything else on a sample of tokens the oracle evaluates alone."""
+    token, everything else on a sample of tokens the oracle evaluates alone.
+    The mid-range batches (M = 32..256, hot / mixed / spread expert reuse)
+    cover both paths at the sizes between decode and prefill."""
     d = X.make_inputs(name)
     s = d["shape"]
     gout, gi = run(d)
@@ -126,8 +129,9 @@ def test_sampled_full_size(name, n_tok):
     r_midq = rows_by_entry(ref["midq"], ref["sorted_entry"], n_tok * k)
     r_mids = rows_by_entry(ref["mids"], ref["sorted_entry"], n_tok * k)
     _check_mid(g_midq, g_mids, r_midq, r_mids)
-    ydiff = _check_y(gi["y"][ent], ref["y"])
-    print(f"{name}: y differs in {ydiff} of {ref['y'].size} sampled elements")
+    if s.M > Y_WRITTEN_ABOVE_M:
+        ydiff = _check_y(gi["y"][ent], ref["y"])
+        print(f"{name}: y differs in {ydiff} of {ref['y'].size} sampled elements")
     if s.shared_I:
         _check_shared_x(gi, ref, tokens)
         sdiff = int(np.count_nonzero(gi["sh_y"][tokens].view(np.uint32) != ref["ys"].view(np.uint32)))
@@ -145,7 +149,8 @@ SMALL = [
     (40, 1024, 32, 256, 4, "zipf", 0),         # skew: one expert takes most tokens
     (3, 512, 4, 128, 2, "normal", 128),        # shared expert
     (20, 512, 1024, 128, 16, "uniform", 0),    # largest E and k
-    # above 64 tokens: 128-row tiles, mid quantization inside gate/up
+    # above 32 tokens: the large path's routing and sort; up to 256 tokens gate/up on
+    # 16-row tiles with its own mid quantization, above on 64-row tiles with it inside
     (65, 512, 16, 128, 2, "normal", 0),        # one token past the small path
     (130, 1024, 32, 256, 8, "zipf", 0),        # skewed: a tile of 128 plus ragged tails
     (300, 512, 8, 512, 2, "normal", 0),        # several full tiles per expert, I = 512
