@@ -73,8 +73,8 @@ typedef struct moe_plan moe_plan; /* opaque; host memory only */
  *   midq         u8    [n, I]       E4M3 mid, rows in sorted order
  *   mids         fp32  [n, I/128]   mid block scales, rows in sorted order
  *   y            fp32  [n, H]       unweighted down output, row = entry t*k+j;
- *                                   written only by calls with M > 32 (up to
- *                                   32 tokens the combine runs in the down
+ *                                   written only by calls with M > 16 (up to
+ *                                   16 tokens the combine runs in the down
  *                                   launch and slot results stay on chip)
  *   sh_xq/sh_xs  u8 [M, H] / fp32 [H/128, M]      shared expert x in E4M3
  *   sh_hq/sh_hs  u8 [M, Is] / fp32 [Is/128, M]    shared expert mid in E4M3

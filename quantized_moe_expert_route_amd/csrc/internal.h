@@ -73,7 +73,7 @@ inline hipError_t launch_k(void (*kern)(KArgs...), dim3 grid, dim3 block, size_t
 // Largest M (and M * top_k) served by the single-workgroup routing/sort
 // path and the small-token kernels (down and combine in one launch, whose
 // per-entry results must fit in LDS).
-constexpr int kSmallM = 32;
+constexpr int kSmallM = 16;
 constexpr int kSmallRows = 512;
 inline bool small_path(int64_t M, int64_t k) { return M <= kSmallM && M * k <= kSmallRows; }
 // Up to kMidM tokens (and at most 16 slots) gate/up runs on 16-row tiles

@@ -504,7 +504,11 @@ hipError_t launch_align(const moe_plan* p, const CallArgs& a, Ev ev) {
                wsp<int>(p, p->X.meta), (int)(p->s.I / 128), (int)(p->s.H / kDownItemCols), wsp<int>(p, p->X.toff),
                (int)mid_path(a.M, p->s.top_k));  // the 16-row tiles of the mid-range gate/up
   if (e != hipSuccess) return e;
-  return launch_k(align_place_kernel, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 4096)), dim3(256), 0,
+  // a thread per entry and per work item: with few rows per expert the items
+  // (tiles x column blocks) far outnumber the entries
+  const int64_t items = p->tb_max * std::max<int64_t>(p->s.H / kDownItemCols, p->s.I / 128);
+  const int64_t threads = std::max(n, items);
+  return launch_k(align_place_kernel, dim3((unsigned)std::min<int64_t>((threads + 255) / 256, 4096)), dim3(256), 0,
                   a.stream, Ev{nullptr, ev.stop}, wsp<int>(p, p->L.topk_ids), (int)n, (int)p->s.top_k, words,
                   wsp<int2>(p, p->X.pw), wsp<int>(p, p->L.offset), wsp<int>(p, p->L.sorted_entry), (int)p->s.E,
                   (int)(p->s.I / 128), (int)(p->s.H / kDownItemCols), wsp<int>(p, p->X.toff), wsp<int>(p, p->X.meta),

@@ -43,7 +43,7 @@ def _check_xq(gi, ref, tokens=None):
 
 # the library writes y to the workspace only above this many tokens (below,
 # the combine runs inside the down launch)
-Y_WRITTEN_ABOVE_M = 32
+Y_WRITTEN_ABOVE_M = 16
 
 
 def _check_mid(gi_midq, gi_mids, ref_midq, ref_mids):
@@ -141,17 +141,20 @@ def test_sampled_full_size(name, n_tok):
 
 SMALL = [
     # (M, H, E, I, k, logits, shared_I)
+    # up to 16 tokens: one workgroup routes and sorts, down and combine in one launch
     (1, 512, 16, 128, 2, "normal", 0),
-    (17, 512, 16, 128, 2, "normal", 0),       # ragged: a tile of 16 plus a tail
+    (16, 512, 64, 128, 8, "ties", 0),          # the last size of the small path
     (5, 1024, 4, 256, 1, "normal", 0),         # top-1
     (9, 512, 8, 384, 8, "ties", 0),            # k = E, many ties, I = 384
     (33, 512, 64, 128, 8, "ties", 0),          # ties and signed zeros
     (40, 1024, 32, 256, 4, "zipf", 0),         # skew: one expert takes most tokens
     (3, 512, 4, 128, 2, "normal", 128),        # shared expert
-    (20, 512, 1024, 128, 16, "uniform", 0),    # largest E and k
-    # above 32 tokens: the large path's routing and sort; up to 256 tokens gate/up on
+    # above 16 tokens: the large path's routing and sort; up to 256 tokens gate/up on
     # 16-row tiles with its own mid quantization, above on 64-row tiles with it inside
-    (65, 512, 16, 128, 2, "normal", 0),        # one token past the small path
+    (17, 512, 16, 128, 2, "normal", 0),        # one token past the small path; ragged tiles
+    (20, 512, 1024, 128, 16, "uniform", 0),    # largest E and k
+    (65, 512, 16, 128, 2, "normal", 0),
+    (257, 512, 64, 128, 8, "uniform", 0),      # one token past the 16-row-tile gate/up
     (130, 1024, 32, 256, 8, "zipf", 0),        # skewed: a tile of 128 plus ragged tails
     (300, 512, 8, 512, 2, "normal", 0),        # several full tiles per expert, I = 512
     (96, 512, 64, 384, 8, "ties", 0),
@@ -312,7 +315,7 @@ def test_variable_m_across_paths_one_plan():
     w = X.make_inputs(base, "normal", 31)
     import torch
 
-    for it, M in enumerate([70, 4, 300, 65, 64, 128, 1]):
+    for it, M in enumerate([70, 4, 300, 65, 16, 17, 257, 256, 64, 128, 1]):
         shape = X.Shape(M=M, H=512, E=16, I=256, top_k=4)
         d = X.make_inputs(shape, "zipf" if it % 2 else "normal", 900 + it, with_weights=False)
         for key in ("w13", "s13", "w2", "s2"):
