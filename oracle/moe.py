@@ -22,6 +22,8 @@ What the call computes, in the pages' order:
    with an fp32 scale ("glm53: FP8 mid hand-off ...", row "mid as FP8 once").
 6. down: y[t, j] = sum over mid blocks b of s_b * (q_b . w2_b); each block
    sum exact, the scales applied in float64, one rounding to fp32.
+5'/6'. the MXFP4 comparison arm (mid_format "mxfp4"): mid quantized per 32
+   with the rule of step 3, down as one exact sum of MXFP4 x MXFP4 products.
 7. combine: out[t] = bf16(sum_j w[t, j] * y[t, j] (+ shared[t])), one
    rounding to bf16.
 8. shared expert (block-FP8, 128x128 weight scales; "IQ2R: load GLM-5.3 ...",
@@ -170,6 +172,26 @@ def down(q: np.ndarray, s: np.ndarray, w2d: np.ndarray) -> np.ndarray:
     return acc.astype(np.float32)
 
 
+# ------------------------------------------------------------------ 5'/6'. MXFP4 mid
+# The comparison arm the pages time against IQ2R is stock MXFP4: experts
+# quantized online to MXFP4 ("IQ2R: load GLM-5.3 packed MoE checkpoints ...",
+# Results (MXFP4 vs IQ2R)). Reading: its activations are MXFP4 in both GEMMs,
+# so mid takes the rule of step 3 (per 32, E8M0 scale, E2M1 codes) in place of
+# step 5, and down multiplies two MXFP4 operands.
+def quantize_mid_mx(h: np.ndarray):
+    """h [r, I] float32 -> (E2M1 codes [r, I], E8M0 scale codes [r, I/32])."""
+    return F.mx_fp4_quantize(h, 32)
+
+
+def down_mx(q: np.ndarray, s: np.ndarray, w2d: np.ndarray) -> np.ndarray:
+    """q [r, I] E2M1 codes, s [r, I/32] E8M0 codes, w2d [H, I] dequantized.
+
+    y = fl32(exact sum over I of mid * w2): every term is a product of two
+    E2M1 values times a power of two.
+    """
+    return _exact_matmul(F.mx_fp4_decode(q, s, 32), w2d).astype(np.float32)
+
+
 # ------------------------------------------------------------------ 8. shared expert
 def _block_fp8_linear(aq, as_, wq, ws) -> np.ndarray:
     """a [r, K] E4M3 codes with fp32 scales per 128 along K; w [n, K] E4M3 codes
@@ -216,15 +238,27 @@ def combine(w: np.ndarray, y: np.ndarray, ys=None) -> np.ndarray:
 
 
 # ------------------------------------------------------------------ whole call
-def moe_forward(x_bits, logits, w13, s13, w2, s2, top_k, scaling, shared=None):
+def _mid_steps(mid_format: str):
+    """(quantize, down) of the mid hand-off: "e4m3" (steps 5, 6) or "mxfp4"."""
+    if mid_format == "e4m3":
+        return quantize_mid, down
+    if mid_format == "mxfp4":
+        return quantize_mid_mx, down_mx
+    raise ValueError(mid_format)
+
+
+def moe_forward(x_bits, logits, w13, s13, w2, s2, top_k, scaling, shared=None, mid_format="e4m3"):
     """The routed-MoE call on all M tokens.
 
     x_bits [M, H] bf16 bits; logits [M, E] fp32; w13 [E, 2I, H/2] u8 and s13
     [E, 2I, H/32] u8 (MXFP4, rows [0, I) gate, [I, 2I) up); w2 [E, H, I/2]
     and s2 [E, H, I/32] (MXFP4 along I); shared = (ws13, ss13, ws2, ss2) or
     None. Returns a dict of every intermediate; rows of h / midq / mids are in
-    sorted (expert-major) order, y is indexed by entry t*k + j.
+    sorted (expert-major) order, y is indexed by entry t*k + j. midq holds
+    one code per element (E4M3, or E2M1 with mid_format "mxfp4"), mids the
+    fp32 scales per 128 (or the E8M0 scale codes per 32).
     """
+    qmid, dmid = _mid_steps(mid_format)
     x_bits = np.asarray(x_bits, np.uint16)
     M, H = x_bits.shape
     E = logits.shape[1]
@@ -237,7 +271,8 @@ def moe_forward(x_bits, logits, w13, s13, w2, s2, top_k, scaling, shared=None):
     n = M * k
     h = np.zeros((n, I), np.float32)
     midq = np.zeros((n, I), np.uint8)
-    mids = np.zeros((n, I // 128), np.float32)
+    mids = (np.zeros((n, I // 128), np.float32) if mid_format == "e4m3"
+            else np.zeros((n, I // 32), np.uint8))
     y = np.zeros((n, H), np.float32)
     for e in range(E):
         lo, hi = offset[e], offset[e + 1]
@@ -246,9 +281,9 @@ def moe_forward(x_bits, logits, w13, s13, w2, s2, top_k, scaling, shared=None):
         entries = sorted_entry[lo:hi]
         toks = entries // k
         he = gate_up(xd[toks], dequant_mxfp4(w13[e], s13[e]), I)
-        qe, se = quantize_mid(he)
+        qe, se = qmid(he)
         h[lo:hi], midq[lo:hi], mids[lo:hi] = he, qe, se
-        y[entries] = down(qe, se, dequant_mxfp4(w2[e], s2[e]))
+        y[entries] = dmid(qe, se, dequant_mxfp4(w2[e], s2[e]))
     ys, sh = (None, None)
     if shared is not None:
         ys, sh = shared_expert(x_bits, *shared)
@@ -259,14 +294,15 @@ def moe_forward(x_bits, logits, w13, s13, w2, s2, top_k, scaling, shared=None):
             "out": out}
 
 
-def expert_dense(xd: np.ndarray, w13e, s13e, w2e, s2e, I: int) -> np.ndarray:
+def expert_dense(xd: np.ndarray, w13e, s13e, w2e, s2e, I: int, mid_format="e4m3") -> np.ndarray:
     """One expert applied to every row of xd (steps 4-6): [r, H] -> [r, H] fp32."""
+    qmid, dmid = _mid_steps(mid_format)
     h = gate_up(xd, dequant_mxfp4(w13e, s13e), I)
-    q, s = quantize_mid(h)
-    return down(q, s, dequant_mxfp4(w2e, s2e))
+    q, s = qmid(h)
+    return dmid(q, s, dequant_mxfp4(w2e, s2e))
 
 
-def moe_dense(x_bits, logits, w13, s13, w2, s2, top_k, scaling, shared=None):
+def moe_dense(x_bits, logits, w13, s13, w2, s2, top_k, scaling, shared=None, mid_format="e4m3"):
     """Brute force: every expert on every token, then masked by the routing.
 
     Shares the per-expert arithmetic with moe_forward but none of its
@@ -278,7 +314,7 @@ def moe_dense(x_bits, logits, w13, s13, w2, s2, top_k, scaling, shared=None):
     ids, w = route(logits, top_k, scaling)
     xq, xs = quantize_x(x_bits)
     xd = F.mx_fp4_decode(xq, xs, 32)
-    all_y = np.stack([expert_dense(xd, w13[e], s13[e], w2[e], s2[e], I) for e in range(E)])
+    all_y = np.stack([expert_dense(xd, w13[e], s13[e], w2[e], s2[e], I, mid_format) for e in range(E)])
     y = np.zeros((M, top_k, H), np.float32)
     for t in range(M):
         for j in range(top_k):

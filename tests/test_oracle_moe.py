@@ -236,3 +236,75 @@ def test_page_mid_block_arithmetic():
         nbytes = q.size * q.itemsize + s.size * s.itemsize
         assert round(nbytes / 1000) == kb_fp8
         assert round(h.size * 4 / 1000) == kb_f32
+
+
+# ------------------------------------------------------------ MXFP4 mid (the comparison arm)
+def _grid_mid(rng, r, I):
+    """Mid rows on the MXFP4 grid: random E2M1 codes and E8M0 scales per 32,
+    each block holding a +-6 so that the MX rule recovers its scale."""
+    codes = rng.integers(0, 16, size=(r, I)).astype(np.uint8)
+    codes[:, ::32] = np.where(rng.integers(0, 2, size=(r, I // 32)) == 1, 15, 7)
+    sc = rng.integers(118, 136, size=(r, I // 32)).astype(np.uint8)
+    return codes, sc, F.mx_fp4_decode(codes, sc).astype(np.float32)
+
+
+def test_mx_mid_on_grid_round_trips():
+    rng = np.random.default_rng(11)
+    codes, sc, h = _grid_mid(rng, 5, 256)
+    q, s = O.quantize_mid_mx(h)
+    assert np.array_equal(s, sc)
+    assert np.array_equal(q, codes)  # signs of zeros included
+    # amax 4 * 2^e picks the same scale as 6 * 2^e (floor(log2) - 2)
+    h4 = np.zeros((1, 32), np.float32)
+    h4[0, 3] = -4.0 * 2.0 ** -5
+    q4, s4 = O.quantize_mid_mx(h4)
+    assert s4[0, 0] == 127 - 5 and q4[0, 3] == 8 | 6
+
+
+def test_mx_down_brute_force_fractions():
+    """y[r, n] = fl32(sum_i mid[r, i] * w2[n, i]), summed exactly with Fractions
+    on a tiny case with a different scale in every 32-block of both operands."""
+    from fractions import Fraction
+    rng = np.random.default_rng(12)
+    r, H, I = 3, 4, 128
+    codes, sc, _ = _grid_mid(rng, r, I)
+    wc = rng.integers(0, 16, size=(H, I)).astype(np.uint8)
+    ws = rng.integers(117, 124, size=(H, I // 32)).astype(np.uint8)
+    w2d = O.dequant_mxfp4(F.pack_fp4(wc), ws)
+    y = O.down_mx(codes, sc, w2d)
+    mag = [0, 1, 2, 3, 4, 6, 8, 12]  # E2M1 magnitudes times 2
+
+    def val(c, e):
+        v = Fraction(mag[c & 7], 2) * Fraction(2) ** (int(e) - 127)
+        return -v if c & 8 else v
+
+    for a in range(r):
+        for n in range(H):
+            tot = sum(val(codes[a, i], sc[a, i // 32]) * val(wc[n, i], ws[n, i // 32]) for i in range(I))
+            assert float(tot) == float(Fraction(float(tot)))  # exact in float64 here
+            assert y[a, n] == np.float32(float(tot)), (a, n)
+
+
+@pytest.mark.parametrize("M,E,k,kind", [(4, 16, 2, "normal"), (8, 16, 4, "ties"), (3, 4, 4, "uniform")])
+def test_mx_mid_dense_equals_sparse(M, E, k, kind):
+    shape = X.Shape(M=M, H=512, E=E, I=128, top_k=k)
+    d = X.make_inputs(shape, kind, 17)
+    sparse = _run(d, mid_format="mxfp4")
+    assert sparse["midq"].shape == (M * k, 128) and sparse["mids"].shape == (M * k, 4)
+    assert sparse["mids"].dtype == np.uint8
+    assert np.array_equal(sparse["out"], _run(d, fn=O.moe_dense, mid_format="mxfp4"))
+
+
+def test_mx_mid_invariants():
+    d = X.make_inputs("c0")
+    out = _run(d, x_bits=np.zeros_like(d["x"]), mid_format="mxfp4")["out"]
+    assert np.all(F.bf16_decode(out) == 0)
+    p = np.array([2, 0, 3, 1])
+    a = _run(d, mid_format="mxfp4")["out"]
+    b = _run(d, x_bits=d["x"][p], logits=d["logits"][p], mid_format="mxfp4")["out"]
+    assert np.array_equal(a[p], b)
+    # the E4M3 and MXFP4 arms share routing, sort, x and h, and differ after
+    r8, r4 = _run(d), _run(d, mid_format="mxfp4")
+    for key in ("ids", "sorted_entry", "xq", "h"):
+        assert np.array_equal(r8[key], r4[key])
+    assert not np.array_equal(r8["out"], r4["out"])
