@@ -80,11 +80,11 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measure(name, steps, warmup, n_sets):
+def measure(name, steps, warmup, n_sets, mid_fmt=0):
     import torch
 
     from quantized_moe_expert_route_amd import fixtures as X
-    from quantized_moe_expert_route_amd.binding import HipEvents, Plan, pack_w13, stage_names
+    from quantized_moe_expert_route_amd.binding import HipEvents, Plan, pack_w13, pack_w2, stage_names
 
     wl = X.WORKLOADS[name]
     s = wl.shape
@@ -92,6 +92,8 @@ def measure(name, steps, warmup, n_sets):
     base = X.make_inputs(name)
     t = {k: torch.from_numpy(base[k]).to(dev) for k in ("w13", "s13", "w2", "s2")}
     t["w13"], t["s13"] = pack_w13(t["w13"], t["s13"])  # load-time packing, outside the timed calls
+    if mid_fmt:
+        t["w2"], t["s2"] = pack_w2(t["w2"], t["s2"])  # the MXFP4-mid down reads packed down weights
     torch.cuda.synchronize()
     sets = []
     for i in range(n_sets):
@@ -101,6 +103,7 @@ def measure(name, steps, warmup, n_sets):
     if s.shared_I:
         sh = [torch.from_numpy(base[k]).to(dev) for k in ("ws13", "ss13", "ws2", "ss2")]
         plan.set_shared(*sh)
+    plan.set_mid_format(mid_fmt)
     x = torch.empty_like(sets[0][0])
     logits = torch.empty_like(sets[0][1])
     out = torch.empty((s.M, s.H), dtype=torch.int16, device=dev)
@@ -264,6 +267,9 @@ def main():
     ap.add_argument("--also", default="c2,c3,c4,m256_hot,m256_mixed",
                     help="more workloads reported in the same line ('' for none); mid-range batches are "
                          "m{32,64,128,256}_{hot,mixed,spread}")
+    ap.add_argument("--mxfp4", default="m256_hot,m256_mixed",
+                    help="workloads also timed with the MXFP4 mid hand-off (the pages' stock MXFP4 comparison "
+                         "arm), reported as '<name>/mxfp4'; up to 256 tokens ('' for none)")
     ap.add_argument("--sets", type=int, default=8, help="distinct input batches cycled through the steps")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -294,9 +300,12 @@ def main():
           f"warm {head['warm_us']:.1f} us, "
           f"stages {json.dumps({k: round(v, 1) for k, v in head['stage_us'].items()})}", file=sys.stderr, flush=True)
     others = {}
-    for name in [c for c in args.also.split(",") if c and c != args.config]:
-        r = measure(name, max(10, args.steps // 2), max(3, args.warmup // 2), min(args.sets, 4))
+    runs = [(c, 0) for c in args.also.split(",") if c and c != args.config]
+    runs += [(c, 1) for c in args.mxfp4.split(",") if c]
+    for name, fmt in runs:
+        r = measure(name, max(10, args.steps // 2), max(3, args.warmup // 2), min(args.sets, 4), mid_fmt=fmt)
         mu = r["cold_us"].mean()
+        name = f"{name}/mxfp4" if fmt else name
         others[name] = {
             "us_per_call_cold": round(mu, 2), "us_per_call_graph_replay": round(float(r["graph_us"].mean()), 2),
             "us_per_call_warm": round(r["warm_us"], 2),

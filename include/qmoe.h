@@ -128,6 +128,24 @@ moe_status moe_plan_set_workspace(moe_plan* plan, void* workspace, size_t bytes,
 moe_status moe_plan_set_shared(moe_plan* plan, const void* ws13, const float* ss13,
                                const void* ws2, const float* ss2);
 
+/* Format of the mid hand-off between gate/up and down. MOE_MID_E4M3 (the
+ * default): one E4M3 code per element and an fp32 scale per 128 ("glm53: FP8
+ * mid hand-off, early split rows, ...", Modifications table, row "mid as FP8
+ * once"), down on exact bf16 products. MOE_MID_MXFP4: the comparison arm the
+ * pages time against IQ2R, stock experts quantized online to MXFP4 ("IQ2R:
+ * load GLM-5.3 packed MoE checkpoints with TP slicing", Results (MXFP4 vs
+ * IQ2R)), read as FP4 activations in both GEMMs: mid per 32 as E2M1 codes
+ * with an E8M0 scale (the rule x takes), down on the scaled FP4 MFMA. With
+ * MXFP4, moe_forward's w2 and s2 are the packed ones of moe_pack_w2, the
+ * workspace's midq holds [n, I/2] codes (element 2i in the low nibble) and
+ * mids [n, I/32] scale bytes, rows in sorted order, y is written for every
+ * M, and moe_forward returns MOE_ERR_UNSUPPORTED for M > 256. */
+typedef enum { MOE_MID_E4M3 = 0, MOE_MID_MXFP4 = 1 } moe_mid_format;
+
+/* Select the mid format for the plan's later calls. MOE_ERR_INVALID_ARG for
+ * a NULL plan or an unknown format. Host-only. */
+moe_status moe_plan_set_mid_format(moe_plan* plan, int format);
+
 /* Rewrite the routed experts' gate/up weights into the packed layout that
  * moe_forward reads, once, when the weights are loaded (the MoE method of
  * "IQ2R: load GLM-5.3 packed MoE checkpoints with TP slicing", Summary,
@@ -152,14 +170,30 @@ moe_status moe_plan_set_shared(moe_plan* plan, const void* ws13, const float* ss
 moe_status moe_pack_w13(const void* w13, const void* s13, int64_t E, int64_t I, int64_t H,
                         void* w13_packed, void* s13_packed, void* stream);
 
+/* Rewrite the routed experts' down weights for the MXFP4-mid down
+ * (MOE_MID_MXFP4 only; the E4M3 mid reads them row-major), once, at load
+ * time. Inputs, row-major: w2 u8 MXFP4 [E, H, I/2] along I, s2 u8 E8M0
+ * [E, H, I/32]. Outputs, caller-allocated device buffers:
+ *   w2_packed [E*H/16][I/128][4][16][16] (the size of w2): bytes 16*g ..
+ *     16*g + 15 of K-step ks of row 16*rb + r at
+ *     (((rb * I/128 + ks) * 4 + g) * 16 + r) * 16
+ *   s2_packed [E*H/16][4][16][4] (E*H*16 bytes): byte ks of the dword at
+ *     (rb * 4 + g) * 16 + r holds the scale of MX block 4*ks + g of row
+ *     16*rb + r for ks < I/128, zero above
+ * (rows are the E*H output columns, experts one after another). A byte
+ * permutation: nothing is rounded. Validation and errors as moe_pack_w13. */
+moe_status moe_pack_w2(const void* w2, const void* s2, int64_t E, int64_t I, int64_t H,
+                       void* w2_packed, void* s2_packed, void* stream);
+
 /* The routed-MoE call on M tokens (0 <= M <= shape.M; M = 0 enqueues nothing):
  *   x      bf16 [M, H]
  *   logits fp32 [M, E]     (finite or -inf)
  *   w13    gate/up weights in the packed layout of moe_pack_w13 (the
  *          MXFP4 [E, 2I, H/2] rows [0, I) gate, [I, 2I) up, along H)
  *   s13    their E8M0 scales, packed by moe_pack_w13 ([E, 2I, H/32])
- *   w2     u8 MXFP4 [E, H, I/2]    along I, row-major
- *   s2     u8 E8M0  [E, H, I/32]
+ *   w2     u8 MXFP4 [E, H, I/2]    along I, row-major (packed by
+ *          moe_pack_w2 when the plan's mid format is MOE_MID_MXFP4)
+ *   s2     u8 E8M0  [E, H, I/32]   (packed likewise)
  *   out    bf16 [M, H]  fully overwritten; must not alias any input
  * Returns after enqueueing; faults inside kernels surface at the caller's
  * next synchronisation. MOE_ERR_WORKSPACE if no workspace is bound,

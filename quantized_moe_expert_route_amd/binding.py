@@ -15,6 +15,7 @@ from typing import Dict, Optional
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libqmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE, MOE_ERR_HIP = range(6)
+MID_E4M3, MID_MXFP4 = 0, 1  # moe_mid_format
 
 
 class moe_shape(ctypes.Structure):
@@ -78,6 +79,10 @@ def lib() -> ctypes.CDLL:
     L.moe_forward.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp]
     L.moe_pack_w13.restype = st
     L.moe_pack_w13.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp]
+    L.moe_pack_w2.restype = st
+    L.moe_pack_w2.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp]
+    L.moe_plan_set_mid_format.restype = st
+    L.moe_plan_set_mid_format.argtypes = [vp, ctypes.c_int]
     _lib = L
     return L
 
@@ -131,6 +136,24 @@ def pack_w13(w13, s13, out=None, stream=None):
     return wp, sp
 
 
+def pack_w2(w2, s2, out=None, stream=None):
+    """Down weights and scales (row-major MXFP4 [E, H, I/2] and E8M0
+    [E, H, I/32], uint8 device tensors) -> (w2_packed, s2_packed) in the
+    layout the MXFP4-mid down reads (moe_pack_w2); s2_packed is [E, H, 16]."""
+    import torch
+
+    E, H, Ih = w2.shape
+    if tuple(s2.shape) != (E, H, Ih // 16):
+        raise ValueError("w2 must be [E, H, I/2] and s2 [E, H, I/32]")
+    if out is None:
+        out = (torch.empty_like(w2), torch.empty((E, H, 16), dtype=torch.uint8, device=w2.device))
+    wp, sp = out
+    st = lib().moe_pack_w2(_ptr(w2), _ptr(s2), E, 2 * Ih, H, _ptr(wp), _ptr(sp), _stream(stream))
+    if st != MOE_OK:
+        raise MoeError(st, "moe_pack_w2")
+    return wp, sp
+
+
 class Plan:
     """A plan for one shape, owning a device workspace allocated through torch."""
 
@@ -164,6 +187,12 @@ class Plan:
         st = lib().moe_plan_set_shared(self._h, _ptr(ws13), _ptr(ss13), _ptr(ws2), _ptr(ss2))
         if st != MOE_OK:
             raise MoeError(st, "moe_plan_set_shared")
+
+    def set_mid_format(self, fmt: int):
+        """MID_E4M3 (default) or MID_MXFP4 for the plan's later calls."""
+        st = lib().moe_plan_set_mid_format(self._h, int(fmt))
+        if st != MOE_OK:
+            raise MoeError(st, "moe_plan_set_mid_format")
 
     def set_stage_events(self, events):
         """events: raw hipEvent_t handles (ints), [start0, stop0, start1, stop1, ...]

@@ -142,14 +142,16 @@ int moe_plan_stage_launches(const moe_plan* plan, int64_t M, int stage) {
   if (!plan || M < 0 || M > plan->s.M || stage < 0 || stage >= kStages) return -1;
   if (M == 0) return 0;
   const bool small = small_path(M, plan->s.top_k);
+  const bool mx = plan->mid_fmt == MOE_MID_MXFP4;
+  if (mx && !mid_path(M, plan->s.top_k)) return -1;  // not served
   switch (stage) {
     case 0: return 1;                             // route + x quantization (+ sort when small; + the shared expert's x when large)
     case 1: return small ? 0 : 3;                 // align
     case 2: return 1;                             // gate_up (+ mid quantization when large)
     case 3: return mid_path(M, plan->s.top_k) ? 1 : 0;  // act_quant (inside gate/up above kMidM)
     case 4: return plan->s.shared_I > 0 ? (small ? 4 : 3) : 0;  // shared expert
-    case 5: return 1;                             // down (+ combine when small)
-    default: return small ? 0 : 1;                // combine
+    case 5: return 1;                             // down (+ combine when small, E4M3 mid)
+    default: return small && !mx ? 0 : 1;         // combine
   }
 }
 
@@ -234,6 +236,12 @@ moe_status moe_plan_set_shared(moe_plan* plan, const void* ws13, const float* ss
   return MOE_OK;
 }
 
+moe_status moe_plan_set_mid_format(moe_plan* plan, int format) {
+  if (!plan || (format != MOE_MID_E4M3 && format != MOE_MID_MXFP4)) return MOE_ERR_INVALID_ARG;
+  plan->mid_fmt = format;
+  return MOE_OK;
+}
+
 moe_status moe_plan_set_stage_events(moe_plan* plan, void* const* events, int n) {
   if (!plan) return MOE_ERR_INVALID_ARG;
   if (!events) {
@@ -282,6 +290,28 @@ moe_status moe_pack_w13(const void* w13, const void* s13, int64_t E, int64_t I, 
              : MOE_ERR_HIP;
 }
 
+moe_status moe_pack_w2(const void* w2, const void* s2, int64_t E, int64_t I, int64_t H, void* w2_packed,
+                       void* s2_packed, void* stream) {
+  if (!w2 || !s2 || !w2_packed || !s2_packed) return MOE_ERR_INVALID_ARG;
+  if (E <= 0 || I <= 0 || H <= 0) return MOE_ERR_INVALID_ARG;
+  if (H % 512 != 0 || I % 128 != 0 || I > 512 || E > 1024 || H > 65536) return MOE_ERR_UNSUPPORTED;
+  const void* ptrs[4] = {w2, s2, w2_packed, s2_packed};
+  for (const void* q : ptrs)
+    if (!aligned16(q)) return MOE_ERR_INVALID_ARG;
+  const size_t wb = (size_t)E * H * (I / 2), sb = (size_t)E * H * (I / 32), spb = (size_t)E * H * 16;
+  if (overlaps(w2_packed, wb, w2, wb) || overlaps(w2_packed, wb, s2, sb) || overlaps(s2_packed, spb, w2, wb) ||
+      overlaps(s2_packed, spb, s2, sb) || overlaps(w2_packed, wb, s2_packed, spb))
+    return MOE_ERR_INVALID_ARG;
+  const int dev = ptr_device(w2);
+  if (dev < 0) return MOE_ERR_DEVICE;
+  for (const void* q : ptrs)
+    if (ptr_device(q) != dev) return MOE_ERR_DEVICE;
+  DeviceGuard guard(dev);
+  if (!guard.ok) return MOE_ERR_DEVICE;
+  return launch_pack_w2(w2, s2, E, I, H, w2_packed, s2_packed, (hipStream_t)stream) == hipSuccess ? MOE_OK
+                                                                                               : MOE_ERR_HIP;
+}
+
 moe_status moe_forward(moe_plan* plan, int64_t M, const void* x, const float* logits, const void* w13,
                        const void* s13, const void* w2, const void* s2, void* out, void* stream) {
   if (!plan) return MOE_ERR_INVALID_ARG;
@@ -289,6 +319,8 @@ moe_status moe_forward(moe_plan* plan, int64_t M, const void* x, const float* lo
   if (!plan->ws) return MOE_ERR_WORKSPACE;
   if (plan->s.shared_I > 0 && !plan->ws13) return MOE_ERR_INVALID_ARG;
   if (M == 0) return MOE_OK;
+  const bool mx = plan->mid_fmt == MOE_MID_MXFP4;
+  if (mx && !mid_path(M, plan->s.top_k)) return MOE_ERR_UNSUPPORTED;
   const void* ptrs[7] = {x, logits, w13, s13, w2, s2, out};
   for (const void* q : ptrs)
     if (!q || !aligned16(q)) return MOE_ERR_INVALID_ARG;
@@ -304,12 +336,13 @@ moe_status moe_forward(moe_plan* plan, int64_t M, const void* x, const float* lo
   if (!guard.ok) return MOE_ERR_DEVICE;
   CallArgs a{M, x, logits, w13, s13, w2, s2, out, (hipStream_t)stream};
   const bool small = small_path(M, plan->s.top_k);
+  const bool fused_combine = small && !mx;  // down and combine in one launch
   Ev ev[kStages];
   if (plan->n_events)
     for (int i = 0; i < kStages; ++i) ev[i] = Ev{plan->events[2 * i], plan->events[2 * i + 1]};
   if (plan->call_start) {
     ev[0].start = plan->call_start;             // the route launch comes first
-    ev[small ? 5 : 6].stop = plan->call_stop;   // down (+ combine) or the combine comes last
+    ev[fused_combine ? 5 : 6].stop = plan->call_stop;  // down (+ combine) or the combine comes last
   }
   // a stage with no launch of its own still records its (empty) interval
   auto none = [&](int i) -> hipError_t {
@@ -322,8 +355,11 @@ moe_status moe_forward(moe_plan* plan, int64_t M, const void* x, const float* lo
   // tiles; the mid quantization; down with the combine (a workgroup owns 16
   // output columns of every slot, so the slot results never leave it).
   // Above kSmallM: routing spread over the GPU, a second launch sorts;
-  // gate/up on 128-row tiles with the mid quantization inside (every item
-  // owns whole mid blocks); down to y in HBM; the combine.
+  // gate/up on 16-row tiles and the mid quantization up to kMidM tokens,
+  // above on 64-row tiles with the mid quantization inside (every item owns
+  // whole mid blocks); down to y in HBM; the combine.
+  // With the MXFP4 mid (up to kMidM tokens): its own quantization and down
+  // kernel on the 16-row tiles, then the combine, for every M.
   // A stage is never folded into its producer through a last-arriver
   // counter: the device-scope release/acquire that needs writes back and
   // invalidates a whole L2 of an XCD per workgroup and costs more than a
@@ -332,10 +368,12 @@ moe_status moe_forward(moe_plan* plan, int64_t M, const void* x, const float* lo
   if (e == hipSuccess) e = small ? none(1) : launch_align(plan, a, ev[1]);
   const bool tiles16 = mid_path(M, plan->s.top_k);  // 16-row-tile gate/up, mid quantization on its own
   if (e == hipSuccess) e = tiles16 ? launch_gate_up(plan, a, ev[2]) : launch_gate_up_big(plan, a, ev[2]);
-  if (e == hipSuccess) e = tiles16 ? launch_act_quant(plan, a, ev[3]) : none(3);
+  if (e == hipSuccess)
+    e = mx ? launch_act_quant_mx(plan, a, ev[3]) : tiles16 ? launch_act_quant(plan, a, ev[3]) : none(3);
   if (e == hipSuccess) e = plan->s.shared_I > 0 ? launch_shared(plan, a, ev[4]) : none(4);
-  if (e == hipSuccess) e = small ? launch_down_combine(plan, a, ev[5]) : launch_down_big(plan, a, ev[5]);
-  if (e == hipSuccess) e = small ? none(6) : launch_combine(plan, a, ev[6]);
+  if (e == hipSuccess)
+    e = mx ? launch_down_fp4(plan, a, ev[5]) : small ? launch_down_combine(plan, a, ev[5]) : launch_down_big(plan, a, ev[5]);
+  if (e == hipSuccess) e = fused_combine ? none(6) : launch_combine(plan, a, ev[6]);
   return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

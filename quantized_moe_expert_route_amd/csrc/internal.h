@@ -51,6 +51,7 @@ struct moe_plan {
   hipEvent_t events[16];
   int n_events;
   hipEvent_t call_start, call_stop;
+  int mid_fmt;     // moe_mid_format
 };
 
 namespace qmoe {
@@ -102,6 +103,10 @@ hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t s);
 // row-major MXFP4 gate/up weights and scales -> the packed layout (pack.hip)
 hipError_t launch_pack_w13(const void* w13, const void* s13, int64_t E, int64_t I, int64_t H, void* w13p, void* s13p,
                            hipStream_t stream);
+// row-major MXFP4 down weights and scales -> the packed layout of the
+// MXFP4-mid down (pack.hip)
+hipError_t launch_pack_w2(const void* w2, const void* s2, int64_t E, int64_t I, int64_t H, void* w2p, void* s2p,
+                          hipStream_t stream);
 // Small M (<= kSmallM): route + sort + x quantization in one workgroup.
 hipError_t launch_route_small(const moe_plan* p, const CallArgs& a, Ev ev);
 hipError_t launch_route(const moe_plan* p, const CallArgs& a, Ev ev);
@@ -117,5 +122,9 @@ hipError_t launch_shared(const moe_plan* p, const CallArgs& a, Ev ev);
 hipError_t launch_gate_up_big(const moe_plan* p, const CallArgs& a, Ev ev);
 hipError_t launch_down_big(const moe_plan* p, const CallArgs& a, Ev ev);
 hipError_t launch_combine(const moe_plan* p, const CallArgs& a, Ev ev);
+// MXFP4 mid hand-off (a4w4.hip): mid per 32 as E2M1 + E8M0; down on the
+// scaled FP4 MFMA over 16-row tiles, y to HBM
+hipError_t launch_act_quant_mx(const moe_plan* p, const CallArgs& a, Ev ev);
+hipError_t launch_down_fp4(const moe_plan* p, const CallArgs& a, Ev ev);
 
 }  // namespace qmoe

@@ -52,6 +52,39 @@ __global__ __launch_bounds__(256) void pack_s13_kernel(const uint8_t* __restrict
   }
 }
 
+// Down weights for the MXFP4-mid down (rows are output columns, K = I <= 512,
+// so at most four K-steps): dword d of row block rb holds, for lane (g, r),
+// the scale bytes of MX blocks 4 ks + g of row 16 rb + r in byte ks, ks <
+// nks; the other bytes are zero.
+__global__ __launch_bounds__(256) void pack_s2_kernel(const uint8_t* __restrict__ s, uint32_t* __restrict__ sp,
+                                                      int64_t dwords, int nks, int64_t row_bytes) {
+  for (int64_t d = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; d < dwords; d += (int64_t)gridDim.x * blockDim.x) {
+    const int r = (int)(d & 15), g = (int)((d >> 4) & 3);
+    const int64_t rb = d >> 6;
+    const uint8_t* src = s + (rb * 16 + r) * row_bytes + g;
+    uint32_t v = 0;
+    for (int ks = 0; ks < nks; ++ks) v |= (uint32_t)src[4 * ks] << (8 * ks);
+    sp[d] = v;
+  }
+}
+
+hipError_t launch_pack_w2(const void* w2, const void* s2, int64_t E, int64_t I, int64_t H, void* w2p, void* s2p,
+                          hipStream_t stream) {
+  const int64_t rows = E * H;
+  const int64_t units = rows * (I / 32);  // 16-byte units of w2
+  const int64_t dwords = rows * 4;        // one dword per lane per 16-row block
+  auto blocks = [](int64_t n) { return (int)std::min<int64_t>((n + 255) / 256, 65536); };
+  hipLaunchKernelGGL(pack_w13_kernel, dim3(blocks(units)), dim3(256), 0, stream,
+                     reinterpret_cast<const uint8_t*>(w2), reinterpret_cast<uint8_t*>(w2p), units, (int)(I / 128),
+                     I / 2);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(pack_s2_kernel, dim3(blocks(dwords)), dim3(256), 0, stream,
+                     reinterpret_cast<const uint8_t*>(s2), reinterpret_cast<uint32_t*>(s2p), dwords, (int)(I / 128),
+                     I / 32);
+  return hipGetLastError();
+}
+
 hipError_t launch_pack_w13(const void* w13, const void* s13, int64_t E, int64_t I, int64_t H, void* w13p, void* s13p,
                            hipStream_t stream) {
   const int64_t rows = E * 2 * I;

@@ -84,6 +84,7 @@ def test_null_and_unbound_arguments_fail_before_any_device_work():
     assert L.moe_plan_layout(None, None) == B.MOE_ERR_INVALID_ARG
     assert L.moe_plan_set_stage_events(None, None, 0) == B.MOE_ERR_INVALID_ARG
     assert L.moe_plan_workspace_bytes(None) == 0
+    assert L.moe_plan_set_mid_format(None, B.MID_MXFP4) == B.MOE_ERR_INVALID_ARG
     L.moe_plan_destroy(None)
 
 
@@ -99,6 +100,12 @@ def test_pack_w13_validates_before_any_device_work():
     assert L.moe_pack_w13(a + 8, b, 4, 128, 512, c, d, None) == B.MOE_ERR_INVALID_ARG  # misaligned
     # the packed weights would overlap the input
     assert L.moe_pack_w13(a, b, 4, 128, 512, a + 256, d, None) == B.MOE_ERR_INVALID_ARG
+    # the down-weight packing validates the same way
+    assert L.moe_pack_w2(None, b, 4, 128, 512, c, d, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_w2(a, b, 4, 128, 640, c, d, None) == B.MOE_ERR_UNSUPPORTED
+    assert L.moe_pack_w2(a, b, 4, 640, 512, c, d, None) == B.MOE_ERR_UNSUPPORTED    # I > 512
+    assert L.moe_pack_w2(a, b + 4, 4, 128, 512, c, d, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_w2(a, b, 4, 128, 512, c, a + 16, None) == B.MOE_ERR_INVALID_ARG  # overlap
 
 
 def test_plan_needs_a_gfx950_device():

@@ -52,3 +52,49 @@ def test_expected_layout_places_a_known_byte():
     rb, r = (e * 2 * I + row) // 16, row % 16
     assert ew[(((rb * (H // 128) + ks) * 4 + g) * 16 + r) * 16 + b] == 7 and ew.sum() == 7
     assert es[(((rb * (H // 512) + kq) * 4 + gs) * 16 + r) * 4 + j] == 9 and es.sum() == 9
+
+
+def expected_packed_w2(w2, s2):
+    """w2 [E, H, I/2] -> [E*H/16][I/128][4 g][16 r][16 B];
+    s2 [E, H, I/32] -> [E*H/16][4 g][16 r][4 ks], byte ks of (g, r) being MX
+    block 4 ks + g of the row for ks < I/128, zero above."""
+    E, H, Ib = w2.shape
+    nrb, nks = E * H // 16, Ib // 64
+    wp = w2.reshape(nrb, 16, nks, 4, 16).transpose(0, 2, 3, 1, 4)
+    sp = np.zeros((nrb, 4, 16, 4), np.uint8)
+    sp[..., :nks] = s2.reshape(nrb, 16, nks, 4).transpose(0, 3, 1, 2)
+    return np.ascontiguousarray(wp).ravel(), sp.ravel()
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("E,I,H", [(3, 128, 512), (2, 384, 1536), (5, 256, 1024), (2, 512, 512)])
+def test_pack_w2_is_the_documented_permutation(E, I, H):
+    import torch
+
+    from quantized_moe_expert_route_amd.binding import pack_w2
+
+    rng = np.random.default_rng(E * 999 + I + H)
+    w2 = rng.integers(0, 256, (E, H, I // 2), dtype=np.uint8)
+    s2 = rng.integers(0, 256, (E, H, I // 32), dtype=np.uint8)
+    dev = torch.device("cuda", 0)
+    wt, st = torch.from_numpy(w2).to(dev), torch.from_numpy(s2).to(dev)
+    wp, sp = pack_w2(wt, st)
+    torch.cuda.synchronize()
+    ew, es = expected_packed_w2(w2, s2)
+    np.testing.assert_array_equal(wp.cpu().numpy().ravel(), ew)
+    np.testing.assert_array_equal(sp.cpu().numpy().ravel(), es)
+    np.testing.assert_array_equal(wt.cpu().numpy(), w2)
+    np.testing.assert_array_equal(st.cpu().numpy(), s2)
+
+
+def test_expected_w2_layout_places_a_known_byte():
+    E, I, H = 2, 256, 512
+    w2 = np.zeros((E, H, I // 2), np.uint8)
+    s2 = np.zeros((E, H, I // 32), np.uint8)
+    e, row, ks, g, b = 1, 300, 1, 3, 11    # byte 64 ks + 16 g + b of output column `row`
+    w2[e, row, 64 * ks + 16 * g + b] = 5
+    s2[e, row, 4 * ks + g] = 6             # MX block 4 ks + g
+    ew, es = expected_packed_w2(w2, s2)
+    rb, r = (e * H + row) // 16, row % 16
+    assert ew[(((rb * (I // 128) + ks) * 4 + g) * 16 + r) * 16 + b] == 5 and ew.sum() == 5
+    assert es[((rb * 4 + g) * 16 + r) * 4 + ks] == 6 and es.sum() == 6
