@@ -146,7 +146,7 @@ int moe_plan_stage_launches(const moe_plan* plan, int64_t M, int stage) {
   if (mx && !mid_path(M, plan->s.top_k)) return -1;  // not served
   switch (stage) {
     case 0: return 1;                             // route + x quantization (+ sort when small; + the shared expert's x when large)
-    case 1: return small ? 0 : 3;                 // align
+    case 1: return small ? 0 : mid_path(M, plan->s.top_k) ? 1 : 3;  // align
     case 2: return 1;                             // gate_up (+ mid quantization when large)
     case 3: return mid_path(M, plan->s.top_k) ? 1 : 0;  // act_quant (inside gate/up above kMidM)
     case 4: return plan->s.shared_I > 0 ? (small ? 4 : 3) : 0;  // shared expert

@@ -439,6 +439,56 @@ __global__ __launch_bounds__(256) void align_place_kernel(const int* __restrict_
     dn_items[i] = big_item(i, E, n_nc, kBigRows, s_toff[1], s_off);
 }
 
+// The sort for kSmallM < M <= kMidM in one workgroup (the token bitmap has
+// at most kMidM / 32 words a row, so the whole of it fits in LDS): the
+// bitmap is read once and left zero, an expert's count is the popcount of
+// its row, the offsets and the 16-row tiles come from one scan, and an
+// entry's place is its expert's offset plus the popcount of the row below
+// its token; the down work items (tiles of kBigRows rows) follow from a
+// second scan. Same results as the three-launch sort.
+constexpr int kMidWords = kMidM / 32;
+__global__ __launch_bounds__(1024) void align_mid_kernel(uint32_t* __restrict__ bitmap, int words,
+                                                         const int* __restrict__ topk_ids, int n, int k, int E,
+                                                         int* __restrict__ count, int* __restrict__ offset,
+                                                         int* __restrict__ sorted_entry, int4* __restrict__ tiles,
+                                                         int* __restrict__ meta, int n_nc, int4* __restrict__ dn_items) {
+  __shared__ uint32_t s_bm[1024 * kMidWords];
+  __shared__ int s_off[1025];
+  __shared__ int s_toff[1025];
+  __shared__ int s_tmp[64];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < E * words; i += 1024) {
+    const uint32_t v = bitmap[i];
+    s_bm[i] = v;
+    if (v) bitmap[i] = 0u;
+  }
+  __syncthreads();
+  int c = 0;
+  if (tid < E)
+    for (int w = 0; w < words; ++w) c += __popc(s_bm[tid * words + w]);
+  write_offsets_tiles(c, E, s_off, s_tmp, count, offset, tiles, meta, true);  // ends with a barrier
+  int n_tb;
+  const int tb = (c + kBigRows - 1) / kBigRows;
+  const int t0 = block_exclusive_scan(tb, s_tmp, &n_tb);
+  if (tid < E) s_toff[tid] = t0;
+  if (tid == 0) {
+    s_off[E] = n;
+    s_toff[E] = n_tb;
+    meta[1] = 0;
+    meta[2] = n_tb * n_nc;
+  }
+  __syncthreads();
+  for (int i = tid; i < n; i += 1024) {
+    const int e = topk_ids[i], t = i / k;
+    const uint32_t* row = s_bm + e * words;
+    int rank = __popc(row[t >> 5] & ((1u << (t & 31)) - 1u));
+    for (int w = 0; w < (t >> 5); ++w) rank += __popc(row[w]);
+    sorted_entry[s_off[e] + rank] = i;
+  }
+  const int n_dn = n_tb * n_nc;
+  for (int i = tid; i < n_dn; i += 1024) dn_items[i] = big_item(i, E, n_nc, kBigRows, s_toff, s_off);
+}
+
 __global__ void zero_kernel(uint4* p, size_t n16) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
     p[i] = make_uint4(0, 0, 0, 0);
@@ -496,6 +546,11 @@ hipError_t launch_route(const moe_plan* p, const CallArgs& a, Ev ev) {
 hipError_t launch_align(const moe_plan* p, const CallArgs& a, Ev ev) {
   const int words = (int)((a.M + 31) / 32);
   const int64_t n = a.M * p->s.top_k;
+  if (mid_path(a.M, p->s.top_k))
+    return launch_k(align_mid_kernel, dim3(1), dim3(1024), 0, a.stream, ev, wsp<uint32_t>(p, p->X.bitmap), words,
+                    wsp<int>(p, p->L.topk_ids), (int)n, (int)p->s.top_k, (int)p->s.E, wsp<int>(p, p->L.count),
+                    wsp<int>(p, p->L.offset), wsp<int>(p, p->L.sorted_entry), wsp<int4>(p, p->X.tiles),
+                    wsp<int>(p, p->X.meta), (int)(p->s.H / kDownItemCols), wsp<int4>(p, p->X.dn_items));
   hipError_t e = launch_k(align_rows_kernel, dim3((unsigned)p->s.E), dim3(256), 0, a.stream, Ev{ev.start, nullptr},
                           wsp<uint32_t>(p, p->X.bitmap), words, wsp<int2>(p, p->X.pw), wsp<int>(p, p->L.count));
   if (e != hipSuccess) return e;
