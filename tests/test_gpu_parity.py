@@ -326,3 +326,40 @@ def test_variable_m_across_paths_one_plan():
         _check_routing(gi, ref["ids"], ref["w"], ref["count"], ref["offset"], ref["sorted_entry"])
         _check_mid(gi["midq"], gi["mids"], ref["midq"], ref["mids"])
         assert np.array_equal(gout, ref["out"]), f"M={M}: output differs"
+
+
+@pytest.mark.parametrize("name,n_tok", [("c3", 6), ("c4", 6)])
+def test_stage_isolated_full_size(name, n_tok):
+    """Each late stage fed the GPU's own inputs, at the benchmark's sizes: the
+    oracle's down on the GPU's mid rows against the GPU's y, the oracle's
+    combine on the GPU's y (and shared-expert y) against the GPU's output, and
+    at c4 the oracle's shared down on the GPU's shared mid. This separates a
+    stage's own error from differences it inherits (a mid code one E4M3 step
+    off moves every output of its token)."""
+    d = X.make_inputs(name)
+    s = d["shape"]
+    k, H = s.top_k, s.H
+    gout, gi = run(d)
+    tokens = np.sort(np.random.default_rng(77).choice(s.M, n_tok, replace=False))
+    ent = (tokens[:, None] * k + np.arange(k)[None, :]).ravel()
+    pos = np.empty(s.M * k, np.int64)
+    pos[gi["sorted_entry"]] = np.arange(s.M * k)  # sorted row of each entry
+    ids = gi["ids"].ravel()
+    y_ref = np.empty((len(ent), H), np.float32)
+    for i, e_i in enumerate(ent):
+        r, e = pos[e_i], ids[e_i]
+        y_ref[i] = O.down(gi["midq"][r:r + 1], gi["mids"][r:r + 1], O.dequant_mxfp4(d["w2"][e], d["s2"][e]))[0]
+    ydiff = _check_y(gi["y"][ent], y_ref)
+    ys = None
+    if s.shared_I:
+        ys = gi["sh_y"][tokens]
+        ys_ref = O._block_fp8_linear(gi["sh_hq"][tokens], gi["sh_hs"][tokens], d["ws2"], d["ss2"])
+        # E4M3 x E4M3 block sums may need more than binary32's 24 bits inside
+        # the MFMA: fp32-sized differences, never a wrong term
+        err = float(np.max(np.abs(ys.astype(np.float64) - ys_ref)))
+        assert err <= 1e-5 * float(np.max(np.abs(ys_ref))), f"shared down (isolated) off by {err}"
+        sdiff = int(np.count_nonzero(ys.view(np.uint32) != ys_ref.view(np.uint32)))
+        print(f"{name}: shared down (isolated) differs in {sdiff} of {ys_ref.size}, max {err:.3e}")
+    out_ref = O.combine(gi["w"][tokens], gi["y"][ent].reshape(n_tok, k, H), ys)
+    assert np.array_equal(gout[tokens], out_ref), "combine on the GPU's own y differs from the oracle's"
+    print(f"{name}: down (isolated) differs in {ydiff} of {y_ref.size}; combine (isolated) exact")
