@@ -279,32 +279,43 @@ def test_run_to_run_bitwise():
     assert np.array_equal(a, b)
 
 
-def test_graph_replay_matches_eager():
+@pytest.mark.parametrize("name,mxfp4", [("c1", False), ("m64_mixed", False), ("c3", False), ("m256_hot", True)])
+def test_graph_replay_matches_eager(name, mxfp4):
+    """Replays of a captured call (small, mid-range and large paths; the
+    MXFP4 mid) equal the eager call bitwise, with eager calls between them:
+    every call leaves the token bitmap zero for the next."""
     import torch
 
-    d = X.make_inputs("c1")
+    from quantized_moe_expert_route_amd.binding import MID_MXFP4, pack_w2
+
+    d = X.make_inputs(name)
     s = d["shape"]
     g = upload(d)
     plan = make_plan(s)
+    w2, s2 = g["w2"], g["s2"]
+    if mxfp4:
+        plan.set_mid_format(MID_MXFP4)
+        w2, s2 = pack_w2(w2, s2)
+    call = lambda o: plan.forward(g["x"], g["logits"], g["w13"], g["s13"], w2, s2, o)
     eager = torch.empty((s.M, s.H), dtype=torch.int16, device="cuda")
-    plan.forward(g["x"], g["logits"], g["w13"], g["s13"], g["w2"], g["s2"], eager)
+    call(eager)
     torch.cuda.synchronize()
     out = torch.empty_like(eager)
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(stream):
-        plan.forward(g["x"], g["logits"], g["w13"], g["s13"], g["w2"], g["s2"], out)  # warm-up off-graph
+        call(out)  # warm-up off-graph
     torch.cuda.current_stream().wait_stream(stream)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        plan.forward(g["x"], g["logits"], g["w13"], g["s13"], g["w2"], g["s2"], out)
+        call(out)
     for i in range(5):
         out.fill_(-1)
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, eager), f"replay {i} differs from the eager call"
-        plan.forward(g["x"], g["logits"], g["w13"], g["s13"], g["w2"], g["s2"], eager)  # eager work between
+        call(eager)  # eager work between
         torch.cuda.synchronize()
 
 
