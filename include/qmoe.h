@@ -12,13 +12,15 @@
  *   2. a stable sort of the M*k (token, slot) entries by expert
  *   3. x (bf16) -> MXFP4 once per token (E2M1, one E8M0 scale per 32)
  *   4. gate/up GEMM on MXFP4 expert weights, h = SiLU(gate) * up
- *   5. h -> FP8 E4M3 once per 128-element block, with an fp32 scale
+ *   5. h -> FP8 E4M3 once per 128-element block, with an fp32 scale (or,
+ *      with moe_plan_set_mid_format, MXFP4 per 32 for the stock MXFP4 arm)
  *   6. down GEMM on MXFP4 expert weights
  *   7. out (bf16) = sum over slots of weight * down output (+ shared expert)
  *   8. optional block-FP8 shared expert (128x128 weight scales), weight 1
  *
  * Conventions for every entry point:
- *   - All tensors are dense, row-major, 16-byte aligned device pointers on
+ *   - All tensors are dense, row-major (the weights moe_pack_w13 and
+ *     moe_pack_w2 write excepted), 16-byte aligned device pointers on
  *     the plan's device. The caller owns every buffer (inputs, weights,
  *     output, workspace); the library never allocates device memory and
  *     never synchronizes a stream. `stream` is a hipStream_t (NULL = the
@@ -223,7 +225,9 @@ int moe_stage_count(void);
 const char* moe_stage_name(int i);
 
 /* Kernels that stage `stage` launches for a call of M tokens on this plan
- * (0 when the stage is folded into another one), or -1 for bad arguments. */
+ * with its current mid format (0 when the stage is folded into another
+ * one), or -1 for bad arguments or a call the plan would not serve (M > 256
+ * with MOE_MID_MXFP4). */
 int moe_plan_stage_launches(const moe_plan* plan, int64_t M, int stage);
 
 /* Static text for a status code. */
