@@ -117,6 +117,23 @@ def route(logits: np.ndarray, k: int, scaling: float):
     return ids, w
 
 
+def route_shared_slot(logits: np.ndarray, k: int, scaling: float):
+    """Routing with the shared expert fused as the last expert and the last
+    slot ("[HIP] IQ2R: GLM-5.3 packed MoE path for TP4/TP8 on gfx950",
+    Summary: 256 routed experts plus the shared expert as expert 256, top-9).
+    Reading: slots 0..k-2 are the top-(k-1) of the first E-1 logits with the
+    weights of `route` over those k-1 slots; slot k-1 is expert E-1 with
+    weight 1 (the shared expert's output is added unscaled). The last logits
+    column is not read."""
+    logits = np.asarray(logits, np.float32)
+    M, E = logits.shape
+    assert k >= 2 and E >= 2
+    ids_r, w_r = route(logits[:, :E - 1], k - 1, scaling)
+    ids = np.concatenate([ids_r, np.full((M, 1), E - 1, np.int32)], axis=1)
+    w = np.concatenate([w_r, np.ones((M, 1), np.float32)], axis=1)
+    return ids, w
+
+
 # ------------------------------------------------------------------ 2. align
 def align(ids: np.ndarray, E: int):
     """Stable grouping of the M*k entries (entry = t*k + j) by expert.
@@ -247,7 +264,8 @@ def _mid_steps(mid_format: str):
     raise ValueError(mid_format)
 
 
-def moe_forward(x_bits, logits, w13, s13, w2, s2, top_k, scaling, shared=None, mid_format="e4m3"):
+def moe_forward(x_bits, logits, w13, s13, w2, s2, top_k, scaling, shared=None, mid_format="e4m3",
+                shared_slot=False):
     """The routed-MoE call on all M tokens.
 
     x_bits [M, H] bf16 bits; logits [M, E] fp32; w13 [E, 2I, H/2] u8 and s13
@@ -256,7 +274,8 @@ def moe_forward(x_bits, logits, w13, s13, w2, s2, top_k, scaling, shared=None, m
     None. Returns a dict of every intermediate; rows of h / midq / mids are in
     sorted (expert-major) order, y is indexed by entry t*k + j. midq holds
     one code per element (E4M3, or E2M1 with mid_format "mxfp4"), mids the
-    fp32 scales per 128 (or the E8M0 scale codes per 32).
+    fp32 scales per 128 (or the E8M0 scale codes per 32). With shared_slot,
+    expert E-1 is the shared expert, routed by `route_shared_slot`.
     """
     qmid, dmid = _mid_steps(mid_format)
     x_bits = np.asarray(x_bits, np.uint16)
@@ -264,7 +283,7 @@ def moe_forward(x_bits, logits, w13, s13, w2, s2, top_k, scaling, shared=None, m
     E = logits.shape[1]
     I = w13.shape[1] // 2
     k = top_k
-    ids, w = route(logits, k, scaling)
+    ids, w = (route_shared_slot if shared_slot else route)(logits, k, scaling)
     count, offset, sorted_entry = align(ids, E)
     xq, xs = quantize_x(x_bits)
     xd = F.mx_fp4_decode(xq, xs, 32)
@@ -302,7 +321,8 @@ def expert_dense(xd: np.ndarray, w13e, s13e, w2e, s2e, I: int, mid_format="e4m3"
     return dmid(q, s, dequant_mxfp4(w2e, s2e))
 
 
-def moe_dense(x_bits, logits, w13, s13, w2, s2, top_k, scaling, shared=None, mid_format="e4m3"):
+def moe_dense(x_bits, logits, w13, s13, w2, s2, top_k, scaling, shared=None, mid_format="e4m3",
+              shared_slot=False):
     """Brute force: every expert on every token, then masked by the routing.
 
     Shares the per-expert arithmetic with moe_forward but none of its
@@ -311,7 +331,7 @@ def moe_dense(x_bits, logits, w13, s13, w2, s2, top_k, scaling, shared=None, mid
     M, H = x_bits.shape
     E = logits.shape[1]
     I = w13.shape[1] // 2
-    ids, w = route(logits, top_k, scaling)
+    ids, w = (route_shared_slot if shared_slot else route)(logits, top_k, scaling)
     xq, xs = quantize_x(x_bits)
     xd = F.mx_fp4_decode(xq, xs, 32)
     all_y = np.stack([expert_dense(xd, w13[e], s13[e], w2[e], s2[e], I, mid_format) for e in range(E)])

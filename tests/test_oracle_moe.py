@@ -308,3 +308,38 @@ def test_mx_mid_invariants():
     for key in ("ids", "sorted_entry", "xq", "h"):
         assert np.array_equal(r8[key], r4[key])
     assert not np.array_equal(r8["out"], r4["out"])
+
+
+# ------------------------------------------------------------ shared expert as the last slot
+def test_shared_slot_routing_brute_force():
+    """Slots 0..k-2: the brute-force top-(k-1) of the first E-1 logits, with
+    weights summing to the scaling factor over those slots; slot k-1: expert
+    E-1 with weight exactly 1; the last logits column is never read."""
+    rng = np.random.default_rng(21)
+    M, E, k = 6, 17, 4
+    lg = rng.normal(size=(M, E)).astype(np.float32)
+    ids, w = O.route_shared_slot(lg, k, 2.5)
+    for t in range(M):
+        assert list(ids[t, :k - 1]) == _brute_topk(lg[t, :E - 1], k - 1)
+        assert ids[t, k - 1] == E - 1 and w[t, k - 1] == np.float32(1.0)
+        assert abs(float(np.sum(w[t, :k - 1], dtype=np.float64)) - 2.5) < 1e-5
+    lg2 = lg.copy()
+    lg2[:, E - 1] = 1e30  # would win every routed slot if it were read
+    assert np.array_equal(O.route_shared_slot(lg2, k, 2.5)[0], ids)
+
+
+def test_shared_slot_equals_routed_plus_shared_expert():
+    """The fused call equals the routed call over the first E-1 experts with
+    k-1 slots plus the shared expert applied to every token, added with weight
+    1 before the one bf16 rounding (dense evaluation of the shared expert)."""
+    shape = X.Shape(M=5, H=512, E=9, I=128, top_k=3)
+    d = X.make_inputs(shape, "normal", 23)
+    fused = _run(d, shared_slot=True)
+    k, E = shape.top_k, shape.E
+    routed = _run(d, logits=d["logits"][:, :E - 1], w13=d["w13"][:E - 1], s13=d["s13"][:E - 1],
+                  w2=d["w2"][:E - 1], s2=d["s2"][:E - 1], top_k=k - 1)
+    xd = F.mx_fp4_decode(*O.quantize_x(d["x"]))
+    ysh = O.expert_dense(xd, d["w13"][E - 1], d["s13"][E - 1], d["w2"][E - 1], d["s2"][E - 1], shape.I)
+    ref = O.combine(routed["w"], routed["y"].reshape(shape.M, k - 1, shape.H), ysh)
+    assert np.array_equal(fused["out"], ref)
+    assert np.array_equal(fused["out"], _run(d, fn=O.moe_dense, shared_slot=True))
