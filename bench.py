@@ -97,13 +97,15 @@ def measure(name, steps, warmup, n_sets, mid_fmt=0):
     torch.cuda.synchronize()
     sets = []
     for i in range(n_sets):
-        d = X.make_inputs(X.Shape(**vars(s)), wl.logits, wl.seed * 1000 + i, with_weights=False) if i else base
+        d = (X.make_inputs(X.Shape(**vars(s)), wl.logits, wl.seed * 1000 + i, with_weights=False,
+                           shared_slot=wl.shared_slot) if i else base)
         sets.append((torch.from_numpy(d["x"].view(np.int16)).to(dev), torch.from_numpy(d["logits"]).to(dev)))
     plan = Plan(s.M, s.H, s.E, s.I, s.top_k, s.routed_scaling, s.shared_I)
     if s.shared_I:
         sh = [torch.from_numpy(base[k]).to(dev) for k in ("ws13", "ss13", "ws2", "ss2")]
         plan.set_shared(*sh)
     plan.set_mid_format(mid_fmt)
+    plan.set_shared_slot(wl.shared_slot)
     x = torch.empty_like(sets[0][0])
     logits = torch.empty_like(sets[0][1])
     out = torch.empty((s.M, s.H), dtype=torch.int16, device=dev)

@@ -144,6 +144,18 @@ moe_status moe_plan_set_shared(moe_plan* plan, const void* ws13, const float* ss
  * M, and moe_forward returns MOE_ERR_UNSUPPORTED for M > 256. */
 typedef enum { MOE_MID_E4M3 = 0, MOE_MID_MXFP4 = 1 } moe_mid_format;
 
+/* Fuse a shared expert as the last expert and the last slot ("[HIP] IQ2R:
+ * GLM-5.3 packed MoE path for TP4/TP8 on gfx950", Summary: 256 routed
+ * experts plus the shared expert as expert 256, top-9). With on = 1 the
+ * plan's expert E-1 is the shared expert, given in the routed experts'
+ * format as the last expert of w13/s13/w2/s2; slots 0..top_k-2 of every
+ * token are routed over the first E-1 logits (the last logits column is not
+ * read, weights renormalized over those slots) and slot top_k-1 is expert
+ * E-1 with weight 1. MOE_ERR_INVALID_ARG for a NULL plan, on not 0 or 1,
+ * top_k < 2, or a plan with a block-FP8 shared expert (shape.shared_I > 0).
+ * Host-only; applies to later calls. */
+moe_status moe_plan_set_shared_slot(moe_plan* plan, int on);
+
 /* Select the mid format for the plan's later calls. MOE_ERR_INVALID_ARG for
  * a NULL plan or an unknown format. Host-only. */
 moe_status moe_plan_set_mid_format(moe_plan* plan, int format);

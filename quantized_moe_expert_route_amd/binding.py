@@ -81,6 +81,8 @@ def lib() -> ctypes.CDLL:
     L.moe_pack_w13.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp]
     L.moe_pack_w2.restype = st
     L.moe_pack_w2.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp]
+    L.moe_plan_set_shared_slot.restype = st
+    L.moe_plan_set_shared_slot.argtypes = [vp, ctypes.c_int]
     L.moe_plan_set_mid_format.restype = st
     L.moe_plan_set_mid_format.argtypes = [vp, ctypes.c_int]
     _lib = L
@@ -187,6 +189,12 @@ class Plan:
         st = lib().moe_plan_set_shared(self._h, _ptr(ws13), _ptr(ss13), _ptr(ws2), _ptr(ss2))
         if st != MOE_OK:
             raise MoeError(st, "moe_plan_set_shared")
+
+    def set_shared_slot(self, on: bool):
+        """Expert E-1 as the shared expert, fused as the last slot of every token."""
+        st = lib().moe_plan_set_shared_slot(self._h, int(bool(on)))
+        if st != MOE_OK:
+            raise MoeError(st, "moe_plan_set_shared_slot")
 
     def set_mid_format(self, fmt: int):
         """MID_E4M3 (default) or MID_MXFP4 for the plan's later calls."""

@@ -236,6 +236,13 @@ moe_status moe_plan_set_shared(moe_plan* plan, const void* ws13, const float* ss
   return MOE_OK;
 }
 
+moe_status moe_plan_set_shared_slot(moe_plan* plan, int on) {
+  if (!plan || (on != 0 && on != 1)) return MOE_ERR_INVALID_ARG;
+  if (on && (plan->s.top_k < 2 || plan->s.shared_I > 0)) return MOE_ERR_INVALID_ARG;
+  plan->shared_slot = on;
+  return MOE_OK;
+}
+
 moe_status moe_plan_set_mid_format(moe_plan* plan, int format) {
   if (!plan || (format != MOE_MID_E4M3 && format != MOE_MID_MXFP4)) return MOE_ERR_INVALID_ARG;
   plan->mid_fmt = format;

@@ -38,14 +38,19 @@ namespace qmoe {
 // and no tile is loaded twice. The tile descriptors arrive through scalar
 // loads, so the first weight loads do not queue behind the mid staging.
 //
-// MID_LDS: the n mid rows are widened to bf16 once per workgroup into LDS,
-// with their scales; otherwise each slot carries its tile's E4M3 mid rows
-// in registers and widens them itself. (Quantizing mid inside this launch
+// MID_LDS: the n mid rows are staged in LDS with their scales, widened to
+// bf16 once per workgroup while n * I <= kDcMidBytes; above (ST = 12, e.g.
+// a ninth slot at M = 16) bf16 rows would leave one workgroup per CU, so
+// they stay E4M3 (half the bytes) and each fragment is widened as it is
+// read (still once per workgroup, but on the MFMA's path: slower while the
+// bf16 rows fit). Otherwise each slot carries its tile's E4M3 mid rows in
+// registers and widens them itself. (Quantizing mid inside this launch
 // instead, redundantly per workgroup, measured slower than its own launch.)
 constexpr int kDcThreads = 256;
 constexpr int kDcWaves = kDcThreads / 64;
-constexpr int kDcMidBytes = 32 * 1024;  // n * I staged in LDS from E4M3: 8 uint4 per thread
-constexpr int kDcPad = 16;              // LDS bytes after each staged bf16 mid row
+constexpr int kDcMidBytes = 32 * 1024;  // n * I staged in LDS from E4M3: ST = 8 uint4 per thread
+constexpr int kDcMidBytesMax = 48 * 1024;  // ST = 12: n up to 192 at I = 256 (the shared expert as a ninth slot)
+constexpr int kDcPad = 16;              // LDS bytes after each staged mid row
 
 template <int NB, bool MID_LDS>
 struct DcSlot {
@@ -68,23 +73,24 @@ __device__ __forceinline__ uint32_t scale_byte(const uint4& v, int b, int g) {
   return ((b == 0 ? v.x : b == 1 ? v.y : b == 2 ? v.z : v.w) >> (8 * g)) & 0xFFu;
 }
 
-size_t down_combine_lds_bytes(int64_t n, int64_t I, bool mid_lds) {
+size_t down_combine_lds_bytes(int64_t n, int64_t I, bool mid_lds, bool mid_bf16) {
   size_t b = (size_t)(n + 1) * 16 * 4;
-  if (mid_lds) b += (size_t)n * (2 * I + kDcPad) + (size_t)n * (I / 128) * 4 + (size_t)n * 4;
+  if (mid_lds) b += (size_t)n * ((mid_bf16 ? 2 : 1) * I + kDcPad) + (size_t)n * (I / 128) * 4 + (size_t)n * 4;
   return b;
 }
 
-template <int NB, int D, bool MID_LDS>
+template <int NB, int D, bool MID_LDS, int ST = 8>
 __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
     const uint8_t* __restrict__ midq, const float* __restrict__ mids, const uint8_t* __restrict__ w2, const uint8_t* __restrict__ s2, const int* __restrict__ sorted_entry,
     const int4* __restrict__ tiles, const int* __restrict__ meta, int H, int k, int M, int cw,
     const float* __restrict__ topk_w, const float* __restrict__ ys, uint16_t* __restrict__ out) {
   constexpr int I = NB * 128;
-  constexpr int LDA = 2 * I + kDcPad;  // bytes per staged bf16 mid row
+  constexpr bool A16 = ST == 8;  // mid staged widened to bf16 (else E4M3, widened at each read)
+  constexpr int LDA = (A16 ? 2 : 1) * I + kDcPad;  // bytes per staged mid row; the pad spreads 16 rows over the banks
   extern __shared__ __align__(16) uint8_t dyn[];
   const int n = M * k;
   float* yl = reinterpret_cast<float*>(dyn);            // [n + 1][16]; row n takes dropped rows
-  uint8_t* ml = reinterpret_cast<uint8_t*>(yl + (n + 1) * 16);  // [n][LDA]  (MID_LDS) bf16 mid
+  uint8_t* ml = reinterpret_cast<uint8_t*>(yl + (n + 1) * 16);  // [n][LDA]  (MID_LDS) bf16 or E4M3 mid
   float* msl = reinterpret_cast<float*>(ml + n * LDA);  // [n][NB]   (MID_LDS)
   int* sel = reinterpret_cast<int*>(msl + n * NB);      // [n]       (MID_LDS) sorted_entry
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -107,18 +113,23 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
 #pragma unroll
   for (int d = 0; d < D; ++d) T[d] = tiles[my > 0 ? base + min(d, my - 1) : 0];
   __builtin_amdgcn_sched_barrier(0);
-  constexpr int kSt = MID_LDS ? kDcMidBytes / 16 / kDcThreads : 1;
+  constexpr int kSt = MID_LDS ? ST : 1;
   uint4 st[kSt];
-  float sts = 0.f;
-  int ste = 0;
+  constexpr int kSs = ST == 8 ? 1 : 2;  // mid scales and entries a thread stages (n * NB <= kSs * kDcThreads)
+  float sts[kSs];
+  int ste[kSs];
   if (MID_LDS) {
 #pragma unroll
     for (int q = 0; q < kSt; ++q) {
       const int idx = tid + kDcThreads * q;
       st[q] = idx < n * (I / 16) ? ld16(midq + 16 * (size_t)idx) : make_uint4(0, 0, 0, 0);
     }
-    sts = tid < n * NB ? mids[tid] : 0.f;
-    ste = tid < n ? sorted_entry[tid] : 0;
+#pragma unroll
+    for (int q = 0; q < kSs; ++q) {
+      const int idx = tid + kDcThreads * q;
+      sts[q] = idx < n * NB ? mids[idx] : 0.f;
+      ste[q] = idx < n ? sorted_entry[idx] : 0;
+    }
   }
 
   auto load = [&](const int4 tl, DcSlot<NB, MID_LDS>& S) {
@@ -159,8 +170,15 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
         for (int i2 = 0; i2 < 4; ++i2) sc[i2] = msl[min(tl.y + 4 * g + i2, tl.z - 1) * NB + b];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const uint4 av = *reinterpret_cast<const uint4*>(ml + arow * LDA + 2 * (128 * b + 32 * g + 8 * q));
-          const v8s fa = as_v8s(av.x, av.y, av.z, av.w);
+          v8s fa;
+          if (A16) {
+            const uint4 av = *reinterpret_cast<const uint4*>(ml + arow * LDA + 2 * (128 * b + 32 * g + 8 * q));
+            fa = as_v8s(av.x, av.y, av.z, av.w);
+          } else {  // 8 E4M3 codes widened to bf16 as they are read (exact)
+            const uint2 av = *reinterpret_cast<const uint2*>(ml + arow * LDA + 128 * b + 32 * g + 8 * q);
+            fa = as_v8s(fp8x2_bf16<false>(av.x), fp8x2_bf16<true>(av.x), fp8x2_bf16<false>(av.y),
+                        fp8x2_bf16<true>(av.y));
+          }
           const v8s fb = as_v8s(cvt_fp4x2_bf16<0>(qw[q], wsc), cvt_fp4x2_bf16<1>(qw[q], wsc),
                                 cvt_fp4x2_bf16<2>(qw[q], wsc), cvt_fp4x2_bf16<3>(qw[q], wsc));
           P = mfma_bf16(fa, fb, P);
@@ -200,22 +218,30 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
     __builtin_amdgcn_sched_barrier(0);  // slot by slot, in issue order
   }
 
-  // ---- staged mid to LDS, widened to bf16
+  // ---- staged mid to LDS (widened to bf16 when A16)
   if (MID_LDS) {
 #pragma unroll
     for (int q = 0; q < kSt; ++q) {
       const int idx = tid + kDcThreads * q;
       if (idx < n * (I / 16)) {
         const int row = idx / (I / 16), c = idx - row * (I / 16);
-        uint4* dst = reinterpret_cast<uint4*>(ml + row * LDA + 32 * c);  // E4M3 -> bf16, exact
-        dst[0] = make_uint4(fp8x2_bf16<false>(st[q].x), fp8x2_bf16<true>(st[q].x), fp8x2_bf16<false>(st[q].y),
-                            fp8x2_bf16<true>(st[q].y));
-        dst[1] = make_uint4(fp8x2_bf16<false>(st[q].z), fp8x2_bf16<true>(st[q].z), fp8x2_bf16<false>(st[q].w),
-                            fp8x2_bf16<true>(st[q].w));
+        if (A16) {
+          uint4* dst = reinterpret_cast<uint4*>(ml + row * LDA + 32 * c);  // E4M3 -> bf16, exact
+          dst[0] = make_uint4(fp8x2_bf16<false>(st[q].x), fp8x2_bf16<true>(st[q].x), fp8x2_bf16<false>(st[q].y),
+                              fp8x2_bf16<true>(st[q].y));
+          dst[1] = make_uint4(fp8x2_bf16<false>(st[q].z), fp8x2_bf16<true>(st[q].z), fp8x2_bf16<false>(st[q].w),
+                              fp8x2_bf16<true>(st[q].w));
+        } else {
+          *reinterpret_cast<uint4*>(ml + row * LDA + 16 * c) = st[q];
+        }
       }
     }
-    if (tid < n * NB) msl[tid] = sts;
-    if (tid < n) sel[tid] = ste;
+#pragma unroll
+    for (int q = 0; q < kSs; ++q) {
+      const int idx = tid + kDcThreads * q;
+      if (idx < n * NB) msl[idx] = sts[q];
+      if (idx < n) sel[idx] = ste[q];
+    }
     barrier_lds();
   }
 
@@ -338,8 +364,9 @@ hipError_t launch_down_combine(const moe_plan* p, const CallArgs& a, Ev ev) {
   const int H = (int)p->s.H;
   const int64_t n = a.M * p->s.top_k, I = p->s.I;
   if (n > kSmallRows) return hipErrorInvalidValue;
-  const bool mid_lds = n * I <= kDcMidBytes && n * (I / 128) <= kDcThreads && n <= kDcThreads;
-  const size_t lds = down_combine_lds_bytes(n, I, mid_lds);
+  const bool mid_lds = n * I <= kDcMidBytesMax && n * (I / 128) <= 2 * kDcThreads && n <= 2 * kDcThreads;
+  const bool wide = n * I > kDcMidBytes;  // 12 staging registers a thread instead of 8
+  const size_t lds = down_combine_lds_bytes(n, I, mid_lds, mid_lds && !wide);
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   const float* ys = p->s.shared_I > 0 ? wsp<float>(p, p->L.sh_y) : nullptr;
   const int cw = down_combine_cols(H, p->num_cus);
@@ -352,10 +379,14 @@ hipError_t launch_down_combine(const moe_plan* p, const CallArgs& a, Ev ev) {
   };
   // weights of D tiles in flight per wave; fewer when the slots also carry mid rows
   switch (I / 128) {
-    case 1: return mid_lds ? go(down_combine_kernel<1, 8, true>) : go(down_combine_kernel<1, 6, false>);
-    case 2: return mid_lds ? go(down_combine_kernel<2, 8, true>) : go(down_combine_kernel<2, 3, false>);
-    case 3: return mid_lds ? go(down_combine_kernel<3, 5, true>) : go(down_combine_kernel<3, 2, false>);
-    case 4: return mid_lds ? go(down_combine_kernel<4, 4, true>) : go(down_combine_kernel<4, 2, false>);
+    case 1: return !mid_lds ? go(down_combine_kernel<1, 6, false>)
+                   : wide   ? go(down_combine_kernel<1, 8, true, 12>) : go(down_combine_kernel<1, 8, true>);
+    case 2: return !mid_lds ? go(down_combine_kernel<2, 3, false>)
+                   : wide   ? go(down_combine_kernel<2, 8, true, 12>) : go(down_combine_kernel<2, 8, true>);
+    case 3: return !mid_lds ? go(down_combine_kernel<3, 2, false>)
+                   : wide   ? go(down_combine_kernel<3, 5, true, 12>) : go(down_combine_kernel<3, 5, true>);
+    case 4: return !mid_lds ? go(down_combine_kernel<4, 2, false>)
+                   : wide   ? go(down_combine_kernel<4, 4, true, 12>) : go(down_combine_kernel<4, 4, true>);
     default: return hipErrorInvalidValue;
   }
 }

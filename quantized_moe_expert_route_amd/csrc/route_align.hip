@@ -78,6 +78,26 @@ __device__ __forceinline__ float route_weight(float sel_l, int k, int lane, floa
   return __fdiv_rn(sig, S + 1e-20f) * scaling;
 }
 
+// One token's slots, lane j < k holding slot j's expert and weight. With
+// shared_slot the shared expert is the last expert and the last slot
+// ("[HIP] IQ2R: GLM-5.3 packed MoE path for TP4/TP8 on gfx950", Summary:
+// the shared expert fused as expert 256 of a top-9 call): slots 0..k-2 are
+// routed over the first E-1 logits, slot k-1 is expert E-1 with weight 1.
+template <int EC>
+__device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int k, float scaling,
+                                            int shared_slot, int lane, uint32_t& sel_e, float& w) {
+  const int kr = k - shared_slot, er = E - shared_slot;
+  uint32_t key[EC];
+  float sel_l = 0.f;
+  load_keys<EC>(row, er, lane, key);
+  topk_wave<EC>(key, kr, lane, sel_e, sel_l);
+  w = route_weight(sel_l, kr, lane, scaling);
+  if (shared_slot && lane == k - 1) {
+    sel_e = (uint32_t)(E - 1);
+    w = 1.0f;
+  }
+}
+
 // One 32-element block of a bf16 row -> 16 bytes of E2M1 + an E8M0 byte.
 __device__ __forceinline__ void quant_block_mx(const uint16_t* __restrict__ src, uint8_t* __restrict__ dq,
                                                uint8_t* __restrict__ ds) {
@@ -175,7 +195,7 @@ __global__ __launch_bounds__(1024) void route_align_small_kernel(
     const float* __restrict__ logits, const uint16_t* __restrict__ x, int M, int E, int k, int H, float scaling,
     int* __restrict__ topk_ids, float* __restrict__ topk_w, int* __restrict__ count, int* __restrict__ offset,
     int* __restrict__ sorted_entry, int4* __restrict__ tiles, int* __restrict__ meta, uint8_t* __restrict__ xq,
-    uint8_t* __restrict__ xs) {
+    uint8_t* __restrict__ xs, int shared_slot) {
   __shared__ uint32_t s_mask[1024][2];  // expert -> tokens 0..63
   __shared__ int s_ids[64 * 16];
   __shared__ int s_off[1024];
@@ -197,11 +217,8 @@ __global__ __launch_bounds__(1024) void route_align_small_kernel(
   // top-k, one wave per token
   for (int t = wave; t < M; t += 16) {
     uint32_t sel_e = 0;
-    float sel_l = 0.f;
-    uint32_t key[EC];
-    load_keys<EC>(logits + (size_t)t * E, E, lane, key);
-    topk_wave<EC>(key, k, lane, sel_e, sel_l);
-    const float w = route_weight(sel_l, k, lane, scaling);
+    float w = 0.f;
+    route_token<EC>(logits + (size_t)t * E, E, k, scaling, shared_slot, lane, sel_e, w);
     if (lane < k) {
       topk_ids[t * k + lane] = (int)sel_e;
       topk_w[t * k + lane] = w;
@@ -288,16 +305,13 @@ __global__ __launch_bounds__(256) void route_kernel(
     const float* __restrict__ logits, const uint16_t* __restrict__ x, int M, int E, int k, int H,
     float scaling, int* __restrict__ topk_ids, float* __restrict__ topk_w,
     uint32_t* __restrict__ bitmap, int words, uint8_t* __restrict__ xq, uint8_t* __restrict__ xs,
-    uint8_t* __restrict__ sh_xq, float* __restrict__ sh_xs, int route_blocks) {
+    uint8_t* __restrict__ sh_xq, float* __restrict__ sh_xs, int route_blocks, int shared_slot) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if ((int)blockIdx.x < route_blocks) {
     for (int t = blockIdx.x * 4 + wave; t < M; t += route_blocks * 4) {
       uint32_t sel_e = 0;
-      float sel_l = 0.f;
-      uint32_t key[EC];
-      load_keys<EC>(logits + (size_t)t * E, E, lane, key);
-      topk_wave<EC>(key, k, lane, sel_e, sel_l);
-      const float w = route_weight(sel_l, k, lane, scaling);
+      float w = 0.f;
+      route_token<EC>(logits + (size_t)t * E, E, k, scaling, shared_slot, lane, sel_e, w);
       if (lane < k) {
         topk_ids[(size_t)t * k + lane] = (int)sel_e;
         topk_w[(size_t)t * k + lane] = w;
@@ -520,7 +534,7 @@ hipError_t launch_route_small(const moe_plan* p, const CallArgs& a, Ev ev) {
                     reinterpret_cast<const uint16_t*>(a.x), M, E, k, H, p->s.routed_scaling,
                     wsp<int>(p, p->L.topk_ids), wsp<float>(p, p->L.topk_w), wsp<int>(p, p->L.count),
                     wsp<int>(p, p->L.offset), wsp<int>(p, p->L.sorted_entry), wsp<int4>(p, p->X.tiles),
-                    wsp<int>(p, p->X.meta), wsp<uint8_t>(p, p->L.xq), wsp<uint8_t>(p, p->L.xs));
+                    wsp<int>(p, p->X.meta), wsp<uint8_t>(p, p->L.xq), wsp<uint8_t>(p, p->L.xs), p->shared_slot);
   });
 }
 
@@ -539,7 +553,7 @@ hipError_t launch_route(const moe_plan* p, const CallArgs& a, Ev ev) {
     return launch_k(sh ? route_kernel<EC, true> : route_kernel<EC, false>, dim3(blocks), dim3(256), 0, a.stream,
                     ev, a.logits, reinterpret_cast<const uint16_t*>(a.x), M, E, k, H, p->s.routed_scaling,
                     wsp<int>(p, p->L.topk_ids), wsp<float>(p, p->L.topk_w), wsp<uint32_t>(p, p->X.bitmap), words,
-                    wsp<uint8_t>(p, p->L.xq), wsp<uint8_t>(p, p->L.xs), sh_xq, sh_xs, route_blocks);
+                    wsp<uint8_t>(p, p->L.xq), wsp<uint8_t>(p, p->L.xs), sh_xq, sh_xs, route_blocks, p->shared_slot);
   });
 }
 

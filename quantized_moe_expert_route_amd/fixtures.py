@@ -66,6 +66,7 @@ class Workload:
     shape: Shape
     logits: str  # "normal" | "uniform" | "correlated" | "zipf" | "hot" | "mixed" | "spread"
     seed: int
+    shared_slot: bool = False  # expert E-1 is the shared expert, the last slot of every token
 
 
 WORKLOADS: Dict[str, Workload] = {
@@ -82,12 +83,21 @@ for _m in (32, 64, 128, 256):
     for _kind in ("hot", "mixed", "spread"):
         WORKLOADS[f"m{_m}_{_kind}"] = Workload(f"m{_m}_{_kind}", Shape(M=_m, H=6144, E=256, I=256, top_k=8), _kind, 1)
 
+# The pages' fused form of the shared expert: 256 routed experts plus the
+# shared expert as expert 256, top-9 (TP8 shapes of c1 and c2; experts
+# 0..255 are c1's / c2's, the logits are drawn for 257 columns and the last
+# column is not read).
+WORKLOADS["c1s"] = Workload("c1s", Shape(M=4, H=6144, E=257, I=256, top_k=9), "uniform", 1, True)
+WORKLOADS["c2s"] = Workload("c2s", Shape(M=16, H=6144, E=257, I=256, top_k=9), "correlated", 2, True)
+
 WORKLOAD_TITLES = {
     "c0": "tiny H512 E16 top2 I128 M4",
     "c1": "TP8-rank decode H6144 E256 top8 I256 M4, MXFP4 experts, uniform logits",
     "c2": "TP8-rank verify H6144 E256 top8 I256 M16, MXFP4 experts, correlated rows",
     "c3": "TP4-rank prefill H6144 E256 top8 I512 M1024, MXFP4 experts, Zipf(1.1) routing",
     "c4": "TP4-rank large prefill H6144 E256 top8 I512 M4096 + block-FP8 shared expert I512, Zipf(1.1)",
+    "c1s": "TP8-rank decode H6144 E256+1 top9 I256 M4, shared expert fused as expert 256 (slot 9), uniform logits",
+    "c2s": "TP8-rank verify H6144 E256+1 top9 I256 M16, shared expert fused as expert 256 (slot 9), correlated rows",
 }
 for _name, _wl in WORKLOADS.items():
     if _name not in WORKLOAD_TITLES:
@@ -266,16 +276,18 @@ def make_shared(shape: Shape, seed: int):
 
 
 def make_inputs(name_or_shape, logits: Optional[str] = None, seed: Optional[int] = None,
-                experts: Optional[np.ndarray] = None, with_weights: bool = True):
+                experts: Optional[np.ndarray] = None, with_weights: bool = True, shared_slot: bool = False):
     """All inputs of one call as numpy arrays.
 
     `name_or_shape` is a workload name ("c0".."c4") or a Shape (then `logits`
     and `seed` are required). Returns a dict with shape, x (bf16 bits), logits,
     w13, s13, w2, s2 and, when shape.shared_I > 0, the shared expert tensors.
     """
+    slot = shared_slot
     if isinstance(name_or_shape, str):
         wl = WORKLOADS[name_or_shape]
         shape, kind, sd = wl.shape, wl.logits, wl.seed
+        slot = slot or wl.shared_slot
         if logits is not None:
             kind = logits
         if seed is not None:
@@ -283,7 +295,14 @@ def make_inputs(name_or_shape, logits: Optional[str] = None, seed: Optional[int]
     else:
         shape, kind, sd = name_or_shape, logits, seed
         assert kind is not None and sd is not None
-    d = {"shape": shape, "seed": sd, "x": make_x(shape, sd), "logits": make_logits(shape, kind, sd)}
+    if slot:
+        # the routed experts' logits as for E-1 experts and k-1 slots, then the
+        # shared expert's column (never read)
+        routed = dataclasses.replace(shape, E=shape.E - 1, top_k=shape.top_k - 1)
+        lg = np.concatenate([make_logits(routed, kind, sd), np.zeros((shape.M, 1), np.float32)], axis=1)
+    else:
+        lg = make_logits(shape, kind, sd)
+    d = {"shape": shape, "seed": sd, "x": make_x(shape, sd), "logits": lg}
     if with_weights:
         d["w13"], d["s13"], d["w2"], d["s2"] = make_weights(shape, sd, experts)
     if shape.shared_I > 0:

@@ -80,15 +80,15 @@ def read_intermediates(plan, s, M):
     return {key: t.cpu().numpy() for key, t in r.items()}
 
 
-def oracle(d, tokens=None):
+def oracle(d, tokens=None, **kw):
     """Oracle on all tokens, or only on `tokens` (per-token results are
-    independent of the other tokens)."""
+    independent of the other tokens); keyword options go to moe_forward."""
     s = d["shape"]
     x, lg = d["x"], d["logits"]
     if tokens is not None:
         x, lg = x[tokens], lg[tokens]
     shared = (d["ws13"], d["ss13"], d["ws2"], d["ss2"]) if s.shared_I else None
-    return O.moe_forward(x, lg, d["w13"], d["s13"], d["w2"], d["s2"], s.top_k, s.routed_scaling, shared)
+    return O.moe_forward(x, lg, d["w13"], d["s13"], d["w2"], d["s2"], s.top_k, s.routed_scaling, shared, **kw)
 
 
 def rows_by_entry(sorted_rows, sorted_entry, n):

@@ -85,6 +85,7 @@ def test_null_and_unbound_arguments_fail_before_any_device_work():
     assert L.moe_plan_set_stage_events(None, None, 0) == B.MOE_ERR_INVALID_ARG
     assert L.moe_plan_workspace_bytes(None) == 0
     assert L.moe_plan_set_mid_format(None, B.MID_MXFP4) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_plan_set_shared_slot(None, 1) == B.MOE_ERR_INVALID_ARG
     L.moe_plan_destroy(None)
 
 

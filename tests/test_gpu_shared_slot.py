@@ -1,0 +1,70 @@
+"""GPU parity of the shared expert fused as the last expert and the last slot
+(moe_plan_set_shared_slot), against the oracle's shared_slot routing: the
+same bars as the routed call (ids, weights and sort bit-exact, mid within one
+E4M3 step, output within 1e-2 x RMS), on the small, mid-range and large
+paths and at the pages' model shape (256 routed experts + the shared one as
+expert 256, top-9)."""
+
+import numpy as np
+import pytest
+
+from quantized_moe_expert_route_amd import fixtures as X
+
+from moe_gpu import make_plan, oracle, run, upload
+from test_gpu_parity import _check_mid, _check_out, _check_routing, _check_xq
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_slot(d):
+    plan = make_plan(d["shape"])
+    plan.set_shared_slot(True)
+    return run(d, plan=plan)
+
+
+@pytest.mark.parametrize("M,H,E,I,k,kind", [
+    (4, 512, 17, 128, 3, "normal"),      # small path
+    (16, 512, 65, 256, 9, "ties"),       # small path, ties among the routed logits
+    (40, 1024, 33, 256, 5, "zipf"),      # mid-range path
+    (300, 512, 17, 128, 3, "normal"),    # large path
+])
+def test_shared_slot_shapes(M, H, E, I, k, kind):
+    shape = X.Shape(M=M, H=H, E=E, I=I, top_k=k)
+    d = X.make_inputs(shape, kind, 3000 + M)
+    gout, gi = _run_slot(d)
+    ref = oracle(d, shared_slot=True)
+    _check_routing(gi, ref["ids"], ref["w"], ref["count"], ref["offset"], ref["sorted_entry"])
+    assert np.all(gi["ids"][:, -1] == E - 1) and np.all(gi["w"][:, -1] == 1.0)
+    assert gi["count"][E - 1] == M
+    _check_xq(gi, ref)
+    _check_mid(gi["midq"], gi["mids"], ref["midq"], ref["mids"])
+    _check_out(gout, ref["out"])
+
+
+@pytest.mark.parametrize("name", ["c1s", "c2s"])
+def test_shared_slot_full_size(name):
+    d = X.make_inputs(name)
+    assert X.WORKLOADS[name].shared_slot
+    gout, gi = _run_slot(d)
+    ref = oracle(d, shared_slot=True)
+    _check_routing(gi, ref["ids"], ref["w"], ref["count"], ref["offset"], ref["sorted_entry"])
+    _check_xq(gi, ref)
+    _check_mid(gi["midq"], gi["mids"], ref["midq"], ref["mids"])
+    ndiff = _check_out(gout, ref["out"])
+    print(f"{name}: {ndiff} of {ref['out'].size} bf16 outputs differ")
+
+
+def test_shared_slot_last_logits_column_not_read():
+    """Changing the shared expert's logits column changes nothing."""
+    import torch
+
+    shape = X.Shape(M=8, H=512, E=17, I=128, top_k=3)
+    d = X.make_inputs(shape, "normal", 55)
+    a, _ = _run_slot(d)
+    d2 = dict(d)
+    lg = d["logits"].copy()
+    lg[:, -1] = 1e30
+    d2["logits"] = lg
+    b, _ = _run_slot(d2)
+    assert np.array_equal(a, b)
+    torch.cuda.synchronize()
