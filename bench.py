@@ -266,9 +266,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c1", help="headline workload (c1..c4)")
-    ap.add_argument("--also", default="c2,c3,c4,m256_hot,m256_mixed",
+    ap.add_argument("--also", default="c2,c3,c4,c1s,c2s,m256_hot,m256_mixed",
                     help="more workloads reported in the same line ('' for none); mid-range batches are "
-                         "m{32,64,128,256}_{hot,mixed,spread}")
+                         "m{32,64,128,256}_{hot,mixed,spread}; c1s/c2s add the shared expert as expert 256, top-9")
     ap.add_argument("--mxfp4", default="m256_hot,m256_mixed",
                     help="workloads also timed with the MXFP4 mid hand-off (the pages' stock MXFP4 comparison "
                          "arm), reported as '<name>/mxfp4'; up to 256 tokens ('' for none)")
