@@ -68,3 +68,18 @@ def test_shared_slot_last_logits_column_not_read():
     b, _ = _run_slot(d2)
     assert np.array_equal(a, b)
     torch.cuda.synchronize()
+
+
+def test_shared_slot_argument_checks():
+    """The setter refuses what it cannot serve, before any call."""
+    from quantized_moe_expert_route_amd.binding import MOE_ERR_INVALID_ARG, MoeError
+
+    plan = make_plan(X.Shape(M=4, H=512, E=8, I=128, top_k=1))
+    with pytest.raises(MoeError) as ei:
+        plan.set_shared_slot(True)  # top_k 1: no routed slot left
+    assert ei.value.status == MOE_ERR_INVALID_ARG
+    plan = make_plan(X.Shape(M=4, H=512, E=8, I=128, top_k=2, shared_I=128))
+    with pytest.raises(MoeError) as ei:
+        plan.set_shared_slot(True)  # a block-FP8 shared expert is bound to this shape
+    assert ei.value.status == MOE_ERR_INVALID_ARG
+    plan.set_shared_slot(False)
