@@ -274,6 +274,9 @@ def main():
                          "arm), reported as '<name>/mxfp4'; up to 256 tokens ('' for none)")
     ap.add_argument("--sets", type=int, default=8, help="distinct input batches cycled through the steps")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--torch-read", type=int, default=0, metavar="MIB",
+                    help="only time torch's reduction over a cold MIB MiB buffer (the same 1 GiB flush before "
+                         "each) and print its rate: a library baseline for reading that many bytes once")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device-to-device copies of MIB MiB (the known-size kernel that "
                          "scales the HBM byte counters of a profiler run), then exit")
@@ -286,6 +289,25 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.torch_read:
+        n = args.torch_read * 1024 * 1024 // 4
+        buf = torch.ones(n, dtype=torch.float32, device="cuda")
+        flush = torch.ones(256 * 1024 * 1024, dtype=torch.float32, device="cuda")
+        sink = torch.empty((), dtype=torch.float32, device="cuda")
+        us = []
+        for i in range(25):
+            torch.sum(flush, 0, out=sink)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            torch.sum(buf, 0, out=sink)
+            e1.record()
+            torch.cuda.synchronize()
+            if i >= 5:
+                us.append(e0.elapsed_time(e1) * 1000.0)
+        med = float(np.median(us))
+        print(json.dumps({"torch_read_bytes": 4 * n, "us_median": round(med, 2),
+                          "GBps": round(4 * n / (med * 1e-6) / 1e9, 1), "reads": len(us)}))
+        return
     if args.copy_calibration:
         n = args.copy_calibration * 1024 * 1024 // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
