@@ -109,8 +109,8 @@ def test_mx_small_shapes(M, H, E, I, k, kind, Is):
     print(f"M={M}: y differs in {ydiff}, out in {ndiff} elements")
 
 
-@pytest.mark.parametrize("name,n_tok", [("c1", 0), ("c2", 0), ("m256_hot", 8), ("m256_mixed", 8),
-                                        ("m64_spread", 6)])
+@pytest.mark.parametrize("name,n_tok", [("c1", 0), ("c2", 0), ("t4_m16_hot", 0), ("m256_hot", 8),
+                                        ("m256_mixed", 8), ("m64_spread", 6)])
 def test_mx_full_size(name, n_tok):
     """The benchmark's shapes: every token (n_tok = 0) or a sample the oracle
     evaluates alone; routing and sort on every token."""

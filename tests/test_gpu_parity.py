@@ -87,7 +87,7 @@ def _check_shared_x(gi, ref, tokens=None):
     np.testing.assert_array_equal(s.view(np.uint32), ref["shared"]["xs8"].view(np.uint32))
 
 
-@pytest.mark.parametrize("name", ["c0", "c1", "c2"])
+@pytest.mark.parametrize("name", ["c0", "c1", "c2", "t4_m16_hot"])
 def test_stagewise_full(name):
     d = X.make_inputs(name)
     s = d["shape"]
