@@ -210,8 +210,11 @@ def test_shared_x_codes_on_exact_midpoints():
     _check_out(gout, ref["out"])
 
 
-def test_degenerate_inputs():
-    shape = X.Shape(M=6, H=512, E=16, I=128, top_k=4)
+@pytest.mark.parametrize("M", [6, 40, 300])  # small, mid-range and large paths
+def test_degenerate_inputs(M):
+    """x = 0; all logits -inf (every token on experts 0..k-1 with weight 0:
+    the most skewed sort); all logits equal."""
+    shape = X.Shape(M=M, H=512, E=16, I=128, top_k=4)
     d = X.make_inputs(shape, "normal", 5)
     # x = 0: every output zero
     d0 = dict(d, x=np.zeros_like(d["x"]))
