@@ -144,6 +144,7 @@ SMALL = [
     # up to 16 tokens: one workgroup routes and sorts, down and combine in one launch
     (1, 512, 16, 128, 2, "normal", 0),
     (16, 512, 64, 128, 8, "ties", 0),          # the last size of the small path
+    (4, 65536, 4, 128, 2, "normal", 0),        # largest H
     (5, 1024, 4, 256, 1, "normal", 0),         # top-1
     (9, 512, 8, 384, 8, "ties", 0),            # k = E, many ties, I = 384
     (33, 512, 64, 128, 8, "ties", 0),          # ties and signed zeros
@@ -153,6 +154,7 @@ SMALL = [
     # 16-row tiles with its own mid quantization, above on 64-row tiles with it inside
     (17, 512, 16, 128, 2, "normal", 0),        # one token past the small path; ragged tiles
     (20, 512, 1024, 128, 16, "uniform", 0),    # largest E and k
+    (20, 65536, 4, 128, 2, "normal", 0),       # largest H (mid-range path)
     (65, 512, 16, 128, 2, "normal", 0),
     (257, 512, 64, 128, 8, "uniform", 0),      # one token past the 16-row-tile gate/up
     (130, 1024, 32, 256, 8, "zipf", 0),        # skewed: a tile of 128 plus ragged tails
