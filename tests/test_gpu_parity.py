@@ -159,6 +159,7 @@ SMALL = [
     (257, 512, 64, 128, 8, "uniform", 0),      # one token past the 16-row-tile gate/up
     (130, 1024, 32, 256, 8, "zipf", 0),        # skewed: a tile of 128 plus ragged tails
     (300, 512, 8, 512, 2, "normal", 0),        # several full tiles per expert, I = 512
+    (257, 65536, 2, 128, 1, "normal", 0),      # largest H (large path: x scales staged in 11 parts)
     (96, 512, 64, 384, 8, "ties", 0),
     (70, 512, 4, 128, 2, "normal", 128),       # with the shared expert
     (72, 8192, 8, 128, 2, "normal", 0),        # H past 6144: x scales staged in two parts
