@@ -380,3 +380,25 @@ def test_stage_isolated_full_size(name, n_tok):
     out_ref = O.combine(gi["w"][tokens], gi["y"][ent].reshape(n_tok, k, H), ys)
     assert np.array_equal(gout[tokens], out_ref), "combine on the GPU's own y differs from the oracle's"
     print(f"{name}: down (isolated) differs in {ydiff} of {y_ref.size}; combine (isolated) exact")
+
+
+def test_largest_m_sampled():
+    """16384 tokens (131072 entries) at a small H: routing, weights and the
+    sort checked on every token, x, mid and output on sampled tokens."""
+    shape = X.Shape(M=16384, H=512, E=64, I=128, top_k=8)
+    d = X.make_inputs(shape, "zipf", 4242)
+    gout, gi = run(d)
+    ids, w = O.route(d["logits"], shape.top_k, shape.routed_scaling)
+    count, offset, se = O.align(ids, shape.E)
+    _check_routing(gi, ids, w, count, offset, se)
+    tokens = np.sort(np.random.default_rng(8).choice(shape.M, 12, replace=False))
+    ref = oracle(d, tokens)
+    _check_xq(gi, ref, tokens)
+    k = shape.top_k
+    ent = (tokens[:, None] * k + np.arange(k)[None, :]).ravel()
+    g_midq = rows_by_entry(gi["midq"], gi["sorted_entry"], shape.M * k)[ent]
+    g_mids = rows_by_entry(gi["mids"], gi["sorted_entry"], shape.M * k)[ent]
+    _check_mid(g_midq, g_mids, rows_by_entry(ref["midq"], ref["sorted_entry"], len(tokens) * k),
+               rows_by_entry(ref["mids"], ref["sorted_entry"], len(tokens) * k))
+    _check_y(gi["y"][ent], ref["y"])
+    _check_out(gout[tokens], ref["out"])
