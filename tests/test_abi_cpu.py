@@ -120,3 +120,20 @@ def test_plan_needs_a_gfx950_device():
     assert not out.value
     # host addresses are not device memory
     assert B.lib().moe_pack_w13(0x10000, 0x80000, 4, 128, 512, 0x100000, 0x180000, None) == B.MOE_ERR_DEVICE
+
+
+def test_header_compiles_as_plain_c(tmp_path):
+    """include/qmoe.h is a C ABI: it compiles as C99 (pedantic) and as C++."""
+    import shutil
+    import subprocess
+
+    if shutil.which("gcc") is None:
+        pytest.skip("no host C compiler")
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    src = tmp_path / "use.c"
+    src.write_text('#include "qmoe.h"\nint main(void) { moe_plan* p = 0; '
+                   'return (int)moe_plan_set_mid_format(p, MOE_MID_MXFP4) + (int)moe_plan_set_shared_slot(p, 1); }\n')
+    for cmd in (["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only"],
+                ["g++", "-std=c++17", "-Wall", "-Wextra", "-Werror", "-fsyntax-only", "-x", "c++"]):
+        r = subprocess.run(cmd + ["-I", inc, str(src)], capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
