@@ -343,3 +343,19 @@ def test_shared_slot_equals_routed_plus_shared_expert():
     ref = O.combine(routed["w"], routed["y"].reshape(shape.M, k - 1, shape.H), ysh)
     assert np.array_equal(fused["out"], ref)
     assert np.array_equal(fused["out"], _run(d, fn=O.moe_dense, shared_slot=True))
+
+
+def test_shared_slot_workloads_extend_c1_and_c2():
+    """c1s / c2s are c1 / c2 with one more expert: the same x, the same
+    routed experts' weights and logits; the shared expert's logits column is
+    present but never read, and the oracle's routed slots equal c1's / c2's."""
+    for fused, base in (("c1s", "c1"), ("c2s", "c2")):
+        d, b = X.make_inputs(fused), X.make_inputs(base)
+        E = b["shape"].E
+        assert d["shape"].E == E + 1 and d["shape"].top_k == b["shape"].top_k + 1
+        assert np.array_equal(d["x"], b["x"]) and np.array_equal(d["logits"][:, :E], b["logits"])
+        for key in ("w13", "s13", "w2", "s2"):
+            assert np.array_equal(d[key][:E], b[key])
+        ids, w = O.route_shared_slot(d["logits"], d["shape"].top_k, 2.5)
+        ids_b, w_b = O.route(b["logits"], b["shape"].top_k, 2.5)
+        assert np.array_equal(ids[:, :-1], ids_b) and np.array_equal(w[:, :-1], w_b)
