@@ -166,3 +166,40 @@ def test_fp8_block_quantize_identity_and_scale():
     # zero block
     c, s = F.fp8_block_quantize(np.zeros((1, 128), np.float32))
     assert s[0, 0] == 0 and np.all(c & 0x7F == 0)
+
+
+def _fl32_exact(q):
+    """Nearest binary32 to the rational q (ties to the even significand), by
+    exact comparison with the neighbours of a first guess."""
+    from fractions import Fraction
+
+    f = np.float32(float(q))
+    cands = [np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))]
+    best = min(cands, key=lambda c: (abs(Fraction(float(c)) - q), int(np.float32(c).view(np.uint32)) & 1))
+    return np.float32(best)
+
+
+@pytest.mark.parametrize("amax_bits,h_bits", [(1080849678, 1052916628), (1076355820, 1066788362),
+                                             (1081177291, 990226892), (1057125413, 1029067032)])
+def test_fp8_block_quantize_divides(amax_bits, h_bits):
+    """Codes come from the IEEE quotient fl32(h / s), not from h * fl32(1/s):
+    on these (amax, h) pairs the two land on opposite sides of an E4M3
+    rounding midpoint (pairs found by a seeded search over midpoints). The
+    expected code is derived independently: the exact rational quotient
+    rounded to binary32 by comparison, then torch's E4M3 cast."""
+    import torch
+    from fractions import Fraction
+
+    amax = np.array([amax_bits], np.uint32).view(np.float32)[0]
+    h = np.array([h_bits], np.uint32).view(np.float32)[0]
+    block = np.zeros((1, 128), np.float32)
+    block[0, 0] = amax
+    block[0, 5] = h
+    c, s = F.fp8_block_quantize(block)
+    s_ref = _fl32_exact(Fraction(float(amax)) / 448)
+    assert s[0, 0] == s_ref
+    q = _fl32_exact(Fraction(float(h)) / Fraction(float(s_ref)))
+    want = torch.tensor([float(q)], dtype=torch.float32).to(torch.float8_e4m3fn).view(torch.uint8).item()
+    assert int(c[0, 5]) == want
+    recip = np.float32(h * np.float32(np.float32(1.0) / s_ref))
+    assert int(F.e4m3_encode(np.float64(recip))) != want, "the case must tell division from reciprocal"

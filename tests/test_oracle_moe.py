@@ -359,3 +359,68 @@ def test_shared_slot_workloads_extend_c1_and_c2():
         ids, w = O.route_shared_slot(d["logits"], d["shape"].top_k, 2.5)
         ids_b, w_b = O.route(b["logits"], b["shape"].top_k, 2.5)
         assert np.array_equal(ids[:, :-1], ids_b) and np.array_equal(w[:, :-1], w_b)
+
+
+# ------------------------------------------------------------ shared expert, whole chain
+def _e4m3_grid(rng, shape):
+    return (rng.integers(0, 126, size=shape) | (rng.integers(0, 2, size=shape) << 7)).astype(np.uint8)
+
+
+def _torch_fp8_quant(h):
+    """Per-128 E4M3 quantization written with torch ops (an independent
+    library): s = amax / 448 in binary32, codes = torch's E4M3 cast of h / s."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(h, np.float32)).reshape(h.shape[0], -1, 128)
+    s = t.abs().amax(-1) / 448.0
+    safe = torch.where(s > 0, s, torch.ones_like(s))
+    q = (t / safe[..., None]).to(torch.float8_e4m3fn).to(torch.float64)
+    q = torch.where(s[..., None] > 0, q, torch.zeros_like(q))
+    return q.reshape(h.shape).numpy(), s.numpy()
+
+
+def test_shared_expert_chain_on_grid():
+    """The block-FP8 shared expert as an explicit chain. x on the E4M3 grid
+    with every 128-block's amax 448 (so its quantization is the identity) and
+    unit weight scales make the first GEMM a plain float64 matmul; then
+    h = fl32(SiLU(gate rows [0, Is)) * up rows [Is, 2 Is)), h requantized per
+    128 with torch's E4M3 cast, and the down GEMM with per-128x128 scales
+    (powers of two per block, to see each block scale land on its block)."""
+    rng = np.random.default_rng(11)
+    M, H, Is = 3, 256, 256
+    xc = _e4m3_grid(rng, (M, H))
+    xc[:, ::128] = 0x7E  # +448 in every block
+    xv = F.e4m3_decode(xc)
+    x_bits = F.bf16_encode(xv)  # E4M3 values are exact in bf16
+    ws13 = _e4m3_grid(rng, (2 * Is, H))
+    ss13 = np.ones((2 * Is // 128, H // 128), np.float32)
+    ws2 = _e4m3_grid(rng, (H, Is))
+    ss2 = np.array([[1.0, 0.25], [4.0, 0.5]], np.float32)  # [H/128, Is/128]
+    y, inter = O.shared_expert(x_bits, ws13, ss13, ws2, ss2)
+    assert np.array_equal(inter["xq8"], xc) and np.all(inter["xs8"] == 1.0)
+
+    w13v = F.e4m3_decode(ws13)
+    g = np.matmul(xv, w13v[:Is].T).astype(np.float32).astype(np.float64)
+    u = np.matmul(xv, w13v[Is:].T).astype(np.float32).astype(np.float64)
+    h = (g / (1.0 + np.exp(-g)) * u).astype(np.float32)
+    assert np.array_equal(inter["h"], h)
+    qv, hs = _torch_fp8_quant(h)
+    assert np.array_equal(inter["hs"], hs)
+    assert np.array_equal(F.e4m3_decode(inter["hq"]), qv)
+    w2v = F.e4m3_decode(ws2)
+    acc = np.zeros((M, H))
+    for b in range(Is // 128):
+        blk = slice(128 * b, 128 * (b + 1))
+        S = np.matmul(qv[:, blk], w2v[:, blk].T)
+        acc += hs[:, b].astype(np.float64)[:, None] * np.repeat(ss2[:, b].astype(np.float64), 128)[None, :] * S
+    assert np.array_equal(y, acc.astype(np.float32))
+
+    # plausible mistakes change the result
+    swapped = np.concatenate([ws13[Is:], ws13[:Is]])
+    assert not np.array_equal(O.shared_expert(x_bits, swapped, ss13, ws2, ss2)[0], y)
+    h_wrong = (u / (1.0 + np.exp(-u)) * g).astype(np.float32)  # SiLU on the up half
+    assert not np.array_equal(h_wrong, h)
+    y_unquant = np.matmul(h.astype(np.float64), w2v.T)  # h not requantized
+    assert not np.array_equal(y_unquant.astype(np.float32), y)
+    ss2_t = np.ascontiguousarray(ss2[::-1])  # block scales on the wrong output rows
+    assert not np.array_equal(O.shared_expert(x_bits, ws13, ss13, ws2, ss2_t)[0], y)
