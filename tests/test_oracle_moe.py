@@ -393,15 +393,17 @@ def test_shared_expert_chain_on_grid():
     xv = F.e4m3_decode(xc)
     x_bits = F.bf16_encode(xv)  # E4M3 values are exact in bf16
     ws13 = _e4m3_grid(rng, (2 * Is, H))
-    ss13 = np.ones((2 * Is // 128, H // 128), np.float32)
+    # one power-of-two weight scale puts g and u in SiLU's curved range
+    ss13 = np.full((2 * Is // 128, H // 128), 2.0 ** -17, np.float32)
     ws2 = _e4m3_grid(rng, (H, Is))
     ss2 = np.array([[1.0, 0.25], [4.0, 0.5]], np.float32)  # [H/128, Is/128]
     y, inter = O.shared_expert(x_bits, ws13, ss13, ws2, ss2)
     assert np.array_equal(inter["xq8"], xc) and np.all(inter["xs8"] == 1.0)
 
     w13v = F.e4m3_decode(ws13)
-    g = np.matmul(xv, w13v[:Is].T).astype(np.float32).astype(np.float64)
-    u = np.matmul(xv, w13v[Is:].T).astype(np.float32).astype(np.float64)
+    g = (np.matmul(xv, w13v[:Is].T) * 2.0 ** -17).astype(np.float32).astype(np.float64)
+    u = (np.matmul(xv, w13v[Is:].T) * 2.0 ** -17).astype(np.float32).astype(np.float64)
+    assert 0.5 < np.median(np.abs(g)) < 8.0
     h = (g / (1.0 + np.exp(-g)) * u).astype(np.float32)
     assert np.array_equal(inter["h"], h)
     qv, hs = _torch_fp8_quant(h)
