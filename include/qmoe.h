@@ -26,8 +26,8 @@
  *     never synchronizes a stream. `stream` is a hipStream_t (NULL = the
  *     default stream). All GPU work of a call is enqueued on that stream in
  *     order, so a call may be captured into a HIP graph.
- *   - Arguments are validated before anything is enqueued; on an error
- *     nothing is launched and nothing is written.
+ *   - Arguments are validated before anything is enqueued; on a validation
+ *     error nothing is launched and nothing is written.
  *   - MXFP4 bytes hold two E2M1 codes, element 2i in the low nibble.
  *   - One plan, with its workspace, serves one stream at a time.
  */
@@ -78,10 +78,13 @@ typedef struct moe_plan moe_plan; /* opaque; host memory only */
  *                                   written only by calls with M > 16 (up to
  *                                   16 tokens the combine runs in the down
  *                                   launch and slot results stay on chip)
- *   sh_xq/sh_xs  u8 [M, H] / fp32 [H/128, M]      shared expert x in E4M3
- *   sh_hq/sh_hs  u8 [M, Is] / fp32 [Is/128, M]    shared expert mid in E4M3
- *                                   (scales K-block major: block b of token t
- *                                   at b * M + t)
+ *   sh_xq/sh_xs  i8 [M, H/128, 3, 128] / fp32 [H/128, M]  shared expert x
+ *   sh_hq/sh_hs  i8 [M, Is/128, 3, 128] / fp32 [Is/128, M] shared expert mid
+ *                                   (E4M3 values v as digit rows: for each
+ *                                   128-block, three planes of 128 int8 d0,
+ *                                   d1, d2 with v * 2^9 = d0 + 2^7 d1 +
+ *                                   2^14 d2, all of v's sign; scales K-block
+ *                                   major: block b of token t at b * M + t)
  *   sh_y         fp32  [M, H]       shared expert output
  * Offsets of absent parts (no shared expert) are 0. */
 typedef struct {
@@ -122,13 +125,28 @@ moe_status moe_plan_layout(const moe_plan* plan, moe_ws_layout* out);
  * misaligned, MOE_ERR_DEVICE if it lives on another device. */
 moe_status moe_plan_set_workspace(moe_plan* plan, void* workspace, size_t bytes, void* stream);
 
-/* Bind the block-FP8 shared expert (required iff shape.shared_I > 0):
+/* Bytes of the device buffer moe_plan_set_shared packs the shared expert's
+ * weights into: 9 * shared_I * H (0 for a plan without a shared expert). */
+size_t moe_plan_shared_pack_bytes(const moe_plan* plan);
+
+/* Bind the block-FP8 shared expert (required iff shape.shared_I > 0; "IQ2R:
+ * load GLM-5.3 packed MoE checkpoints with TP slicing", Summary: the shared
+ * experts keep the base model's block-FP8 configuration). Inputs, row-major:
  *   ws13 u8 (E4M3) [2*Is, H]  rows [0, Is) gate, [Is, 2*Is) up
  *   ss13 fp32 [2*Is/128, H/128]  one scale per 128x128 block
  *   ws2  u8 (E4M3) [H, Is];  ss2 fp32 [H/128, Is/128]
- * Pointers are kept, not copied; they must stay valid while the plan is used. */
-moe_status moe_plan_set_shared(moe_plan* plan, const void* ws13, const float* ss13,
-                               const void* ws2, const float* ss2);
+ * `packed` is a caller-owned device buffer of at least
+ * moe_plan_shared_pack_bytes(plan) bytes, not overlapping the inputs; the
+ * call enqueues on `stream` the one-time rewrite of ws13 and ws2 into it
+ * (each E4M3 value as three int8 digits of its value times 2^9, the
+ * operands of the exact int8-MFMA GEMMs; nothing is rounded). The plan
+ * keeps `packed`, ss13 and ss2 (not copied: they must stay valid while the
+ * plan is used); ws13 and ws2 are read only by the enqueued rewrite.
+ * MOE_ERR_INVALID_ARG for null or misaligned pointers, a plan without a
+ * shared expert, a short or overlapping `packed`; MOE_ERR_DEVICE for
+ * pointers on another device than the plan's. */
+moe_status moe_plan_set_shared(moe_plan* plan, const void* ws13, const float* ss13, const void* ws2,
+                               const float* ss2, void* packed, size_t packed_bytes, void* stream);
 
 /* Format of the mid hand-off between gate/up and down. MOE_MID_E4M3 (the
  * default): one E4M3 code per element and an fp32 scale per 128 ("glm53: FP8
@@ -211,7 +229,11 @@ moe_status moe_pack_w2(const void* w2, const void* s2, int64_t E, int64_t I, int
  *   out    bf16 [M, H]  fully overwritten; must not alias any input
  * Returns after enqueueing; faults inside kernels surface at the caller's
  * next synchronisation. MOE_ERR_WORKSPACE if no workspace is bound,
- * MOE_ERR_INVALID_ARG if the shared expert is required but not bound. */
+ * MOE_ERR_INVALID_ARG if the shared expert is required but not bound.
+ * MOE_ERR_HIP when a launch fails once the call has started enqueueing: the
+ * launches already enqueued stay (and may write the workspace and `out`),
+ * and the workspace is unbound, so later calls return MOE_ERR_WORKSPACE
+ * until moe_plan_set_workspace binds (and re-initialises) one again. */
 moe_status moe_forward(moe_plan* plan, int64_t M, const void* x, const float* logits,
                        const void* w13, const void* s13, const void* w2, const void* s2,
                        void* out, void* stream);

@@ -68,7 +68,9 @@ def lib() -> ctypes.CDLL:
     L.moe_plan_set_workspace.restype = st
     L.moe_plan_set_workspace.argtypes = [vp, vp, ctypes.c_size_t, vp]
     L.moe_plan_set_shared.restype = st
-    L.moe_plan_set_shared.argtypes = [vp, vp, vp, vp, vp]
+    L.moe_plan_set_shared.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.moe_plan_shared_pack_bytes.restype = ctypes.c_size_t
+    L.moe_plan_shared_pack_bytes.argtypes = [vp]
     L.moe_plan_set_stage_events.restype = st
     L.moe_plan_set_stage_events.argtypes = [vp, ctypes.POINTER(vp), ctypes.c_int]
     L.moe_plan_set_call_events.restype = st
@@ -184,11 +186,20 @@ class Plan:
             raise MoeError(st, "moe_plan_layout")
         return {f: getattr(L, f) for f in LAYOUT_FIELDS}
 
-    def set_shared(self, ws13, ss13, ws2, ss2):
-        self._shared = (ws13, ss13, ws2, ss2)  # keep the tensors alive
-        st = lib().moe_plan_set_shared(self._h, _ptr(ws13), _ptr(ss13), _ptr(ws2), _ptr(ss2))
+    def set_shared(self, ws13, ss13, ws2, ss2, stream=None):
+        """Bind the block-FP8 shared expert: row-major E4M3 ws13 [2 Is, H] and
+        ws2 [H, Is] (uint8), fp32 block scales ss13 [2 Is/128, H/128] and ss2
+        [H/128, Is/128]. The library packs the weights into a buffer this
+        object allocates and keeps (with the scales)."""
+        import torch
+
+        nbytes = lib().moe_plan_shared_pack_bytes(self._h)
+        packed = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=self.device)
+        st = lib().moe_plan_set_shared(self._h, _ptr(ws13), _ptr(ss13), _ptr(ws2), _ptr(ss2), _ptr(packed),
+                                       packed.numel(), _stream(stream))
         if st != MOE_OK:
             raise MoeError(st, "moe_plan_set_shared")
+        self._shared = (ss13, ss2, packed)  # kept alive while the plan uses them
 
     def set_shared_slot(self, on: bool):
         """Expert E-1 as the shared expert, fused as the last slot of every token."""

@@ -78,10 +78,10 @@ Layout make_layout(const moe_shape& s) {
   r.L.mids = take(4 * n * (I / 128));
   r.L.y = take(4 * n * H);
   if (Is > 0) {
-    r.L.sh_xq = take(M * H);
+    r.L.sh_xq = take(3 * M * H);  // int8 digit rows
     r.L.sh_xs = take(4 * M * (H / 128));
     r.X.sh_h = take(4 * M * Is);
-    r.L.sh_hq = take(M * Is);
+    r.L.sh_hq = take(3 * M * Is);
     r.L.sh_hs = take(4 * M * (Is / 128));
     r.L.sh_y = take(4 * M * H);
   }
@@ -220,18 +220,35 @@ moe_status moe_plan_set_workspace(moe_plan* plan, void* workspace, size_t bytes,
   return MOE_OK;
 }
 
+size_t moe_plan_shared_pack_bytes(const moe_plan* plan) {
+  if (!plan || plan->s.shared_I == 0) return 0;
+  return (size_t)9 * (size_t)plan->s.shared_I * (size_t)plan->s.H;  // three digit planes of 3 Is x H values
+}
+
 moe_status moe_plan_set_shared(moe_plan* plan, const void* ws13, const float* ss13, const void* ws2,
-                               const float* ss2) {
+                               const float* ss2, void* packed, size_t packed_bytes, void* stream) {
   if (!plan) return MOE_ERR_INVALID_ARG;
   if (plan->s.shared_I == 0) return MOE_ERR_INVALID_ARG;
-  const void* ptrs[4] = {ws13, ss13, ws2, ss2};
+  const void* ptrs[5] = {ws13, ss13, ws2, ss2, packed};
   for (const void* q : ptrs) {
     if (!q || !aligned16(q)) return MOE_ERR_INVALID_ARG;
     if (ptr_device(q) != plan->device) return MOE_ERR_DEVICE;
   }
-  plan->ws13 = ws13;
+  const size_t Is = (size_t)plan->s.shared_I, H = (size_t)plan->s.H;
+  const size_t need = moe_plan_shared_pack_bytes(plan);
+  if (packed_bytes < need) return MOE_ERR_INVALID_ARG;
+  if (overlaps(packed, need, ws13, 2 * Is * H) || overlaps(packed, need, ws2, H * Is) ||
+      overlaps(packed, need, ss13, 4 * (2 * Is / 128) * (H / 128)) ||
+      overlaps(packed, need, ss2, 4 * (H / 128) * (Is / 128)))
+    return MOE_ERR_INVALID_ARG;
+  DeviceGuard guard(plan->device);
+  if (!guard.ok) return MOE_ERR_DEVICE;
+  if (launch_pack_shared(ws13, ws2, (int64_t)Is, (int64_t)H, packed, (hipStream_t)stream) != hipSuccess) {
+    plan->ws13 = nullptr;
+    return MOE_ERR_HIP;
+  }
+  plan->ws13 = packed;
   plan->ss13 = ss13;
-  plan->ws2 = ws2;
   plan->ss2 = ss2;
   return MOE_OK;
 }
@@ -381,7 +398,14 @@ moe_status moe_forward(moe_plan* plan, int64_t M, const void* x, const float* lo
   if (e == hipSuccess)
     e = mx ? launch_down_fp4(plan, a, ev[5]) : small ? launch_down_combine(plan, a, ev[5]) : launch_down_big(plan, a, ev[5]);
   if (e == hipSuccess) e = fused_combine ? none(6) : launch_combine(plan, a, ev[6]);
-  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  if (e != hipSuccess) {
+    // a launch after the routing may have left bits in the token bitmap that
+    // only the sort clears: unbind the workspace so that no later call runs
+    // on it before moe_plan_set_workspace zeroes it again
+    plan->ws = nullptr;
+    return MOE_ERR_HIP;
+  }
+  return MOE_OK;
 }
 
 }  // extern "C"

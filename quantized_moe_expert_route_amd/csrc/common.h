@@ -115,6 +115,63 @@ __device__ __forceinline__ uint32_t e4m3_code(float v) {
   return c | sign;
 }
 
+// E4M3 value times 2^9 as base-128 digits. Every E4M3 value is an integer
+// multiple of 2^-9 (the subnormal step) of magnitude <= 448, so v * 2^9 is an
+// integer below 2^18: v * 2^9 = d0 + 2^7 d1 + 2^14 d2 with the value's sign
+// on every digit, |d0|, |d1| <= 127, |d2| <= 14. Returns d0, d1, d2 as int8
+// in bytes 0, 1, 2. Products of such digits summed by the int8 MFMA are exact
+// integers, which makes E4M3 x E4M3 block sums exact.
+__device__ __forceinline__ uint32_t e4m3_digits(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const uint32_t mag = e ? ((8u | m) << (e - 1)) : m;
+  uint32_t u0 = mag & 127u, u1 = (mag >> 7) & 127u, u2 = mag >> 14;
+  if (c & 0x80u) {
+    u0 = (0u - u0) & 255u;
+    u1 = (0u - u1) & 255u;
+    u2 = (0u - u2) & 255u;
+  }
+  return u0 | (u1 << 8) | (u2 << 16);
+}
+
+// Four E4M3 codes (a dword, first code in the low byte) -> their digit planes:
+// byte q of plane p is digit p of code q.
+__device__ __forceinline__ void e4m3x4_digits(uint32_t w, uint32_t& p0, uint32_t& p1, uint32_t& p2) {
+  p0 = p1 = p2 = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t d = e4m3_digits((w >> (8 * q)) & 255u);
+    p0 |= (d & 255u) << (8 * q);
+    p1 |= ((d >> 8) & 255u) << (8 * q);
+    p2 |= (d >> 16) << (8 * q);
+  }
+}
+
+// Operand layout of the shared-expert GEMMs ("digit rows"): a row of K E4M3
+// values is stored as [K/128][3][128] int8: for each 128-block, digit plane 0,
+// then 1, then 2 of its 128 values (e4m3_digits), so a row's block is one
+// contiguous 384-byte run.
+constexpr int kShDigitBlock = 3 * 128;
+
+// 8 E4M3 codes (lo, hi: first code in the low byte) of elements off..off+7 of
+// a 128-block -> their digits at `blk` (the block's 384-byte run).
+__device__ __forceinline__ void store_digits8(uint8_t* blk, int off, uint32_t lo, uint32_t hi) {
+  uint32_t a0, a1, a2, b0, b1, b2;
+  e4m3x4_digits(lo, a0, a1, a2);
+  e4m3x4_digits(hi, b0, b1, b2);
+  *reinterpret_cast<uint2*>(blk + off) = make_uint2(a0, b0);
+  *reinterpret_cast<uint2*>(blk + 128 + off) = make_uint2(a1, b1);
+  *reinterpret_cast<uint2*>(blk + 256 + off) = make_uint2(a2, b2);
+}
+
+// 2 E4M3 codes (low byte first) of elements off, off+1 -> their digits.
+__device__ __forceinline__ void store_digits2(uint8_t* blk, int off, uint32_t c01) {
+  uint32_t p0, p1, p2;
+  e4m3x4_digits(c01, p0, p1, p2);
+  *reinterpret_cast<uint16_t*>(blk + off) = (uint16_t)p0;
+  *reinterpret_cast<uint16_t*>(blk + 128 + off) = (uint16_t)p1;
+  *reinterpret_cast<uint16_t*>(blk + 256 + off) = (uint16_t)p2;
+}
+
 // E4M3 code -> bf16 bits (every E4M3 value is exact in bf16).
 __host__ __device__ constexpr uint16_t e4m3_to_bf16_bits(uint32_t c) {
   uint32_t s = (c & 0x80u) << 8;
@@ -152,6 +209,17 @@ __device__ __forceinline__ v4f mfma_fp4(uint4 a, uint4 b, v4f c, uint32_t sa, ui
   v8i A = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
   v8i B = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, c, 4, 4, 0, (int)sa, 0, (int)sb);
+}
+
+// v_mfma_i32_16x16x64_i8: lane l holds row (A) / column (B) l%16 and 16
+// int8 K elements; A and B take the same K bytes from a lane, so the exact
+// int32 dot products do not depend on the order the unit reads them in.
+// D: lane l, element i = D[4*(l/16)+i][l%16].
+typedef int v4i __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4i mfma_i8(uint4 a, uint4 b, v4i c) {
+  const v4i A = {(int)a.x, (int)a.y, (int)a.z, (int)a.w};
+  const v4i B = {(int)b.x, (int)b.y, (int)b.z, (int)b.w};
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, c, 0, 0, 0);
 }
 
 // v_mfma_f32_16x16x32_bf16: lane l holds row/column l%16 and K elements

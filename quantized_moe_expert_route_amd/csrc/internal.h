@@ -44,9 +44,8 @@ struct moe_plan {
   qmoe::Internal X;
   uint8_t* ws;
   size_t ws_bytes;
-  const void* ws13;
+  const void* ws13;   // the shared expert's gate/up and down weights as digit rows (moe_plan_set_shared)
   const float* ss13;
-  const void* ws2;
   const float* ss2;
   hipEvent_t events[16];
   int n_events;
@@ -118,6 +117,10 @@ hipError_t launch_act_quant(const moe_plan* p, const CallArgs& a, Ev ev);
 int down_combine_cols(int H, int cus);
 hipError_t launch_down_combine(const moe_plan* p, const CallArgs& a, Ev ev);
 hipError_t launch_shared(const moe_plan* p, const CallArgs& a, Ev ev);
+// row-major E4M3 shared-expert weights -> digit rows: gate/up [2 Is, H/128,
+// 3, 128], then down [H, Is/128, 3, 128], at `packed` (shared.hip)
+hipError_t launch_pack_shared(const void* ws13, const void* ws2, int64_t Is, int64_t H, void* packed,
+                              hipStream_t stream);
 // large M: LDS-staged tiles (kGuRows rows for gate/up, which includes the mid
 // quantization; kBigRows rows for down)
 hipError_t launch_gate_up_big(const moe_plan* p, const CallArgs& a, Ev ev);

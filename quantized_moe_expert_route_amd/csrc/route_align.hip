@@ -241,8 +241,8 @@ __global__ __launch_bounds__(1024) void route_align_small_kernel(
 // x of one token, 8 elements a lane, 512 a load instruction (whole cache
 // lines): the 4 lanes of a 32-block form its E8M0 scale and E2M1 codes (the
 // same arithmetic as quant_block_mx), and with SH the 16 lanes of a
-// 128-block also form the shared expert's E4M3 codes and fp32 scale, so x is
-// read once for both. A unit is kXU loads of one row.
+// 128-block also form the shared expert's E4M3 codes (stored as int8 digits)
+// and fp32 scale, so x is read once for both. A unit is kXU loads of one row.
 constexpr int kXU = 4;
 
 template <bool SH>
@@ -291,7 +291,8 @@ __device__ __forceinline__ void quant_x_unit(const uint16_t* __restrict__ x, int
           if (q < 2) lo |= c << (16 * q); else hi |= c << (16 * (q - 2));
         }
       }
-      *reinterpret_cast<uint2*>(sq + (size_t)t * H + e0) = make_uint2(lo, hi);
+      // as digit rows ([H/128][3][128] per token) for the exact int8 GEMM
+      store_digits8(sq + ((size_t)t * (H >> 7) + (e0 >> 7)) * kShDigitBlock, e0 & 127, lo, hi);
       if ((lane & 15) == 0) ss[(size_t)(e0 >> 7) * M + t] = sc;
     }
   }

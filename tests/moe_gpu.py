@@ -72,12 +72,31 @@ def read_intermediates(plan, s, M):
     }
     if s.shared_I:
         Is = s.shared_I
-        r["sh_xq"] = v("sh_xq", torch.uint8, (M, H))
+        r["sh_xq"] = v("sh_xq", torch.int8, (M, H // 128, 3, 128))
         r["sh_xs"] = v("sh_xs", torch.float32, (H // 128, M)).t()  # stored K-block major
-        r["sh_hq"] = v("sh_hq", torch.uint8, (M, Is))
+        r["sh_hq"] = v("sh_hq", torch.int8, (M, Is // 128, 3, 128))
         r["sh_hs"] = v("sh_hs", torch.float32, (Is // 128, M)).t()
         r["sh_y"] = v("sh_y", torch.float32, (M, H))
-    return {key: t.cpu().numpy() for key, t in r.items()}
+    out = {key: t.cpu().numpy() for key, t in r.items()}
+    for key in ("sh_xq", "sh_hq"):
+        if key in out:
+            out[key] = digit_rows_to_codes(out[key])
+    return out
+
+
+def digit_rows_to_codes(d):
+    """Shared-expert operands as stored, [rows, K/128, 3, 128] int8 digits d0,
+    d1, d2 of v * 2^9 = d0 + 2^7 d1 + 2^14 d2, -> E4M3 codes [rows, K] (a zero
+    value gives code 0; compare decoded values where -0 may occur)."""
+    d = d.astype(np.int64)
+    alpha = d[:, :, 0] + 128 * d[:, :, 1] + 16384 * d[:, :, 2]
+    v = np.ldexp(alpha.astype(np.float64), -9).reshape(d.shape[0], -1)
+    codes = F.e4m3_encode(v)
+    assert np.array_equal(F.e4m3_decode(codes), v), "digits do not form E4M3 values"
+    # the three digits of a value carry its sign
+    s = np.sign(d)
+    assert np.all((s[:, :, 0] * s[:, :, 1] >= 0) & (s[:, :, 0] * s[:, :, 2] >= 0) & (s[:, :, 1] * s[:, :, 2] >= 0))
+    return codes
 
 
 def oracle(d, tokens=None, **kw):

@@ -69,7 +69,7 @@ def test_workspace_holds_the_documented_intermediates():
     nbytes = B.shape_workspace_bytes(M, H, E, I, k, 2.5, Is)
     n = M * k
     documented = (4 * n * 3 + 4 * E + 4 * (E + 1) + M * H // 2 + M * H // 32 + n * I + 4 * n * I // 128
-                  + 4 * n * H + M * H + 4 * M * H // 128 + M * Is + 4 * M * Is // 128 + 4 * M * H)
+                  + 4 * n * H + 3 * M * H + 4 * M * H // 128 + 3 * M * Is + 4 * M * Is // 128 + 4 * M * H)
     assert nbytes >= documented
     assert nbytes < documented * 1.5
 
@@ -86,6 +86,8 @@ def test_null_and_unbound_arguments_fail_before_any_device_work():
     assert L.moe_plan_workspace_bytes(None) == 0
     assert L.moe_plan_set_mid_format(None, B.MID_MXFP4) == B.MOE_ERR_INVALID_ARG
     assert L.moe_plan_set_shared_slot(None, 1) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_plan_set_shared(None, None, None, None, None, None, 0, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_plan_shared_pack_bytes(None) == 0
     L.moe_plan_destroy(None)
 
 
