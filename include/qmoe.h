@@ -83,8 +83,10 @@ typedef struct moe_plan moe_plan; /* opaque; host memory only */
  *                                   (E4M3 values v as digit rows: for each
  *                                   128-block, three planes of 128 int8 d0,
  *                                   d1, d2 with v * 2^9 = d0 + 2^7 d1 +
- *                                   2^14 d2, all of v's sign; scales K-block
- *                                   major: block b of token t at b * M + t)
+ *                                   2^14 d2, all of v's sign; rows past M,
+ *                                   up to a multiple of 128, are padding;
+ *                                   scales K-block major: block b of token t
+ *                                   at b * M + t)
  *   sh_y         fp32  [M, H]       shared expert output
  * Offsets of absent parts (no shared expert) are 0. */
 typedef struct {

@@ -78,10 +78,12 @@ Layout make_layout(const moe_shape& s) {
   r.L.mids = take(4 * n * (I / 128));
   r.L.y = take(4 * n * H);
   if (Is > 0) {
-    r.L.sh_xq = take(3 * M * H);  // int8 digit rows
+    // int8 digit rows, padded to whole 128-row tiles of the shared-expert GEMMs
+    const size_t M128 = (M + 127) / 128 * 128;
+    r.L.sh_xq = take(3 * M128 * H);
     r.L.sh_xs = take(4 * M * (H / 128));
     r.X.sh_h = take(4 * M * Is);
-    r.L.sh_hq = take(3 * M * Is);
+    r.L.sh_hq = take(3 * M128 * Is);
     r.L.sh_hs = take(4 * M * (Is / 128));
     r.L.sh_y = take(4 * M * H);
   }

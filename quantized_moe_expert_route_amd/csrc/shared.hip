@@ -15,7 +15,7 @@
 // MFMA returns it in every case. Here every E4M3 operand is held as three
 // base-128 int8 digits of v * 2^9 (e4m3_digits) and the int8 MFMA sums the
 // nine digit-pair products exactly in int32; the five power-of-128 sums of a
-// block are folded into two int32 (no overflow: see sh_fold) and one exact
+// block are folded into two int32 (no overflow: see the bounds below) and one exact
 // float64. The block sum times (activation scale x weight scale) is then
 // formed and added in float64 in block order and rounded once to fp32.
 #include "common.h"
@@ -97,42 +97,56 @@ __global__ __launch_bounds__(256) void sh_pack_kernel(const uint8_t* __restrict_
 // SiLU(g) * u, g and u from weight rows o and o + n_out.
 //
 // Workgroup tile: 128 token rows x 64 weight rows (GATED: 32 gate + the 32
-// matching up rows, 32 outputs; else 64 outputs), one 128-K block per step,
-// both operands' three digit planes staged in LDS (two buffers, one register
-// stage of loads in flight; loads cover whole 128-byte lines). Each of 8
-// waves owns 32 rows x 32 weight rows (GATED: 16 gate + 16 up) as 2 x 2
-// int8-MFMA tiles with five int32 accumulators each, one per power of 128.
+// matching up rows, 32 outputs; else 64 outputs), one 128-K block per step.
+// Both operands' three digit planes go from global memory straight into LDS
+// (global_load_lds: each wave instruction fills one contiguous 1 KB, eight
+// 128-byte rows, every lane fetching the chunk the swizzle puts at its
+// place), two stage buffers, the next block's loads issued before the
+// current block is multiplied. Each of 8 waves owns 32 rows x 32 weight
+// rows (GATED: 16 gate + 16 up) as 2 x 2 int8-MFMA tiles with five int32
+// accumulators each, one per power of 128.
 constexpr int kShBM = 128;  // token rows per tile
 constexpr int kShBN = 64;   // weight rows per tile
 constexpr int kShThreads = 512;
 
 // Staged 128-byte rows, 16-byte chunk c of row R at R * 128 + 16 * (c ^ ((R >> 1) & 7)):
-// a 16-byte access of 16 lanes is served by the 64 banks together, and both
-// the staging stores (8 lanes a row, two rows) and the fragment reads (16
-// rows, one chunk) then meet 16 different 16-byte bank groups.
+// a 16-byte access of 16 lanes is served by the 64 banks together, and the
+// fragment reads (16 rows, one chunk) then meet 16 different 16-byte bank
+// groups.
 __device__ __forceinline__ int sw128(int row, int chunk) { return row * 128 + 16 * (chunk ^ ((row >> 1) & 7)); }
 
-struct alignas(16) ShSmem {  // 16-byte aligned: every LDS access is one b128 op
-  uint8_t a[2][3][kShBM * 128];
-  uint8_t b[2][3][kShBN * 128];
-  float as[2][kShBM];
+struct alignas(16) ShStage {  // 16-byte aligned: every fragment read is one b128 op
+  uint8_t a[3][kShBM * 128];
+  uint8_t b[3][kShBN * 128];
+  float as[kShBM];
 };
 
-struct ShRegs {
-  uint4 a0[3], a1[3], b[3];
-  float sa;
-};
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void gbl_void;
 
-// Block sum of one output from its five power sums P_p = sum over digit pairs
+// 16 bytes a lane from global memory into LDS at dst + 16 * lane (dst the
+// same for the whole wave)
+__device__ __forceinline__ void dma16(const uint8_t* src, uint8_t* dst) {
+  __builtin_amdgcn_global_load_lds((gbl_void*)src, (lds_void*)dst, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(0): the wave's loads into LDS have landed
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Block sums from the five power sums P_p = sum over digit pairs
 // (i, j) with i + j = p of the int8 dot products. T = sum_p 128^p P_p is the
 // block's exact sum times 2^18. Bounds (128 products, |d0|,|d1| <= 127,
 // |d2| <= 14): |P0| < 2^21, |P1| < 2^22, so LOW = P0 + 2^7 P1 < 2^30;
 // |P2| < 2^21.3, |P3| < 2^18.8, |P4| < 2^14.7, so HIGH = P2 + 2^7 P3 +
 // 2^14 P4 < 2^29; T = 2^14 HIGH + LOW < 2^44 is exact in float64.
-__device__ __forceinline__ double sh_fold(int p0, int p1, int p2, int p3, int p4) {
-  const int lo = p0 + p1 * 128;
-  const int hi = p2 + p3 * 128 + p4 * 16384;
-  return fma((double)hi, 16384.0, (double)lo);
+//
+// acc + fl64(s * T) with the product rounded on its own, as the block sums'
+// scaling and accumulation are defined (s * T needs up to ~92 bits: a fused
+// multiply-add would round once where the definition rounds twice)
+__device__ __forceinline__ double add_scaled(double acc, double s, double T) {
+#pragma clang fp contract(off)
+  const double t = s * T;
+  return acc + t;
 }
 
 template <bool GATED>
@@ -141,46 +155,52 @@ __global__ __launch_bounds__(kShThreads, 1) void sh_gemm_kernel(const uint8_t* _
                                                                 const uint8_t* __restrict__ w,
                                                                 const float* __restrict__ ws, int rows, int K,
                                                                 int n_out, float* __restrict__ out) {
-  __shared__ ShSmem sm;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  __shared__ ShStage st0, st1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 3, wn = wave >> 2;  // rows 32 wm .., weight rows of wn
   const int r = lane & 15, g = lane >> 4;
   constexpr int BO = GATED ? kShBN / 2 : kShBN;  // outputs per tile
   const int tiles_n = n_out / BO;
   const int row0 = (blockIdx.x / tiles_n) * kShBM, o0 = (blockIdx.x % tiles_n) * BO;
   const int nkb = K / 128;
-  const size_t rowbytes = (size_t)3 * K;  // one digit row
+  const uint32_t rowbytes = 3u * (uint32_t)K;  // one digit row
   // tile weight row rr (0..63) -> weight matrix row
   auto brow = [&](int rr) { return GATED ? (rr < 32 ? o0 + rr : n_out + o0 + rr - 32) : o0 + rr; };
-  // staging: thread (sr, sc) loads chunk sc of rows sr and sr + 64 of A and
-  // row sr of B, for each digit plane; rows past the end read the last row
-  // (their results are never written)
-  const int sr = tid >> 3, sc = tid & 7;
-  const uint8_t* pa0 = a + (size_t)min(row0 + sr, rows - 1) * rowbytes + 16 * sc;
-  const uint8_t* pa1 = a + (size_t)min(row0 + sr + 64, rows - 1) * rowbytes + 16 * sc;
-  const uint8_t* pb = w + (size_t)brow(sr) * rowbytes + 16 * sc;
+  // Loads into LDS: the A tile is 48 regions of 1 KB (plane p = region / 16,
+  // rows 8 * (region % 16) .. + 8), 6 per wave; the B tile 24 (plane
+  // region / 8, rows 8 * (region % 8) ..), 3 per wave. Lane l of a region
+  // fills row R = first + l / 8 at chunk place l % 8, which holds logical
+  // chunk (l % 8) ^ ((R >> 1) & 7) = (l % 8) ^ (4 * (region % 2) + l / 16):
+  // a lane's offset is one of two values (lofs) plus a part common to the
+  // wave. A's rows are padded to a multiple of 128 in the workspace, so rows
+  // past the end are read (and never written out) without a clamp. Offsets
+  // are 32-bit (a tile's A rows span < 2^25 bytes, all of w < 2^30).
+  const uint32_t lrow = (uint32_t)(lane >> 3) * rowbytes;
+  const uint32_t lofs0 = lrow + 16u * (uint32_t)((lane & 7) ^ (lane >> 4));
+  const uint32_t lofs1 = lrow + 16u * (uint32_t)((lane & 7) ^ (4 + (lane >> 4)));
+  const uint8_t* abase = a + (size_t)row0 * rowbytes;
+  // (the wave-uniform part of an offset goes through readfirstlane, which
+  // keeps the compiler from hoisting one register per load out of the loop)
+  auto dma = [&](int kb, ShStage& S) {
+    const uint32_t o = (uint32_t)kb * kShDigitBlock;
+#pragma unroll
+    for (int q = 0; q < 6; ++q) {
+      const int reg = wave * 6 + q, rb = reg & 15;
+      const uint32_t u = __builtin_amdgcn_readfirstlane((uint32_t)(8 * rb) * rowbytes + 128u * (reg >> 4) + o);
+      dma16(abase + (u + ((rb & 1) ? lofs1 : lofs0)), &S.a[reg >> 4][1024 * rb]);
+    }
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const int reg = wave * 3 + q, rb = reg & 7;
+      const int wr = brow(8 * rb);  // the region's first weight row (its 8 rows are consecutive)
+      const uint32_t u = __builtin_amdgcn_readfirstlane((uint32_t)wr * rowbytes + 128u * (reg >> 3) + o);
+      dma16(w + (u + ((rb & 1) ? lofs1 : lofs0)), &S.b[reg >> 3][1024 * rb]);
+    }
+  };
   const float* psa = as + min(row0 + (tid & (kShBM - 1)), rows - 1);  // + kb * rows
   const float* pwg = ws + (size_t)(brow(0) / 128) * nkb;
   const float* pwu = ws + (size_t)(brow(kShBN - 1) / 128) * nkb;
-  auto load = [&](int kb, ShRegs& R) {
-    const size_t o = (size_t)kb * kShDigitBlock;
-#pragma unroll
-    for (int p = 0; p < 3; ++p) {
-      R.a0[p] = ld16(pa0 + o + 128 * p);
-      R.a1[p] = ld16(pa1 + o + 128 * p);
-      R.b[p] = ld16(pb + o + 128 * p);
-    }
-    R.sa = psa[(size_t)kb * rows];
-  };
-  auto store = [&](const ShRegs& R, int s) {
-#pragma unroll
-    for (int p = 0; p < 3; ++p) {
-      *reinterpret_cast<uint4*>(&sm.a[s][p][sw128(sr, sc)]) = R.a0[p];
-      *reinterpret_cast<uint4*>(&sm.a[s][p][sw128(sr + 64, sc)]) = R.a1[p];
-      *reinterpret_cast<uint4*>(&sm.b[s][p][sw128(sr, sc)]) = R.b[p];
-    }
-    if (tid < kShBM) sm.as[s][tid] = R.sa;
-  };
   double acc[2][2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -191,8 +211,34 @@ __global__ __launch_bounds__(kShThreads, 1) void sh_gemm_kernel(const uint8_t* _
   // tile weight rows of column group j: GATED gate 16 wn (j = 0) and up
   // 32 + 16 wn (j = 1); else 32 wn + 16 j
   auto wrow = [&](int j) { return GATED ? 32 * j + 16 * wn : 32 * wn + 16 * j; };
-  auto compute = [&](int s, int kb) {
-    v4i P[5][2][2];
+  // The two waves on a SIMD (w and w + 4) take turns: waves 0..3 multiply a
+  // block and then finish it in float64; waves 4..7 first finish the previous
+  // block and then multiply, so one wave's float64 work runs beside the other
+  // wave's MFMAs. Right after its MFMAs every wave folds the five power sums
+  // into HIGH/LOW (hl); what waits for the float64 step is hl with the
+  // block's scales (sa_p, swg_p, swu_p).
+  const bool fold_first = wave >= 4;
+  v4i P[5][2][2];
+  int hl[2][2][4][2];
+  float sa_p[2][4];
+  float swg_p = 0.f, swu_p = 0.f;
+  auto fold = [&]() {
+    // the weight scale times 2^-18 (exact)
+    const double swg = (double)swg_p * 0x1p-18, swu = (double)swu_p * 0x1p-18;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const double sa = (double)sa_p[i][v];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const double sab = sa * (GATED && j == 1 ? swu : swg);
+          const double T = fma((double)hl[i][j][v][0], 16384.0, (double)hl[i][j][v][1]);
+          acc[i][j][v] = add_scaled(acc[i][j][v], sab, T);
+        }
+      }
+  };
+  auto multiply = [&](const ShStage& S, int kb) {
 #pragma unroll
     for (int q = 0; q < 5; ++q)
 #pragma unroll
@@ -202,57 +248,84 @@ __global__ __launch_bounds__(kShThreads, 1) void sh_gemm_kernel(const uint8_t* _
     // K half h: lane group g supplies bytes 64 h + 16 g .. + 16 of its row
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      uint4 A[2][3], B[2][3];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int p = 0; p < 3; ++p)
-          A[i][p] = *reinterpret_cast<const uint4*>(&sm.a[s][p][sw128(32 * wm + 16 * i + r, 4 * h + g)]);
+      uint4 B[2][3];
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int p = 0; p < 3; ++p)
-          B[j][p] = *reinterpret_cast<const uint4*>(&sm.b[s][p][sw128(wrow(j) + r, 4 * h + g)]);
+          B[j][p] = *reinterpret_cast<const uint4*>(&S.b[p][sw128(wrow(j) + r, 4 * h + g)]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 2; ++i) {
+        uint4 A[3];
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+          A[p] = *reinterpret_cast<const uint4*>(&S.a[p][sw128(32 * wm + 16 * i + r, 4 * h + g)]);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          P[0][i][j] = mfma_i8(A[i][0], B[j][0], P[0][i][j]);
-          P[1][i][j] = mfma_i8(A[i][0], B[j][1], mfma_i8(A[i][1], B[j][0], P[1][i][j]));
-          P[2][i][j] = mfma_i8(A[i][0], B[j][2], mfma_i8(A[i][1], B[j][1], mfma_i8(A[i][2], B[j][0], P[2][i][j])));
-          P[3][i][j] = mfma_i8(A[i][1], B[j][2], mfma_i8(A[i][2], B[j][1], P[3][i][j]));
-          P[4][i][j] = mfma_i8(A[i][2], B[j][2], P[4][i][j]);
+          P[0][i][j] = mfma_i8(A[0], B[j][0], P[0][i][j]);
+          P[1][i][j] = mfma_i8(A[0], B[j][1], mfma_i8(A[1], B[j][0], P[1][i][j]));
+          P[2][i][j] = mfma_i8(A[0], B[j][2], mfma_i8(A[1], B[j][1], mfma_i8(A[2], B[j][0], P[2][i][j])));
+          P[3][i][j] = mfma_i8(A[1], B[j][2], mfma_i8(A[2], B[j][1], P[3][i][j]));
+          P[4][i][j] = mfma_i8(A[2], B[j][2], P[4][i][j]);
         }
+      }
     }
-    // exact block sum times 2^18, scaled by (activation scale x weight scale
-    // x 2^-18: exact) and added in float64 in block order
-    const double swg = (double)pwg[kb] * 0x1p-18, swu = (double)pwu[kb] * 0x1p-18;
+    // HIGH = P2 + 2^7 P3 + 2^14 P4, LOW = P0 + 2^7 P1, and the block's scales
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const double sa = (double)sm.as[s][32 * wm + 16 * i + 4 * g + v];
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const double sab = sa * (GATED && j == 1 ? swu : swg);
-          const double T = sh_fold(P[0][i][j][v], P[1][i][j][v], P[2][i][j][v], P[3][i][j][v], P[4][i][j][v]);
-          acc[i][j][v] = __dadd_rn(acc[i][j][v], __dmul_rn(sab, T));
+        for (int v = 0; v < 4; ++v) {
+          hl[i][j][v][0] = P[2][i][j][v] + P[3][i][j][v] * 128 + P[4][i][j][v] * 16384;
+          hl[i][j][v][1] = P[0][i][j][v] + P[1][i][j][v] * 128;
         }
-      }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sa_p[i][v] = S.as[32 * wm + 16 * i + 4 * g + v];
+    swg_p = pwg[kb];
+    swu_p = pwu[kb];
   };
-  ShRegs R;
-  load(0, R);
-  store(R, 0);
-  if (nkb > 1) load(1, R);
-  barrier_lds();
-  // step kb is multiplied while the loads of kb + 1 are in flight; its LDS
-  // buffer is filled after the multiply, behind one barrier per step
-  for (int kb = 0; kb < nkb; ++kb) {
-    compute(kb & 1, kb);
-    if (kb + 1 < nkb) store(R, (kb + 1) & 1);
+  // (scheduling fences keep the phases apart: interleaved, the compiler's
+  // schedule held more values than the register file)
+  auto compute = [&](const ShStage& S, int kb) {
+    if (fold_first) {
+      if (kb > 0) fold();
+      __builtin_amdgcn_sched_barrier(0);
+      multiply(S, kb);
+    } else {
+      multiply(S, kb);
+      __builtin_amdgcn_sched_barrier(0);
+      fold();
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // one step: the next block's loads go out, this block is multiplied, then
+  // the wave's loads are waited for and one barrier makes every wave's
+  // loads visible (and frees this block's stage for the step after next)
+  auto step = [&](int kb, const ShStage& cur, ShStage& nxt) {
+    const bool more = kb + 1 < nkb;
+    float sa_n = 0.f;
+    if (more) {
+      dma(kb + 1, nxt);
+      if (tid < kShBM) sa_n = psa[(size_t)(kb + 1) * rows];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    compute(cur, kb);
+    if (more && tid < kShBM) nxt.as[tid] = sa_n;
+    wait_vm0();
     barrier_lds();
-    if (kb + 2 < nkb) load(kb + 2, R);
+  };
+  dma(0, st0);
+  if (tid < kShBM) st0.as[tid] = psa[0];
+  wait_vm0();
+  barrier_lds();
+  for (int kb = 0; kb < nkb; kb += 2) {
+    step(kb, st0, st1);
+    if (kb + 1 < nkb) step(kb + 1, st1, st0);
   }
+  if (fold_first) fold();
   // D row 4g + v of 16-row group i, column r of weight-row group j
 #pragma unroll
   for (int i = 0; i < 2; ++i)
