@@ -240,6 +240,29 @@ moe_status moe_forward(moe_plan* plan, int64_t M, const void* x, const float* lo
                        const void* w13, const void* s13, const void* w2, const void* s2,
                        void* out, void* stream);
 
+/* Bytes of the device scratch moe_forward_noalloc runs on: 64 MiB, one copy
+ * per device the library runs on, held until the process ends. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* moe_forward for callers that cannot allocate device memory or bind a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same call, the same kernels and results, with
+ * the library's static per-device scratch of MOE_NOALLOC_SCRATCH_BYTES as
+ * the workspace instead of the plan's (which is neither needed nor touched;
+ * the intermediates of moe_plan_layout are then in that scratch). Allocates
+ * nothing and calls no allocating routine. The caller still passes inputs
+ * and outputs as for moe_forward, with the same checks.
+ * MOE_ERR_UNSUPPORTED when the plan's workspace (moe_plan_workspace_bytes,
+ * set by its shape's maximum M) exceeds MOE_NOALLOC_SCRATCH_BYTES, before
+ * anything is enqueued; MOE_ERR_HIP when the scratch's address cannot be
+ * found or a launch fails. Every call on a device shares that device's
+ * scratch, which keeps the last call's contents: calls that may overlap on
+ * one device (other streams, other host threads) race and must not be
+ * issued; the call clears what it needs zeroed itself. */
+moe_status moe_forward_noalloc(moe_plan* plan, int64_t M, const void* x, const float* logits,
+                               const void* w13, const void* s13, const void* w2, const void* s2,
+                               void* out, void* stream);
+
 /* Profiling aid: when `events` is non-NULL, moe_forward brackets stage i
  * with events[2i] (start of its first kernel) and events[2i+1] (end of its
  * last kernel), hipEvent_t handles, so hipEventElapsedTime(events[2i],

@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "lib
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE, MOE_ERR_HIP = range(6)
 MID_E4M3, MID_MXFP4 = 0, 1  # moe_mid_format
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES of include/qmoe.h
 
 
 class moe_shape(ctypes.Structure):
@@ -79,6 +80,8 @@ def lib() -> ctypes.CDLL:
     L.moe_plan_stage_launches.argtypes = [vp, i64, ctypes.c_int]
     L.moe_forward.restype = st
     L.moe_forward.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.moe_forward_noalloc.restype = st
+    L.moe_forward_noalloc.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp]
     L.moe_pack_w13.restype = st
     L.moe_pack_w13.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp]
     L.moe_pack_w2.restype = st
@@ -243,6 +246,17 @@ class Plan:
                                _ptr(s2), _ptr(out), _stream(stream))
         if st != MOE_OK:
             raise MoeError(st, "moe_forward")
+        return out
+
+    def forward_noalloc(self, x, logits, w13, s13, w2, s2, out, M: Optional[int] = None, stream=None):
+        """moe_forward_noalloc: the same call on the library's static device
+        scratch instead of this plan's workspace (nothing is allocated)."""
+        if M is None:
+            M = x.shape[0]
+        st = lib().moe_forward_noalloc(self._h, int(M), _ptr(x), _ptr(logits), _ptr(w13), _ptr(s13), _ptr(w2),
+                                       _ptr(s2), _ptr(out), _stream(stream))
+        if st != MOE_OK:
+            raise MoeError(st, "moe_forward_noalloc")
         return out
 
     def stage_launches(self, M: int):

@@ -8,6 +8,7 @@
 #include "internal.h"
 
 #include <climits>
+#include <mutex>
 
 using namespace qmoe;
 
@@ -122,6 +123,102 @@ struct DeviceGuard {
   }
 };
 
+// Checks of a call shared by moe_forward and moe_forward_noalloc (the
+// workspace, `ws` of `ws_bytes` or none, is the caller's concern).
+moe_status check_call(const moe_plan* plan, int64_t M, const void* const ptrs[7], const void* ws, size_t ws_bytes) {
+  if (plan->s.shared_I > 0 && !plan->ws13) return MOE_ERR_INVALID_ARG;
+  if (M == 0) return MOE_OK;
+  const bool mx = plan->mid_fmt == MOE_MID_MXFP4;
+  if (mx && !mid_path(M, plan->s.top_k)) return MOE_ERR_UNSUPPORTED;
+  for (int i = 0; i < 7; ++i)
+    if (!ptrs[i] || !aligned16(ptrs[i])) return MOE_ERR_INVALID_ARG;
+  for (int i = 0; i < 7; ++i)
+    if (ptr_device(ptrs[i]) != plan->device) return MOE_ERR_DEVICE;
+  const void* x = ptrs[0];
+  const void* logits = ptrs[1];
+  const void* out = ptrs[6];
+  const size_t H = (size_t)plan->s.H, E = (size_t)plan->s.E;
+  const size_t out_bytes = (size_t)M * H * 2;
+  if (overlaps(out, out_bytes, x, (size_t)M * H * 2) || overlaps(out, out_bytes, logits, (size_t)M * E * 4) ||
+      (ws && overlaps(out, out_bytes, ws, ws_bytes)))
+    return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+// The launch sequence of one call on the workspace of `plan` (the plan's
+// device current, the call's arguments checked).
+hipError_t enqueue_call(const moe_plan* plan, const CallArgs& a) {
+  const int64_t M = a.M;
+  const bool mx = plan->mid_fmt == MOE_MID_MXFP4;
+  const bool small = small_path(M, plan->s.top_k);
+  const bool fused_combine = small && !mx;  // down and combine in one launch
+  Ev ev[kStages];
+  if (plan->n_events)
+    for (int i = 0; i < kStages; ++i) ev[i] = Ev{plan->events[2 * i], plan->events[2 * i + 1]};
+  if (plan->call_start) {
+    ev[0].start = plan->call_start;             // the route launch comes first
+    ev[fused_combine ? 5 : 6].stop = plan->call_stop;  // down (+ combine) or the combine comes last
+  }
+  // a stage with no launch of its own still records its (empty) interval
+  auto none = [&](int i) -> hipError_t {
+    if (!plan->n_events) return hipSuccess;
+    hipError_t e = hipEventRecord(ev[i].start, a.stream);
+    return e != hipSuccess ? e : hipEventRecord(ev[i].stop, a.stream);
+  };
+  // Up to kSmallM tokens: routing + sort + x quantization in one launch
+  // (workgroup 0 routes and sorts, the others quantize x); gate/up on 16-row
+  // tiles; the mid quantization; down with the combine (a workgroup owns 16
+  // output columns of every slot, so the slot results never leave it).
+  // Above kSmallM: routing spread over the GPU, a second launch sorts;
+  // gate/up on 16-row tiles and the mid quantization up to kMidM tokens,
+  // above on 64-row tiles with the mid quantization inside (every item owns
+  // whole mid blocks); down to y in HBM; the combine.
+  // With the MXFP4 mid (up to kMidM tokens): its own quantization and down
+  // kernel on the 16-row tiles, then the combine, for every M.
+  // A stage is never folded into its producer through a last-arriver
+  // counter: the device-scope release/acquire that needs writes back and
+  // invalidates a whole L2 of an XCD per workgroup and costs more than a
+  // launch.
+  hipError_t e = small ? launch_route_small(plan, a, ev[0]) : launch_route(plan, a, ev[0]);
+  if (e == hipSuccess) e = small ? none(1) : launch_align(plan, a, ev[1]);
+  const bool tiles16 = mid_path(M, plan->s.top_k);  // 16-row-tile gate/up, mid quantization on its own
+  if (e == hipSuccess) e = tiles16 ? launch_gate_up(plan, a, ev[2]) : launch_gate_up_big(plan, a, ev[2]);
+  if (e == hipSuccess)
+    e = mx ? launch_act_quant_mx(plan, a, ev[3]) : tiles16 ? launch_act_quant(plan, a, ev[3]) : none(3);
+  if (e == hipSuccess) e = plan->s.shared_I > 0 ? launch_shared(plan, a, ev[4]) : none(4);
+  if (e == hipSuccess)
+    e = mx ? launch_down_fp4(plan, a, ev[5]) : small ? launch_down_combine(plan, a, ev[5]) : launch_down_big(plan, a, ev[5]);
+  if (e == hipSuccess) e = fused_combine ? none(6) : launch_combine(plan, a, ev[6]);
+  return e;
+}
+
+// Scratch of moe_forward_noalloc: the workspace of its calls, one copy per
+// device, held until the process ends. In host code `scratch` names a host
+// stand-in; the device address of a device's copy comes from
+// hipGetSymbolAddress with that device current, looked up once per device
+// (at plan creation, else at the first call) and kept in g_scratch.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+// With `dev` current: the device address of its copy of `scratch`.
+hipError_t scratch_address(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return e != hipSuccess ? e : hipErrorInvalidSymbol;
+    }
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -180,6 +277,10 @@ moe_status moe_plan_create(const moe_shape* shape, moe_plan** out) {
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_ERR_DEVICE;
   if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return MOE_ERR_DEVICE;
+  // set-up of moe_forward_noalloc's scratch on this device (a failure here
+  // is reported by that entry point, which looks again)
+  void* sp = nullptr;
+  (void)scratch_address(dev, &sp);
   moe_plan* p = new (std::nothrow) moe_plan;
   if (!p) return MOE_ERR_INVALID_ARG;
   memset(p, 0, sizeof(*p));
@@ -343,64 +444,13 @@ moe_status moe_forward(moe_plan* plan, int64_t M, const void* x, const float* lo
   if (!plan) return MOE_ERR_INVALID_ARG;
   if (M < 0 || M > plan->s.M) return MOE_ERR_INVALID_ARG;
   if (!plan->ws) return MOE_ERR_WORKSPACE;
-  if (plan->s.shared_I > 0 && !plan->ws13) return MOE_ERR_INVALID_ARG;
-  if (M == 0) return MOE_OK;
-  const bool mx = plan->mid_fmt == MOE_MID_MXFP4;
-  if (mx && !mid_path(M, plan->s.top_k)) return MOE_ERR_UNSUPPORTED;
   const void* ptrs[7] = {x, logits, w13, s13, w2, s2, out};
-  for (const void* q : ptrs)
-    if (!q || !aligned16(q)) return MOE_ERR_INVALID_ARG;
-  for (const void* q : ptrs)
-    if (ptr_device(q) != plan->device) return MOE_ERR_DEVICE;
-  const size_t H = (size_t)plan->s.H, E = (size_t)plan->s.E;
-  const size_t out_bytes = (size_t)M * H * 2;
-  if (overlaps(out, out_bytes, x, (size_t)M * H * 2) || overlaps(out, out_bytes, logits, (size_t)M * E * 4) ||
-      overlaps(out, out_bytes, plan->ws, plan->L.total_bytes))
-    return MOE_ERR_INVALID_ARG;
-
+  moe_status st = check_call(plan, M, ptrs, plan->ws, plan->L.total_bytes);
+  if (st != MOE_OK || M == 0) return st;
   DeviceGuard guard(plan->device);
   if (!guard.ok) return MOE_ERR_DEVICE;
   CallArgs a{M, x, logits, w13, s13, w2, s2, out, (hipStream_t)stream};
-  const bool small = small_path(M, plan->s.top_k);
-  const bool fused_combine = small && !mx;  // down and combine in one launch
-  Ev ev[kStages];
-  if (plan->n_events)
-    for (int i = 0; i < kStages; ++i) ev[i] = Ev{plan->events[2 * i], plan->events[2 * i + 1]};
-  if (plan->call_start) {
-    ev[0].start = plan->call_start;             // the route launch comes first
-    ev[fused_combine ? 5 : 6].stop = plan->call_stop;  // down (+ combine) or the combine comes last
-  }
-  // a stage with no launch of its own still records its (empty) interval
-  auto none = [&](int i) -> hipError_t {
-    if (!plan->n_events) return hipSuccess;
-    hipError_t e = hipEventRecord(ev[i].start, a.stream);
-    return e != hipSuccess ? e : hipEventRecord(ev[i].stop, a.stream);
-  };
-  // Up to kSmallM tokens: routing + sort + x quantization in one launch
-  // (workgroup 0 routes and sorts, the others quantize x); gate/up on 16-row
-  // tiles; the mid quantization; down with the combine (a workgroup owns 16
-  // output columns of every slot, so the slot results never leave it).
-  // Above kSmallM: routing spread over the GPU, a second launch sorts;
-  // gate/up on 16-row tiles and the mid quantization up to kMidM tokens,
-  // above on 64-row tiles with the mid quantization inside (every item owns
-  // whole mid blocks); down to y in HBM; the combine.
-  // With the MXFP4 mid (up to kMidM tokens): its own quantization and down
-  // kernel on the 16-row tiles, then the combine, for every M.
-  // A stage is never folded into its producer through a last-arriver
-  // counter: the device-scope release/acquire that needs writes back and
-  // invalidates a whole L2 of an XCD per workgroup and costs more than a
-  // launch.
-  hipError_t e = small ? launch_route_small(plan, a, ev[0]) : launch_route(plan, a, ev[0]);
-  if (e == hipSuccess) e = small ? none(1) : launch_align(plan, a, ev[1]);
-  const bool tiles16 = mid_path(M, plan->s.top_k);  // 16-row-tile gate/up, mid quantization on its own
-  if (e == hipSuccess) e = tiles16 ? launch_gate_up(plan, a, ev[2]) : launch_gate_up_big(plan, a, ev[2]);
-  if (e == hipSuccess)
-    e = mx ? launch_act_quant_mx(plan, a, ev[3]) : tiles16 ? launch_act_quant(plan, a, ev[3]) : none(3);
-  if (e == hipSuccess) e = plan->s.shared_I > 0 ? launch_shared(plan, a, ev[4]) : none(4);
-  if (e == hipSuccess)
-    e = mx ? launch_down_fp4(plan, a, ev[5]) : small ? launch_down_combine(plan, a, ev[5]) : launch_down_big(plan, a, ev[5]);
-  if (e == hipSuccess) e = fused_combine ? none(6) : launch_combine(plan, a, ev[6]);
-  if (e != hipSuccess) {
+  if (enqueue_call(plan, a) != hipSuccess) {
     // a launch after the routing may have left bits in the token bitmap that
     // only the sort clears: unbind the workspace so that no later call runs
     // on it before moe_plan_set_workspace zeroes it again
@@ -408,6 +458,35 @@ moe_status moe_forward(moe_plan* plan, int64_t M, const void* x, const float* lo
     return MOE_ERR_HIP;
   }
   return MOE_OK;
+}
+
+moe_status moe_forward_noalloc(moe_plan* plan, int64_t M, const void* x, const float* logits, const void* w13,
+                               const void* s13, const void* w2, const void* s2, void* out, void* stream) {
+  if (!plan) return MOE_ERR_INVALID_ARG;
+  if (M < 0 || M > plan->s.M) return MOE_ERR_INVALID_ARG;
+  if (plan->L.total_bytes > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_UNSUPPORTED;
+  const void* ptrs[7] = {x, logits, w13, s13, w2, s2, out};
+  moe_status st = check_call(plan, M, ptrs, nullptr, 0);
+  if (st != MOE_OK || M == 0) return st;
+  DeviceGuard guard(plan->device);
+  if (!guard.ok) return MOE_ERR_DEVICE;
+  void* sp = nullptr;
+  if (scratch_address(plan->device, &sp) != hipSuccess) return MOE_ERR_HIP;
+  // the call runs on a copy of the plan whose workspace is this device's
+  // scratch; the plan itself (and its bound workspace) is not touched
+  moe_plan q = *plan;
+  q.ws = reinterpret_cast<uint8_t*>(sp);
+  q.ws_bytes = (size_t)MOE_NOALLOC_SCRATCH_BYTES;
+  CallArgs a{M, x, logits, w13, s13, w2, s2, out, (hipStream_t)stream};
+  // every call on the device shares the scratch, and a call of another plan
+  // leaves other data where this plan keeps its token bitmap: clear it (a
+  // fill kernel, not a memset node, so the call can be captured) before the
+  // routing sets its bits; the single-workgroup sort up to kSmallM tokens
+  // keeps its bitmap in LDS and needs none
+  hipError_t e = hipSuccess;
+  if (!small_path(M, q.s.top_k)) e = launch_zero(q.ws + q.X.sync_begin, q.X.sync_bytes, a.stream);
+  if (e == hipSuccess) e = enqueue_call(&q, a);
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 }  // extern "C"

@@ -139,3 +139,10 @@ def test_header_compiles_as_plain_c(tmp_path):
                 ["g++", "-std=c++17", "-Wall", "-Wextra", "-Werror", "-fsyntax-only", "-x", "c++"]):
         r = subprocess.run(cmd + ["-I", inc, str(src)], capture_output=True, text=True)
         assert r.returncode == 0, r.stderr
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(os.path.join(ROOT, "include", "qmoe.h")).read()
+    m = re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == B.NOALLOC_SCRATCH_BYTES
+    assert B.lib().moe_forward_noalloc(None, 4, None, None, None, None, None, None, None, None) == B.MOE_ERR_INVALID_ARG

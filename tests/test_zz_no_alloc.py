@@ -1,0 +1,70 @@
+"""moe_forward_noalloc (the entry point that runs on the library's static
+device scratch, for callers that cannot allocate) against moe_forward on the
+same inputs: two calls in a row on one plan, the second smaller, on the
+small-token path and on the paths that sort with the token bitmap."""
+
+import numpy as np
+import pytest
+
+from quantized_moe_expert_route_amd import fixtures as X
+
+from moe_gpu import make_plan, upload
+
+pytestmark = pytest.mark.gpu
+
+
+def _call(plan, g, M, noalloc):
+    import torch
+
+    H = plan.shape.H
+    out = torch.full((M, H), -1, dtype=torch.int16, device=g["x"].device)
+    f = plan.forward_noalloc if noalloc else plan.forward
+    f(g["x"], g["logits"], g["w13"], g["s13"], g["w2"], g["s2"], out, M=M)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("shape,kind,m1,m2", [
+    (X.Shape(M=16, H=6144, E=256, I=256, top_k=8), "uniform", 16, 4),  # decode shapes, small path
+    (X.Shape(M=64, H=1024, E=32, I=256, top_k=8), "zipf", 64, 20),     # bitmap sort, 16-row tiles
+    (X.Shape(M=300, H=512, E=16, I=128, top_k=4), "normal", 300, 140),  # the large path, then the mid-range one
+    (X.Shape(M=40, H=1536, E=8, I=128, top_k=2, shared_I=128), "normal", 40, 12),  # with the shared expert
+])
+def test_noalloc_equals_forward(shape, kind, m1, m2):
+    d = X.make_inputs(shape, kind, 31)
+    g = upload(d)
+    plan = make_plan(shape)
+    if shape.shared_I:
+        plan.set_shared(g["ws13"], g["ss13"], g["ws2"], g["ss2"])
+    for M in (m1, m2):
+        # the second call uses other rows of x and logits and fewer tokens
+        gx = dict(g, x=g["x"][shape.M - M:].contiguous(), logits=g["logits"][shape.M - M:].contiguous())
+        ref = _call(plan, gx, M, noalloc=False)
+        got = _call(plan, gx, M, noalloc=True)
+        assert np.array_equal(got, ref), f"M={M}: noalloc output differs from moe_forward's"
+
+
+def test_noalloc_after_other_plans_and_rejects_large():
+    """A call after calls of other plans (whose data sits where this plan
+    keeps its token bitmap) still equals moe_forward; a plan whose workspace
+    exceeds the scratch is refused before anything runs."""
+    from quantized_moe_expert_route_amd.binding import MoeError, NOALLOC_SCRATCH_BYTES, MOE_ERR_UNSUPPORTED
+
+    a = X.Shape(M=200, H=2048, E=64, I=256, top_k=8)
+    b = X.Shape(M=48, H=512, E=16, I=128, top_k=2)
+    da, db = X.make_inputs(a, "zipf", 5), X.make_inputs(b, "ties", 6)
+    ga, gb = upload(da), upload(db)
+    pa, pb = make_plan(a), make_plan(b)
+    ref_b = _call(pb, gb, b.M, noalloc=False)
+    _call(pa, ga, a.M, noalloc=True)
+    assert np.array_equal(_call(pb, gb, b.M, noalloc=True), ref_b)
+    _call(pa, ga, 37, noalloc=True)
+    assert np.array_equal(_call(pb, gb, b.M, noalloc=True), ref_b)
+    big = X.Shape(M=4096, H=6144, E=256, I=512, top_k=8)
+    pbig = make_plan(big)
+    assert pbig.workspace.numel() > NOALLOC_SCRATCH_BYTES
+    gbig = {k: gb[k] for k in gb}
+    with pytest.raises(MoeError) as e:
+        pbig.forward_noalloc(gbig["x"], gbig["logits"], gbig["w13"], gbig["s13"], gbig["w2"], gbig["s2"],
+                             gbig["x"], M=1)
+    assert e.value.status == MOE_ERR_UNSUPPORTED
