@@ -240,17 +240,38 @@ def shared_expert(x_bits, ws13, ss13, ws2, ss2):
 
 
 # ------------------------------------------------------------------ 7. combine
+def combine_partial(w: np.ndarray, y: np.ndarray, ys=None) -> np.ndarray:
+    """The combine's float64 sum before its rounding: w [M, k] fp32, y [M, k, H]
+    fp32 (+ ys [M, H]) -> [M, H] float64, products of two fp32 values (exact)
+    added in slot order, then ys."""
+    acc = np.zeros((y.shape[0], y.shape[2]))
+    for j in range(y.shape[1]):
+        acc += np.asarray(w[:, j], np.float64)[:, None] * y[:, j, :].astype(np.float64)
+    if ys is not None:
+        acc += np.asarray(ys, np.float64)
+    return acc
+
+
 def combine(w: np.ndarray, y: np.ndarray, ys=None) -> np.ndarray:
     """w [M, k] fp32, y [M, k, H] fp32 (+ ys [M, H]) -> out bf16 bits [M, H].
 
     Float64 sum in slot order (products of two fp32 values are exact), then
     one rounding to bf16.
     """
-    acc = np.zeros((y.shape[0], y.shape[2]))
-    for j in range(y.shape[1]):
-        acc += np.asarray(w[:, j], np.float64)[:, None] * y[:, j, :].astype(np.float64)
-    if ys is not None:
-        acc += np.asarray(ys, np.float64)
+    return F.bf16_encode(combine_partial(w, y, ys))
+
+
+def tp_exchange_sum(partials) -> np.ndarray:
+    """Tensor-parallel partial-sum exchange ("glm53: FP8 mid hand-off, early
+    split rows, ...", Accuracy Tests: a rank's peers' partial sums arrive
+    tagged with the launch's epoch). Reading: every rank's float64 partial
+    (combine_partial of its slice) is exchanged whole, the partials are added
+    in float64 in rank order 0, 1, ... starting from zero, and the sum is
+    rounded once to bf16, so every rank forms the same output bits.
+    partials: sequence of [M, H] float64 -> out bf16 bits [M, H]."""
+    acc = np.zeros(np.asarray(partials[0]).shape)
+    for p in partials:
+        acc = acc + np.asarray(p, np.float64)
     return F.bf16_encode(acc)
 
 

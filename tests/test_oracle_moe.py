@@ -426,3 +426,34 @@ def test_shared_expert_chain_on_grid():
     assert not np.array_equal(y_unquant.astype(np.float32), y)
     ss2_t = np.ascontiguousarray(ss2[::-1])  # block scales on the wrong output rows
     assert not np.array_equal(O.shared_expert(x_bits, ws13, ss13, ws2, ss2_t)[0], y)
+
+
+
+# ------------------------------------------------------------ tensor-parallel partial exchange
+def test_tp_exchange_sum_pins():
+    """A single rank's exchange equals the plain combine; zero peer partials
+    (the one-GPU loopback) change nothing, whatever the rank; with values
+    exact in float64 the result is the exact sum rounded once (checked with
+    integer arithmetic); the rank order is the summation order."""
+    d = X.make_inputs("c0")
+    ref = _run(d)
+    s = d["shape"]
+    y = ref["y"].reshape(s.M, s.top_k, s.H)
+    P = O.combine_partial(ref["w"], y)
+    assert np.array_equal(F.bf16_encode(P), ref["out"])
+    assert np.array_equal(O.tp_exchange_sum([P]), ref["out"])
+    z = np.zeros_like(P)
+    for r in range(8):
+        parts = [z] * 8
+        parts[r] = P
+        assert np.array_equal(O.tp_exchange_sum(parts), ref["out"])
+    rng = np.random.default_rng(5)
+    ints = [rng.integers(-2 ** 40, 2 ** 40, size=(3, 64)) for _ in range(4)]
+    exact = sum(int_ for int_ in ints)  # int64, exact
+    got = O.tp_exchange_sum([np.ldexp(i.astype(np.float64), -30) for i in ints])
+    assert np.array_equal(got, F.bf16_encode(np.ldexp(exact.astype(np.float64), -30)))
+    # order matters where float64 rounds: (big + 1) - big != (big - big) + 1
+    big = np.full((1, 1), 2.0 ** 60)
+    one = np.full((1, 1), 1.0)
+    assert F.bf16_decode(O.tp_exchange_sum([big, one, -big]))[0, 0] == 0.0
+    assert F.bf16_decode(O.tp_exchange_sum([big, -big, one]))[0, 0] == 1.0
