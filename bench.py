@@ -84,7 +84,7 @@ def measure(name, steps, warmup, n_sets, mid_fmt=0):
     import torch
 
     from quantized_moe_expert_route_amd import fixtures as X
-    from quantized_moe_expert_route_amd.binding import HipEvents, Plan, pack_w13, pack_w2, stage_names
+    from quantized_moe_expert_route_amd.binding import HipEvents, Plan, layout_for, pack_w13, pack_w2, stage_names
 
     wl = X.WORKLOADS[name]
     s = wl.shape
@@ -105,6 +105,7 @@ def measure(name, steps, warmup, n_sets, mid_fmt=0):
         sh = [torch.from_numpy(base[k]).to(dev) for k in ("ws13", "ss13", "ws2", "ss2")]
         plan.set_shared(*sh)
     plan.set_mid_format(mid_fmt)
+    plan.set_weight_layout(layout_for(mid_fmt))
     plan.set_shared_slot(wl.shared_slot)
     x = torch.empty_like(sets[0][0])
     logits = torch.empty_like(sets[0][1])

@@ -180,6 +180,22 @@ moe_status moe_plan_set_shared_slot(moe_plan* plan, int on);
  * a NULL plan or an unknown format. Host-only. */
 moe_status moe_plan_set_mid_format(moe_plan* plan, int format);
 
+/* Layout of the weights a call receives, declared by the caller once they
+ * are in place (the MoE method of "IQ2R: load GLM-5.3 packed MoE checkpoints
+ * with TP slicing", Summary, allocates packed expert tensors when the
+ * checkpoint is loaded). Flags: MOE_LAYOUT_W13_PACKED, w13/s13 written by
+ * moe_pack_w13; MOE_LAYOUT_W2_PACKED, w2/s2 written by moe_pack_w2. The
+ * kernels read gate/up weights only packed, and down weights packed exactly
+ * when the mid format is MOE_MID_MXFP4, so moe_forward and
+ * moe_forward_noalloc return MOE_ERR_UNSUPPORTED, before anything is
+ * enqueued, unless the plan's declared layout is MOE_LAYOUT_W13_PACKED with
+ * MOE_LAYOUT_W2_PACKED matching the mid format (a new plan declares
+ * nothing: a caller passing row-major weights is refused, not served with
+ * a wrong result). MOE_ERR_INVALID_ARG for a NULL plan or unknown flags.
+ * Host-only; applies to later calls. */
+typedef enum { MOE_LAYOUT_W13_PACKED = 1, MOE_LAYOUT_W2_PACKED = 2 } moe_weight_layout;
+moe_status moe_plan_set_weight_layout(moe_plan* plan, unsigned layout);
+
 /* Rewrite the routed experts' gate/up weights into the packed layout that
  * moe_forward reads, once, when the weights are loaded (the MoE method of
  * "IQ2R: load GLM-5.3 packed MoE checkpoints with TP slicing", Summary,
@@ -223,7 +239,8 @@ moe_status moe_pack_w2(const void* w2, const void* s2, int64_t E, int64_t I, int
  *   x      bf16 [M, H]
  *   logits fp32 [M, E]     (finite or -inf)
  *   w13    gate/up weights in the packed layout of moe_pack_w13 (the
- *          MXFP4 [E, 2I, H/2] rows [0, I) gate, [I, 2I) up, along H)
+ *          MXFP4 [E, 2I, H/2] rows [0, I) gate, [I, 2I) up, along H),
+ *          declared with moe_plan_set_weight_layout
  *   s13    their E8M0 scales, packed by moe_pack_w13 ([E, 2I, H/32])
  *   w2     u8 MXFP4 [E, H, I/2]    along I, row-major (packed by
  *          moe_pack_w2 when the plan's mid format is MOE_MID_MXFP4)
@@ -231,7 +248,8 @@ moe_status moe_pack_w2(const void* w2, const void* s2, int64_t E, int64_t I, int
  *   out    bf16 [M, H]  fully overwritten; must not alias any input
  * Returns after enqueueing; faults inside kernels surface at the caller's
  * next synchronisation. MOE_ERR_WORKSPACE if no workspace is bound,
- * MOE_ERR_INVALID_ARG if the shared expert is required but not bound.
+ * MOE_ERR_INVALID_ARG if the shared expert is required but not bound,
+ * MOE_ERR_UNSUPPORTED if the declared weight layout is not the one read.
  * MOE_ERR_HIP when a launch fails once the call has started enqueueing: the
  * launches already enqueued stay (and may write the workspace and `out`),
  * and the workspace is unbound, so later calls return MOE_ERR_WORKSPACE

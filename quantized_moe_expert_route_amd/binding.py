@@ -16,6 +16,13 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "lib
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE, MOE_ERR_HIP = range(6)
 MID_E4M3, MID_MXFP4 = 0, 1  # moe_mid_format
+LAYOUT_W13_PACKED, LAYOUT_W2_PACKED = 1, 2  # moe_weight_layout flags
+
+
+def layout_for(mid_format: int) -> int:
+    """The weight layout calls with this mid format read: gate/up packed, and
+    down packed with the MXFP4 mid."""
+    return LAYOUT_W13_PACKED | (LAYOUT_W2_PACKED if mid_format == MID_MXFP4 else 0)
 NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES of include/qmoe.h
 
 
@@ -90,6 +97,8 @@ def lib() -> ctypes.CDLL:
     L.moe_plan_set_shared_slot.argtypes = [vp, ctypes.c_int]
     L.moe_plan_set_mid_format.restype = st
     L.moe_plan_set_mid_format.argtypes = [vp, ctypes.c_int]
+    L.moe_plan_set_weight_layout.restype = st
+    L.moe_plan_set_weight_layout.argtypes = [vp, ctypes.c_uint]
     _lib = L
     return L
 
@@ -165,7 +174,7 @@ class Plan:
     """A plan for one shape, owning a device workspace allocated through torch."""
 
     def __init__(self, M: int, H: int, E: int, I: int, top_k: int, routed_scaling: float = 2.5,
-                 shared_I: int = 0, device=None):
+                 shared_I: int = 0, device=None, weight_layout: int = LAYOUT_W13_PACKED):
         import torch
 
         self.shape = moe_shape(M, H, E, I, top_k, routed_scaling, shared_I)
@@ -181,6 +190,15 @@ class Plan:
             raise MoeError(st, "moe_plan_set_workspace")
         self._shared = None
         self._events = None
+        self.set_weight_layout(weight_layout)
+
+    def set_weight_layout(self, layout: int):
+        """Declare the layout of the weights later calls pass (LAYOUT_W13_PACKED:
+        w13/s13 from pack_w13, the only gate/up layout served; | LAYOUT_W2_PACKED:
+        w2/s2 from pack_w2, required by and only by the MXFP4 mid)."""
+        st = lib().moe_plan_set_weight_layout(self._h, int(layout))
+        if st != MOE_OK:
+            raise MoeError(st, "moe_plan_set_weight_layout")
 
     def layout(self) -> Dict[str, int]:
         L = moe_ws_layout()
@@ -211,7 +229,9 @@ class Plan:
             raise MoeError(st, "moe_plan_set_shared_slot")
 
     def set_mid_format(self, fmt: int):
-        """MID_E4M3 (default) or MID_MXFP4 for the plan's later calls."""
+        """MID_E4M3 (default) or MID_MXFP4 for the plan's later calls (the
+        MXFP4 mid reads packed down weights: declare them with
+        set_weight_layout(LAYOUT_W13_PACKED | LAYOUT_W2_PACKED))."""
         st = lib().moe_plan_set_mid_format(self._h, int(fmt))
         if st != MOE_OK:
             raise MoeError(st, "moe_plan_set_mid_format")

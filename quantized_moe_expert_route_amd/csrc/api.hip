@@ -127,8 +127,12 @@ struct DeviceGuard {
 // workspace, `ws` of `ws_bytes` or none, is the caller's concern).
 moe_status check_call(const moe_plan* plan, int64_t M, const void* const ptrs[7], const void* ws, size_t ws_bytes) {
   if (plan->s.shared_I > 0 && !plan->ws13) return MOE_ERR_INVALID_ARG;
-  if (M == 0) return MOE_OK;
   const bool mx = plan->mid_fmt == MOE_MID_MXFP4;
+  // the weights must be in the layout the kernels read, as declared: gate/up
+  // packed (row-major is not served), down packed exactly for the MXFP4 mid
+  if (!(plan->layout & MOE_LAYOUT_W13_PACKED) || mx != ((plan->layout & MOE_LAYOUT_W2_PACKED) != 0))
+    return MOE_ERR_UNSUPPORTED;
+  if (M == 0) return MOE_OK;
   if (mx && !mid_path(M, plan->s.top_k)) return MOE_ERR_UNSUPPORTED;
   for (int i = 0; i < 7; ++i)
     if (!ptrs[i] || !aligned16(ptrs[i])) return MOE_ERR_INVALID_ARG;
@@ -360,6 +364,12 @@ moe_status moe_plan_set_shared_slot(moe_plan* plan, int on) {
   if (!plan || (on != 0 && on != 1)) return MOE_ERR_INVALID_ARG;
   if (on && (plan->s.top_k < 2 || plan->s.shared_I > 0)) return MOE_ERR_INVALID_ARG;
   plan->shared_slot = on;
+  return MOE_OK;
+}
+
+moe_status moe_plan_set_weight_layout(moe_plan* plan, unsigned layout) {
+  if (!plan || (layout & ~(unsigned)(MOE_LAYOUT_W13_PACKED | MOE_LAYOUT_W2_PACKED))) return MOE_ERR_INVALID_ARG;
+  plan->layout = layout;
   return MOE_OK;
 }
 

@@ -51,6 +51,7 @@ struct moe_plan {
   int n_events;
   hipEvent_t call_start, call_stop;
   int mid_fmt;     // moe_mid_format
+  unsigned layout; // moe_weight_layout flags declared by the caller
   int shared_slot; // 1: expert E-1 is the shared expert, slot top_k-1 of every token
 };
 

@@ -34,7 +34,7 @@ def _upload_mx(d):
 def _run_mx(d, plan=None, g=None, M=None, fmt=None):
     import torch
 
-    from quantized_moe_expert_route_amd.binding import MID_MXFP4
+    from quantized_moe_expert_route_amd.binding import MID_MXFP4, layout_for
 
     s = d["shape"]
     M = s.M if M is None else M
@@ -45,6 +45,7 @@ def _run_mx(d, plan=None, g=None, M=None, fmt=None):
         if s.shared_I:
             plan.set_shared(g["ws13"], g["ss13"], g["ws2"], g["ss2"])
     plan.set_mid_format(fmt)
+    plan.set_weight_layout(layout_for(fmt))
     out = torch.full((max(M, 1), s.H), -1, dtype=torch.int16, device=g["x"].device)
     w2, s2 = (g["w2p"], g["s2p"]) if fmt == MID_MXFP4 else (g["w2"], g["s2"])
     plan.forward(g["x"], g["logits"], g["w13"], g["s13"], w2, s2, out, M=M)
@@ -157,13 +158,14 @@ def test_mx_rejects_large_m():
     nothing enqueued); the E4M3 mid serves them on the same plan."""
     import torch
 
-    from quantized_moe_expert_route_amd.binding import MID_E4M3, MID_MXFP4, MOE_ERR_UNSUPPORTED, MoeError
+    from quantized_moe_expert_route_amd.binding import MID_E4M3, MID_MXFP4, MOE_ERR_UNSUPPORTED, MoeError, layout_for
 
     shape = X.Shape(M=300, H=512, E=16, I=128, top_k=2)
     d = X.make_inputs(shape, "normal", 5)
     g = upload(d)
     plan = make_plan(shape)
     plan.set_mid_format(MID_MXFP4)
+    plan.set_weight_layout(layout_for(MID_MXFP4))
     out = torch.empty((300, 512), dtype=torch.int16, device=g["x"].device)
     with pytest.raises(MoeError) as ei:
         plan.forward(g["x"], g["logits"], g["w13"], g["s13"], g["w2"], g["s2"], out, M=300)
@@ -172,5 +174,6 @@ def test_mx_rejects_large_m():
     plan.set_mid_format(MID_MXFP4)
     assert plan.stage_launches(256)[3] == 1 and plan.stage_launches(4)[6] == 1  # own quantization, combine
     plan.set_mid_format(MID_E4M3)
+    plan.set_weight_layout(layout_for(MID_E4M3))
     plan.forward(g["x"], g["logits"], g["w13"], g["s13"], g["w2"], g["s2"], out, M=300)
     torch.cuda.synchronize()

@@ -298,7 +298,7 @@ def test_graph_replay_matches_eager(name, mxfp4):
     every call leaves the token bitmap zero for the next."""
     import torch
 
-    from quantized_moe_expert_route_amd.binding import MID_MXFP4, pack_w2
+    from quantized_moe_expert_route_amd.binding import MID_MXFP4, layout_for, pack_w2
 
     d = X.make_inputs(name)
     s = d["shape"]
@@ -307,6 +307,7 @@ def test_graph_replay_matches_eager(name, mxfp4):
     w2, s2 = g["w2"], g["s2"]
     if mxfp4:
         plan.set_mid_format(MID_MXFP4)
+        plan.set_weight_layout(layout_for(MID_MXFP4))
         w2, s2 = pack_w2(w2, s2)
     call = lambda o: plan.forward(g["x"], g["logits"], g["w13"], g["s13"], w2, s2, o)
     eager = torch.empty((s.M, s.H), dtype=torch.int16, device="cuda")
@@ -432,3 +433,37 @@ def test_c4_shared_expert_every_token():
     out_ref = O.combine(gi["w"], gi["y"].reshape(s.M, s.top_k, s.H), ys_ref)
     _check_out(gout, out_ref)
     assert np.array_equal(gout, out_ref), "out differs from the combine of the GPU's y and the oracle's shared output"
+
+
+def test_declared_weight_layout_is_required():
+    """A call is refused (MOE_ERR_UNSUPPORTED, nothing enqueued, out left as
+    it was) unless the plan declares the weight layout its kernels read:
+    packed gate/up weights, and packed down weights exactly with the MXFP4
+    mid."""
+    import torch
+
+    from quantized_moe_expert_route_amd.binding import (LAYOUT_W13_PACKED, LAYOUT_W2_PACKED, MID_E4M3, MID_MXFP4,
+                                                        MOE_ERR_UNSUPPORTED, MoeError)
+
+    shape = X.Shape(M=4, H=512, E=16, I=128, top_k=2)
+    d = X.make_inputs(shape, "normal", 3)
+    g = upload(d)
+    plan = make_plan(shape)
+    out = torch.full((4, 512), 7, dtype=torch.int16, device=g["x"].device)
+    for fmt, layout in ((MID_E4M3, 0), (MID_E4M3, LAYOUT_W2_PACKED), (MID_E4M3, LAYOUT_W13_PACKED | LAYOUT_W2_PACKED),
+                        (MID_MXFP4, LAYOUT_W13_PACKED)):
+        plan.set_mid_format(fmt)
+        plan.set_weight_layout(layout)
+        with pytest.raises(MoeError) as e:
+            plan.forward(g["x"], g["logits"], g["w13"], g["s13"], g["w2"], g["s2"], out)
+        assert e.value.status == MOE_ERR_UNSUPPORTED
+        with pytest.raises(MoeError) as e:
+            plan.forward_noalloc(g["x"], g["logits"], g["w13"], g["s13"], g["w2"], g["s2"], out)
+        assert e.value.status == MOE_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert bool((out == 7).all()), "a refused call wrote its output"
+    plan.set_mid_format(MID_E4M3)
+    plan.set_weight_layout(LAYOUT_W13_PACKED)
+    plan.forward(g["x"], g["logits"], g["w13"], g["s13"], g["w2"], g["s2"], out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint16), oracle(d)["out"])

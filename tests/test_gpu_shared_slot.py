@@ -92,7 +92,7 @@ def test_shared_slot_with_mxfp4_mid(M):
     import torch
 
     from oracle import formats as F
-    from quantized_moe_expert_route_amd.binding import MID_MXFP4, pack_w2
+    from quantized_moe_expert_route_amd.binding import MID_MXFP4, layout_for, pack_w2
 
     shape = X.Shape(M=M, H=512, E=17, I=256, top_k=5)
     d = X.make_inputs(shape, "normal", 4100 + M)
@@ -100,6 +100,7 @@ def test_shared_slot_with_mxfp4_mid(M):
     plan = make_plan(shape)
     plan.set_shared_slot(True)
     plan.set_mid_format(MID_MXFP4)
+    plan.set_weight_layout(layout_for(MID_MXFP4))
     w2p, s2p = pack_w2(g["w2"], g["s2"])
     out = torch.full((M, shape.H), -1, dtype=torch.int16, device="cuda")
     plan.forward(g["x"], g["logits"], g["w13"], g["s13"], w2p, s2p, out)
