@@ -258,6 +258,52 @@ moe_status moe_forward(moe_plan* plan, int64_t M, const void* x, const float* lo
                        const void* w13, const void* s13, const void* w2, const void* s2,
                        void* out, void* stream);
 
+/* Tensor-parallel partial-sum exchange ("glm53: FP8 mid hand-off, early
+ * split rows, per-row up/gate jobs, ...", Accuracy Tests: a rank's peers'
+ * partial sums arrive tagged with the launch's epoch, and a one-GPU check
+ * runs rank 0 alone with zero peer partials and its pushes going to scratch
+ * sinks). With an exchange set on the plan, a call's combine keeps the
+ * rank's float64 partial (the slot-order sum before its bf16 rounding) in
+ * the rank's own inbox slot, then an epilogue launch pushes it to every
+ * peer, waits for the peers' partials, adds all tp partials in float64 in
+ * rank order 0..tp-1 and rounds once to bf16 into `out`: every rank forms
+ * the same bits. All buffers are caller-owned device memory; M below is the
+ * plan's maximum M, slots are indexed by rank:
+ *   inbox       fp64 [tp][M][H]: slot r receives rank r's partial (the
+ *               rank's own slot is written by the combine)
+ *   inbox_tags  u32 [tp][M][H/512]: tag of each 512-column chunk of a slot,
+ *               written (by the sender, after the chunk) as the epoch
+ *   push[p], push_tags[p]  for p != rank: where this rank's partial and its
+ *               tags go for peer p ([M][H] and [M][H/512]; peer p's inbox
+ *               slot `rank` in a real group, scratch sinks in a loopback);
+ *               entries p >= tp and p == rank are ignored
+ *   epoch       nonzero tag of this call's partials (a new one every call)
+ *   spin_limit  polls of a peer's tag before the wait gives up: the chunk
+ *               is then summed with whatever its slot holds and *status gets
+ *               bit 0 set (the call never hangs)
+ *   status      u32: set by the epilogue on a failed wait, never cleared */
+#define MOE_TP_MAX 8
+typedef struct {
+  int32_t tp;            /* ranks in the group, 1..MOE_TP_MAX */
+  int32_t rank;          /* this rank, 0..tp-1 */
+  uint32_t epoch;
+  int32_t spin_limit;    /* > 0 */
+  double* inbox;
+  uint32_t* inbox_tags;
+  double* push[MOE_TP_MAX];
+  uint32_t* push_tags[MOE_TP_MAX];
+  uint32_t* status;
+} moe_tp_exchange;
+
+/* Turn the exchange on for later calls (copied into the plan: set a new
+ * epoch before every call), or off with NULL. MOE_ERR_INVALID_ARG for a NULL
+ * plan, tp or rank out of range, a zero epoch, spin_limit <= 0, or a NULL or
+ * misaligned (16 bytes; tags 4) pointer that the group needs;
+ * MOE_ERR_UNSUPPORTED for H % 512 != 0 (always true of a valid plan) or the
+ * MXFP4 mid (its combine is not split); MOE_ERR_DEVICE for pointers on
+ * another device. Host-only. */
+moe_status moe_plan_set_tp_exchange(moe_plan* plan, const moe_tp_exchange* x);
+
 /* Bytes of the device scratch moe_forward_noalloc runs on: 64 MiB, one copy
  * per device the library runs on, held until the process ends. */
 #define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)

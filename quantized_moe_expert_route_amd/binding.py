@@ -39,6 +39,16 @@ class moe_ws_layout(ctypes.Structure):
     _fields_ = [(f, ctypes.c_size_t) for f in LAYOUT_FIELDS]
 
 
+TP_MAX = 8  # MOE_TP_MAX
+
+
+class moe_tp_exchange(ctypes.Structure):
+    _fields_ = [("tp", ctypes.c_int32), ("rank", ctypes.c_int32), ("epoch", ctypes.c_uint32),
+                ("spin_limit", ctypes.c_int32), ("inbox", ctypes.c_void_p), ("inbox_tags", ctypes.c_void_p),
+                ("push", ctypes.c_void_p * TP_MAX), ("push_tags", ctypes.c_void_p * TP_MAX),
+                ("status", ctypes.c_void_p)]
+
+
 class MoeError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -99,6 +109,8 @@ def lib() -> ctypes.CDLL:
     L.moe_plan_set_mid_format.argtypes = [vp, ctypes.c_int]
     L.moe_plan_set_weight_layout.restype = st
     L.moe_plan_set_weight_layout.argtypes = [vp, ctypes.c_uint]
+    L.moe_plan_set_tp_exchange.restype = st
+    L.moe_plan_set_tp_exchange.argtypes = [vp, ctypes.POINTER(moe_tp_exchange)]
     _lib = L
     return L
 
@@ -227,6 +239,27 @@ class Plan:
         st = lib().moe_plan_set_shared_slot(self._h, int(bool(on)))
         if st != MOE_OK:
             raise MoeError(st, "moe_plan_set_shared_slot")
+
+    def set_tp_exchange(self, tp=None, rank=0, epoch=1, inbox=None, inbox_tags=None, push=(), push_tags=(),
+                        status=None, spin_limit=1 << 20):
+        """Tensor-parallel exchange epilogue (moe_plan_set_tp_exchange); tp=None
+        turns it off. inbox: float64 [tp, M, H], inbox_tags: int32 [tp, M, H/512],
+        push / push_tags: per rank (None at this rank), status: int32 [1]."""
+        if tp is None:
+            st = lib().moe_plan_set_tp_exchange(self._h, None)
+            self._tpx = None
+        else:
+            x = moe_tp_exchange()
+            x.tp, x.rank, x.epoch, x.spin_limit = tp, rank, epoch, spin_limit
+            x.inbox, x.inbox_tags, x.status = _ptr(inbox), _ptr(inbox_tags), _ptr(status)
+            for p in range(tp):
+                if p != rank:
+                    x.push[p] = _ptr(push[p])
+                    x.push_tags[p] = _ptr(push_tags[p])
+            st = lib().moe_plan_set_tp_exchange(self._h, ctypes.byref(x))
+            self._tpx = (inbox, inbox_tags, tuple(push), tuple(push_tags), status)  # kept alive
+        if st != MOE_OK:
+            raise MoeError(st, "moe_plan_set_tp_exchange")
 
     def set_mid_format(self, fmt: int):
         """MID_E4M3 (default) or MID_MXFP4 for the plan's later calls (the

@@ -161,7 +161,8 @@ hipError_t enqueue_call(const moe_plan* plan, const CallArgs& a) {
     for (int i = 0; i < kStages; ++i) ev[i] = Ev{plan->events[2 * i], plan->events[2 * i + 1]};
   if (plan->call_start) {
     ev[0].start = plan->call_start;             // the route launch comes first
-    ev[fused_combine ? 5 : 6].stop = plan->call_stop;  // down (+ combine) or the combine comes last
+    // down (+ combine), the combine, or the exchange comes last
+    ev[fused_combine && plan->tpx.tp == 0 ? 5 : 6].stop = plan->call_stop;
   }
   // a stage with no launch of its own still records its (empty) interval
   auto none = [&](int i) -> hipError_t {
@@ -192,6 +193,13 @@ hipError_t enqueue_call(const moe_plan* plan, const CallArgs& a) {
   if (e == hipSuccess) e = plan->s.shared_I > 0 ? launch_shared(plan, a, ev[4]) : none(4);
   if (e == hipSuccess)
     e = mx ? launch_down_fp4(plan, a, ev[5]) : small ? launch_down_combine(plan, a, ev[5]) : launch_down_big(plan, a, ev[5]);
+  if (plan->tpx.tp > 0) {
+    // the combine (its own launch, or inside down) left the rank's partial
+    // in its inbox slot; the exchange epilogue forms `out`
+    if (e == hipSuccess && !fused_combine) e = launch_combine(plan, a, Ev{ev[6].start, nullptr});
+    if (e == hipSuccess) e = launch_tp_exchange(plan, a, fused_combine ? ev[6] : Ev{nullptr, ev[6].stop});
+    return e;
+  }
   if (e == hipSuccess) e = fused_combine ? none(6) : launch_combine(plan, a, ev[6]);
   return e;
 }
@@ -254,7 +262,7 @@ int moe_plan_stage_launches(const moe_plan* plan, int64_t M, int stage) {
     case 3: return mid_path(M, plan->s.top_k) ? 1 : 0;  // act_quant (inside gate/up above kMidM)
     case 4: return plan->s.shared_I > 0 ? (small ? 4 : 3) : 0;  // shared expert
     case 5: return 1;                             // down (+ combine when small, E4M3 mid)
-    default: return small && !mx ? 0 : 1;         // combine
+    default: return (small && !mx ? 0 : 1) + (plan->tpx.tp > 0 ? 1 : 0);  // combine (+ the exchange)
   }
 }
 
@@ -367,6 +375,32 @@ moe_status moe_plan_set_shared_slot(moe_plan* plan, int on) {
   return MOE_OK;
 }
 
+moe_status moe_plan_set_tp_exchange(moe_plan* plan, const moe_tp_exchange* x) {
+  if (!plan) return MOE_ERR_INVALID_ARG;
+  if (!x) {
+    memset(&plan->tpx, 0, sizeof(plan->tpx));
+    return MOE_OK;
+  }
+  if (x->tp < 1 || x->tp > MOE_TP_MAX || x->rank < 0 || x->rank >= x->tp || x->epoch == 0 || x->spin_limit <= 0)
+    return MOE_ERR_INVALID_ARG;
+  if (plan->s.H % 512 != 0 || plan->mid_fmt == MOE_MID_MXFP4) return MOE_ERR_UNSUPPORTED;
+  auto ok = [&](const void* q, unsigned align) -> moe_status {
+    if (!q || ((uintptr_t)q & (align - 1))) return MOE_ERR_INVALID_ARG;
+    return ptr_device(q) == plan->device ? MOE_OK : MOE_ERR_DEVICE;
+  };
+  moe_status st = ok(x->inbox, 16);
+  if (st == MOE_OK) st = ok(x->inbox_tags, 4);
+  if (st == MOE_OK) st = ok(x->status, 4);
+  for (int p = 0; st == MOE_OK && p < x->tp; ++p) {
+    if (p == x->rank) continue;
+    st = ok(x->push[p], 16);
+    if (st == MOE_OK) st = ok(x->push_tags[p], 4);
+  }
+  if (st != MOE_OK) return st;
+  plan->tpx = *x;
+  return MOE_OK;
+}
+
 moe_status moe_plan_set_weight_layout(moe_plan* plan, unsigned layout) {
   if (!plan || (layout & ~(unsigned)(MOE_LAYOUT_W13_PACKED | MOE_LAYOUT_W2_PACKED))) return MOE_ERR_INVALID_ARG;
   plan->layout = layout;
@@ -375,6 +409,7 @@ moe_status moe_plan_set_weight_layout(moe_plan* plan, unsigned layout) {
 
 moe_status moe_plan_set_mid_format(moe_plan* plan, int format) {
   if (!plan || (format != MOE_MID_E4M3 && format != MOE_MID_MXFP4)) return MOE_ERR_INVALID_ARG;
+  if (format == MOE_MID_MXFP4 && plan->tpx.tp > 0) return MOE_ERR_UNSUPPORTED;  // exchange is for the E4M3 mid
   plan->mid_fmt = format;
   return MOE_OK;
 }

@@ -83,7 +83,8 @@ template <int NB, int D, bool MID_LDS, int ST = 8>
 __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
     const uint8_t* __restrict__ midq, const float* __restrict__ mids, const uint8_t* __restrict__ w2, const uint8_t* __restrict__ s2, const int* __restrict__ sorted_entry,
     const int4* __restrict__ tiles, const int* __restrict__ meta, int H, int k, int M, int cw,
-    const float* __restrict__ topk_w, const float* __restrict__ ys, uint16_t* __restrict__ out) {
+    const float* __restrict__ topk_w, const float* __restrict__ ys, uint16_t* __restrict__ out,
+    double* __restrict__ partial) {
   constexpr int I = NB * 128;
   constexpr bool A16 = ST == 8;  // mid staged widened to bf16 (else E4M3, widened at each read)
   constexpr int LDA = (A16 ? 2 : 1) * I + kDcPad;  // bytes per staged mid row; the pad spreads 16 rows over the banks
@@ -313,8 +314,11 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
       a0 += (double)ys[(size_t)t * H + c0 + cc];
       a1 += (double)ys[(size_t)t * H + c0 + cc + 1];
     }
-    *reinterpret_cast<uint32_t*>(out + (size_t)t * H + c0 + cc) =
-        bf16_rne_from_double(a0) | (bf16_rne_from_double(a1) << 16);
+    if (partial)  // the sum before its rounding, for the tensor-parallel exchange
+      *reinterpret_cast<double2*>(partial + (size_t)t * H + c0 + cc) = make_double2(a0, a1);
+    else
+      *reinterpret_cast<uint32_t*>(out + (size_t)t * H + c0 + cc) =
+          bf16_rne_from_double(a0) | (bf16_rne_from_double(a1) << 16);
   }
 }
 
@@ -323,7 +327,7 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
 // of a y row, so each load instruction covers whole cache lines.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, const float* __restrict__ w,
                                                       const float* __restrict__ ys, int M, int H, int k,
-                                                      uint16_t* __restrict__ out) {
+                                                      uint16_t* __restrict__ out, double* __restrict__ partial) {
   const int per_tok = H / 4;
   const int64_t total = (int64_t)M * per_tok;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
@@ -340,9 +344,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       const float4 a = *reinterpret_cast<const float4*>(ys + (size_t)t * H + c);
       acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
     }
-    const uint32_t o0 = bf16_rne_from_double(acc[0]) | (bf16_rne_from_double(acc[1]) << 16);
-    const uint32_t o1 = bf16_rne_from_double(acc[2]) | (bf16_rne_from_double(acc[3]) << 16);
-    *reinterpret_cast<uint2*>(out + (size_t)t * H + c) = make_uint2(o0, o1);
+    if (partial) {  // the sum before its rounding, for the tensor-parallel exchange
+      double2* pp = reinterpret_cast<double2*>(partial + (size_t)t * H + c);
+      pp[0] = make_double2(acc[0], acc[1]);
+      pp[1] = make_double2(acc[2], acc[3]);
+    } else {
+      const uint32_t o0 = bf16_rne_from_double(acc[0]) | (bf16_rne_from_double(acc[1]) << 16);
+      const uint32_t o1 = bf16_rne_from_double(acc[2]) | (bf16_rne_from_double(acc[3]) << 16);
+      *reinterpret_cast<uint2*>(out + (size_t)t * H + c) = make_uint2(o0, o1);
+    }
   }
 }
 
@@ -375,7 +385,7 @@ hipError_t launch_down_combine(const moe_plan* p, const CallArgs& a, Ev ev) {
                     wsp<float>(p, p->L.mids), reinterpret_cast<const uint8_t*>(a.w2),
                     reinterpret_cast<const uint8_t*>(a.s2), wsp<int>(p, p->L.sorted_entry), wsp<int4>(p, p->X.tiles),
                     wsp<int>(p, p->X.meta), H, (int)p->s.top_k, (int)a.M, cw, wsp<float>(p, p->L.topk_w), ys,
-                    reinterpret_cast<uint16_t*>(a.out));
+                    reinterpret_cast<uint16_t*>(a.out), tp_own_partial(p));
   };
   // weights of D tiles in flight per wave; fewer when the slots also carry mid rows
   switch (I / 128) {
@@ -397,7 +407,8 @@ hipError_t launch_combine(const moe_plan* p, const CallArgs& a, Ev ev) {
   const int blocks = (int)std::min<int64_t>((total + 255) / 256, 8192);
   const float* ys = p->s.shared_I > 0 ? wsp<float>(p, p->L.sh_y) : nullptr;
   return launch_k(combine_kernel, dim3(blocks), dim3(256), 0, a.stream, ev, wsp<float>(p, p->L.y),
-                  wsp<float>(p, p->L.topk_w), ys, (int)a.M, H, (int)p->s.top_k, reinterpret_cast<uint16_t*>(a.out));
+                  wsp<float>(p, p->L.topk_w), ys, (int)a.M, H, (int)p->s.top_k, reinterpret_cast<uint16_t*>(a.out),
+                  tp_own_partial(p));
 }
 
 }  // namespace qmoe

@@ -50,6 +50,7 @@ struct moe_plan {
   hipEvent_t events[16];
   int n_events;
   hipEvent_t call_start, call_stop;
+  moe_tp_exchange tpx;  // tensor-parallel exchange epilogue (tpx.tp > 0: on)
   int mid_fmt;     // moe_mid_format
   unsigned layout; // moe_weight_layout flags declared by the caller
   int shared_slot; // 1: expert E-1 is the shared expert, slot top_k-1 of every token
@@ -127,6 +128,14 @@ hipError_t launch_pack_shared(const void* ws13, const void* ws2, int64_t Is, int
 hipError_t launch_gate_up_big(const moe_plan* p, const CallArgs& a, Ev ev);
 hipError_t launch_down_big(const moe_plan* p, const CallArgs& a, Ev ev);
 hipError_t launch_combine(const moe_plan* p, const CallArgs& a, Ev ev);
+// With the tensor-parallel exchange on, the combines write the rank's float64
+// partial into its own inbox slot instead of bf16 `out` (else nullptr).
+inline double* tp_own_partial(const moe_plan* p) {
+  return p->tpx.tp > 0 ? p->tpx.inbox + (size_t)p->tpx.rank * (size_t)p->s.M * (size_t)p->s.H : nullptr;
+}
+// the exchange: push the partial to the peers, wait for theirs, sum in rank
+// order, one bf16 rounding into `out` (tp_exchange.hip)
+hipError_t launch_tp_exchange(const moe_plan* p, const CallArgs& a, Ev ev);
 // MXFP4 mid hand-off (a4w4.hip): mid per 32 as E2M1 + E8M0; down on the
 // scaled FP4 MFMA over 16-row tiles, y to HBM
 hipError_t launch_act_quant_mx(const moe_plan* p, const CallArgs& a, Ev ev);

@@ -89,6 +89,7 @@ def test_null_and_unbound_arguments_fail_before_any_device_work():
     assert L.moe_plan_set_shared(None, None, None, None, None, None, 0, None) == B.MOE_ERR_INVALID_ARG
     assert L.moe_plan_shared_pack_bytes(None) == 0
     assert L.moe_plan_set_weight_layout(None, B.LAYOUT_W13_PACKED) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_plan_set_tp_exchange(None, None) == B.MOE_ERR_INVALID_ARG
     L.moe_plan_destroy(None)
 
 
