@@ -80,7 +80,10 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measure(name, steps, warmup, n_sets, mid_fmt=0):
+def measure(name, steps, warmup, n_sets, mid_fmt=0, tp_loopback=0):
+    """Time `name`'s calls. tp_loopback = T > 0 runs them with the
+    tensor-parallel exchange epilogue as rank 0 of T alone: the peers'
+    partials zeros tagged with the epoch, the pushes into scratch sinks."""
     import torch
 
     from quantized_moe_expert_route_amd import fixtures as X
@@ -107,6 +110,14 @@ def measure(name, steps, warmup, n_sets, mid_fmt=0):
     plan.set_mid_format(mid_fmt)
     plan.set_weight_layout(layout_for(mid_fmt))
     plan.set_shared_slot(wl.shared_slot)
+    if tp_loopback:
+        T = tp_loopback
+        inbox = torch.zeros((T, s.M, s.H), dtype=torch.float64, device=dev)
+        tags = torch.ones((T, s.M, s.H // 512), dtype=torch.int32, device=dev)
+        sinks = [None] + [torch.empty((s.M, s.H), dtype=torch.float64, device=dev) for _ in range(T - 1)]
+        sink_tags = [None] + [torch.empty((s.M, s.H // 512), dtype=torch.int32, device=dev) for _ in range(T - 1)]
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+        plan.set_tp_exchange(T, 0, 1, inbox, tags, sinks, sink_tags, status)
     x = torch.empty_like(sets[0][0])
     logits = torch.empty_like(sets[0][1])
     out = torch.empty((s.M, s.H), dtype=torch.int16, device=dev)
@@ -206,6 +217,8 @@ def measure(name, steps, warmup, n_sets, mid_fmt=0):
     # stages folded into another one for this M record an empty pair of events
     launches = np.array(plan.stage_launches(s.M))
     kern_us = np.where(launches[None, :] > 0, stage_us, 0.0)
+    if tp_loopback:
+        assert int(status.item()) == 0, "an exchange wait gave up"
     per_set_act = [n_act[i % n_sets] for i in range(steps)]
     mean_act = float(np.mean(per_set_act))
     res = {
@@ -220,29 +233,69 @@ def measure(name, steps, warmup, n_sets, mid_fmt=0):
     return res
 
 
-def cpu_baseline(res, budget_s=12.0):
-    """The oracle, as it stands, on the host: whole calls on the headline
-    workload's inputs until ~budget_s of CPU work."""
-    from threadpoolctl import threadpool_info
-
+def _time_oracle(d, n_max, budget_s):
     from oracle import moe as O
 
-    d = res["base"]
     s = d["shape"]
     shared = (d["ws13"], d["ss13"], d["ws2"], d["ss2"]) if s.shared_I else None
     times = []
     t_start = time.perf_counter()
-    while True:
+    while len(times) < n_max:
         t0 = time.perf_counter()
         O.moe_forward(d["x"], d["logits"], d["w13"], d["s13"], d["w2"], d["s2"], s.top_k, s.routed_scaling, shared)
         times.append(time.perf_counter() - t0)
-        if time.perf_counter() - t_start > budget_s or len(times) >= 20:
+        if time.perf_counter() - t_start > budget_s:
             break
+    return float(np.median(times) * 1e6), len(times)
+
+
+def cpu_baseline(res, budget_s=12.0):
+    """The oracle, as it stands, on the host: whole calls on the headline
+    workload's inputs (median of up to 5, within ~budget_s of CPU work), with
+    every BLAS thread and with one; and the tiny c0 call likewise."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from quantized_moe_expert_route_amd import fixtures as X
+
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": float(np.median(times) * 1e6), "unit": "us per call", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{len(times)} whole calls of the {res['name']} workload (M={s.M}), median; "
-                      f"host os.cpu_count()={os.cpu_count()}, affinity={len(os.sched_getaffinity(0))}"}
+    d = res["base"]
+    multi, n_multi = _time_oracle(d, 5, budget_s)
+    with threadpool_limits(1):
+        single, n_single = _time_oracle(d, 5, budget_s / 2)
+    d0 = X.make_inputs("c0")
+    c0_multi, _ = _time_oracle(d0, 5, 2.0)
+    with threadpool_limits(1):
+        c0_single, _ = _time_oracle(d0, 5, 2.0)
+    return {"value": round(multi, 1), "unit": "us per call", "cores": int(threads), "kind": "oracle",
+            "sample": f"whole calls of the {res['name']} workload (M={d['shape'].M}): median of {n_multi} with "
+                      f"{threads} BLAS threads; host os.cpu_count()={os.cpu_count()}, "
+                      f"affinity={len(os.sched_getaffinity(0))}",
+            "single_thread_us": round(single, 1), "single_thread_calls": n_single,
+            "c0_us": round(c0_multi, 1), "c0_single_thread_us": round(c0_single, 1)}
+
+
+def cpu_full():
+    """The oracle on every configuration: c0-c2 median of 5 with all BLAS
+    threads and with one, c3/c4 once with all threads (minutes of CPU work;
+    not part of the default run)."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from quantized_moe_expert_route_amd import fixtures as X
+
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    out = {"cores": int(threads), "cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
+           "unit": "us per call", "configs": {}}
+    for name in ("c0", "c1", "c2", "c3", "c4"):
+        d = X.make_inputs(name)
+        reps = 5 if name in ("c0", "c1", "c2") else 1
+        multi, n = _time_oracle(d, reps, 1e9)
+        row = {"multi_thread_us": round(multi, 1), "runs": n}
+        if reps == 5:
+            with threadpool_limits(1):
+                row["single_thread_us"] = round(_time_oracle(d, reps, 1e9)[0], 1)
+        out["configs"][name] = row
+        print(f"[cpu] {name}: {row}", file=sys.stderr, flush=True)
+    return out
 
 
 def traffic_for(name, kernel):
@@ -275,6 +328,13 @@ def main():
                          "arm), reported as '<name>/mxfp4'; up to 256 tokens ('' for none)")
     ap.add_argument("--sets", type=int, default=8, help="distinct input batches cycled through the steps")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="only time the CPU oracle on c0..c4 (c0-c2 median of 5, all threads and one; c3/c4 once) "
+                         "and print it as JSON; needs no GPU")
+    ap.add_argument("--tp-loopback", default="c1",
+                    help="workloads also timed with the tensor-parallel exchange epilogue as rank 0 of TP8 alone "
+                         "(zero peer partials tagged with the epoch, pushes into scratch sinks), reported as "
+                         "'<name>/tp8_loopback' ('' for none)")
     ap.add_argument("--torch-read", type=int, default=0, metavar="MIB",
                     help="only time torch's reduction over a cold MIB MiB buffer (the same 1 GiB flush before "
                          "each) and print its rate: a library baseline for reading that many bytes once")
@@ -282,6 +342,9 @@ def main():
                     help="only run 5 plain device-to-device copies of MIB MiB (the known-size kernel that "
                          "scales the HBM byte counters of a profiler run), then exit")
     args = ap.parse_args()
+    if args.cpu_full:
+        print(json.dumps(cpu_full()))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               f"(the path is one tensor-parallel rank's call on one MI355X)", file=sys.stderr)
@@ -327,10 +390,13 @@ def main():
     others = {}
     runs = [(c, 0) for c in args.also.split(",") if c and c != args.config]
     runs += [(c, 1) for c in args.mxfp4.split(",") if c]
-    for name, fmt in runs:
-        r = measure(name, max(10, args.steps // 2), max(3, args.warmup // 2), min(args.sets, 4), mid_fmt=fmt)
+    runs += [(c, 8) for c in args.tp_loopback.split(",") if c]
+    for name, mode in runs:
+        fmt, tp = (mode, 0) if mode < 2 else (0, mode)
+        r = measure(name, max(10, args.steps // 2), max(3, args.warmup // 2), min(args.sets, 4), mid_fmt=fmt,
+                    tp_loopback=tp)
         mu = r["cold_us"].mean()
-        name = f"{name}/mxfp4" if fmt else name
+        name = f"{name}/mxfp4" if fmt else f"{name}/tp{tp}_loopback" if tp else name
         others[name] = {
             "us_per_call_cold": round(mu, 2), "us_per_call_graph_replay": round(float(r["graph_us"].mean()), 2),
             "us_per_call_warm": round(r["warm_us"], 2),
@@ -346,7 +412,7 @@ def main():
     gu_us = head["stage_us"]["gate_up"]
     achieved = head["gate_up_bytes"] / (gu_us * 1e-6) / 1e9
     line = {
-        "metric": "us per local MoE call (cold MALL, hipGraph replay)",
+        "metric": "us per local MoE call (cold MALL, device span of the call's kernels)",
         "value": round(mu, 3),
         "unit": "us",
         "n_gpus": 1,
@@ -374,8 +440,11 @@ def main():
         "stage_timing": "events recorded by the launches of each stage (start of its first kernel, end "
                         "of its last); 0 for a stage folded into another; cold, eager",
         "timed_region_s": round(head["wall_s"], 4),
+        "roofline_call": {"bound": "hbm", "frac": round(head["bytes"] / (mu * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                          "note": "the whole call's algorithmic bytes over its device span, against 8 TB/s"},
         "roofline": {
             "kernel": "gate_up",
+            "note": "the dominant kernel of the call (gate/up weight streaming), not the whole call",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
