@@ -69,6 +69,23 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     return LIB
 
 
+PROBE_SRC = os.path.join(ROOT, "tests", "probe", "mfma_probe.hip")
+PROBE_LIB = os.path.join(ROOT, "tests", "probe", "libmfma_probe.so")
+
+
+def build_probe() -> str:
+    """Compile the MFMA characterization probe the GPU tests load (test
+    infrastructure, not part of libqmoe.so)."""
+    if not os.path.exists(PROBE_SRC):
+        return ""
+    cmd = [_hipcc(), *FLAGS, "-shared", PROBE_SRC, "-o", PROBE_LIB + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("probe build failed:\n" + r.stdout + r.stderr)
+    os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
+    return PROBE_LIB
+
+
 def resource_usage() -> dict:
     """Per-kernel register and scratch use of this build, from the compiler's
     kernel-resource-usage remarks: {kernel: {"VGPRs": .., "AGPRs": ..,
@@ -98,3 +115,4 @@ def resource_usage() -> dict:
 
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_probe())

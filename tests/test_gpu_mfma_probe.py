@@ -1,0 +1,64 @@
+"""Characterization of the MFMA arithmetic behind the down kernels' design:
+the scaled FP8 x FP4 MFMA does not return a 128-element block's dot product
+when a small product sits beside a large one (it drops the small products),
+while the bf16 MFMA on the same values widened to bf16 does (its products are
+exact and its sum is exact while representable in binary32). This is why the
+down GEMMs widen to bf16 (and the shared expert uses int8 digits) although
+the FP8 x FP4 MFMA would need half the MFMA cycles."""
+
+import ctypes
+import os
+
+import numpy as np
+import pytest
+
+from oracle import formats as F
+
+pytestmark = pytest.mark.gpu
+
+LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "probe", "libmfma_probe.so")
+
+
+def _probe(a_codes, b_codes):
+    import torch
+
+    if not os.path.exists(LIB):
+        raise RuntimeError(f"{LIB} is missing: build it with __graft_entry__.build()")
+    L = ctypes.CDLL(LIB)
+    L.qmoe_probe_dot128.argtypes = [ctypes.c_void_p] * 5
+    dev = torch.device("cuda", 0)
+    a = torch.from_numpy(a_codes.astype(np.uint8)).to(dev)
+    b = torch.from_numpy(F.pack_fp4(b_codes.astype(np.uint8))).to(dev)
+    d8 = torch.zeros((16, 16), dtype=torch.float32, device=dev)
+    d16 = torch.zeros_like(d8)
+    st = L.qmoe_probe_dot128(a.data_ptr(), b.data_ptr(), d8.data_ptr(), d16.data_ptr(),
+                             torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == 0
+    return d8.cpu().numpy(), d16.cpu().numpy()
+
+
+def test_fp8_mfma_drops_small_products_bf16_does_not():
+    # A: row m holds one 448 and 127 copies of a small E4M3 value v_m (v_m
+    # from 2^-9, the subnormal step, up to 2^0); B: every element 1.0
+    small = [0x01, 0x02, 0x04, 0x08, 0x10, 0x18, 0x20, 0x28, 0x30, 0x38]  # 2^-9 .. 2^0
+    a = np.zeros((16, 128), np.uint8)
+    for m, c in enumerate(small):
+        a[m, :] = c
+        a[m, 5] = 0x7E  # 448
+    a[12, :] = 0x01  # only small products: 128 x 2^-9
+    b = np.full((16, 128), 2, np.uint8)  # E2M1 code 2 = 1.0
+    d8, d16 = _probe(a, b)
+    exact = F.e4m3_decode(a).sum(axis=1)  # float64, exact here
+    for m in range(16):
+        assert np.all(d16[m] == exact[m]), f"bf16 MFMA row {m}: {d16[m, 0]} != {exact[m]}"
+        print(f"row {m}: exact {exact[m]!r}  bf16 {d16[m, 0]!r}  fp8xfp4 {d8[m, 0]!r}")
+    # 448 (K position 5) beside products of 2^-9 .. 2^-6: the FP8 x FP4 MFMA
+    # loses the 7 small products that share its group of 8 K positions (they
+    # lie more than 2^13 below it); from 2^-5 on, and without a large
+    # product, the sum is exact
+    vals = F.e4m3_decode(np.array(small, np.uint8))
+    for m in range(4):
+        assert np.all(d8[m] == exact[m] - 7 * vals[m]), f"row {m}: {d8[m, 0]!r}"
+    for m in list(range(4, 10)) + [12]:
+        assert np.all(d8[m] == exact[m]), f"row {m}: {d8[m, 0]!r}"
