@@ -202,6 +202,7 @@ class Plan:
             raise MoeError(st, "moe_plan_set_workspace")
         self._shared = None
         self._events = None
+        self._layout = LAYOUT_W13_PACKED
         self.set_weight_layout(weight_layout)
 
     def set_weight_layout(self, layout: int):
@@ -211,6 +212,45 @@ class Plan:
         st = lib().moe_plan_set_weight_layout(self._h, int(layout))
         if st != MOE_OK:
             raise MoeError(st, "moe_plan_set_weight_layout")
+        self._layout = int(layout)
+
+    def _tensor(self, name, t, dtypes, numel=None, rows=None, cols=None, min_numel=None):
+        """The library sees bare pointers: a tensor on another device, of
+        another element type, strided, or smaller than the plan's shape would
+        be read or written out of bounds, so each is checked here."""
+        import torch
+
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch tensor")
+        if t.device != self.device:
+            raise ValueError(f"{name} is on {t.device}, the plan on {self.device}")
+        if t.dtype not in dtypes:
+            raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if numel is not None and t.numel() != numel:
+            raise ValueError(f"{name} holds {t.numel()} elements, the plan's shape needs {numel}")
+        if min_numel is not None and t.numel() < min_numel:
+            raise ValueError(f"{name} holds {t.numel()} elements, at least {min_numel} are needed")
+        if cols is not None and (t.dim() != 2 or t.shape[1] != cols or t.shape[0] < rows):
+            raise ValueError(f"{name} is {tuple(t.shape)}, expected at least [{rows}, {cols}]")
+
+    def _check_call(self, M, x, logits, w13, s13, w2, s2, out):
+        import torch
+
+        s = self.shape
+        if not 0 <= int(M) <= s.M:
+            raise ValueError(f"M = {M} outside [0, {s.M}] (the plan's shape)")
+        H, E, I = s.H, s.E, s.I
+        bf16 = (torch.int16, torch.bfloat16)
+        self._tensor("x", x, bf16, rows=M, cols=H)
+        self._tensor("logits", logits, (torch.float32,), rows=M, cols=E)
+        self._tensor("out", out, bf16, rows=M, cols=H)
+        u8 = (torch.uint8,)
+        self._tensor("w13", w13, u8, numel=E * 2 * I * H // 2)
+        self._tensor("s13", s13, u8, numel=E * 2 * I * H // 32)
+        self._tensor("w2", w2, u8, numel=E * H * I // 2)
+        self._tensor("s2", s2, u8, numel=E * H * (16 if self._layout & LAYOUT_W2_PACKED else I // 32))
 
     def layout(self) -> Dict[str, int]:
         L = moe_ws_layout()
@@ -226,6 +266,11 @@ class Plan:
         object allocates and keeps (with the scales)."""
         import torch
 
+        H, Is = self.shape.H, self.shape.shared_I
+        self._tensor("ws13", ws13, (torch.uint8,), numel=2 * Is * H)
+        self._tensor("ss13", ss13, (torch.float32,), numel=(2 * Is // 128) * (H // 128))
+        self._tensor("ws2", ws2, (torch.uint8,), numel=H * Is)
+        self._tensor("ss2", ss2, (torch.float32,), numel=(H // 128) * (Is // 128))
         nbytes = lib().moe_plan_shared_pack_bytes(self._h)
         packed = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=self.device)
         st = lib().moe_plan_set_shared(self._h, _ptr(ws13), _ptr(ss13), _ptr(ws2), _ptr(ss2), _ptr(packed),
@@ -249,6 +294,17 @@ class Plan:
             st = lib().moe_plan_set_tp_exchange(self._h, None)
             self._tpx = None
         else:
+            import torch
+
+            M, H = self.shape.M, self.shape.H
+            tags = (torch.int32, torch.uint32)
+            self._tensor("inbox", inbox, (torch.float64,), numel=tp * M * H)
+            self._tensor("inbox_tags", inbox_tags, tags, numel=tp * M * (H // 512))
+            self._tensor("status", status, tags, min_numel=1)
+            for p in range(tp):
+                if p != rank:
+                    self._tensor(f"push[{p}]", push[p], (torch.float64,), min_numel=M * H)
+                    self._tensor(f"push_tags[{p}]", push_tags[p], tags, min_numel=M * (H // 512))
             x = moe_tp_exchange()
             x.tp, x.rank, x.epoch, x.spin_limit = tp, rank, epoch, spin_limit
             x.inbox, x.inbox_tags, x.status = _ptr(inbox), _ptr(inbox_tags), _ptr(status)
@@ -295,6 +351,7 @@ class Plan:
         """Enqueue the call on `stream` (default: torch's current stream)."""
         if M is None:
             M = x.shape[0]
+        self._check_call(M, x, logits, w13, s13, w2, s2, out)
         st = lib().moe_forward(self._h, int(M), _ptr(x), _ptr(logits), _ptr(w13), _ptr(s13), _ptr(w2),
                                _ptr(s2), _ptr(out), _stream(stream))
         if st != MOE_OK:
@@ -306,6 +363,7 @@ class Plan:
         scratch instead of this plan's workspace (nothing is allocated)."""
         if M is None:
             M = x.shape[0]
+        self._check_call(M, x, logits, w13, s13, w2, s2, out)
         st = lib().moe_forward_noalloc(self._h, int(M), _ptr(x), _ptr(logits), _ptr(w13), _ptr(s13), _ptr(w2),
                                        _ptr(s2), _ptr(out), _stream(stream))
         if st != MOE_OK:

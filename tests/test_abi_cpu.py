@@ -148,3 +148,40 @@ def test_noalloc_scratch_size_matches_header():
     m = re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
     assert m and int(m.group(1)) << int(m.group(2)) == B.NOALLOC_SCRATCH_BYTES
     assert B.lib().moe_forward_noalloc(None, 4, None, None, None, None, None, None, None, None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_plan_call_checks_reject_bad_tensors():
+    """The binding checks every tensor a call passes before the library sees
+    its bare pointer (host logic only: a plan object without a device plan)."""
+    import torch
+
+    M, H, E, I = 4, 512, 16, 128
+    p = B.Plan.__new__(B.Plan)
+    p._h = ctypes.c_void_p()
+    p.shape = B.moe_shape(M, H, E, I, 2, 2.5, 0)
+    p.device = torch.device("cpu")
+    p._layout = B.LAYOUT_W13_PACKED
+    u8 = lambda n: torch.zeros(n, dtype=torch.uint8)
+    good = dict(x=torch.zeros((M, H), dtype=torch.int16), logits=torch.zeros((M, E)),
+                w13=u8(E * 2 * I * H // 2), s13=u8(E * 2 * I * H // 32), w2=u8(E * H * I // 2), s2=u8(E * H * I // 32),
+                out=torch.zeros((M, H), dtype=torch.bfloat16))
+    p._check_call(M, **good)
+    p._check_call(2, **dict(good, x=torch.zeros((2, H), dtype=torch.int16)))  # rows >= the call's M suffice
+    bad = [
+        (M, dict(x=torch.zeros((M - 1, H), dtype=torch.int16))),           # fewer rows than M
+        (M, dict(x=torch.zeros((H, M), dtype=torch.int16).t())),           # strided view
+        (M, dict(logits=torch.zeros((M, E), dtype=torch.float64))),       # wrong dtype
+        (M, dict(logits=torch.zeros((M, E + 1)))),                        # wrong width
+        (M, dict(out=torch.zeros((M, H), dtype=torch.int32))),
+        (M, dict(w13=u8(E * 2 * I * H // 2 - 1))),
+        (M, dict(w2=u8(E * H * I // 2 + 16))),
+        (M, dict(s2=u8(E * H * 16))),                                     # packed scales, row-major declared
+        (M + 1, dict(x=torch.zeros((M + 1, H), dtype=torch.int16))),      # beyond the plan's M
+    ]
+    for m, change in bad:
+        with pytest.raises(ValueError):
+            p._check_call(m, **dict(good, **change))
+    with pytest.raises(TypeError):
+        p._check_call(M, **dict(good, x=None))
+    p._layout = B.LAYOUT_W13_PACKED | B.LAYOUT_W2_PACKED
+    p._check_call(M, **dict(good, s2=u8(E * H * 16)))

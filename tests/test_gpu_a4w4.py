@@ -158,7 +158,8 @@ def test_mx_rejects_large_m():
     nothing enqueued); the E4M3 mid serves them on the same plan."""
     import torch
 
-    from quantized_moe_expert_route_amd.binding import MID_E4M3, MID_MXFP4, MOE_ERR_UNSUPPORTED, MoeError, layout_for
+    from quantized_moe_expert_route_amd.binding import (MID_E4M3, MID_MXFP4, MOE_ERR_UNSUPPORTED, MoeError,
+                                                        layout_for, pack_w2)
 
     shape = X.Shape(M=300, H=512, E=16, I=128, top_k=2)
     d = X.make_inputs(shape, "normal", 5)
@@ -167,8 +168,9 @@ def test_mx_rejects_large_m():
     plan.set_mid_format(MID_MXFP4)
     plan.set_weight_layout(layout_for(MID_MXFP4))
     out = torch.empty((300, 512), dtype=torch.int16, device=g["x"].device)
+    w2p, s2p = pack_w2(g["w2"], g["s2"])
     with pytest.raises(MoeError) as ei:
-        plan.forward(g["x"], g["logits"], g["w13"], g["s13"], g["w2"], g["s2"], out, M=300)
+        plan.forward(g["x"], g["logits"], g["w13"], g["s13"], w2p, s2p, out, M=300)
     assert ei.value.status == MOE_ERR_UNSUPPORTED
     assert plan.stage_launches(300) == [-1] * len(plan.stage_launches(300))  # not served
     plan.set_mid_format(MID_MXFP4)

@@ -48,7 +48,7 @@ def test_noalloc_after_other_plans_and_rejects_large():
     """A call after calls of other plans (whose data sits where this plan
     keeps its token bitmap) still equals moe_forward; a plan whose workspace
     exceeds the scratch is refused before anything runs."""
-    from quantized_moe_expert_route_amd.binding import MoeError, NOALLOC_SCRATCH_BYTES, MOE_ERR_UNSUPPORTED
+    from quantized_moe_expert_route_amd.binding import MOE_ERR_UNSUPPORTED, NOALLOC_SCRATCH_BYTES, lib
 
     a = X.Shape(M=200, H=2048, E=64, I=256, top_k=8)
     b = X.Shape(M=48, H=512, E=16, I=128, top_k=2)
@@ -63,8 +63,8 @@ def test_noalloc_after_other_plans_and_rejects_large():
     big = X.Shape(M=4096, H=6144, E=256, I=512, top_k=8)
     pbig = make_plan(big)
     assert pbig.workspace.numel() > NOALLOC_SCRATCH_BYTES
-    gbig = {k: gb[k] for k in gb}
-    with pytest.raises(MoeError) as e:
-        pbig.forward_noalloc(gbig["x"], gbig["logits"], gbig["w13"], gbig["s13"], gbig["w2"], gbig["s2"],
-                             gbig["x"], M=1)
-    assert e.value.status == MOE_ERR_UNSUPPORTED
+    # through the C ABI with the small plan's tensors: refused on the
+    # workspace size before any pointer is used (the binding would refuse
+    # these tensors' sizes first)
+    args = [gb[k].data_ptr() for k in ("x", "logits", "w13", "s13", "w2", "s2")] + [gb["x"].data_ptr(), None]
+    assert lib().moe_forward_noalloc(pbig._h, 1, *args) == MOE_ERR_UNSUPPORTED
