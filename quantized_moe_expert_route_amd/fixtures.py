@@ -280,6 +280,46 @@ def make_shared(shape: Shape, seed: int):
     return ws13, ss13, ws2, ss2
 
 
+def make_extreme_inputs(shape: Shape, seed: int):
+    """Inputs whose scale bytes reach both ends of the E8M0 range, for the
+    edge cases of the formats (scale byte 0, whose power 2^-127 lies below
+    binary32's normal range; bf16 subnormal x; widened weights below bf16's
+    normal range; magnitudes near 2^+-100).
+
+    Token t belongs to group g = t % 4 and is routed to experts 2g and 2g + 1
+    only (those two logits get +2.0 on U[0, 1) draws), so each expert sees
+    tokens of one magnitude. Starting from make_inputs' draws (weight scale
+    bytes 119..121), per group:
+      g0  x ~ N(0, 1)                     w13 bytes as drawn   w2 bytes as drawn
+      g1  x * 2^-100                      w13 bytes + 100      w2 bytes - 119 (0..2)
+      g2  x * 2^100                       w13 bytes - 100      w2 bytes + 110 (229..231)
+      g3  x * 0.3 * 2^-126 in even blocks
+          of 32 (some bf16 subnormals),
+          x * 2^-124 in odd blocks        w13 bytes + 128      w2 bytes - 60
+    Needs E >= 8, top_k == 2 and H a multiple of 64.
+    """
+    assert shape.E >= 8 and shape.top_k == 2 and shape.H % 64 == 0 and shape.shared_I == 0
+    M, H, E = shape.M, shape.H, shape.E
+    d = make_inputs(shape, "uniform", seed)
+    grp = np.arange(M) % 4
+    lg = d["logits"]
+    lg[np.arange(M), 2 * grp] += np.float32(2.0)
+    lg[np.arange(M), 2 * grp + 1] += np.float32(2.0)
+    a = _rng(seed, _T_X).standard_normal((M, H), dtype=np.float32).astype(np.float64)
+    even = (np.arange(H) // 32) % 2 == 0
+    factor = np.ones((M, H))
+    factor[grp == 1] = 2.0 ** -100
+    factor[grp == 2] = 2.0 ** 100
+    factor[np.ix_(grp == 3, even)] = 0.3 * 2.0 ** -126
+    factor[np.ix_(grp == 3, ~even)] = 2.0 ** -124
+    d["x"] = bf16_bits_from_f32((a * factor).astype(np.float32))
+    for g, d13, d2 in ((1, 100, -119), (2, -100, 110), (3, 128, -60)):
+        for e in (2 * g, 2 * g + 1):
+            d["s13"][e] = (d["s13"][e].astype(np.int64) + d13).astype(np.uint8)
+            d["s2"][e] = (d["s2"][e].astype(np.int64) + d2).astype(np.uint8)
+    return d
+
+
 def make_inputs(name_or_shape, logits: Optional[str] = None, seed: Optional[int] = None,
                 experts: Optional[np.ndarray] = None, with_weights: bool = True, shared_slot: bool = False):
     """All inputs of one call as numpy arrays.

@@ -457,3 +457,22 @@ def test_tp_exchange_sum_pins():
     one = np.full((1, 1), 1.0)
     assert F.bf16_decode(O.tp_exchange_sum([big, one, -big]))[0, 0] == 0.0
     assert F.bf16_decode(O.tp_exchange_sum([big, -big, one]))[0, 0] == 1.0
+
+
+@pytest.mark.parametrize("M", [8, 300])
+def test_extreme_scale_inputs_reach_the_edges(M):
+    """The extreme-scale fixture reaches scale byte 0 on x and on w2, bf16
+    subnormal x and binary32-subnormal outputs, routes each token group to its
+    own experts only, and the oracle's exactness assertions hold on it."""
+    shape = X.Shape(M=M, H=512, E=16, I=128, top_k=2)
+    d = X.make_extreme_inputs(shape, 7)
+    r = O.moe_forward(d["x"], d["logits"], d["w13"], d["s13"], d["w2"], d["s2"], 2, 2.5)
+    grp = np.arange(M) % 4
+    assert np.array_equal(np.sort(r["ids"], axis=1), np.stack([2 * grp, 2 * grp + 1], axis=1))
+    assert (r["xs"][grp == 3] == 0).any() and (d["s2"][2:4] == 0).any()
+    assert int(d["s13"].max()) >= 247 and int(d["s2"].max()) >= 229
+    xv = F.bf16_decode(d["x"])
+    assert ((np.abs(xv) < 2.0 ** -126) & (xv != 0)).any()
+    y = np.abs(r["y"].reshape(M, 2, -1)[grp == 1])
+    assert ((y < 2.0 ** -126) & (y > 0)).any()
+    assert np.all(np.isfinite(F.bf16_decode(r["out"])))
