@@ -88,7 +88,12 @@ typedef struct moe_plan moe_plan; /* opaque; host memory only */
  *                                   scales K-block major: block b of token t
  *                                   at b * M + t)
  *   sh_y         fp32  [M, H]       shared expert output
- * Offsets of absent parts (no shared expert) are 0. */
+ * A call of at most 16 tokens (and 512 slots) with the E4M3 mid and
+ * shared_I <= 512 runs the shared expert inside the routed launches: its
+ * sh_xq and sh_hq then hold plain E4M3 codes, u8 [M, H] and u8 [M, Is]
+ * (scales as above), and sh_y is not written (each down workgroup adds its
+ * columns of the shared output into the combine). Offsets of absent parts
+ * (no shared expert) are 0. */
 typedef struct {
   size_t total_bytes;
   size_t topk_ids, topk_w, count, offset, sorted_entry;
@@ -128,7 +133,7 @@ moe_status moe_plan_layout(const moe_plan* plan, moe_ws_layout* out);
 moe_status moe_plan_set_workspace(moe_plan* plan, void* workspace, size_t bytes, void* stream);
 
 /* Bytes of the device buffer moe_plan_set_shared packs the shared expert's
- * weights into: 9 * shared_I * H (0 for a plan without a shared expert). */
+ * weights into: 12 * shared_I * H (0 for a plan without a shared expert). */
 size_t moe_plan_shared_pack_bytes(const moe_plan* plan);
 
 /* Bind the block-FP8 shared expert (required iff shape.shared_I > 0; "IQ2R:
@@ -141,7 +146,9 @@ size_t moe_plan_shared_pack_bytes(const moe_plan* plan);
  * moe_plan_shared_pack_bytes(plan) bytes, not overlapping the inputs; the
  * call enqueues on `stream` the one-time rewrite of ws13 and ws2 into it
  * (each E4M3 value as three int8 digits of its value times 2^9, the
- * operands of the exact int8-MFMA GEMMs; nothing is rounded). The plan
+ * operands of the exact int8-MFMA GEMMs; nothing is rounded), followed by
+ * a copy of the E4M3 codes themselves (read by calls that run the shared
+ * expert inside the routed launches). The plan
  * keeps `packed`, ss13 and ss2 (not copied: they must stay valid while the
  * plan is used); ws13 and ws2 are read only by the enqueued rewrite.
  * MOE_ERR_INVALID_ARG for null or misaligned pointers, a plan without a

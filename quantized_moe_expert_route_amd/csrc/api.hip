@@ -87,6 +87,7 @@ Layout make_layout(const moe_shape& s) {
     r.L.sh_hq = take(3 * M128 * Is);
     r.L.sh_hs = take(4 * M * (Is / 128));
     r.L.sh_y = take(4 * M * H);
+    r.X.sh_part = take(8 * std::min<size_t>(M, kSmallM) * (H / 128) * 2 * Is);
   }
   r.L.total_bytes = align256(off);
   return r;
@@ -190,7 +191,8 @@ hipError_t enqueue_call(const moe_plan* plan, const CallArgs& a) {
   if (e == hipSuccess) e = tiles16 ? launch_gate_up(plan, a, ev[2]) : launch_gate_up_big(plan, a, ev[2]);
   if (e == hipSuccess)
     e = mx ? launch_act_quant_mx(plan, a, ev[3]) : tiles16 ? launch_act_quant(plan, a, ev[3]) : none(3);
-  if (e == hipSuccess) e = plan->s.shared_I > 0 ? launch_shared(plan, a, ev[4]) : none(4);
+  // (a fused shared expert runs inside the routed launches: no pass of its own)
+  if (e == hipSuccess) e = plan->s.shared_I > 0 && !shared_fused(plan, M) ? launch_shared(plan, a, ev[4]) : none(4);
   if (e == hipSuccess)
     e = mx ? launch_down_fp4(plan, a, ev[5]) : small ? launch_down_combine(plan, a, ev[5]) : launch_down_big(plan, a, ev[5]);
   if (plan->tpx.tp > 0) {
@@ -260,7 +262,7 @@ int moe_plan_stage_launches(const moe_plan* plan, int64_t M, int stage) {
     case 1: return small ? 0 : mid_path(M, plan->s.top_k) ? 1 : 3;  // align
     case 2: return 1;                             // gate_up (+ mid quantization when large)
     case 3: return mid_path(M, plan->s.top_k) ? 1 : 0;  // act_quant (inside gate/up above kMidM)
-    case 4: return plan->s.shared_I > 0 ? (small ? 4 : 3) : 0;  // shared expert
+    case 4: return plan->s.shared_I > 0 && !shared_fused(plan, M) ? (small ? 4 : 3) : 0;  // shared expert (0: inside the routed launches)
     case 5: return 1;                             // down (+ combine when small, E4M3 mid)
     default: return (small && !mx ? 0 : 1) + (plan->tpx.tp > 0 ? 1 : 0);  // combine (+ the exchange)
   }
@@ -337,7 +339,8 @@ moe_status moe_plan_set_workspace(moe_plan* plan, void* workspace, size_t bytes,
 
 size_t moe_plan_shared_pack_bytes(const moe_plan* plan) {
   if (!plan || plan->s.shared_I == 0) return 0;
-  return (size_t)9 * (size_t)plan->s.shared_I * (size_t)plan->s.H;  // three digit planes of 3 Is x H values
+  // three digit planes of the 3 Is x H values, then the values' E4M3 codes
+  return (size_t)12 * (size_t)plan->s.shared_I * (size_t)plan->s.H;
 }
 
 moe_status moe_plan_set_shared(moe_plan* plan, const void* ws13, const float* ss13, const void* ws2,

@@ -15,6 +15,7 @@
 // runs inside the down launch; above, y goes through HBM to its own launch.
 #include "common.h"
 #include "internal.h"
+#include "shared_small.h"
 
 #include <algorithm>
 #include <type_traits>
@@ -84,7 +85,7 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
     const uint8_t* __restrict__ midq, const float* __restrict__ mids, const uint8_t* __restrict__ w2, const uint8_t* __restrict__ s2, const int* __restrict__ sorted_entry,
     const int4* __restrict__ tiles, const int* __restrict__ meta, int H, int k, int M, int cw,
     const float* __restrict__ topk_w, const float* __restrict__ ys, uint16_t* __restrict__ out,
-    double* __restrict__ partial) {
+    double* __restrict__ partial, SharedSmall sh) {
   constexpr int I = NB * 128;
   constexpr bool A16 = ST == 8;  // mid staged widened to bf16 (else E4M3, widened at each read)
   constexpr int LDA = (A16 ? 2 : 1) * I + kDcPad;  // bytes per staged mid row; the pad spreads 16 rows over the banks
@@ -299,6 +300,15 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
     }
   }
   __syncthreads();
+  // the block-FP8 shared expert's down for this workgroup's columns (run
+  // inside the small-token launches), in the LDS after the slot results
+  // (the staged mid rows there are no longer read)
+  float* ysl = nullptr;
+  if (sh.hq) {
+    uint8_t* shl = dyn + (((size_t)(n + 1) * 16 * 4 + 15) & ~(size_t)15);
+    ysl = reinterpret_cast<float*>(shl + shared_down_lds(sh.Is) - 16 * 16 * 4);
+    shared_down_cols(sh, M, c0, cw, shl, ysl);
+  }
   // out[t, c0 + 2p .. + 2): float64 products and sum in slot order (+ shared), one bf16 rounding
   const int pairs = cw >> 1;
   for (int idx = tid; idx < M * pairs; idx += kDcThreads) {
@@ -310,7 +320,10 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
       a0 += wj * (double)py[0];
       a1 += wj * (double)py[1];
     }
-    if (ys) {
+    if (ysl) {
+      a0 += (double)ysl[t * 16 + cc];
+      a1 += (double)ysl[t * 16 + cc + 1];
+    } else if (ys) {
       a0 += (double)ys[(size_t)t * H + c0 + cc];
       a1 += (double)ys[(size_t)t * H + c0 + cc + 1];
     }
@@ -376,16 +389,18 @@ hipError_t launch_down_combine(const moe_plan* p, const CallArgs& a, Ev ev) {
   if (n > kSmallRows) return hipErrorInvalidValue;
   const bool mid_lds = n * I <= kDcMidBytesMax && n * (I / 128) <= 2 * kDcThreads && n <= 2 * kDcThreads;
   const bool wide = n * I > kDcMidBytes;  // 12 staging registers a thread instead of 8
-  const size_t lds = down_combine_lds_bytes(n, I, mid_lds, mid_lds && !wide);
+  const SharedSmall sh = shared_small(p, a.M);  // the shared expert inside this launch, or none
+  size_t lds = down_combine_lds_bytes(n, I, mid_lds, mid_lds && !wide);
+  if (sh.hq) lds = std::max(lds, (((size_t)(n + 1) * 16 * 4 + 15) & ~(size_t)15) + shared_down_lds(sh.Is));
   if (lds > 160 * 1024) return hipErrorInvalidValue;
-  const float* ys = p->s.shared_I > 0 ? wsp<float>(p, p->L.sh_y) : nullptr;
+  const float* ys = p->s.shared_I > 0 && !sh.hq ? wsp<float>(p, p->L.sh_y) : nullptr;
   const int cw = down_combine_cols(H, p->num_cus);
   auto go = [&](auto kern) {
     return launch_k(kern, dim3(H / cw), dim3(kDcThreads), lds, a.stream, ev, wsp<uint8_t>(p, p->L.midq),
                     wsp<float>(p, p->L.mids), reinterpret_cast<const uint8_t*>(a.w2),
                     reinterpret_cast<const uint8_t*>(a.s2), wsp<int>(p, p->L.sorted_entry), wsp<int4>(p, p->X.tiles),
                     wsp<int>(p, p->X.meta), H, (int)p->s.top_k, (int)a.M, cw, wsp<float>(p, p->L.topk_w), ys,
-                    reinterpret_cast<uint16_t*>(a.out), tp_own_partial(p));
+                    reinterpret_cast<uint16_t*>(a.out), tp_own_partial(p), sh);
   };
   // weights of D tiles in flight per wave; fewer when the slots also carry mid rows
   switch (I / 128) {

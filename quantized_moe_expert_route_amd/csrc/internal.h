@@ -27,6 +27,7 @@ struct Internal {
   size_t pw;       // int2 [E, ceil(M/32)]: {set bits of row e before word w, word w}
   size_t h;        // fp32 [n, I]: SiLU(gate)*up, rows in sorted order
   size_t sh_h;     // fp32 [M, Is]
+  size_t sh_part;  // float64 [min(M, kSmallM), H/128, 2 Is]: block partials of the fused shared gate/up
   size_t sync_begin, sync_bytes;  // region zeroed once when the workspace is bound
 };
 
@@ -85,6 +86,10 @@ inline bool small_path(int64_t M, int64_t k) { return M <= kSmallM && M * k <= k
 // chip idle.
 constexpr int kMidM = 256;
 inline bool mid_path(int64_t M, int64_t k) { return M <= kMidM && k <= 16; }
+// Up to kSmallM tokens with the E4M3 mid, a block-FP8 shared expert of at
+// most kSmallSharedI columns runs inside the routed launches
+// (shared_small.h) instead of a pass of its own.
+constexpr int kSmallSharedI = 512;
 
 struct CallArgs {
   int64_t M;
@@ -119,8 +124,13 @@ hipError_t launch_act_quant(const moe_plan* p, const CallArgs& a, Ev ev);
 int down_combine_cols(int H, int cus);
 hipError_t launch_down_combine(const moe_plan* p, const CallArgs& a, Ev ev);
 hipError_t launch_shared(const moe_plan* p, const CallArgs& a, Ev ev);
+inline bool shared_fused(const moe_plan* p, int64_t M) {
+  return p->s.shared_I > 0 && p->s.shared_I <= kSmallSharedI && p->mid_fmt == MOE_MID_E4M3 &&
+         small_path(M, p->s.top_k);
+}
 // row-major E4M3 shared-expert weights -> digit rows: gate/up [2 Is, H/128,
-// 3, 128], then down [H, Is/128, 3, 128], at `packed` (shared.hip)
+// 3, 128], then down [H, Is/128, 3, 128], then the E4M3 codes themselves
+// (gate/up [2 Is, H], down [H, Is]), at `packed` (shared.hip)
 hipError_t launch_pack_shared(const void* ws13, const void* ws2, int64_t Is, int64_t H, void* packed,
                               hipStream_t stream);
 // large M: LDS-staged tiles (kGuRows rows for gate/up, which includes the mid

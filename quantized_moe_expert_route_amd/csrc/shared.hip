@@ -350,8 +350,14 @@ hipError_t launch_pack_shared(const void* ws13, const void* ws2, int64_t Is, int
   hipError_t e = launch_k(sh_pack_kernel, dim3(blocks(2 * Is * H / 16)), dim3(256), 0, stream, Ev{},
                           reinterpret_cast<const uint8_t*>(ws13), 2 * Is, (int)H, p13);
   if (e != hipSuccess) return e;
-  return launch_k(sh_pack_kernel, dim3(blocks(H * Is / 16)), dim3(256), 0, stream, Ev{},
-                  reinterpret_cast<const uint8_t*>(ws2), H, (int)Is, p2);
+  e = launch_k(sh_pack_kernel, dim3(blocks(H * Is / 16)), dim3(256), 0, stream, Ev{},
+               reinterpret_cast<const uint8_t*>(ws2), H, (int)Is, p2);
+  if (e != hipSuccess) return e;
+  // the E4M3 codes as given, for the shared expert inside the small-token launches
+  uint8_t* c13 = p13 + 9 * Is * H;
+  e = hipMemcpyAsync(c13, ws13, (size_t)(2 * Is * H), hipMemcpyDeviceToDevice, stream);
+  if (e != hipSuccess) return e;
+  return hipMemcpyAsync(c13 + 2 * Is * H, ws2, (size_t)(H * Is), hipMemcpyDeviceToDevice, stream);
 }
 
 hipError_t launch_shared(const moe_plan* p, const CallArgs& a, Ev ev) {

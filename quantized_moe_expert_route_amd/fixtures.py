@@ -94,6 +94,12 @@ WORKLOADS["t4_m16_hot"] = Workload("t4_m16_hot", Shape(M=16, H=6144, E=256, I=51
 WORKLOADS["c1s"] = Workload("c1s", Shape(M=4, H=6144, E=257, I=256, top_k=9), "uniform", 1, True)
 WORKLOADS["c2s"] = Workload("c2s", Shape(M=16, H=6144, E=257, I=256, top_k=9), "correlated", 2, True)
 
+# c1 and c2 with the block-FP8 shared expert at its TP8 share (I 256 of the
+# 512 it has at TP4 in c4): up to 16 tokens it runs inside the routed
+# launches, as the pages' fused decode does.
+WORKLOADS["c1b"] = Workload("c1b", Shape(M=4, H=6144, E=256, I=256, top_k=8, shared_I=256), "uniform", 1)
+WORKLOADS["c2b"] = Workload("c2b", Shape(M=16, H=6144, E=256, I=256, top_k=8, shared_I=256), "correlated", 2)
+
 WORKLOAD_TITLES = {
     "c0": "tiny H512 E16 top2 I128 M4",
     "c1": "TP8-rank decode H6144 E256 top8 I256 M4, MXFP4 experts, uniform logits",
@@ -103,6 +109,8 @@ WORKLOAD_TITLES = {
     "t4_m16_hot": "TP4-rank batch H6144 E256 top8 I512 M16, hot routing (every token on the same 8 experts)",
     "c1s": "TP8-rank decode H6144 E256+1 top9 I256 M4, shared expert fused as expert 256 (slot 9), uniform logits",
     "c2s": "TP8-rank verify H6144 E256+1 top9 I256 M16, shared expert fused as expert 256 (slot 9), correlated rows",
+    "c1b": "TP8-rank decode H6144 E256 top8 I256 M4 + block-FP8 shared expert I256 inside the routed launches",
+    "c2b": "TP8-rank verify H6144 E256 top8 I256 M16 + block-FP8 shared expert I256 inside the routed launches",
 }
 for _name, _wl in WORKLOADS.items():
     if _name not in WORKLOAD_TITLES:

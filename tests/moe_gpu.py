@@ -70,18 +70,31 @@ def read_intermediates(plan, s, M):
         "mids": v("mids", torch.float32, (n, I // 128)),
         "y": v("y", torch.float32, (n, H)),
     }
+    fused = shared_fused(s, M)
     if s.shared_I:
         Is = s.shared_I
-        r["sh_xq"] = v("sh_xq", torch.int8, (M, H // 128, 3, 128))
+        if fused:  # inside the small-token launches: E4M3 codes, no sh_y
+            r["sh_xq"] = v("sh_xq", torch.uint8, (M, H))
+            r["sh_hq"] = v("sh_hq", torch.uint8, (M, Is))
+        else:
+            r["sh_xq"] = v("sh_xq", torch.int8, (M, H // 128, 3, 128))
+            r["sh_hq"] = v("sh_hq", torch.int8, (M, Is // 128, 3, 128))
+            r["sh_y"] = v("sh_y", torch.float32, (M, H))
         r["sh_xs"] = v("sh_xs", torch.float32, (H // 128, M)).t()  # stored K-block major
-        r["sh_hq"] = v("sh_hq", torch.int8, (M, Is // 128, 3, 128))
         r["sh_hs"] = v("sh_hs", torch.float32, (Is // 128, M)).t()
-        r["sh_y"] = v("sh_y", torch.float32, (M, H))
     out = {key: t.cpu().numpy() for key, t in r.items()}
-    for key in ("sh_xq", "sh_hq"):
-        if key in out:
-            out[key] = digit_rows_to_codes(out[key])
+    if not fused:
+        for key in ("sh_xq", "sh_hq"):
+            if key in out:
+                out[key] = digit_rows_to_codes(out[key])
     return out
+
+
+def shared_fused(s, M, mid_format="e4m3"):
+    """Whether a call of M tokens runs the block-FP8 shared expert inside the
+    small-token launches (the library's rule: up to 16 tokens and 512 slots,
+    the E4M3 mid, shared_I up to 512)."""
+    return bool(s.shared_I) and s.shared_I <= 512 and M <= 16 and M * s.top_k <= 512 and mid_format == "e4m3"
 
 
 def digit_rows_to_codes(d):

@@ -155,7 +155,11 @@ SMALL = [
     (9, 512, 8, 384, 8, "ties", 0),            # k = E, many ties, I = 384
     (33, 512, 64, 128, 8, "ties", 0),          # ties and signed zeros
     (40, 1024, 32, 256, 4, "zipf", 0),         # skew: one expert takes most tokens
-    (3, 512, 4, 128, 2, "normal", 128),        # shared expert
+    (3, 512, 4, 128, 2, "normal", 128),        # shared expert (inside the small-token launches)
+    (1, 512, 4, 128, 2, "normal", 512),        # one token, the widest fused shared expert
+    (16, 1536, 16, 256, 8, "ties", 384),       # 16 tokens with a fused shared expert
+    (12, 65536, 4, 128, 2, "normal", 128),     # fused shared expert at the largest H
+    (5, 512, 8, 128, 2, "normal", 640),        # a shared expert too wide to fuse: its own pass
     # above 16 tokens: the large path's routing and sort; up to 256 tokens gate/up on
     # 16-row tiles with its own mid quantization, above on 64-row tiles with it inside
     (17, 512, 16, 128, 2, "normal", 0),        # one token past the small path; ragged tiles
@@ -185,7 +189,40 @@ def test_small_shapes(M, H, E, I, k, kind, Is):
     _check_mid(gi["midq"], gi["mids"], ref["midq"], ref["mids"])
     if Is:
         _check_shared_x(gi, ref)
+        _check_shared_mid(gi, ref)
     _check_out(gout, ref["out"])
+
+
+def _check_shared_mid(gi, ref, tokens=None):
+    """The shared expert's E4M3 mid codes and per-128 scales: bit-exact."""
+    q, s = gi["sh_hq"], gi["sh_hs"]
+    if tokens is not None:
+        q, s = q[tokens], s[tokens]
+    np.testing.assert_array_equal(F.e4m3_decode(q), F.e4m3_decode(ref["shared"]["hq"]))
+    np.testing.assert_array_equal(s.view(np.uint32), ref["shared"]["hs"].view(np.uint32))
+
+
+@pytest.mark.parametrize("name", ["c1b", "c2b"])
+def test_fused_shared_expert(name):
+    """Up to 16 tokens the block-FP8 shared expert runs inside the routed
+    launches (its stage launches nothing of its own): its x codes and scales,
+    its mid codes and scales and the output equal the oracle bit for bit."""
+    d = X.make_inputs(name)
+    s = d["shape"]
+    g = upload(d)
+    plan = make_plan(s)
+    plan.set_shared(g["ws13"], g["ss13"], g["ws2"], g["ss2"])
+    launches = plan.stage_launches(s.M)
+    assert launches[4] == 0 and launches == [1, 0, 1, 1, 0, 1, 0]
+    gout, gi = run(d, plan=plan, g=g)
+    ref = oracle(d)
+    _check_routing(gi, ref["ids"], ref["w"], ref["count"], ref["offset"], ref["sorted_entry"])
+    _check_xq(gi, ref)
+    _check_mid(gi["midq"], gi["mids"], ref["midq"], ref["mids"])
+    _check_shared_x(gi, ref)
+    _check_shared_mid(gi, ref)
+    ndiff = _check_out(gout, ref["out"])
+    assert ndiff == 0, "expected the oracle's bf16 output exactly"
 
 
 def test_shared_x_codes_on_exact_midpoints():
@@ -291,7 +328,8 @@ def test_run_to_run_bitwise():
     assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("name,mxfp4", [("c1", False), ("m64_mixed", False), ("c3", False), ("m256_hot", True)])
+@pytest.mark.parametrize("name,mxfp4", [("c1", False), ("c1b", False), ("m64_mixed", False), ("c3", False),
+                                        ("m256_hot", True)])
 def test_graph_replay_matches_eager(name, mxfp4):
     """Replays of a captured call (small, mid-range and large paths; the
     MXFP4 mid) equal the eager call bitwise, with eager calls between them:
@@ -304,6 +342,8 @@ def test_graph_replay_matches_eager(name, mxfp4):
     s = d["shape"]
     g = upload(d)
     plan = make_plan(s)
+    if s.shared_I:
+        plan.set_shared(g["ws13"], g["ss13"], g["ws2"], g["ss2"])
     w2, s2 = g["w2"], g["s2"]
     if mxfp4:
         plan.set_mid_format(MID_MXFP4)
