@@ -80,7 +80,9 @@ size_t down_combine_lds_bytes(int64_t n, int64_t I, bool mid_lds, bool mid_bf16)
   return b;
 }
 
-template <int NB, int D, bool MID_LDS, int ST = 8>
+// SH: the block-FP8 shared expert runs inside this launch (its own
+// instantiations, so that the routed-only ones carry none of its registers)
+template <int NB, int D, bool MID_LDS, int ST = 8, bool SH = false>
 __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
     const uint8_t* __restrict__ midq, const float* __restrict__ mids, const uint8_t* __restrict__ w2, const uint8_t* __restrict__ s2, const int* __restrict__ sorted_entry,
     const int4* __restrict__ tiles, const int* __restrict__ meta, int H, int k, int M, int cw,
@@ -111,6 +113,10 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
   // same values to the same places); a wave without tiles loads tile 0 and
   // computes nothing. The loads are unconditional so that every later wait
   // counts exactly.
+  // the fused shared expert's down operands come first, so they have landed
+  // by the end of the ring
+  SharedDownPre sdp;
+  if (SH) shared_down_fetch(sh, M, c0, cw, sdp);
   int4 T[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) T[d] = tiles[my > 0 ? base + min(d, my - 1) : 0];
@@ -304,10 +310,10 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
   // inside the small-token launches), in the LDS after the slot results
   // (the staged mid rows there are no longer read)
   float* ysl = nullptr;
-  if (sh.hq) {
+  if (SH) {
     uint8_t* shl = dyn + (((size_t)(n + 1) * 16 * 4 + 15) & ~(size_t)15);
     ysl = reinterpret_cast<float*>(shl + shared_down_lds(sh.Is) - 16 * 16 * 4);
-    shared_down_cols(sh, M, c0, cw, shl, ysl);
+    shared_down_cols(sh, M, c0, cw, sdp, shl, ysl);
   }
   // out[t, c0 + 2p .. + 2): float64 products and sum in slot order (+ shared), one bf16 rounding
   const int pairs = cw >> 1;
@@ -403,17 +409,21 @@ hipError_t launch_down_combine(const moe_plan* p, const CallArgs& a, Ev ev) {
                     reinterpret_cast<uint16_t*>(a.out), tp_own_partial(p), sh);
   };
   // weights of D tiles in flight per wave; fewer when the slots also carry mid rows
-  switch (I / 128) {
-    case 1: return !mid_lds ? go(down_combine_kernel<1, 6, false>)
-                   : wide   ? go(down_combine_kernel<1, 8, true, 12>) : go(down_combine_kernel<1, 8, true>);
-    case 2: return !mid_lds ? go(down_combine_kernel<2, 3, false>)
-                   : wide   ? go(down_combine_kernel<2, 8, true, 12>) : go(down_combine_kernel<2, 8, true>);
-    case 3: return !mid_lds ? go(down_combine_kernel<3, 2, false>)
-                   : wide   ? go(down_combine_kernel<3, 5, true, 12>) : go(down_combine_kernel<3, 5, true>);
-    case 4: return !mid_lds ? go(down_combine_kernel<4, 2, false>)
-                   : wide   ? go(down_combine_kernel<4, 4, true, 12>) : go(down_combine_kernel<4, 4, true>);
-    default: return hipErrorInvalidValue;
-  }
+  auto pick = [&](auto shc) {
+    constexpr bool S = decltype(shc)::value;
+    switch (I / 128) {
+      case 1: return !mid_lds ? go(down_combine_kernel<1, 6, false, 8, S>)
+                     : wide   ? go(down_combine_kernel<1, 8, true, 12, S>) : go(down_combine_kernel<1, 8, true, 8, S>);
+      case 2: return !mid_lds ? go(down_combine_kernel<2, 3, false, 8, S>)
+                     : wide   ? go(down_combine_kernel<2, 8, true, 12, S>) : go(down_combine_kernel<2, 8, true, 8, S>);
+      case 3: return !mid_lds ? go(down_combine_kernel<3, 2, false, 8, S>)
+                     : wide   ? go(down_combine_kernel<3, 5, true, 12, S>) : go(down_combine_kernel<3, 5, true, 8, S>);
+      case 4: return !mid_lds ? go(down_combine_kernel<4, 2, false, 8, S>)
+                     : wide   ? go(down_combine_kernel<4, 4, true, 12, S>) : go(down_combine_kernel<4, 4, true, 8, S>);
+      default: return hipErrorInvalidValue;
+    }
+  };
+  return sh.hq ? pick(std::true_type()) : pick(std::false_type());
 }
 
 hipError_t launch_combine(const moe_plan* p, const CallArgs& a, Ev ev) {

@@ -51,16 +51,8 @@ __global__ __launch_bounds__(256) void gate_up_m16_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const uint8_t* __restrict__ w13p,
     const uint8_t* __restrict__ s13p, const int* __restrict__ sorted_entry,
     const int4* __restrict__ tiles, const int* __restrict__ meta, float* __restrict__ hout, int H,
-    int I, int k, int routed_blocks, SharedSmall sh, int M, int sh_items) {
+    int I, int k) {
   __shared__ v4f red[2][4][64];
-  if ((int)blockIdx.x >= routed_blocks) {
-    // the block-FP8 shared expert's gate/up partials (workgroups after the
-    // routed ones; the x slice of an item in dynamic LDS)
-    extern __shared__ __align__(16) uint8_t sh_lds[];
-    for (int it = (int)blockIdx.x - routed_blocks; it < sh_items; it += (int)gridDim.x - routed_blocks)
-      shared_gate_up_item(sh, it, M, H, sh_lds);
-    return;
-  }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4;
   const int n_it = I / 16;
@@ -68,7 +60,7 @@ __global__ __launch_bounds__(256) void gate_up_m16_kernel(
   const size_t Hb = (size_t)H / 2, Hs = (size_t)H / 32;
   const int nss = H / 512, nks = H / 128;
   const size_t nrb = (size_t)I / 8;  // 16-row blocks of an expert's 2I rows
-  for (int w = blockIdx.x; w < n_work; w += routed_blocks) {
+  for (int w = blockIdx.x; w < n_work; w += gridDim.x) {
     const int4 tl = tiles[w / n_it];
     const int it = w % n_it;
     const int e = tl.x, r0 = tl.y, r1 = tl.z;
@@ -132,24 +124,24 @@ __global__ __launch_bounds__(256) void gate_up_m16_kernel(
 }
 
 // One wave per (row, 128-block): s = fl32(amax / 448), q = E4M3(fl32(h / s)).
-// With the shared expert inside the small-token launches, the waves after
-// the routed ones form its h from the gate/up partials and quantize it
-// (one wave per token and 128-block).
+// With the shared expert inside the small-token launches, the workgroups
+// after the routed ones form its h from the gate/up partials and quantize
+// it (one workgroup per token and 128-block).
 __global__ __launch_bounds__(256) void act_quant_kernel(const float* __restrict__ h, int rows, int I,
                                                         uint8_t* __restrict__ q, float* __restrict__ s,
-                                                        SharedSmall sh, int M, int H) {
+                                                        int routed_blocks, SharedSmall sh, int M, int H) {
+  if ((int)blockIdx.x >= routed_blocks) {
+    __shared__ float u_lds[130];
+    const int snb = sh.Is / 128;
+    for (int sb = (int)blockIdx.x - routed_blocks; sb < M * snb; sb += (int)gridDim.x - routed_blocks)
+      shared_mid_block(sh, sb / snb, sb % snb, M, H, u_lds);
+    return;
+  }
   const int nb = I / 128;
-  const int routed = rows * nb;
-  const int snb = sh.part ? sh.Is / 128 : 0;
-  const int total = routed + M * snb;
-  for (int wv = blockIdx.x * 4 + (threadIdx.x >> 6); wv < total; wv += gridDim.x * 4) {
-    if (wv < routed) {
-      const int row = wv / nb, b = wv % nb;
-      quant_mid_rows(h, row, row + 1, 1, I, b, q, s);
-    } else {
-      const int sw = wv - routed, m = sw / snb;
-      shared_mid_wave(sh, m, sw - m * snb, M, H);
-    }
+  const int total = rows * nb;
+  for (int wv = blockIdx.x * 4 + (threadIdx.x >> 6); wv < total; wv += routed_blocks * 4) {
+    const int row = wv / nb, b = wv % nb;
+    quant_mid_rows(h, row, row + 1, 1, I, b, q, s);
   }
 }
 
@@ -159,26 +151,22 @@ hipError_t launch_gate_up(const moe_plan* p, const CallArgs& a, Ev ev) {
   const int64_t t16 = (n + std::min<int64_t>(p->s.E, n) * (kTileRows - 1) + kTileRows - 1) / kTileRows;
   const int64_t work_max = t16 * (I / 16);
   const int blocks = (int)std::min<int64_t>(work_max, 2048);
-  // the fused shared expert's items: 16 outputs x 2 K-blocks each
-  const SharedSmall sh = shared_small(p, a.M);
-  const int sh_items = sh.part ? (sh.Is / kSsOut) * (int)(p->s.H / 128 / kSsKb) : 0;
-  const int sh_blocks = std::min(sh_items, 1024);
-  const size_t lds = sh.part ? shared_gate_up_lds((int)a.M) : 0;
-  return launch_k(gate_up_m16_kernel, dim3(blocks + sh_blocks), dim3(256), lds, a.stream, ev,
-                  wsp<uint8_t>(p, p->L.xq), wsp<uint8_t>(p, p->L.xs), reinterpret_cast<const uint8_t*>(a.w13),
+  return launch_k(gate_up_m16_kernel, dim3(blocks), dim3(256), 0, a.stream, ev, wsp<uint8_t>(p, p->L.xq),
+                  wsp<uint8_t>(p, p->L.xs), reinterpret_cast<const uint8_t*>(a.w13),
                   reinterpret_cast<const uint8_t*>(a.s13), wsp<int>(p, p->L.sorted_entry), wsp<int4>(p, p->X.tiles),
-                  wsp<int>(p, p->X.meta), wsp<float>(p, p->X.h), (int)p->s.H, I, (int)p->s.top_k, blocks, sh,
-                  (int)a.M, sh_items);
+                  wsp<int>(p, p->X.meta), wsp<float>(p, p->X.h), (int)p->s.H, I, (int)p->s.top_k);
 }
 
 hipError_t launch_act_quant(const moe_plan* p, const CallArgs& a, Ev ev) {
   const int rows = (int)(a.M * p->s.top_k);
   const int I = (int)p->s.I;
-  const SharedSmall sh = shared_small(p, a.M);
-  const int64_t waves = (int64_t)rows * (I / 128) + (sh.part ? a.M * (sh.Is / 128) : 0);
-  const int blocks = (int)std::min<int64_t>((waves + 3) / 4, 8192);
-  return launch_k(act_quant_kernel, dim3(blocks), dim3(256), 0, a.stream, ev, wsp<float>(p, p->X.h), rows, I,
-                  wsp<uint8_t>(p, p->L.midq), wsp<float>(p, p->L.mids), sh, (int)a.M, (int)p->s.H);
+  const SharedSmall sh = shared_small(p, a.M);  // the fused shared expert's h: a workgroup per 128-block
+  const int64_t waves = (int64_t)rows * (I / 128);
+  const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>((waves + 3) / 4, 8192));
+  const int sh_blocks = sh.part ? (int)(a.M * (sh.Is / 128)) : 0;
+  return launch_k(act_quant_kernel, dim3(blocks + sh_blocks), dim3(256), 0, a.stream, ev, wsp<float>(p, p->X.h),
+                  rows, I, wsp<uint8_t>(p, p->L.midq), wsp<float>(p, p->L.mids), blocks, sh, (int)a.M,
+                  (int)p->s.H);
 }
 
 }  // namespace qmoe

@@ -24,6 +24,7 @@
 // global memory and a one-workgroup align launch ranks the entries.
 #include "common.h"
 #include "internal.h"
+#include "shared_small.h"
 
 #include <algorithm>
 
@@ -195,7 +196,7 @@ __global__ __launch_bounds__(1024) void route_align_small_kernel(
     const float* __restrict__ logits, const uint16_t* __restrict__ x, int M, int E, int k, int H, float scaling,
     int* __restrict__ topk_ids, float* __restrict__ topk_w, int* __restrict__ count, int* __restrict__ offset,
     int* __restrict__ sorted_entry, int4* __restrict__ tiles, int* __restrict__ meta, uint8_t* __restrict__ xq,
-    uint8_t* __restrict__ xs, int shared_slot, uint8_t* __restrict__ sh_x8, float* __restrict__ sh_xs) {
+    uint8_t* __restrict__ xs, int shared_slot, SharedSmall sh) {
   __shared__ uint32_t s_mask[1024][2];  // expert -> tokens 0..63
   __shared__ int s_ids[64 * 16];
   __shared__ int s_off[1024];
@@ -203,25 +204,12 @@ __global__ __launch_bounds__(1024) void route_align_small_kernel(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int xq_groups = (M * (H >> 5) + 63) >> 6;
   if ((int)blockIdx.x > xq_groups) {
-    // the block-FP8 shared expert's x (run inside the small-token launches):
-    // one wave per 128-block, s = fl32(amax / 448), codes E4M3(fl32(x / s)),
-    // scales K-block major
-    const int nb = H >> 7;
-    const int wv = ((int)blockIdx.x - 1 - xq_groups) * 16 + wave;
-    if (wv < M * nb) {
-      const int t = wv / nb, b = wv - t * nb;
-      const uint32_t pair = *reinterpret_cast<const uint32_t*>(x + (size_t)t * H + b * 128 + 2 * lane);
-      const float v0 = __uint_as_float(pair << 16), v1 = __uint_as_float(pair & 0xFFFF0000u);
-      const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
-      const float sc = __fdiv_rn(amax, 448.0f);
-      uint32_t c0 = 0, c1 = 0;
-      if (sc > 0.f) {
-        c0 = e4m3_code(__fdiv_rn(v0, sc));
-        c1 = e4m3_code(__fdiv_rn(v1, sc));
-      }
-      *reinterpret_cast<uint16_t*>(sh_x8 + (size_t)t * H + b * 128 + 2 * lane) = (uint16_t)(c0 | (c1 << 8));
-      if (lane == 0) sh_xs[(size_t)b * M + t] = sc;
-    }
+    // the block-FP8 shared expert's gate/up partials (run inside the
+    // small-token launches, beside the routing workgroup)
+    extern __shared__ __align__(16) uint8_t sh_lds[];
+    const int items = (sh.Is / kSsOut) * (H / 128 / sh.kb);
+    const int first = (int)blockIdx.x - 1 - xq_groups, stride = (int)gridDim.x - 1 - xq_groups;
+    for (int it = first; it < items; it += stride) shared_gate_up_item<2>(sh, x, it, M, H, sh_lds);
     return;
   }
   if (blockIdx.x > 0) {
@@ -552,18 +540,22 @@ static hipError_t by_ec(int E, F&& f) {
 hipError_t launch_route_small(const moe_plan* p, const CallArgs& a, Ev ev) {
   const int M = (int)a.M, E = (int)p->s.E, k = (int)p->s.top_k, H = (int)p->s.H;
   const int xq_groups = (int)((a.M * (H / 32) + 63) / 64);
-  // with the shared expert inside the small-token launches: its x, one wave per 128-block
-  const bool shx = shared_fused(p, a.M);
-  const int sh_groups = shx ? (int)((a.M * (H / 128) + 15) / 16) : 0;
+  // with the shared expert inside the small-token launches: its gate/up
+  // items on the workgroups the routing leaves free (two per CU)
+  // (one 1024-thread workgroup of this kernel per CU)
+  const SharedSmall sh = shared_small(p, a.M);
+  const int free_cus = std::max(1, p->num_cus - 1 - xq_groups);
+  const int sh_items = sh.part ? (sh.Is / kSsOut) * (H / 128 / sh.kb) : 0;
+  const int sh_groups = std::min(sh_items, free_cus);
+  const size_t lds = sh.part ? shared_gate_up_lds(sh.kb) : 0;
   return by_ec(E, [&](auto ec) {
-    return launch_k(route_align_small_kernel<decltype(ec)::value>, dim3(1 + xq_groups + sh_groups), dim3(1024), 0,
+    return launch_k(route_align_small_kernel<decltype(ec)::value>, dim3(1 + xq_groups + sh_groups), dim3(1024), lds,
                     a.stream, ev,
                     a.logits,
                     reinterpret_cast<const uint16_t*>(a.x), M, E, k, H, p->s.routed_scaling,
                     wsp<int>(p, p->L.topk_ids), wsp<float>(p, p->L.topk_w), wsp<int>(p, p->L.count),
                     wsp<int>(p, p->L.offset), wsp<int>(p, p->L.sorted_entry), wsp<int4>(p, p->X.tiles),
-                    wsp<int>(p, p->X.meta), wsp<uint8_t>(p, p->L.xq), wsp<uint8_t>(p, p->L.xs), p->shared_slot,
-                    shx ? wsp<uint8_t>(p, p->L.sh_xq) : nullptr, shx ? wsp<float>(p, p->L.sh_xs) : nullptr);
+                    wsp<int>(p, p->X.meta), wsp<uint8_t>(p, p->L.xq), wsp<uint8_t>(p, p->L.xs), p->shared_slot, sh);
   });
 }
 
