@@ -167,8 +167,8 @@ moe_status moe_plan_set_shared(moe_plan* plan, const void* ws13, const float* ss
  * with an E8M0 scale (the rule x takes), down on the scaled FP4 MFMA. With
  * MXFP4, moe_forward's w2 and s2 are the packed ones of moe_pack_w2, the
  * workspace's midq holds [n, I/2] codes (element 2i in the low nibble) and
- * mids [n, I/32] scale bytes, rows in sorted order, y is written for every
- * M, and moe_forward returns MOE_ERR_UNSUPPORTED for M > 256. */
+ * mids [n, I/32] scale bytes, rows in sorted order, and y is written for
+ * every M. */
 typedef enum { MOE_MID_E4M3 = 0, MOE_MID_MXFP4 = 1 } moe_mid_format;
 
 /* Fuse a shared expert as the last expert and the last slot ("[HIP] IQ2R:
@@ -356,8 +356,8 @@ const char* moe_stage_name(int i);
 
 /* Kernels that stage `stage` launches for a call of M tokens on this plan
  * with its current mid format (0 when the stage is folded into another
- * one), or -1 for bad arguments or a call the plan would not serve (M > 256
- * with MOE_MID_MXFP4). */
+ * one), or -1 for bad arguments (M outside [0, the plan's M], an unknown
+ * stage). */
 int moe_plan_stage_launches(const moe_plan* plan, int64_t M, int stage);
 
 /* Static text for a status code. */

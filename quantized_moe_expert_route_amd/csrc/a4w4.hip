@@ -15,16 +15,6 @@ namespace qmoe {
 
 constexpr int kDfCbs = 4;  // column blocks whose weights a wave has in flight
 
-// E8M0 scale byte of a 32-block from the largest |fp32| bit pattern of the
-// block: floor(log2 amax) - 2 + 127, clamped to [0, 254]; 0 for a zero block.
-__device__ __forceinline__ uint32_t mx_scale_code_f32(uint32_t amax_bits) {
-  if (amax_bits == 0) return 0;
-  const int ex = (int)(amax_bits >> 23);
-  const int fl = ex != 0 ? ex - 127 : -149 + (31 - __clz(amax_bits));  // subnormal: mantissa * 2^-149
-  const int c = fl - 2 + 127;
-  return (uint32_t)(c < 0 ? 0 : (c > 254 ? 254 : c));
-}
-
 // A thread quantizes 8 consecutive elements of a row; the 4 lanes of a quad
 // form one 32-block (I/8 is a multiple of 16, so quads never straddle rows
 // and a grid-stride step keeps them whole).

@@ -134,7 +134,6 @@ moe_status check_call(const moe_plan* plan, int64_t M, const void* const ptrs[7]
   if (!(plan->layout & MOE_LAYOUT_W13_PACKED) || mx != ((plan->layout & MOE_LAYOUT_W2_PACKED) != 0))
     return MOE_ERR_UNSUPPORTED;
   if (M == 0) return MOE_OK;
-  if (mx && !mid_path(M, plan->s.top_k)) return MOE_ERR_UNSUPPORTED;
   for (int i = 0; i < 7; ++i)
     if (!ptrs[i] || !aligned16(ptrs[i])) return MOE_ERR_INVALID_ARG;
   for (int i = 0; i < 7; ++i)
@@ -179,8 +178,9 @@ hipError_t enqueue_call(const moe_plan* plan, const CallArgs& a) {
   // gate/up on 16-row tiles and the mid quantization up to kMidM tokens,
   // above on 64-row tiles with the mid quantization inside (every item owns
   // whole mid blocks); down to y in HBM; the combine.
-  // With the MXFP4 mid (up to kMidM tokens): its own quantization and down
-  // kernel on the 16-row tiles, then the combine, for every M.
+  // With the MXFP4 mid: its own quantization (inside the 64-row-tile gate/up
+  // above kMidM) and down kernel on the 16-row tiles, then the combine, for
+  // every M.
   // A stage is never folded into its producer through a last-arriver
   // counter: the device-scope release/acquire that needs writes back and
   // invalidates a whole L2 of an XCD per workgroup and costs more than a
@@ -190,7 +190,7 @@ hipError_t enqueue_call(const moe_plan* plan, const CallArgs& a) {
   const bool tiles16 = mid_path(M, plan->s.top_k);  // 16-row-tile gate/up, mid quantization on its own
   if (e == hipSuccess) e = tiles16 ? launch_gate_up(plan, a, ev[2]) : launch_gate_up_big(plan, a, ev[2]);
   if (e == hipSuccess)
-    e = mx ? launch_act_quant_mx(plan, a, ev[3]) : tiles16 ? launch_act_quant(plan, a, ev[3]) : none(3);
+    e = !tiles16 ? none(3) : mx ? launch_act_quant_mx(plan, a, ev[3]) : launch_act_quant(plan, a, ev[3]);
   // (a fused shared expert runs inside the routed launches: no pass of its own)
   if (e == hipSuccess) e = plan->s.shared_I > 0 && !shared_fused(plan, M) ? launch_shared(plan, a, ev[4]) : none(4);
   if (e == hipSuccess)
@@ -256,9 +256,8 @@ int moe_plan_stage_launches(const moe_plan* plan, int64_t M, int stage) {
   if (M == 0) return 0;
   const bool small = small_path(M, plan->s.top_k);
   const bool mx = plan->mid_fmt == MOE_MID_MXFP4;
-  if (mx && !mid_path(M, plan->s.top_k)) return -1;  // not served
   switch (stage) {
-    case 0: return 1;                             // route + x quantization (+ sort when small; + the shared expert's x when large)
+    case 0: return 1;                             // route + x quantization (+ sort when small; + the shared expert's x when large, its gate/up partials when fused)
     case 1: return small ? 0 : mid_path(M, plan->s.top_k) ? 1 : 3;  // align
     case 2: return 1;                             // gate_up (+ mid quantization when large)
     case 3: return mid_path(M, plan->s.top_k) ? 1 : 0;  // act_quant (inside gate/up above kMidM)

@@ -95,6 +95,16 @@ __device__ __forceinline__ uint32_t mx_scale_code(uint32_t amax_bits16) {
   return (uint32_t)(c < 0 ? 0 : (c > 254 ? 254 : c));
 }
 
+// E8M0 scale byte of a 32-block from the largest |fp32| bit pattern of the
+// block: floor(log2 amax) - 2 + 127, clamped to [0, 254]; 0 for a zero block.
+__device__ __forceinline__ uint32_t mx_scale_code_f32(uint32_t amax_bits) {
+  if (amax_bits == 0) return 0;
+  const int ex = (int)(amax_bits >> 23);
+  const int fl = ex != 0 ? ex - 127 : -149 + (31 - __clz(amax_bits));  // subnormal: mantissa * 2^-149
+  const int c = fl - 2 + 127;
+  return (uint32_t)(c < 0 ? 0 : (c > 254 ? 254 : c));
+}
+
 // ----------------------------------------------------------------- E4M3FN
 // Round |v| to the nearest E4M3 value, ties to the even code, saturating to
 // 448; sign copied from v. Exact: the scalings by powers of two are exact and

@@ -71,6 +71,9 @@ struct alignas(16) GuSmem {  // 16-byte aligned: staging and fragment accesses c
 };
 constexpr int kGuBD = 2;  // K-steps of a wave's weight fragments held in registers (divides 8)
 
+// MX: the mid leaves as MXFP4 (per 32 columns an E8M0 scale and E2M1 codes,
+// the rule x takes), midq [n, I/2], mids bytes [n, I/32]; else E4M3 per 128.
+template <bool MX>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gate_up_big_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const uint8_t* __restrict__ w13,
     const uint8_t* __restrict__ s13, const int* __restrict__ sorted_entry, const int4* __restrict__ items,
@@ -244,10 +247,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
         u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x4E, 0xF, 0xF, false));
         u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x141, 0xF, 0xF, false));
         u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x140, 0xF, 0xF, false));
-        if (re == 0) red[wn][16 * i + 4 * ge + v] = __uint_as_float(u);
+        if (MX) pm[i][v] = __uint_as_float(u);  // the amax of the row's 32 columns of this wave
+        else if (re == 0) red[wn][16 * i + 4 * ge + v] = __uint_as_float(u);
       }
     __syncthreads();  // also: every wave is past its last read of the staging buffers
     uint8_t* qs = reinterpret_cast<uint8_t*>(&sm.a);  // [kGuR][128] codes, in the idle A buffers
+    if (MX) {
+      // a wave's 32 columns are one MX block of each row: scale byte from
+      // the amax's exponent, codes E2M1(h * 2^(127 - s)), one a byte in qs
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int row = 16 * i + 4 * ge + v;
+          const uint32_t sc = mx_scale_code_f32(__float_as_uint(pm[i][v]));
+          const int sh = 127 - (int)sc;
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            qs[row * 128 + 32 * wn + 16 * j + re] = row < rows ? (uint8_t)e2m1_code(ldexpf(hv[i][j][v], sh)) : 0;
+          if (re == 0 && row < rows)
+            reinterpret_cast<uint8_t*>(mids)[(size_t)(r0 + row) * (I / 32) + 4 * ib + wn] = (uint8_t)sc;
+        }
+      __syncthreads();
+      // coalesced copy: kGuR rows x 64 bytes, element 2i in the low nibble
+      {
+        const int row = tid >> 2, c = tid & 3;  // 16 bytes (32 codes) a thread
+        if (row < rows) {
+          const uint4 a = *reinterpret_cast<const uint4*>(&qs[row * 128 + 32 * c]);
+          const uint4 b = *reinterpret_cast<const uint4*>(&qs[row * 128 + 32 * c + 16]);
+          const uint32_t wv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+          uint32_t o[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t w0 = wv[2 * q], w1 = wv[2 * q + 1];
+            o[q] = (w0 & 0xFu) | ((w0 >> 4) & 0xF0u) | ((w0 >> 8) & 0xF00u) | ((w0 >> 12) & 0xF000u) |
+                   ((w1 & 0xFu) << 16) | ((w1 << 12) & 0xF00000u) | ((w1 << 8) & 0xF000000u) | ((w1 << 4) & 0xF0000000u);
+          }
+          *reinterpret_cast<uint4*>(midq + (size_t)(r0 + row) * (I / 2) + 64 * ib + 16 * c) =
+              make_uint4(o[0], o[1], o[2], o[3]);
+        }
+      }
+      __syncthreads();
+      continue;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -524,7 +566,8 @@ hipError_t launch_gate_up_big(const moe_plan* p, const CallArgs& a, Ev ev) {
   const int64_t tiles = (n + std::min<int64_t>(p->s.E, n) * (kGuR - 1) + kGuR - 1) / kGuR;
   const int64_t items = tiles * (p->s.I / 128);
   const int blocks = (int)std::min<int64_t>(items, 512);  // two per CU
-  return launch_k(gate_up_big_kernel, dim3(blocks), dim3(256), 0, a.stream, ev, wsp<uint8_t>(p, p->L.xq),
+  auto kern = p->mid_fmt == MOE_MID_MXFP4 ? gate_up_big_kernel<true> : gate_up_big_kernel<false>;
+  return launch_k(kern, dim3(blocks), dim3(256), 0, a.stream, ev, wsp<uint8_t>(p, p->L.xq),
                   wsp<uint8_t>(p, p->L.xs), reinterpret_cast<const uint8_t*>(a.w13),
                   reinterpret_cast<const uint8_t*>(a.s13), wsp<int>(p, p->L.sorted_entry),
                   wsp<int4>(p, p->X.gu_items), wsp<int>(p, p->X.meta), (int)p->s.H, (int)p->s.I,

@@ -161,18 +161,26 @@ static_assert(kSmallRows < (1 << 16) && kMidM * 16 < (1 << 16), "rows and tiles 
 
 // Offsets (and with_tiles: tiles of kTileRows sorted rows, meta[0]) from
 // per-expert counts (thread e holds count c of expert e). Leaves offsets in
-// s_off. Tiles are written only where the 16-row-tile gate/up runs (up to
-// kMidM tokens), where the row total is below 2^16: rows and tiles then
-// share one scan, packed as rows | tiles << 16.
+// s_off. Tiles are written where the 16-row tiles are used (the mid-range
+// gate/up up to kMidM tokens, the MXFP4-mid down at every M). While the row
+// total is below 2^16 (packed == true: up to kMidM tokens) rows and tiles
+// share one scan, packed as rows | tiles << 16; else two scans.
 __device__ void write_offsets_tiles(int c, int E, int* s_off, int* s_tmp, int* __restrict__ count,
                                     int* __restrict__ offset, int4* __restrict__ tiles, int* __restrict__ meta,
-                                    bool with_tiles = true) {
+                                    bool with_tiles = true, bool packed = true) {
   const int tid = threadIdx.x;
   const int nt = with_tiles ? (c + kTileRows - 1) / kTileRows : 0;
-  int total;
-  const int pre = block_exclusive_scan(with_tiles ? c | (nt << 16) : c, s_tmp, &total);
-  const int off = with_tiles ? pre & 0xFFFF : pre, toff = pre >> 16;
-  const int total_rows = with_tiles ? total & 0xFFFF : total, total_tiles = total >> 16;
+  int total, off, toff, total_rows, total_tiles;
+  if (packed || !with_tiles) {
+    const int pre = block_exclusive_scan(with_tiles ? c | (nt << 16) : c, s_tmp, &total);
+    off = with_tiles ? pre & 0xFFFF : pre;
+    toff = pre >> 16;
+    total_rows = with_tiles ? total & 0xFFFF : total;
+    total_tiles = total >> 16;
+  } else {
+    off = block_exclusive_scan(c, s_tmp, &total_rows);
+    toff = block_exclusive_scan(nt, s_tmp, &total_tiles);
+  }
   if (tid < E) {
     count[tid] = c;
     offset[tid] = off;
@@ -435,7 +443,7 @@ __global__ __launch_bounds__(1024) void align_offsets_kernel(
   const int tid = threadIdx.x;
   const int c = tid < E ? count_in[tid] : 0;
   __syncthreads();  // count_in may be count itself
-  write_offsets_tiles(c, E, s_off, s_tmp, count, offset, tiles, meta, with_tiles != 0);
+  write_offsets_tiles(c, E, s_off, s_tmp, count, offset, tiles, meta, with_tiles != 0, with_tiles == 1);
   write_tile_prefixes(c, E, n_iblk, n_nc, s_tmp, toff, meta);
 }
 
@@ -592,7 +600,9 @@ hipError_t launch_align(const moe_plan* p, const CallArgs& a, Ev ev) {
   e = launch_k(align_offsets_kernel, dim3(1), dim3(1024), 0, a.stream, Ev{}, wsp<int>(p, p->L.count),
                (int)p->s.E, wsp<int>(p, p->L.count), wsp<int>(p, p->L.offset), wsp<int4>(p, p->X.tiles),
                wsp<int>(p, p->X.meta), (int)(p->s.I / 128), (int)(p->s.H / kDownItemCols), wsp<int>(p, p->X.toff),
-               (int)mid_path(a.M, p->s.top_k));  // the 16-row tiles of the mid-range gate/up
+               // the 16-row tiles: of the mid-range gate/up (1: rows packed
+               // with tiles in one scan), of the MXFP4-mid down above kMidM (2)
+               mid_path(a.M, p->s.top_k) ? 1 : p->mid_fmt == MOE_MID_MXFP4 ? 2 : 0);
   if (e != hipSuccess) return e;
   // a thread per entry and per work item: with few rows per expert the items
   // (tiles x column blocks) far outnumber the entries

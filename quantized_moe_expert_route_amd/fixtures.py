@@ -87,6 +87,11 @@ for _m in (32, 64, 128, 256):
 # MXFP4 arm); it shares c3's weights (seed 3).
 WORKLOADS["t4_m16_hot"] = Workload("t4_m16_hot", Shape(M=16, H=6144, E=256, I=512, top_k=8), "hot", 3)
 
+# The TP4 shape at M = 4096 with spread and hot routing (rows the pages time
+# for both weight formats; c3's weights, no shared expert).
+WORKLOADS["t4_m4096_spread"] = Workload("t4_m4096_spread", Shape(M=4096, H=6144, E=256, I=512, top_k=8), "spread", 3)
+WORKLOADS["t4_m4096_hot"] = Workload("t4_m4096_hot", Shape(M=4096, H=6144, E=256, I=512, top_k=8), "hot", 3)
+
 # The pages' fused form of the shared expert: 256 routed experts plus the
 # shared expert as expert 256, top-9 (TP8 shapes of c1 and c2; experts
 # 0..255 are c1's / c2's, the logits are drawn for 257 columns and the last
@@ -107,6 +112,8 @@ WORKLOAD_TITLES = {
     "c3": "TP4-rank prefill H6144 E256 top8 I512 M1024, MXFP4 experts, Zipf(1.1) routing",
     "c4": "TP4-rank large prefill H6144 E256 top8 I512 M4096 + block-FP8 shared expert I512, Zipf(1.1)",
     "t4_m16_hot": "TP4-rank batch H6144 E256 top8 I512 M16, hot routing (every token on the same 8 experts)",
+    "t4_m4096_spread": "TP4-rank prefill H6144 E256 top8 I512 M4096, spread routing (token t on experts 8t..8t+7 mod 256)",
+    "t4_m4096_hot": "TP4-rank prefill H6144 E256 top8 I512 M4096, hot routing (every token on the same 8 experts)",
     "c1s": "TP8-rank decode H6144 E256+1 top9 I256 M4, shared expert fused as expert 256 (slot 9), uniform logits",
     "c2s": "TP8-rank verify H6144 E256+1 top9 I256 M16, shared expert fused as expert 256 (slot 9), correlated rows",
     "c1b": "TP8-rank decode H6144 E256 top8 I256 M4 + block-FP8 shared expert I256 inside the routed launches",

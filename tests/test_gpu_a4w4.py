@@ -93,6 +93,9 @@ SHAPES = [
     (3, 512, 4, 128, 2, "normal", 128),        # with the shared expert
     (256, 512, 16, 384, 4, "normal", 0),       # the largest M served; I = 384 (3 K-steps)
     (70, 512, 8, 512, 2, "normal", 0),         # I = 512 (4 K-steps)
+    (257, 512, 16, 128, 4, "normal", 0),       # above 256 tokens: the mid quantized inside the 64-row gate/up
+    (300, 1024, 32, 256, 8, "zipf", 0),        # large path, skewed
+    (600, 512, 8, 512, 2, "normal", 128),      # large path, I = 512, with the shared expert
 ]
 
 
@@ -111,7 +114,8 @@ def test_mx_small_shapes(M, H, E, I, k, kind, Is):
 
 
 @pytest.mark.parametrize("name,n_tok", [("c1", 0), ("c2", 0), ("t4_m16_hot", 0), ("m256_hot", 8),
-                                        ("m256_mixed", 8), ("m64_spread", 6)])
+                                        ("m256_mixed", 8), ("m64_spread", 6), ("c3", 8),
+                                        ("t4_m4096_spread", 6), ("t4_m4096_hot", 6)])
 def test_mx_full_size(name, n_tok):
     """The benchmark's shapes: every token (n_tok = 0) or a sample the oracle
     evaluates alone; routing and sort on every token."""
@@ -153,29 +157,23 @@ def test_mx_and_e4m3_alternate_on_one_plan():
         assert np.array_equal(gout, ref["out"]), f"format {fmt}: output differs"
 
 
-def test_mx_rejects_large_m():
-    """Calls above 256 tokens are not served with the MXFP4 mid (host check,
-    nothing enqueued); the E4M3 mid serves them on the same plan."""
+def test_mx_served_above_256_tokens_on_one_plan():
+    """One plan at 300 tokens switching formats: the MXFP4 mid (quantized
+    inside the 64-row-tile gate/up) and the E4M3 mid each match their own
+    oracle; the stages launch what the plan reports."""
     import torch
 
-    from quantized_moe_expert_route_amd.binding import (MID_E4M3, MID_MXFP4, MOE_ERR_UNSUPPORTED, MoeError,
-                                                        layout_for, pack_w2)
+    from quantized_moe_expert_route_amd.binding import MID_E4M3, MID_MXFP4
 
     shape = X.Shape(M=300, H=512, E=16, I=128, top_k=2)
     d = X.make_inputs(shape, "normal", 5)
-    g = upload(d)
-    plan = make_plan(shape)
-    plan.set_mid_format(MID_MXFP4)
-    plan.set_weight_layout(layout_for(MID_MXFP4))
-    out = torch.empty((300, 512), dtype=torch.int16, device=g["x"].device)
-    w2p, s2p = pack_w2(g["w2"], g["s2"])
-    with pytest.raises(MoeError) as ei:
-        plan.forward(g["x"], g["logits"], g["w13"], g["s13"], w2p, s2p, out, M=300)
-    assert ei.value.status == MOE_ERR_UNSUPPORTED
-    assert plan.stage_launches(300) == [-1] * len(plan.stage_launches(300))  # not served
-    plan.set_mid_format(MID_MXFP4)
-    assert plan.stage_launches(256)[3] == 1 and plan.stage_launches(4)[6] == 1  # own quantization, combine
-    plan.set_mid_format(MID_E4M3)
-    plan.set_weight_layout(layout_for(MID_E4M3))
-    plan.forward(g["x"], g["logits"], g["w13"], g["s13"], g["w2"], g["s2"], out, M=300)
-    torch.cuda.synchronize()
+    plan, g = None, None
+    for fmt in (MID_MXFP4, MID_E4M3):
+        gout, gi, plan, g = _run_mx(d, plan=plan, g=g, fmt=fmt)
+        ref = O.moe_forward(d["x"], d["logits"], d["w13"], d["s13"], d["w2"], d["s2"], 2, 2.5, None,
+                            mid_format="mxfp4" if fmt == MID_MXFP4 else "e4m3")
+        if fmt == MID_MXFP4:
+            _check_mid_mx(gi["midq"], gi["mids"], ref["midq"], ref["mids"])
+            assert plan.stage_launches(300)[3] == 0  # the mid quantization is inside gate/up
+        _check_out(gout, ref["out"])
+        assert np.array_equal(gout, ref["out"]), f"format {fmt}: output differs"
