@@ -167,7 +167,7 @@ static_assert(kSmallRows < (1 << 16) && kMidM * 16 < (1 << 16), "rows and tiles 
 // share one scan, packed as rows | tiles << 16; else two scans.
 __device__ void write_offsets_tiles(int c, int E, int* s_off, int* s_tmp, int* __restrict__ count,
                                     int* __restrict__ offset, int4* __restrict__ tiles, int* __restrict__ meta,
-                                    bool with_tiles = true, bool packed = true) {
+                                    bool with_tiles = true, bool packed = true, int* s_toff = nullptr) {
   const int tid = threadIdx.x;
   const int nt = with_tiles ? (c + kTileRows - 1) / kTileRows : 0;
   int total, off, toff, total_rows, total_tiles;
@@ -185,16 +185,34 @@ __device__ void write_offsets_tiles(int c, int E, int* s_off, int* s_tmp, int* _
     count[tid] = c;
     offset[tid] = off;
     s_off[tid] = off;
-    for (int i = 0; with_tiles && i < nt; ++i) {
+    if (s_toff) s_toff[tid] = toff;
+    for (int i = 0; with_tiles && !s_toff && i < nt; ++i) {
       const int r0 = off + i * kTileRows;
       tiles[toff + i] = make_int4(tid, r0, min(r0 + kTileRows, off + c), 0);
     }
   }
   if (tid == 0) {
     offset[E] = total_rows;
+    s_off[E] = total_rows;
+    if (s_toff) s_toff[E] = total_tiles;
     if (with_tiles) meta[0] = total_tiles;
   }
   __syncthreads();
+  if (with_tiles && s_toff) {
+    // many tiles (large M): every thread writes some, each finding its
+    // expert by binary search of the tile prefix
+    for (int i = tid; i < total_tiles; i += blockDim.x) {
+      int lo = 0, hi = E;  // largest e with s_toff[e] <= i
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_toff[mid] <= i) lo = mid; else hi = mid;
+      }
+      int e = lo;
+      while (s_toff[e + 1] == s_toff[e]) ++e;  // skip experts without tiles
+      const int r0 = s_off[e] + (i - s_toff[e]) * kTileRows;
+      tiles[i] = make_int4(e, r0, min(r0 + kTileRows, s_off[e + 1]), 0);
+    }
+  }
 }
 
 // ---------------------------------------------------------------- M <= kSmallM
@@ -207,7 +225,7 @@ __global__ __launch_bounds__(1024) void route_align_small_kernel(
     uint8_t* __restrict__ xs, int shared_slot, SharedSmall sh) {
   __shared__ uint32_t s_mask[1024][2];  // expert -> tokens 0..63
   __shared__ int s_ids[64 * 16];
-  __shared__ int s_off[1024];
+  __shared__ int s_off[1025];
   __shared__ int s_tmp[64];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int xq_groups = (M * (H >> 5) + 63) >> 6;
@@ -438,12 +456,14 @@ __global__ __launch_bounds__(1024) void align_offsets_kernel(
     const int* __restrict__ count_in, int E, int* __restrict__ count, int* __restrict__ offset,
     int4* __restrict__ tiles, int* __restrict__ meta, int n_iblk, int n_nc, int* __restrict__ toff,
     int with_tiles) {
-  __shared__ int s_off[1024];
+  __shared__ int s_off[1025];
   __shared__ int s_tmp[64];
+  __shared__ int s_t16[1025];  // 16-row tile prefix per expert (large M, MXFP4 mid)
   const int tid = threadIdx.x;
   const int c = tid < E ? count_in[tid] : 0;
   __syncthreads();  // count_in may be count itself
-  write_offsets_tiles(c, E, s_off, s_tmp, count, offset, tiles, meta, with_tiles != 0, with_tiles == 1);
+  write_offsets_tiles(c, E, s_off, s_tmp, count, offset, tiles, meta, with_tiles != 0, with_tiles == 1,
+                      with_tiles == 2 ? s_t16 : nullptr);
   write_tile_prefixes(c, E, n_iblk, n_nc, s_tmp, toff, meta);
 }
 
