@@ -42,17 +42,19 @@ __global__ __launch_bounds__(256) void act_quant_mx_kernel(const float* __restri
   }
 }
 
-// down on MXFP4 x MXFP4, w2 packed by moe_pack_w2. Work item = (16-row tile,
-// group of cbg 64-column blocks). The workgroup stages the tile's mid rows
-// (16 x I/2 bytes, contiguous in sorted order) and scale bytes in LDS with
-// one coalesced read; each wave then holds its A fragments in registers and
-// streams the B fragments of its 16 columns of every column block in the
-// group: in K-step ks lane 16 g + r supplies MX block 4 ks + g of tile row r
-// (A) and of weight column r (B), and a packed K-step of a 16-column block
-// is 1 KB contiguous in lane order. Items are ordered column group first, so
-// the tiles of one expert sharing a w2 slice are adjacent, and each XCD
-// (blockIdx % 8) walks its own contiguous eighth of them.
-template <int NKS>
+// down on MXFP4 x MXFP4, w2 packed by moe_pack_w2. Work item = (tile of RB
+// x 16 sorted rows, group of cbg 64-column blocks): 16-row tiles up to
+// kMidM tokens, 64-row tiles above (RB = 4: each weight fragment then feeds
+// four MFMA row blocks instead of one). The workgroup stages the tile's mid
+// rows (RB x 16 x I/2 bytes, contiguous in sorted order) and scale bytes in
+// LDS with one coalesced read; each wave then holds its A fragments in
+// registers and streams the B fragments of its 16 columns of every column
+// block in the group: in K-step ks lane 16 g + r supplies MX block 4 ks + g
+// of tile row r (A) and of weight column r (B), and a packed K-step of a
+// 16-column block is 1 KB contiguous in lane order. Items are ordered column
+// group first, so the tiles of one expert sharing a w2 slice are adjacent,
+// and each XCD (blockIdx % 8) walks its own contiguous eighth of them.
+template <int NKS, int RB>
 __global__ __launch_bounds__(256) void down_fp4_kernel(const uint8_t* __restrict__ midq, const uint8_t* __restrict__ mids,
                                                        const uint8_t* __restrict__ w2p, const uint32_t* __restrict__ s2p,
                                                        const int* __restrict__ sorted_entry,
@@ -61,8 +63,9 @@ __global__ __launch_bounds__(256) void down_fp4_kernel(const uint8_t* __restrict
   constexpr int I = NKS * 128;
   constexpr int Ib = I / 2, Isc = I / 32;
   constexpr int LDA = Ib + 16;  // padded row: the 16 rows of a fragment read meet 16 different bank groups
-  __shared__ __align__(16) uint8_t sm_a[16 * LDA];
-  __shared__ uint8_t sm_s[16 * 16];
+  constexpr int TR = 16 * RB;   // rows per tile
+  __shared__ __align__(16) uint8_t sm_a[TR * LDA];
+  __shared__ uint8_t sm_s[TR * 16];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, g = lane >> 4;
   const int nt = meta[0];
@@ -78,29 +81,39 @@ __global__ __launch_bounds__(256) void down_fp4_kernel(const uint8_t* __restrict
     const int4 tl = tiles[ti];  // {expert, row_begin, row_end, 0}
     __syncthreads();  // the previous item's LDS reads are done
     // rows past the tile's end repeat its last row (their results are dropped)
-    if (tid < Ib) {
-      constexpr int cpr = Ib / 16;  // 16-byte chunks per row
-      const int rr = tid / cpr, c = tid - rr * cpr;
-      const int row = min(tl.y + rr, tl.z - 1);
-      *reinterpret_cast<uint4*>(sm_a + rr * LDA + 16 * c) = ld16(midq + (size_t)row * Ib + 16 * c);
+    constexpr int cpr = Ib / 16;  // 16-byte chunks per row
+#pragma unroll
+    for (int q = 0; q < (TR * cpr + 255) / 256; ++q) {
+      const int idx = tid + 256 * q;
+      if (idx < TR * cpr) {
+        const int rr = idx / cpr, c = idx - rr * cpr;
+        const int row = min(tl.y + rr, tl.z - 1);
+        *reinterpret_cast<uint4*>(sm_a + rr * LDA + 16 * c) = ld16(midq + (size_t)row * Ib + 16 * c);
+      }
     }
-    if (tid < 16 * Isc) {
-      const int rr = tid / Isc, c = tid - rr * Isc;
+    for (int idx = tid; idx < TR * Isc; idx += 256) {
+      const int rr = idx / Isc, c = idx - rr * Isc;
       sm_s[rr * 16 + c] = mids[(size_t)min(tl.y + rr, tl.z - 1) * Isc + c];
     }
     __syncthreads();
-    uint4 a[NKS];
-    uint32_t sa[NKS];
+    // row blocks of the tile that hold rows (a 64-row tile of a small expert
+    // computes only its first ones)
+    const int nrb = min(RB, (tl.z - tl.y + 15) / 16);
+    uint4 a[RB][NKS];
+    uint32_t sa[RB][NKS];
+    int ent[RB][4];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      a[ks] = *reinterpret_cast<const uint4*>(sm_a + r * LDA + 64 * ks + 16 * g);
-      sa[ks] = sm_s[r * 16 + 4 * ks + g];
-    }
-    int ent[4];
+    for (int i2 = 0; i2 < RB; ++i2) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = tl.y + 4 * g + i;
-      ent[i] = m < tl.z ? sorted_entry[m] : -1;
+      for (int ks = 0; ks < NKS; ++ks) {
+        a[i2][ks] = *reinterpret_cast<const uint4*>(sm_a + (16 * i2 + r) * LDA + 64 * ks + 16 * g);
+        sa[i2][ks] = sm_s[(16 * i2 + r) * 16 + 4 * ks + g];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = tl.y + 16 * i2 + 4 * g + i;
+        ent[i2][i] = m < tl.z ? sorted_entry[m] : -1;
+      }
     }
     const int cb0 = cg * cbg, cb1 = min(ncb, cb0 + cbg);
     for (int cb = cb0; cb < cb1; cb += kDfCbs) {
@@ -118,14 +131,20 @@ __global__ __launch_bounds__(256) void down_fp4_kernel(const uint8_t* __restrict
 #pragma unroll
       for (int q = 0; q < kDfCbs; ++q) {
         if (cb + q < cb1) {
-          v4f acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < NKS; ++ks) acc = mfma_fp4(a[ks], b[q][ks], acc, sa[ks], (sb[q] >> (8 * ks)) & 0xFFu);
           const int col = (cb + q) * 64 + wave * 16 + r;
-          // D row 4 g + i of the tile, column r
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (ent[i] >= 0) y[(size_t)ent[i] * H + col] = acc[i];
+          for (int i2 = 0; i2 < RB; ++i2) {
+            if (i2 < nrb) {
+              v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int ks = 0; ks < NKS; ++ks)
+                acc = mfma_fp4(a[i2][ks], b[q][ks], acc, sa[i2][ks], (sb[q] >> (8 * ks)) & 0xFFu);
+              // D row 16 i2 + 4 g + i of the tile, column r
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (ent[i2][i] >= 0) y[(size_t)ent[i2][i] * H + col] = acc[i];
+            }
+          }
         }
       }
     }
@@ -144,7 +163,9 @@ hipError_t launch_act_quant_mx(const moe_plan* p, const CallArgs& a, Ev ev) {
 hipError_t launch_down_fp4(const moe_plan* p, const CallArgs& a, Ev ev) {
   const int H = (int)p->s.H, I = (int)p->s.I;
   const int64_t n = a.M * p->s.top_k;
-  const int64_t t16 = (n + std::min<int64_t>(p->s.E, n) * (kTileRows - 1) + kTileRows - 1) / kTileRows;
+  const bool big = !mid_path(a.M, p->s.top_k);  // 64-row tiles above kMidM tokens
+  const int tr = big ? kFp4BigRows : kTileRows;
+  const int64_t t16 = (n + std::min<int64_t>(p->s.E, n) * (tr - 1) + tr - 1) / tr;
   const int ncb = H / 64;
   // column blocks per item: as many as still leave ~2048 items to spread
   int cbg = 1;
@@ -158,10 +179,10 @@ hipError_t launch_down_fp4(const moe_plan* p, const CallArgs& a, Ev ev) {
                     wsp<int4>(p, p->X.tiles), wsp<int>(p, p->X.meta), H, cbg, wsp<float>(p, p->L.y));
   };
   switch (I / 128) {
-    case 1: return go(down_fp4_kernel<1>);
-    case 2: return go(down_fp4_kernel<2>);
-    case 3: return go(down_fp4_kernel<3>);
-    case 4: return go(down_fp4_kernel<4>);
+    case 1: return big ? go(down_fp4_kernel<1, 4>) : go(down_fp4_kernel<1, 1>);
+    case 2: return big ? go(down_fp4_kernel<2, 4>) : go(down_fp4_kernel<2, 1>);
+    case 3: return big ? go(down_fp4_kernel<3, 4>) : go(down_fp4_kernel<3, 1>);
+    case 4: return big ? go(down_fp4_kernel<4, 4>) : go(down_fp4_kernel<4, 1>);
     default: return hipErrorInvalidValue;
   }
 }

@@ -12,6 +12,7 @@
 namespace qmoe {
 
 constexpr int kTileRows = 16;  // sorted rows per tile of the small-token kernels
+constexpr int kFp4BigRows = 64;  // sorted rows per tile of the MXFP4-mid down above kMidM tokens
 constexpr int kBigRows = 32;   // sorted rows per tile of the large-token down kernel
 constexpr int kGuRows = 64;    // sorted rows per tile of the large-token gate/up kernel
 constexpr int kDownItemCols = 256; // output columns per down work item of the large-token kernel

@@ -159,17 +159,19 @@ __device__ int block_exclusive_scan(int v, int* s_tmp, int* total) {
 
 static_assert(kSmallRows < (1 << 16) && kMidM * 16 < (1 << 16), "rows and tiles share one packed scan");
 
-// Offsets (and with_tiles: tiles of kTileRows sorted rows, meta[0]) from
-// per-expert counts (thread e holds count c of expert e). Leaves offsets in
-// s_off. Tiles are written where the 16-row tiles are used (the mid-range
-// gate/up up to kMidM tokens, the MXFP4-mid down at every M). While the row
-// total is below 2^16 (packed == true: up to kMidM tokens) rows and tiles
-// share one scan, packed as rows | tiles << 16; else two scans.
+// Offsets (and with_tiles: tiles of sorted rows, meta[0]) from per-expert
+// counts (thread e holds count c of expert e). Leaves offsets in s_off.
+// Tiles are written where they are used: of kTileRows rows for the
+// mid-range gate/up and down up to kMidM tokens (packed == true: the row
+// total is below 2^16, so rows and tiles share one scan, packed as rows |
+// tiles << 16), of kFp4BigRows rows for the MXFP4-mid down above (two
+// scans; every thread writes some tiles, finding its expert in s_toff).
 __device__ void write_offsets_tiles(int c, int E, int* s_off, int* s_tmp, int* __restrict__ count,
                                     int* __restrict__ offset, int4* __restrict__ tiles, int* __restrict__ meta,
                                     bool with_tiles = true, bool packed = true, int* s_toff = nullptr) {
   const int tid = threadIdx.x;
-  const int nt = with_tiles ? (c + kTileRows - 1) / kTileRows : 0;
+  const int tr = s_toff ? kFp4BigRows : kTileRows;  // rows per tile
+  const int nt = with_tiles ? (c + tr - 1) / tr : 0;
   int total, off, toff, total_rows, total_tiles;
   if (packed || !with_tiles) {
     const int pre = block_exclusive_scan(with_tiles ? c | (nt << 16) : c, s_tmp, &total);
@@ -209,8 +211,8 @@ __device__ void write_offsets_tiles(int c, int E, int* s_off, int* s_tmp, int* _
       }
       int e = lo;
       while (s_toff[e + 1] == s_toff[e]) ++e;  // skip experts without tiles
-      const int r0 = s_off[e] + (i - s_toff[e]) * kTileRows;
-      tiles[i] = make_int4(e, r0, min(r0 + kTileRows, s_off[e + 1]), 0);
+      const int r0 = s_off[e] + (i - s_toff[e]) * kFp4BigRows;
+      tiles[i] = make_int4(e, r0, min(r0 + kFp4BigRows, s_off[e + 1]), 0);
     }
   }
 }
@@ -458,7 +460,7 @@ __global__ __launch_bounds__(1024) void align_offsets_kernel(
     int with_tiles) {
   __shared__ int s_off[1025];
   __shared__ int s_tmp[64];
-  __shared__ int s_t16[1025];  // 16-row tile prefix per expert (large M, MXFP4 mid)
+  __shared__ int s_t16[1025];  // tile prefix per expert (large M, MXFP4 mid)
   const int tid = threadIdx.x;
   const int c = tid < E ? count_in[tid] : 0;
   __syncthreads();  // count_in may be count itself
@@ -620,8 +622,9 @@ hipError_t launch_align(const moe_plan* p, const CallArgs& a, Ev ev) {
   e = launch_k(align_offsets_kernel, dim3(1), dim3(1024), 0, a.stream, Ev{}, wsp<int>(p, p->L.count),
                (int)p->s.E, wsp<int>(p, p->L.count), wsp<int>(p, p->L.offset), wsp<int4>(p, p->X.tiles),
                wsp<int>(p, p->X.meta), (int)(p->s.I / 128), (int)(p->s.H / kDownItemCols), wsp<int>(p, p->X.toff),
-               // the 16-row tiles: of the mid-range gate/up (1: rows packed
-               // with tiles in one scan), of the MXFP4-mid down above kMidM (2)
+               // the tiles: 16 rows for the mid-range gate/up (1: rows
+               // packed with tiles in one scan), kFp4BigRows rows for the
+               // MXFP4-mid down above kMidM (2)
                mid_path(a.M, p->s.top_k) ? 1 : p->mid_fmt == MOE_MID_MXFP4 ? 2 : 0);
   if (e != hipSuccess) return e;
   // a thread per entry and per work item: with few rows per expert the items
