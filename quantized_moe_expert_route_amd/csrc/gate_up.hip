@@ -56,18 +56,26 @@ __global__ __launch_bounds__(256) void gate_up_m16_kernel(
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4;
   const int n_it = I / 16;
-  const int n_work = meta[0] * n_it;
+  // The first item's tile is read beside meta (the grid never exceeds the
+  // tile array's bound, so the read is in bounds; it is used only when the
+  // item exists): one memory round trip fewer before the weights move.
+  int4 tl = tiles[blockIdx.x / n_it];
+  int n_tiles = meta[0];
+  asm volatile("" : "+s"(n_tiles), "+s"(tl.x), "+s"(tl.y), "+s"(tl.z));  // both loads in flight together
+  const int n_work = n_tiles * n_it;
   const size_t Hb = (size_t)H / 2, Hs = (size_t)H / 32;
   const int nss = H / 512, nks = H / 128;
   const size_t nrb = (size_t)I / 8;  // 16-row blocks of an expert's 2I rows
   for (int w = blockIdx.x; w < n_work; w += gridDim.x) {
-    const int4 tl = tiles[w / n_it];
+    if (w != (int)blockIdx.x) tl = tiles[w / n_it];
     const int it = w % n_it;
     const int e = tl.x, r0 = tl.y, r1 = tl.z;
     const bool rv = r0 + r < r1;
-    const int tok = rv ? sorted_entry[r0 + r] / k : 0;
-    const uint8_t* pa = xq + (size_t)tok * Hb + 16 * g;  // + 64 ks
-    const uint8_t* psa = xs + (size_t)tok * Hs;          // + 16 ss: byte 4 j + g is K-step 4 ss + j
+    // the row's entry is waited for only after the first weight loads are
+    // out (the empty asm keeps its use inside the loop, behind them)
+    int se = sorted_entry[min(r0 + r, r1 - 1)];
+    const uint8_t* pa = xq;   // the row's token's x: + 64 ks (set once the entry is in)
+    const uint8_t* psa = xs;  // its scales: + 16 ss: byte 4 j + g is K-step 4 ss + j
     const size_t rbg = (size_t)e * nrb + it, rbu = rbg + I / 16;
     const uint8_t* pg = w13p + rbg * nks * 1024 + 16 * lane;  // + 1024 ks
     const uint8_t* pu = w13p + rbu * nks * 1024 + 16 * lane;
@@ -91,6 +99,12 @@ __global__ __launch_bounds__(256) void gate_up_m16_kernel(
         }
         sg[q] = ld4(psg + 256 * ss);
         su[q] = ld4(psu + 256 * ss);
+        if (q == 0) {
+          asm volatile("" : "+v"(se));
+          const size_t tok = rv ? (size_t)(se / k) : 0;
+          pa = xq + tok * Hb + 16 * g;
+          psa = xs + tok * Hs;
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) a[q][j] = rv ? ld16(pa + (4 * ss + j) * 64) : make_uint4(0, 0, 0, 0);
         sa[q] = rv ? ld16(psa + 16 * ss) : make_uint4(0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu);

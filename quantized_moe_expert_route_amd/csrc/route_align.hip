@@ -33,10 +33,16 @@ namespace qmoe {
 // Top-k of one logits row by one wave. Lane j < k receives slot j's expert
 // and logit.
 // Keys of one logits row: lane l holds experts l + 64c; every real key is > 0.
+// The loads are unconditional (lanes past E read the row's last logit) so
+// that all of them are in flight together: each one under its own branch
+// waited for the one before it, one memory round trip per 64 experts.
 template <int EC>
 __device__ __forceinline__ void load_keys(const float* __restrict__ row, int E, int lane, uint32_t (&key)[EC]) {
+  float v[EC];
 #pragma unroll
-  for (int c = 0; c < EC; ++c) key[c] = lane + 64 * c < E ? order_key(row[lane + 64 * c]) : 0u;
+  for (int c = 0; c < EC; ++c) v[c] = row[max(min(lane + 64 * c, E - 1), 0)];
+#pragma unroll
+  for (int c = 0; c < EC; ++c) key[c] = lane + 64 * c < E ? order_key(v[c]) : 0u;
 }
 
 // k rounds: the wave's largest key, and of the experts holding it the lowest
