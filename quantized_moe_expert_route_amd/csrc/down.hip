@@ -27,7 +27,7 @@ namespace qmoe {
 // picked per H so that the CUs carry equal shares of w2; lanes of the
 // 16-column MFMA past cw repeat column cw - 1 and their results are never
 // read): its four waves
-// take contiguous runs of the 16-row tiles, keep each (entry, column) result
+// take every fourth 16-row tile (wave w: tiles w, w + 4, ...), keep each (entry, column) result
 // in LDS, and when every tile is done the workgroup forms out[t, c0 .. c0+16)
 // from the token's k slots, so no slot result leaves the workgroup.
 //
@@ -85,7 +85,7 @@ size_t down_combine_lds_bytes(int64_t n, int64_t I, bool mid_lds, bool mid_bf16)
 template <int NB, int D, bool MID_LDS, int ST = 8, bool SH = false>
 __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
     const uint8_t* __restrict__ midq, const float* __restrict__ mids, const uint8_t* __restrict__ w2, const uint8_t* __restrict__ s2, const int* __restrict__ sorted_entry,
-    const int4* __restrict__ tiles, const int* __restrict__ meta, int H, int k, int M, int cw,
+    const int4* __restrict__ tiles, const int* __restrict__ meta, int tmax, int H, int k, int M, int cw,
     const float* __restrict__ topk_w, const float* __restrict__ ys, uint16_t* __restrict__ out,
     double* __restrict__ partial, SharedSmall sh) {
   constexpr int I = NB * 128;
@@ -101,10 +101,20 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
   const int r = lane & 15, g = lane >> 4;
   const int c0 = blockIdx.x * cw;
   const int rc = min(r, cw - 1);  // the lane's weight column
+  // wave w takes tiles w, w + kDcWaves, ... (my of them); its first D
+  // descriptors are read beside meta (indices clamped to the tile array's
+  // bound, tmax), so the weight loads wait for one round trip, not two
+  int4 T[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) T[d] = tiles[min(wave + kDcWaves * d, tmax - 1)];
+  const int4 t_first = tiles[0];
   const int nt = meta[0];
-  const int per = (nt + kDcWaves - 1) / kDcWaves;
-  const int base = wave * per;                                    // this wave's tiles [base, base + my)
-  const int my = max(0, min(per, nt - base));
+  // (all of these loads are issued before the first wait)
+  asm volatile("" ::"s"(nt), "s"(t_first.x), "s"(T[0].x), "s"(T[min(1, D - 1)].x), "s"(T[min(2, D - 1)].x),
+               "s"(T[min(3, D - 1)].x), "s"(T[min(4, D - 1)].x), "s"(T[min(5, D - 1)].x), "s"(T[min(6, D - 1)].x),
+               "s"(T[min(7, D - 1)].x));
+  const int my = wave < nt ? (nt - 1 - wave) / kDcWaves + 1 : 0;
+  auto tile_of = [&](int i) { return wave + kDcWaves * i; };  // the wave's i-th tile
 
   // ---- descriptors of the wave's first D tiles, then the staging loads
   // (both from L2); the weight loads wait only for the descriptors, the LDS
@@ -117,9 +127,14 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
   // by the end of the ring
   SharedDownPre sdp;
   if (SH) shared_down_fetch(sh, M, c0, cw, sdp);
-  int4 T[D];
+  // slots past the run repeat its last tile; a wave without tiles holds tile 0
+  if (my == 0) {
 #pragma unroll
-  for (int d = 0; d < D; ++d) T[d] = tiles[my > 0 ? base + min(d, my - 1) : 0];
+    for (int d = 0; d < D; ++d) T[d] = t_first;
+  }
+#pragma unroll
+  for (int d = 1; d < D; ++d)
+    if (d >= my && my > 0) T[d] = T[d - 1];
   __builtin_amdgcn_sched_barrier(0);
   constexpr int kSt = MID_LDS ? ST : 1;
   uint4 st[kSt];
@@ -268,8 +283,8 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
     for (; i0 + 2 * D <= my; i0 += D) {
 #pragma unroll
       for (int d = 0; d < D; d += 2) {  // two independent tiles per step
-        const int4 tn0 = tiles[base + i0 + D + d];
-        const int4 tn1 = tiles[base + i0 + D + min(d + 1, D - 1)];
+        const int4 tn0 = tiles[tile_of(i0 + D + d)];
+        const int4 tn1 = tiles[tile_of(i0 + D + min(d + 1, D - 1))];
         compute(T[d], S[d]);
         if (d + 1 < D) compute(T[d + 1], S[d + 1]);
         __builtin_amdgcn_sched_barrier(0);
@@ -295,7 +310,7 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
 #pragma unroll
       for (int d = 0; d < D; ++d) {
         if (d < rest) {
-          T[d] = tiles[base + i0 + D + d];
+          T[d] = tiles[tile_of(i0 + D + d)];
           load(T[d], S[d]);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -401,11 +416,13 @@ hipError_t launch_down_combine(const moe_plan* p, const CallArgs& a, Ev ev) {
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   const float* ys = p->s.shared_I > 0 && !sh.hq ? wsp<float>(p, p->L.sh_y) : nullptr;
   const int cw = down_combine_cols(H, p->num_cus);
+  // the tile array's bound for this call (tiles of kTileRows sorted rows)
+  const int tmax = (int)((n + std::min<int64_t>(p->s.E, n) * (kTileRows - 1) + kTileRows - 1) / kTileRows);
   auto go = [&](auto kern) {
     return launch_k(kern, dim3(H / cw), dim3(kDcThreads), lds, a.stream, ev, wsp<uint8_t>(p, p->L.midq),
                     wsp<float>(p, p->L.mids), reinterpret_cast<const uint8_t*>(a.w2),
                     reinterpret_cast<const uint8_t*>(a.s2), wsp<int>(p, p->L.sorted_entry), wsp<int4>(p, p->X.tiles),
-                    wsp<int>(p, p->X.meta), H, (int)p->s.top_k, (int)a.M, cw, wsp<float>(p, p->L.topk_w), ys,
+                    wsp<int>(p, p->X.meta), tmax, H, (int)p->s.top_k, (int)a.M, cw, wsp<float>(p, p->L.topk_w), ys,
                     reinterpret_cast<uint16_t*>(a.out), tp_own_partial(p), sh);
   };
   // weights of D tiles in flight per wave; fewer when the slots also carry mid rows
