@@ -106,23 +106,15 @@ __device__ __forceinline__ uint32_t mx_scale_code_f32(uint32_t amax_bits) {
 }
 
 // ----------------------------------------------------------------- E4M3FN
-// Round |v| to the nearest E4M3 value, ties to the even code, saturating to
-// 448; sign copied from v. Exact: the scalings by powers of two are exact and
-// rintf rounds half to even.
-__device__ __forceinline__ uint32_t e4m3_code(float v) {
-  uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-  float a = fabsf(v);
-  uint32_t c;
-  if (!(a < 448.0f)) {
-    c = 0x7Eu;
-  } else if (a < 0.015625f) {  // below 2^-6: multiples of 2^-9
-    c = (uint32_t)rintf(a * 512.0f);
-  } else {
-    int e = (int)((__float_as_uint(a) >> 23) & 255u) - 127;  // -6..8
-    uint32_t q = (uint32_t)rintf(ldexpf(a, 3 - e));          // 8..16
-    c = ((uint32_t)(e + 7) << 3) + (q - 8u);
-  }
-  return c | sign;
+// E4M3 codes of a and b (bytes 0 and 1): the nearest E4M3 value, ties to the
+// even code, the sign kept (also on zero), by the hardware conversion
+// v_cvt_pk_fp8_f32. Every caller converts quotients v / s with s =
+// fl32(amax / 448) and |v| <= amax, which lie below 464 in magnitude; over
+// every fp32 of magnitude below 464, of either sign, the instruction returns
+// exactly the nearest-even code (tests/test_gpu_mfma_probe.py compares it
+// with a reference encoder on all of them). It does not saturate above 464.
+__device__ __forceinline__ uint32_t e4m3_pack2(float a, float b) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
 }
 
 // E4M3 value times 2^9 as base-128 digits. Every E4M3 value is an integer

@@ -37,12 +37,8 @@ __device__ __forceinline__ void quant_mid_rows(const float* __restrict__ h, int 
     const float2 v = *reinterpret_cast<const float2*>(h + base);
     const float amax = wave_max(fmaxf(fabsf(v.x), fabsf(v.y)));
     const float sc = __fdiv_rn(amax, 448.0f);
-    uint32_t c0 = 0, c1 = 0;
-    if (sc > 0.f) {
-      c0 = e4m3_code(__fdiv_rn(v.x, sc));
-      c1 = e4m3_code(__fdiv_rn(v.y, sc));
-    }
-    *reinterpret_cast<uint16_t*>(q + base) = (uint16_t)(c0 | (c1 << 8));
+    const uint32_t c01 = sc > 0.f ? e4m3_pack2(__fdiv_rn(v.x, sc), __fdiv_rn(v.y, sc)) : 0u;
+    *reinterpret_cast<uint16_t*>(q + base) = (uint16_t)c01;
     if (lane == 0) s[(size_t)row * nb + b] = sc;
   }
 }

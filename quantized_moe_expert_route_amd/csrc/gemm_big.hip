@@ -297,11 +297,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
         const int row = 16 * i + 4 * ge + v;
         const float amax = fmaxf(fmaxf(red[0][row], red[1][row]), fmaxf(red[2][row], red[3][row]));
         const float sc = __fdiv_rn(amax, 448.0f);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const uint32_t c = sc > 0.f && row < rows ? e4m3_code(__fdiv_rn(hv[i][j][v], sc)) : 0u;
-          qs[row * 128 + 32 * wn + 16 * j + re] = (uint8_t)c;
-        }
+        const uint32_t c01 =
+            sc > 0.f && row < rows ? e4m3_pack2(__fdiv_rn(hv[i][0][v], sc), __fdiv_rn(hv[i][1][v], sc)) : 0u;
+        qs[row * 128 + 32 * wn + re] = (uint8_t)c01;
+        qs[row * 128 + 32 * wn + 16 + re] = (uint8_t)(c01 >> 8);
         if (wn == 0 && re == 0 && row < rows) mids[(size_t)(r0 + row) * (I / 128) + ib] = sc;
       }
     __syncthreads();

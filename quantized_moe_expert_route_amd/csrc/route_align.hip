@@ -331,8 +331,8 @@ __device__ __forceinline__ void quant_x_unit(const uint16_t* __restrict__ x, int
       if (sc > 0.f) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const uint32_t c = e4m3_code(__fdiv_rn(__uint_as_float(w32[q] << 16), sc)) |
-                             (e4m3_code(__fdiv_rn(__uint_as_float(w32[q] & 0xFFFF0000u), sc)) << 8);
+          const uint32_t c = e4m3_pack2(__fdiv_rn(__uint_as_float(w32[q] << 16), sc),
+                                        __fdiv_rn(__uint_as_float(w32[q] & 0xFFFF0000u), sc));
           if (q < 2) lo |= c << (16 * q); else hi |= c << (16 * (q - 2));
         }
       }

@@ -39,12 +39,8 @@ __global__ __launch_bounds__(256) void sh_quant_x_kernel(const uint16_t* __restr
     const float v0 = __uint_as_float(pair << 16), v1 = __uint_as_float(pair & 0xFFFF0000u);
     const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
     const float sc = __fdiv_rn(amax, 448.0f);
-    uint32_t c0 = 0, c1 = 0;
-    if (sc > 0.f) {
-      c0 = e4m3_code(__fdiv_rn(v0, sc));
-      c1 = e4m3_code(__fdiv_rn(v1, sc));
-    }
-    store_digits2(q + ((size_t)t * nb + b) * kShDigitBlock, 2 * lane, c0 | (c1 << 8));
+    const uint32_t c01 = sc > 0.f ? e4m3_pack2(__fdiv_rn(v0, sc), __fdiv_rn(v1, sc)) : 0u;
+    store_digits2(q + ((size_t)t * nb + b) * kShDigitBlock, 2 * lane, c01);
     if (lane == 0) s[(size_t)b * M + t] = sc;
   }
 }
@@ -61,12 +57,8 @@ __global__ __launch_bounds__(256) void sh_act_quant_kernel(const float* __restri
     const float2 v = *reinterpret_cast<const float2*>(h + (size_t)row * I + b * 128 + 2 * lane);
     const float amax = wave_max(fmaxf(fabsf(v.x), fabsf(v.y)));
     const float sc = __fdiv_rn(amax, 448.0f);
-    uint32_t c0 = 0, c1 = 0;
-    if (sc > 0.f) {
-      c0 = e4m3_code(__fdiv_rn(v.x, sc));
-      c1 = e4m3_code(__fdiv_rn(v.y, sc));
-    }
-    store_digits2(q + ((size_t)row * nb + b) * kShDigitBlock, 2 * lane, c0 | (c1 << 8));
+    const uint32_t c01 = sc > 0.f ? e4m3_pack2(__fdiv_rn(v.x, sc), __fdiv_rn(v.y, sc)) : 0u;
+    store_digits2(q + ((size_t)row * nb + b) * kShDigitBlock, 2 * lane, c01);
     if (lane == 0) s[(size_t)b * rows + row] = sc;
   }
 }

@@ -142,16 +142,12 @@ __device__ __forceinline__ void shared_gate_up_item(const SharedSmall& sh, const
       const float v0 = __uint_as_float(xv[u] << 16), v1 = __uint_as_float(xv[u] & 0xFFFF0000u);
       const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
       const float sc = __fdiv_rn(amax, 448.0f);
-      uint32_t c0 = 0, c1 = 0;
-      if (sc > 0.f) {
-        c0 = e4m3_code(__fdiv_rn(v0, sc));
-        c1 = e4m3_code(__fdiv_rn(v1, sc));
-      }
-      const v2f d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c0 | (c1 << 8), 1.0f, false);
+      const uint32_t c01 = sc > 0.f ? e4m3_pack2(__fdiv_rn(v0, sc), __fdiv_rn(v1, sc)) : 0u;
+      const v2f d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c01, 1.0f, false);
       *reinterpret_cast<double2*>(&sx[m * KW + 128 * bb + 2 * lane]) = make_double2((double)d[0], (double)d[1]);
       if (lane == 0) ssc[m * KB + bb] = sc;
       if (og == 0) {
-        *reinterpret_cast<uint16_t*>(sh.x8 + (size_t)m * H + k0 + 128 * bb + 2 * lane) = (uint16_t)(c0 | (c1 << 8));
+        *reinterpret_cast<uint16_t*>(sh.x8 + (size_t)m * H + k0 + 128 * bb + 2 * lane) = (uint16_t)c01;
         if (lane == 0) sh.xs[(size_t)(k0 / 128 + bb) * M + m] = sc;
       }
     }
@@ -230,7 +226,7 @@ __device__ __forceinline__ void shared_mid_block(const SharedSmall& sh, int m, i
   if (tid < 128) {
     const float amax = fmaxf(u_lds[128], u_lds[129]);
     const float sc = __fdiv_rn(amax, 448.0f);
-    const uint32_t code = sc > 0.f ? e4m3_code(__fdiv_rn(h, sc)) : 0u;
+    const uint32_t code = sc > 0.f ? e4m3_pack2(__fdiv_rn(h, sc), 0.f) & 0xFFu : 0u;
     sh.hq[(size_t)m * Is + col] = (uint8_t)code;
     if (tid == 0) sh.hs[(size_t)c * M + m] = sc;
   }

@@ -10,8 +10,14 @@
 // with the same values. The probes are built so that B is the same in every
 // K position of a column, so neither result depends on how the MFMA spreads
 // K over lanes.
+//
+// qmoe_probe_e4m3_cvt: the hardware fp32 -> E4M3 conversion the quantizers
+// use (v_cvt_pk_fp8_f32) against a reference encoder written from the
+// format's definition (qmoe_probe_e4m3_ref, also callable on the host), on
+// every fp32 of magnitude below 464, of both signs.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <string.h>
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -55,3 +61,68 @@ extern "C" int qmoe_probe_dot128(const void* a, const void* b, void* d8, void* d
                      (float*)d8, (float*)d16);
   return (int)hipGetLastError();
 }
+
+// E4M3FN value of a non-negative code 0..126: k 2^-9 below code 8, else
+// (1 + m/8) 2^(e-7) with exponent field e and mantissa field m.
+__host__ __device__ inline double e4m3_ref_value(uint32_t c) {
+  if (c < 8) return (double)c / 512.0;
+  const int e = (int)(c >> 3) - 7;
+  double v = 1.0 + (double)(c & 7u) / 8.0;
+  for (int i = 0; i < e; ++i) v *= 2.0;
+  for (int i = 0; i > e; --i) v *= 0.5;
+  return v;
+}
+
+// The nearest E4M3 value to |v| (ties to the even code, 448 above 448), the
+// sign bit of v kept: a binary search over the ascending non-negative codes.
+__host__ __device__ inline uint32_t e4m3_ref(float v) {
+  const double a = fabs((double)v);
+  uint32_t bits;
+  memcpy(&bits, &v, 4);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  uint32_t lo = 0, hi = 126;  // the largest code whose value is <= a
+  if (a >= 448.0) return 126u | sign;
+  while (hi - lo > 1) {
+    const uint32_t mid = (lo + hi) / 2;
+    if (e4m3_ref_value(mid) <= a) lo = mid; else hi = mid;
+  }
+  if (e4m3_ref_value(hi) <= a) lo = hi;
+  uint32_t c = lo;
+  if (lo < 126) {
+    const double dlo = a - e4m3_ref_value(lo), dhi = e4m3_ref_value(lo + 1) - a;
+    if (dhi < dlo || (dhi == dlo && (lo & 1u))) c = lo + 1;
+  }
+  return c | sign;
+}
+
+constexpr uint32_t kCvtEnd = 0x43E80000u;  // bits of 464.0f
+
+// thread t: the non-negative bit patterns t, t + n, ... below kCvtEnd, each
+// with both signs; counts[t] mismatches, first[2t] the first one's bits and
+// first[2t+1] its codes (hardware | reference << 16)
+__global__ void e4m3_cvt_kernel(uint32_t* __restrict__ counts, uint32_t* __restrict__ first, int n) {
+  const uint32_t t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= (uint32_t)n) return;
+  uint32_t bad = 0, fb = 0xFFFFFFFFu, fc = 0;
+  for (uint32_t b = t; b < kCvtEnd; b += (uint32_t)n) {
+    const float v = __uint_as_float(b);
+    const uint32_t hw = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, -v, 0, false) & 0xFFFFu;
+    const uint32_t ref = e4m3_ref(v) | (e4m3_ref(-v) << 8);
+    if (hw != ref) {
+      if (!bad) fb = b, fc = hw | (ref << 16);
+      ++bad;
+    }
+  }
+  counts[t] = bad;
+  first[2 * t] = fb;
+  first[2 * t + 1] = fc;
+}
+
+extern "C" int qmoe_probe_e4m3_cvt(void* counts, void* first, int n, void* stream) {
+  if (n <= 0 || n % 256) return -1;
+  hipLaunchKernelGGL(e4m3_cvt_kernel, dim3(n / 256), dim3(256), 0, (hipStream_t)stream, (uint32_t*)counts,
+                     (uint32_t*)first, n);
+  return (int)hipGetLastError();
+}
+
+extern "C" uint32_t qmoe_probe_e4m3_ref(float v) { return e4m3_ref(v); }

@@ -1,10 +1,18 @@
-"""Characterization of the MFMA arithmetic behind the down kernels' design:
+"""Characterization of the hardware arithmetic the kernels rely on.
+
+The MFMA arithmetic behind the down kernels' design:
 the scaled FP8 x FP4 MFMA does not return a 128-element block's dot product
 when a small product sits beside a large one (it drops the small products),
 while the bf16 MFMA on the same values widened to bf16 does (its products are
 exact and its sum is exact while representable in binary32). This is why the
 down GEMMs widen to bf16 (and the shared expert uses int8 digits) although
-the FP8 x FP4 MFMA would need half the MFMA cycles."""
+the FP8 x FP4 MFMA would need half the MFMA cycles.
+
+The fp32 -> E4M3 conversion (v_cvt_pk_fp8_f32) every E4M3 quantizer uses:
+equal to nearest-even rounding onto the E4M3 grid (the reference encoder of
+the probe library, itself checked against the oracle's encoder on the CPU in
+test_probe_e4m3_reference.py) on every fp32 of magnitude below 464, the
+range the quantizers' quotients v / fl32(amax / 448) lie in."""
 
 import ctypes
 import os
@@ -62,3 +70,22 @@ def test_fp8_mfma_drops_small_products_bf16_does_not():
         assert np.all(d8[m] == exact[m] - 7 * vals[m]), f"row {m}: {d8[m, 0]!r}"
     for m in list(range(4, 10)) + [12]:
         assert np.all(d8[m] == exact[m]), f"row {m}: {d8[m, 0]!r}"
+
+
+def test_hw_e4m3_conversion_on_every_fp32_below_464():
+    import torch
+
+    L = ctypes.CDLL(LIB)
+    L.qmoe_probe_e4m3_cvt.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    n = 1 << 20
+    dev = torch.device("cuda", 0)
+    counts = torch.zeros(n, dtype=torch.int32, device=dev)
+    first = torch.zeros(2 * n, dtype=torch.int32, device=dev)
+    st = L.qmoe_probe_e4m3_cvt(counts.data_ptr(), first.data_ptr(), n, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == 0
+    c = counts.cpu().numpy()
+    if c.sum():
+        f = first.cpu().numpy().view(np.uint32).reshape(n, 2)[c > 0][:8]
+        raise AssertionError(f"{int(c.sum())} mismatches; first (bits, hw | ref << 16): "
+                             + ", ".join(f"({b:#010x}, {v:#010x})" for b, v in f))
