@@ -188,9 +188,12 @@ hipError_t enqueue_call(const moe_plan* plan, const CallArgs& a) {
   hipError_t e = small ? launch_route_small(plan, a, ev[0]) : launch_route(plan, a, ev[0]);
   if (e == hipSuccess) e = small ? none(1) : launch_align(plan, a, ev[1]);
   const bool tiles16 = mid_path(M, plan->s.top_k);  // 16-row-tile gate/up, mid quantization on its own
-  if (e == hipSuccess) e = tiles16 ? launch_gate_up(plan, a, ev[2]) : launch_gate_up_big(plan, a, ev[2]);
+  const bool gq = gq_path(plan, M);  // 16-row tiles, the mid quantized inside gate/up
   if (e == hipSuccess)
-    e = !tiles16 ? none(3) : mx ? launch_act_quant_mx(plan, a, ev[3]) : launch_act_quant(plan, a, ev[3]);
+    e = gq ? launch_gate_up_quant(plan, a, ev[2]) : tiles16 ? launch_gate_up(plan, a, ev[2])
+                                                            : launch_gate_up_big(plan, a, ev[2]);
+  if (e == hipSuccess)
+    e = !tiles16 || gq ? none(3) : mx ? launch_act_quant_mx(plan, a, ev[3]) : launch_act_quant(plan, a, ev[3]);
   // (a fused shared expert runs inside the routed launches: no pass of its own)
   if (e == hipSuccess) e = plan->s.shared_I > 0 && !shared_fused(plan, M) ? launch_shared(plan, a, ev[4]) : none(4);
   if (e == hipSuccess)
@@ -260,7 +263,7 @@ int moe_plan_stage_launches(const moe_plan* plan, int64_t M, int stage) {
     case 0: return 1;                             // route + x quantization (+ sort when small; + the shared expert's x when large, its gate/up partials when fused)
     case 1: return small ? 0 : mid_path(M, plan->s.top_k) ? 1 : 3;  // align
     case 2: return 1;                             // gate_up (+ mid quantization when large)
-    case 3: return mid_path(M, plan->s.top_k) ? 1 : 0;  // act_quant (inside gate/up above kMidM)
+    case 3: return mid_path(M, plan->s.top_k) && !gq_path(plan, M) ? 1 : 0;  // act_quant (inside gate/up above kMidM and on the gq path)
     case 4: return plan->s.shared_I > 0 && !shared_fused(plan, M) ? (small ? 4 : 3) : 0;  // shared expert (0: inside the routed launches)
     case 5: return 1;                             // down (+ combine when small, E4M3 mid)
     default: return (small && !mx ? 0 : 1) + (plan->tpx.tp > 0 ? 1 : 0);  // combine (+ the exchange)

@@ -144,7 +144,7 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const float* __restrict_
     __shared__ float u_lds[130];
     const int snb = sh.Is / 128;
     for (int sb = (int)blockIdx.x - routed_blocks; sb < M * snb; sb += (int)gridDim.x - routed_blocks)
-      shared_mid_block(sh, sb / snb, sb % snb, M, H, u_lds);
+      shared_mid_block(sh, sb / snb, sb % snb, M, H, u_lds, threadIdx.x, true);
     return;
   }
   const int nb = I / 128;
@@ -152,6 +152,148 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const float* __restrict_
   for (int wv = blockIdx.x * 4 + (threadIdx.x >> 6); wv < total; wv += routed_blocks * 4) {
     const int row = wv / nb, b = wv % nb;
     quant_mid_rows(h, row, row + 1, 1, I, b, q, s);
+  }
+}
+
+// Gate/up with the mid quantization in the same launch (gq_path): a
+// workgroup of 16 waves owns one 128-column mid block b of one 16-row tile;
+// wave w < 8 takes gate row block w of the block, wave 8 + w up row block w,
+// each over all of K with its weights streamed straight into registers (a
+// ring of R super-steps of 4 K-steps: 1 KB packed pieces, one scale dword a
+// lane per super-step). The tile's x rows (MXFP4 codes and scales, zeros past
+// the tile's end) sit in LDS, rows padded by 16 bytes. The gate and up
+// results meet in LDS; wave m then forms row m's SiLU(g) * u, its 128-block
+// amax and E4M3 codes by the same arithmetic as the mid quantization's own
+// launch. Workgroups past the routed ones form the fused shared expert's mid
+// blocks, four (token, block) items each.
+constexpr int kGqThreads = 1024;
+
+size_t gate_up_quant_lds(int64_t H) { return (size_t)16 * (H / 2 + 16) + (size_t)16 * (H / 32 + 16) + 2 * 16 * 128 * 4; }
+
+template <int KST>
+__global__ __launch_bounds__(kGqThreads) void gate_up_quant_kernel(
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const uint8_t* __restrict__ w13p,
+    const uint8_t* __restrict__ s13p, const int* __restrict__ sorted_entry, const int4* __restrict__ tiles,
+    const int* __restrict__ meta, int I, int k, int tmax, uint8_t* __restrict__ midq, float* __restrict__ mids,
+    int routed_wgs, SharedSmall sh, int M) {
+  constexpr int H = 2048 * KST;                 // KST: 16-byte x chunks a staging thread
+  constexpr int NKS = H / 128, NSS = H / 512;   // K-steps, super-steps (4 K-steps)
+  constexpr int CPR = H / 32, SPR = H / 512;    // 16-byte chunks per x row / scale row
+  constexpr int LX = H / 2 + 16, LS = H / 32 + 16;  // LDS bytes per staged x row / scale row
+  constexpr int R = NSS < 4 ? NSS : 4;          // super-steps of weights in flight
+  extern __shared__ __align__(16) uint8_t gq_lds[];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r = lane & 15, g = lane >> 4;
+  if ((int)blockIdx.x >= routed_wgs) {
+    float* u_lds = reinterpret_cast<float*>(gq_lds) + 132 * (tid >> 8);
+    const int snb = sh.Is / 128, items = M * snb;
+    const int stride = 4 * ((int)gridDim.x - routed_wgs);
+    for (int i0 = 4 * ((int)blockIdx.x - routed_wgs); i0 < items; i0 += stride) {
+      const int it = i0 + (tid >> 8);
+      shared_mid_block(sh, it / snb, it % snb, M, H, u_lds, tid & 255, it < items);
+    }
+    return;
+  }
+  const int nblk = I / 128;
+  const int tile = (int)blockIdx.x / nblk, b = (int)blockIdx.x - tile * nblk;
+  // the tile is read beside meta (index clamped to the tile array's bound)
+  const int4 tl = tiles[min(tile, tmax - 1)];
+  const int nt = meta[0];
+  asm volatile("" ::"s"(nt), "s"(tl.x));
+  if (tile >= nt) return;
+  const int e = tl.x, r0 = tl.y, rows = tl.z - tl.y;
+  uint8_t* xl = gq_lds;                                 // [16][LX] E2M1 codes
+  uint8_t* sl = xl + 16 * LX;                           // [16][LS] E8M0 scales
+  float* gul = reinterpret_cast<float*>(sl + 16 * LS);  // [2][16][128] gate, up
+  // The staging threads' entries first, so that waiting for them does not
+  // wait for the weights (loads complete in issue order); every load is
+  // unconditional (rows past the tile's end read its last row and are
+  // stored as zeros), so no branch makes the compiler wait early.
+  int se[KST];
+#pragma unroll
+  for (int q = 0; q < KST; ++q) se[q] = sorted_entry[r0 + min((tid + kGqThreads * q) / CPR, rows - 1)];
+  const int sse = sorted_entry[r0 + min(tid / SPR, rows - 1)];
+  // wave w: gate row block w (w < 8) or up row block w - 8 of mid block b
+  const size_t rb = (size_t)e * (I / 8) + (wave < 8 ? 0 : I / 16) + 8 * b + (wave & 7);
+  const uint8_t* pw = w13p + rb * NKS * 1024 + 16 * lane;  // + 1024 ks
+  const uint8_t* ps = s13p + rb * NSS * 256 + 4 * lane;    // + 256 ss: byte j is K-step 4 ss + j
+  uint4 wb[R][4];
+  uint32_t ws[R];
+  auto load = [&](int ss, int q) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wb[q][j] = ld16(pw + (size_t)(4 * ss + j) * 1024);
+    ws[q] = ld4(ps + 256 * ss);
+  };
+#pragma unroll
+  for (int q = 0; q < R; ++q) load(q, q);
+  // the tile's x rows into LDS
+  uint4 xv[KST];
+#pragma unroll
+  for (int q = 0; q < KST; ++q) xv[q] = ld16(xq + (size_t)(se[q] / k) * (H / 2) + 16 * ((tid + kGqThreads * q) % CPR));
+  const uint4 sv = ld16(xs + (size_t)(sse / k) * (H / 32) + 16 * (tid % SPR));
+#pragma unroll
+  for (int q = 0; q < KST; ++q) {
+    const int idx = tid + kGqThreads * q, row = idx / CPR;  // 16 CPR = KST x 1024: every idx is a chunk
+    *reinterpret_cast<uint4*>(xl + row * LX + 16 * (idx % CPR)) = row < rows ? xv[q] : make_uint4(0, 0, 0, 0);
+  }
+  if (tid < 16 * SPR)
+    *reinterpret_cast<uint4*>(sl + (tid / SPR) * LS + 16 * (tid % SPR)) =
+        tid / SPR < rows ? sv : make_uint4(0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu);
+  __syncthreads();
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  const uint8_t* xr = xl + r * LX + 16 * g;  // + 64 ks
+  const uint8_t* sr = sl + r * LS;            // + 16 ss: byte 4 j + g is K-step 4 ss + j
+#pragma unroll
+  for (int ss = 0; ss < NSS; ++ss) {
+    const int q = ss % R;
+    const uint4 sa4 = *reinterpret_cast<const uint4*>(sr + 16 * ss);
+    const uint32_t xw[4] = {sa4.x, sa4.y, sa4.z, sa4.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint4 a = *reinterpret_cast<const uint4*>(xr + 64 * (4 * ss + j));
+      acc = mfma_fp4(a, wb[q][j], acc, (xw[j] >> (8 * g)) & 0xFFu, (ws[q] >> (8 * j)) & 0xFFu);
+    }
+    if (ss + R < NSS) load(ss + R, q);  // the slot's next super-step
+  }
+  // D[4 g + i][r]: tile row 4 g + i, column r of the wave's 16 (gate or up) columns
+  float* gw = gul + (wave < 8 ? 0 : 16 * 128) + 16 * (wave & 7) + r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) gw[(4 * g + i) * 128] = acc[i];
+  __syncthreads();
+  // wave m: tile row m, columns 2 lane, 2 lane + 1 of the block
+  const float2 G = *reinterpret_cast<const float2*>(gul + wave * 128 + 2 * lane);
+  const float2 U = *reinterpret_cast<const float2*>(gul + 16 * 128 + wave * 128 + 2 * lane);
+  const float h0 = silu_mul(G.x, U.x), h1 = silu_mul(G.y, U.y);
+  const float amax = wave_max(fmaxf(fabsf(h0), fabsf(h1)));
+  const float sc = __fdiv_rn(amax, 448.0f);
+  const uint32_t c01 = sc > 0.f ? e4m3_pack2(__fdiv_rn(h0, sc), __fdiv_rn(h1, sc)) : 0u;
+  if (wave < rows) {
+    *reinterpret_cast<uint16_t*>(midq + (size_t)(r0 + wave) * I + 128 * b + 2 * lane) = (uint16_t)c01;
+    if (lane == 0) mids[(size_t)(r0 + wave) * nblk + b] = sc;
+  }
+}
+
+hipError_t launch_gate_up_quant(const moe_plan* p, const CallArgs& a, Ev ev) {
+  const int64_t H = p->s.H, I = p->s.I, n = a.M * p->s.top_k;
+  const int tmax = (int)((n + std::min<int64_t>(p->s.E, n) * (kTileRows - 1) + kTileRows - 1) / kTileRows);
+  const int routed = tmax * (int)(I / 128);
+  const SharedSmall sh = shared_small(p, a.M);  // the fused shared expert's h: four 128-blocks a workgroup
+  const int sh_wgs = sh.part ? (int)((a.M * (sh.Is / 128) + 3) / 4) : 0;
+  const size_t lds = std::max(gate_up_quant_lds(H), (size_t)4 * 132 * 4);
+  if (H % 2048 || H > kGqMaxH || lds > 160 * 1024) return hipErrorInvalidValue;
+  auto go = [&](auto kern) {
+    return launch_k(kern, dim3(routed + sh_wgs), dim3(kGqThreads), lds, a.stream, ev, wsp<uint8_t>(p, p->L.xq),
+                    wsp<uint8_t>(p, p->L.xs), reinterpret_cast<const uint8_t*>(a.w13),
+                    reinterpret_cast<const uint8_t*>(a.s13), wsp<int>(p, p->L.sorted_entry), wsp<int4>(p, p->X.tiles),
+                    wsp<int>(p, p->X.meta), (int)I, (int)p->s.top_k, tmax, wsp<uint8_t>(p, p->L.midq),
+                    wsp<float>(p, p->L.mids), routed, sh, (int)a.M);
+  };
+  switch (H / 2048) {
+    case 1: return go(gate_up_quant_kernel<1>);
+    case 2: return go(gate_up_quant_kernel<2>);
+    case 3: return go(gate_up_quant_kernel<3>);
+    case 4: return go(gate_up_quant_kernel<4>);
+    default: return hipErrorInvalidValue;
   }
 }
 

@@ -120,6 +120,21 @@ hipError_t launch_route_small(const moe_plan* p, const CallArgs& a, Ev ev);
 hipError_t launch_route(const moe_plan* p, const CallArgs& a, Ev ev);
 hipError_t launch_align(const moe_plan* p, const CallArgs& a, Ev ev);
 hipError_t launch_gate_up(const moe_plan* p, const CallArgs& a, Ev ev);
+// Mid-range calls with at least 8 entries per expert on average (M k >= 8 E),
+// the E4M3 mid and H a multiple of 2048 up to kGqMaxH (the tile's x rows
+// staged whole in LDS): gate/up and the mid quantization in one launch
+// (gate_up.hip), no h and no act_quant launch. Its work unit streams a whole
+// 128-column mid block's weights (786 KB at H 6144) at up to ~45 GB/s per
+// CU: with fewer entries the units are too few, or too unequal, to keep the
+// chip busy, and the 16-column items of the two-launch path win (c1 41 us
+// against 34; TP8 M 32..128 hot and mixed +1..+12 us; M 256: hot 73.5 ->
+// 64.7, mixed 171 -> 169, spread 163 -> 158 us).
+constexpr int kGqMaxH = 8192;
+inline bool gq_path(const moe_plan* p, int64_t M) {
+  return mid_path(M, p->s.top_k) && M * p->s.top_k >= 8 * p->s.E && p->mid_fmt == MOE_MID_E4M3 &&
+         p->s.H % 2048 == 0 && p->s.H <= kGqMaxH;
+}
+hipError_t launch_gate_up_quant(const moe_plan* p, const CallArgs& a, Ev ev);
 hipError_t launch_act_quant(const moe_plan* p, const CallArgs& a, Ev ev);
 // small M: down and the combine in one launch; y stays on chip
 int down_combine_cols(int H, int cus);

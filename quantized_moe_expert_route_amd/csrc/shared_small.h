@@ -194,12 +194,20 @@ __device__ __forceinline__ void shared_gate_up_item(const SharedSmall& sh, const
   __syncthreads();  // the LDS is reused by the workgroup's next item
 }
 
-// Token m, columns [128 c, 128 c + 128) of h on a workgroup of 256 threads:
-// thread t adds the partials of column 128 c + t % 128 of gate (t < 128) or
-// of up in block order, rounded to fp32; then SiLU(g) * u and the block's
-// E4M3 codes and scale (the routed mid's rule). `u_lds` holds 130 floats.
-__device__ __forceinline__ void shared_mid_block(const SharedSmall& sh, int m, int c, int M, int H, float* u_lds) {
-  const int tid = threadIdx.x;
+// Token m, columns [128 c, 128 c + 128) of h on a group of 256 threads (tid
+// 0..255; the workgroup's barriers are reached by all its threads, valid or
+// not): thread t adds the partials of column 128 c + t % 128 of gate
+// (t < 128) or of up in block order, rounded to fp32; then SiLU(g) * u and
+// the block's E4M3 codes and scale (the routed mid's rule). `u_lds` holds
+// 130 floats. A group without an item (valid false) only takes the barriers.
+__device__ __forceinline__ void shared_mid_block(const SharedSmall& sh, int m, int c, int M, int H, float* u_lds,
+                                                 int tid, bool valid) {
+  if (!valid) {
+    __syncthreads();
+    __syncthreads();
+    __syncthreads();
+    return;
+  }
   const int nkb = H / 128, Is = sh.Is;
   const int col = 128 * c + (tid & 127);
   const double* p = sh.part + (size_t)m * nkb * (2 * Is) + (tid >= 128 ? Is : 0) + col;

@@ -175,6 +175,12 @@ SMALL = [
     (72, 8192, 8, 128, 2, "normal", 0),        # H past 6144: x scales staged in two parts
     (80, 1536, 8, 128, 2, "normal", 128),      # shared expert, H = 3 x 512
     (66, 9216, 4, 128, 2, "normal", 128),      # x rows past 8192: the route reads them in two chunks
+    # at least 8 entries per expert (M k >= 8 E) and H a multiple of 2048 up to
+    # 8192: gate/up and the mid quantization in one launch
+    (16, 2048, 16, 256, 8, "ties", 256),       # with the fused shared expert's mid blocks (32 of them)
+    (13, 4096, 8, 384, 8, "normal", 128),      # three mid blocks; 13 shared mid blocks, 4 to a workgroup
+    (200, 6144, 16, 256, 8, "zipf", 0),        # ragged tiles of a skewed mid-range call
+    (8, 2048, 1, 128, 1, "normal", 0),         # one expert, one tile
 ]
 
 
