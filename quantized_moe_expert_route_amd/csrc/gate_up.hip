@@ -165,12 +165,13 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const float* __restrict_
 // results meet in LDS; wave m then forms row m's SiLU(g) * u, its 128-block
 // amax and E4M3 codes by the same arithmetic as the mid quantization's own
 // launch. Workgroups past the routed ones form the fused shared expert's mid
-// blocks, four (token, block) items each.
+// blocks, four (token, block) items each. With the MXFP4 mid the epilogue
+// forms the mid per 32 columns instead (E8M0 scale + E2M1 codes).
 constexpr int kGqThreads = 1024;
 
 size_t gate_up_quant_lds(int64_t H) { return (size_t)16 * (H / 2 + 16) + (size_t)16 * (H / 32 + 16) + 2 * 16 * 128 * 4; }
 
-template <int KST>
+template <int KST, bool MX>
 __global__ __launch_bounds__(kGqThreads) void gate_up_quant_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, const uint8_t* __restrict__ w13p,
     const uint8_t* __restrict__ s13p, const int* __restrict__ sorted_entry, const int4* __restrict__ tiles,
@@ -264,12 +265,30 @@ __global__ __launch_bounds__(kGqThreads) void gate_up_quant_kernel(
   const float2 G = *reinterpret_cast<const float2*>(gul + wave * 128 + 2 * lane);
   const float2 U = *reinterpret_cast<const float2*>(gul + 16 * 128 + wave * 128 + 2 * lane);
   const float h0 = silu_mul(G.x, U.x), h1 = silu_mul(G.y, U.y);
-  const float amax = wave_max(fmaxf(fabsf(h0), fabsf(h1)));
-  const float sc = __fdiv_rn(amax, 448.0f);
-  const uint32_t c01 = sc > 0.f ? e4m3_pack2(__fdiv_rn(h0, sc), __fdiv_rn(h1, sc)) : 0u;
-  if (wave < rows) {
-    *reinterpret_cast<uint16_t*>(midq + (size_t)(r0 + wave) * I + 128 * b + 2 * lane) = (uint16_t)c01;
-    if (lane == 0) mids[(size_t)(r0 + wave) * nblk + b] = sc;
+  if (MX) {
+    // MXFP4 mid: the 16 lanes of a 32-column block form its E8M0 scale from
+    // the largest |h| bits and the E2M1 codes of h 2^(127 - s) (the rule of
+    // the separate MXFP4 mid quantization); rows of I/2 code bytes and I/32
+    // scale bytes
+    uint32_t am = max(__float_as_uint(h0) & 0x7FFFFFFFu, __float_as_uint(h1) & 0x7FFFFFFFu);
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) am = max(am, (uint32_t)__shfl_xor((int)am, o, 64));
+    const uint32_t sc = mx_scale_code_f32(am);
+    const int sh = 127 - (int)sc;
+    const uint32_t code = e2m1_code(ldexpf(h0, sh)) | (e2m1_code(ldexpf(h1, sh)) << 4);
+    if (wave < rows) {
+      midq[(size_t)(r0 + wave) * (I / 2) + 64 * b + lane] = (uint8_t)code;
+      if ((lane & 15) == 0)
+        reinterpret_cast<uint8_t*>(mids)[(size_t)(r0 + wave) * (I / 32) + 4 * b + (lane >> 4)] = (uint8_t)sc;
+    }
+  } else {
+    const float amax = wave_max(fmaxf(fabsf(h0), fabsf(h1)));
+    const float sc = __fdiv_rn(amax, 448.0f);
+    const uint32_t c01 = sc > 0.f ? e4m3_pack2(__fdiv_rn(h0, sc), __fdiv_rn(h1, sc)) : 0u;
+    if (wave < rows) {
+      *reinterpret_cast<uint16_t*>(midq + (size_t)(r0 + wave) * I + 128 * b + 2 * lane) = (uint16_t)c01;
+      if (lane == 0) mids[(size_t)(r0 + wave) * nblk + b] = sc;
+    }
   }
 }
 
@@ -288,13 +307,17 @@ hipError_t launch_gate_up_quant(const moe_plan* p, const CallArgs& a, Ev ev) {
                     wsp<int>(p, p->X.meta), (int)I, (int)p->s.top_k, tmax, wsp<uint8_t>(p, p->L.midq),
                     wsp<float>(p, p->L.mids), routed, sh, (int)a.M);
   };
-  switch (H / 2048) {
-    case 1: return go(gate_up_quant_kernel<1>);
-    case 2: return go(gate_up_quant_kernel<2>);
-    case 3: return go(gate_up_quant_kernel<3>);
-    case 4: return go(gate_up_quant_kernel<4>);
-    default: return hipErrorInvalidValue;
-  }
+  auto pick = [&](auto mxc) {
+    constexpr bool MXV = decltype(mxc)::value;
+    switch (H / 2048) {
+      case 1: return go(gate_up_quant_kernel<1, MXV>);
+      case 2: return go(gate_up_quant_kernel<2, MXV>);
+      case 3: return go(gate_up_quant_kernel<3, MXV>);
+      case 4: return go(gate_up_quant_kernel<4, MXV>);
+      default: return hipErrorInvalidValue;
+    }
+  };
+  return p->mid_fmt == MOE_MID_MXFP4 ? pick(std::true_type()) : pick(std::false_type());
 }
 
 hipError_t launch_gate_up(const moe_plan* p, const CallArgs& a, Ev ev) {

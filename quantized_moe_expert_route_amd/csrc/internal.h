@@ -120,8 +120,8 @@ hipError_t launch_route_small(const moe_plan* p, const CallArgs& a, Ev ev);
 hipError_t launch_route(const moe_plan* p, const CallArgs& a, Ev ev);
 hipError_t launch_align(const moe_plan* p, const CallArgs& a, Ev ev);
 hipError_t launch_gate_up(const moe_plan* p, const CallArgs& a, Ev ev);
-// Mid-range calls with at least 8 entries per expert on average (M k >= 8 E),
-// the E4M3 mid and H a multiple of 2048 up to kGqMaxH (the tile's x rows
+// Mid-range calls with at least 8 entries per expert on average (M k >= 8 E)
+// and H a multiple of 2048 up to kGqMaxH (the tile's x rows
 // staged whole in LDS): gate/up and the mid quantization in one launch
 // (gate_up.hip), no h and no act_quant launch. Its work unit streams a whole
 // 128-column mid block's weights (786 KB at H 6144) at up to ~45 GB/s per
@@ -131,8 +131,7 @@ hipError_t launch_gate_up(const moe_plan* p, const CallArgs& a, Ev ev);
 // 64.7, mixed 171 -> 169, spread 163 -> 158 us).
 constexpr int kGqMaxH = 8192;
 inline bool gq_path(const moe_plan* p, int64_t M) {
-  return mid_path(M, p->s.top_k) && M * p->s.top_k >= 8 * p->s.E && p->mid_fmt == MOE_MID_E4M3 &&
-         p->s.H % 2048 == 0 && p->s.H <= kGqMaxH;
+  return mid_path(M, p->s.top_k) && M * p->s.top_k >= 8 * p->s.E && p->s.H % 2048 == 0 && p->s.H <= kGqMaxH;
 }
 hipError_t launch_gate_up_quant(const moe_plan* p, const CallArgs& a, Ev ev);
 hipError_t launch_act_quant(const moe_plan* p, const CallArgs& a, Ev ev);

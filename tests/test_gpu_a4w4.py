@@ -96,6 +96,9 @@ SHAPES = [
     (257, 512, 16, 128, 4, "normal", 0),       # above 256 tokens: the mid quantized inside the 64-row gate/up
     (300, 1024, 32, 256, 8, "zipf", 0),        # large path, skewed
     (600, 512, 8, 512, 2, "normal", 128),      # large path, I = 512, with the shared expert
+    # M k >= 8 E, H a multiple of 2048 up to 8192: gate/up and the MXFP4 mid in one launch
+    (16, 2048, 16, 256, 8, "ties", 0),
+    (100, 4096, 8, 384, 4, "zipf", 0),         # three mid blocks, skewed tiles
 ]
 
 
