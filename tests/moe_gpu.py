@@ -53,6 +53,13 @@ def run(d, plan=None, g=None, M=None):
     return out[:M].cpu().numpy().view(np.uint16), read_intermediates(plan, s, M)
 
 
+def y_written(plan, M):
+    """Whether the call wrote y: its combine stage has a launch of its own
+    (besides the tensor-parallel exchange, when that is on)."""
+    tp = 1 if getattr(plan, "_tpx", None) is not None else 0
+    return plan.stage_launches(M)[6] > tp
+
+
 def read_intermediates(plan, s, M):
     import torch
 
@@ -68,7 +75,9 @@ def read_intermediates(plan, s, M):
         "xs": v("xs", torch.uint8, (M, H // 32)),
         "midq": v("midq", torch.uint8, (n, I)),
         "mids": v("mids", torch.float32, (n, I // 128)),
-        "y": v("y", torch.float32, (n, H)),
+        # y (the down output per entry) is in the workspace only when the
+        # combine has a launch of its own (else it runs inside the down launch)
+        "y": v("y", torch.float32, (n, H)) if y_written(plan, M) else None,
     }
     fused = shared_fused(s, M)
     if s.shared_I:
@@ -82,7 +91,7 @@ def read_intermediates(plan, s, M):
             r["sh_y"] = v("sh_y", torch.float32, (M, H))
         r["sh_xs"] = v("sh_xs", torch.float32, (H // 128, M)).t()  # stored K-block major
         r["sh_hs"] = v("sh_hs", torch.float32, (Is // 128, M)).t()
-    out = {key: t.cpu().numpy() for key, t in r.items()}
+    out = {key: None if t is None else t.cpu().numpy() for key, t in r.items()}
     if not fused:
         for key in ("sh_xq", "sh_hq"):
             if key in out:

@@ -44,7 +44,7 @@ def test_extreme_scales(M):
     _check_xq(gi, ref)
     assert (ref["xs"] == 0).any() and (d["s2"] == 0).any(), "the inputs reach scale byte 0"
     _check_mid(gi["midq"], gi["mids"], ref["midq"], ref["mids"])
-    if M > 16:
+    if gi["y"] is not None:  # (the combine inside the down launch: no y)
         _check_y(gi["y"], ref["y"])
     nd = _check_out_by_group(gout, ref["out"], M)
     print(f"M={M}: {nd} differing bf16 elements in all")
