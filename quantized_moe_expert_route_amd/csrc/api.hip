@@ -175,9 +175,10 @@ hipError_t enqueue_call(const moe_plan* plan, const CallArgs& a) {
   // tiles; the mid quantization; down with the combine (a workgroup owns 16
   // output columns of every slot, so the slot results never leave it).
   // Above kSmallM: routing spread over the GPU, a second launch sorts;
-  // gate/up on 16-row tiles and the mid quantization up to kMidM tokens,
-  // above on 64-row tiles with the mid quantization inside (every item owns
-  // whole mid blocks); down to y in HBM; the combine.
+  // gate/up on 16-row tiles and the mid quantization up to kMidM tokens (in
+  // one launch where M k >= 8 E: gq_path), above on 64-row tiles with the
+  // mid quantization inside (every item owns whole mid blocks); down to y in
+  // HBM; the combine.
   // With the MXFP4 mid: its own quantization (inside the 64-row-tile gate/up
   // above kMidM) and down kernel on the 16-row tiles, then the combine, for
   // every M.

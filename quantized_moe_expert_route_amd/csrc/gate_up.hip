@@ -7,7 +7,9 @@
 // (Modifications table, row "mid as FP8 once": each 128-element mid block is
 // quantized to FP8 once with its scale, and the down GEMM reads those bytes).
 //
-// Work item = (tile of up to 16 sorted rows of one expert, 16 columns of I).
+// gate_up_m16_kernel (its mid quantized by act_quant_kernel, a launch of
+// its own): work item = (tile of up to 16 sorted rows of one expert, 16
+// columns of I).
 // A workgroup of 4 waves computes the gate and the up columns of the item,
 // each wave a quarter of the K super-steps (4 K-steps of 128); the four
 // partial sums are added in wave order through LDS. In K-step ks lane
@@ -15,7 +17,8 @@
 // for x and for the weights alike, so every MFMA pairs matching K. The
 // weights come packed (moe_pack_w13): a K-step of the item's 16 gate (or up)
 // rows is 1 KB contiguous in lane order, and a row block's scales of a
-// super-step are one dword per lane.
+// super-step are one dword per lane. gate_up_quant_kernel (below) does
+// gate/up and the mid quantization in one launch on larger work items.
 #include "common.h"
 #include "internal.h"
 #include "shared_small.h"
