@@ -44,9 +44,10 @@ __global__ __launch_bounds__(256) void act_quant_mx_kernel(const float* __restri
 
 // down on MXFP4 x MXFP4, w2 packed by moe_pack_w2. Work item = (tile of RB
 // x 16 sorted rows, group of cbg 64-column blocks): 16-row tiles up to
-// kMidM tokens, 64-row tiles above (RB = 4: each weight fragment then feeds
-// four MFMA row blocks instead of one). The workgroup stages the tile's mid
-// rows (RB x 16 x I/2 bytes, contiguous in sorted order) and scale bytes in
+// kSmallM tokens, 64-row tiles above (RB = 4: each weight fragment then feeds
+// four MFMA row blocks instead of one). The workgroup stages the row blocks
+// of the tile that hold rows (up to RB x 16 x I/2 bytes, contiguous in
+// sorted order) and their scale bytes in
 // LDS with one coalesced read; each wave then holds its A fragments in
 // registers and streams the B fragments of its 16 columns of every column
 // block in the group: in K-step ks lane 16 g + r supplies MX block 4 ks + g
@@ -80,25 +81,25 @@ __global__ __launch_bounds__(256) void down_fp4_kernel(const uint8_t* __restrict
     const int cg = (int)(w / nt), ti = (int)(w - (int64_t)cg * nt);
     const int4 tl = tiles[ti];  // {expert, row_begin, row_end, 0}
     __syncthreads();  // the previous item's LDS reads are done
-    // rows past the tile's end repeat its last row (their results are dropped)
+    // rows past the tile's end repeat its last row (their results are
+    // dropped); only the row blocks that hold rows are staged
+    const int nrb = min(RB, (tl.z - tl.y + 15) / 16);
     constexpr int cpr = Ib / 16;  // 16-byte chunks per row
 #pragma unroll
     for (int q = 0; q < (TR * cpr + 255) / 256; ++q) {
       const int idx = tid + 256 * q;
-      if (idx < TR * cpr) {
+      if (idx < 16 * nrb * cpr) {
         const int rr = idx / cpr, c = idx - rr * cpr;
         const int row = min(tl.y + rr, tl.z - 1);
         *reinterpret_cast<uint4*>(sm_a + rr * LDA + 16 * c) = ld16(midq + (size_t)row * Ib + 16 * c);
       }
     }
-    for (int idx = tid; idx < TR * Isc; idx += 256) {
+    for (int idx = tid; idx < 16 * nrb * Isc; idx += 256) {
       const int rr = idx / Isc, c = idx - rr * Isc;
       sm_s[rr * 16 + c] = mids[(size_t)min(tl.y + rr, tl.z - 1) * Isc + c];
     }
     __syncthreads();
-    // row blocks of the tile that hold rows (a 64-row tile of a small expert
-    // computes only its first ones)
-    const int nrb = min(RB, (tl.z - tl.y + 15) / 16);
+    // (a 64-row tile of a small expert computes only its first row blocks)
     uint4 a[RB][NKS];
     uint32_t sa[RB][NKS];
     int ent[RB][4];
@@ -163,7 +164,13 @@ hipError_t launch_act_quant_mx(const moe_plan* p, const CallArgs& a, Ev ev) {
 hipError_t launch_down_fp4(const moe_plan* p, const CallArgs& a, Ev ev) {
   const int H = (int)p->s.H, I = (int)p->s.I;
   const int64_t n = a.M * p->s.top_k;
-  const bool big = !mid_path(a.M, p->s.top_k);  // 64-row tiles above kMidM tokens
+  // 64-row tiles above kSmallM tokens: above kMidM in the tile array, from
+  // the one-workgroup sort of mid-range calls where the E4M3 down keeps its
+  // items (their count in meta[3]); 16-row tiles for the small path
+  const bool big = !small_path(a.M, p->s.top_k);
+  const bool mid = big && mid_path(a.M, p->s.top_k);
+  const int4* tiles = mid ? wsp<int4>(p, p->X.dn_items) : wsp<int4>(p, p->X.tiles);
+  const int* meta = wsp<int>(p, p->X.meta) + (mid ? 3 : 0);
   const int tr = big ? kFp4BigRows : kTileRows;
   const int64_t t16 = (n + std::min<int64_t>(p->s.E, n) * (tr - 1) + tr - 1) / tr;
   const int ncb = H / 64;
@@ -176,7 +183,7 @@ hipError_t launch_down_fp4(const moe_plan* p, const CallArgs& a, Ev ev) {
     return launch_k(kern, dim3(blocks), dim3(256), 0, a.stream, ev, wsp<uint8_t>(p, p->L.midq),
                     wsp<uint8_t>(p, p->L.mids), reinterpret_cast<const uint8_t*>(a.w2),
                     reinterpret_cast<const uint32_t*>(a.s2), wsp<int>(p, p->L.sorted_entry),
-                    wsp<int4>(p, p->X.tiles), wsp<int>(p, p->X.meta), H, cbg, wsp<float>(p, p->L.y));
+                    tiles, meta, H, cbg, wsp<float>(p, p->L.y));
   };
   switch (I / 128) {
     case 1: return big ? go(down_fp4_kernel<1, 4>) : go(down_fp4_kernel<1, 1>);

@@ -513,7 +513,8 @@ __global__ __launch_bounds__(1024) void align_mid_kernel(uint32_t* __restrict__ 
                                                          const int* __restrict__ topk_ids, int n, int k, int E,
                                                          int* __restrict__ count, int* __restrict__ offset,
                                                          int* __restrict__ sorted_entry, int4* __restrict__ tiles,
-                                                         int* __restrict__ meta, int n_nc, int4* __restrict__ dn_items) {
+                                                         int* __restrict__ meta, int n_nc, int4* __restrict__ dn_items,
+                                                         int fp4_tiles) {
   __shared__ uint32_t s_bm[1024 * kMidWords];
   __shared__ int s_off[1025];
   __shared__ int s_toff[1025];
@@ -530,14 +531,19 @@ __global__ __launch_bounds__(1024) void align_mid_kernel(uint32_t* __restrict__ 
     for (int w = 0; w < words; ++w) c += __popc(s_bm[tid * words + w]);
   write_offsets_tiles(c, E, s_off, s_tmp, count, offset, tiles, meta, true);  // ends with a barrier
   int n_tb;
-  const int tb = (c + kBigRows - 1) / kBigRows;
+  // the E4M3 down's items are on tiles of kBigRows rows; with the MXFP4 mid
+  // the down runs on tiles of kFp4BigRows rows instead, written to the same
+  // place ({expert, row_begin, row_end, 0}; their count in meta[3])
+  const int tr = fp4_tiles ? kFp4BigRows : kBigRows;
+  const int tb = (c + tr - 1) / tr;
   const int t0 = block_exclusive_scan(tb, s_tmp, &n_tb);
   if (tid < E) s_toff[tid] = t0;
   if (tid == 0) {
     s_off[E] = n;
     s_toff[E] = n_tb;
     meta[1] = 0;
-    meta[2] = n_tb * n_nc;
+    meta[2] = fp4_tiles ? 0 : n_tb * n_nc;
+    meta[3] = fp4_tiles ? n_tb : 0;
   }
   __syncthreads();
   for (int i = tid; i < n; i += 1024) {
@@ -546,6 +552,14 @@ __global__ __launch_bounds__(1024) void align_mid_kernel(uint32_t* __restrict__ 
     int rank = __popc(row[t >> 5] & ((1u << (t & 31)) - 1u));
     for (int w = 0; w < (t >> 5); ++w) rank += __popc(row[w]);
     sorted_entry[s_off[e] + rank] = i;
+  }
+  if (fp4_tiles) {
+    if (tid < E)
+      for (int i = 0; i < tb; ++i) {
+        const int r0 = s_off[tid] + i * kFp4BigRows;
+        dn_items[t0 + i] = make_int4(tid, r0, min(r0 + kFp4BigRows, s_off[tid] + c), 0);
+      }
+    return;
   }
   const int n_dn = n_tb * n_nc;
   for (int i = tid; i < n_dn; i += 1024) dn_items[i] = big_item(i, E, n_nc, kBigRows, s_toff, s_off);
@@ -621,7 +635,8 @@ hipError_t launch_align(const moe_plan* p, const CallArgs& a, Ev ev) {
     return launch_k(align_mid_kernel, dim3(1), dim3(1024), 0, a.stream, ev, wsp<uint32_t>(p, p->X.bitmap), words,
                     wsp<int>(p, p->L.topk_ids), (int)n, (int)p->s.top_k, (int)p->s.E, wsp<int>(p, p->L.count),
                     wsp<int>(p, p->L.offset), wsp<int>(p, p->L.sorted_entry), wsp<int4>(p, p->X.tiles),
-                    wsp<int>(p, p->X.meta), (int)(p->s.H / kDownItemCols), wsp<int4>(p, p->X.dn_items));
+                    wsp<int>(p, p->X.meta), (int)(p->s.H / kDownItemCols), wsp<int4>(p, p->X.dn_items),
+                    p->mid_fmt == MOE_MID_MXFP4 ? 1 : 0);
   hipError_t e = launch_k(align_rows_kernel, dim3((unsigned)p->s.E), dim3(256), 0, a.stream, Ev{ev.start, nullptr},
                           wsp<uint32_t>(p, p->X.bitmap), words, wsp<int2>(p, p->X.pw), wsp<int>(p, p->L.count));
   if (e != hipSuccess) return e;
