@@ -561,8 +561,18 @@ __global__ __launch_bounds__(1024) void align_mid_kernel(uint32_t* __restrict__ 
       }
     return;
   }
-  const int n_dn = n_tb * n_nc;
-  for (int i = tid; i < n_dn; i += 1024) dn_items[i] = big_item(i, E, n_nc, kBigRows, s_toff, s_off);
+  // the down items, a thread per (expert, column block): the expert's items
+  // fill [toff[e] n_nc, toff[e+1] n_nc) in the order (column block, row tile)
+  // of big_item, without a search per item
+  for (int pr = tid; pr < E * n_nc; pr += 1024) {
+    const int e = pr / n_nc, b = pr - e * n_nc;
+    const int nte = s_toff[e + 1] - s_toff[e];
+    int4* dst = dn_items + (size_t)s_toff[e] * n_nc + (size_t)b * nte;
+    for (int mt = 0; mt < nte; ++mt) {
+      const int r0 = s_off[e] + mt * kBigRows;
+      dst[mt] = make_int4(e, r0, min(r0 + kBigRows, s_off[e + 1]), b);
+    }
+  }
 }
 
 __global__ void zero_kernel(uint4* p, size_t n16) {
