@@ -358,25 +358,40 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
 
 // out[t, c..c+3]: float64 products and sum in slot order (+ shared), then
 // bf16. A thread per 4 columns: consecutive lanes read consecutive 16 bytes
-// of a y row, so each load instruction covers whole cache lines.
+// of a y row, so each load instruction covers whole cache lines. The K slots'
+// loads all go out before the first product (K is the call's top-k: a loop
+// over a runtime count waited for each slot's load before the next).
+template <int K>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, const float* __restrict__ w,
-                                                      const float* __restrict__ ys, int M, int H, int k,
+                                                      const float* __restrict__ ys, int M, int H,
                                                       uint16_t* __restrict__ out, double* __restrict__ partial) {
   const int per_tok = H / 4;
   const int64_t total = (int64_t)M * per_tok;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
     const int t = (int)(i / per_tok);
     const int c = (int)(i % per_tok) * 4;
-    double acc[4] = {0, 0, 0, 0};
-    for (int j = 0; j < k; ++j) {
-      const double wj = (double)w[(size_t)t * k + j];
+    // the shared expert's output (without one: slot 0's y again, which the
+    // load below reads anyway; unconditional, so no branch waits for it)
+    const float* pb = ys ? ys + (size_t)t * H + c : y + (size_t)t * K * H + c;
+    const float4 b = *reinterpret_cast<const float4*>(pb);
+    float wv[K];
+    v4f a[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      wv[j] = w[(size_t)t * K + j];
       // y is read once: non-temporal loads keep it from displacing cached lines
-      const v4f a = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(y + ((size_t)t * k + j) * H + c));
-      acc[0] += wj * (double)a[0]; acc[1] += wj * (double)a[1]; acc[2] += wj * (double)a[2]; acc[3] += wj * (double)a[3];
+      a[j] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(y + ((size_t)t * K + j) * H + c));
     }
-    if (ys) {
-      const float4 a = *reinterpret_cast<const float4*>(ys + (size_t)t * H + c);
-      acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+    asm volatile("" ::"v"(b.x), "v"(b.y), "v"(b.z), "v"(b.w));  // keeps b's load with the others
+    double acc[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const double wj = (double)wv[j];
+      acc[0] += wj * (double)a[j][0]; acc[1] += wj * (double)a[j][1];
+      acc[2] += wj * (double)a[j][2]; acc[3] += wj * (double)a[j][3];
+    }
+    if (ys) {  // the shared expert's output, the last term
+      acc[0] += b.x; acc[1] += b.y; acc[2] += b.z; acc[3] += b.w;
     }
     if (partial) {  // the sum before its rounding, for the tensor-parallel exchange
       double2* pp = reinterpret_cast<double2*>(partial + (size_t)t * H + c);
@@ -448,9 +463,29 @@ hipError_t launch_combine(const moe_plan* p, const CallArgs& a, Ev ev) {
   const int64_t total = a.M * (H / 4);
   const int blocks = (int)std::min<int64_t>((total + 255) / 256, 8192);
   const float* ys = p->s.shared_I > 0 ? wsp<float>(p, p->L.sh_y) : nullptr;
-  return launch_k(combine_kernel, dim3(blocks), dim3(256), 0, a.stream, ev, wsp<float>(p, p->L.y),
-                  wsp<float>(p, p->L.topk_w), ys, (int)a.M, H, (int)p->s.top_k, reinterpret_cast<uint16_t*>(a.out),
-                  tp_own_partial(p));
+  auto go = [&](auto kern) {
+    return launch_k(kern, dim3(blocks), dim3(256), 0, a.stream, ev, wsp<float>(p, p->L.y), wsp<float>(p, p->L.topk_w),
+                    ys, (int)a.M, H, reinterpret_cast<uint16_t*>(a.out), tp_own_partial(p));
+  };
+  switch (p->s.top_k) {
+    case 1: return go(combine_kernel<1>);
+    case 2: return go(combine_kernel<2>);
+    case 3: return go(combine_kernel<3>);
+    case 4: return go(combine_kernel<4>);
+    case 5: return go(combine_kernel<5>);
+    case 6: return go(combine_kernel<6>);
+    case 7: return go(combine_kernel<7>);
+    case 8: return go(combine_kernel<8>);
+    case 9: return go(combine_kernel<9>);
+    case 10: return go(combine_kernel<10>);
+    case 11: return go(combine_kernel<11>);
+    case 12: return go(combine_kernel<12>);
+    case 13: return go(combine_kernel<13>);
+    case 14: return go(combine_kernel<14>);
+    case 15: return go(combine_kernel<15>);
+    case 16: return go(combine_kernel<16>);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace qmoe

@@ -520,6 +520,11 @@ __global__ __launch_bounds__(1024) void align_mid_kernel(uint32_t* __restrict__ 
   __shared__ int s_toff[1025];
   __shared__ int s_tmp[64];
   const int tid = threadIdx.x;
+  // the entries' experts are read beside the bitmap (n <= kMidM * 16)
+  constexpr int kPre = kMidM * 16 / 1024;
+  int pre_e[kPre];
+#pragma unroll
+  for (int q = 0; q < kPre; ++q) pre_e[q] = topk_ids[min(tid + 1024 * q, n - 1)];
   for (int i = tid; i < E * words; i += 1024) {
     const uint32_t v = bitmap[i];
     s_bm[i] = v;
@@ -546,8 +551,11 @@ __global__ __launch_bounds__(1024) void align_mid_kernel(uint32_t* __restrict__ 
     meta[3] = fp4_tiles ? n_tb : 0;
   }
   __syncthreads();
-  for (int i = tid; i < n; i += 1024) {
-    const int e = topk_ids[i], t = i / k;
+#pragma unroll
+  for (int q = 0; q < kPre; ++q) {
+    const int i = tid + 1024 * q;
+    if (i >= n) break;
+    const int e = pre_e[q], t = i / k;
     const uint32_t* row = s_bm + e * words;
     int rank = __popc(row[t >> 5] & ((1u << (t & 31)) - 1u));
     for (int w = 0; w < (t >> 5); ++w) rank += __popc(row[w]);
