@@ -99,6 +99,7 @@ SHAPES = [
     # M k >= 8 E, H a multiple of 2048 up to 8192: gate/up and the MXFP4 mid in one launch
     (16, 2048, 16, 256, 8, "ties", 0),
     (100, 4096, 8, 384, 4, "zipf", 0),         # three mid blocks, skewed tiles
+    (64, 2048, 8, 512, 2, "normal", 0),        # I = 512: four mid blocks a tile
 ]
 
 

@@ -176,6 +176,7 @@ SMALL = [
     (13, 4096, 8, 384, 8, "normal", 128),      # three mid blocks; 13 shared mid blocks, 4 to a workgroup
     (200, 6144, 16, 256, 8, "zipf", 0),        # ragged tiles of a skewed mid-range call
     (8, 2048, 1, 128, 1, "normal", 0),         # one expert, one tile
+    (64, 2048, 8, 512, 2, "normal", 0),        # I = 512: four mid blocks a tile
 ]
 
 
