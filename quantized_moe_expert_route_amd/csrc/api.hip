@@ -65,7 +65,6 @@ Layout make_layout(const moe_shape& s) {
   r.X.meta = take(256);
   r.X.gu_items = take(16 * (size_t)r.tg * (I / 128));
   r.X.dn_items = take(16 * (size_t)r.tb * (H / kDownItemCols));
-  r.X.toff = take(4 * 2 * (E + 1));
   // the token bitmap: zeroed when the workspace is bound, and
   // left zero by every call
   r.X.bitmap = take(4 * E * (size_t)r.words);
@@ -262,7 +261,7 @@ int moe_plan_stage_launches(const moe_plan* plan, int64_t M, int stage) {
   const bool mx = plan->mid_fmt == MOE_MID_MXFP4;
   switch (stage) {
     case 0: return 1;                             // route + x quantization (+ sort when small; + the shared expert's x when large, its gate/up partials when fused)
-    case 1: return small ? 0 : mid_path(M, plan->s.top_k) ? 1 : 3;  // align
+    case 1: return small ? 0 : mid_path(M, plan->s.top_k) ? 1 : 2;  // align
     case 2: return 1;                             // gate_up (+ mid quantization when large)
     case 3: return mid_path(M, plan->s.top_k) && !gq_path(plan, M) ? 1 : 0;  // act_quant (inside gate/up above kMidM and on the gq path)
     case 4: return plan->s.shared_I > 0 && !shared_fused(plan, M) ? (small ? 4 : 3) : 0;  // shared expert (0: inside the routed launches)

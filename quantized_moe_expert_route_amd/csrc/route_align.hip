@@ -165,62 +165,33 @@ __device__ int block_exclusive_scan(int v, int* s_tmp, int* total) {
 
 static_assert(kSmallRows < (1 << 16) && kMidM * 16 < (1 << 16), "rows and tiles share one packed scan");
 
-// Offsets (and with_tiles: tiles of sorted rows, meta[0]) from per-expert
-// counts (thread e holds count c of expert e). Leaves offsets in s_off.
-// Tiles are written where they are used: of kTileRows rows for the
-// mid-range gate/up and down up to kMidM tokens (packed == true: the row
+// Offsets, 16-row tiles of sorted rows and meta[0] from per-expert counts
+// (thread e holds count c of expert e), for the small-token kernels and the
+// mid-range gate/up up to kMidM tokens; leaves the offsets in s_off. The row
 // total is below 2^16, so rows and tiles share one scan, packed as rows |
-// tiles << 16), of kFp4BigRows rows for the MXFP4-mid down above (two
-// scans; every thread writes some tiles, finding its expert in s_toff).
+// tiles << 16.
 __device__ void write_offsets_tiles(int c, int E, int* s_off, int* s_tmp, int* __restrict__ count,
-                                    int* __restrict__ offset, int4* __restrict__ tiles, int* __restrict__ meta,
-                                    bool with_tiles = true, bool packed = true, int* s_toff = nullptr) {
+                                    int* __restrict__ offset, int4* __restrict__ tiles, int* __restrict__ meta) {
   const int tid = threadIdx.x;
-  const int tr = s_toff ? kFp4BigRows : kTileRows;  // rows per tile
-  const int nt = with_tiles ? (c + tr - 1) / tr : 0;
-  int total, off, toff, total_rows, total_tiles;
-  if (packed || !with_tiles) {
-    const int pre = block_exclusive_scan(with_tiles ? c | (nt << 16) : c, s_tmp, &total);
-    off = with_tiles ? pre & 0xFFFF : pre;
-    toff = pre >> 16;
-    total_rows = with_tiles ? total & 0xFFFF : total;
-    total_tiles = total >> 16;
-  } else {
-    off = block_exclusive_scan(c, s_tmp, &total_rows);
-    toff = block_exclusive_scan(nt, s_tmp, &total_tiles);
-  }
+  const int nt = (c + kTileRows - 1) / kTileRows;
+  int total;
+  const int pre = block_exclusive_scan(c | (nt << 16), s_tmp, &total);
+  const int off = pre & 0xFFFF, toff = pre >> 16;
   if (tid < E) {
     count[tid] = c;
     offset[tid] = off;
     s_off[tid] = off;
-    if (s_toff) s_toff[tid] = toff;
-    for (int i = 0; with_tiles && !s_toff && i < nt; ++i) {
+    for (int i = 0; i < nt; ++i) {
       const int r0 = off + i * kTileRows;
       tiles[toff + i] = make_int4(tid, r0, min(r0 + kTileRows, off + c), 0);
     }
   }
   if (tid == 0) {
-    offset[E] = total_rows;
-    s_off[E] = total_rows;
-    if (s_toff) s_toff[E] = total_tiles;
-    if (with_tiles) meta[0] = total_tiles;
+    offset[E] = total & 0xFFFF;
+    s_off[E] = total & 0xFFFF;
+    meta[0] = total >> 16;
   }
   __syncthreads();
-  if (with_tiles && s_toff) {
-    // many tiles (large M): every thread writes some, each finding its
-    // expert by binary search of the tile prefix
-    for (int i = tid; i < total_tiles; i += blockDim.x) {
-      int lo = 0, hi = E;  // largest e with s_toff[e] <= i
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (s_toff[mid] <= i) lo = mid; else hi = mid;
-      }
-      int e = lo;
-      while (s_toff[e + 1] == s_toff[e]) ++e;  // skip experts without tiles
-      const int r0 = s_off[e] + (i - s_toff[e]) * kFp4BigRows;
-      tiles[i] = make_int4(e, r0, min(r0 + kFp4BigRows, s_off[e + 1]), 0);
-    }
-  }
 }
 
 // ---------------------------------------------------------------- M <= kSmallM
@@ -378,27 +349,10 @@ __global__ __launch_bounds__(256) void route_kernel(
 // Work items of the large-token GEMMs, per expert in the order (column
 // block, row tile) so that the row tiles sharing a weight block are adjacent:
 // gate/up items on tiles of kGuRows rows, down items on tiles of kBigRows.
-// One workgroup forms the tile prefixes (write_tile_prefixes); the items
-// themselves are written by every workgroup of the placement launch, a
+// Every workgroup of the placement launch forms the offsets and tile
+// prefixes from the counts itself and writes its share of the items, a
 // thread per item, the expert found by binary search of the prefix in LDS
 // (one workgroup writing all of them was bound by one CU's store rate).
-__device__ void write_tile_prefixes(int c, int E, int n_iblk, int n_nc, int* s_tmp, int* __restrict__ toff,
-                                    int* __restrict__ meta) {
-  const int tid = threadIdx.x;
-  for (int pass = 0; pass < 2; ++pass) {
-    const int tr = pass == 0 ? kGuRows : kBigRows;
-    const int nt = (c + tr - 1) / tr;
-    int total_tiles;
-    const int t0 = block_exclusive_scan(nt, s_tmp, &total_tiles);
-    if (tid < E) toff[pass * (E + 1) + tid] = t0;
-    if (tid == 0) {
-      toff[pass * (E + 1) + E] = total_tiles;
-      meta[1 + pass] = total_tiles * (pass == 0 ? n_iblk : n_nc);
-    }
-    __syncthreads();  // s_tmp is reused
-  }
-}
-
 // Item i of a pass from the tile prefix s_toff and the row offsets s_off.
 __device__ __forceinline__ int4 big_item(int i, int E, int nb, int tr, const int* s_toff, const int* s_off) {
   const int tile = i / nb;  // items of expert e occupy [toff[e] * nb, toff[e + 1] * nb)
@@ -416,15 +370,17 @@ __device__ __forceinline__ int4 big_item(int i, int E, int nb, int tr, const int
   return make_int4(e, r0, min(r0 + tr, s_off[e + 1]), b);
 }
 
-// Sort for M > kSmallM in three launches, none with a serial chain:
+// Sort for M > kSmallM in two launches, none with a serial chain:
 // 1. one workgroup per expert row of the token bitmap (bit t of row e: token
 //    t picked e): the exclusive prefix of the words' popcounts, stored with
 //    the word, and the row total (the expert's count); it is the bitmap's
 //    only reader and leaves it zero for the next call;
-// 2. one workgroup: offsets and the tile prefixes from the counts;
-// 3. one thread per entry t*k+j: its place in expert e's run is offset[e]
-//    plus the number of e's tokens before t (prefix + popcount below bit t),
-//    so entries of earlier tokens come first; and one thread per work item.
+// 2. every workgroup forms the offsets and the tile prefixes from the counts
+//    (workgroup 0 also stores them); then one thread per entry t*k+j: its
+//    place in expert e's run is offset[e] plus the number of e's tokens
+//    before t (prefix + popcount below bit t), so entries of earlier tokens
+//    come first; and one thread per work item (and per 64-row tile of the
+//    MXFP4-mid down).
 __global__ __launch_bounds__(256) void align_rows_kernel(uint32_t* __restrict__ bitmap, int words,
                                                          int2* __restrict__ pw, int* __restrict__ count) {
   __shared__ int s_wsum[4];
@@ -460,45 +416,64 @@ __global__ __launch_bounds__(256) void align_rows_kernel(uint32_t* __restrict__ 
   if (tid == 0) count[e] = carry;
 }
 
-__global__ __launch_bounds__(1024) void align_offsets_kernel(
-    const int* __restrict__ count_in, int E, int* __restrict__ count, int* __restrict__ offset,
-    int4* __restrict__ tiles, int* __restrict__ meta, int n_iblk, int n_nc, int* __restrict__ toff,
-    int with_tiles) {
+__global__ __launch_bounds__(1024) void align_place_kernel(const int* __restrict__ topk_ids, int n, int k, int words,
+                                                           const int2* __restrict__ pw, const int* __restrict__ count,
+                                                           int* __restrict__ offset, int* __restrict__ sorted_entry,
+                                                           int E, int n_iblk, int n_nc, int* __restrict__ meta,
+                                                           int4* __restrict__ tiles, int fp4_tiles,
+                                                           int4* __restrict__ gu_items, int4* __restrict__ dn_items) {
   __shared__ int s_off[1025];
+  __shared__ int s_toff[3][1025];  // tile prefixes: gate/up (kGuRows), down (kBigRows), MXFP4-mid down (kFp4BigRows)
   __shared__ int s_tmp[64];
-  __shared__ int s_t16[1025];  // tile prefix per expert (large M, MXFP4 mid)
   const int tid = threadIdx.x;
-  const int c = tid < E ? count_in[tid] : 0;
-  __syncthreads();  // count_in may be count itself
-  write_offsets_tiles(c, E, s_off, s_tmp, count, offset, tiles, meta, with_tiles != 0, with_tiles == 1,
-                      with_tiles == 2 ? s_t16 : nullptr);
-  write_tile_prefixes(c, E, n_iblk, n_nc, s_tmp, toff, meta);
-}
-
-__global__ __launch_bounds__(256) void align_place_kernel(const int* __restrict__ topk_ids, int n, int k, int words,
-                                                          const int2* __restrict__ pw, const int* __restrict__ offset,
-                                                          int* __restrict__ sorted_entry, int E, int n_iblk, int n_nc,
-                                                          const int* __restrict__ toff, const int* __restrict__ meta,
-                                                          int4* __restrict__ gu_items, int4* __restrict__ dn_items) {
-  __shared__ int s_off[1025];
-  __shared__ int s_toff[2][1025];
-  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) {
+  const int c = tid < E ? count[tid] : 0;
+  int tot, ng, nd, nf = 0;
+  const int off = block_exclusive_scan(c, s_tmp, &tot);
+  const int pg = block_exclusive_scan((c + kGuRows - 1) / kGuRows, s_tmp, &ng);
+  const int pd = block_exclusive_scan((c + kBigRows - 1) / kBigRows, s_tmp, &nd);
+  const int pf = fp4_tiles ? block_exclusive_scan((c + kFp4BigRows - 1) / kFp4BigRows, s_tmp, &nf) : 0;
+  if (tid < E) {
+    s_off[tid] = off;
+    s_toff[0][tid] = pg;
+    s_toff[1][tid] = pd;
+    s_toff[2][tid] = pf;
+  }
+  if (tid == 0) {
+    s_off[E] = tot;
+    s_toff[0][E] = ng;
+    s_toff[1][E] = nd;
+    s_toff[2][E] = nf;
+  }
+  if (blockIdx.x == 0) {
+    if (tid <= E) offset[tid] = tid < E ? off : tot;
+    if (tid == 0) {
+      meta[0] = nf;
+      meta[1] = ng * n_iblk;
+      meta[2] = nd * n_nc;
+    }
+  }
+  __syncthreads();
+  const int gsz = (int)gridDim.x * 1024, g0 = (int)blockIdx.x * 1024 + tid;
+  for (int i = g0; i < n; i += gsz) {
     const int e = topk_ids[i], t = i / k;
     const int2 v = pw[(size_t)e * words + (t >> 5)];
     const int rank = v.x + __popc((uint32_t)v.y & ((1u << (t & 31)) - 1u));
-    sorted_entry[offset[e] + rank] = i;
+    sorted_entry[s_off[e] + rank] = i;
   }
-  for (int i = threadIdx.x; i <= E; i += 256) {
-    s_off[i] = offset[i];
-    s_toff[0][i] = toff[i];
-    s_toff[1][i] = toff[E + 1 + i];
+  for (int i = g0; i < ng * n_iblk; i += gsz) gu_items[i] = big_item(i, E, n_iblk, kGuRows, s_toff[0], s_off);
+  for (int i = g0; i < nd * n_nc; i += gsz) dn_items[i] = big_item(i, E, n_nc, kBigRows, s_toff[1], s_off);
+  // the MXFP4-mid down's tiles: the expert by binary search of their prefix
+  for (int i = g0; i < nf; i += gsz) {
+    int lo = 0, hi = E;  // largest e with s_toff[2][e] <= i
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_toff[2][mid] <= i) lo = mid; else hi = mid;
+    }
+    int e = lo;
+    while (s_toff[2][e + 1] == s_toff[2][e]) ++e;  // skip experts without tiles
+    const int r0 = s_off[e] + (i - s_toff[2][e]) * kFp4BigRows;
+    tiles[i] = make_int4(e, r0, min(r0 + kFp4BigRows, s_off[e + 1]), 0);
   }
-  __syncthreads();
-  const int n_gu = meta[1], n_dn = meta[2];
-  for (int i = blockIdx.x * 256 + threadIdx.x; i < n_gu; i += gridDim.x * 256)
-    gu_items[i] = big_item(i, E, n_iblk, kGuRows, s_toff[0], s_off);
-  for (int i = blockIdx.x * 256 + threadIdx.x; i < n_dn; i += gridDim.x * 256)
-    dn_items[i] = big_item(i, E, n_nc, kBigRows, s_toff[1], s_off);
 }
 
 // The sort for kSmallM < M <= kMidM in one workgroup (the token bitmap has
@@ -534,7 +509,7 @@ __global__ __launch_bounds__(1024) void align_mid_kernel(uint32_t* __restrict__ 
   int c = 0;
   if (tid < E)
     for (int w = 0; w < words; ++w) c += __popc(s_bm[tid * words + w]);
-  write_offsets_tiles(c, E, s_off, s_tmp, count, offset, tiles, meta, true);  // ends with a barrier
+  write_offsets_tiles(c, E, s_off, s_tmp, count, offset, tiles, meta);  // ends with a barrier
   int n_tb;
   // the E4M3 down's items are on tiles of kBigRows rows; with the MXFP4 mid
   // the down runs on tiles of kFp4BigRows rows instead, written to the same
@@ -658,22 +633,15 @@ hipError_t launch_align(const moe_plan* p, const CallArgs& a, Ev ev) {
   hipError_t e = launch_k(align_rows_kernel, dim3((unsigned)p->s.E), dim3(256), 0, a.stream, Ev{ev.start, nullptr},
                           wsp<uint32_t>(p, p->X.bitmap), words, wsp<int2>(p, p->X.pw), wsp<int>(p, p->L.count));
   if (e != hipSuccess) return e;
-  e = launch_k(align_offsets_kernel, dim3(1), dim3(1024), 0, a.stream, Ev{}, wsp<int>(p, p->L.count),
-               (int)p->s.E, wsp<int>(p, p->L.count), wsp<int>(p, p->L.offset), wsp<int4>(p, p->X.tiles),
-               wsp<int>(p, p->X.meta), (int)(p->s.I / 128), (int)(p->s.H / kDownItemCols), wsp<int>(p, p->X.toff),
-               // the tiles: 16 rows for the mid-range gate/up (1: rows
-               // packed with tiles in one scan), kFp4BigRows rows for the
-               // MXFP4-mid down above kMidM (2)
-               mid_path(a.M, p->s.top_k) ? 1 : p->mid_fmt == MOE_MID_MXFP4 ? 2 : 0);
-  if (e != hipSuccess) return e;
   // a thread per entry and per work item: with few rows per expert the items
   // (tiles x column blocks) far outnumber the entries
   const int64_t items = p->tb_max * std::max<int64_t>(p->s.H / kDownItemCols, p->s.I / 128);
   const int64_t threads = std::max(n, items);
-  return launch_k(align_place_kernel, dim3((unsigned)std::min<int64_t>((threads + 255) / 256, 4096)), dim3(256), 0,
+  return launch_k(align_place_kernel, dim3((unsigned)std::min<int64_t>((threads + 1023) / 1024, 1024)), dim3(1024), 0,
                   a.stream, Ev{nullptr, ev.stop}, wsp<int>(p, p->L.topk_ids), (int)n, (int)p->s.top_k, words,
-                  wsp<int2>(p, p->X.pw), wsp<int>(p, p->L.offset), wsp<int>(p, p->L.sorted_entry), (int)p->s.E,
-                  (int)(p->s.I / 128), (int)(p->s.H / kDownItemCols), wsp<int>(p, p->X.toff), wsp<int>(p, p->X.meta),
+                  wsp<int2>(p, p->X.pw), wsp<int>(p, p->L.count), wsp<int>(p, p->L.offset),
+                  wsp<int>(p, p->L.sorted_entry), (int)p->s.E, (int)(p->s.I / 128), (int)(p->s.H / kDownItemCols),
+                  wsp<int>(p, p->X.meta), wsp<int4>(p, p->X.tiles), p->mid_fmt == MOE_MID_MXFP4 ? 1 : 0,
                   wsp<int4>(p, p->X.gu_items), wsp<int4>(p, p->X.dn_items));
 }
 
