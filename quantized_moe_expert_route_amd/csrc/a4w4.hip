@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256) void act_quant_mx_kernel(const float* __restri
     const int sh = 127 - (int)sc;
     uint32_t packed = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) packed |= e2m1_code(ldexpf(v[i], sh)) << (4 * i);
+    for (int i = 0; i < 4; ++i) packed |= e2m1_pack2(ldexpf(v[2 * i], sh), ldexpf(v[2 * i + 1], sh)) << (8 * i);
     *reinterpret_cast<uint32_t*>(q + (size_t)row * (I / 2) + c / 2) = packed;
     if ((u & 3) == 0) s[(size_t)row * (I / 32) + c / 32] = (uint8_t)sc;
   }

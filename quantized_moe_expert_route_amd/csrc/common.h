@@ -74,14 +74,16 @@ __device__ __forceinline__ float key_to_float(uint32_t k) {
 }
 
 // ----------------------------------------------------------------- E2M1 / MX
-// Nearest E2M1 magnitude code of |v| (|v| < 8 here), ties to the even code,
-// saturating at 6: the decision points are the midpoints of the value grid
-// 0, .5, 1, 1.5, 2, 3, 4, 6.
-__device__ __forceinline__ uint32_t e2m1_code(float v) {
-  float a = fabsf(v);
-  uint32_t c = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
-             : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.0f ? 6u : 7u;
-  return c | ((__float_as_uint(v) >> 28) & 8u);
+// E2M1 codes of a (bits 0-3) and b (bits 4-7): the nearest E2M1 value
+// (0, .5, 1, 1.5, 2, 3, 4, 6), ties to the even code, 6 above 6, the sign
+// kept (also on zero), by the hardware conversion v_cvt_scalef32_pk_fp4_f32
+// with a unit scale. Every caller converts scaled elements v * 2^-X of a
+// block with X = floor(log2 amax) - 2, which lie below 8 in magnitude; over
+// every fp32 of magnitude below 8, of either sign, the instruction returns
+// exactly that code (tests/test_gpu_mfma_probe.py compares it with a
+// reference encoder on all of them).
+__device__ __forceinline__ uint32_t e2m1_pack2(float a, float b) {
+  return (uint32_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, 1.0f, 0) & 0xFFu;
 }
 
 // E8M0 scale byte of a 32-block from the largest |bf16| bit pattern of the block.

@@ -278,7 +278,7 @@ __global__ __launch_bounds__(kGqThreads) void gate_up_quant_kernel(
     for (int o = 1; o < 16; o <<= 1) am = max(am, (uint32_t)__shfl_xor((int)am, o, 64));
     const uint32_t sc = mx_scale_code_f32(am);
     const int sh = 127 - (int)sc;
-    const uint32_t code = e2m1_code(ldexpf(h0, sh)) | (e2m1_code(ldexpf(h1, sh)) << 4);
+    const uint32_t code = e2m1_pack2(ldexpf(h0, sh), ldexpf(h1, sh));
     if (wave < rows) {
       midq[(size_t)(r0 + wave) * (I / 2) + 64 * b + lane] = (uint8_t)code;
       if ((lane & 15) == 0)

@@ -262,9 +262,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
           const int row = 16 * i + 4 * ge + v;
           const uint32_t sc = mx_scale_code_f32(__float_as_uint(pm[i][v]));
           const int sh = 127 - (int)sc;
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            qs[row * 128 + 32 * wn + 16 * j + re] = row < rows ? (uint8_t)e2m1_code(ldexpf(hv[i][j][v], sh)) : 0;
+          const uint32_t cp = row < rows ? e2m1_pack2(ldexpf(hv[i][0][v], sh), ldexpf(hv[i][1][v], sh)) : 0u;
+          qs[row * 128 + 32 * wn + re] = (uint8_t)(cp & 15u);
+          qs[row * 128 + 32 * wn + 16 + re] = (uint8_t)(cp >> 4);
           if (re == 0 && row < rows)
             reinterpret_cast<uint8_t*>(mids)[(size_t)(r0 + row) * (I / 32) + 4 * ib + wn] = (uint8_t)sc;
         }

@@ -85,6 +85,9 @@ inline bool small_path(int64_t M, int64_t k) { return M <= kSmallM && M * k <= k
 // sort otherwise): with few rows per expert, 64-row tiles leave most of the
 // chip idle.
 constexpr int kMidM = 256;
+// Largest E of a plan (a routing workgroup gathers its tokens' bitmap bits
+// per expert in LDS).
+constexpr int kRouteMaxE = 1024;
 inline bool mid_path(int64_t M, int64_t k) { return M <= kMidM && k <= 16; }
 // Up to kSmallM tokens with the E4M3 mid, a block-FP8 shared expert of at
 // most kSmallSharedI columns runs inside the routed launches

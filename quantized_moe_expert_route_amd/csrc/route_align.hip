@@ -91,18 +91,24 @@ __device__ __forceinline__ float route_weight(float sel_l, int k, int lane, floa
 // the shared expert fused as expert 256 of a top-9 call): slots 0..k-2 are
 // routed over the first E-1 logits, slot k-1 is expert E-1 with weight 1.
 template <int EC>
-__device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int k, float scaling,
-                                            int shared_slot, int lane, uint32_t& sel_e, float& w) {
-  const int kr = k - shared_slot, er = E - shared_slot;
-  uint32_t key[EC];
+__device__ __forceinline__ void route_keys(uint32_t (&key)[EC], int E, int k, float scaling, int shared_slot,
+                                           int lane, uint32_t& sel_e, float& w) {
+  const int kr = k - shared_slot;
   float sel_l = 0.f;
-  load_keys<EC>(row, er, lane, key);
   topk_wave<EC>(key, kr, lane, sel_e, sel_l);
   w = route_weight(sel_l, kr, lane, scaling);
   if (shared_slot && lane == k - 1) {
     sel_e = (uint32_t)(E - 1);
     w = 1.0f;
   }
+}
+
+template <int EC>
+__device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int k, float scaling,
+                                            int shared_slot, int lane, uint32_t& sel_e, float& w) {
+  uint32_t key[EC];
+  load_keys<EC>(row, E - shared_slot, lane, key);
+  route_keys<EC>(key, E, k, scaling, shared_slot, lane, sel_e, w);
 }
 
 // One 32-element block of a bf16 row -> 16 bytes of E2M1 + an E8M0 byte.
@@ -127,7 +133,7 @@ __device__ __forceinline__ void quant_block_mx(const uint16_t* __restrict__ src,
   for (int i = 0; i < 16; ++i) {
     const float f0 = ldexpf(__uint_as_float(w32[i] << 16), sh);
     const float f1 = ldexpf(__uint_as_float(w32[i] & 0xFFFF0000u), sh);
-    packed[i >> 2] |= (e2m1_code(f0) | (e2m1_code(f1) << 4)) << (8 * (i & 3));
+    packed[i >> 2] |= e2m1_pack2(f0, f1) << (8 * (i & 3));
   }
   *reinterpret_cast<uint4*>(dq) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
   *ds = (uint8_t)sc;
@@ -288,7 +294,7 @@ __device__ __forceinline__ void quant_x_unit(const uint16_t* __restrict__ x, int
       for (int q = 0; q < 4; ++q) {
         const float f0 = ldexpf(__uint_as_float(w32[q] << 16), sh);
         const float f1 = ldexpf(__uint_as_float(w32[q] & 0xFFFF0000u), sh);
-        packed |= (e2m1_code(f0) | (e2m1_code(f1) << 4)) << (8 * q);
+        packed |= e2m1_pack2(f0, f1) << (8 * q);
       }
       *reinterpret_cast<uint32_t*>(xq + (size_t)t * (H >> 1) + (e0 >> 1)) = packed;
       if ((lane & 3) == 0) xs[(size_t)t * (H >> 5) + (e0 >> 5)] = (uint8_t)sc;
@@ -314,9 +320,14 @@ __device__ __forceinline__ void quant_x_unit(const uint16_t* __restrict__ x, int
   }
 }
 
-// Workgroups [0, route_blocks) route, one wave per token (top-k, weights,
-// the token's bits in the expert x token bitmap); the rest quantize x, one
-// wave per unit of kXU loads of a row. The two roles share no registers.
+// Workgroups [0, route_blocks) route, one wave per token: workgroup b takes
+// tokens [4 b, 4 b + 4), an eighth of word b / 8 of each expert row of the
+// expert x token bitmap; the bits of its tokens gather in LDS and each
+// nonzero eighth goes to the bitmap with one atomic OR, so at most 8 atomics
+// meet on a word even when every token picks the same experts (one per token
+// and slot met 32 there, and serialized: t4 hot routing 26 -> 17 us). The
+// rest quantize x, one wave per unit of kXU loads of a row. The two roles
+// share no registers.
 template <int EC, bool SH>
 __global__ __launch_bounds__(256) void route_kernel(
     const float* __restrict__ logits, const uint16_t* __restrict__ x, int M, int E, int k, int H,
@@ -325,15 +336,26 @@ __global__ __launch_bounds__(256) void route_kernel(
     uint8_t* __restrict__ sh_xq, float* __restrict__ sh_xs, int route_blocks, int shared_slot) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if ((int)blockIdx.x < route_blocks) {
-    for (int t = blockIdx.x * 4 + wave; t < M; t += route_blocks * 4) {
+    __shared__ uint32_t s_bits[kRouteMaxE];
+    for (int e = threadIdx.x; e < E; e += 256) s_bits[e] = 0u;
+    const int t = blockIdx.x * 4 + wave;
+    uint32_t key[EC];
+    load_keys<EC>(logits + (size_t)min(t, M - 1) * E, E - shared_slot, lane, key);
+    __syncthreads();
+    if (t < M) {
       uint32_t sel_e = 0;
       float w = 0.f;
-      route_token<EC>(logits + (size_t)t * E, E, k, scaling, shared_slot, lane, sel_e, w);
+      route_keys<EC>(key, E, k, scaling, shared_slot, lane, sel_e, w);
       if (lane < k) {
         topk_ids[(size_t)t * k + lane] = (int)sel_e;
         topk_w[(size_t)t * k + lane] = w;
-        atomicOr(&bitmap[(size_t)sel_e * words + (t >> 5)], 1u << (t & 31));
+        atomicOr(&s_bits[sel_e], 1u << (t & 31));
       }
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 256) {
+      const uint32_t bits = s_bits[e];
+      if (bits) atomicOr(&bitmap[(size_t)e * words + (blockIdx.x >> 3)], bits);
     }
     return;
   }
@@ -604,10 +626,10 @@ hipError_t launch_route_small(const moe_plan* p, const CallArgs& a, Ev ev) {
 
 hipError_t launch_route(const moe_plan* p, const CallArgs& a, Ev ev) {
   const int M = (int)a.M, E = (int)p->s.E, k = (int)p->s.top_k, H = (int)p->s.H;
-  const int route_blocks = (int)std::min<int64_t>((a.M + 3) / 4, 2048);
+  // a routing workgroup per 4 tokens
+  const int words = (int)((a.M + 31) / 32), route_blocks = (int)((a.M + 3) / 4);
   const int64_t units = a.M * ((H + 512 * kXU - 1) / (512 * kXU));
   const int blocks = route_blocks + (int)std::min<int64_t>((units + 3) / 4, 2048);
-  const int words = (int)((a.M + 31) / 32);
   // with a shared expert, its E4M3 x comes from the same read of x
   const bool sh = p->s.shared_I > 0;
   uint8_t* sh_xq = sh ? wsp<uint8_t>(p, p->L.sh_xq) : nullptr;

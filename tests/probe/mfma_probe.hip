@@ -15,6 +15,10 @@
 // use (v_cvt_pk_fp8_f32) against a reference encoder written from the
 // format's definition (qmoe_probe_e4m3_ref, also callable on the host), on
 // every fp32 of magnitude below 464, of both signs.
+//
+// qmoe_probe_e2m1_cvt: the same for the hardware fp32 -> E2M1 conversion
+// (v_cvt_scalef32_pk_fp4_f32 with a unit scale; the first operand in the low
+// nibble) against qmoe_probe_e2m1_ref, on every fp32 of magnitude below 8.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
@@ -126,3 +130,55 @@ extern "C" int qmoe_probe_e4m3_cvt(void* counts, void* first, int n, void* strea
 }
 
 extern "C" uint32_t qmoe_probe_e4m3_ref(float v) { return e4m3_ref(v); }
+
+// The nearest E2M1 magnitude to |v| among 0, .5, 1, 1.5, 2, 3, 4, 6 (ties to
+// the even code, 6 above 6), the sign bit of v in bit 3: a scan of the
+// ascending grid.
+__host__ __device__ inline uint32_t e2m1_ref(float v) {
+  const double grid[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+  const double a = fabs((double)v);
+  uint32_t bits;
+  memcpy(&bits, &v, 4);
+  uint32_t c = 7;
+  for (uint32_t i = 0; i < 7; ++i) {
+    const double mid = (grid[i] + grid[i + 1]) / 2;
+    if (a < mid || (a == mid && (i & 1u) == 0)) {
+      c = i;
+      break;
+    }
+  }
+  return c | ((bits >> 28) & 8u);
+}
+
+constexpr uint32_t kFp4CvtEnd = 0x41000000u;  // bits of 8.0f
+
+// thread t: the non-negative bit patterns t, t + n, ... below kFp4CvtEnd, each
+// with both signs (v in the low nibble, -v in the high one); counts[t]
+// mismatches, first[2t] the first one's bits and first[2t+1] its codes
+// (hardware | reference << 16)
+__global__ void e2m1_cvt_kernel(uint32_t* __restrict__ counts, uint32_t* __restrict__ first, int n) {
+  const uint32_t t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= (uint32_t)n) return;
+  uint32_t bad = 0, fb = 0xFFFFFFFFu, fc = 0;
+  for (uint32_t b = t; b < kFp4CvtEnd; b += (uint32_t)n) {
+    const float v = __uint_as_float(b);
+    const uint32_t hw = (uint32_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v, -v, 1.0f, 0) & 0xFFu;
+    const uint32_t ref = e2m1_ref(v) | (e2m1_ref(-v) << 4);
+    if (hw != ref) {
+      if (!bad) fb = b, fc = hw | (ref << 16);
+      ++bad;
+    }
+  }
+  counts[t] = bad;
+  first[2 * t] = fb;
+  first[2 * t + 1] = fc;
+}
+
+extern "C" int qmoe_probe_e2m1_cvt(void* counts, void* first, int n, void* stream) {
+  if (n <= 0 || n % 256) return -1;
+  hipLaunchKernelGGL(e2m1_cvt_kernel, dim3(n / 256), dim3(256), 0, (hipStream_t)stream, (uint32_t*)counts,
+                     (uint32_t*)first, n);
+  return (int)hipGetLastError();
+}
+
+extern "C" uint32_t qmoe_probe_e2m1_ref(float v) { return e2m1_ref(v); }

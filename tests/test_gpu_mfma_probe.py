@@ -12,7 +12,13 @@ The fp32 -> E4M3 conversion (v_cvt_pk_fp8_f32) every E4M3 quantizer uses:
 equal to nearest-even rounding onto the E4M3 grid (the reference encoder of
 the probe library, itself checked against the oracle's encoder on the CPU in
 test_probe_e4m3_reference.py) on every fp32 of magnitude below 464, the
-range the quantizers' quotients v / fl32(amax / 448) lie in."""
+range the quantizers' quotients v / fl32(amax / 448) lie in.
+
+The fp32 -> E2M1 conversion (v_cvt_scalef32_pk_fp4_f32, unit scale) every
+MXFP4 quantizer uses: equal to nearest-even rounding onto the E2M1 grid with
+saturation at 6 and the sign kept (the probe's reference encoder, checked
+against the oracle's in test_probe_e4m3_reference.py) on every fp32 of
+magnitude below 8, the range of the scaled elements v * 2^-X."""
 
 import ctypes
 import os
@@ -72,16 +78,17 @@ def test_fp8_mfma_drops_small_products_bf16_does_not():
         assert np.all(d8[m] == exact[m]), f"row {m}: {d8[m, 0]!r}"
 
 
-def test_hw_e4m3_conversion_on_every_fp32_below_464():
+def _exhaustive_cvt(fn):
     import torch
 
     L = ctypes.CDLL(LIB)
-    L.qmoe_probe_e4m3_cvt.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    f = getattr(L, fn)
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     n = 1 << 20
     dev = torch.device("cuda", 0)
     counts = torch.zeros(n, dtype=torch.int32, device=dev)
     first = torch.zeros(2 * n, dtype=torch.int32, device=dev)
-    st = L.qmoe_probe_e4m3_cvt(counts.data_ptr(), first.data_ptr(), n, torch.cuda.current_stream().cuda_stream)
+    st = f(counts.data_ptr(), first.data_ptr(), n, torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     assert st == 0
     c = counts.cpu().numpy()
@@ -89,3 +96,11 @@ def test_hw_e4m3_conversion_on_every_fp32_below_464():
         f = first.cpu().numpy().view(np.uint32).reshape(n, 2)[c > 0][:8]
         raise AssertionError(f"{int(c.sum())} mismatches; first (bits, hw | ref << 16): "
                              + ", ".join(f"({b:#010x}, {v:#010x})" for b, v in f))
+
+
+def test_hw_e4m3_conversion_on_every_fp32_below_464():
+    _exhaustive_cvt("qmoe_probe_e4m3_cvt")
+
+
+def test_hw_e2m1_conversion_on_every_fp32_below_8():
+    _exhaustive_cvt("qmoe_probe_e2m1_cvt")

@@ -330,17 +330,26 @@ def test_run_to_run_bitwise():
     assert np.array_equal(a, b)
 
 
+# block-FP8 shared expert in a pass of its own: above kSmallM, and at
+# M <= kSmallM with shared_I above the limit of the fused form
+_GRAPH_SHAPES = {
+    "shared_large": (X.Shape(M=200, H=1024, E=32, I=256, top_k=4, shared_I=256), "zipf", 41),
+    "shared_small_wide": (X.Shape(M=12, H=1024, E=32, I=256, top_k=4, shared_I=640), "normal", 42),
+}
+
+
 @pytest.mark.parametrize("name,mxfp4", [("c1", False), ("c1b", False), ("m64_mixed", False), ("c3", False),
-                                        ("m256_hot", True)])
+                                        ("m256_hot", True), ("shared_large", False), ("shared_small_wide", False)])
 def test_graph_replay_matches_eager(name, mxfp4):
     """Replays of a captured call (small, mid-range and large paths; the
-    MXFP4 mid) equal the eager call bitwise, with eager calls between them:
-    every call leaves the token bitmap zero for the next."""
+    MXFP4 mid; the block-FP8 shared expert's own pass) equal the eager call
+    bitwise, with eager calls between them: every call leaves the token
+    bitmap zero for the next."""
     import torch
 
     from quantized_moe_expert_route_amd.binding import MID_MXFP4, layout_for, pack_w2
 
-    d = X.make_inputs(name)
+    d = X.make_inputs(*_GRAPH_SHAPES[name]) if name in _GRAPH_SHAPES else X.make_inputs(name)
     s = d["shape"]
     g = upload(d)
     plan = make_plan(s)
