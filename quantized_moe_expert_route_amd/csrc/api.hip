@@ -65,9 +65,10 @@ Layout make_layout(const moe_shape& s) {
   r.X.meta = take(256);
   r.X.gu_items = take(16 * (size_t)r.tg * (I / 128));
   r.X.dn_items = take(16 * (size_t)r.tb * (H / kDownItemCols));
-  // the token bitmap: zeroed when the workspace is bound, and
-  // left zero by every call
+  // the token bitmap and the one-launch sort's counter: zeroed when the
+  // workspace is bound, and left zero by every call
   r.X.bitmap = take(4 * E * (size_t)r.words);
+  r.X.done = take(4);
   r.X.sync_begin = r.X.bitmap;
   r.X.sync_bytes = align256(off) - r.X.bitmap;
   r.X.pw = take(8 * E * (size_t)r.words);

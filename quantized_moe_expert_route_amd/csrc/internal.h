@@ -24,6 +24,7 @@ struct Internal {
   size_t gu_items; // int4 [TG * I/128]: {expert, row_begin, row_end, column block}, tiles of kGuRows, large M
   size_t dn_items; // int4 [TB * H/kDownItemCols]: {expert, row_begin, row_end, column chunk} (M > kSmallM); mid-range calls with the MXFP4 mid: its 64-row tiles
   size_t bitmap;   // uint32 [E, ceil(M/32)]: bit t of row e = token t picked e; zero between calls
+  size_t done;     // int: workgroups of the one-launch sort past their bitmap copy; zero between calls
   size_t pw;       // int2 [E, ceil(M/32)]: {set bits of row e before word w, word w}
   size_t h;        // fp32 [n, I]: SiLU(gate)*up, rows in sorted order
   size_t sh_h;     // fp32 [M, Is]
@@ -88,6 +89,16 @@ constexpr int kMidM = 256;
 // Largest E of a plan (a routing workgroup gathers its tokens' bitmap bits
 // per expert in LDS).
 constexpr int kRouteMaxE = 1024;
+// Above kMidM tokens the sort runs in one launch while the token bitmap (E x
+// ceil(M/32) words) is small enough for every workgroup to copy it into LDS
+// (c3's 8192 words: align 12.7 -> 10.1 us; at 32768 words, c4's, the copies
+// made the one launch slower than two: 14.5 against 12.9 us) and its rows'
+// prefixes fit 16 bits (M <= 65536); in two launches otherwise.
+constexpr int kAlignLdsWords = 8192;
+inline bool align_one_launch(int64_t E, int64_t M) {
+  const int64_t words = (M + 31) / 32;
+  return E * words <= kAlignLdsWords && words <= 2048;
+}
 inline bool mid_path(int64_t M, int64_t k) { return M <= kMidM && k <= 16; }
 // Up to kSmallM tokens with the E4M3 mid, a block-FP8 shared expert of at
 // most kSmallSharedI columns runs inside the routed launches

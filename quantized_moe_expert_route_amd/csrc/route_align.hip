@@ -438,18 +438,16 @@ __global__ __launch_bounds__(256) void align_rows_kernel(uint32_t* __restrict__ 
   if (tid == 0) count[e] = carry;
 }
 
-__global__ __launch_bounds__(1024) void align_place_kernel(const int* __restrict__ topk_ids, int n, int k, int words,
-                                                           const int2* __restrict__ pw, const int* __restrict__ count,
-                                                           int* __restrict__ offset, int* __restrict__ sorted_entry,
-                                                           int E, int n_iblk, int n_nc, int* __restrict__ meta,
-                                                           int4* __restrict__ tiles, int fp4_tiles,
-                                                           int4* __restrict__ gu_items, int4* __restrict__ dn_items) {
-  __shared__ int s_off[1025];
-  __shared__ int s_toff[3][1025];  // tile prefixes: gate/up (kGuRows), down (kBigRows), MXFP4-mid down (kFp4BigRows)
-  __shared__ int s_tmp[64];
+// The offsets and the tile prefixes (gate/up kGuRows, down kBigRows, with
+// fp4_tiles the MXFP4-mid down's kFp4BigRows) from the experts' counts
+// (thread e < E holds count e) into s_off / s_toff; workgroup 0 also stores
+// offset[] and meta. Ends with a barrier.
+__device__ void align_scans(int c, int E, int fp4_tiles, int n_iblk, int n_nc, int* s_off, int (*s_toff)[1025],
+                            int* s_tmp, int* __restrict__ offset, int* __restrict__ meta, int& ng, int& nd,
+                            int& nf) {
   const int tid = threadIdx.x;
-  const int c = tid < E ? count[tid] : 0;
-  int tot, ng, nd, nf = 0;
+  int tot;
+  nf = 0;
   const int off = block_exclusive_scan(c, s_tmp, &tot);
   const int pg = block_exclusive_scan((c + kGuRows - 1) / kGuRows, s_tmp, &ng);
   const int pd = block_exclusive_scan((c + kBigRows - 1) / kBigRows, s_tmp, &nd);
@@ -475,13 +473,14 @@ __global__ __launch_bounds__(1024) void align_place_kernel(const int* __restrict
     }
   }
   __syncthreads();
-  const int gsz = (int)gridDim.x * 1024, g0 = (int)blockIdx.x * 1024 + tid;
-  for (int i = g0; i < n; i += gsz) {
-    const int e = topk_ids[i], t = i / k;
-    const int2 v = pw[(size_t)e * words + (t >> 5)];
-    const int rank = v.x + __popc((uint32_t)v.y & ((1u << (t & 31)) - 1u));
-    sorted_entry[s_off[e] + rank] = i;
-  }
+}
+
+// The gate/up and down work items and the MXFP4-mid down's 64-row tiles, a
+// thread each over the grid.
+__device__ void align_items(int E, int n_iblk, int n_nc, int ng, int nd, int nf, const int* s_off,
+                            const int (*s_toff)[1025], int4* __restrict__ tiles, int4* __restrict__ gu_items,
+                            int4* __restrict__ dn_items) {
+  const int gsz = (int)gridDim.x * 1024, g0 = (int)blockIdx.x * 1024 + threadIdx.x;
   for (int i = g0; i < ng * n_iblk; i += gsz) gu_items[i] = big_item(i, E, n_iblk, kGuRows, s_toff[0], s_off);
   for (int i = g0; i < nd * n_nc; i += gsz) dn_items[i] = big_item(i, E, n_nc, kBigRows, s_toff[1], s_off);
   // the MXFP4-mid down's tiles: the expert by binary search of their prefix
@@ -495,6 +494,117 @@ __global__ __launch_bounds__(1024) void align_place_kernel(const int* __restrict
     while (s_toff[2][e + 1] == s_toff[2][e]) ++e;  // skip experts without tiles
     const int r0 = s_off[e] + (i - s_toff[2][e]) * kFp4BigRows;
     tiles[i] = make_int4(e, r0, min(r0 + kFp4BigRows, s_off[e + 1]), 0);
+  }
+}
+
+__global__ __launch_bounds__(1024) void align_place_kernel(const int* __restrict__ topk_ids, int n, int k, int words,
+                                                           const int2* __restrict__ pw, const int* __restrict__ count,
+                                                           int* __restrict__ offset, int* __restrict__ sorted_entry,
+                                                           int E, int n_iblk, int n_nc, int* __restrict__ meta,
+                                                           int4* __restrict__ tiles, int fp4_tiles,
+                                                           int4* __restrict__ gu_items, int4* __restrict__ dn_items) {
+  __shared__ int s_off[1025];
+  __shared__ int s_toff[3][1025];  // tile prefixes: gate/up (kGuRows), down (kBigRows), MXFP4-mid down (kFp4BigRows)
+  __shared__ int s_tmp[64];
+  const int tid = threadIdx.x;
+  int ng, nd, nf;
+  align_scans(tid < E ? count[tid] : 0, E, fp4_tiles, n_iblk, n_nc, s_off, s_toff, s_tmp, offset, meta, ng, nd, nf);
+  const int gsz = (int)gridDim.x * 1024, g0 = (int)blockIdx.x * 1024 + tid;
+  for (int i = g0; i < n; i += gsz) {
+    const int e = topk_ids[i], t = i / k;
+    const int2 v = pw[(size_t)e * words + (t >> 5)];
+    const int rank = v.x + __popc((uint32_t)v.y & ((1u << (t & 31)) - 1u));
+    sorted_entry[s_off[e] + rank] = i;
+  }
+  align_items(E, n_iblk, n_nc, ng, nd, nf, s_off, s_toff, tiles, gu_items, dn_items);
+}
+
+// The large-token sort in one launch while the whole token bitmap fits in
+// LDS (align_one_launch): every workgroup copies it into
+// LDS, forms the popcount prefix of each row at every 8th word and the
+// experts' counts, then as align_place_kernel the offsets, the entries'
+// places (prefix + popcounts of the words between + popcount below bit t)
+// and the work items. The workgroup whose copy completes last (a counter in
+// the workspace, reset by it) clears the bitmap for the next call: every
+// other workgroup's copy is complete by then.
+__global__ __launch_bounds__(1024) void align_big_kernel(uint32_t* __restrict__ bitmap, int words,
+                                                         int* __restrict__ done, const int* __restrict__ topk_ids,
+                                                         int n, int k, int* __restrict__ count,
+                                                         int* __restrict__ offset, int* __restrict__ sorted_entry,
+                                                         int E, int n_iblk, int n_nc, int* __restrict__ meta,
+                                                         int4* __restrict__ tiles, int fp4_tiles,
+                                                         int4* __restrict__ gu_items, int4* __restrict__ dn_items) {
+  __shared__ __align__(16) uint32_t s_bm[kAlignLdsWords];
+  __shared__ __align__(16) uint16_t s_pre[kAlignLdsWords / 8 + kRouteMaxE];
+  __shared__ int s_off[1025];
+  __shared__ int s_toff[3][1025];
+  __shared__ int s_tmp[64];
+  __shared__ int s_last;
+  const int tid = threadIdx.x;
+  const int nw = E * words, ng8 = (words + 7) >> 3;
+  const int gsz = (int)gridDim.x * 1024, g0 = (int)blockIdx.x * 1024 + tid;
+  int e_first = topk_ids[min(g0, n - 1)];  // this thread's first entry's expert, read beside the copy
+  {
+    // the copy in 16-byte pieces, all of a thread's loads in flight together
+    // (unconditional, from a clamped index; kAlignLdsWords / 4 / 1024 of them)
+    const int nw4 = nw >> 2;
+    const uint4* src = reinterpret_cast<const uint4*>(bitmap);
+    uint4* dst = reinterpret_cast<uint4*>(s_bm);
+    uint4 v[kAlignLdsWords / 4096];
+    if (nw4 > 0) {
+#pragma unroll
+      for (int q = 0; q < kAlignLdsWords / 4096; ++q) v[q] = src[min(tid + 1024 * q, nw4 - 1)];
+      // (the loads are used here, so none sinks into its store's branch)
+#pragma unroll
+      for (int q = 0; q < kAlignLdsWords / 4096; ++q)
+        asm volatile("" : "+v"(v[q].x), "+v"(v[q].y), "+v"(v[q].z), "+v"(v[q].w));
+      asm volatile("" : "+v"(e_first));
+#pragma unroll
+      for (int q = 0; q < kAlignLdsWords / 4096; ++q)
+        if (tid + 1024 * q < nw4) dst[tid + 1024 * q] = v[q];
+    }
+    for (int i = 4 * nw4 + tid; i < nw; i += 1024) s_bm[i] = bitmap[i];
+  }
+  __syncthreads();
+  if (tid == 0) s_last = atomicAdd(done, 1) == (int)gridDim.x - 1;
+  // popcounts of the rows' 8-word groups, then each row's exclusive prefix
+  // over its groups (a thread a row) and its total, the expert's count
+  for (int q = tid; q < E * ng8; q += 1024) {
+    const int e = q / ng8, w0 = 8 * (q - e * ng8);
+    const uint32_t* row = s_bm + e * words;
+    int c = 0;
+    for (int w = w0; w < min(w0 + 8, words); ++w) c += __popc(row[w]);
+    s_pre[q] = (uint16_t)c;
+  }
+  __syncthreads();
+  if (tid < E) {
+    int run = 0;
+    for (int g = 0; g < ng8; ++g) {
+      const int c = s_pre[tid * ng8 + g];
+      s_pre[tid * ng8 + g] = (uint16_t)run;
+      run += c;
+    }
+    s_off[tid] = run;
+  }
+  __syncthreads();
+  const int c = tid < E ? s_off[tid] : 0;
+  if (blockIdx.x == 0 && tid < E) count[tid] = c;
+  __syncthreads();  // s_off is rewritten by the scans
+  int ng, nd, nf;
+  align_scans(c, E, fp4_tiles, n_iblk, n_nc, s_off, s_toff, s_tmp, offset, meta, ng, nd, nf);
+  for (int i = g0; i < n; i += gsz) {
+    const int e = i == g0 ? e_first : topk_ids[i], t = i / k, w = t >> 5;
+    const uint32_t* row = s_bm + e * words;
+    int rank = s_pre[e * ng8 + (w >> 3)] + __popc(row[w] & ((1u << (t & 31)) - 1u));
+    for (int v = w & ~7; v < w; ++v) rank += __popc(row[v]);
+    sorted_entry[s_off[e] + rank] = i;
+  }
+  align_items(E, n_iblk, n_nc, ng, nd, nf, s_off, s_toff, tiles, gu_items, dn_items);
+  if (s_last) {  // (s_last was written before two barriers)
+    const int nw4 = nw >> 2;
+    for (int i = tid; i < nw4; i += 1024) reinterpret_cast<uint4*>(bitmap)[i] = make_uint4(0u, 0u, 0u, 0u);
+    for (int i = 4 * nw4 + tid; i < nw; i += 1024) bitmap[i] = 0u;
+    if (tid == 0) *done = 0;
   }
 }
 
@@ -652,14 +762,20 @@ hipError_t launch_align(const moe_plan* p, const CallArgs& a, Ev ev) {
                     wsp<int>(p, p->L.offset), wsp<int>(p, p->L.sorted_entry), wsp<int4>(p, p->X.tiles),
                     wsp<int>(p, p->X.meta), (int)(p->s.H / kDownItemCols), wsp<int4>(p, p->X.dn_items),
                     p->mid_fmt == MOE_MID_MXFP4 ? 1 : 0);
+  const int64_t items = p->tb_max * std::max<int64_t>(p->s.H / kDownItemCols, p->s.I / 128);
+  const int64_t threads = std::max(n, items);
+  const unsigned grid = (unsigned)std::min<int64_t>((threads + 1023) / 1024, 1024);
+  if (align_one_launch(p->s.E, a.M))
+    return launch_k(align_big_kernel, dim3(grid), dim3(1024), 0, a.stream, ev, wsp<uint32_t>(p, p->X.bitmap), words,
+                    wsp<int>(p, p->X.done), wsp<int>(p, p->L.topk_ids), (int)n, (int)p->s.top_k,
+                    wsp<int>(p, p->L.count), wsp<int>(p, p->L.offset), wsp<int>(p, p->L.sorted_entry), (int)p->s.E,
+                    (int)(p->s.I / 128), (int)(p->s.H / kDownItemCols), wsp<int>(p, p->X.meta),
+                    wsp<int4>(p, p->X.tiles), p->mid_fmt == MOE_MID_MXFP4 ? 1 : 0, wsp<int4>(p, p->X.gu_items),
+                    wsp<int4>(p, p->X.dn_items));
   hipError_t e = launch_k(align_rows_kernel, dim3((unsigned)p->s.E), dim3(256), 0, a.stream, Ev{ev.start, nullptr},
                           wsp<uint32_t>(p, p->X.bitmap), words, wsp<int2>(p, p->X.pw), wsp<int>(p, p->L.count));
   if (e != hipSuccess) return e;
-  // a thread per entry and per work item: with few rows per expert the items
-  // (tiles x column blocks) far outnumber the entries
-  const int64_t items = p->tb_max * std::max<int64_t>(p->s.H / kDownItemCols, p->s.I / 128);
-  const int64_t threads = std::max(n, items);
-  return launch_k(align_place_kernel, dim3((unsigned)std::min<int64_t>((threads + 1023) / 1024, 1024)), dim3(1024), 0,
+  return launch_k(align_place_kernel, dim3(grid), dim3(1024), 0,
                   a.stream, Ev{nullptr, ev.stop}, wsp<int>(p, p->L.topk_ids), (int)n, (int)p->s.top_k, words,
                   wsp<int2>(p, p->X.pw), wsp<int>(p, p->L.count), wsp<int>(p, p->L.offset),
                   wsp<int>(p, p->L.sorted_entry), (int)p->s.E, (int)(p->s.I / 128), (int)(p->s.H / kDownItemCols),
