@@ -270,7 +270,7 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
 
   // ---- the ring. A run that fits the slots is computed straight from the
   // prologue's loads (one path, so each wait counts exactly); a longer one
-  // goes through full batches (every reload is a new tile), then the tail.
+  // reloads each slot right after computing it, batch by batch.
   if (my > 0 && my <= D) {
 #pragma unroll
     for (int d = 0; d < D; d += 2) {
@@ -279,12 +279,16 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
       __builtin_amdgcn_sched_barrier(0);
     }
   } else if (my > D) {
+    // while tiles remain after the batch in the slots, each slot is
+    // reloaded as soon as its tile is computed, so the next batch's loads
+    // overlap this batch's products; slots past the wave's run reload its
+    // last tile (loaded, never computed), so every load is unconditional
     int i0 = 0;
-    for (; i0 + 2 * D <= my; i0 += D) {
+    for (; i0 + D < my; i0 += D) {
 #pragma unroll
       for (int d = 0; d < D; d += 2) {  // two independent tiles per step
-        const int4 tn0 = tiles[tile_of(i0 + D + d)];
-        const int4 tn1 = tiles[tile_of(i0 + D + min(d + 1, D - 1))];
+        const int4 tn0 = tiles[tile_of(min(i0 + D + d, my - 1))];
+        const int4 tn1 = tiles[tile_of(min(i0 + D + min(d + 1, D - 1), my - 1))];
         compute(T[d], S[d]);
         if (d + 1 < D) compute(T[d + 1], S[d + 1]);
         __builtin_amdgcn_sched_barrier(0);
@@ -297,27 +301,13 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // the slots hold tiles i0 .. i0 + D - 1 (past my: repeats of the last);
-    // fewer than D tiles remain after them
+    // the slots hold tiles i0 .. my - 1 (1 to D of them), then repeats
+    const int rest = my - i0;
 #pragma unroll
     for (int d = 0; d < D; d += 2) {
-      compute(T[d], S[d]);
-      if (d + 1 < D) compute(T[d + 1], S[d + 1]);
+      if (d < rest) compute(T[d], S[d]);
+      if (d + 1 < D && d + 1 < rest) compute(T[d + 1], S[d + 1]);
       __builtin_amdgcn_sched_barrier(0);
-    }
-    const int rest = my - i0 - D;  // tiles after the slots' ones: fewer than D
-    if (rest > 0) {
-#pragma unroll
-      for (int d = 0; d < D; ++d) {
-        if (d < rest) {
-          T[d] = tiles[tile_of(i0 + D + d)];
-          load(T[d], S[d]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int d = 0; d < D; ++d)
-        if (d < rest) compute(T[d], S[d]);
     }
   }
   __syncthreads();
