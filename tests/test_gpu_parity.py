@@ -517,3 +517,26 @@ def test_declared_weight_layout_is_required():
     plan.forward(g["x"], g["logits"], g["w13"], g["s13"], g["w2"], g["s2"], out)
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy().view(np.uint16), oracle(d)["out"])
+
+
+@pytest.mark.parametrize("active", [33, 40, 63, 64, 65, 100, 128])
+def test_small_down_ring_batches(active):
+    """Sixteen tokens whose top-8 cover exactly `active` experts, one 16-row
+    tile each: the small-path down's waves take up to 32 tiles against 8
+    ring slots, so runs of 9, 16, 17, 25 and 32 tiles exercise the reloads
+    of full batches, of a last partial batch (slots past the run reload its
+    last tile and skip its products) and none. Output, mid and routing equal
+    the oracle's bit for bit."""
+    shape = X.Shape(M=16, H=1024, E=128, I=256, top_k=8)
+    d = X.make_inputs(shape, "normal", 500 + active)
+    lg = np.random.default_rng(active).standard_normal((16, 128)).astype(np.float32)
+    for t in range(16):
+        for j in range(8):
+            lg[t, (8 * t + j) % active] = np.float32(10.0 - 0.5 * j)  # slot j: expert (8t + j) mod active
+    d["logits"] = lg
+    gout, gi = run(d)
+    ref = oracle(d)
+    assert int(np.count_nonzero(ref["count"])) == active
+    _check_routing(gi, ref["ids"], ref["w"], ref["count"], ref["offset"], ref["sorted_entry"])
+    _check_mid(gi["midq"], gi["mids"], ref["midq"], ref["mids"])
+    assert _check_out(gout, ref["out"]) == 0, "expected the oracle's bf16 output exactly"
