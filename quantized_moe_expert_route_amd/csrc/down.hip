@@ -82,7 +82,7 @@ size_t down_combine_lds_bytes(int64_t n, int64_t I, bool mid_lds, bool mid_bf16)
 
 // SH: the block-FP8 shared expert runs inside this launch (its own
 // instantiations, so that the routed-only ones carry none of its registers)
-template <int NB, int D, bool MID_LDS, int ST = 8, bool SH = false>
+template <int NB, int D, bool MID_LDS, int ST = 8, bool SH = false, bool LONG = true>
 __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
     const uint8_t* __restrict__ midq, const float* __restrict__ mids, const uint8_t* __restrict__ w2, const uint8_t* __restrict__ s2, const int* __restrict__ sorted_entry,
     const int4* __restrict__ tiles, const int* __restrict__ meta, int tmax, int H, int k, int M, int cw,
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
       if (d + 1 < D) compute(T[d + 1], S[d + 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
-  } else if (my > D) {
+  } else if (LONG && my > D) {  // (without LONG the launch guarantees my <= D)
     // while tiles remain after the batch in the slots, each slot is
     // reloaded as soon as its tile is computed, so the next batch's loads
     // overlap this batch's products; slots past the wave's run reload its
@@ -430,22 +430,29 @@ hipError_t launch_down_combine(const moe_plan* p, const CallArgs& a, Ev ev) {
                     wsp<int>(p, p->X.meta), tmax, H, (int)p->s.top_k, (int)a.M, cw, wsp<float>(p, p->L.topk_w), ys,
                     reinterpret_cast<uint16_t*>(a.out), tp_own_partial(p), sh);
   };
-  // weights of D tiles in flight per wave; fewer when the slots also carry mid rows
-  auto pick = [&](auto shc) {
-    constexpr bool S = decltype(shc)::value;
+  // weights of D tiles in flight per wave; fewer when the slots also carry
+  // mid rows. A call of at most kDcWaves * D entries has at most that many
+  // tiles, so no wave has more tiles than slots: its kernel carries no
+  // reload path (which alone made the c1 down ~0.7 us slower).
+  auto pick = [&](auto shc, auto lc) {
+    constexpr bool S = decltype(shc)::value, L = decltype(lc)::value;
     switch (I / 128) {
-      case 1: return !mid_lds ? go(down_combine_kernel<1, 6, false, 8, S>)
-                     : wide   ? go(down_combine_kernel<1, 8, true, 12, S>) : go(down_combine_kernel<1, 8, true, 8, S>);
-      case 2: return !mid_lds ? go(down_combine_kernel<2, 3, false, 8, S>)
-                     : wide   ? go(down_combine_kernel<2, 8, true, 12, S>) : go(down_combine_kernel<2, 8, true, 8, S>);
-      case 3: return !mid_lds ? go(down_combine_kernel<3, 2, false, 8, S>)
-                     : wide   ? go(down_combine_kernel<3, 5, true, 12, S>) : go(down_combine_kernel<3, 5, true, 8, S>);
-      case 4: return !mid_lds ? go(down_combine_kernel<4, 2, false, 8, S>)
-                     : wide   ? go(down_combine_kernel<4, 4, true, 12, S>) : go(down_combine_kernel<4, 4, true, 8, S>);
+      case 1: return !mid_lds ? go(down_combine_kernel<1, 6, false, 8, S, L>)
+                     : wide   ? go(down_combine_kernel<1, 8, true, 12, S, L>) : go(down_combine_kernel<1, 8, true, 8, S, L>);
+      case 2: return !mid_lds ? go(down_combine_kernel<2, 3, false, 8, S, L>)
+                     : wide   ? go(down_combine_kernel<2, 8, true, 12, S, L>) : go(down_combine_kernel<2, 8, true, 8, S, L>);
+      case 3: return !mid_lds ? go(down_combine_kernel<3, 2, false, 8, S, L>)
+                     : wide   ? go(down_combine_kernel<3, 5, true, 12, S, L>) : go(down_combine_kernel<3, 5, true, 8, S, L>);
+      case 4: return !mid_lds ? go(down_combine_kernel<4, 2, false, 8, S, L>)
+                     : wide   ? go(down_combine_kernel<4, 4, true, 12, S, L>) : go(down_combine_kernel<4, 4, true, 8, S, L>);
       default: return hipErrorInvalidValue;
     }
   };
-  return sh.hq ? pick(std::true_type()) : pick(std::false_type());
+  const int nb = (int)(I / 128);
+  const int64_t d_slots = !mid_lds ? (nb == 1 ? 6 : nb == 2 ? 3 : 2) : (nb <= 2 ? 8 : nb == 3 ? 5 : 4);
+  const bool lng = n > kDcWaves * d_slots;
+  if (sh.hq) return lng ? pick(std::true_type(), std::true_type()) : pick(std::true_type(), std::false_type());
+  return lng ? pick(std::false_type(), std::true_type()) : pick(std::false_type(), std::false_type());
 }
 
 hipError_t launch_combine(const moe_plan* p, const CallArgs& a, Ev ev) {
