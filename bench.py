@@ -201,6 +201,36 @@ def measure(name, steps, warmup, n_sets, mid_fmt=0, tp_loopback=0):
     torch.cuda.synchronize()
     graph_us = np.array([a.elapsed_time(b) * 1000.0 for a, b in zip(ev0, ev1)])
 
+    # cold calls as a difference of two graphs (the protocol's cross-check):
+    # R x [flush, call] against R x [flush], each replayed whole and timed by
+    # events around the replay; no host launch gaps and no event packets
+    # between the call's kernels (one input set)
+    R = 16
+    x.copy_(sets[0][0])
+    logits.copy_(sets[0][1])
+    torch.cuda.synchronize()
+    g_f, g_fc = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_f):
+        for _ in range(R):
+            torch.sum(flush, 0, out=sink)
+    with torch.cuda.graph(g_fc):
+        for _ in range(R):
+            torch.sum(flush, 0, out=sink)
+            call()
+    torch.cuda.synchronize()
+    t_f, t_fc = [], []
+    for rep in range(6):
+        for gr, acc in ((g_f, t_f), (g_fc, t_fc)):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            gr.replay()
+            b.record()
+            torch.cuda.synchronize()
+            if rep:  # the first replay of each warms up
+                acc.append(a.elapsed_time(b) * 1000.0)
+    graph_delta_us = (float(np.median(t_fc)) - float(np.median(t_f))) / R
+    del g_f, g_fc
+
     # warm: the same inputs back to back (weights partly MALL-resident)
     x.copy_(sets[0][0])
     logits.copy_(sets[0][1])
@@ -239,6 +269,7 @@ def measure(name, steps, warmup, n_sets, mid_fmt=0, tp_loopback=0):
     mean_act = float(np.mean(per_set_act))
     res = {
         "name": name, "shape": s, "cold_us": cold_us, "graph_us": graph_us, "warm_us": warm_us, "wall_s": wall,
+        "graph_delta_us": graph_delta_us,
         "stage_us": dict(zip(names, kern_us.mean(0).tolist())), "n_act": mean_act,
         "n_act_sets": n_act, "bytes": float(np.mean([call_bytes(s, a) for a in per_set_act])),
         "gate_up_bytes": float(np.mean([gate_up_bytes(s, a) for a in per_set_act])),
@@ -400,7 +431,8 @@ def main():
     from quantized_moe_expert_route_amd import fixtures as X
 
     head = measure(args.config, args.steps, args.warmup, args.sets)
-    print(f"[bench] {args.config}: cold {head['cold_us'].mean():.1f} us (graph replay {head['graph_us'].mean():.1f}), "
+    print(f"[bench] {args.config}: cold {head['cold_us'].mean():.1f} us (graph replay {head['graph_us'].mean():.1f}, "
+          f"graph difference {head['graph_delta_us']:.1f}), "
           f"warm {head['warm_us']:.1f} us, "
           f"stages {json.dumps({k: round(v, 1) for k, v in head['stage_us'].items()})}", file=sys.stderr, flush=True)
     others = {}
@@ -415,6 +447,7 @@ def main():
         name = f"{name}/mxfp4" if fmt else f"{name}/tp{tp}_loopback" if tp else name
         others[name] = {
             "us_per_call_cold": round(mu, 2), "us_per_call_graph_replay": round(float(r["graph_us"].mean()), 2),
+            "us_per_call_graph_difference": round(r["graph_delta_us"], 2),
             "us_per_call_warm": round(r["warm_us"], 2),
             "n_active_experts": round(r["n_act"], 1),
             "hbm_frac": round(r["bytes"] / (mu * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
@@ -449,6 +482,7 @@ def main():
         },
         "us_per_call_p50": round(float(np.median(head["cold_us"])), 3),
         "us_per_call_graph_replay": round(float(head["graph_us"].mean()), 3),
+        "us_per_call_graph_difference": round(head["graph_delta_us"], 3),
         "us_per_call_warm": round(head["warm_us"], 3),
         "hbm_frac_call": round(head["bytes"] / (mu * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "fp4_mfma_frac_call": round(head["flops"] / (mu * 1e-6) / 1e12 / FP4_PEAK_TFLOPS, 6),

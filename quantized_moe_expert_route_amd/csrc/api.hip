@@ -159,8 +159,9 @@ hipError_t enqueue_call(const moe_plan* plan, const CallArgs& a) {
   Ev ev[kStages];
   if (plan->n_events)
     for (int i = 0; i < kStages; ++i) ev[i] = Ev{plan->events[2 * i], plan->events[2 * i + 1]};
+  const bool rq = rq_path(plan, M);  // gate/up routes for itself: no routing launch
   if (plan->call_start) {
-    ev[0].start = plan->call_start;             // the route launch comes first
+    ev[rq ? 2 : 0].start = plan->call_start;    // the route launch (or the routing gate/up) comes first
     // down (+ combine), the combine, or the exchange comes last
     ev[fused_combine && plan->tpx.tp == 0 ? 5 : 6].stop = plan->call_stop;
   }
@@ -173,7 +174,10 @@ hipError_t enqueue_call(const moe_plan* plan, const CallArgs& a) {
   // Up to kSmallM tokens: routing + sort + x quantization in one launch
   // (workgroup 0 routes and sorts, the others quantize x); gate/up on 16-row
   // tiles; the mid quantization; down with the combine (a workgroup owns 16
-  // output columns of every slot, so the slot results never leave it).
+  // output columns of every slot, so the slot results never leave it). Up
+  // to kRqM tokens (rq_path) gate/up routes, sorts and quantizes x itself.
+  // (With the block-FP8 shared expert the routing launch also runs its
+  // gate/up partials, so that case keeps it.)
   // Above kSmallM: routing spread over the GPU, a second launch sorts;
   // gate/up on 16-row tiles and the mid quantization up to kMidM tokens (in
   // one launch where M k >= 8 E: gq_path), above on 64-row tiles with the
@@ -186,13 +190,14 @@ hipError_t enqueue_call(const moe_plan* plan, const CallArgs& a) {
   // counter: the device-scope release/acquire that needs writes back and
   // invalidates a whole L2 of an XCD per workgroup and costs more than a
   // launch.
-  hipError_t e = small ? launch_route_small(plan, a, ev[0]) : launch_route(plan, a, ev[0]);
+  hipError_t e = rq ? none(0) : small ? launch_route_small(plan, a, ev[0]) : launch_route(plan, a, ev[0]);
   if (e == hipSuccess) e = small ? none(1) : launch_align(plan, a, ev[1]);
   const bool tiles16 = mid_path(M, plan->s.top_k);  // 16-row-tile gate/up, mid quantization on its own
   const bool gq = gq_path(plan, M);  // 16-row tiles, the mid quantized inside gate/up
   if (e == hipSuccess)
-    e = gq ? launch_gate_up_quant(plan, a, ev[2]) : tiles16 ? launch_gate_up(plan, a, ev[2])
-                                                            : launch_gate_up_big(plan, a, ev[2]);
+    e = rq ? launch_gate_up_route(plan, a, ev[2]) : gq ? launch_gate_up_quant(plan, a, ev[2])
+        : tiles16 ? launch_gate_up(plan, a, ev[2])
+                  : launch_gate_up_big(plan, a, ev[2]);
   if (e == hipSuccess)
     e = !tiles16 || gq ? none(3) : mx ? launch_act_quant_mx(plan, a, ev[3]) : launch_act_quant(plan, a, ev[3]);
   // (a fused shared expert runs inside the routed launches: no pass of its own)
@@ -261,7 +266,7 @@ int moe_plan_stage_launches(const moe_plan* plan, int64_t M, int stage) {
   const bool small = small_path(M, plan->s.top_k);
   const bool mx = plan->mid_fmt == MOE_MID_MXFP4;
   switch (stage) {
-    case 0: return 1;                             // route + x quantization (+ sort when small; + the shared expert's x when large, its gate/up partials when fused)
+    case 0: return rq_path(plan, M) ? 0 : 1;      // route + x quantization (+ sort when small; + the shared expert's x when large, its gate/up partials when fused); inside gate/up on the rq path
     case 1: return small ? 0 : mid_path(M, plan->s.top_k) ? 1 : 2;  // align
     case 2: return 1;                             // gate_up (+ mid quantization when large)
     case 3: return mid_path(M, plan->s.top_k) && !gq_path(plan, M) ? 1 : 0;  // act_quant (inside gate/up above kMidM and on the gq path)

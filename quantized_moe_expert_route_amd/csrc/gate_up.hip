@@ -21,6 +21,7 @@
 // gate/up and the mid quantization in one launch on larger work items.
 #include "common.h"
 #include "internal.h"
+#include "route_common.h"
 #include "shared_small.h"
 
 #include <algorithm>
@@ -131,6 +132,207 @@ __global__ __launch_bounds__(256) void gate_up_m16_kernel(
       const float G = ((red[0][0][l][i] + red[0][1][l][i]) + red[0][2][l][i]) + red[0][3][l][i];
       const float U = ((red[1][0][l][i] + red[1][1][l][i]) + red[1][2][l][i]) + red[1][3][l][i];
       if (r0 + m < r1) hout[(size_t)(r0 + m) * I + it * 16 + n] = silu_mul(G, U);
+    }
+    __syncthreads();
+  }
+}
+
+// Gate/up that routes for itself (rq_path: up to kRqM tokens, E <= kRqMaxE,
+// H <= kRqMaxH, the E4M3 mid, no shared expert): the call has no routing
+// launch. Every workgroup ranks the M tokens' logits (a wave per token, the
+// rounds of the routing launch, so the same ids and weights), orders the
+// M k entries expert-major in LDS (each expert holds at most M <= 16 rows:
+// one 16-row tile per active expert), finds its item's expert and rows,
+// issues the item's x and weight loads, and quantizes its rows of x to MXFP4
+// into LDS while the weights are in flight; then the item runs as in
+// gate_up_m16_kernel, x read from LDS. Workgroup 0 stores the routing, the
+// sort and the tiles for the launches after this one; the workgroup of each
+// tile's first column group stores its rows' x codes. The weights thus start
+// moving one logits round trip after the launch, where a routing launch of
+// its own put its whole span (launch, logits, ranking, sort, stores) first
+// ("glm53: FP8 mid hand-off, ...", Modifications table, row "per-row up/gate
+// jobs": the routing rounds overlapped with the first weight loads).
+constexpr int kRqXB = kRqM * (kRqMaxH / 32) / 256;  // x blocks a thread quantizes (at most)
+static_assert(kRqM * (kRqMaxH / 32) % 256 == 0 && kRqMaxH / 512 <= 4 * kSS, "rq tile shape");
+
+template <int EC>
+__global__ __launch_bounds__(256) void gate_up_route_kernel(
+    const float* __restrict__ logits, const uint16_t* __restrict__ x, int M, int E, int k, int H, float scaling,
+    const uint8_t* __restrict__ w13p, const uint8_t* __restrict__ s13p, int I, int* __restrict__ topk_ids,
+    float* __restrict__ topk_w, int* __restrict__ count, int* __restrict__ offset, int* __restrict__ sorted_entry,
+    int4* __restrict__ tiles, int* __restrict__ meta, uint8_t* __restrict__ xq, uint8_t* __restrict__ xs,
+    float* __restrict__ hout) {
+  __shared__ v4f red[2][4][64];
+  __shared__ uint32_t s_bits[kRqMaxE];  // expert -> its tokens (bit t)
+  __shared__ int s_ids[kRqM * 16];      // entry t k + j -> expert
+  __shared__ int s_off[kRqMaxE + 1];    // expert -> its first sorted row
+  __shared__ int s_te[kRqMaxE];         // tile -> expert
+  __shared__ int s_tmp[4];
+  __shared__ __align__(16) uint8_t s_xq[kRqM][kRqMaxH / 2];   // the tile's rows of x: E2M1 codes
+  __shared__ __align__(16) uint8_t s_xs[kRqM][kRqMaxH / 32];  // and E8M0 scales
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r = lane & 15, g = lane >> 4;
+
+  // ---- routing: wave t ranks token t (its logits requested first)
+  uint32_t key[EC];
+  load_keys<EC>(logits + (size_t)min(wave, M - 1) * E, E, lane, key);
+  s_bits[tid] = 0u;  // kRqMaxE == blockDim
+  __syncthreads();
+  if (wave < M) {
+    uint32_t sel_e = 0;
+    float w = 0.f;
+    route_keys<EC>(key, E, k, scaling, 0, lane, sel_e, w);
+    if (lane < k) {
+      s_ids[wave * k + lane] = (int)sel_e;
+      atomicOr(&s_bits[sel_e], 1u << wave);
+      if (blockIdx.x == 0) {
+        topk_ids[wave * k + lane] = (int)sel_e;
+        topk_w[wave * k + lane] = w;
+      }
+    }
+  }
+  __syncthreads();
+  // counts, offsets and the tile list: thread e, one packed scan of
+  // rows | tiles << 16 (a tile per active expert)
+  const int c = tid < E ? __popc(s_bits[tid]) : 0;
+  const int v = c | ((c > 0 ? 1 : 0) << 16);
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int nb = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += nb;
+  }
+  if (lane == 63) s_tmp[wave] = incl;
+  __syncthreads();
+  int pre = incl - v;
+  for (int ww = 0; ww < wave; ++ww) pre += s_tmp[ww];
+  const int total = s_tmp[0] + s_tmp[1] + s_tmp[2] + s_tmp[3];
+  const int nt = total >> 16;
+  if (tid < E) {
+    s_off[tid] = pre & 0xFFFF;
+    if (c) s_te[pre >> 16] = tid;
+  }
+  __syncthreads();
+  if (blockIdx.x == 0) {  // the routing, the sort and the tiles for the later launches
+    if (tid < E) {
+      count[tid] = c;
+      offset[tid] = pre & 0xFFFF;
+      if (c) tiles[pre >> 16] = make_int4(tid, pre & 0xFFFF, (pre & 0xFFFF) + c, 0);
+    }
+    if (tid == 0) {
+      offset[E] = total & 0xFFFF;
+      meta[0] = nt;
+    }
+    if (tid < M * k) {
+      const int e = s_ids[tid], t = tid / k;
+      sorted_entry[s_off[e] + __popc(s_bits[e] & ((1u << t) - 1u))] = tid;
+    }
+  }
+
+  const int n_it = I / 16;
+  const int n_work = nt * n_it;
+  const size_t Hs = (size_t)H / 32;
+  const int nss = H / 512, nks = H / 128, nblk = H / 32;
+  const size_t nrb = (size_t)I / 8;  // 16-row blocks of an expert's 2I rows
+  const int per = (nss + 3) / 4;     // super-steps a wave owns (at most kSS)
+  const int ss_beg = min(nss, wave * per), ss_end = min(nss, (wave + 1) * per);
+  for (int wi = blockIdx.x; wi < n_work; wi += gridDim.x) {
+    const int it = wi % n_it;
+    const int e = s_te[wi / n_it];
+    const uint32_t bits = s_bits[e];
+    const int r0 = s_off[e], nrow = __popc(bits);
+    // x of the tile's rows: thread b takes blocks b, b + 256, ... of the
+    // nrow x H/32 (row, 32-block) pairs, loaded before the weights so that
+    // waiting for them does not wait for the weights (past the last pair:
+    // its last block again, not used)
+    const int nxb = nrow * nblk;
+    uint4 xv[kRqXB][4];
+    int xrow[kRqXB], xblk[kRqXB];
+#pragma unroll
+    for (int q = 0; q < kRqXB; ++q) {
+      const int b = min(tid + 256 * q, nxb - 1);
+      xrow[q] = b / nblk;
+      xblk[q] = b - xrow[q] * nblk;
+      uint32_t rb = bits;  // token of row xrow[q]: its xrow[q]-th set bit
+      for (int z = 0; z < xrow[q]; ++z) rb &= rb - 1u;
+      const uint16_t* src = x + (size_t)(__ffs(rb) - 1) * H + 32 * xblk[q];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) xv[q][u] = ld16(src + 8 * u);
+    }
+    // the wave's weight fragments, all its super-steps at once
+    const size_t rbg = (size_t)e * nrb + it, rbu = rbg + I / 16;
+    const uint8_t* pg = w13p + rbg * nks * 1024 + 16 * lane;  // + 1024 ks
+    const uint8_t* pu = w13p + rbu * nks * 1024 + 16 * lane;
+    const uint8_t* psg = s13p + rbg * nss * 256 + 4 * lane;  // + 256 ss: byte j is K-step 4 ss + j
+    const uint8_t* psu = s13p + rbu * nss * 256 + 4 * lane;
+    uint4 bg[kSS][4], bu[kSS][4];
+    uint32_t sg[kSS], su[kSS];
+#pragma unroll
+    for (int q = 0; q < kSS; ++q) {
+      const int ss = min(ss_beg + q, ss_end - 1);  // clamped (also for a wave without steps): loaded, not used
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bg[q][j] = ld16(pg + (size_t)(4 * ss + j) * 1024);
+        bu[q][j] = ld16(pu + (size_t)(4 * ss + j) * 1024);
+      }
+      sg[q] = ld4(psg + 256 * ss);
+      su[q] = ld4(psu + 256 * ss);
+    }
+    // x -> MXFP4 into LDS (the routing launch's quantizer, the same codes)
+#pragma unroll
+    for (int q = 0; q < kRqXB; ++q) {
+      if (tid + 256 * q < nxb) {
+        uint32_t w32[16];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          w32[4 * u] = xv[q][u].x; w32[4 * u + 1] = xv[q][u].y; w32[4 * u + 2] = xv[q][u].z; w32[4 * u + 3] = xv[q][u].w;
+        }
+        quant_block_mx_words(w32, &s_xq[xrow[q]][16 * xblk[q]], &s_xs[xrow[q]][xblk[q]]);
+      }
+    }
+    __syncthreads();
+    if (it == 0) {  // the tile's rows of x for the caller (a token in several tiles: the same bytes again)
+      const int rowb = (int)(H / 2 + Hs);
+      for (int b = tid; b < nrow * (rowb / 16); b += 256) {
+        const int rr = b / (rowb / 16), o = 16 * (b - rr * (rowb / 16));
+        uint32_t rb = bits;
+        for (int z = 0; z < rr; ++z) rb &= rb - 1u;
+        const size_t t = (size_t)(__ffs(rb) - 1);
+        if (o < H / 2) *reinterpret_cast<uint4*>(xq + t * (H / 2) + o) = *reinterpret_cast<const uint4*>(&s_xq[rr][o]);
+        else *reinterpret_cast<uint4*>(xs + t * Hs + (o - H / 2)) = *reinterpret_cast<const uint4*>(&s_xs[rr][o - H / 2]);
+      }
+    }
+    // the products: lane 16 g + r supplies row r's MX block 4 ks + g
+    const bool rv = r < nrow;
+    const int rl = rv ? r : 0;
+    v4f accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < kSS; ++q) {
+      const int ss = ss_beg + q;
+      if (ss < ss_end) {
+        const uint4 sa = rv ? *reinterpret_cast<const uint4*>(&s_xs[rl][16 * ss])
+                            : make_uint4(0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu);
+        const uint32_t xw[4] = {sa.x, sa.y, sa.z, sa.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint4 a = rv ? *reinterpret_cast<const uint4*>(&s_xq[rl][64 * (4 * ss + j) + 16 * g])
+                             : make_uint4(0, 0, 0, 0);
+          const uint32_t xa = (xw[j] >> (8 * g)) & 0xFFu;
+          accg = mfma_fp4(a, bg[q][j], accg, xa, (sg[q] >> (8 * j)) & 0xFFu);
+          accu = mfma_fp4(a, bu[q][j], accu, xa, (su[q] >> (8 * j)) & 0xFFu);
+        }
+      }
+    }
+    red[0][wave][lane] = accg;
+    red[1][wave][lane] = accu;
+    __syncthreads();
+    {
+      // thread -> (row m, column n) of the 16x16 item
+      const int m = tid >> 4, n = tid & 15;
+      const int l = n + 16 * (m >> 2), i = m & 3;
+      const float G = ((red[0][0][l][i] + red[0][1][l][i]) + red[0][2][l][i]) + red[0][3][l][i];
+      const float U = ((red[1][0][l][i] + red[1][1][l][i]) + red[1][2][l][i]) + red[1][3][l][i];
+      if (m < nrow) hout[(size_t)(r0 + m) * I + it * 16 + n] = silu_mul(G, U);
     }
     __syncthreads();
   }
@@ -333,6 +535,23 @@ hipError_t launch_gate_up(const moe_plan* p, const CallArgs& a, Ev ev) {
                   wsp<uint8_t>(p, p->L.xs), reinterpret_cast<const uint8_t*>(a.w13),
                   reinterpret_cast<const uint8_t*>(a.s13), wsp<int>(p, p->L.sorted_entry), wsp<int4>(p, p->X.tiles),
                   wsp<int>(p, p->X.meta), wsp<float>(p, p->X.h), (int)p->s.H, I, (int)p->s.top_k);
+}
+
+hipError_t launch_gate_up_route(const moe_plan* p, const CallArgs& a, Ev ev) {
+  const int I = (int)p->s.I, E = (int)p->s.E, H = (int)p->s.H;
+  if (a.M > kRqM || E > kRqMaxE || H > kRqMaxH || p->s.top_k > 16) return hipErrorInvalidValue;
+  const int64_t n = a.M * p->s.top_k;
+  const int64_t tiles = std::min<int64_t>(E, n);  // one tile per active expert
+  const int blocks = (int)std::min<int64_t>(tiles * (I / 16), 2048);
+  auto go = [&](auto kern) {
+    return launch_k(kern, dim3(blocks), dim3(256), 0, a.stream, ev, a.logits, reinterpret_cast<const uint16_t*>(a.x),
+                    (int)a.M, E, (int)p->s.top_k, H, p->s.routed_scaling, reinterpret_cast<const uint8_t*>(a.w13),
+                    reinterpret_cast<const uint8_t*>(a.s13), I, wsp<int>(p, p->L.topk_ids),
+                    wsp<float>(p, p->L.topk_w), wsp<int>(p, p->L.count), wsp<int>(p, p->L.offset),
+                    wsp<int>(p, p->L.sorted_entry), wsp<int4>(p, p->X.tiles), wsp<int>(p, p->X.meta),
+                    wsp<uint8_t>(p, p->L.xq), wsp<uint8_t>(p, p->L.xs), wsp<float>(p, p->X.h));
+  };
+  return E <= 64 ? go(gate_up_route_kernel<1>) : E <= 128 ? go(gate_up_route_kernel<2>) : go(gate_up_route_kernel<4>);
 }
 
 hipError_t launch_act_quant(const moe_plan* p, const CallArgs& a, Ev ev) {

@@ -147,6 +147,17 @@ inline bool gq_path(const moe_plan* p, int64_t M) {
   return mid_path(M, p->s.top_k) && M * p->s.top_k >= 8 * p->s.E && p->s.H % 2048 == 0 && p->s.H <= kGqMaxH;
 }
 hipError_t launch_gate_up_quant(const moe_plan* p, const CallArgs& a, Ev ev);
+// Up to kRqM tokens (E <= kRqMaxE, H <= kRqMaxH, the E4M3 mid, no shared
+// expert, no shared slot): gate/up routes, sorts and quantizes x itself
+// (gate_up.hip), so the call has no routing launch.
+constexpr int kRqM = 4;
+constexpr int kRqMaxE = 256;
+constexpr int kRqMaxH = 6144;
+inline bool rq_path(const moe_plan* p, int64_t M) {
+  return M >= 1 && M <= kRqM && p->s.E <= kRqMaxE && p->s.H <= kRqMaxH && p->s.top_k <= 16 &&
+         p->mid_fmt == MOE_MID_E4M3 && p->s.shared_I == 0 && !p->shared_slot;
+}
+hipError_t launch_gate_up_route(const moe_plan* p, const CallArgs& a, Ev ev);
 hipError_t launch_act_quant(const moe_plan* p, const CallArgs& a, Ev ev);
 // small M: down and the combine in one launch; y stays on chip
 int down_combine_cols(int H, int cus);

@@ -258,7 +258,7 @@ def test_shared_x_codes_on_exact_midpoints():
     _check_out(gout, ref["out"])
 
 
-@pytest.mark.parametrize("M", [6, 40, 300])  # small, mid-range and large paths
+@pytest.mark.parametrize("M", [3, 6, 40, 300])  # routing inside gate/up, small, mid-range and large paths
 def test_degenerate_inputs(M):
     """x = 0; all logits -inf (every token on experts 0..k-1 with weight 0:
     the most skewed sort); all logits equal."""
@@ -539,4 +539,31 @@ def test_small_down_ring_batches(active):
     assert int(np.count_nonzero(ref["count"])) == active
     _check_routing(gi, ref["ids"], ref["w"], ref["count"], ref["offset"], ref["sorted_entry"])
     _check_mid(gi["midq"], gi["mids"], ref["midq"], ref["mids"])
+    assert _check_out(gout, ref["out"]) == 0, "expected the oracle's bf16 output exactly"
+
+
+@pytest.mark.parametrize("M,H,E,I,k,kind,inside", [
+    (1, 6144, 256, 256, 8, "uniform", True),
+    (2, 2048, 200, 256, 8, "ties", True),      # tied logits: the lower expert id wins, as in the routing launch
+    (3, 2048, 128, 128, 4, "normal", True),
+    (4, 1024, 64, 512, 2, "normal", True),
+    (4, 512, 16, 128, 16, "normal", True),     # k = E: every expert active
+    (4, 6144, 256, 256, 8, "uniform", True),   # c1's shape
+    (5, 2048, 128, 256, 8, "uniform", False),  # past kRqM: the routing launch
+    (4, 8192, 64, 128, 4, "normal", False),    # past kRqMaxH: the routing launch
+])
+def test_routing_inside_gate_up(M, H, E, I, k, kind, inside):
+    """Up to 4 tokens (E <= 256, H <= 6144, no shared expert) the gate/up
+    launch routes, sorts and quantizes x itself: the call has no routing
+    launch. Ids, weights, counts, offsets, the sorted entries, x's codes, the
+    mid and the output equal the oracle's bit for bit on either path."""
+    shape = X.Shape(M=M, H=H, E=E, I=I, top_k=k)
+    d = X.make_inputs(shape, kind, 900 + M + E)
+    plan = make_plan(shape)
+    assert plan.stage_launches(M) == [0 if inside else 1, 0, 1, 1, 0, 1, 0]
+    gout, gi = run(d, plan=plan)
+    ref = oracle(d)
+    _check_routing(gi, ref["ids"], ref["w"], ref["count"], ref["offset"], ref["sorted_entry"])
+    _check_xq(gi, ref)
+    np.testing.assert_array_equal(gi["midq"], ref["midq"])
     assert _check_out(gout, ref["out"]) == 0, "expected the oracle's bf16 output exactly"
