@@ -175,7 +175,8 @@ hipError_t enqueue_call(const moe_plan* plan, const CallArgs& a) {
   // (workgroup 0 routes and sorts, the others quantize x); gate/up on 16-row
   // tiles; the mid quantization; down with the combine (a workgroup owns 16
   // output columns of every slot, so the slot results never leave it). Up
-  // to kRqM tokens (rq_path) gate/up routes, sorts and quantizes x itself.
+  // to kRqM tokens (rq_path) gate/up routes, sorts and quantizes x itself,
+  // and for at most kQdBlocks mid blocks (qd_path) down quantizes the mid.
   // (With the block-FP8 shared expert the routing launch also runs its
   // gate/up partials, so that case keeps it.)
   // Above kSmallM: routing spread over the GPU, a second launch sorts;
@@ -199,7 +200,9 @@ hipError_t enqueue_call(const moe_plan* plan, const CallArgs& a) {
         : tiles16 ? launch_gate_up(plan, a, ev[2])
                   : launch_gate_up_big(plan, a, ev[2]);
   if (e == hipSuccess)
-    e = !tiles16 || gq ? none(3) : mx ? launch_act_quant_mx(plan, a, ev[3]) : launch_act_quant(plan, a, ev[3]);
+    e = !tiles16 || gq || qd_path(plan, M) ? none(3)
+        : mx                              ? launch_act_quant_mx(plan, a, ev[3])
+                                          : launch_act_quant(plan, a, ev[3]);
   // (a fused shared expert runs inside the routed launches: no pass of its own)
   if (e == hipSuccess) e = plan->s.shared_I > 0 && !shared_fused(plan, M) ? launch_shared(plan, a, ev[4]) : none(4);
   if (e == hipSuccess)
@@ -269,7 +272,7 @@ int moe_plan_stage_launches(const moe_plan* plan, int64_t M, int stage) {
     case 0: return rq_path(plan, M) ? 0 : 1;      // route + x quantization (+ sort when small; + the shared expert's x when large, its gate/up partials when fused); inside gate/up on the rq path
     case 1: return small ? 0 : mid_path(M, plan->s.top_k) ? 1 : 2;  // align
     case 2: return 1;                             // gate_up (+ mid quantization when large)
-    case 3: return mid_path(M, plan->s.top_k) && !gq_path(plan, M) ? 1 : 0;  // act_quant (inside gate/up above kMidM and on the gq path)
+    case 3: return mid_path(M, plan->s.top_k) && !gq_path(plan, M) && !qd_path(plan, M) ? 1 : 0;  // act_quant (inside gate/up above kMidM and on the gq path, inside down on the qd path)
     case 4: return plan->s.shared_I > 0 && !shared_fused(plan, M) ? (small ? 4 : 3) : 0;  // shared expert (0: inside the routed launches)
     case 5: return 1;                             // down (+ combine when small, E4M3 mid)
     default: return (small && !mx ? 0 : 1) + (plan->tpx.tp > 0 ? 1 : 0);  // combine (+ the exchange)

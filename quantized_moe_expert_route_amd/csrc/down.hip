@@ -45,13 +45,29 @@ namespace qmoe {
 // they stay E4M3 (half the bytes) and each fragment is widened as it is
 // read (still once per workgroup, but on the MFMA's path: slower while the
 // bf16 rows fit). Otherwise each slot carries its tile's E4M3 mid rows in
-// registers and widens them itself. (Quantizing mid inside this launch
-// instead, redundantly per workgroup, measured slower than its own launch.)
+// registers and widens them itself.
+//
+// QF (qd_path: at most kQdBlocks (row, 128-block) pairs of mid, e.g. M = 4
+// at top-8 and I = 256): every workgroup quantizes mid itself from h with
+// the arithmetic of act_quant_kernel (s = fl32(amax / 448), q = E4M3(fl32(h
+// / s))) while its weights are in flight, and workgroup 0 stores the codes
+// and scales; the call then has no act_quant launch. Sixteen lanes hold the
+// 128 values of a block, eight each.
 constexpr int kDcThreads = 256;
 constexpr int kDcWaves = kDcThreads / 64;
 constexpr int kDcMidBytes = 32 * 1024;  // n * I staged in LDS from E4M3: ST = 8 uint4 per thread
 constexpr int kDcMidBytesMax = 48 * 1024;  // ST = 12: n up to 192 at I = 256 (the shared expert as a ninth slot)
 constexpr int kDcPad = 16;              // LDS bytes after each staged mid row
+constexpr int kQdPasses = kQdBlocks / (kDcThreads / 16);  // blocks of h a thread quantizes (QF)
+static_assert(2 * kQdPasses == 8, "QF stages h in the 8 staging registers of a thread");
+
+// the largest of a value over the 16 lanes of a DPP row (every lane gets it)
+__device__ __forceinline__ uint32_t max16_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // half-row mirror
+  return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row mirror
+}
 
 template <int NB, bool MID_LDS>
 struct DcSlot {
@@ -82,14 +98,16 @@ size_t down_combine_lds_bytes(int64_t n, int64_t I, bool mid_lds, bool mid_bf16)
 
 // SH: the block-FP8 shared expert runs inside this launch (its own
 // instantiations, so that the routed-only ones carry none of its registers)
-template <int NB, int D, bool MID_LDS, int ST = 8, bool SH = false, bool LONG = true>
+template <int NB, int D, bool MID_LDS, int ST = 8, bool SH = false, bool LONG = true, bool QF = false>
 __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
     const uint8_t* __restrict__ midq, const float* __restrict__ mids, const uint8_t* __restrict__ w2, const uint8_t* __restrict__ s2, const int* __restrict__ sorted_entry,
     const int4* __restrict__ tiles, const int* __restrict__ meta, int tmax, int H, int k, int M, int cw,
     const float* __restrict__ topk_w, const float* __restrict__ ys, uint16_t* __restrict__ out,
-    double* __restrict__ partial, SharedSmall sh) {
+    double* __restrict__ partial, SharedSmall sh, const float* __restrict__ hin, uint8_t* __restrict__ mq_out,
+    float* __restrict__ ms_out) {
   constexpr int I = NB * 128;
   constexpr bool A16 = ST == 8;  // mid staged widened to bf16 (else E4M3, widened at each read)
+  static_assert(!QF || (MID_LDS && A16 && !SH), "QF stages the quantized mid as bf16 rows");
   constexpr int LDA = (A16 ? 2 : 1) * I + kDcPad;  // bytes per staged mid row; the pad spreads 16 rows over the banks
   extern __shared__ __align__(16) uint8_t dyn[];
   const int n = M * k;
@@ -141,7 +159,22 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
   constexpr int kSs = ST == 8 ? 1 : 2;  // mid scales and entries a thread stages (n * NB <= kSs * kDcThreads)
   float sts[kSs];
   int ste[kSs];
-  if (MID_LDS) {
+  if (QF) {
+    // h of block qb = 16 p + tid / 16 (row qb / NB, block qb % NB), the
+    // lane's 8 values; past the last block the last one again (unused)
+#pragma unroll
+    for (int p = 0; p < kQdPasses; ++p) {
+      const int qb = min(16 * p + (tid >> 4), n * NB - 1);
+      const float* ph = hin + (size_t)(qb / NB) * I + 128 * (qb % NB) + 8 * (tid & 15);
+      st[2 * p] = ld16(ph);
+      st[2 * p + 1] = ld16(ph + 4);
+    }
+#pragma unroll
+    for (int q = 0; q < kSs; ++q) {
+      const int idx = tid + kDcThreads * q;
+      ste[q] = idx < n ? sorted_entry[idx] : 0;
+    }
+  } else if (MID_LDS) {
 #pragma unroll
     for (int q = 0; q < kSt; ++q) {
       const int idx = tid + kDcThreads * q;
@@ -242,7 +275,44 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
   }
 
   // ---- staged mid to LDS (widened to bf16 when A16)
-  if (MID_LDS) {
+  if (QF) {
+#pragma unroll
+    for (int p = 0; p < kQdPasses; ++p) {
+      const uint4 v0 = st[2 * p], v1 = st[2 * p + 1];
+      const uint32_t vb[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      uint32_t am = 0;  // |h| bit patterns order as the values do
+#pragma unroll
+      for (int i = 0; i < 8; ++i) am = max(am, vb[i] & 0x7FFFFFFFu);
+      am = max16_u32(am);
+      const float sc = __fdiv_rn(__uint_as_float(am), 448.0f);
+      uint32_t lo = 0, hi = 0;
+      if (sc > 0.f) {
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+          lo |= e4m3_pack2(__fdiv_rn(__uint_as_float(vb[i]), sc), __fdiv_rn(__uint_as_float(vb[i + 1]), sc)) << (8 * i);
+          hi |= e4m3_pack2(__fdiv_rn(__uint_as_float(vb[4 + i]), sc), __fdiv_rn(__uint_as_float(vb[5 + i]), sc))
+                << (8 * i);
+        }
+      }
+      const int qb = 16 * p + (tid >> 4);
+      if (qb < n * NB) {
+        const int row = qb / NB, b = qb % NB, kk = 128 * b + 8 * (tid & 15);
+        *reinterpret_cast<uint4*>(ml + row * LDA + 2 * kk) =
+            make_uint4(fp8x2_bf16<false>(lo), fp8x2_bf16<true>(lo), fp8x2_bf16<false>(hi), fp8x2_bf16<true>(hi));
+        if ((tid & 15) == 0) msl[row * NB + b] = sc;
+        if (blockIdx.x == 0) {  // the codes and scales, as the act_quant launch stores them
+          *reinterpret_cast<uint2*>(mq_out + (size_t)row * I + kk) = make_uint2(lo, hi);
+          if ((tid & 15) == 0) ms_out[(size_t)row * NB + b] = sc;
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kSs; ++q) {
+      const int idx = tid + kDcThreads * q;
+      if (idx < n) sel[idx] = ste[q];
+    }
+    barrier_lds();
+  } else if (MID_LDS) {
 #pragma unroll
     for (int q = 0; q < kSt; ++q) {
       const int idx = tid + kDcThreads * q;
@@ -413,6 +483,7 @@ hipError_t launch_down_combine(const moe_plan* p, const CallArgs& a, Ev ev) {
   const int H = (int)p->s.H;
   const int64_t n = a.M * p->s.top_k, I = p->s.I;
   if (n > kSmallRows) return hipErrorInvalidValue;
+  const bool qf = qd_path(p, a.M);  // the mid quantized here from h (no act_quant launch)
   const bool mid_lds = n * I <= kDcMidBytesMax && n * (I / 128) <= 2 * kDcThreads && n <= 2 * kDcThreads;
   const bool wide = n * I > kDcMidBytes;  // 12 staging registers a thread instead of 8
   const SharedSmall sh = shared_small(p, a.M);  // the shared expert inside this launch, or none
@@ -428,8 +499,10 @@ hipError_t launch_down_combine(const moe_plan* p, const CallArgs& a, Ev ev) {
                     wsp<float>(p, p->L.mids), reinterpret_cast<const uint8_t*>(a.w2),
                     reinterpret_cast<const uint8_t*>(a.s2), wsp<int>(p, p->L.sorted_entry), wsp<int4>(p, p->X.tiles),
                     wsp<int>(p, p->X.meta), tmax, H, (int)p->s.top_k, (int)a.M, cw, wsp<float>(p, p->L.topk_w), ys,
-                    reinterpret_cast<uint16_t*>(a.out), tp_own_partial(p), sh);
+                    reinterpret_cast<uint16_t*>(a.out), tp_own_partial(p), sh, wsp<float>(p, p->X.h),
+                    wsp<uint8_t>(p, p->L.midq), wsp<float>(p, p->L.mids));
   };
+
   // weights of D tiles in flight per wave; fewer when the slots also carry
   // mid rows. A call of at most kDcWaves * D entries has at most that many
   // tiles, so no wave has more tiles than slots: its kernel carries no
@@ -451,6 +524,16 @@ hipError_t launch_down_combine(const moe_plan* p, const CallArgs& a, Ev ev) {
   const int nb = (int)(I / 128);
   const int64_t d_slots = !mid_lds ? (nb == 1 ? 6 : nb == 2 ? 3 : 2) : (nb <= 2 ? 8 : nb == 3 ? 5 : 4);
   const bool lng = n > kDcWaves * d_slots;
+  if (qf) {  // at most kQdBlocks mid blocks, no wave with more tiles than slots
+    if (!mid_lds || wide || sh.hq || lng) return hipErrorInvalidValue;
+    switch (nb) {
+      case 1: return go(down_combine_kernel<1, 8, true, 8, false, false, true>);
+      case 2: return go(down_combine_kernel<2, 8, true, 8, false, false, true>);
+      case 3: return go(down_combine_kernel<3, 5, true, 8, false, false, true>);
+      case 4: return go(down_combine_kernel<4, 4, true, 8, false, false, true>);
+      default: return hipErrorInvalidValue;
+    }
+  }
   if (sh.hq) return lng ? pick(std::true_type(), std::true_type()) : pick(std::true_type(), std::false_type());
   return lng ? pick(std::false_type(), std::true_type()) : pick(std::false_type(), std::false_type());
 }

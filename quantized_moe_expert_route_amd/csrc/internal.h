@@ -167,6 +167,16 @@ inline bool shared_fused(const moe_plan* p, int64_t M) {
   return p->s.shared_I > 0 && p->s.shared_I <= kSmallSharedI && p->mid_fmt == MOE_MID_E4M3 &&
          small_path(M, p->s.top_k);
 }
+// Up to kQdBlocks (row, 128-block) pairs of the E4M3 mid (M = 4 at top-8 and
+// I = 256) on the routing gate/up path (rq_path): every down workgroup
+// quantizes the mid from h itself while its weights are in flight
+// (workgroup 0 stores the codes), so the call has no act_quant launch.
+constexpr int kQdBlocks = 64;
+inline bool qd_path(const moe_plan* p, int64_t M) {
+  const int64_t n = M * p->s.top_k, nb = p->s.I / 128;
+  const int64_t slots = nb <= 2 ? 8 : nb == 3 ? 5 : 4;  // the small down's ring slots at this I
+  return rq_path(p, M) && n * nb <= kQdBlocks && n <= 4 * slots;  // no wave with more tiles than slots
+}
 // row-major E4M3 shared-expert weights -> digit rows: gate/up [2 Is, H/128,
 // 3, 128], then down [H, Is/128, 3, 128], then the E4M3 codes themselves
 // (gate/up [2 Is, H], down [H, Is]), at `packed` (shared.hip)

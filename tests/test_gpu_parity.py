@@ -542,28 +542,33 @@ def test_small_down_ring_batches(active):
     assert _check_out(gout, ref["out"]) == 0, "expected the oracle's bf16 output exactly"
 
 
-@pytest.mark.parametrize("M,H,E,I,k,kind,inside", [
-    (1, 6144, 256, 256, 8, "uniform", True),
-    (2, 2048, 200, 256, 8, "ties", True),      # tied logits: the lower expert id wins, as in the routing launch
-    (3, 2048, 128, 128, 4, "normal", True),
-    (4, 1024, 64, 512, 2, "normal", True),
-    (4, 512, 16, 128, 16, "normal", True),     # k = E: every expert active
-    (4, 6144, 256, 256, 8, "uniform", True),   # c1's shape
-    (5, 2048, 128, 256, 8, "uniform", False),  # past kRqM: the routing launch
-    (4, 8192, 64, 128, 4, "normal", False),    # past kRqMaxH: the routing launch
+@pytest.mark.parametrize("M,H,E,I,k,kind,inside,qd", [
+    (1, 6144, 256, 256, 8, "uniform", True, True),
+    (2, 2048, 200, 256, 8, "ties", True, True),     # tied logits: the lower expert id wins, as in the routing launch
+    (3, 2048, 128, 128, 4, "normal", True, True),
+    (4, 1024, 64, 512, 2, "normal", True, True),    # four mid blocks a row: 32 of 64 blocks
+    (4, 512, 16, 128, 16, "normal", True, False),   # k = E: every expert active; 64 rows, more than the ring holds
+    (4, 6144, 256, 256, 8, "uniform", True, True),  # c1's shape: 64 mid blocks, at the limit
+    (4, 2048, 64, 256, 12, "normal", True, False),  # 96 mid blocks: the mid quantization in its own launch
+    (4, 8192, 64, 128, 4, "normal", False, False),  # H past 6144: the routing launch
+    (4, 2048, 320, 128, 8, "uniform", False, False),  # E past 256: the routing launch
 ])
-def test_routing_inside_gate_up(M, H, E, I, k, kind, inside):
+def test_routing_inside_gate_up(M, H, E, I, k, kind, inside, qd):
     """Up to 4 tokens (E <= 256, H <= 6144, no shared expert) the gate/up
     launch routes, sorts and quantizes x itself: the call has no routing
-    launch. Ids, weights, counts, offsets, the sorted entries, x's codes, the
-    mid and the output equal the oracle's bit for bit on either path."""
+    launch; with at most 64 mid blocks (and no more 16-row tiles than the
+    small down's ring holds) each down workgroup also quantizes the mid from
+    h itself, so the call has no act_quant launch either. Ids, weights,
+    counts, offsets, the sorted entries, x's codes, the mid codes and scales
+    and the output equal the oracle's bit for bit on every path."""
     shape = X.Shape(M=M, H=H, E=E, I=I, top_k=k)
     d = X.make_inputs(shape, kind, 900 + M + E)
     plan = make_plan(shape)
-    assert plan.stage_launches(M) == [0 if inside else 1, 0, 1, 1, 0, 1, 0]
+    assert plan.stage_launches(M) == [0 if inside else 1, 0, 1, 0 if qd else 1, 0, 1, 0]
     gout, gi = run(d, plan=plan)
     ref = oracle(d)
     _check_routing(gi, ref["ids"], ref["w"], ref["count"], ref["offset"], ref["sorted_entry"])
     _check_xq(gi, ref)
     np.testing.assert_array_equal(gi["midq"], ref["midq"])
+    np.testing.assert_array_equal(gi["mids"].view(np.uint32), ref["mids"].astype(np.float32).view(np.uint32))
     assert _check_out(gout, ref["out"]) == 0, "expected the oracle's bf16 output exactly"
