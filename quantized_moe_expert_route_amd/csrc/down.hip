@@ -58,8 +58,7 @@ constexpr int kDcWaves = kDcThreads / 64;
 constexpr int kDcMidBytes = 32 * 1024;  // n * I staged in LDS from E4M3: ST = 8 uint4 per thread
 constexpr int kDcMidBytesMax = 48 * 1024;  // ST = 12: n up to 192 at I = 256 (the shared expert as a ninth slot)
 constexpr int kDcPad = 16;              // LDS bytes after each staged mid row
-constexpr int kQdPasses = kQdBlocks / (kDcThreads / 16);  // blocks of h a thread quantizes (QF)
-static_assert(2 * kQdPasses == 8, "QF stages h in the 8 staging registers of a thread");
+static_assert(kQdBlocks / (kDcThreads / 16) * 2 <= 8, "QF stages h in the 8 staging registers of a thread");
 
 // the largest of a value over the 16 lanes of a DPP row (every lane gets it)
 __device__ __forceinline__ uint32_t max16_u32(uint32_t v) {
@@ -90,16 +89,16 @@ __device__ __forceinline__ uint32_t scale_byte(const uint4& v, int b, int g) {
   return ((b == 0 ? v.x : b == 1 ? v.y : b == 2 ? v.z : v.w) >> (8 * g)) & 0xFFu;
 }
 
-size_t down_combine_lds_bytes(int64_t n, int64_t I, bool mid_lds, bool mid_bf16) {
-  size_t b = (size_t)(n + 1) * 16 * 4;
+size_t down_combine_lds_bytes(int64_t n, int64_t I, bool mid_lds, bool mid_bf16, int groups = 1) {
+  size_t b = (size_t)groups * (n + 1) * 16 * 4;
   if (mid_lds) b += (size_t)n * ((mid_bf16 ? 2 : 1) * I + kDcPad) + (size_t)n * (I / 128) * 4 + (size_t)n * 4;
   return b;
 }
 
 // SH: the block-FP8 shared expert runs inside this launch (its own
 // instantiations, so that the routed-only ones carry none of its registers)
-template <int NB, int D, bool MID_LDS, int ST = 8, bool SH = false, bool LONG = true, bool QF = false>
-__global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
+template <int NB, int D, bool MID_LDS, int ST = 8, bool SH = false, bool LONG = true, bool QF = false, int G = 1>
+__global__ __launch_bounds__(kDcThreads * G) void down_combine_kernel(
     const uint8_t* __restrict__ midq, const float* __restrict__ mids, const uint8_t* __restrict__ w2, const uint8_t* __restrict__ s2, const int* __restrict__ sorted_entry,
     const int4* __restrict__ tiles, const int* __restrict__ meta, int tmax, int H, int k, int M, int cw,
     const float* __restrict__ topk_w, const float* __restrict__ ys, uint16_t* __restrict__ out,
@@ -108,16 +107,22 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
   constexpr int I = NB * 128;
   constexpr bool A16 = ST == 8;  // mid staged widened to bf16 (else E4M3, widened at each read)
   static_assert(!QF || (MID_LDS && A16 && !SH), "QF stages the quantized mid as bf16 rows");
+  static_assert(G == 1 || (G == 2 && QF), "two column groups share one workgroup only to share the mid quantization");
+  // G column groups of four waves each; the groups share the staged mid
+  // (with QF: its quantization, half the h traffic and work a group)
+  constexpr int kQP = kQdBlocks / (kDcThreads * G / 16);  // blocks of h a thread quantizes (QF)
   constexpr int LDA = (A16 ? 2 : 1) * I + kDcPad;  // bytes per staged mid row; the pad spreads 16 rows over the banks
   extern __shared__ __align__(16) uint8_t dyn[];
   const int n = M * k;
-  float* yl = reinterpret_cast<float*>(dyn);            // [n + 1][16]; row n takes dropped rows
-  uint8_t* ml = reinterpret_cast<uint8_t*>(yl + (n + 1) * 16);  // [n][LDA]  (MID_LDS) bf16 or E4M3 mid
+  const int tid = threadIdx.x, wave_all = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int grp = G == 1 ? 0 : wave_all >> 2, wave = G == 1 ? wave_all : wave_all & 3;  // group, wave in it
+  const int gtid = G == 1 ? tid : tid & (kDcThreads - 1);                               // thread in the group
+  float* yl = reinterpret_cast<float*>(dyn) + grp * (n + 1) * 16;  // [G][n + 1][16]; row n takes dropped rows
+  uint8_t* ml = reinterpret_cast<uint8_t*>(reinterpret_cast<float*>(dyn) + G * (n + 1) * 16);  // [n][LDA]  (MID_LDS) bf16 or E4M3 mid
   float* msl = reinterpret_cast<float*>(ml + n * LDA);  // [n][NB]   (MID_LDS)
   int* sel = reinterpret_cast<int*>(msl + n * NB);      // [n]       (MID_LDS) sorted_entry
-  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int r = lane & 15, g = lane >> 4;
-  const int c0 = blockIdx.x * cw;
+  const int c0 = (blockIdx.x * G + grp) * cw;
   const int rc = min(r, cw - 1);  // the lane's weight column
   // wave w takes tiles w, w + kDcWaves, ... (my of them); its first D
   // descriptors are read beside meta (indices clamped to the tile array's
@@ -160,18 +165,18 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
   float sts[kSs];
   int ste[kSs];
   if (QF) {
-    // h of block qb = 16 p + tid / 16 (row qb / NB, block qb % NB), the
+    // h of block qb = 16 G p + tid / 16 (row qb / NB, block qb % NB), the
     // lane's 8 values; past the last block the last one again (unused)
 #pragma unroll
-    for (int p = 0; p < kQdPasses; ++p) {
-      const int qb = min(16 * p + (tid >> 4), n * NB - 1);
+    for (int p = 0; p < kQP; ++p) {
+      const int qb = min(16 * G * p + (tid >> 4), n * NB - 1);
       const float* ph = hin + (size_t)(qb / NB) * I + 128 * (qb % NB) + 8 * (tid & 15);
       st[2 * p] = ld16(ph);
       st[2 * p + 1] = ld16(ph + 4);
     }
 #pragma unroll
     for (int q = 0; q < kSs; ++q) {
-      const int idx = tid + kDcThreads * q;
+      const int idx = tid + kDcThreads * G * q;
       ste[q] = idx < n ? sorted_entry[idx] : 0;
     }
   } else if (MID_LDS) {
@@ -277,7 +282,7 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
   // ---- staged mid to LDS (widened to bf16 when A16)
   if (QF) {
 #pragma unroll
-    for (int p = 0; p < kQdPasses; ++p) {
+    for (int p = 0; p < kQP; ++p) {
       const uint4 v0 = st[2 * p], v1 = st[2 * p + 1];
       const uint32_t vb[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
       uint32_t am = 0;  // |h| bit patterns order as the values do
@@ -294,7 +299,7 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
                 << (8 * i);
         }
       }
-      const int qb = 16 * p + (tid >> 4);
+      const int qb = 16 * G * p + (tid >> 4);
       if (qb < n * NB) {
         const int row = qb / NB, b = qb % NB, kk = 128 * b + 8 * (tid & 15);
         *reinterpret_cast<uint4*>(ml + row * LDA + 2 * kk) =
@@ -308,7 +313,7 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
     }
 #pragma unroll
     for (int q = 0; q < kSs; ++q) {
-      const int idx = tid + kDcThreads * q;
+      const int idx = tid + kDcThreads * G * q;
       if (idx < n) sel[idx] = ste[q];
     }
     barrier_lds();
@@ -392,7 +397,7 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(
   }
   // out[t, c0 + 2p .. + 2): float64 products and sum in slot order (+ shared), one bf16 rounding
   const int pairs = cw >> 1;
-  for (int idx = tid; idx < M * pairs; idx += kDcThreads) {
+  for (int idx = gtid; idx < M * pairs; idx += kDcThreads) {
     const int t = idx / pairs, cc = 2 * (idx - t * pairs);
     double a0 = 0.0, a1 = 0.0;
     for (int j = 0; j < k; ++j) {
@@ -526,6 +531,26 @@ hipError_t launch_down_combine(const moe_plan* p, const CallArgs& a, Ev ev) {
   const bool lng = n > kDcWaves * d_slots;
   if (qf) {  // at most kQdBlocks mid blocks, no wave with more tiles than slots
     if (!mid_lds || wide || sh.hq || lng) return hipErrorInvalidValue;
+    if (H % (2 * cw) == 0) {
+      // two column groups a workgroup share the mid quantization: half the
+      // h reads and quantizing work of one workgroup per group
+      const size_t lds2 = down_combine_lds_bytes(n, I, true, true, 2);
+      auto go2 = [&](auto kern) {
+        return launch_k(kern, dim3(H / (2 * cw)), dim3(2 * kDcThreads), lds2, a.stream, ev,
+                        wsp<uint8_t>(p, p->L.midq), wsp<float>(p, p->L.mids), reinterpret_cast<const uint8_t*>(a.w2),
+                        reinterpret_cast<const uint8_t*>(a.s2), wsp<int>(p, p->L.sorted_entry),
+                        wsp<int4>(p, p->X.tiles), wsp<int>(p, p->X.meta), tmax, H, (int)p->s.top_k, (int)a.M, cw,
+                        wsp<float>(p, p->L.topk_w), ys, reinterpret_cast<uint16_t*>(a.out), tp_own_partial(p), sh,
+                        wsp<float>(p, p->X.h), wsp<uint8_t>(p, p->L.midq), wsp<float>(p, p->L.mids));
+      };
+      switch (nb) {
+        case 1: return go2(down_combine_kernel<1, 8, true, 8, false, false, true, 2>);
+        case 2: return go2(down_combine_kernel<2, 8, true, 8, false, false, true, 2>);
+        case 3: return go2(down_combine_kernel<3, 5, true, 8, false, false, true, 2>);
+        case 4: return go2(down_combine_kernel<4, 4, true, 8, false, false, true, 2>);
+        default: return hipErrorInvalidValue;
+      }
+    }
     switch (nb) {
       case 1: return go(down_combine_kernel<1, 8, true, 8, false, false, true>);
       case 2: return go(down_combine_kernel<2, 8, true, 8, false, false, true>);
