@@ -141,8 +141,8 @@ __global__ __launch_bounds__(256) void gate_up_m16_kernel(
 // H <= kRqMaxH, the E4M3 mid, no shared expert): the call has no routing
 // launch. Every workgroup ranks the M tokens' logits (a wave per token, the
 // rounds of the routing launch, so the same ids and weights), orders the
-// M k entries expert-major in LDS (each expert holds at most M <= 16 rows:
-// one 16-row tile per active expert), finds its item's expert and rows,
+// M k entries expert-major in LDS (each expert holds at most M <= kRqM
+// rows: one 16-row tile per active expert), finds its item's expert and rows,
 // issues the item's x and weight loads, and quantizes its rows of x to MXFP4
 // into LDS while the weights are in flight; then the item runs as in
 // gate_up_m16_kernel, x read from LDS. Workgroup 0 stores the routing, the
@@ -153,7 +153,8 @@ __global__ __launch_bounds__(256) void gate_up_m16_kernel(
 // ("glm53: FP8 mid hand-off, ...", Modifications table, row "per-row up/gate
 // jobs": the routing rounds overlapped with the first weight loads).
 constexpr int kRqXB = kRqM * (kRqMaxH / 32) / 256;  // x blocks a thread quantizes (at most)
-static_assert(kRqM * (kRqMaxH / 32) % 256 == 0 && kRqMaxH / 512 <= 4 * kSS, "rq tile shape");
+static_assert(kRqM * (kRqMaxH / 32) % 256 == 0 && kRqMaxH / 512 <= 4 * kSS && kRqM <= 16, "rq tile shape");
+static_assert(kRqMaxE == 256 && kRqM <= 4, "a thread per expert, a wave per token");
 
 template <int EC>
 __global__ __launch_bounds__(256) void gate_up_route_kernel(
