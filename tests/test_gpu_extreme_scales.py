@@ -34,7 +34,7 @@ def _check_out_by_group(gout, rout, M):
     return total
 
 
-@pytest.mark.parametrize("M", [8, 40, 300])  # small, mid-range and large paths
+@pytest.mark.parametrize("M", [4, 8, 40, 300])  # routing gate/up with the mid quantized in down, small, mid-range and large paths
 def test_extreme_scales(M):
     shape = X.Shape(M=M, H=512, E=16, I=128, top_k=2)
     d = X.make_extreme_inputs(shape, 7)
