@@ -179,17 +179,16 @@ __global__ __launch_bounds__(256) void gate_up_route_kernel(
   load_keys<EC>(logits + (size_t)min(wave, M - 1) * E, E, lane, key);
   s_bits[tid] = 0u;  // kRqMaxE == blockDim
   __syncthreads();
+  // the ids only: the weights matter to the combine alone, so workgroup 0
+  // forms them (route_weight) once its weight loads are out
+  float sel_l = 0.f;
   if (wave < M) {
     uint32_t sel_e = 0;
-    float w = 0.f;
-    route_keys<EC>(key, E, k, scaling, 0, lane, sel_e, w);
+    topk_wave<EC>(key, k, lane, sel_e, sel_l);
     if (lane < k) {
       s_ids[wave * k + lane] = (int)sel_e;
       atomicOr(&s_bits[sel_e], 1u << wave);
-      if (blockIdx.x == 0) {
-        topk_ids[wave * k + lane] = (int)sel_e;
-        topk_w[wave * k + lane] = w;
-      }
+      if (blockIdx.x == 0) topk_ids[wave * k + lane] = (int)sel_e;
     }
   }
   __syncthreads();
@@ -278,6 +277,10 @@ __global__ __launch_bounds__(256) void gate_up_route_kernel(
       }
       sg[q] = ld4(psg + 256 * ss);
       su[q] = ld4(psu + 256 * ss);
+    }
+    if (blockIdx.x == 0 && wi == 0 && wave < M) {  // the routing weights (route_keys' second half)
+      const float w = route_weight(sel_l, k, lane, scaling);
+      if (lane < k) topk_w[wave * k + lane] = w;
     }
     // x -> MXFP4 into LDS (the routing launch's quantizer, the same codes)
 #pragma unroll
