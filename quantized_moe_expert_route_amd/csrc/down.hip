@@ -127,11 +127,35 @@ __global__ __launch_bounds__(kDcThreads * G) void down_combine_kernel(
   // wave w takes tiles w, w + kDcWaves, ... (my of them); its first D
   // descriptors are read beside meta (indices clamped to the tile array's
   // bound, tmax), so the weight loads wait for one round trip, not two
+  const int nt = meta[0];
   int4 T[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) T[d] = tiles[min(wave + kDcWaves * d, tmax - 1)];
   const int4 t_first = tiles[0];
-  const int nt = meta[0];
+  constexpr int kSt = MID_LDS ? ST : 1;
+  uint4 st[kSt];
+  constexpr int kSs = ST == 8 ? 1 : 2;  // mid scales and entries a thread stages (n * NB <= kSs * kDcThreads)
+  float sts[kSs];
+  int ste[kSs];
+  if (QF) {
+    // h of block qb = 16 G p + tid / 16 (row qb / NB, block qb % NB), the
+    // lane's 8 values (past the last block the last one again, unused), and
+    // the sorted entries: none depends on the descriptors, so they go out
+    // before the wait for them
+#pragma unroll
+    for (int p = 0; p < kQP; ++p) {
+      const int qb = min(16 * G * p + (tid >> 4), n * NB - 1);
+      const float* ph = hin + (size_t)(qb / NB) * I + 128 * (qb % NB) + 8 * (tid & 15);
+      st[2 * p] = ld16(ph);
+      st[2 * p + 1] = ld16(ph + 4);
+    }
+#pragma unroll
+    for (int q = 0; q < kSs; ++q) {
+      const int idx = tid + kDcThreads * G * q;
+      ste[q] = idx < n ? sorted_entry[idx] : 0;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
   // (all of these loads are issued before the first wait)
   asm volatile("" ::"s"(nt), "s"(t_first.x), "s"(T[0].x), "s"(T[min(1, D - 1)].x), "s"(T[min(2, D - 1)].x),
                "s"(T[min(3, D - 1)].x), "s"(T[min(4, D - 1)].x), "s"(T[min(5, D - 1)].x), "s"(T[min(6, D - 1)].x),
@@ -159,27 +183,7 @@ __global__ __launch_bounds__(kDcThreads * G) void down_combine_kernel(
   for (int d = 1; d < D; ++d)
     if (d >= my && my > 0) T[d] = T[d - 1];
   __builtin_amdgcn_sched_barrier(0);
-  constexpr int kSt = MID_LDS ? ST : 1;
-  uint4 st[kSt];
-  constexpr int kSs = ST == 8 ? 1 : 2;  // mid scales and entries a thread stages (n * NB <= kSs * kDcThreads)
-  float sts[kSs];
-  int ste[kSs];
-  if (QF) {
-    // h of block qb = 16 G p + tid / 16 (row qb / NB, block qb % NB), the
-    // lane's 8 values; past the last block the last one again (unused)
-#pragma unroll
-    for (int p = 0; p < kQP; ++p) {
-      const int qb = min(16 * G * p + (tid >> 4), n * NB - 1);
-      const float* ph = hin + (size_t)(qb / NB) * I + 128 * (qb % NB) + 8 * (tid & 15);
-      st[2 * p] = ld16(ph);
-      st[2 * p + 1] = ld16(ph + 4);
-    }
-#pragma unroll
-    for (int q = 0; q < kSs; ++q) {
-      const int idx = tid + kDcThreads * G * q;
-      ste[q] = idx < n ? sorted_entry[idx] : 0;
-    }
-  } else if (MID_LDS) {
+  if (!QF && MID_LDS) {
 #pragma unroll
     for (int q = 0; q < kSt; ++q) {
       const int idx = tid + kDcThreads * q;
