@@ -58,7 +58,6 @@ constexpr int kDcWaves = kDcThreads / 64;
 constexpr int kDcMidBytes = 32 * 1024;  // n * I staged in LDS from E4M3: ST = 8 uint4 per thread
 constexpr int kDcMidBytesMax = 48 * 1024;  // ST = 12: n up to 192 at I = 256 (the shared expert as a ninth slot)
 constexpr int kDcPad = 16;              // LDS bytes after each staged mid row
-static_assert(kQdBlocks / (kDcThreads / 16) * 2 <= 8, "QF stages h in the 8 staging registers of a thread");
 
 // the largest of a value over the 16 lanes of a DPP row (every lane gets it)
 __device__ __forceinline__ uint32_t max16_u32(uint32_t v) {
@@ -134,6 +133,7 @@ __global__ __launch_bounds__(kDcThreads * G) void down_combine_kernel(
   const int4 t_first = tiles[0];
   constexpr int kSt = MID_LDS ? ST : 1;
   uint4 st[kSt];
+  uint4 hv[QF ? 2 * kQP : 1];  // (QF) the thread's h values
   constexpr int kSs = ST == 8 ? 1 : 2;  // mid scales and entries a thread stages (n * NB <= kSs * kDcThreads)
   float sts[kSs];
   int ste[kSs];
@@ -146,8 +146,8 @@ __global__ __launch_bounds__(kDcThreads * G) void down_combine_kernel(
     for (int p = 0; p < kQP; ++p) {
       const int qb = min(16 * G * p + (tid >> 4), n * NB - 1);
       const float* ph = hin + (size_t)(qb / NB) * I + 128 * (qb % NB) + 8 * (tid & 15);
-      st[2 * p] = ld16(ph);
-      st[2 * p + 1] = ld16(ph + 4);
+      hv[2 * p] = ld16(ph);
+      hv[2 * p + 1] = ld16(ph + 4);
     }
 #pragma unroll
     for (int q = 0; q < kSs; ++q) {
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(kDcThreads * G) void down_combine_kernel(
   if (QF) {
 #pragma unroll
     for (int p = 0; p < kQP; ++p) {
-      const uint4 v0 = st[2 * p], v1 = st[2 * p + 1];
+      const uint4 v0 = hv[2 * p], v1 = hv[2 * p + 1];
       const uint32_t vb[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
       uint32_t am = 0;  // |h| bit patterns order as the values do
 #pragma unroll

@@ -552,6 +552,7 @@ def test_small_down_ring_batches(active):
     (4, 2048, 64, 256, 12, "normal", True, False),  # 96 mid blocks: the mid quantization in its own launch
     (4, 8192, 64, 128, 4, "normal", False, False),  # H past 6144: the routing launch
     (4, 2048, 320, 128, 8, "uniform", False, False),  # E past 256: the routing launch
+    (4, 2048, 64, 512, 16, "normal", True, False),  # 256 mid blocks, 32 KB of mid (four blocks a row)
 ])
 def test_routing_inside_gate_up(M, H, E, I, k, kind, inside, qd):
     """Up to 4 tokens (E <= 256, H <= 6144, no shared expert) the gate/up
@@ -572,3 +573,4 @@ def test_routing_inside_gate_up(M, H, E, I, k, kind, inside, qd):
     np.testing.assert_array_equal(gi["midq"], ref["midq"])
     np.testing.assert_array_equal(gi["mids"].view(np.uint32), ref["mids"].astype(np.float32).view(np.uint32))
     assert _check_out(gout, ref["out"]) == 0, "expected the oracle's bf16 output exactly"
+
